@@ -1,0 +1,156 @@
+"""Oracle paged decode attention (float64), single pass and split-K.
+
+TEST INFRASTRUCTURE (see the package header).
+
+What it follows:
+  * [VLLBC] walk-through of paper §4.1-4.2: the KV cache of a sequence is cut
+    into blocks of B tokens; attention reads it block by block through the
+    block table instead of from one contiguous array.  (The block-wise
+    formula itself is lost from the extracted page.)
+  * [PUFANYI] "按 Block 分配" (the kernel reads through the table, no copy to
+    a contiguous buffer) and its closing remark that paging keeps the dense
+    attention semantics: the result equals attention over the same tokens
+    laid out contiguously.
+  * [DEEPSONAR] §2.1: grouped-query attention, where 64 query heads share
+    8 KV heads.
+
+Readings (listed in the design doc):
+  * The decode step scores the one new query vector of each (sequence, query
+    head) against the keys of all context_len cached tokens with
+    x_t = scale * <q, k_t>, applies a softmax over t and returns
+    sum_t softmax(x)_t v_t.  context_len >= 1.  ``scale`` is the fp32 value the
+    kernel receives, widened exactly.
+  * Query head h reads KV head floor(h / G), G = H / H_kv (contiguous groups).
+  * Split-K: the context is cut at logical positions into partitions of P
+    tokens; partition p yields m_p = max x, l_p = sum exp(x - m_p) and
+    o_p = sum exp(x - m_p) v / l_p; the merge takes M = max m_p,
+    a_p = l_p exp(m_p - M) and returns sum a_p o_p / sum a_p.  Only the
+    ceil(L / P) non-empty partitions exist.
+
+Pinned by tests/test_oracle_attention.py: brute force against a dense
+softmax attention built from scipy.special.softmax on contiguous K/V, closed
+forms (one token -> its value; equal keys or scale 0 -> mean of V), invariance
+under any permutation of physical blocks, shared-prefix identity, GQA equal to
+MHA with repeated KV heads, and split-K merge equal to the single pass.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .dtypes import decode
+
+
+def widen_scale(scale: float) -> float:
+    """The fp32 softmax scale as the kernel sees it, as a float64."""
+    return float(np.float32(scale))
+
+
+def gather_tokens(cache: np.ndarray, table_row, length: int, kv_head: int,
+                  block_size: int) -> np.ndarray:
+    """Rows [length, head_size] of one KV head of one sequence, read through
+    its block table: position t is (table_row[t div B], kv_head, t mod B)."""
+    t = np.arange(length)
+    blocks = np.asarray(table_row, dtype=np.int64)[t // block_size]
+    return cache[blocks, kv_head, t % block_size, :]
+
+
+def kv_head_of(h: int, group: int) -> int:
+    """KV head read by query head ``h`` when ``group`` query heads share one."""
+    return h // group
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * K q)^T V for one query vector (float64)."""
+    x = scale * (K @ q)
+    m = x.max()
+    w = np.exp(x - m)
+    return (w @ V) / w.sum()
+
+
+def paged_attention(query, key_cache, value_cache, block_tables, context_lens,
+                    scale: float, dtype: str, pairs=None) -> np.ndarray:
+    """Decode attention of every (sequence, query head), or of ``pairs``.
+
+    query: raw [S, H, D]; caches: raw [NB, H_kv, B, D]; block_tables: [S, W]
+    ints; context_lens: [S].  Returns float64 [S, H, D] (rows not in ``pairs``
+    are left zero).
+    """
+    S, H, D = query.shape
+    H_kv, B = key_cache.shape[1], key_cache.shape[2]
+    if H % H_kv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = H // H_kv
+    sc = widen_scale(scale)
+    out = np.zeros((S, H, D), dtype=np.float64)
+    wanted = None if pairs is None else {(int(s), int(h)) for s, h in pairs}
+    for s in range(S):
+        L = int(context_lens[s])
+        if L < 1:
+            raise ValueError("context_len must be >= 1")
+        for g in range(H_kv):
+            heads = [h for h in range(H) if kv_head_of(h, G) == g
+                     and (wanted is None or (s, h) in wanted)]
+            if not heads:
+                continue
+            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B), dtype)
+            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B), dtype)
+            for h in heads:
+                out[s, h] = attend(decode(query[s, h], dtype), K, V, sc)
+    return out
+
+
+def split_partials(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                   partition_size: int):
+    """(m, l, o) of every non-empty partition of one query's context."""
+    L = K.shape[0]
+    num_parts = -(-L // partition_size)
+    m = np.empty(num_parts)
+    l = np.empty(num_parts)
+    o = np.empty((num_parts, K.shape[1]))
+    for p in range(num_parts):
+        lo, hi = p * partition_size, min((p + 1) * partition_size, L)
+        x = scale * (K[lo:hi] @ q)
+        m[p] = x.max()
+        w = np.exp(x - m[p])
+        l[p] = w.sum()
+        o[p] = (w @ V[lo:hi]) / l[p]
+    return m, l, o
+
+
+def merge_partials(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """Combine partition results into the softmax-weighted output."""
+    M = m.max()
+    a = l * np.exp(m - M)
+    return (a @ o) / a.sum()
+
+
+def paged_attention_split(query, key_cache, value_cache, block_tables, context_lens,
+                          scale: float, dtype: str, partition_size: int, pairs=None):
+    """Same result as ``paged_attention`` computed partition by partition.
+
+    Returns (out [S, H, D], partials) where partials[(s, h)] = (m, l, o).
+    """
+    S, H, D = query.shape
+    H_kv, B = key_cache.shape[1], key_cache.shape[2]
+    G = H // H_kv
+    sc = widen_scale(scale)
+    out = np.zeros((S, H, D), dtype=np.float64)
+    partials = {}
+    wanted = None if pairs is None else {(int(s), int(h)) for s, h in pairs}
+    for s in range(S):
+        L = int(context_lens[s])
+        if L < 1:
+            raise ValueError("context_len must be >= 1")
+        for g in range(H_kv):
+            heads = [h for h in range(H) if kv_head_of(h, G) == g
+                     and (wanted is None or (s, h) in wanted)]
+            if not heads:
+                continue
+            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B), dtype)
+            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B), dtype)
+            for h in heads:
+                m, l, o = split_partials(decode(query[s, h], dtype), K, V, sc, partition_size)
+                partials[(s, h)] = (m, l, o)
+                out[s, h] = merge_partials(m, l, o)
+    return out, partials

@@ -1,0 +1,50 @@
+"""Oracle slot mapping: logical token position -> physical cache slot.
+
+TEST INFRASTRUCTURE (see the package header).
+
+What it follows:
+  * [PUFANYI] "按 Block 分配": position p lives in logical block p div B; the
+    block table names its physical block; inside that block it sits at
+    offset p mod B (the [3, 0, 4] example sends position 8 to P4, offset 0).
+  * [CSDN] §2.3 (slot-mapping kernel, context-parallel world size 1): the
+    slot id is physical_block * B + offset, one entry per scheduled token, the
+    tokens of request r being those between query_start_loc[r] and
+    query_start_loc[r + 1].
+
+Readings (listed in the design doc):
+  * The padding id the kernel writes for unused entries is -1 (the page names
+    a PAD_ID constant but not its value), and entries from the number of
+    scheduled tokens up to the buffer length are filled with it.
+
+Pinned by: tests/test_oracle_slots.py (the [3, 0, 4] example, the 7-token
+growth example, and bijection onto the occupied slots of random pools).
+"""
+
+from __future__ import annotations
+
+PAD_SLOT = -1
+
+
+def slot_of(table_row, pos: int, block_size: int) -> int:
+    """Physical slot of logical position ``pos`` of one sequence."""
+    logical_block = pos // block_size
+    offset = pos % block_size
+    return int(table_row[logical_block]) * block_size + offset
+
+
+def compute_slot_mapping(query_start_loc, positions, block_tables, block_size: int,
+                         max_num_tokens: int):
+    """Slot of every scheduled token; entries past the last token are PAD_SLOT.
+
+    query_start_loc: [S + 1] ints; positions: [T] ints; block_tables: S rows.
+    Returns a Python list of length ``max_num_tokens``.
+    """
+    num_reqs = len(query_start_loc) - 1
+    num_tokens = int(query_start_loc[num_reqs])
+    if num_tokens > max_num_tokens:
+        raise ValueError("more tokens than the slot buffer holds")
+    out = [PAD_SLOT] * max_num_tokens
+    for r in range(num_reqs):
+        for i in range(int(query_start_loc[r]), int(query_start_loc[r + 1])):
+            out[i] = slot_of(block_tables[r], int(positions[i]), block_size)
+    return out
