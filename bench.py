@@ -1,0 +1,217 @@
+"""Benchmark of the paged-KV decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: copy-on-write block
+copies, slot mapping, cache scatter of the new tokens, and paged decode
+attention (single pass, or split-K when the workload uses partitions).  The
+host allocator runs once at set-up; the step's inputs are resident in HBM when
+the timed region starts.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+METRIC = "paged decode attention: KV tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "llama7b_fp16"
+ATTN_SRC = os.path.join(REPO, "paged_kv_cache_123_amd", "csrc", "attention_kernels.hip")
+
+
+def attention_bytes(w, context_lens) -> int:
+    """Algorithmic bytes of one attention launch: every cached K and V row of
+    every (sequence, KV head) once, q in, out back, the table entries and the
+    context lengths."""
+    e = w.elem_bytes
+    kv = int(sum(context_lens)) * 2 * w.num_kv_heads * w.head_size * e
+    qo = 2 * w.num_seqs * w.num_heads * w.head_size * e
+    tables = 4 * int(sum(-(-int(L) // w.block_size) for L in context_lens))
+    return kv + qo + tables + 4 * w.num_seqs
+
+
+def step_bytes(w, step) -> int:
+    """Algorithmic bytes of the whole step: attention plus the slot mapping
+    (positions, one table entry, slot: 20 B per token), the scatter (read and
+    write of each new K/V row) and the block copies (read + write of K and V)."""
+    e = w.elem_bytes
+    T = step.num_tokens
+    row = w.num_kv_heads * w.head_size * e
+    blk = w.num_kv_heads * w.block_size * w.head_size * e
+    return (attention_bytes(w, step.context_lens_host) + 20 * T + 4 * row * T
+            + 4 * blk * len(step.cow_pairs_host))
+
+
+def pmc_traffic(workload: str, per_launch_bytes: int):
+    """HBM traffic of the attention kernel from a committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(REPO, "profiles", f"paged_attention_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, vals, step, budget_s: float):
+    """Oracle attention (float64 NumPy, one BLAS thread) over the first
+    sequences of the batch, until about ``budget_s`` of CPU work."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import paged_attention
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    tables = step.tables_host
+    lens = step.context_lens_host
+    q = host(step.query)
+    done_tokens, done_seqs, t_used = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        for s in range(w.num_seqs):
+            used = np.unique(tables[s][tables[s] >= 0])
+            idx = torch.from_numpy(used.astype(np.int64)).to(step.key_cache.device)
+            kc = host(step.key_cache.index_select(0, idx))
+            vc = host(step.value_cache.index_select(0, idx))
+            remap = np.full(w.num_blocks, -1, dtype=np.int64)
+            remap[used] = np.arange(used.size)
+            row = np.where(tables[s:s + 1] >= 0, remap[np.maximum(tables[s:s + 1], 0)], -1)
+            t0 = time.perf_counter()
+            paged_attention(q[s:s + 1], kc, vc, row, lens[s:s + 1], w.scale, w.dtype)
+            t_used += time.perf_counter() - t0
+            done_tokens += int(lens[s])
+            done_seqs += 1
+            if t_used >= budget_s:
+                break
+    return {"value": done_tokens / t_used, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done_seqs} of {w.num_seqs} sequences ({done_tokens} KV tokens, "
+                      f"all {w.num_heads} heads), float64 NumPy, 1 BLAS thread, "
+                      f"{t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the workload's split-K partition (0 = single pass)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_123_amd.step import DecodeStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = W.make(args.workload)
+    part = w.partition_size if args.partition_size is None else args.partition_size
+    print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
+    vals = W.make_values(w, "cuda")
+    step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
+                      w.scale, part)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    a_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    a_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step.copy_blocks()
+        step.slot_mapping_kernel()
+        step.scatter()
+        a_start[i].record(stream)
+        step.attention()
+        a_end[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = [a.elapsed_time(b) for a, b in zip(a_start, a_end)]
+    ms_per_step = total_ms / args.steps
+    attn_avg_ms = float(np.mean(attn_ms))
+
+    kv_tokens = int(step.context_lens_host.sum())
+    attn_bytes = attention_bytes(w, step.context_lens_host)
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    value = kv_tokens / (ms_per_step * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_size": w.head_size,
+            "block_size": w.block_size,
+            "kv_tokens": kv_tokens,
+            "max_context_len": int(step.max_context_len),
+            "num_blocks": w.num_blocks,
+            "partition_size": part,
+            "cow_copies": int(len(step.cow_pairs_host)),
+            "step_tokens": int(step.num_tokens),
+        },
+        "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
+        "attention_ms": {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),
+                         "p90": float(np.percentile(attn_ms, 90))},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel" + (" + split_reduce_kernel" if part else ""),
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": pmc_traffic(w.name, attn_bytes),
+            "algorithmic_bytes_per_launch": attn_bytes,
+        },
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, vals, step, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

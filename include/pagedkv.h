@@ -1,0 +1,236 @@
+/*
+ * pagedkv.h — C ABI of the paged-KV decode library for MI355X (gfx950).
+ *
+ * The KV cache of every sequence lives in one pool of fixed-size physical
+ * blocks of B token slots; a per-sequence block table maps logical block i to
+ * an arbitrary physical block.  Sources (web pages on PagedAttention):
+ *   [CSDN]      "PagedAttention 核心创新深度分析" (openeuler.csdn.net)
+ *   [VLLBC]     "paged-attention-kv-cache" visual reading (blog.vllbc.top)
+ *   [DEEPSONAR] "vLLM 的 PagedAttention：显存管理如何撑起大模型推理"
+ *   [PUFANYI]   "Infra: PagedAttention" (pufanyi.com)
+ *
+ * Conventions shared by every call
+ *   - Every call returns int32_t status: PA_OK, PA_EINVAL (a host-side
+ *     argument is invalid: null pointer, unsupported size or dtype, bad
+ *     alignment, unknown sequence), PA_ENOMEM (host allocator only: the pool
+ *     is short; nothing was changed), PA_ELAUNCH (the HIP launch failed).
+ *     Nothing aborts or throws across the ABI; pa_last_error() gives the
+ *     message of the last failing call on the calling thread.
+ *   - Device buffers are owned by the caller.  The library never allocates
+ *     device memory; the split-K workspace is caller-provided.
+ *   - Kernel launches are asynchronous on the caller's hipStream_t, passed as
+ *     void* (NULL = the default stream).  A call returns once its kernels are
+ *     enqueued.
+ *   - Index data that lives on the device (block tables, slots, lengths,
+ *     positions) is trusted: out-of-range values are undefined behaviour, as
+ *     for any indirection a kernel follows.  Host-side sizes are validated.
+ *   - KV cache layout (fixed by this ABI; the pages leave it open): key and
+ *     value caches are each [num_blocks][num_kv_heads][B][head_size],
+ *     row-major, elements of the storage dtype.  Slot s is row
+ *     (s / B, :, s % B, :).  Both cache pointers must be 16-byte aligned.
+ *   - Storage dtypes: PA_F32, PA_F16, PA_BF16.  Attention accumulates in fp32
+ *     and rounds its output to the storage dtype (round to nearest even).
+ *   - Query head h reads KV head h / (num_heads / num_kv_heads): groups of
+ *     consecutive query heads share one KV head ([DEEPSONAR] section 2.1
+ *     describes 64 query heads sharing 8 KV heads).
+ *   - Supported shapes: head_size in {64, 128}; block_size in
+ *     {1, 2, 4, 8, 16, 32, 64, 128}; num_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_status { PA_OK = 0, PA_EINVAL = 1, PA_ENOMEM = 2, PA_ELAUNCH = 3 };
+enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+/* Library version string, e.g. "0.1.0". Static storage. */
+const char* pa_version(void);
+/* Name of a status code. Static storage. */
+const char* pa_status_string(int32_t status);
+/* Message of the last failing call on this thread ("" if none). Valid until
+ * the next failing call on this thread. */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Slot mapping.  [PUFANYI] "按 Block 分配": position p of a sequence is in
+ * logical block p / B, found through the block table, at offset p % B.
+ * [CSDN] section 2.3 (slot-mapping kernel, context-parallel world size 1):
+ * slot = block_tables[r][p / B] * B + p % B for every scheduled token of
+ * request r, the tokens of request r being [query_start_loc[r],
+ * query_start_loc[r+1]).
+ *
+ *   query_start_loc  device int32 [num_reqs + 1], non-decreasing, from 0
+ *   positions        device int64 [num_tokens], logical position per token
+ *   block_tables     device int32 rows of bt_stride entries, one per request
+ *   slot_mapping     device int64 [max_num_tokens] (output); entries
+ *                    [num_tokens, max_num_tokens) are set to -1 (padding)
+ *   num_tokens must equal query_start_loc[num_reqs].
+ * Errors: PA_EINVAL for null pointers, num_reqs < 1, num_tokens < 0,
+ * max_num_tokens < num_tokens, bt_stride < 1, block_size < 1.
+ * ---------------------------------------------------------------------- */
+int32_t pa_compute_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
+                                const int32_t* block_tables, int64_t bt_stride,
+                                int32_t num_reqs, int64_t num_tokens, int64_t max_num_tokens,
+                                int32_t block_size, int64_t* slot_mapping, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Cache scatter.  [VLLBC] walk-through of paper section 4.2 and [PUFANYI]
+ * "按 Block 分配": each new token's key and value rows are stored at its
+ * slot, filling the tail block.  Bit copy, no arithmetic.
+ *
+ *   key, value       device [num_tokens][key_stride] / [..][value_stride]
+ *                    elements; token i's rows are [num_kv_heads][head_size]
+ *                    contiguous starting at element i * stride
+ *   slot_mapping     device int64 [num_tokens]; tokens with slot < 0 are
+ *                    skipped; two tokens with the same slot race
+ *   key_cache, value_cache  device caches (layout above), written in place
+ * Errors: PA_EINVAL for null pointers, bad sizes or dtype, stride smaller
+ * than num_kv_heads * head_size, misaligned caches.
+ * ---------------------------------------------------------------------- */
+int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
+                             int64_t value_stride, void* key_cache, void* value_cache,
+                             const int64_t* slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                             int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block copy for copy-on-write.  [VLLBC] paper section 4.4 / Fig. 8 and
+ * [PUFANYI] "共享前缀，分叉时 Copy-on-write": before a writer appends to a
+ * shared, partly filled tail block, the whole physical block (all KV heads,
+ * all B slots, key and value) is copied into a fresh block.
+ *
+ *   block_mapping    device int64 [num_pairs][2] = (src, dst) block ids; a
+ *                    dst must not repeat nor be another pair's src
+ * Errors: PA_EINVAL for null pointers, num_pairs < 0, bad sizes or dtype.
+ * num_pairs == 0 launches nothing.
+ * ---------------------------------------------------------------------- */
+int32_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                       int64_t num_pairs, int32_t num_kv_heads, int32_t head_size,
+                       int32_t block_size, int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention, single pass.  [VLLBC] walk-through of paper
+ * sections 4.1-4.2: the new query token of every sequence is scored against
+ * all of its cached keys, read block by block through the block table; the
+ * scores go through a softmax and weight the cached values.  [PUFANYI]
+ * closing section: the result is that of dense attention over the same
+ * tokens.  Per (sequence s, query head h), with g = h / (H / H_kv):
+ *   x_t = scale * <query[s][h], K[s][g][t]>,  t < context_lens[s]
+ *   out[s][h] = sum_t softmax(x)_t * V[s][g][t]
+ *
+ *   out, query       device [num_seqs][num_heads][head_size], storage dtype
+ *   block_tables     device int32 rows of bt_stride entries; row s needs
+ *                    ceil(context_lens[s] / B) valid block ids
+ *   context_lens     device int32 [num_seqs], each in [1, max_context_len]
+ *   max_context_len  host bound on context_lens (used to size launches)
+ * Errors: PA_EINVAL for null pointers, unsupported shapes or dtype,
+ * num_heads % num_kv_heads != 0, max_context_len < 1.
+ * ---------------------------------------------------------------------- */
+int32_t pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  int64_t bt_stride, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size,
+                                  int32_t max_context_len, float scale, int32_t dtype,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Split-K variant for long contexts.  The pages do not describe it; it is
+ * the standard partition/merge of a softmax: the context of each sequence is
+ * cut at logical positions into partitions of partition_size tokens; a first
+ * kernel computes per (s, h, partition p) m_p = max x, l_p = sum exp(x - m_p)
+ * and o_p = sum exp(x - m_p) v / l_p over the partition; a second kernel
+ * merges them with M = max m_p, a_p = l_p exp(m_p - M),
+ * out = sum a_p o_p / sum a_p.  Same result as the single pass up to
+ * rounding.
+ *
+ * pa_split_workspace_bytes gives the workspace size for a launch (host call).
+ * Workspace contents (fp32, caller-owned, no initialisation needed):
+ *   max_logits [num_seqs][num_heads][NP], exp_sums [num_seqs][num_heads][NP],
+ *   tmp_out [num_seqs][num_heads][NP][head_size],
+ *   NP = ceil(max_context_len / partition_size), sections 256-byte aligned.
+ * partition_size must be a multiple of block_size and of 16, at most 4096.
+ * Errors: as pa_paged_attention_decode, plus PA_EINVAL for a bad
+ * partition_size, a null workspace or workspace_bytes too small.
+ * ---------------------------------------------------------------------- */
+size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                int32_t max_context_len, int32_t partition_size);
+
+int32_t pa_paged_attention_decode_split(void* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const int32_t* block_tables,
+                                        int64_t bt_stride, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t block_size, int32_t max_context_len,
+                                        float scale, int32_t dtype, int32_t partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator (CPU memory only; no device calls).  Generates the
+ * block tables, slots and copy-on-write pairs the kernels consume.
+ *   [PUFANYI] "按 Block 分配": a sequence of T tokens holds ceil(T/B)
+ *   blocks; new tokens fill the tail block first, a fresh block is taken
+ *   only when the tail is full.
+ *   [CSDN] section 3.2.1: fresh blocks come from the head of the free queue;
+ *   a request that does not fit fails without side effects.
+ *   [CSDN] sections 3.1.2 and 3.2.4: a released request drops its blocks
+ *   tail first; blocks whose count reaches 0 join the tail of the queue.
+ *   [CSDN] section 3.2.3 (touch) and [VLLBC] paper section 4.4 / Fig. 8:
+ *   sharing raises per-block reference counts; a writer whose partly filled
+ *   tail is shared copies it to a fresh block first (copy-on-write); the
+ *   last holder writes in place.
+ * The free queue starts in the caller's order (initial_free_order, a
+ * permutation of 0..num_blocks-1; NULL means ascending).  Sequences are
+ * named by caller-chosen int64 ids.  A pool is not thread-safe.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_pool pa_pool;
+
+/* Create a pool. *out receives the handle. PA_EINVAL for sizes < 1 or an
+ * initial order that is not a permutation. */
+int32_t pa_pool_create(int32_t num_blocks, int32_t block_size,
+                       const int32_t* initial_free_order, pa_pool** out);
+/* Destroy a pool (NULL is ignored). */
+void pa_pool_destroy(pa_pool* pool);
+/* Register an empty sequence. PA_EINVAL if the id exists. */
+int32_t pa_pool_add_seq(pa_pool* pool, int64_t seq);
+/* child shares every block of parent (each count + 1) and its length.
+ * PA_EINVAL if parent is unknown or child exists. */
+int32_t pa_pool_fork(pa_pool* pool, int64_t parent, int64_t child);
+/* Append n >= 1 tokens to seq.  slots_out (host int64 [n]) receives the
+ * physical slot of each new token; cow_pair_out (host int64 [2], may be NULL
+ * only if the caller knows no copy can happen) receives (src, dst) when the
+ * shared tail was copied, and *n_cow_out (0 or 1) says whether it was.
+ * All-or-nothing: PA_ENOMEM leaves the pool unchanged. */
+int32_t pa_pool_append(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_out,
+                       int64_t* cow_pair_out, int32_t* n_cow_out);
+/* Release seq: counts drop tail first; blocks reaching 0 join the queue tail. */
+int32_t pa_pool_free_seq(pa_pool* pool, int64_t seq);
+/* Length (tokens) and number of blocks held by seq. */
+int32_t pa_pool_seq_len(const pa_pool* pool, int64_t seq, int64_t* len_out);
+int32_t pa_pool_seq_num_blocks(const pa_pool* pool, int64_t seq, int32_t* n_out);
+/* Block tables of num_seqs sequences into host int32 out[num_seqs][width],
+ * unused entries -1; context_lens_out (host int32 [num_seqs], may be NULL)
+ * receives the lengths.  PA_EINVAL if a sequence holds more than width
+ * blocks or is unknown. */
+int32_t pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t num_seqs,
+                             int32_t* out, int32_t width, int32_t* context_lens_out);
+/* Number of free blocks; reference count of one block (-1 if out of range). */
+int32_t pa_pool_num_free(const pa_pool* pool);
+int32_t pa_pool_ref(const pa_pool* pool, int32_t block);
+/* Free queue from head to tail into host int32 out[cap]; returns the count
+ * written, or -1 on a null argument. */
+int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap);
+/* Number of copy-on-write copies performed since creation. */
+int64_t pa_pool_num_cow(const pa_pool* pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

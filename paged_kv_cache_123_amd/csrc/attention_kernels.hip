@@ -1,0 +1,459 @@
+// Paged decode attention for gfx950: single pass, split-K partition, reduce.
+//
+// What is computed ([VLLBC] walk-through of paper sections 4.1-4.2; [PUFANYI]
+// "按 Block 分配" and its closing section; [DEEPSONAR] section 2.1 for GQA):
+// for each sequence s and query head h, the new query q is scored against
+// every cached key of KV head g = h / G, read block by block through the
+// block table; softmax over the scores weights the cached values.
+//
+// Work decomposition (CDNA4, wave64):
+//   * One workgroup of NW waves per (sequence, KV head, partition).  It serves
+//     all G query heads of the KV head, so every K/V byte is read once.
+//   * A tile is 16 consecutive logical tokens.  Each token's head_size row is
+//     spread over LPT = D / VEC lanes, each lane owning one 16-byte vector
+//     (VEC elements), so one wave-wide load covers TPL = 64 / LPT tokens and a
+//     tile takes U = 16 / TPL loads per cache: whole 1-4 KiB contiguous runs.
+//   * Waves take tiles round-robin; the next tile's K/V loads are issued
+//     before the current tile is consumed (register double buffering).
+//   * Scores: per-lane partial dot product (v_dot2 for 16-bit storage), then
+//     an LPT-lane butterfly sum with DPP.  Each lane group (the LPT lanes of a
+//     token) keeps its own online-softmax state (m, l, acc) in the log2
+//     domain, so the main loop has no cross-lane max/sum traffic; lane groups
+//     are merged with shuffles at the end and waves through LDS, in a fixed
+//     order that depends only on logical positions (results are bit-identical
+//     under any permutation of physical blocks).
+//   * The block-table entries of a chunk of up to 2048 tokens are staged in
+//     LDS once per workgroup.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+#include "pagedkv.h"
+
+namespace pa {
+namespace {
+
+constexpr int kTile = 16;          // tokens per tile
+constexpr int kChunkTokens = 2048;  // tokens whose table entries are staged at once
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- storage traits -------------------------------------------------------
+template <int DT>
+struct St;
+
+template <>
+struct St<PA_F32> {
+  static constexpr int VEC = 4;
+  using QReg = float4;
+  __device__ static QReg load_q(const void* p, int64_t idx) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+  }
+  __device__ static float dot(const QReg& q, const uint4& k) {
+    float s = q.x * __uint_as_float(k.x);
+    s = fmaf(q.y, __uint_as_float(k.y), s);
+    s = fmaf(q.z, __uint_as_float(k.z), s);
+    s = fmaf(q.w, __uint_as_float(k.w), s);
+    return s;
+  }
+  __device__ static void to_float(const uint4& v, float (&f)[VEC]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static void store(void* p, int64_t idx, float x) {
+    static_cast<float*>(p)[idx] = x;
+  }
+};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+template <>
+struct St<PA_F16> {
+  static constexpr int VEC = 8;
+  using QReg = uint4;  // 8 halves, packed
+  __device__ static QReg load_q(const void* p, int64_t idx) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+  }
+  __device__ static float d2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                  c, false);
+  }
+  __device__ static float dot(const QReg& q, const uint4& k) {
+    float s = d2(q.x, k.x, 0.0f);
+    s = d2(q.y, k.y, s);
+    s = d2(q.z, k.z, s);
+    s = d2(q.w, k.w, s);
+    return s;
+  }
+  __device__ static void to_float(const uint4& v, float (&f)[VEC]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2_t h = __builtin_bit_cast(half2_t, w[i]);
+      f[2 * i] = static_cast<float>(h.x);
+      f[2 * i + 1] = static_cast<float>(h.y);
+    }
+  }
+  __device__ static void store(void* p, int64_t idx, float x) {
+    static_cast<_Float16*>(p)[idx] = static_cast<_Float16>(x);
+  }
+};
+
+template <>
+struct St<PA_BF16> {
+  static constexpr int VEC = 8;
+  using QReg = uint4;
+  __device__ static QReg load_q(const void* p, int64_t idx) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+  }
+  __device__ static float d2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                           __builtin_bit_cast(bf162_t, b), c, false);
+  }
+  __device__ static float dot(const QReg& q, const uint4& k) {
+    float s = d2(q.x, k.x, 0.0f);
+    s = d2(q.y, k.y, s);
+    s = d2(q.z, k.z, s);
+    s = d2(q.w, k.w, s);
+    return s;
+  }
+  __device__ static void to_float(const uint4& v, float (&f)[VEC]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(void* p, int64_t idx, float x) {
+    // round to nearest even; NaN stays a quiet NaN
+    uint32_t u = __float_as_uint(x);
+    uint16_t b;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      b = static_cast<uint16_t>((u >> 16) | 0x40);
+    } else {
+      u += 0x7fffu + ((u >> 16) & 1u);
+      b = static_cast<uint16_t>(u >> 16);
+    }
+    static_cast<uint16_t*>(p)[idx] = b;
+  }
+};
+
+// ---- cross-lane sums -------------------------------------------------------
+// Sum over aligned groups of N lanes (N = 8, 16, 32); every lane of a group
+// ends with the group sum.  Within a 16-lane DPP row: xor 1, xor 2 (quad
+// permutes), then half-row mirror and row mirror; 32 adds a swap of rows.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  if constexpr (N >= 16) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, false);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// ---- the decode kernel ------------------------------------------------------
+// FINAL: write out[s][h][:] in storage dtype (single pass); otherwise write the
+// partition's (m, l, o) to the split workspace.
+template <int DT, int D, int G, int NW, bool FINAL>
+__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
+    void* __restrict__ out, const void* __restrict__ query, const void* __restrict__ key_cache,
+    const void* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
+    int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,
+    int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
+    float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
+    float* __restrict__ ws_out) {
+  using S = St<DT>;
+  constexpr int VEC = S::VEC;
+  constexpr int LPT = D / VEC;    // lanes per token
+  constexpr int TPL = 64 / LPT;   // tokens per wave-wide load
+  constexpr int U = kTile / TPL;  // loads per tile per cache
+  static_assert(LPT >= 8 && LPT <= 32 && U >= 1, "unsupported head size");
+
+  const int p = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int L = context_lens[s];
+  const int t_begin = FINAL ? 0 : p * partition_size;
+  if (t_begin >= L) return;  // empty partition: the reduce never reads it
+  const int t_end = FINAL ? L : min(L, t_begin + partition_size);
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int lg = lane / LPT;   // lane group = token within a load
+  const int sub = lane % LPT;  // which 16-byte vector of the row
+  const int B = 1 << log2_block;
+  // strides in 16-byte vectors: a block is [H_kv][B][D], a token row D / VEC
+  const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * LPT;
+  const int64_t head_off_v = static_cast<int64_t>(kvh) * B * LPT + sub;
+  const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
+  const int32_t h0 = kvh * G;
+
+  typename S::QReg q[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    q[j] = S::load_q(query, (static_cast<int64_t>(s) * num_heads + h0 + j) * D + sub * VEC);
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[j][e] = 0.0f;
+  }
+
+  __shared__ int32_t sm_bt[kChunkTokens];
+  const uint4* kc = static_cast<const uint4*>(key_cache);
+  const uint4* vc = static_cast<const uint4*>(value_cache);
+
+  for (int c0 = t_begin; c0 < t_end; c0 += kChunkTokens) {
+    const int c1 = min(c0 + kChunkTokens, t_end);
+    const int b0 = c0 >> log2_block;
+    const int nb = ((c1 - 1) >> log2_block) - b0 + 1;
+    for (int i = threadIdx.x; i < nb; i += NW * 64) sm_bt[i] = bt_row[b0 + i];
+    __syncthreads();
+
+    const int ntiles = (c1 - c0 + kTile - 1) / kTile;
+    // index (in 16-byte vectors) of this lane's part of token t, which is
+    // clamped into the chunk so that tail lanes read a real, finite row
+    auto vec_index = [&](int t) -> int64_t {
+      const int tc = min(t, c1 - 1);
+      const int32_t phys = sm_bt[(tc >> log2_block) - b0];
+      const int off = tc & (B - 1);
+      return static_cast<int64_t>(phys) * blk_stride_v + head_off_v + off * LPT;
+    };
+
+    uint4 kr[U], vr[U];
+    int ti = wave;
+    if (ti < ntiles) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = vec_index(c0 + ti * kTile + u * TPL + lg);
+        kr[u] = kc[idx];
+        vr[u] = vc[idx];
+      }
+    }
+    for (; ti < ntiles; ti += NW) {
+      const int t0 = c0 + ti * kTile;
+      uint4 kn[U], vn[U];
+      const bool more = ti + NW < ntiles;
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t idx = vec_index(t0 + NW * kTile + u * TPL + lg);
+          kn[u] = kc[idx];
+          vn[u] = vc[idx];
+        }
+      }
+      // scores of this lane group's U tokens for all G heads (log2 domain)
+      float x[G][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool valid = t0 + u * TPL + lg < c1;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float d = group_sum<LPT>(S::dot(q[j], kr[u]));
+          x[j][u] = valid ? d * scale_log2 : -INFINITY;
+        }
+      }
+      float vf[U][VEC];
+#pragma unroll
+      for (int u = 0; u < U; ++u) S::to_float(vr[u], vf[u]);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float mt = m[j];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mt = fmaxf(mt, x[j][u]);
+        const float ms = mt == -INFINITY ? 0.0f : mt;
+        const float c = __builtin_amdgcn_exp2f(m[j] - ms);
+        l[j] *= c;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[j][e] *= c;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pr = __builtin_amdgcn_exp2f(x[j][u] - ms);
+          l[j] += pr;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pr, vf[u][e], acc[j][e]);
+        }
+        m[j] = mt;
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kr[u] = kn[u];
+          vr[u] = vn[u];
+        }
+      }
+    }
+    __syncthreads();  // sm_bt is rewritten by the next chunk
+  }
+
+  // ---- merge the lane groups of this wave (lanes sharing `sub`) ----
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float mo = __shfl_xor(m[j], off);
+      const float lo = __shfl_xor(l[j], off);
+      const float mt = fmaxf(m[j], mo);
+      const float ms = mt == -INFINITY ? 0.0f : mt;
+      const float ca = __builtin_amdgcn_exp2f(m[j] - ms);
+      const float cb = __builtin_amdgcn_exp2f(mo - ms);
+      // a + b == b + a exactly, so both partner lanes end with the same value
+      l[j] = l[j] * ca + lo * cb;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = __shfl_xor(acc[j][e], off);
+        acc[j][e] = acc[j][e] * ca + ao * cb;
+      }
+      m[j] = mt;
+    }
+  }
+
+  // ---- merge the waves through LDS, in wave order ----
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
+  if (lg == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm_acc[wave][j][sub * VEC + e] = acc[j][e];
+      if (sub == 0) {
+        sm_m[wave][j] = m[j];
+        sm_l[wave][j] = l[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += NW * 64) {
+    const int j = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
+    float lsum = 0.0f, a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = __builtin_amdgcn_exp2f(sm_m[w][j] - M);  // idle wave: exp2(-inf) = 0
+      lsum = fmaf(sm_l[w][j], c, lsum);
+      a = fmaf(sm_acc[w][j][d], c, a);
+    }
+    const int64_t row = static_cast<int64_t>(s) * num_heads + h0 + j;
+    if constexpr (FINAL) {
+      S::store(out, row * D + d, a / lsum);
+    } else {
+      const int64_t slot = row * num_partitions + p;
+      ws_out[slot * D + d] = a / lsum;
+      if (d == 0) {
+        ws_max[slot] = M * kLn2;
+        ws_sum[slot] = lsum;
+      }
+    }
+  }
+}
+
+// Merge of the partitions of one (sequence, head): M = max m_p,
+// a_p = l_p exp(m_p - M), out = sum a_p o_p / sum a_p, in partition order.
+template <int DT, int D>
+__global__ __launch_bounds__(D) void split_reduce_kernel(
+    void* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t num_heads,
+    int32_t partition_size, int32_t num_partitions, const float* __restrict__ ws_max,
+    const float* __restrict__ ws_sum, const float* __restrict__ ws_out) {
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int d = threadIdx.x;
+  const int L = context_lens[s];
+  const int np = min((L + partition_size - 1) / partition_size, num_partitions);
+  const int64_t row = static_cast<int64_t>(s) * num_heads + h;
+  const float* mrow = ws_max + row * num_partitions;
+  const float* lrow = ws_sum + row * num_partitions;
+  const float* orow = ws_out + row * num_partitions * D;
+  float M = -INFINITY;
+  for (int i = 0; i < np; ++i) M = fmaxf(M, mrow[i]);
+  float wsum = 0.0f, a = 0.0f;
+  for (int i = 0; i < np; ++i) {
+    const float w = lrow[i] * __builtin_amdgcn_exp2f((mrow[i] - M) * kLog2e);
+    wsum += w;
+    a = fmaf(w, orow[static_cast<int64_t>(i) * D + d], a);
+  }
+  St<DT>::store(out, row * D + d, a / wsum);
+}
+
+template <int DT, int D, int G, bool FINAL>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  int log2_block = 0;
+  while ((1 << log2_block) < a.block_size) ++log2_block;
+  const dim3 grid(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, NW, FINAL>), grid, dim3(NW * 64), 0, stream,
+                     a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
+                     a.context_lens, a.num_heads, a.num_kv_heads, log2_block, a.partition_size,
+                     a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum, a.ws_out);
+  return hipGetLastError();
+}
+
+template <int DT, int D, bool FINAL>
+hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return launch_decode_t<DT, D, 1, FINAL>(a, stream);
+    case 2: return launch_decode_t<DT, D, 2, FINAL>(a, stream);
+    case 4: return launch_decode_t<DT, D, 4, FINAL>(a, stream);
+    case 8: return launch_decode_t<DT, D, 8, FINAL>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool FINAL>
+hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_size == 64;
+  switch (a.dtype) {
+    case PA_F32:
+      return d64 ? dispatch_g<PA_F32, 64, FINAL>(a, stream)
+                 : dispatch_g<PA_F32, 128, FINAL>(a, stream);
+    case PA_F16:
+      return d64 ? dispatch_g<PA_F16, 64, FINAL>(a, stream)
+                 : dispatch_g<PA_F16, 128, FINAL>(a, stream);
+    case PA_BF16:
+      return d64 ? dispatch_g<PA_BF16, 64, FINAL>(a, stream)
+                 : dispatch_g<PA_BF16, 128, FINAL>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((split_reduce_kernel<DT, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
+                     stream, a.out, a.context_lens, a.num_heads, a.partition_size,
+                     a.num_partitions, a.ws_max, a.ws_sum, a.ws_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.partition_size == 0 ? dispatch_decode<true>(a, stream)
+                               : dispatch_decode<false>(a, stream);
+}
+
+hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream) {
+  const bool d64 = a.head_size == 64;
+  switch (a.dtype) {
+    case PA_F32:
+      return d64 ? launch_reduce_t<PA_F32, 64>(a, stream) : launch_reduce_t<PA_F32, 128>(a, stream);
+    case PA_F16:
+      return d64 ? launch_reduce_t<PA_F16, 64>(a, stream) : launch_reduce_t<PA_F16, 128>(a, stream);
+    case PA_BF16:
+      return d64 ? launch_reduce_t<PA_BF16, 64>(a, stream)
+                 : launch_reduce_t<PA_BF16, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,216 @@
+// Host block allocator: physical block pool with reference counts and
+// copy-on-write, producing the block tables and slots the kernels consume.
+//
+// Semantics ([PUFANYI] "按 Block 分配"; [CSDN] sections 3.1.2, 3.2.1, 3.2.3,
+// 3.2.4; [VLLBC] paper section 4.4 / Fig. 8) are described in pagedkv.h.
+// Design: the free queue is an intrusive doubly linked list over block ids
+// (prev/next arrays), so taking the head, appending at the tail and removing
+// an arbitrary block are all O(1) with no allocation after creation.
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+#include "status.h"
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> blocks;
+  int64_t len = 0;
+};
+
+}  // namespace
+
+struct pa_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ref;
+  // Free queue as a linked list; kNone marks list ends / "not queued".
+  static constexpr int32_t kNone = -1;
+  std::vector<int32_t> prev, next;
+  std::vector<uint8_t> queued;
+  int32_t head = kNone, tail = kNone, num_free = 0;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t num_cow = 0;
+
+  void push_tail(int32_t b) {
+    prev[b] = tail;
+    next[b] = kNone;
+    if (tail != kNone) next[tail] = b; else head = b;
+    tail = b;
+    queued[b] = 1;
+    ++num_free;
+  }
+  int32_t pop_head() {
+    int32_t b = head;
+    head = next[b];
+    if (head != kNone) prev[head] = kNone; else tail = kNone;
+    prev[b] = next[b] = kNone;
+    queued[b] = 0;
+    --num_free;
+    return b;
+  }
+  int32_t take() {  // caller checked num_free
+    int32_t b = pop_head();
+    ref[b] = 1;
+    return b;
+  }
+  int64_t fresh_blocks_needed(const Seq& s, int32_t n) const {
+    const int64_t B = block_size;
+    int64_t need = 0;
+    if (s.len % B != 0 && ref[s.blocks.back()] > 1) need += 1;  // copy of the shared tail
+    need += (s.len + n + B - 1) / B - (s.len + B - 1) / B;
+    return need;
+  }
+};
+
+extern "C" {
+
+int32_t pa_pool_create(int32_t num_blocks, int32_t block_size,
+                       const int32_t* initial_free_order, pa_pool** out) {
+  if (!out) return pa::fail(PA_EINVAL, "pa_pool_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks < 1 || block_size < 1)
+    return pa::fail(PA_EINVAL, "pa_pool_create: num_blocks and block_size must be >= 1");
+  auto* p = new pa_pool();
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ref.assign(num_blocks, 0);
+  p->prev.assign(num_blocks, pa_pool::kNone);
+  p->next.assign(num_blocks, pa_pool::kNone);
+  p->queued.assign(num_blocks, 0);
+  for (int32_t i = 0; i < num_blocks; ++i) {
+    int32_t b = initial_free_order ? initial_free_order[i] : i;
+    if (b < 0 || b >= num_blocks || p->queued[b]) {
+      delete p;
+      return pa::fail(PA_EINVAL, "pa_pool_create: initial_free_order is not a permutation");
+    }
+    p->push_tail(b);
+  }
+  *out = p;
+  return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+int32_t pa_pool_add_seq(pa_pool* pool, int64_t seq) {
+  if (!pool) return pa::fail(PA_EINVAL, "pa_pool_add_seq: pool is NULL");
+  if (pool->seqs.count(seq)) return pa::fail(PA_EINVAL, "pa_pool_add_seq: sequence exists");
+  pool->seqs.emplace(seq, Seq{});
+  return PA_OK;
+}
+
+int32_t pa_pool_fork(pa_pool* pool, int64_t parent, int64_t child) {
+  if (!pool) return pa::fail(PA_EINVAL, "pa_pool_fork: pool is NULL");
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return pa::fail(PA_EINVAL, "pa_pool_fork: unknown parent");
+  if (pool->seqs.count(child)) return pa::fail(PA_EINVAL, "pa_pool_fork: child exists");
+  Seq c = it->second;
+  for (int32_t b : c.blocks) pool->ref[b] += 1;
+  pool->seqs.emplace(child, std::move(c));
+  return PA_OK;
+}
+
+int32_t pa_pool_append(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_out,
+                       int64_t* cow_pair_out, int32_t* n_cow_out) {
+  if (!pool || !slots_out) return pa::fail(PA_EINVAL, "pa_pool_append: NULL argument");
+  if (n < 1) return pa::fail(PA_EINVAL, "pa_pool_append: n must be >= 1");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return pa::fail(PA_EINVAL, "pa_pool_append: unknown sequence");
+  Seq& s = it->second;
+  const int64_t B = pool->block_size;
+  const bool will_copy = s.len % B != 0 && pool->ref[s.blocks.back()] > 1;
+  if (will_copy && !cow_pair_out)
+    return pa::fail(PA_EINVAL, "pa_pool_append: a copy is needed but cow_pair_out is NULL");
+  if (pool->fresh_blocks_needed(s, n) > pool->num_free)
+    return pa::fail(PA_ENOMEM, "pa_pool_append: not enough free blocks");
+  if (n_cow_out) *n_cow_out = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (s.len % B == 0) {
+      s.blocks.push_back(pool->take());
+    } else if (pool->ref[s.blocks.back()] > 1) {
+      const int32_t old = s.blocks.back();
+      const int32_t fresh = pool->take();
+      pool->ref[old] -= 1;
+      s.blocks.back() = fresh;
+      cow_pair_out[0] = old;
+      cow_pair_out[1] = fresh;
+      if (n_cow_out) *n_cow_out = 1;
+      pool->num_cow += 1;
+    }
+    slots_out[i] = static_cast<int64_t>(s.blocks[s.len / B]) * B + s.len % B;
+    s.len += 1;
+  }
+  return PA_OK;
+}
+
+int32_t pa_pool_free_seq(pa_pool* pool, int64_t seq) {
+  if (!pool) return pa::fail(PA_EINVAL, "pa_pool_free_seq: pool is NULL");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return pa::fail(PA_EINVAL, "pa_pool_free_seq: unknown sequence");
+  const std::vector<int32_t>& blocks = it->second.blocks;
+  for (auto b = blocks.rbegin(); b != blocks.rend(); ++b) {
+    if (--pool->ref[*b] == 0) pool->push_tail(*b);
+  }
+  pool->seqs.erase(it);
+  return PA_OK;
+}
+
+int32_t pa_pool_seq_len(const pa_pool* pool, int64_t seq, int64_t* len_out) {
+  if (!pool || !len_out) return pa::fail(PA_EINVAL, "pa_pool_seq_len: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return pa::fail(PA_EINVAL, "pa_pool_seq_len: unknown sequence");
+  *len_out = it->second.len;
+  return PA_OK;
+}
+
+int32_t pa_pool_seq_num_blocks(const pa_pool* pool, int64_t seq, int32_t* n_out) {
+  if (!pool || !n_out) return pa::fail(PA_EINVAL, "pa_pool_seq_num_blocks: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return pa::fail(PA_EINVAL, "pa_pool_seq_num_blocks: unknown sequence");
+  *n_out = static_cast<int32_t>(it->second.blocks.size());
+  return PA_OK;
+}
+
+int32_t pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t num_seqs,
+                             int32_t* out, int32_t width, int32_t* context_lens_out) {
+  if (!pool || !seqs || !out) return pa::fail(PA_EINVAL, "pa_pool_block_tables: NULL argument");
+  if (num_seqs < 0 || width < 1)
+    return pa::fail(PA_EINVAL, "pa_pool_block_tables: bad num_seqs or width");
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    auto it = pool->seqs.find(seqs[r]);
+    if (it == pool->seqs.end())
+      return pa::fail(PA_EINVAL, "pa_pool_block_tables: unknown sequence");
+    if (static_cast<int64_t>(it->second.blocks.size()) > width)
+      return pa::fail(PA_EINVAL, "pa_pool_block_tables: table wider than width");
+  }
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    const Seq& s = pool->seqs.find(seqs[r])->second;
+    int32_t* row = out + static_cast<int64_t>(r) * width;
+    const int32_t nb = static_cast<int32_t>(s.blocks.size());
+    for (int32_t j = 0; j < width; ++j) row[j] = j < nb ? s.blocks[j] : -1;
+    if (context_lens_out) context_lens_out[r] = static_cast<int32_t>(s.len);
+  }
+  return PA_OK;
+}
+
+int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->num_free : -1; }
+
+int32_t pa_pool_ref(const pa_pool* pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+  return pool->ref[block];
+}
+
+int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap) {
+  if (!pool || (!out && cap > 0)) return -1;
+  int32_t n = 0;
+  for (int32_t b = pool->head; b != pa_pool::kNone && n < cap; b = pool->next[b]) out[n++] = b;
+  return n;
+}
+
+int64_t pa_pool_num_cow(const pa_pool* pool) { return pool ? pool->num_cow : -1; }
+
+}  // extern "C"

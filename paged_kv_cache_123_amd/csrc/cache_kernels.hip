@@ -1,0 +1,155 @@
+// Integer and copy kernels of the paged-KV path: slot mapping, the cache
+// scatter of new tokens, and whole-block copies for copy-on-write.
+//
+// Sources: [PUFANYI] "按 Block 分配" (position -> logical block -> physical
+// block + offset); [CSDN] section 2.3 (per-request slot mapping over
+// query_start_loc); [VLLBC] paper sections 4.2 and 4.4 / Fig. 8 (new tokens
+// fill the tail block; copy-on-write copies one whole block).
+//
+// All three are bandwidth-trivial; they move 16-byte units per lane so every
+// wave touches whole 1 KiB runs of the cache.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+
+namespace pa {
+namespace {
+
+// One workgroup per request: its tokens [qsl[r], qsl[r+1]) get
+// slot = table[r][pos / B] * B + pos % B.  Workgroups past num_reqs write the
+// padding entries [num_tokens, max_num_tokens) with -1.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ qsl, const int64_t* __restrict__ positions,
+    const int32_t* __restrict__ block_tables, int64_t bt_stride, int32_t num_reqs,
+    int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
+    int64_t* __restrict__ slot_mapping) {
+  const int64_t r = blockIdx.x;
+  if (r < num_reqs) {
+    const int64_t begin = qsl[r], end = qsl[r + 1];
+    const int32_t* row = block_tables + r * bt_stride;
+    for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
+      const int64_t pos = positions[i];
+      const int64_t blk = row[pos / block_size];
+      slot_mapping[i] = blk * block_size + pos % block_size;
+    }
+    return;
+  }
+  const int64_t pad_begin = num_tokens + (r - num_reqs) * 4096;
+  const int64_t pad_end = pad_begin + 4096 < max_num_tokens ? pad_begin + 4096 : max_num_tokens;
+  for (int64_t i = pad_begin + threadIdx.x; i < pad_end; i += blockDim.x) slot_mapping[i] = -1;
+}
+
+// One workgroup per token.  Unit = 16 bytes when every row start is 16-byte
+// aligned, else the element size; the copy is a bit copy either way.
+template <typename U>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const U* __restrict__ key, const U* __restrict__ value, int64_t key_stride_u,
+    int64_t value_stride_u, U* __restrict__ key_cache, U* __restrict__ value_cache,
+    const int64_t* __restrict__ slot_mapping, int32_t row_units, int32_t head_units,
+    int32_t block_size) {
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot % block_size;
+  const int32_t num_heads = row_units / head_units;
+  const U* ksrc = key + i * key_stride_u;
+  const U* vsrc = value + i * value_stride_u;
+  // cache element (blk, h, off, :) starts at ((blk * H + h) * B + off) * head
+  for (int32_t u = threadIdx.x; u < row_units; u += blockDim.x) {
+    const int32_t h = u / head_units, e = u % head_units;
+    const int64_t dst = ((blk * num_heads + h) * block_size + off) * head_units + e;
+    key_cache[dst] = ksrc[u];
+    value_cache[dst] = vsrc[u];
+  }
+}
+
+// grid.x = pair, grid.y = chunk of the block; a block is one contiguous run of
+// block_units 16-byte units in each cache.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+    const int64_t* __restrict__ block_mapping, int64_t block_units, int64_t chunk_units) {
+  const int64_t pair = blockIdx.x;
+  const int64_t src = block_mapping[2 * pair], dst = block_mapping[2 * pair + 1];
+  const int64_t begin = blockIdx.y * chunk_units;
+  const int64_t end = begin + chunk_units < block_units ? begin + chunk_units : block_units;
+  const uint4* ks = key_cache + src * block_units;
+  const uint4* vs = value_cache + src * block_units;
+  uint4* kd = key_cache + dst * block_units;
+  uint4* vd = value_cache + dst * block_units;
+  for (int64_t u = begin + threadIdx.x; u < end; u += blockDim.x) {
+    kd[u] = ks[u];
+    vd[u] = vs[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
+                               const int32_t* block_tables, int64_t bt_stride, int32_t num_reqs,
+                               int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
+                               int64_t* slot_mapping, hipStream_t stream) {
+  const int64_t pad = max_num_tokens - num_tokens;
+  const int64_t pad_groups = (pad + 4095) / 4096;
+  const int64_t grid = num_reqs + pad_groups;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, stream,
+                     query_start_loc, positions, block_tables, bt_stride, num_reqs, num_tokens,
+                     max_num_tokens, block_size, slot_mapping);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
+                                    int64_t value_stride, void* key_cache, void* value_cache,
+                                    const int64_t* slot_mapping, int64_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                    int32_t elem_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t head_bytes = static_cast<int64_t>(head_size) * elem_bytes;
+  const bool vec16 = head_bytes % 16 == 0 && (key_stride * elem_bytes) % 16 == 0 &&
+                     (value_stride * elem_bytes) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(key) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(value) % 16 == 0;
+  const dim3 grid(static_cast<uint32_t>(num_tokens));
+  if (vec16) {
+    const int32_t head_units = static_cast<int32_t>(head_bytes / 16);
+    const int32_t row_units = head_units * num_kv_heads;
+    const int32_t threads = row_units < 256 ? ((row_units + 63) / 64) * 64 : 256;
+    hipLaunchKernelGGL(reshape_and_cache_kernel<uint4>, grid, dim3(threads), 0, stream,
+                       static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                       key_stride * elem_bytes / 16, value_stride * elem_bytes / 16,
+                       static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache),
+                       slot_mapping, row_units, head_units, block_size);
+  } else if (elem_bytes == 4) {
+    const int32_t row_units = head_size * num_kv_heads;
+    hipLaunchKernelGGL(reshape_and_cache_kernel<uint32_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value),
+                       key_stride, value_stride, static_cast<uint32_t*>(key_cache),
+                       static_cast<uint32_t*>(value_cache), slot_mapping, row_units, head_size,
+                       block_size);
+  } else {
+    const int32_t row_units = head_size * num_kv_heads;
+    hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                       key_stride, value_stride, static_cast<uint16_t*>(key_cache),
+                       static_cast<uint16_t*>(value_cache), slot_mapping, row_units, head_size,
+                       block_size);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                              int64_t num_pairs, int64_t block_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t block_units = block_bytes / 16;
+  const int64_t chunk_units = 2048;  // 32 KiB of each cache per workgroup
+  const int64_t chunks = (block_units + chunk_units - 1) / chunk_units;
+  hipLaunchKernelGGL(copy_blocks_kernel,
+                     dim3(static_cast<uint32_t>(num_pairs), static_cast<uint32_t>(chunks)),
+                     dim3(256), 0, stream, static_cast<uint4*>(key_cache),
+                     static_cast<uint4*>(value_cache), block_mapping, block_units, chunk_units);
+  return hipGetLastError();
+}
+
+}  // namespace pa

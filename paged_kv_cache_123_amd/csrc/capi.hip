@@ -1,0 +1,199 @@
+// extern "C" entry points of the device half of pagedkv.h: host-side argument
+// validation, then the launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "launch.h"
+#include "pagedkv.h"
+#include "status.h"
+
+namespace {
+
+using pa::fail;
+
+int32_t elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool pow2_in(int32_t v, int32_t lo, int32_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+int32_t launched(hipError_t e, const char* who) {
+  if (e == hipSuccess) return PA_OK;
+  std::string msg = std::string(who) + ": launch failed: " + hipGetErrorString(e);
+  return fail(PA_ELAUNCH, msg.c_str());
+}
+
+// Shared checks of the two attention entry points.
+int32_t check_decode(const char* who, void* out, const void* query, const void* key_cache,
+                     const void* value_cache, const int32_t* block_tables, int64_t bt_stride,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                     int32_t max_context_len, int32_t dtype) {
+  std::string w(who);
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PA_EINVAL, (w + ": NULL pointer").c_str());
+  if (num_seqs < 1 || num_heads < 1 || num_kv_heads < 1 || max_context_len < 1)
+    return fail(PA_EINVAL, (w + ": sizes must be >= 1").c_str());
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, (w + ": num_heads must be a multiple of num_kv_heads").c_str());
+  const int32_t g = num_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_EINVAL, (w + ": num_heads / num_kv_heads must be 1, 2, 4 or 8").c_str());
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_EINVAL, (w + ": head_size must be 64 or 128").c_str());
+  if (!pow2_in(block_size, 1, 128))
+    return fail(PA_EINVAL, (w + ": block_size must be a power of two in [1, 128]").c_str());
+  if (elem_bytes(dtype) == 0) return fail(PA_EINVAL, (w + ": unknown dtype").c_str());
+  if (bt_stride < (max_context_len + block_size - 1) / block_size)
+    return fail(PA_EINVAL, (w + ": bt_stride smaller than ceil(max_context_len / B)").c_str());
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_EINVAL, (w + ": out, query and caches must be 16-byte aligned").c_str());
+  return PA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_compute_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
+                                const int32_t* block_tables, int64_t bt_stride,
+                                int32_t num_reqs, int64_t num_tokens, int64_t max_num_tokens,
+                                int32_t block_size, int64_t* slot_mapping, void* stream) {
+  if (!query_start_loc || !block_tables || !slot_mapping || (!positions && num_tokens > 0))
+    return fail(PA_EINVAL, "pa_compute_slot_mapping: NULL pointer");
+  if (num_reqs < 1 || num_tokens < 0 || max_num_tokens < num_tokens || bt_stride < 1 ||
+      block_size < 1)
+    return fail(PA_EINVAL, "pa_compute_slot_mapping: bad sizes");
+  return launched(pa::launch_slot_mapping(query_start_loc, positions, block_tables, bt_stride,
+                                          num_reqs, num_tokens, max_num_tokens, block_size,
+                                          slot_mapping, static_cast<hipStream_t>(stream)),
+                  "pa_compute_slot_mapping");
+}
+
+int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
+                             int64_t value_stride, void* key_cache, void* value_cache,
+                             const int64_t* slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                             int32_t dtype, void* stream) {
+  const int32_t eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PA_EINVAL, "pa_reshape_and_cache: unknown dtype");
+  if (num_tokens < 0 || num_kv_heads < 1 || head_size < 1 || block_size < 1)
+    return fail(PA_EINVAL, "pa_reshape_and_cache: bad sizes");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_EINVAL, "pa_reshape_and_cache: NULL pointer");
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_size;
+  if (key_stride < row || value_stride < row)
+    return fail(PA_EINVAL, "pa_reshape_and_cache: stride smaller than num_kv_heads*head_size");
+  if (!aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_EINVAL, "pa_reshape_and_cache: caches must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(key) % eb != 0 || reinterpret_cast<uintptr_t>(value) % eb != 0)
+    return fail(PA_EINVAL, "pa_reshape_and_cache: key/value not aligned to their element size");
+  return launched(pa::launch_reshape_and_cache(key, value, key_stride, value_stride, key_cache,
+                                               value_cache, slot_mapping, num_tokens,
+                                               num_kv_heads, head_size, block_size, eb,
+                                               static_cast<hipStream_t>(stream)),
+                  "pa_reshape_and_cache");
+}
+
+int32_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                       int64_t num_pairs, int32_t num_kv_heads, int32_t head_size,
+                       int32_t block_size, int32_t dtype, void* stream) {
+  const int32_t eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PA_EINVAL, "pa_copy_blocks: unknown dtype");
+  if (num_pairs < 0 || num_kv_heads < 1 || head_size < 1 || block_size < 1)
+    return fail(PA_EINVAL, "pa_copy_blocks: bad sizes");
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_mapping)
+    return fail(PA_EINVAL, "pa_copy_blocks: NULL pointer");
+  const int64_t block_bytes =
+      static_cast<int64_t>(num_kv_heads) * block_size * head_size * eb;
+  if (block_bytes % 16 != 0 || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_EINVAL, "pa_copy_blocks: blocks must be whole 16-byte units, caches aligned");
+  return launched(pa::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
+                                         block_bytes, static_cast<hipStream_t>(stream)),
+                  "pa_copy_blocks");
+}
+
+int32_t pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  int64_t bt_stride, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size,
+                                  int32_t max_context_len, float scale, int32_t dtype,
+                                  void* stream) {
+  int32_t st = check_decode("pa_paged_attention_decode", out, query, key_cache, value_cache,
+                            block_tables, bt_stride, context_lens, num_seqs, num_heads,
+                            num_kv_heads, head_size, block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                   /*partition_size=*/0, /*num_partitions=*/1, scale, dtype,
+                   nullptr, nullptr, nullptr};
+  return launched(pa::launch_decode(a, static_cast<hipStream_t>(stream)),
+                  "pa_paged_attention_decode");
+}
+
+size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 1 || num_heads < 1 || head_size < 1 || max_context_len < 1 ||
+      partition_size < 1)
+    return 0;
+  const size_t np = (static_cast<size_t>(max_context_len) + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  return 2 * align256(rows * sizeof(float)) + align256(rows * head_size * sizeof(float));
+}
+
+int32_t pa_paged_attention_decode_split(void* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const int32_t* block_tables,
+                                        int64_t bt_stride, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t block_size, int32_t max_context_len,
+                                        float scale, int32_t dtype, int32_t partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_decode("pa_paged_attention_decode_split", out, query, key_cache,
+                            value_cache, block_tables, bt_stride, context_lens, num_seqs,
+                            num_heads, num_kv_heads, head_size, block_size, max_context_len,
+                            dtype);
+  if (st != PA_OK) return st;
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_decode_split: partition_size must be a multiple of 16 and "
+                "of block_size, at most 4096");
+  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                               partition_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_EINVAL, "pa_paged_attention_decode_split: workspace missing or too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL, "pa_paged_attention_decode_split: workspace must be 256-byte aligned");
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  char* ws = static_cast<char*>(workspace);
+  float* ws_max = reinterpret_cast<float*>(ws);
+  float* ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  float* ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, partition_size,
+                   np, scale, dtype, ws_max, ws_sum, ws_out};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_split (partition)");
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_split (reduce)");
+}
+
+}  // extern "C"

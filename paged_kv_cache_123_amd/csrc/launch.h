@@ -1,0 +1,48 @@
+// Internal launchers of the HIP kernels, called by the ABI layer after it has
+// validated every host-side argument.  Each returns hipSuccess or the launch
+// error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
+                               const int32_t* block_tables, int64_t bt_stride, int32_t num_reqs,
+                               int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
+                               int64_t* slot_mapping, hipStream_t stream);
+
+// elem_bytes: storage element size; row_elems = num_kv_heads * head_size.
+hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
+                                    int64_t value_stride, void* key_cache, void* value_cache,
+                                    const int64_t* slot_mapping, int64_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                    int32_t elem_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                              int64_t num_pairs, int64_t block_bytes, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;                 // final output (single pass) or nullptr
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  int64_t bt_stride;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_heads, num_kv_heads, head_size, block_size;
+  int32_t partition_size;    // tokens per partition (split) or 0 (single pass)
+  int32_t num_partitions;    // NP (split) or 1
+  float scale;
+  int32_t dtype;
+  float* ws_max;             // split workspace sections, or nullptr
+  float* ws_sum;
+  float* ws_out;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,185 @@
+"""Torch-tensor front end of the device entry points of pagedkv.h.
+
+Argument marshalling only: shapes, dtypes and devices are checked here, sizes
+are read off the tensors, and the call goes to the HIP library on the current
+torch stream.  Every computation happens in the library's kernels.
+
+Tensor shapes (see include/pagedkv.h for the semantics):
+  key_cache, value_cache  [num_blocks, num_kv_heads, block_size, head_size]
+  query, out              [num_seqs, num_heads, head_size]
+  block_tables            int32 [num_seqs, width]
+  context_lens            int32 [num_seqs]
+  key, value (new tokens) [num_tokens, num_kv_heads, head_size] (token stride free)
+  slot_mapping            int64 [>= num_tokens]
+  block_mapping           int64 [num_pairs, 2]
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import PA_BF16, PA_F16, PA_F32, check, lib
+
+_DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported storage dtype {t.dtype}") from None
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("pagedkv kernels take device tensors")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _contig(name: str, t: torch.Tensor) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _cache_shape(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_size]")
+    if key_cache.dtype != value_cache.dtype:
+        raise ValueError("key and value caches differ in dtype")
+    _contig("key_cache", key_cache)
+    _contig("value_cache", value_cache)
+    return tuple(int(x) for x in key_cache.shape)
+
+
+def compute_slot_mapping(query_start_loc: torch.Tensor, positions: torch.Tensor,
+                         block_tables: torch.Tensor, block_size: int,
+                         slot_mapping: torch.Tensor, num_tokens: int) -> None:
+    """slot_mapping[i] = block_tables[r, pos_i // B] * B + pos_i % B; tail -> -1."""
+    _dev(query_start_loc, positions, block_tables, slot_mapping)
+    if query_start_loc.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise TypeError("query_start_loc and block_tables must be int32")
+    if positions.dtype != torch.int64 or slot_mapping.dtype != torch.int64:
+        raise TypeError("positions and slot_mapping must be int64")
+    for n, t in (("query_start_loc", query_start_loc), ("positions", positions),
+                 ("block_tables", block_tables), ("slot_mapping", slot_mapping)):
+        _contig(n, t)
+    num_reqs = query_start_loc.numel() - 1
+    if block_tables.dim() != 2 or block_tables.shape[0] < num_reqs:
+        raise ValueError("block_tables must be [>= num_reqs, width]")
+    if positions.numel() < num_tokens:
+        raise ValueError("positions shorter than num_tokens")
+    check(lib().pa_compute_slot_mapping(
+        query_start_loc.data_ptr(), positions.data_ptr(), block_tables.data_ptr(),
+        block_tables.stride(0), num_reqs, num_tokens, slot_mapping.numel(), block_size,
+        slot_mapping.data_ptr(), _stream()))
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Store each new token's K/V rows at its slot (slots < 0 are skipped)."""
+    _dev(key, value, key_cache, value_cache, slot_mapping)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise TypeError("new K/V must have the cache dtype")
+    if key.dim() != 3 or tuple(key.shape[1:]) != (hkv, D) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_size]")
+    for n, t in (("key", key), ("value", value)):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{n} rows must be contiguous [num_kv_heads, head_size]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < key.shape[0]:
+        raise ValueError("slot_mapping must be int64 with an entry per token")
+    check(lib().pa_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), key_cache.data_ptr(),
+        value_cache.data_ptr(), slot_mapping.data_ptr(), key.shape[0], hkv, D, B,
+        _dtype(key_cache), _stream()))
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                block_mapping: torch.Tensor) -> None:
+    """cache[dst] = cache[src] for every (src, dst) row, key and value."""
+    _dev(key_cache, value_cache, block_mapping)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if block_mapping.dtype != torch.int64 or (block_mapping.numel() and
+                                              tuple(block_mapping.shape[1:]) != (2,)):
+        raise ValueError("block_mapping must be int64 [num_pairs, 2]")
+    _contig("block_mapping", block_mapping)
+    n = block_mapping.shape[0] if block_mapping.numel() else 0
+    check(lib().pa_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(),
+                               block_mapping.data_ptr(), n, hkv, D, B, _dtype(key_cache),
+                               _stream()))
+
+
+def _attn_common(out, query, key_cache, value_cache, block_tables, context_lens):
+    _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if query.dim() != 3 or query.shape[2] != D or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
+    if query.dtype != key_cache.dtype or out.dtype != key_cache.dtype:
+        raise TypeError("query/out must have the cache dtype")
+    for n, t in (("query", query), ("out", out), ("block_tables", block_tables),
+                 ("context_lens", context_lens)):
+        _contig(n, t)
+    S = query.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] < S:
+        raise ValueError("block_tables must be int32 [num_seqs, width]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() < S:
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    return S, query.shape[1], hkv, D, B
+
+
+def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                           value_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float,
+                           max_context_len: int) -> None:
+    """Single-pass paged decode attention into ``out``."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
+    check(lib().pa_paged_attention_decode(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), _stream()))
+
+
+def split_workspace_bytes(num_seqs: int, num_heads: int, head_size: int,
+                          max_context_len: int, partition_size: int) -> int:
+    return int(lib().pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                              partition_size))
+
+
+def alloc_split_workspace(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,
+                          partition_size: int, device) -> torch.Tensor:
+    """A byte tensor large enough for the split-K workspace (256-byte aligned)."""
+    n = split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len, partition_size)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def paged_attention_decode_split(out: torch.Tensor, query: torch.Tensor,
+                                 key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                 scale: float, max_context_len: int, partition_size: int,
+                                 workspace: torch.Tensor) -> None:
+    """Split-K paged decode attention (partition kernel + reduce kernel)."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
+    _dev(workspace)
+    check(lib().pa_paged_attention_decode_split(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), partition_size, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+
+
+def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head_size: int,
+                    max_context_len: int, partition_size: int):
+    """(max_logits [S,H,NP], exp_sums [S,H,NP], tmp_out [S,H,NP,D]) views of a
+    split workspace, in the layout pagedkv.h documents."""
+    np_ = -(-max_context_len // partition_size)
+    rows = num_seqs * num_heads * np_
+    sec = -(-rows * 4 // 256) * 256
+    f = workspace.view(torch.uint8)
+    mx = f[:rows * 4].view(torch.float32).view(num_seqs, num_heads, np_)
+    sm = f[sec:sec + rows * 4].view(torch.float32).view(num_seqs, num_heads, np_)
+    to = f[2 * sec:2 * sec + rows * head_size * 4].view(torch.float32)
+    return mx, sm, to.view(num_seqs, num_heads, np_, head_size)

@@ -1,0 +1,73 @@
+"""Oracle side of the GPU parity tests: replays a workload's allocator history
+through the oracle pool and applies the oracle's cache writes and attention
+to host copies of the inputs.  Imports nothing from the product package."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle.allocator import OraclePool
+from oracle.attention import paged_attention, paged_attention_split
+from oracle.cache_ops import copy_blocks, reshape_and_cache
+from oracle.slots import compute_slot_mapping
+
+
+def to_host(t):
+    """Raw storage array of a torch tensor: float32 / float16 / uint16 (bf16 bits)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class OracleStep:
+    def __init__(self, w):
+        pool = OraclePool(w.num_blocks, w.block_size, w.free_order)
+        for op in w.prefill:
+            if op[0] == "add":
+                pool.add_seq(op[1])
+            elif op[0] == "append":
+                pool.append(op[1], op[2])
+            else:
+                pool.fork(op[1], op[2])
+        positions, qsl, cow, slots = [], [0], [], []
+        for s, n in w.step:
+            start = pool.seq_len(s)
+            sl, c = pool.append(s, n)
+            slots += sl
+            cow += c
+            positions += list(range(start, start + n))
+            qsl.append(qsl[-1] + n)
+        self.pool = pool
+        self.seqs = [s for s, _ in w.step]
+        width = max(len(pool.block_table(s)) for s in self.seqs)
+        self.tables = np.full((len(self.seqs), width), -1, dtype=np.int64)
+        for r, s in enumerate(self.seqs):
+            t = pool.block_table(s)
+            self.tables[r, :len(t)] = t
+        self.context_lens = np.array([pool.seq_len(s) for s in self.seqs], dtype=np.int64)
+        self.positions = positions
+        self.query_start_loc = qsl
+        self.cow_pairs = cow
+        self.alloc_slots = slots
+        self.w = w
+
+    def slot_mapping(self, max_num_tokens=None):
+        T = self.query_start_loc[-1]
+        return compute_slot_mapping(self.query_start_loc, self.positions, self.tables,
+                                    self.w.block_size, max_num_tokens or T)
+
+    def apply_copies(self, kc, vc):
+        copy_blocks(kc, vc, self.cow_pairs)
+
+    def apply_scatter(self, kc, vc, new_key, new_value):
+        reshape_and_cache(kc, vc, new_key, new_value, self.slot_mapping(), self.w.block_size)
+
+    def attention(self, query, kc, vc, pairs=None, tables=None):
+        t = self.tables if tables is None else tables
+        return paged_attention(query, kc, vc, t, self.context_lens, self.w.scale, self.w.dtype,
+                               pairs=pairs)
+
+    def attention_split(self, query, kc, vc, partition_size, pairs=None):
+        return paged_attention_split(query, kc, vc, self.tables, self.context_lens, self.w.scale,
+                                     self.w.dtype, partition_size, pairs=pairs)

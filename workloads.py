@@ -1,0 +1,223 @@
+"""Seeded synthetic workloads for the paged-KV decode path.
+
+Shared by the tests, bench.py and the oracle side.  A workload is a recipe:
+model shape, storage dtype, the pool size and its initial free order, the
+host-allocator operations that build the cache before the decode step (add,
+append, fork), the tokens the step appends, and value tensors drawn from a
+seeded generator.  It holds no part of the method: block tables, slots and
+copy-on-write pairs come from replaying the operations through an allocator
+(the library's or the oracle's), and attention is computed by the kernels or
+by the oracle.
+
+Shapes follow the model families the pages discuss: Llama-7B (32 heads of
+128, fp16), a Qwen2.5-72B-style GQA layer (64 query heads sharing 8 KV heads),
+parallel sampling with a shared prompt, and a long context cut into
+partitions.  Structure comes from numpy.random.default_rng(seed); values come
+from a torch generator seeded with the same seed on the target device.
+
+A decode step's context length counts the token the step writes: a sequence
+listed with length L is prefilled with L - 1 tokens and the step appends the
+L-th, so attention covers L tokens.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str                 # storage dtype: "f32" | "f16" | "bf16"
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    sigma: float               # standard deviation of q, K and V values
+    seed: int
+    free_order: np.ndarray     # int32 [num_blocks], head of the free queue first
+    seqs: list                 # sequence ids, one per batch row of the step
+    prefill: list              # ("add", s) | ("append", s, n) | ("fork", parent, child)
+    step: list                 # (s, n): tokens appended by the step, in order
+    context_lens: list         # tokens each row attends over after the step
+    partition_size: int = 0    # split-K partition (0: single pass)
+    notes: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.seqs)
+
+    @property
+    def num_step_tokens(self) -> int:
+        return sum(n for _, n in self.step)
+
+    @property
+    def max_context_len(self) -> int:
+        return int(max(self.context_lens))
+
+    @property
+    def kv_tokens(self) -> int:
+        return int(sum(self.context_lens))
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def table_width(self) -> int:
+        return -(-self.max_context_len // self.block_size)
+
+
+def _decode_batch(name, seed, lens, *, dtype, H, Hkv, D, B, num_blocks, sigma,
+                  partition_size=0, notes="", rng=None):
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    order = rng.permutation(num_blocks).astype(np.int32)
+    prefill, step = [], []
+    for s, L in enumerate(lens):
+        prefill.append(("add", s))
+        if L > 1:
+            prefill.append(("append", s, int(L) - 1))
+        step.append((s, 1))
+    return Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                    block_size=B, num_blocks=num_blocks, scale=1.0 / math.sqrt(D), sigma=sigma,
+                    seed=seed, free_order=order, seqs=list(range(len(lens))), prefill=prefill,
+                    step=step, context_lens=[int(L) for L in lens],
+                    partition_size=partition_size, notes=notes)
+
+
+def custom_decode(name, seed, lens, *, dtype, H, Hkv, D, B, num_blocks=None, sigma=1.0,
+                  partition_size=0):
+    """A decode batch with the given context lengths (edge-case tests)."""
+    lens = [int(L) for L in lens]
+    nb = num_blocks if num_blocks is not None else _blocks_for(lens, B) + 3
+    return _decode_batch(name, seed, lens, dtype=dtype, H=H, Hkv=Hkv, D=D, B=B,
+                         num_blocks=nb, sigma=sigma, partition_size=partition_size)
+
+
+def _blocks_for(lens, B) -> int:
+    """Pool sizing only: blocks that sequences of these lengths occupy."""
+    return int(sum(-(-int(L) // B) for L in lens))
+
+
+def tiny_fp32(num_seqs=None):
+    lens = [7, 9, 16, 37]
+    return _decode_batch("tiny_fp32", 1, lens, dtype="f32", H=2, Hkv=2, D=64, B=4,
+                         num_blocks=32, sigma=1.0,
+                         notes="4 sequences, B=4, MHA 2x64 fp32, 32-block pool")
+
+
+def llama7b_fp16(num_seqs=64):
+    rng = np.random.default_rng(2)
+    lens = rng.integers(128, 2049, size=64)[:num_seqs]
+    nb = math.ceil(1.1 * _blocks_for(lens, 16))
+    return _decode_batch("llama7b_fp16", 2, lens, dtype="f16", H=32, Hkv=32, D=128, B=16,
+                         num_blocks=nb, sigma=1.0, rng=rng,
+                         notes="Llama-7B layer: 32x128 MHA fp16, B=16, L~U[128,2048], pool +10%")
+
+
+def qwen72b_gqa_bf16(num_seqs=256):
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal(256)[:num_seqs]
+    lens = np.clip(np.rint(np.exp(math.log(1024.0) + z)), 16, 8192).astype(np.int64)
+    nb = _blocks_for(lens, 16)
+    return _decode_batch("qwen72b_gqa_bf16", 3, lens, dtype="bf16", H=64, Hkv=8, D=128, B=16,
+                         num_blocks=nb, sigma=0.5, rng=rng,
+                         notes="GQA 64q/8kv x128 bf16, B=16, lognormal lengths (median 1024, "
+                               "sigma 1, clipped [16, 8192]), pool exactly full")
+
+
+def shared_prefix_bf16(num_groups=16):
+    """Parallel sampling: each prompt group's blocks are shared by 8 samples
+    (fork), then every sample appends 1-64 tokens of its own."""
+    rng = np.random.default_rng(4)
+    samples, B = 8, 16
+    r = rng.integers(1, 16, size=16)[:num_groups]
+    prompts = 1024 + r
+    appends = rng.integers(1, 65, size=(16, samples))[:num_groups]
+    prefill, step, seqs, lens = [], [], [], []
+    for g in range(num_groups):
+        lead = g * samples
+        prefill += [("add", lead), ("append", lead, int(prompts[g]))]
+        for j in range(1, samples):
+            prefill.append(("fork", lead, lead + j))
+        for j in range(samples):
+            step.append((lead + j, int(appends[g, j])))
+            seqs.append(lead + j)
+            lens.append(int(prompts[g] + appends[g, j]))
+    # pool sizing: shared prompt blocks once, plus each sample's own blocks
+    own = sum(-(-int(prompts[g] + appends[g, j]) // B) - int(prompts[g]) // B
+              for g in range(num_groups) for j in range(samples))
+    unique = sum(int(p) // B for p in prompts) + own
+    nb = math.ceil(1.1 * unique)
+    order = rng.permutation(nb).astype(np.int32)
+    return Workload(name="shared_prefix_bf16", dtype="bf16", num_heads=32, num_kv_heads=32,
+                    head_size=128, block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(128),
+                    sigma=1.0, seed=4, free_order=order, seqs=seqs, prefill=prefill, step=step,
+                    context_lens=lens,
+                    notes=f"{num_groups} prompts x 8 samples, prompt 1024+U[1,15] shared "
+                          "(refcount 8), each sample appends U[1,64] tokens; 32x128 bf16, B=16",
+                    extra={"unique_blocks": unique, "prompts": prompts.tolist()})
+
+
+def long_context_bf16(num_seqs=32, context_len=32768):
+    lens = [context_len] * num_seqs
+    nb = math.ceil(1.05 * _blocks_for(lens, 64))
+    return _decode_batch("long_context_bf16", 5, lens, dtype="bf16", H=32, Hkv=32, D=128, B=64,
+                         num_blocks=nb, sigma=1.0, partition_size=512,
+                         notes=f"{num_seqs} x {context_len} tokens, 32x128 MHA bf16, B=64, "
+                               "split-K partitions of 512, pool +5%")
+
+
+CONFIGS = {
+    "tiny_fp32": tiny_fp32,
+    "llama7b_fp16": llama7b_fp16,
+    "qwen72b_gqa_bf16": qwen72b_gqa_bf16,
+    "shared_prefix_bf16": shared_prefix_bf16,
+    "long_context_bf16": long_context_bf16,
+}
+
+
+def make(name: str, **kw) -> Workload:
+    return CONFIGS[name](**kw)
+
+
+def make_values(w: Workload, device, chunk_elems: int = 1 << 26):
+    """Seeded value tensors of a workload on ``device``.
+
+    Returns dict(key_cache, value_cache [NB, H_kv, B, D], query [S, H, D],
+    new_key, new_value [T, H_kv, D]); every element ~ N(0, sigma^2), drawn in
+    fp32 and rounded to the storage dtype.  Unused cache slots hold values
+    too, so nothing depends on memory the step never writes.
+    """
+    import torch
+
+    tdt = getattr(torch, TORCH_DTYPES[w.dtype])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+
+    def draw(shape):
+        out = torch.empty(shape, dtype=tdt, device=device)
+        flat = out.view(shape[0], -1)
+        per_row = flat.shape[1]
+        rows = max(1, chunk_elems // max(per_row, 1))
+        for i in range(0, shape[0], rows):
+            j = min(shape[0], i + rows)
+            x = torch.randn((j - i, per_row), generator=gen, device=device, dtype=torch.float32)
+            flat[i:j] = (x * w.sigma).to(tdt)
+        return out
+
+    cache_shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_size)
+    return {
+        "key_cache": draw(cache_shape),
+        "value_cache": draw(cache_shape),
+        "query": draw((w.num_seqs, w.num_heads, w.head_size)),
+        "new_key": draw((w.num_step_tokens, w.num_kv_heads, w.head_size)),
+        "new_value": draw((w.num_step_tokens, w.num_kv_heads, w.head_size)),
+    }
