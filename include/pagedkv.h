@@ -140,6 +140,16 @@ int32_t pa_paged_attention_decode(void* out, const void* query, const void* key_
                                   int32_t max_context_len, float scale, int32_t dtype,
                                   void* stream);
 
+/* Kernel choice for the attention calls (process-wide, not thread-safe):
+ * 0 = automatic (matrix-core kernel for grouped-query heads, num_heads /
+ * num_kv_heads >= 2, with 16-bit storage and head_size 128; vector kernel
+ * otherwise), 1 = vector kernel always, 2 = matrix-core kernel wherever it
+ * applies (16-bit storage, head_size 128).  Every choice computes the same
+ * result within the stated tolerances.  The initial mode comes from the
+ * environment variable PAGEDKV_DECODE_KERNEL=valu|mfma if set, else 0.
+ * Returns the previous mode, or -1 (mode unchanged) for a mode outside 0..2. */
+int32_t pa_set_decode_kernel(int32_t mode);
+
 /* ------------------------------------------------------------------------
  * Split-K variant for long contexts.  The pages do not describe it; it is
  * the standard partition/merge of a softmax: the context of each sequence is

@@ -6,12 +6,12 @@ torch/ctypes binding.
           paged_attention_decode, paged_attention_decode_split
   host  - Pool: the host block allocator (reference counts, copy-on-write)
   step  - DecodeStep: host allocation + one decode step on the device
+  build - compiles libpagedkv.so in-tree
 
-Importing the package loads libpagedkv.so and raises if it is not built.
+libpagedkv.so is loaded on first use; every entry point raises ImportError if
+it has not been built (there is no fallback path).
 """
 
 from ._lib import PagedKVError, lib
-
-lib()  # fail loudly when the HIP library has not been built
 
 __all__ = ["PagedKVError", "lib"]

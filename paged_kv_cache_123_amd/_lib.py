@@ -29,6 +29,7 @@ SIGNATURES = {
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pa_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _f32, _i32, _vp]),
+    "pa_set_decode_kernel": (_i32, [_i32]),
     "pa_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_attention_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,

@@ -147,6 +147,14 @@ int32_t pa_paged_attention_decode(void* out, const void* query, const void* key_
                   "pa_paged_attention_decode");
 }
 
+int32_t pa_set_decode_kernel(int32_t mode) {
+  if (mode < 0 || mode > 2) {
+    fail(PA_EINVAL, "pa_set_decode_kernel: mode must be 0, 1 or 2");
+    return -1;
+  }
+  return pa::set_decode_kernel(mode);
+}
+
 size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                 int32_t max_context_len, int32_t partition_size) {
   if (num_seqs < 1 || num_heads < 1 || head_size < 1 || max_context_len < 1 ||

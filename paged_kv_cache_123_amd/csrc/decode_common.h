@@ -1,0 +1,189 @@
+// Device helpers shared by the paged decode kernels: storage-dtype traits
+// (16-byte vector loads, dot products, conversions, rounding stores) and
+// cross-lane sums.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pagedkv.h"
+
+namespace pa {
+namespace dev {
+
+constexpr int kTile = 16;          // tokens per tile
+constexpr int kChunkTokens = 2048;  // tokens whose table entries are staged at once
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- storage traits -------------------------------------------------------
+template <int DT>
+struct St;
+
+template <>
+struct St<PA_F32> {
+  static constexpr int VEC = 4;
+  using QReg = float4;
+  __device__ static QReg load_q(const void* p, int64_t idx) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+  }
+  __device__ static float dot(const QReg& q, const uint4& k) {
+    float s = q.x * __uint_as_float(k.x);
+    s = fmaf(q.y, __uint_as_float(k.y), s);
+    s = fmaf(q.z, __uint_as_float(k.z), s);
+    s = fmaf(q.w, __uint_as_float(k.w), s);
+    return s;
+  }
+  __device__ static void to_float(const uint4& v, float (&f)[VEC]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static void store(void* p, int64_t idx, float x) {
+    static_cast<float*>(p)[idx] = x;
+  }
+};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+template <>
+struct St<PA_F16> {
+  static constexpr int VEC = 8;
+  using QReg = uint4;  // 8 halves, packed
+  __device__ static QReg load_q(const void* p, int64_t idx) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+  }
+  __device__ static float d2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                  c, false);
+  }
+  __device__ static float dot(const QReg& q, const uint4& k) {
+    float s = d2(q.x, k.x, 0.0f);
+    s = d2(q.y, k.y, s);
+    s = d2(q.z, k.z, s);
+    s = d2(q.w, k.w, s);
+    return s;
+  }
+  __device__ static void to_float(const uint4& v, float (&f)[VEC]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2_t h = __builtin_bit_cast(half2_t, w[i]);
+      f[2 * i] = static_cast<float>(h.x);
+      f[2 * i + 1] = static_cast<float>(h.y);
+    }
+  }
+  __device__ static void store(void* p, int64_t idx, float x) {
+    static_cast<_Float16*>(p)[idx] = static_cast<_Float16>(x);
+  }
+};
+
+template <>
+struct St<PA_BF16> {
+  static constexpr int VEC = 8;
+  using QReg = uint4;
+  __device__ static QReg load_q(const void* p, int64_t idx) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+  }
+  __device__ static float d2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                           __builtin_bit_cast(bf162_t, b), c, false);
+  }
+  __device__ static float dot(const QReg& q, const uint4& k) {
+    float s = d2(q.x, k.x, 0.0f);
+    s = d2(q.y, k.y, s);
+    s = d2(q.z, k.z, s);
+    s = d2(q.w, k.w, s);
+    return s;
+  }
+  __device__ static void to_float(const uint4& v, float (&f)[VEC]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(void* p, int64_t idx, float x) {
+    // round to nearest even; NaN stays a quiet NaN
+    uint32_t u = __float_as_uint(x);
+    uint16_t b;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      b = static_cast<uint16_t>((u >> 16) | 0x40);
+    } else {
+      u += 0x7fffu + ((u >> 16) & 1u);
+      b = static_cast<uint16_t>(u >> 16);
+    }
+    static_cast<uint16_t*>(p)[idx] = b;
+  }
+};
+
+// ---- cross-lane sums -------------------------------------------------------
+// Sum over aligned groups of N lanes (N = 8, 16, 32); every lane of a group
+// ends with the group sum.  Within a 16-lane DPP row: xor 1, xor 2 (quad
+// permutes), then half-row mirror and row mirror; 32 adds a swap of rows.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  if constexpr (N >= 16) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, false);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+
+// ---- matrix-core helpers (16-bit storage only) ---------------------------
+// Lane layouts (wave64, probed on gfx950):
+//   16x16x32: lane l holds A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]
+//   16x16x16: lane l holds A[l%16][4*(l/16) .. +4] and B[4*(l/16) .. +4][l%16]
+//   result:   lane l holds C[4*(l/16) .. +4][l%16]
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+struct Mma;
+
+template <>
+struct Mma<PA_BF16> {
+  __device__ static f32x4 k32(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4 k16(const uint2& a, const uint2& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  }
+  // 16-bit pattern of x rounded to nearest even, and its value as float
+  __device__ static uint32_t round16(float x, float& back) {
+    const __bf16 h = static_cast<__bf16>(x);
+    back = static_cast<float>(h);
+    return __builtin_bit_cast(uint16_t, h);
+  }
+};
+
+template <>
+struct Mma<PA_F16> {
+  __device__ static f32x4 k32(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4 k16(const uint2& a, const uint2& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t round16(float x, float& back) {
+    const _Float16 h = static_cast<_Float16>(x);
+    back = static_cast<float>(h);
+    return __builtin_bit_cast(uint16_t, h);
+  }
+};
+
+}  // namespace dev
+}  // namespace pa

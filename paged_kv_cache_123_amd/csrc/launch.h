@@ -42,7 +42,16 @@ struct DecodeArgs {
   float* ws_out;
 };
 
+// Paged decode attention (single pass when partition_size == 0, else the
+// partition kernel).  Picks the matrix-core kernel for grouped-query heads
+// with 16-bit storage and head_size 128, the vector kernel otherwise; the
+// choice can be forced where both apply (set_decode_kernel, or the
+// environment variable PAGEDKV_DECODE_KERNEL=valu|mfma at start-up).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+bool decode_mfma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// mode: 0 automatic, 1 vector kernel, 2 matrix-core kernel; returns the previous mode.
+int set_decode_kernel(int mode);
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -143,6 +143,16 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, key_cache: to
         B, max_context_len, scale, _dtype(key_cache), _stream()))
 
 
+DECODE_KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+def set_decode_kernel(mode: str) -> str:
+    """Select the attention kernel ("auto", "valu" or "mfma"); returns the
+    previous choice.  Process-wide."""
+    prev = lib().pa_set_decode_kernel(DECODE_KERNELS[mode])
+    return {v: k for k, v in DECODE_KERNELS.items()}[prev]
+
+
 def split_workspace_bytes(num_seqs: int, num_heads: int, head_size: int,
                           max_context_len: int, partition_size: int) -> int:
     return int(lib().pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,

@@ -26,6 +26,19 @@ def _require_gpu():
     assert torch.cuda.is_available(), "GPU tests need a visible GPU"
 
 
+@pytest.fixture
+def decode_kernel(request):
+    """Force one attention kernel for the test ("valu" or "mfma")."""
+    from paged_kv_cache_123_amd import ops
+    mode = getattr(request, "param", "auto")
+    prev = ops.set_decode_kernel(mode)
+    yield mode
+    ops.set_decode_kernel(prev)
+
+
+BOTH = pytest.mark.parametrize("decode_kernel", ["valu", "mfma"], indirect=True)
+
+
 def check_attention(got_raw, want, dtype, what=""):
     got = decode(got_raw, dtype)
     assert got.shape == want.shape
@@ -118,32 +131,39 @@ def test_growth_example_on_device():
         assert pool.block_table(0) == want_table
 
 
-def test_llama7b_fp16_full_step():
+@BOTH
+def test_llama7b_fp16_full_step(decode_kernel):
     full_parity(W.llama7b_fp16())
 
 
-def test_llama7b_fp16_split():
+@BOTH
+def test_llama7b_fp16_split(decode_kernel):
     full_parity(W.llama7b_fp16(num_seqs=16), partition_size=256)
 
 
-def test_qwen72b_gqa_bf16_full_step():
+@BOTH
+def test_qwen72b_gqa_bf16_full_step(decode_kernel):
     full_parity(W.qwen72b_gqa_bf16())
 
 
-def test_qwen72b_gqa_bf16_split():
+@BOTH
+def test_qwen72b_gqa_bf16_split(decode_kernel):
     full_parity(W.qwen72b_gqa_bf16(num_seqs=64), partition_size=512)
 
 
-def test_shared_prefix_bf16_full_step():
+@BOTH
+def test_shared_prefix_bf16_full_step(decode_kernel):
     step, ora, _ = full_parity(W.shared_prefix_bf16())
     assert len(ora.cow_pairs) == 16 * 7  # the first 7 writers of each group copy
 
 
-def test_long_context_small_split():
+@BOTH
+def test_long_context_small_split(decode_kernel):
     full_parity(W.long_context_bf16(num_seqs=2, context_len=5000))
 
 
-def test_long_context_full_size_sampled():
+@BOTH
+def test_long_context_full_size_sampled(decode_kernel):
     """32 x 32768 tokens, B=64, partitions of 512: kernels at full size,
     oracle on sampled (sequence, head) pairs and the blocks they read."""
     _require_gpu()
@@ -199,14 +219,16 @@ EDGE_CASES = [
 
 @pytest.mark.parametrize("dtype,D,B,G,part", EDGE_CASES,
                          ids=[f"{c[0]}-D{c[1]}-B{c[2]}-G{c[3]}-P{c[4]}" for c in EDGE_CASES])
-def test_edge_shapes(dtype, D, B, G, part):
+@BOTH
+def test_edge_shapes(dtype, D, B, G, part, decode_kernel):
     hkv = 2
     w = W.custom_decode(f"edge_{dtype}_{D}_{B}_{G}", 7, EDGE_LENS, dtype=dtype, H=hkv * G,
                         Hkv=hkv, D=D, B=B, partition_size=part)
     full_parity(w)
 
 
-def test_split_with_empty_partitions():
+@BOTH
+def test_split_with_empty_partitions(decode_kernel):
     """max_context_len far above every length: most partitions are empty."""
     _require_gpu()
     from paged_kv_cache_123_amd import ops
@@ -261,7 +283,8 @@ def test_split_partials_match_oracle():
 
 # ---- determinism and invariances (bit-identical) -----------------------------
 
-def test_rerun_is_bit_identical():
+@BOTH
+def test_rerun_is_bit_identical(decode_kernel):
     _require_gpu()
     w = W.qwen72b_gqa_bf16(num_seqs=32)
     step = _step(w, W.make_values(w, DEV))
@@ -270,8 +293,9 @@ def test_rerun_is_bit_identical():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@BOTH
 @pytest.mark.parametrize("part", [0, 128])
-def test_physical_permutation_is_bit_identical(part):
+def test_physical_permutation_is_bit_identical(part, decode_kernel):
     """Moving every physical block elsewhere (and the tables with it) leaves
     the attention output bit for bit unchanged."""
     _require_gpu()
@@ -299,7 +323,8 @@ def test_physical_permutation_is_bit_identical(part):
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
-def test_shared_prefix_identity_after_cow():
+@BOTH
+def test_shared_prefix_identity_after_cow(decode_kernel):
     """Two forks of one prompt that append the same token read identical
     outputs, although one copied its tail and the other wrote in place."""
     _require_gpu()
