@@ -182,6 +182,44 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Planned launch (load balance).  The two calls above launch one workgroup
+ * per (sequence, KV head[, partition]) in index order, including partitions
+ * past a sequence's end.  With lengths that vary a lot, a launch that starts
+ * the largest pieces of work first and contains no empty pieces finishes
+ * sooner; this pair of calls provides that.  Same results as the calls above.
+ *
+ * pa_decode_plan (host only): from host context lengths, the list of every
+ * non-empty (sequence, partition) item — one item (s, 0) per sequence when
+ * partition_size == 0 — ordered by decreasing token count, counted in
+ * buckets of 256 tokens; items of one bucket keep (sequence, partition)
+ * order so that neighbouring sequences, e.g. forks sharing a prompt, stay
+ * together.  items: host int32 [capacity][2]; *num_items receives the
+ * item count.  items == NULL only queries the count.  PA_EINVAL for a null
+ * context_lens/num_items, num_seqs < 1, a length < 1, partition_size < 0, or
+ * a capacity below the count.
+ *
+ * pa_paged_attention_decode_planned: attention driven by such a list (copied
+ * to the device by the caller: work_items = device int32 [num_work_items][2]).
+ * partition_size == 0: single pass, the list must name every sequence once
+ * as (s, 0) and workspace may be NULL.  partition_size > 0: the split-K
+ * kernels (same rules and workspace as pa_paged_attention_decode_split); the
+ * list must name every non-empty partition once.  Items missing from the
+ * list leave their outputs undefined (no out-of-bounds access).
+ * ---------------------------------------------------------------------- */
+int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
+                       int32_t* items, int64_t capacity, int64_t* num_items);
+
+int32_t pa_paged_attention_decode_planned(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          int64_t bt_stride, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t max_context_len,
+                                          float scale, int32_t dtype, int32_t partition_size,
+                                          const int32_t* work_items, int64_t num_work_items,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (CPU memory only; no device calls).  Generates the
  * block tables, slots and copy-on-write pairs the kernels consume.
  *   [PUFANYI] "按 Block 分配": a sequence of T tokens holds ceil(T/B)

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["cache_kernels.hip", "attention_kernels.hip", "attention_mfma.hip", "capi.hip"]
-CXX_SOURCES = ["block_pool.cpp", "status.cpp"]
+CXX_SOURCES = ["block_pool.cpp", "plan.cpp", "status.cpp"]
 
 # Packed-fp32 instructions are kept out of every HIP build.
 HIPCC_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
@@ -35,27 +35,39 @@ def _run(cmd):
     return "\n".join(lines)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB, obj_dir: str = OBJ) -> str:
+    """Compile every source and link the shared library; returns its path.
+
+    ``defines``: extra NAME=VALUE preprocessor definitions for the HIP sources
+    (tuning constants of the kernels); ``out``/``obj_dir``: where to put the
+    library and objects (defaults: in-tree)."""
+    os.makedirs(obj_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(OBJ, src + ".o")
-        jobs.append(["hipcc", *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(obj_dir, src + ".o")
+        jobs.append(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
-        obj = os.path.join(OBJ, src + ".o")
+        obj = os.path.join(obj_dir, src + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-I/opt/rocm/include", "-c", os.path.join(CSRC, src),
                      "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
-        for out in ex.map(_run, jobs):
-            if verbose and out:
-                print(out)
-    objs = [os.path.join(OBJ, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
-    tmp = LIB + ".tmp"
+        for log in ex.map(_run, jobs):
+            if verbose and log:
+                print(log)
+    objs = [os.path.join(obj_dir, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
+    tmp = out + ".tmp"
     _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--obj-dir", default=OBJ)
+    a = ap.parse_args()
+    print(build(verbose=a.v, defines=a.defines, out=a.out, obj_dir=a.obj_dir))

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,
     int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
-    float* __restrict__ ws_out) {
+    float* __restrict__ ws_out, const int2* __restrict__ items) {
   using S = St<DT>;
   constexpr int VEC = S::VEC;
   constexpr int LPT = D / VEC;    // lanes per token
@@ -58,9 +58,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   constexpr int U = kTile / TPL;  // loads per tile per cache
   static_assert(LPT >= 8 && LPT <= 32 && U >= 1, "unsupported head size");
 
-  const int p = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  const WorkUnit wu = work_unit(items, num_kv_heads);
+  const int p = wu.p;
+  const int kvh = wu.kvh;
+  const int s = wu.s;
   const int L = context_lens[s];
   const int t_begin = FINAL ? 0 : p * partition_size;
   if (t_begin >= L) return;  // empty partition: the reduce never reads it
@@ -274,11 +275,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = 4;
   int log2_block = 0;
   while ((1 << log2_block) < a.block_size) ++log2_block;
-  const dim3 grid(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
+  const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))
+                            : dim3(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, NW, FINAL>), grid, dim3(NW * 64), 0, stream,
                      a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
                      a.context_lens, a.num_heads, a.num_kv_heads, log2_block, a.partition_size,
-                     a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum, a.ws_out);
+                     a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum, a.ws_out,
+                     reinterpret_cast<const int2*>(a.items));
   return hipGetLastError();
 }
 

@@ -142,7 +142,7 @@ int32_t pa_paged_attention_decode(void* out, const void* query, const void* key_
   pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
                    num_seqs, num_heads, num_kv_heads, head_size, block_size,
                    /*partition_size=*/0, /*num_partitions=*/1, scale, dtype,
-                   nullptr, nullptr, nullptr};
+                   nullptr, nullptr, nullptr, nullptr, 0};
   return launched(pa::launch_decode(a, static_cast<hipStream_t>(stream)),
                   "pa_paged_attention_decode");
 }
@@ -197,11 +197,57 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
   float* ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
   pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
                    num_seqs, num_heads, num_kv_heads, head_size, block_size, partition_size,
-                   np, scale, dtype, ws_max, ws_sum, ws_out};
+                   np, scale, dtype, ws_max, ws_sum, ws_out, nullptr, 0};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_split (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_split (reduce)");
+}
+
+int32_t pa_paged_attention_decode_planned(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t partition_size, const int32_t* work_items, int64_t num_work_items, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* who = "pa_paged_attention_decode_planned";
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (!work_items || num_work_items < 1 ||
+      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, "pa_paged_attention_decode_planned: bad work list");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) {
+    pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale,
+                     dtype, nullptr, nullptr, nullptr, work_items, num_work_items};
+    return launched(pa::launch_decode(a, s), who);
+  }
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_decode_planned: partition_size must be 0, or a multiple of "
+                "16 and of block_size, at most 4096");
+  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                               partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_decode_planned: workspace missing, too small or misaligned");
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, partition_size, np,
+                   scale, dtype, reinterpret_cast<float*>(ws),
+                   reinterpret_cast<float*>(ws + align256(rows * sizeof(float))),
+                   reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float))),
+                   work_items, num_work_items};
+  st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_planned (partition)");
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_planned (reduce)");
 }
 
 }  // extern "C"

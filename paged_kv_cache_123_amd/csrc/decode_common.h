@@ -136,6 +136,24 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 
+// ---- work units -------------------------------------------------------------
+// (sequence, KV head, partition) of this workgroup.  With a work list,
+// workgroup b serves item b / H_kv, KV head b % H_kv (items are (sequence,
+// partition) pairs, largest first); without one the grid is
+// (partition, KV head, sequence).
+struct WorkUnit {
+  int s, kvh, p;
+};
+
+__device__ __forceinline__ WorkUnit work_unit(const int2* items, int num_kv_heads) {
+  if (items) {
+    const int2 it = items[blockIdx.x / num_kv_heads];
+    return {it.x, static_cast<int>(blockIdx.x % num_kv_heads), it.y};
+  }
+  return {static_cast<int>(blockIdx.z), static_cast<int>(blockIdx.y),
+          static_cast<int>(blockIdx.x)};
+}
+
 // ---- matrix-core helpers (16-bit storage only) ---------------------------
 // Lane layouts (wave64, probed on gfx950):
 //   16x16x32: lane l holds A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]

@@ -40,6 +40,8 @@ struct DecodeArgs {
   float* ws_max;             // split workspace sections, or nullptr
   float* ws_sum;
   float* ws_out;
+  const int32_t* items;      // work list [num_items][2] = (seq, partition), or nullptr
+  int64_t num_items;
 };
 
 // Paged decode attention (single pass when partition_size == 0, else the

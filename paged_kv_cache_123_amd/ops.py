@@ -18,6 +18,10 @@ from __future__ import annotations
 
 import torch
 
+import ctypes
+
+import numpy as np
+
 from ._lib import PA_BF16, PA_F16, PA_F32, check, lib
 
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -193,3 +197,39 @@ def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head
     sm = f[sec:sec + rows * 4].view(torch.float32).view(num_seqs, num_heads, np_)
     to = f[2 * sec:2 * sec + rows * head_size * 4].view(torch.float32)
     return mx, sm, to.view(num_seqs, num_heads, np_, head_size)
+
+
+def decode_plan(context_lens, partition_size: int) -> np.ndarray:
+    """Host work plan: int32 [num_items, 2] of (sequence, partition), every
+    non-empty item once, largest first (partition_size 0: one per sequence)."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    n = ctypes.c_int64(0)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size, None, 0,
+                               ctypes.byref(n)))
+    items = np.empty((n.value, 2), dtype=np.int32)
+    check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size,
+                               items.ctypes.data_as(p32), n.value, ctypes.byref(n)))
+    return items
+
+
+def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
+                                   key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   scale: float, max_context_len: int, partition_size: int,
+                                   work_items: torch.Tensor, workspace=None) -> None:
+    """Attention driven by a work plan (device int32 [num_items, 2])."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
+    _dev(work_items)
+    if work_items.dtype != torch.int32 or work_items.dim() != 2 or work_items.shape[1] != 2:
+        raise ValueError("work_items must be int32 [num_items, 2]")
+    _contig("work_items", work_items)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().pa_paged_attention_decode_planned(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
+        work_items.shape[0], ws_ptr or None, ws_bytes, _stream()))

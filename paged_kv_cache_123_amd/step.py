@@ -8,7 +8,9 @@ copy-on-write pairs.  Device side, in order on one stream:
   copy_blocks            copy-on-write of shared partial tails
   compute_slot_mapping   physical slot of every new token
   reshape_and_cache      new tokens' K/V into their slots
-  paged attention        single pass or split-K (partition + reduce)
+  paged attention        single pass or split-K (partition + reduce), launched
+                         from a host work plan (largest pieces first) unless
+                         ``planned=False``
 
 ([VLLBC] paper sections 4.2 and 4.4 / Fig. 8; [PUFANYI] "按 Block 分配" and
 "共享前缀，分叉时 Copy-on-write"; [CSDN] section 2.3.)
@@ -33,7 +35,7 @@ class DecodeStep:
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
-                 values: dict, scale: float, partition_size: int = 0):
+                 values: dict, scale: float, partition_size: int = 0, planned: bool = True):
         self.pool = Pool(num_blocks, block_size, free_order)
         for op in history:
             if op[0] == "add":
@@ -80,6 +82,9 @@ class DecodeStep:
         self.query_start_loc = torch.from_numpy(self.query_start_loc_host).to(dev)
         self.slot_mapping = torch.empty(self.num_tokens, dtype=torch.int64, device=dev)
         self.out = torch.empty_like(self.query)
+        self.planned = planned
+        self.plan_host = ops.decode_plan(lens, self.partition_size)
+        self.plan = torch.from_numpy(self.plan_host).to(dev)
         self.workspace = None
         if self.partition_size:
             S, H, D = self.query.shape
@@ -99,7 +104,13 @@ class DecodeStep:
                               self.slot_mapping)
 
     def attention(self):
-        if self.partition_size:
+        if self.planned:
+            ops.paged_attention_decode_planned(self.out, self.query, self.key_cache,
+                                               self.value_cache, self.block_tables,
+                                               self.context_lens, self.scale,
+                                               self.max_context_len, self.partition_size,
+                                               self.plan, self.workspace)
+        elif self.partition_size:
             ops.paged_attention_decode_split(self.out, self.query, self.key_cache,
                                              self.value_cache, self.block_tables,
                                              self.context_lens, self.scale,
