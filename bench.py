@@ -26,7 +26,17 @@ sys.path.insert(0, REPO)
 METRIC = "paged decode attention: KV tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "llama7b_fp16"
-ATTN_SRC = os.path.join(REPO, "paged_kv_cache_123_amd", "csrc", "attention_kernels.hip")
+CSRC = os.path.join(REPO, "paged_kv_cache_123_amd", "csrc")
+ATTN_SRCS = [os.path.join(CSRC, f) for f in ("attention_kernels.hip", "attention_mfma.hip",
+                                             "decode_common.h")]
+
+
+def attention_source_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the attention kernel sources."""
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def attention_bytes(w, context_lens) -> int:
@@ -59,10 +69,59 @@ def pmc_traffic(workload: str, per_launch_bytes: int):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != src_hash:
+    if rec.get("kernel_source_sha256_16") != attention_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def read_reference(nbytes: int = 2 << 30, reps: int = 10):
+    """Achievable read bandwidth on this GPU for the access pattern of a paged
+    cache: whole 4 KiB blocks in a random order (and, for context, in
+    sequential order), timed with HIP events around the library's read probe."""
+    import torch
+
+    from paged_kv_cache_123_amd import ops
+    nblk = nbytes // 4096
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    orders = {"random_4k": torch.randperm(nblk, generator=g).to(torch.int32).cuda(),
+              "sequential_4k": torch.arange(nblk, dtype=torch.int32, device="cuda")}
+    out = {}
+    for name, order in orders.items():
+        ops.probe_read_blocks(buf, order, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            ops.probe_read_blocks(buf, order, sink)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = nblk * 4096 / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+    del buf
+    return out
+
+
+def calibrate_counters() -> dict:
+    """Kernels of known byte count for scaling FETCH_SIZE / WRITE_SIZE: the read
+    probe over 1 GiB (reads only) and copy_blocks of 2048 blocks of 128 KiB in
+    each cache (256 MiB read + 256 MiB written)."""
+    import torch
+
+    from paged_kv_cache_123_amd import ops
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    order = torch.arange(nbytes // 4096, dtype=torch.int32, device="cuda")
+    ops.probe_read_blocks(buf, order, sink)
+    kc = torch.empty((4096, 32, 16, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    pairs = torch.stack([torch.arange(0, 2048), torch.arange(2048, 4096)], 1).cuda()
+    ops.copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    blk = 32 * 16 * 128 * 2
+    return {"probe_read_bytes": nbytes, "copy_blocks_read_bytes": 2 * 2048 * blk,
+            "copy_blocks_write_bytes": 2 * 2048 * blk}
 
 
 def cpu_baseline(w, vals, step, budget_s: float):
@@ -123,6 +182,9 @@ def main():
                     help="attention kernel (auto: matrix cores for grouped-query heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-read-reference", action="store_true")
+    ap.add_argument("--calibrate-counters", action="store_true",
+                    help="only run kernels of known byte count (for rocprofv3 --pmc scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -136,6 +198,9 @@ def main():
     from paged_kv_cache_123_amd.step import DecodeStep
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_counters:
+        print(json.dumps(calibrate_counters()), flush=True)
+        return
     ops.set_decode_kernel(args.kernel)
     w = W.make(args.workload)
     part = w.partition_size if args.partition_size is None else args.partition_size
@@ -219,6 +284,10 @@ def main():
         },
         "wall_s_timed_region": wall,
     }
+    if not args.no_read_reference:
+        ref = read_reference()
+        result["read_reference_gbps"] = ref
+        result["roofline"]["frac_of_random_4k_read"] = achieved / ref["random_4k"]
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, vals, step, args.cpu_budget)

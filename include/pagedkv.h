@@ -277,6 +277,20 @@ int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap);
 /* Number of copy-on-write copies performed since creation. */
 int64_t pa_pool_num_cow(const pa_pool* pool);
 
+/* ------------------------------------------------------------------------
+ * Diagnostic (not part of the decode path): reads num_blocks whole 4 KiB
+ * blocks of buffer, block block_order[i] for i = 0..num_blocks-1, with `grid`
+ * workgroups of 256 lanes x 16 bytes.  A reference of achievable read
+ * bandwidth for a given block order, and a kernel of known byte count for
+ * calibrating hardware counters.
+ *   buffer       device, 16-byte aligned, >= 4096 * (max(block_order) + 1) bytes
+ *   block_order  device int32 [num_blocks], each in range (trusted)
+ *   sink         device, >= 4 bytes (written only on a one-in-2^32 value)
+ * Errors: PA_EINVAL for null pointers, num_blocks < 1, grid < 1, alignment.
+ * ---------------------------------------------------------------------- */
+int32_t pa_probe_read_blocks(const void* buffer, const int32_t* block_order, int64_t num_blocks,
+                             void* sink, int32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["cache_kernels.hip", "attention_kernels.hip", "attention_mfma.hip", "capi.hip"]
+HIP_SOURCES = ["cache_kernels.hip", "attention_kernels.hip", "attention_mfma.hip", "capi.hip",
+               "probe_kernels.hip"]
 CXX_SOURCES = ["block_pool.cpp", "plan.cpp", "status.cpp"]
 
 # Packed-fp32 instructions are kept out of every HIP build.

@@ -113,28 +113,20 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
       return static_cast<int64_t>(phys) * blk_stride_v + head_off_v + off * LPT;
     };
 
-    uint4 kr[U], vr[U];
-    int ti = wave;
-    if (ti < ntiles) {
+    // This wave's tiles are wave, wave + NW, ...; kPrefetch of them are in
+    // flight while one is consumed (a ring of kPrefetch + 1 register slots).
+    const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
+    auto load_tile = [&](int it, uint4 (&kd)[U], uint4 (&vd)[U]) {
+      const int t0 = c0 + (wave + it * NW) * kTile;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t idx = vec_index(c0 + ti * kTile + u * TPL + lg);
-        kr[u] = kc[idx];
-        vr[u] = vc[idx];
+        const int64_t idx = vec_index(t0 + u * TPL + lg);
+        kd[u] = kc[idx];
+        vd[u] = vc[idx];
       }
-    }
-    for (; ti < ntiles; ti += NW) {
-      const int t0 = c0 + ti * kTile;
-      uint4 kn[U], vn[U];
-      const bool more = ti + NW < ntiles;
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t idx = vec_index(t0 + NW * kTile + u * TPL + lg);
-          kn[u] = kc[idx];
-          vn[u] = vc[idx];
-        }
-      }
+    };
+    auto consume = [&](int it, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+      const int t0 = c0 + (wave + it * NW) * kTile;
       // scores of this lane group's U tokens for all G heads (log2 domain)
       float x[G][U];
 #pragma unroll
@@ -168,11 +160,19 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
         }
         m[j] = mt;
       }
-      if (more) {
+    };
+    constexpr int NBUF = kPrefetch + 1;
+    uint4 kb[NBUF][U], vb[NBUF][U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kr[u] = kn[u];
-          vr[u] = vn[u];
+    for (int j = 0; j < kPrefetch; ++j)
+      if (j < my_tiles) load_tile(j, kb[j], vb[j]);
+    for (int it = 0; it < my_tiles; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        if (it + j < my_tiles) {
+          if (it + j + kPrefetch < my_tiles)
+            load_tile(it + j + kPrefetch, kb[(j + kPrefetch) % NBUF], vb[(j + kPrefetch) % NBUF]);
+          consume(it + j, kb[j], vb[j]);
         }
       }
     }
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(D) void split_reduce_kernel(
 
 template <int DT, int D, int G, bool FINAL>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
+  constexpr int NW = PA_VALU_WAVES;
   int log2_block = 0;
   while ((1 << log2_block) < a.block_size) ++log2_block;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))

@@ -115,26 +115,16 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
       return static_cast<int64_t>(phys) * blk_stride_v + head_off_v + off * DV + vec;
     };
 
-    uint4 kr[NK], vr[U];
-    int ti = wave;
-    if (ti < ntiles) {
-      const int t0 = c0 + ti * kTile;
+    const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
+    auto load_tile = [&](int it, uint4 (&kd)[NK], uint4 (&vd)[U]) {
+      const int t0 = c0 + (wave + it * NW) * kTile;
 #pragma unroll
-      for (int k = 0; k < NK; ++k) kr[k] = kc[vec_index(t0 + k_tok, k * 4 + grp)];
+      for (int k = 0; k < NK; ++k) kd[k] = kc[vec_index(t0 + k_tok, k * 4 + grp)];
 #pragma unroll
-      for (int u = 0; u < U; ++u) vr[u] = vc[vec_index(t0 + grp + 4 * u, col)];
-    }
-    for (; ti < ntiles; ti += NW) {
-      const int t0 = c0 + ti * kTile;
-      uint4 kn[NK], vn[U];
-      const bool more = ti + NW < ntiles;
-      if (more) {
-        const int t1 = t0 + NW * kTile;
-#pragma unroll
-        for (int k = 0; k < NK; ++k) kn[k] = kc[vec_index(t1 + k_tok, k * 4 + grp)];
-#pragma unroll
-        for (int u = 0; u < U; ++u) vn[u] = vc[vec_index(t1 + grp + 4 * u, col)];
-      }
+      for (int u = 0; u < U; ++u) vd[u] = vc[vec_index(t0 + grp + 4 * u, col)];
+    };
+    auto consume = [&](int it, const uint4 (&kr)[NK], const uint4 (&vr)[U]) {
+      const int t0 = c0 + (wave + it * NW) * kTile;
       // scores of tokens grp + 4j for head col
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -173,11 +163,20 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
         o[e] = MM::k16(a, phi, o[e]);
         o[e] = MM::k16(a, plo, o[e]);
       }
-      if (more) {
+    };
+    constexpr int NBUF = kPrefetch + 1;
+    uint4 kb[NBUF][NK], vb[NBUF][U];
 #pragma unroll
-        for (int k = 0; k < NK; ++k) kr[k] = kn[k];
+    for (int j = 0; j < kPrefetch; ++j)
+      if (j < my_tiles) load_tile(j, kb[j], vb[j]);
+    for (int it = 0; it < my_tiles; it += NBUF) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) vr[u] = vn[u];
+      for (int j = 0; j < NBUF; ++j) {
+        if (it + j < my_tiles) {
+          if (it + j + kPrefetch < my_tiles)
+            load_tile(it + j + kPrefetch, kb[(j + kPrefetch) % NBUF], vb[(j + kPrefetch) % NBUF]);
+          consume(it + j, kb[j], vb[j]);
+        }
       }
     }
     __syncthreads();
@@ -229,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
 
 template <int DT, int G, bool FINAL>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
+  constexpr int NW = PA_MFMA_WAVES;
   int log2_block = 0;
   while ((1 << log2_block) < a.block_size) ++log2_block;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))

@@ -12,6 +12,20 @@
 namespace pa {
 namespace dev {
 
+// Tuning constants (overridable at build time with -D):
+//   PA_PREFETCH     tiles each wave keeps in flight ahead of the one it consumes
+//   PA_VALU_WAVES   waves per workgroup of the vector kernel
+//   PA_MFMA_WAVES   waves per workgroup of the matrix-core kernel
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 1
+#endif
+#ifndef PA_VALU_WAVES
+#define PA_VALU_WAVES 4
+#endif
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 4
+#endif
+constexpr int kPrefetch = PA_PREFETCH;
 constexpr int kTile = 16;          // tokens per tile
 constexpr int kChunkTokens = 2048;  // tokens whose table entries are staged at once
 constexpr float kLog2e = 1.4426950408889634f;

@@ -233,3 +233,14 @@ def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
         work_items.shape[0], ws_ptr or None, ws_bytes, _stream()))
+
+
+def probe_read_blocks(buffer: torch.Tensor, block_order: torch.Tensor, sink: torch.Tensor,
+                      grid: int = 16384) -> None:
+    """Diagnostic: read ``buffer`` as whole 4 KiB blocks in ``block_order``."""
+    _dev(buffer, block_order, sink)
+    if block_order.dtype != torch.int32:
+        raise TypeError("block_order must be int32")
+    _contig("block_order", block_order)
+    check(lib().pa_probe_read_blocks(buffer.data_ptr(), block_order.data_ptr(),
+                                     block_order.numel(), sink.data_ptr(), grid, _stream()))
