@@ -2,11 +2,12 @@
 
 A step is one pass of the whole hot path over one batch: copy-on-write block
 copies, slot mapping, cache scatter of the new tokens, and paged decode
-attention (single pass, or split-K when the workload uses partitions).  The
-host allocator runs once at set-up; the step's inputs are resident in HBM when
-the timed region starts.  Prints one JSON line.
+attention (single pass, or split-K when the workload uses partitions).  By
+default the step runs as one launch (pa_decode_step); --unfused times the four
+separate calls.  The host allocator runs once at set-up; the step's inputs are
+resident in HBM when the timed region starts.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--unfused] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -60,6 +61,23 @@ def step_bytes(w, step) -> int:
     blk = w.num_kv_heads * w.block_size * w.head_size * e
     return (attention_bytes(w, step.context_lens_host) + 20 * T + 4 * row * T
             + 4 * blk * len(step.cow_pairs_host))
+
+
+def fused_bytes(w, step) -> int:
+    """Algorithmic bytes of the one-launch step: attention, plus the new
+    tokens' K/V rows read and written (4 * row bytes per token), their slots
+    (8 B each), and the copy-on-write of the slots before each fork's first new
+    token (read + write of K and V)."""
+    e = w.elem_bytes
+    row = w.num_kv_heads * w.head_size * e
+    old_slots = 0
+    qsl = step.query_start_loc_host
+    for r, src in enumerate(step.cow_src_host):
+        if src >= 0:
+            first_new = int(step.context_lens_host[r]) - int(qsl[r + 1] - qsl[r])
+            old_slots += first_new % w.block_size
+    return (attention_bytes(w, step.context_lens_host) + (4 * row + 8) * step.num_tokens
+            + 4 * row * old_slots)
 
 
 def pmc_traffic(workload: str, per_launch_bytes: int):
@@ -180,6 +198,9 @@ def main():
                     help="override the workload's split-K partition (0 = single pass)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"],
                     help="attention kernel (auto: matrix cores for grouped-query heads)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time copy_blocks, slot mapping, scatter and attention as four launches "
+                         "instead of the one-launch step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-read-reference", action="store_true")
@@ -210,8 +231,9 @@ def main():
                       w.scale, part)
     torch.cuda.synchronize()
 
+    fused = not args.unfused
     for _ in range(args.warmup):
-        step.run()
+        step.run(fused=fused)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -223,12 +245,17 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step.copy_blocks()
-        step.slot_mapping_kernel()
-        step.scatter()
-        a_start[i].record(stream)
-        step.attention()
-        a_end[i].record(stream)
+        if fused:
+            a_start[i].record(stream)
+            step.fused()
+            a_end[i].record(stream)
+        else:
+            step.copy_blocks()
+            step.slot_mapping_kernel()
+            step.scatter()
+            a_start[i].record(stream)
+            step.attention()
+            a_end[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -238,7 +265,7 @@ def main():
     attn_avg_ms = float(np.mean(attn_ms))
 
     kv_tokens = int(step.context_lens_host.sum())
-    attn_bytes = attention_bytes(w, step.context_lens_host)
+    attn_bytes = fused_bytes(w, step) if fused else attention_bytes(w, step.context_lens_host)
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     value = kv_tokens / (ms_per_step * 1e-3)
     result = {
@@ -266,6 +293,7 @@ def main():
             "num_blocks": w.num_blocks,
             "partition_size": part,
             "attention_kernel": args.kernel,
+            "fused_step": fused,
             "cow_copies": int(len(step.cow_pairs_host)),
             "step_tokens": int(step.num_tokens),
         },
@@ -274,7 +302,11 @@ def main():
                          "p90": float(np.percentile(attn_ms, 90))},
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel" + (" + split_reduce_kernel" if part else ""),
+            "kernel": ("paged_decode_mfma_kernel" if (args.kernel == "mfma" or (
+                args.kernel == "auto" and w.num_heads > w.num_kv_heads)) else "paged_decode_kernel")
+                      + (" + split_reduce_kernel" if part else "")
+                      + (" (one-launch step: copy-on-write + scatter + attention)" if fused
+                         else ""),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -220,6 +220,39 @@ int32_t pa_paged_attention_decode_planned(void* out, const void* query, const vo
                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * One decode step in one launch (plus the reduce when partition_size > 0).
+ * Does what pa_copy_blocks, pa_compute_slot_mapping, pa_reshape_and_cache and
+ * pa_paged_attention_decode_planned do in sequence, for the usual decode
+ * shape of the step: sequence s appends n_s = query_start_loc[s+1] -
+ * query_start_loc[s] tokens at positions [L_s - n_s, L_s), L_s =
+ * context_lens[s] (lengths after the step), their K/V rows being rows
+ * query_start_loc[s] .. of key / value; when cow_src[s] >= 0, the block of
+ * position L_s - n_s (a fresh copy-on-write block, [VLLBC] paper section
+ * 4.4 / Fig. 8) first receives the slots before that position from block
+ * cow_src[s].  Each attention workgroup writes the rows it then reads, so
+ * the caches, slot_mapping and out end exactly as with the four separate
+ * calls.
+ *   key_cache, value_cache  written in place
+ *   query_start_loc  device int32 [num_seqs + 1]
+ *   key, value       device, 16-byte aligned rows [T][num_kv_heads][head_size]
+ *                    with token strides key_stride / value_stride (elements,
+ *                    a multiple of 16 bytes)
+ *   cow_src          device int64 [num_seqs], -1 for none; may be NULL
+ *   slot_mapping     device int64 [T] receiving the new tokens' slots; may be NULL
+ * The other arguments are those of pa_paged_attention_decode_planned.
+ * ---------------------------------------------------------------------- */
+int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* value_cache,
+                       const int32_t* block_tables, int64_t bt_stride,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                       int32_t max_context_len, float scale, int32_t dtype,
+                       int32_t partition_size, const int32_t* work_items, int64_t num_work_items,
+                       void* workspace, size_t workspace_bytes, const int32_t* query_start_loc,
+                       const void* key, const void* value, int64_t key_stride,
+                       int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (CPU memory only; no device calls).  Generates the
  * block tables, slots and copy-on-write pairs the kernels consume.
  *   [PUFANYI] "按 Block 分配": a sequence of T tokens holds ceil(T/B)

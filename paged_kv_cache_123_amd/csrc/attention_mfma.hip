@@ -47,12 +47,12 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
 
 template <int DT, int G, int NW, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
-    void* __restrict__ out, const void* __restrict__ query, const void* __restrict__ key_cache,
-    const void* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
+    void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
+    const void* value_cache, const int32_t* __restrict__ block_tables,
     int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,
     int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
-    float* __restrict__ ws_out, const int2* __restrict__ items) {
+    float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap) {
   constexpr int D = 128;
   constexpr int DV = D / 8;   // 16-byte vectors per token row
   constexpr int NK = D / 32;  // score MFMAs per tile
@@ -78,6 +78,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
   const int64_t head_off_v = static_cast<int64_t>(kvh) * B * DV;
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
+  if (ap.qsl)
+    apply_appends<DV, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
+                                  static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * DV,
+                                  static_cast<int64_t>(kvh) * (1 << log2_block) * DV);
   const int h0 = kvh * G;
 
   uint4 qv[NK];
@@ -237,7 +241,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
                      stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
                      a.partition_size, a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum,
-                     a.ws_out, reinterpret_cast<const int2*>(a.items));
+                     a.ws_out, reinterpret_cast<const int2*>(a.items), a.append);
   return hipGetLastError();
 }
 

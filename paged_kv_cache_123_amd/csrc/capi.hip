@@ -250,4 +250,60 @@ int32_t pa_paged_attention_decode_planned(
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_planned (reduce)");
 }
 
+int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* value_cache,
+                       const int32_t* block_tables, int64_t bt_stride,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                       int32_t max_context_len, float scale, int32_t dtype,
+                       int32_t partition_size, const int32_t* work_items, int64_t num_work_items,
+                       void* workspace, size_t workspace_bytes, const int32_t* query_start_loc,
+                       const void* key, const void* value, int64_t key_stride,
+                       int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
+                       void* stream) {
+  const char* who = "pa_decode_step";
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (!work_items || num_work_items < 1 ||
+      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, "pa_decode_step: bad work list");
+  if (!query_start_loc || !key || !value)
+    return fail(PA_EINVAL, "pa_decode_step: NULL query_start_loc, key or value");
+  const int32_t eb = elem_bytes(dtype);
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_size;
+  if (key_stride < row || value_stride < row || (key_stride * eb) % 16 != 0 ||
+      (value_stride * eb) % 16 != 0 || !aligned16(key) || !aligned16(value))
+    return fail(PA_EINVAL,
+                "pa_decode_step: key/value rows must be 16-byte aligned with a stride of at least "
+                "num_kv_heads * head_size elements");
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, work_items, num_work_items};
+  a.append = pa::dev::AppendArgs{query_start_loc, cow_src, static_cast<const uint4*>(key),
+                                 static_cast<const uint4*>(value), key_stride * eb / 16,
+                                 value_stride * eb / 16, static_cast<uint4*>(key_cache),
+                                 static_cast<uint4*>(value_cache), slot_mapping};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, "pa_decode_step: bad partition_size");
+  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                               partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL, "pa_decode_step: workspace missing, too small or misaligned");
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  char* ws = static_cast<char*>(workspace);
+  a.partition_size = partition_size;
+  a.num_partitions = np;
+  a.ws_max = reinterpret_cast<float*>(ws);
+  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  st = launched(pa::launch_decode(a, s), "pa_decode_step (partition)");
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), "pa_decode_step (reduce)");
+}
+
 }  // extern "C"

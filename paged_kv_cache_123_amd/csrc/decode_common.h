@@ -168,6 +168,64 @@ __device__ __forceinline__ WorkUnit work_unit(const int2* items, int num_kv_head
           static_cast<int>(blockIdx.x)};
 }
 
+// ---- the step's cache writes, fused into the attention launch ---------------
+// A decode step appends n_s new tokens to every sequence s: positions
+// [L_s - n_s, L_s), where L_s = context_lens[s] counts them; their K/V rows are
+// rows qsl[s] .. qsl[s+1]-1 of key/value.  If cow_src[s] >= 0 the block that
+// holds position L_s - n_s is a fresh copy-on-write copy of block cow_src[s]
+// for the slots before the first new token.  Each attention work item
+// (s, kv head, token range) writes exactly the rows it is about to read, so
+// no other workgroup reads them during the launch.
+struct AppendArgs {
+  const int32_t* qsl;      // [S + 1] token offsets; nullptr = nothing to write
+  const int64_t* cow_src;  // [S] source block or -1; nullptr = no copies
+  const uint4* key;        // new rows, 16-byte units
+  const uint4* value;
+  int64_t key_stride_v;    // units between consecutive tokens
+  int64_t value_stride_v;
+  uint4* key_cache;        // the caches, writable
+  uint4* value_cache;
+  int64_t* slot_mapping;   // [T] slots of the new tokens (written), or nullptr
+};
+
+template <int LPT, int NT>
+__device__ void apply_appends(const AppendArgs& ap, int s, int kvh, int L, int t_begin,
+                              int t_end, const int32_t* bt_row, int log2_block,
+                              int64_t blk_stride_v, int64_t head_off_v) {
+  const int i0 = ap.qsl[s];
+  const int n = ap.qsl[s + 1] - i0;
+  const int p0 = L - n;  // first new position
+  const int B = 1 << log2_block;
+  if (n > 0 && ap.cow_src) {
+    const int64_t src = ap.cow_src[s];
+    const int jb = p0 >> log2_block;
+    const int bstart = jb << log2_block;
+    if (src >= 0 && bstart >= t_begin && bstart < t_end) {
+      const int64_t dst = bt_row[jb];
+      const int units = (p0 - bstart) * LPT;  // old slots of the copied block
+      for (int u = threadIdx.x; u < units; u += NT) {
+        ap.key_cache[dst * blk_stride_v + head_off_v + u] =
+            ap.key_cache[src * blk_stride_v + head_off_v + u];
+        ap.value_cache[dst * blk_stride_v + head_off_v + u] =
+            ap.value_cache[src * blk_stride_v + head_off_v + u];
+      }
+    }
+  }
+  const int a = max(p0, t_begin), b = min(L, t_end);
+  const int units = (b > a ? b - a : 0) * LPT;
+  for (int u = threadIdx.x; u < units; u += NT) {
+    const int t = a + u / LPT, e = u % LPT;
+    const int64_t i = i0 + (t - p0);
+    const int64_t phys = bt_row[t >> log2_block];
+    const int off = t & (B - 1);
+    const int64_t dst = phys * blk_stride_v + head_off_v + static_cast<int64_t>(off) * LPT + e;
+    ap.key_cache[dst] = ap.key[i * ap.key_stride_v + kvh * LPT + e];
+    ap.value_cache[dst] = ap.value[i * ap.value_stride_v + kvh * LPT + e];
+    if (kvh == 0 && e == 0 && ap.slot_mapping) ap.slot_mapping[i] = phys * B + off;
+  }
+  __syncthreads();  // the rows written above are read by other waves below
+}
+
 // ---- matrix-core helpers (16-bit storage only) ---------------------------
 // Lane layouts (wave64, probed on gfx950):
 //   16x16x32: lane l holds A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]

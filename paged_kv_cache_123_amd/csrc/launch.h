@@ -7,6 +7,8 @@
 
 #include <cstdint>
 
+#include "decode_common.h"
+
 namespace pa {
 
 hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
@@ -42,6 +44,7 @@ struct DecodeArgs {
   float* ws_out;
   const int32_t* items;      // work list [num_items][2] = (seq, partition), or nullptr
   int64_t num_items;
+  dev::AppendArgs append;    // the step's cache writes (append.qsl == nullptr: none)
 };
 
 // Paged decode attention (single pass when partition_size == 0, else the

@@ -244,3 +244,47 @@ def probe_read_blocks(buffer: torch.Tensor, block_order: torch.Tensor, sink: tor
     _contig("block_order", block_order)
     check(lib().pa_probe_read_blocks(buffer.data_ptr(), block_order.data_ptr(),
                                      block_order.numel(), sink.data_ptr(), grid, _stream()))
+
+
+def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                value_cache: torch.Tensor, block_tables: torch.Tensor,
+                context_lens: torch.Tensor, scale: float, max_context_len: int,
+                partition_size: int, work_items: torch.Tensor, query_start_loc: torch.Tensor,
+                key: torch.Tensor, value: torch.Tensor, cow_src=None, slot_mapping=None,
+                workspace=None) -> None:
+    """The whole decode step in one launch: copy-on-write of the old slots of
+    fresh tail blocks (``cow_src`` int64 [num_seqs], -1 for none), the new
+    tokens' K/V (rows of ``key``/``value`` per ``query_start_loc``) into their
+    slots, and planned attention over the updated caches."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
+    _dev(work_items, query_start_loc, key, value)
+    if query_start_loc.dtype != torch.int32 or query_start_loc.numel() < S + 1:
+        raise ValueError("query_start_loc must be int32 [num_seqs + 1]")
+    for n, t in (("key", key), ("value", value)):
+        if t.dtype != key_cache.dtype or t.dim() != 3 or tuple(t.shape[1:]) != (hkv, D):
+            raise ValueError(f"{n} must be [num_tokens, num_kv_heads, head_size] in cache dtype")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{n} rows must be contiguous [num_kv_heads, head_size]")
+    cow_ptr = 0
+    if cow_src is not None:
+        _dev(cow_src)
+        if cow_src.dtype != torch.int64 or cow_src.numel() < S:
+            raise ValueError("cow_src must be int64 [num_seqs]")
+        cow_ptr = cow_src.data_ptr()
+    slot_ptr = 0
+    if slot_mapping is not None:
+        _dev(slot_mapping)
+        if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < key.shape[0]:
+            raise ValueError("slot_mapping must be int64 [num_tokens]")
+        slot_ptr = slot_mapping.data_ptr()
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().pa_decode_step(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
+        work_items.shape[0], ws_ptr or None, ws_bytes, query_start_loc.data_ptr(),
+        key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None,
+        slot_ptr or None, _stream()))

@@ -12,6 +12,8 @@ copy-on-write pairs.  Device side, in order on one stream:
                          from a host work plan (largest pieces first) unless
                          ``planned=False``
 
+or all four in one launch (``run(fused=True)``, pa_decode_step).
+
 ([VLLBC] paper sections 4.2 and 4.4 / Fig. 8; [PUFANYI] "按 Block 分配" and
 "共享前缀，分叉时 Copy-on-write"; [CSDN] section 2.3.)
 """
@@ -46,13 +48,14 @@ class DecodeStep:
                 self.pool.fork(op[1], op[2])
             else:
                 raise ValueError(f"unknown operation {op!r}")
-        seqs, positions, qsl, cow = [], [], [0], []
+        seqs, positions, qsl, cow, cow_src = [], [], [0], [], []
         for s, n in appends:
             start = self.pool.seq_len(s)
             _, pair = self.pool.append(s, n)
             seqs.append(s)
             positions.extend(range(start, start + n))
             qsl.append(qsl[-1] + n)
+            cow_src.append(-1 if pair is None else pair[0])
             if pair is not None:
                 cow.append(pair)
         self.seqs = seqs
@@ -62,6 +65,7 @@ class DecodeStep:
         self.tables_host = tables
         self.context_lens_host = lens
         self.cow_pairs_host = np.asarray(cow, dtype=np.int64).reshape(-1, 2)
+        self.cow_src_host = np.asarray(cow_src, dtype=np.int64)
         self.positions_host = np.asarray(positions, dtype=np.int64)
         self.query_start_loc_host = np.asarray(qsl, dtype=np.int32)
         self.num_tokens = int(qsl[-1])
@@ -78,6 +82,7 @@ class DecodeStep:
         self.block_tables = torch.from_numpy(tables).to(dev)
         self.context_lens = torch.from_numpy(lens).to(dev)
         self.cow_pairs = torch.from_numpy(self.cow_pairs_host).to(dev)
+        self.cow_src = torch.from_numpy(self.cow_src_host).to(dev)
         self.positions = torch.from_numpy(self.positions_host).to(dev)
         self.query_start_loc = torch.from_numpy(self.query_start_loc_host).to(dev)
         self.slot_mapping = torch.empty(self.num_tokens, dtype=torch.int64, device=dev)
@@ -121,8 +126,19 @@ class DecodeStep:
                                        self.block_tables, self.context_lens, self.scale,
                                        self.max_context_len)
 
-    def run(self):
-        """The whole step; returns ``out`` [num_seqs, num_heads, head_size]."""
+    def fused(self):
+        """The whole step as one launch (pa_decode_step)."""
+        ops.decode_step(self.out, self.query, self.key_cache, self.value_cache,
+                        self.block_tables, self.context_lens, self.scale, self.max_context_len,
+                        self.partition_size, self.plan, self.query_start_loc, self.new_key,
+                        self.new_value, self.cow_src, self.slot_mapping, self.workspace)
+
+    def run(self, fused: bool = False):
+        """The whole step; returns ``out`` [num_seqs, num_heads, head_size].
+        ``fused``: one launch instead of copy, slot mapping, scatter, attention."""
+        if fused:
+            self.fused()
+            return self.out
         self.copy_blocks()
         self.slot_mapping_kernel()
         self.scatter()

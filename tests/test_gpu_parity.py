@@ -356,3 +356,66 @@ def test_shared_prefix_identity_after_cow(decode_kernel):
     assert len(step.cow_pairs_host) == 7
     for r in range(1, 8):
         assert torch.equal(out[r].view(torch.int16), out[0].view(torch.int16))
+
+
+# ---- the fused step (one launch) --------------------------------------------
+
+def _dead_cow_slots(ora, w):
+    """(block, slot) pairs of copy-on-write destinations past the owner's
+    context: the fused step does not copy them and no one reads them."""
+    dead = []
+    B = w.block_size
+    for r, s in enumerate(ora.seqs):
+        L = int(ora.context_lens[r])
+        for src, dst in ora.cow_pairs:
+            if dst in ora.pool.block_table(s):
+                j = ora.pool.block_table(s).index(dst)
+                for off in range(B):
+                    if j * B + off >= L:
+                        dead.append((dst, off))
+    return dead
+
+
+FUSED_CASES = [
+    ("tiny", lambda: W.tiny_fp32(), None),
+    ("llama16", lambda: W.llama7b_fp16(num_seqs=16), None),
+    ("llama16_p256", lambda: W.llama7b_fp16(num_seqs=16), 256),
+    ("gqa32", lambda: W.qwen72b_gqa_bf16(num_seqs=32), None),
+    ("gqa32_p512", lambda: W.qwen72b_gqa_bf16(num_seqs=32), 512),
+    ("shared4", lambda: W.shared_prefix_bf16(num_groups=4), None),
+    ("shared4_p256", lambda: W.shared_prefix_bf16(num_groups=4), 256),
+    ("long2", lambda: W.long_context_bf16(num_seqs=2, context_len=5000), None),
+]
+
+
+@BOTH
+@pytest.mark.parametrize("name,make,part", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_step_matches_oracle_and_separate_calls(name, make, part, decode_kernel):
+    _require_gpu()
+    w = make()
+    print(f"[fused] {name} kernel={decode_kernel}", flush=True)
+    vals = W.make_values(w, DEV)
+    host = {k: to_host(v) for k, v in vals.items()}
+    ora = OracleStep(w)
+    # separate calls on a copy of the caches
+    sep_vals = {k: v.clone() for k, v in vals.items()}
+    sep = _step(w, sep_vals, part)
+    sep.run()
+    step = _step(w, vals, part)
+    step.slot_mapping.fill_(-7)
+    out = step.run(fused=True)
+    torch.cuda.synchronize()
+    assert to_host(step.slot_mapping).tolist() == ora.slot_mapping()
+    kc, vc = host["key_cache"], host["value_cache"]
+    ora.apply_copies(kc, vc)
+    ora.apply_scatter(kc, vc, host["new_key"], host["new_value"])
+    gk, gv = to_host(step.key_cache), to_host(step.value_cache)
+    for blk, off in _dead_cow_slots(ora, w):
+        gk[blk, :, off, :] = kc[blk, :, off, :]
+        gv[blk, :, off, :] = vc[blk, :, off, :]
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    want = ora.attention(host["query"], kc, vc)
+    check_attention(to_host(out), want, w.dtype, f"fused {name}")
+    # same arithmetic as the four separate calls: identical bits
+    assert torch.equal(out.view(torch.int16) if out.dtype != torch.float32 else out,
+                       sep.out.view(torch.int16) if out.dtype != torch.float32 else sep.out)
