@@ -419,3 +419,48 @@ def test_fused_step_matches_oracle_and_separate_calls(name, make, part, decode_k
     # same arithmetic as the four separate calls: identical bits
     assert torch.equal(out.view(torch.int16) if out.dtype != torch.float32 else out,
                        sep.out.view(torch.int16) if out.dtype != torch.float32 else sep.out)
+
+
+FORK_CASES = [
+    # dtype, D, B, G, partition, prompts, appends per sample (3 samples)
+    ("f32", 64, 4, 1, 16, [7, 13], [[1, 9, 4], [3, 1, 17]]),
+    ("bf16", 128, 4, 8, 16, [6, 30], [[5, 2, 1], [16, 3, 2]]),
+    ("f16", 128, 16, 2, 0, [17, 40], [[1, 33, 15], [64, 2, 7]]),
+    ("bf16", 128, 16, 1, 32, [31, 1], [[2, 40, 1], [1, 1, 48]]),
+    ("bf16", 64, 8, 4, 0, [12, 5], [[9, 1, 3], [4, 12, 1]]),
+]
+
+
+@BOTH
+@pytest.mark.parametrize("dtype,D,B,G,part,prompts,appends", FORK_CASES,
+                         ids=[f"{c[0]}-D{c[1]}-B{c[2]}-G{c[3]}-P{c[4]}" for c in FORK_CASES])
+def test_fused_step_multi_token_forks(dtype, D, B, G, part, prompts, appends, decode_kernel):
+    """Forks of partly filled prompts that append several tokens each: the
+    copy-on-write tail, block and partition boundaries inside one step."""
+    _require_gpu()
+    w = W.custom_forks("forks", 11, prompts, 3, appends, dtype=dtype, H=2 * G, Hkv=2, D=D, B=B,
+                       partition_size=part)
+    vals = W.make_values(w, DEV)
+    host = {k: to_host(v) for k, v in vals.items()}
+    ora = OracleStep(w)
+    assert len(ora.cow_pairs) > 0
+    sep_vals = {k: v.clone() for k, v in vals.items()}
+    sep = _step(w, sep_vals)
+    sep.run()
+    step = _step(w, vals)
+    out = step.run(fused=True)
+    torch.cuda.synchronize()
+    assert to_host(step.slot_mapping).tolist() == ora.slot_mapping()
+    assert to_host(sep.slot_mapping).tolist() == ora.slot_mapping()
+    kc, vc = host["key_cache"], host["value_cache"]
+    ora.apply_copies(kc, vc)
+    ora.apply_scatter(kc, vc, host["new_key"], host["new_value"])
+    assert np.array_equal(to_host(sep.key_cache), kc) and np.array_equal(to_host(sep.value_cache), vc)
+    gk, gv = to_host(step.key_cache), to_host(step.value_cache)
+    for blk, off in _dead_cow_slots(ora, w):
+        gk[blk, :, off, :] = kc[blk, :, off, :]
+        gv[blk, :, off, :] = vc[blk, :, off, :]
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    want = ora.attention(host["query"], kc, vc)
+    check_attention(to_host(out), want, w.dtype, "fused forks")
+    check_attention(to_host(sep.out), want, w.dtype, "separate forks")

@@ -101,6 +101,31 @@ def custom_decode(name, seed, lens, *, dtype, H, Hkv, D, B, num_blocks=None, sig
                          num_blocks=nb, sigma=sigma, partition_size=partition_size)
 
 
+def custom_forks(name, seed, prompts, samples, appends, *, dtype, H, Hkv, D, B,
+                 partition_size=0, sigma=1.0):
+    """Parallel-sampling batch for edge-case tests: prompt g is prefilled once
+    and forked into ``samples`` sequences; sample j of group g then appends
+    appends[g][j] tokens (several tokens per sample, across block and
+    partition boundaries)."""
+    rng = np.random.default_rng(seed)
+    prefill, step, seqs, lens = [], [], [], []
+    for g, P in enumerate(prompts):
+        lead = g * samples
+        prefill += [("add", lead), ("append", lead, int(P))]
+        for j in range(1, samples):
+            prefill.append(("fork", lead, lead + j))
+        for j in range(samples):
+            step.append((lead + j, int(appends[g][j])))
+            seqs.append(lead + j)
+            lens.append(int(P) + int(appends[g][j]))
+    nb = _blocks_for(prompts, B) + sum(-(-int(a) // B) + 1 for row in appends for a in row) + 4
+    order = rng.permutation(nb).astype(np.int32)
+    return Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                    block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(D), sigma=sigma,
+                    seed=seed, free_order=order, seqs=seqs, prefill=prefill, step=step,
+                    context_lens=lens, partition_size=partition_size)
+
+
 def _blocks_for(lens, B) -> int:
     """Pool sizing only: blocks that sequences of these lengths occupy."""
     return int(sum(-(-int(L) // B) for L in lens))
