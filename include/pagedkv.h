@@ -205,6 +205,13 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
  * kernels (same rules and workspace as pa_paged_attention_decode_split); the
  * list must name every non-empty partition once.  Items missing from the
  * list leave their outputs undefined (no out-of-bounds access).
+ * shared_prefix_blocks (device int32 [num_seqs], may be NULL): how many
+ * leading blocks of each sequence's table other sequences also read (forks
+ * of one prompt, [VLLBC] paper section 4.4).  K/V rows of those blocks are
+ * loaded through the caches so that the sharers reuse them; all other rows
+ * are read once and are loaded as non-temporal streams.  A cache hint only:
+ * results do not depend on it.  NULL = nothing shared.  The unplanned calls
+ * above stream every row.
  * ---------------------------------------------------------------------- */
 int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
                        int32_t* items, int64_t capacity, int64_t* num_items);
@@ -217,7 +224,8 @@ int32_t pa_paged_attention_decode_planned(void* out, const void* query, const vo
                                           int32_t block_size, int32_t max_context_len,
                                           float scale, int32_t dtype, int32_t partition_size,
                                           const int32_t* work_items, int64_t num_work_items,
-                                          void* workspace, size_t workspace_bytes, void* stream);
+                                          const int32_t* shared_prefix_blocks, void* workspace,
+                                          size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * One decode step in one launch (plus the reduce when partition_size > 0).
@@ -247,7 +255,8 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                        int32_t max_context_len, float scale, int32_t dtype,
                        int32_t partition_size, const int32_t* work_items, int64_t num_work_items,
-                       void* workspace, size_t workspace_bytes, const int32_t* query_start_loc,
+                       const int32_t* shared_prefix_blocks, void* workspace,
+                       size_t workspace_bytes, const int32_t* query_start_loc,
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
                        void* stream);
@@ -301,6 +310,11 @@ int32_t pa_pool_seq_num_blocks(const pa_pool* pool, int64_t seq, int32_t* n_out)
  * blocks or is unknown. */
 int32_t pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t num_seqs,
                              int32_t* out, int32_t width, int32_t* context_lens_out);
+/* For each of num_seqs sequences, the number of leading blocks of its table
+ * whose reference count is above 1 (blocks other sequences share), into
+ * host int32 out[num_seqs].  PA_EINVAL for an unknown sequence. */
+int32_t pa_pool_shared_prefix_blocks(const pa_pool* pool, const int64_t* seqs, int32_t num_seqs,
+                                     int32_t* out);
 /* Number of free blocks; reference count of one block (-1 if out of range). */
 int32_t pa_pool_num_free(const pa_pool* pool);
 int32_t pa_pool_ref(const pa_pool* pool, int32_t block);
@@ -313,7 +327,8 @@ int64_t pa_pool_num_cow(const pa_pool* pool);
 /* ------------------------------------------------------------------------
  * Diagnostic (not part of the decode path): reads num_blocks whole 4 KiB
  * blocks of buffer, block block_order[i] for i = 0..num_blocks-1, with `grid`
- * workgroups of 256 lanes x 16 bytes.  A reference of achievable read
+ * workgroups of 256 lanes x 16 bytes, as non-temporal loads when
+ * non_temporal != 0.  A reference of achievable read
  * bandwidth for a given block order, and a kernel of known byte count for
  * calibrating hardware counters.
  *   buffer       device, 16-byte aligned, >= 4096 * (max(block_order) + 1) bytes
@@ -322,7 +337,7 @@ int64_t pa_pool_num_cow(const pa_pool* pool);
  * Errors: PA_EINVAL for null pointers, num_blocks < 1, grid < 1, alignment.
  * ---------------------------------------------------------------------- */
 int32_t pa_probe_read_blocks(const void* buffer, const int32_t* block_order, int64_t num_blocks,
-                             void* sink, int32_t grid, void* stream);
+                             void* sink, int32_t grid, int32_t non_temporal, void* stream);
 
 #ifdef __cplusplus
 }

@@ -41,11 +41,11 @@ SIGNATURES = {
     "pa_decode_plan": (_i32, [_pi32, _i32, _i32, _pi32, _i64, _pi64]),
     "pa_paged_attention_decode_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
-                                                 _i64, _vp, _sz, _vp]),
-    "pa_probe_read_blocks": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp]),
+                                                 _i64, _vp, _vp, _sz, _vp]),
+    "pa_probe_read_blocks": (_i32, [_vp, _vp, _i64, _vp, _i32, _i32, _vp]),
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
-                              _i32, _f32, _i32, _i32, _vp, _i64, _vp, _sz, _vp, _vp, _vp, _i64,
-                              _i64, _vp, _vp, _vp]),
+                              _i32, _f32, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp,
+                              _i64, _i64, _vp, _vp, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _pi32, _c.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_add_seq": (_i32, [_vp, _i64]),
@@ -55,6 +55,7 @@ SIGNATURES = {
     "pa_pool_seq_len": (_i32, [_vp, _i64, _pi64]),
     "pa_pool_seq_num_blocks": (_i32, [_vp, _i64, _pi32]),
     "pa_pool_block_tables": (_i32, [_vp, _pi64, _i32, _pi32, _i32, _pi32]),
+    "pa_pool_shared_prefix_blocks": (_i32, [_vp, _pi64, _i32, _pi32]),
     "pa_pool_num_free": (_i32, [_vp]),
     "pa_pool_ref": (_i32, [_vp, _i32]),
     "pa_pool_free_queue": (_i32, [_vp, _pi32, _i32]),

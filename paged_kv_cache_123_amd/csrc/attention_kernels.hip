@@ -50,7 +50,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,
     int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
-    float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap) {
+    float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
+    const int32_t* __restrict__ shared_blocks) {
   using S = St<DT>;
   constexpr int VEC = S::VEC;
   constexpr int LPT = D / VEC;    // lanes per token
@@ -76,6 +77,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * LPT;
   const int64_t head_off_v = static_cast<int64_t>(kvh) * B * LPT + sub;
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
+  // tokens of the leading blocks other sequences share (cached loads)
+  const int shared_tokens = shared_blocks ? (shared_blocks[s] << log2_block) : 0;
   if (ap.qsl)
     apply_appends<LPT, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
                                   static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * LPT,
@@ -122,11 +125,20 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
     auto load_tile = [&](int it, uint4 (&kd)[U], uint4 (&vd)[U]) {
       const int t0 = c0 + (wave + it * NW) * kTile;
+      if (t0 >= shared_tokens) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t idx = vec_index(t0 + u * TPL + lg);
-        kd[u] = kc[idx];
-        vd[u] = vc[idx];
+        for (int u = 0; u < U; ++u) {
+          const int64_t idx = vec_index(t0 + u * TPL + lg);
+          kd[u] = load_stream(kc + idx);
+          vd[u] = load_stream(vc + idx);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t idx = vec_index(t0 + u * TPL + lg);
+          kd[u] = load_cached(kc + idx);
+          vd[u] = load_cached(vc + idx);
+        }
       }
     };
     auto consume = [&](int it, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
@@ -248,12 +260,19 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 }
 
 // Merge of the partitions of one (sequence, head): M = max m_p,
-// a_p = l_p exp(m_p - M), out = sum a_p o_p / sum a_p, in partition order.
+// a_p = l_p exp(m_p - M), out = sum a_p o_p / sum a_p, summed in partition
+// order.  One thread per output dimension; the partition weights are computed
+// once per chunk into LDS, and the o_p loads are unrolled so that eight of
+// them are in flight per thread.
 template <int DT, int D>
 __global__ __launch_bounds__(D) void split_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t num_heads,
     int32_t partition_size, int32_t num_partitions, const float* __restrict__ ws_max,
     const float* __restrict__ ws_sum, const float* __restrict__ ws_out) {
+  constexpr int kChunk = 256;
+  constexpr int NWV = D / 64;
+  __shared__ float sw[kChunk];
+  __shared__ float red[NWV];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
@@ -263,20 +282,41 @@ __global__ __launch_bounds__(D) void split_reduce_kernel(
   const float* mrow = ws_max + row * num_partitions;
   const float* lrow = ws_sum + row * num_partitions;
   const float* orow = ws_out + row * num_partitions * D;
-  float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, mrow[i]);
-  float wsum = 0.0f, a = 0.0f;
-  for (int i = 0; i < np; ++i) {
-    const float w = lrow[i] * __builtin_amdgcn_exp2f((mrow[i] - M) * kLog2e);
-    wsum += w;
-    a = fmaf(w, orow[static_cast<int64_t>(i) * D + d], a);
+
+  float mx = -INFINITY;
+  for (int i = d; i < np; i += D) mx = fmaxf(mx, mrow[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[w]);
+
+  float a = 0.0f, wsum = 0.0f;
+  for (int c0 = 0; c0 < np; c0 += kChunk) {
+    const int cn = min(kChunk, np - c0);
+    __syncthreads();  // sw is rewritten
+    for (int i = d; i < cn; i += D)
+      sw[i] = lrow[c0 + i] * __builtin_amdgcn_exp2f((mrow[c0 + i] - M) * kLog2e);
+    __syncthreads();
+    const float* o = orow + static_cast<int64_t>(c0) * D + d;
+    int i = 0;
+    for (; i + 8 <= cn; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = o[static_cast<int64_t>(i + k) * D];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a = fmaf(sw[i + k], v[k], a);
+    }
+    for (; i < cn; ++i) a = fmaf(sw[i], o[static_cast<int64_t>(i) * D], a);
+    for (int k = 0; k < cn; ++k) wsum += sw[k];
   }
   St<DT>::store(out, row * D + d, a / wsum);
 }
 
-template <int DT, int D, int G, bool FINAL>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = PA_VALU_WAVES;
+template <int DT, int D, int G, bool FINAL, int NW>
+hipError_t launch_decode_nw(const DecodeArgs& a, hipStream_t stream) {
   int log2_block = 0;
   while ((1 << log2_block) < a.block_size) ++log2_block;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))
@@ -285,8 +325,15 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                      a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
                      a.context_lens, a.num_heads, a.num_kv_heads, log2_block, a.partition_size,
                      a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum, a.ws_out,
-                     reinterpret_cast<const int2*>(a.items), a.append);
+                     reinterpret_cast<const int2*>(a.items), a.append,
+                     a.shared_blocks);
   return hipGetLastError();
+}
+
+template <int DT, int D, int G, bool FINAL>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  return a.shared_blocks ? launch_decode_nw<DT, D, G, FINAL, PA_VALU_WAVES_SHARED>(a, stream)
+                         : launch_decode_nw<DT, D, G, FINAL, PA_VALU_WAVES>(a, stream);
 }
 
 template <int DT, int D, bool FINAL>

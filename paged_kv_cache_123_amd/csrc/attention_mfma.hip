@@ -52,7 +52,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,
     int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
-    float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap) {
+    float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
+    const int32_t* __restrict__ shared_blocks) {
   constexpr int D = 128;
   constexpr int DV = D / 8;   // 16-byte vectors per token row
   constexpr int NK = D / 32;  // score MFMAs per tile
@@ -78,6 +79,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
   const int64_t head_off_v = static_cast<int64_t>(kvh) * B * DV;
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
+  // tokens of the leading blocks other sequences share (cached loads)
+  const int shared_tokens = shared_blocks ? (shared_blocks[s] << log2_block) : 0;
   if (ap.qsl)
     apply_appends<DV, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
                                   static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * DV,
@@ -122,10 +125,17 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
     auto load_tile = [&](int it, uint4 (&kd)[NK], uint4 (&vd)[U]) {
       const int t0 = c0 + (wave + it * NW) * kTile;
+      if (t0 >= shared_tokens) {
 #pragma unroll
-      for (int k = 0; k < NK; ++k) kd[k] = kc[vec_index(t0 + k_tok, k * 4 + grp)];
+        for (int k = 0; k < NK; ++k) kd[k] = load_stream(kc + vec_index(t0 + k_tok, k * 4 + grp));
 #pragma unroll
-      for (int u = 0; u < U; ++u) vd[u] = vc[vec_index(t0 + grp + 4 * u, col)];
+        for (int u = 0; u < U; ++u) vd[u] = load_stream(vc + vec_index(t0 + grp + 4 * u, col));
+      } else {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) kd[k] = load_cached(kc + vec_index(t0 + k_tok, k * 4 + grp));
+#pragma unroll
+        for (int u = 0; u < U; ++u) vd[u] = load_cached(vc + vec_index(t0 + grp + 4 * u, col));
+      }
     };
     auto consume = [&](int it, const uint4 (&kr)[NK], const uint4 (&vr)[U]) {
       const int t0 = c0 + (wave + it * NW) * kTile;
@@ -241,7 +251,8 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
                      stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
                      a.partition_size, a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum,
-                     a.ws_out, reinterpret_cast<const int2*>(a.items), a.append);
+                     a.ws_out, reinterpret_cast<const int2*>(a.items), a.append,
+                     a.shared_blocks);
   return hipGetLastError();
 }
 

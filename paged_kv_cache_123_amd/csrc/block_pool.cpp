@@ -197,6 +197,24 @@ int32_t pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t n
   return PA_OK;
 }
 
+int32_t pa_pool_shared_prefix_blocks(const pa_pool* pool, const int64_t* seqs, int32_t num_seqs,
+                                     int32_t* out) {
+  if (!pool || !seqs || !out || num_seqs < 0)
+    return pa::fail(PA_EINVAL, "pa_pool_shared_prefix_blocks: bad argument");
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    auto it = pool->seqs.find(seqs[r]);
+    if (it == pool->seqs.end())
+      return pa::fail(PA_EINVAL, "pa_pool_shared_prefix_blocks: unknown sequence");
+    int32_t n = 0;
+    for (int32_t b : it->second.blocks) {
+      if (pool->ref[b] <= 1) break;
+      ++n;
+    }
+    out[r] = n;
+  }
+  return PA_OK;
+}
+
 int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->num_free : -1; }
 
 int32_t pa_pool_ref(const pa_pool* pool, int32_t block) {

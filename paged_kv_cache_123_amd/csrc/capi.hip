@@ -209,8 +209,8 @@ int32_t pa_paged_attention_decode_planned(
     const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
     int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
-    int32_t partition_size, const int32_t* work_items, int64_t num_work_items, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    int32_t partition_size, const int32_t* work_items, int64_t num_work_items,
+    const int32_t* shared_prefix_blocks, void* workspace, size_t workspace_bytes, void* stream) {
   const char* who = "pa_paged_attention_decode_planned";
   int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
                             context_lens, num_seqs, num_heads, num_kv_heads, head_size,
@@ -224,6 +224,7 @@ int32_t pa_paged_attention_decode_planned(
     pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
                      num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale,
                      dtype, nullptr, nullptr, nullptr, work_items, num_work_items};
+    a.shared_blocks = shared_prefix_blocks;
     return launched(pa::launch_decode(a, s), who);
   }
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
@@ -245,6 +246,7 @@ int32_t pa_paged_attention_decode_planned(
                    reinterpret_cast<float*>(ws + align256(rows * sizeof(float))),
                    reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float))),
                    work_items, num_work_items};
+  a.shared_blocks = shared_prefix_blocks;
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_planned (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_planned (reduce)");
@@ -256,7 +258,8 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                        int32_t max_context_len, float scale, int32_t dtype,
                        int32_t partition_size, const int32_t* work_items, int64_t num_work_items,
-                       void* workspace, size_t workspace_bytes, const int32_t* query_start_loc,
+                       const int32_t* shared_prefix_blocks, void* workspace,
+                       size_t workspace_bytes, const int32_t* query_start_loc,
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
                        void* stream) {
@@ -284,6 +287,7 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                                  static_cast<const uint4*>(value), key_stride * eb / 16,
                                  value_stride * eb / 16, static_cast<uint4*>(key_cache),
                                  static_cast<uint4*>(value_cache), slot_mapping};
+  a.shared_blocks = shared_prefix_blocks;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||

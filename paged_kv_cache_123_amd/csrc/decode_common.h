@@ -13,19 +13,45 @@ namespace pa {
 namespace dev {
 
 // Tuning constants (overridable at build time with -D):
-//   PA_PREFETCH     tiles each wave keeps in flight ahead of the one it consumes
-//   PA_VALU_WAVES   waves per workgroup of the vector kernel
-//   PA_MFMA_WAVES   waves per workgroup of the matrix-core kernel
+//   PA_PREFETCH            tiles each wave keeps in flight ahead of the one it consumes
+//   PA_VALU_WAVES          waves per workgroup of the vector kernel
+//   PA_VALU_WAVES_SHARED   the same when the launch has shared prefix blocks
+//                          (fewer, more numerous workgroups keep the sharers of a
+//                          block in flight together, so they hit in the caches)
+//   PA_MFMA_WAVES          waves per workgroup of the matrix-core kernel
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 1
 #endif
 #ifndef PA_VALU_WAVES
-#define PA_VALU_WAVES 4
+#define PA_VALU_WAVES 8
+#endif
+#ifndef PA_VALU_WAVES_SHARED
+#define PA_VALU_WAVES_SHARED 4
 #endif
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
 #endif
+#ifndef PA_STREAM_LOADS
+#define PA_STREAM_LOADS 1
+#endif
 constexpr int kPrefetch = PA_PREFETCH;
+
+// 16-byte K/V loads.  Rows read once per launch go through load_stream, which
+// marks them non-temporal so they do not displace reusable lines from L2 and
+// the Infinity Cache; rows of blocks shared by several sequences (read by
+// several workgroups) use load_cached.  PA_STREAM_LOADS=0 makes both plain.
+__device__ __forceinline__ uint4 load_cached(const uint4* p) { return *p; }
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+#if PA_STREAM_LOADS
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
 constexpr int kTile = 16;          // tokens per tile
 constexpr int kChunkTokens = 2048;  // tokens whose table entries are staged at once
 constexpr float kLog2e = 1.4426950408889634f;

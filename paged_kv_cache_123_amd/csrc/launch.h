@@ -45,6 +45,7 @@ struct DecodeArgs {
   const int32_t* items;      // work list [num_items][2] = (seq, partition), or nullptr
   int64_t num_items;
   dev::AppendArgs append;    // the step's cache writes (append.qsl == nullptr: none)
+  const int32_t* shared_blocks;  // [S] leading blocks shared with other sequences, or nullptr
 };
 
 // Paged decode attention (single pass when partition_size == 0, else the

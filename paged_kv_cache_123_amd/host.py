@@ -88,6 +88,13 @@ class Pool:
         t, _ = self.block_tables([seq], max(n, 1))
         return [int(b) for b in t[0, :n]]
 
+    def shared_prefix_blocks(self, seqs) -> np.ndarray:
+        """int32 [len(seqs)]: leading blocks of each table with reference count > 1."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        out = np.empty(ids.size, dtype=np.int32)
+        check(lib().pa_pool_shared_prefix_blocks(self._h, _p64(ids), ids.size, _p32(out)))
+        return out
+
     def num_free(self) -> int:
         return int(lib().pa_pool_num_free(self._h))
 

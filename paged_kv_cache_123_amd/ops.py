@@ -199,6 +199,15 @@ def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head
     return mx, sm, to.view(num_seqs, num_heads, np_, head_size)
 
 
+def _shared_ptr(shared_prefix_blocks, S):
+    if shared_prefix_blocks is None:
+        return None
+    _dev(shared_prefix_blocks)
+    if shared_prefix_blocks.dtype != torch.int32 or shared_prefix_blocks.numel() < S:
+        raise ValueError("shared_prefix_blocks must be int32 [num_seqs]")
+    return shared_prefix_blocks.data_ptr()
+
+
 def decode_plan(context_lens, partition_size: int) -> np.ndarray:
     """Host work plan: int32 [num_items, 2] of (sequence, partition), every
     non-empty item once, largest first (partition_size 0: one per sequence)."""
@@ -217,8 +226,10 @@ def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
                                    key_cache: torch.Tensor, value_cache: torch.Tensor,
                                    block_tables: torch.Tensor, context_lens: torch.Tensor,
                                    scale: float, max_context_len: int, partition_size: int,
-                                   work_items: torch.Tensor, workspace=None) -> None:
-    """Attention driven by a work plan (device int32 [num_items, 2])."""
+                                   work_items: torch.Tensor, workspace=None,
+                                   shared_prefix_blocks=None) -> None:
+    """Attention driven by a work plan (device int32 [num_items, 2]).
+    ``shared_prefix_blocks``: optional device int32 [num_seqs] cache hint."""
     S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
     _dev(work_items)
     if work_items.dtype != torch.int32 or work_items.dim() != 2 or work_items.shape[1] != 2:
@@ -232,18 +243,20 @@ def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
-        work_items.shape[0], ws_ptr or None, ws_bytes, _stream()))
+        work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
+        _stream()))
 
 
 def probe_read_blocks(buffer: torch.Tensor, block_order: torch.Tensor, sink: torch.Tensor,
-                      grid: int = 16384) -> None:
+                      grid: int = 16384, non_temporal: bool = False) -> None:
     """Diagnostic: read ``buffer`` as whole 4 KiB blocks in ``block_order``."""
     _dev(buffer, block_order, sink)
     if block_order.dtype != torch.int32:
         raise TypeError("block_order must be int32")
     _contig("block_order", block_order)
     check(lib().pa_probe_read_blocks(buffer.data_ptr(), block_order.data_ptr(),
-                                     block_order.numel(), sink.data_ptr(), grid, _stream()))
+                                     block_order.numel(), sink.data_ptr(), grid,
+                                     int(non_temporal), _stream()))
 
 
 def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
@@ -251,7 +264,7 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                 context_lens: torch.Tensor, scale: float, max_context_len: int,
                 partition_size: int, work_items: torch.Tensor, query_start_loc: torch.Tensor,
                 key: torch.Tensor, value: torch.Tensor, cow_src=None, slot_mapping=None,
-                workspace=None) -> None:
+                workspace=None, shared_prefix_blocks=None) -> None:
     """The whole decode step in one launch: copy-on-write of the old slots of
     fresh tail blocks (``cow_src`` int64 [num_seqs], -1 for none), the new
     tokens' K/V (rows of ``key``/``value`` per ``query_start_loc``) into their
@@ -285,6 +298,7 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
-        work_items.shape[0], ws_ptr or None, ws_bytes, query_start_loc.data_ptr(),
+        work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
+        query_start_loc.data_ptr(),
         key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None,
         slot_ptr or None, _stream()))

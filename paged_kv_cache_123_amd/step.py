@@ -66,6 +66,7 @@ class DecodeStep:
         self.context_lens_host = lens
         self.cow_pairs_host = np.asarray(cow, dtype=np.int64).reshape(-1, 2)
         self.cow_src_host = np.asarray(cow_src, dtype=np.int64)
+        self.shared_blocks_host = self.pool.shared_prefix_blocks(seqs)
         self.positions_host = np.asarray(positions, dtype=np.int64)
         self.query_start_loc_host = np.asarray(qsl, dtype=np.int32)
         self.num_tokens = int(qsl[-1])
@@ -83,6 +84,8 @@ class DecodeStep:
         self.context_lens = torch.from_numpy(lens).to(dev)
         self.cow_pairs = torch.from_numpy(self.cow_pairs_host).to(dev)
         self.cow_src = torch.from_numpy(self.cow_src_host).to(dev)
+        self.shared_blocks = (torch.from_numpy(self.shared_blocks_host).to(dev)
+                              if self.shared_blocks_host.any() else None)
         self.positions = torch.from_numpy(self.positions_host).to(dev)
         self.query_start_loc = torch.from_numpy(self.query_start_loc_host).to(dev)
         self.slot_mapping = torch.empty(self.num_tokens, dtype=torch.int64, device=dev)
@@ -114,7 +117,7 @@ class DecodeStep:
                                                self.value_cache, self.block_tables,
                                                self.context_lens, self.scale,
                                                self.max_context_len, self.partition_size,
-                                               self.plan, self.workspace)
+                                               self.plan, self.workspace, self.shared_blocks)
         elif self.partition_size:
             ops.paged_attention_decode_split(self.out, self.query, self.key_cache,
                                              self.value_cache, self.block_tables,
@@ -131,7 +134,8 @@ class DecodeStep:
         ops.decode_step(self.out, self.query, self.key_cache, self.value_cache,
                         self.block_tables, self.context_lens, self.scale, self.max_context_len,
                         self.partition_size, self.plan, self.query_start_loc, self.new_key,
-                        self.new_value, self.cow_src, self.slot_mapping, self.workspace)
+                        self.new_value, self.cow_src, self.slot_mapping, self.workspace,
+                        self.shared_blocks)
 
     def run(self, fused: bool = False):
         """The whole step; returns ``out`` [num_seqs, num_heads, head_size].

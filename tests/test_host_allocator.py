@@ -149,6 +149,16 @@ def _replay(seed):
             assert ([cow] if cow else []) == want_cow
         assert lib_pool.free_queue() == list(ora.free)
         assert [lib_pool.ref(b) for b in range(nb)] == ora.ref
+        if live:
+            want = []
+            for s in live:
+                n = 0
+                for b in ora.block_table(s):
+                    if ora.ref[b] <= 1:
+                        break
+                    n += 1
+                want.append(n)
+            assert lib_pool.shared_prefix_blocks(live).tolist() == want
         for s in live:
             assert lib_pool.block_table(s) == ora.block_table(s)
             assert lib_pool.seq_len(s) == ora.seq_len(s)
