@@ -211,8 +211,9 @@ def main():
                     help="only run kernels of known byte count (for rocprofv3 --pmc scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the paged-KV path here runs on a single GPU "
+              "(sharding across GPUs is a design note, not code); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

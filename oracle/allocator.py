@@ -22,7 +22,7 @@ What it follows:
     block whose count reaches zero is appended to the tail of the free queue.
   * [CSDN] §3.2.3 (touch): sharing increments the count of every shared block.
 
-Readings where the pages are silent or disagree (listed in the design doc):
+Readings where the pages are silent or disagree:
   * The free queue is a FIFO seeded with an explicit initial order, freed
     blocks go to its tail, and there is no reserved null block ([CSDN] §2.4
     reserves block 0, [PUFANYI] uses P0 as an ordinary block; [VLLBC]'s V1

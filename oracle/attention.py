@@ -14,7 +14,7 @@ What it follows:
   * [DEEPSONAR] §2.1: grouped-query attention, where 64 query heads share
     8 KV heads.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   * The decode step scores the one new query vector of each (sequence, query
     head) against the keys of all context_len cached tokens with
     x_t = scale * <q, k_t>, applies a softmax over t and returns

@@ -11,7 +11,7 @@ What it follows:
     tokens of request r being those between query_start_loc[r] and
     query_start_loc[r + 1].
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   * The padding id the kernel writes for unused entries is -1 (the page names
     a PAD_ID constant but not its value), and entries from the number of
     scheduled tokens up to the buffer length are filled with it.
