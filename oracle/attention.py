@@ -27,6 +27,12 @@ Readings where the pages are silent:
     a_p = l_p exp(m_p - M) and returns sum a_p o_p / sum a_p.  Only the
     ceil(L / P) non-empty partitions exist.
 
+  * Several new tokens per sequence (chunked prefill, speculative drafts):
+    the query tokens of sequence s are rows query_start_loc[s] ..
+    query_start_loc[s+1]-1, the last n_s of its L_s tokens; query token i
+    (position L_s - n_s + i) scores the keys at positions 0 .. L_s - n_s + i
+    (causal over the new tokens, the whole cached context before them).
+
 Pinned by tests/test_oracle_attention.py: brute force against a dense
 softmax attention built from scipy.special.softmax on contiguous K/V, closed
 forms (one token -> its value; equal keys or scale 0 -> mean of V), invariance
@@ -154,3 +160,40 @@ def paged_attention_split(query, key_cache, value_cache, block_tables, context_l
                 partials[(s, h)] = (m, l, o)
                 out[s, h] = merge_partials(m, l, o)
     return out, partials
+
+
+def visible_tokens(L: int, n: int, i: int) -> int:
+    """Keys seen by new token i of n in a context of L tokens: positions
+    0 .. L - n + i, i.e. the cached context and the new tokens up to itself."""
+    return L - n + i + 1
+
+
+def paged_attention_multi(query, key_cache, value_cache, block_tables, context_lens,
+                          query_start_loc, scale: float, dtype: str) -> np.ndarray:
+    """Attention of every new token of every sequence, causal over the new
+    tokens ([CSDN] section 2.3 lays out a step's tokens by query_start_loc;
+    [DEEPSONAR] section 2.5 schedules prefill chunks and speculative tokens
+    the same way as decode tokens).
+
+    query: raw [T, H, D]; returns float64 [T, H, D]."""
+    T, H, D = query.shape
+    H_kv, B = key_cache.shape[1], key_cache.shape[2]
+    G = H // H_kv
+    sc = widen_scale(scale)
+    out = np.zeros((T, H, D), dtype=np.float64)
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        q0, q1 = int(query_start_loc[s]), int(query_start_loc[s + 1])
+        n = q1 - q0
+        if n > L:
+            raise ValueError("more new tokens than the context holds")
+        for g in range(H_kv):
+            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B), dtype)
+            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B), dtype)
+            for i in range(n):
+                visible = visible_tokens(L, n, i)
+                for h in range(H):
+                    if kv_head_of(h, G) == g:
+                        out[q0 + i, h] = attend(decode(query[q0 + i, h], dtype), K[:visible],
+                                                V[:visible], sc)
+    return out

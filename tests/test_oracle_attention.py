@@ -220,3 +220,72 @@ def test_storage_decode_reaches_attention():
         want = paged_attention(decode(enc(q32), dt), decode(enc(kc32), dt),
                                decode(enc(vc32), dt), bt, [6], 0.3, "f64")
         assert np.array_equal(got, want)
+
+
+# ---- several new tokens per sequence (causal over the new tokens) ----------
+
+from oracle.attention import paged_attention_multi  # noqa: E402
+
+
+def _dense_causal(qrows, Klog, Vlog, scale, G, lens, qsl):
+    """Dense reference: scipy softmax over the keys of a boolean causal mask."""
+    T, H, D = qrows.shape
+    out = np.zeros((T, H, D))
+    for s, L in enumerate(lens):
+        n = qsl[s + 1] - qsl[s]
+        pos = np.arange(L)
+        for i in range(n):
+            me = L - n + i
+            mask = pos <= me
+            for h in range(H):
+                g = h // G
+                x = scale * (Klog[s][g] @ qrows[qsl[s] + i, h])
+                p = softmax(np.where(mask, x, -np.inf))
+                out[qsl[s] + i, h] = p @ Vlog[s][g]
+    return out
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_multi_query_equals_dense_causal_softmax(G):
+    rng = np.random.default_rng(40 + G)
+    B, hkv, D = 4, 2, 8
+    lens = [1, 3, 6, 9, 13]
+    nq = [1, 3, 2, 5, 4]
+    qsl = np.concatenate([[0], np.cumsum(nq)])
+    _, kc, vc, bt, Klog, Vlog = _random_case(rng, len(lens), hkv * G, hkv, D, B, lens)
+    q = rng.standard_normal((int(qsl[-1]), hkv * G, D))
+    got = paged_attention_multi(q, kc, vc, bt, lens, qsl, 0.41, "f64")
+    want = _dense_causal(q, Klog, Vlog, float(np.float32(0.41)), G, lens, qsl)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_multi_query_last_token_is_the_decode_result():
+    rng = np.random.default_rng(5)
+    lens, nq = [7, 12, 4], [3, 1, 4]
+    qsl = np.concatenate([[0], np.cumsum(nq)])
+    _, kc, vc, bt, _, _ = _random_case(rng, 3, 4, 2, 8, 4, lens)
+    q = rng.standard_normal((int(qsl[-1]), 4, 8))
+    multi = paged_attention_multi(q, kc, vc, bt, lens, qsl, 0.3, "f64")
+    last = q[qsl[1:] - 1]
+    single = paged_attention(last, kc, vc, bt, lens, 0.3, "f64")
+    assert np.array_equal(multi[qsl[1:] - 1], single)
+
+
+def test_multi_query_prefill_from_empty_context():
+    """All L tokens are new: token 0 sees only itself, so its output is v0
+    exactly; token i sees tokens 0..i."""
+    rng = np.random.default_rng(6)
+    L = 6
+    _, kc, vc, bt, Klog, Vlog = _random_case(rng, 1, 1, 1, 4, 2, [L])
+    q = rng.standard_normal((L, 1, 4))
+    out = paged_attention_multi(q, kc, vc, bt, [L], [0, L], 0.5, "f64")
+    assert np.array_equal(out[0, 0], Vlog[0][0][0])
+    for i in range(L):
+        p = softmax(float(np.float32(0.5)) * (Klog[0][0][: i + 1] @ q[i, 0]))
+        np.testing.assert_allclose(out[i, 0], p @ Vlog[0][0][: i + 1], rtol=0, atol=1e-13)
+
+
+def test_multi_query_rejects_more_queries_than_context():
+    with pytest.raises(ValueError):
+        paged_attention_multi(np.zeros((3, 1, 2)), np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 4, 2)),
+                              np.array([[0]]), [2], [0, 3], 1.0, "f64")

@@ -148,6 +148,8 @@ MUTATIONS = [
     ("GQA head map h mod G", attn_mod, "kv_head_of", lambda h, g: h % g, TT),
     ("merge exponent sign flipped", attn_mod, "merge_partials", _merge_wrong_sign, TT),
     ("merge ignores partition mass", attn_mod, "merge_partials", _merge_ignores_mass, TT),
+    ("causal bound off by one", attn_mod, "visible_tokens", lambda L, n, i: L - n + i, TT),
+    ("causal bound ignores the position", attn_mod, "visible_tokens", lambda L, n, i: L, TT),
     ("slot block/offset transposed", slots_mod, "slot_of", _slot_transposed, TS),
     ("free returns blocks to the queue head", alloc_mod, "OraclePool", _PoolFreeToHead, TA),
     ("COW keeps the old reference", alloc_mod, "OraclePool", _PoolCowKeepsRef, TA),
