@@ -40,13 +40,15 @@ def attention_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def attention_bytes(w, context_lens) -> int:
+def attention_bytes(w, context_lens, query_rows=None) -> int:
     """Algorithmic bytes of one attention launch: every cached K and V row of
-    every (sequence, KV head) once, q in, out back, the table entries and the
+    every (sequence, KV head) once, q in, out back (one row per sequence, or
+    ``query_rows`` when every new token is a query), the table entries and the
     context lengths."""
     e = w.elem_bytes
     kv = int(sum(context_lens)) * 2 * w.num_kv_heads * w.head_size * e
-    qo = 2 * w.num_seqs * w.num_heads * w.head_size * e
+    rows = w.num_seqs if query_rows is None else query_rows
+    qo = 2 * rows * w.num_heads * w.head_size * e
     tables = 4 * int(sum(-(-int(L) // w.block_size) for L in context_lens))
     return kv + qo + tables + 4 * w.num_seqs
 
@@ -59,8 +61,12 @@ def step_bytes(w, step) -> int:
     T = step.num_tokens
     row = w.num_kv_heads * w.head_size * e
     blk = w.num_kv_heads * w.block_size * w.head_size * e
-    return (attention_bytes(w, step.context_lens_host) + 20 * T + 4 * row * T
-            + 4 * blk * len(step.cow_pairs_host))
+    return (attention_bytes(w, step.context_lens_host, _query_rows(step)) + 20 * T
+            + 4 * row * T + 4 * blk * len(step.cow_pairs_host))
+
+
+def _query_rows(step):
+    return step.num_tokens if step.all_queries else None
 
 
 def fused_bytes(w, step) -> int:
@@ -76,8 +82,8 @@ def fused_bytes(w, step) -> int:
         if src >= 0:
             first_new = int(step.context_lens_host[r]) - int(qsl[r + 1] - qsl[r])
             old_slots += first_new % w.block_size
-    return (attention_bytes(w, step.context_lens_host) + (4 * row + 8) * step.num_tokens
-            + 4 * row * old_slots)
+    return (attention_bytes(w, step.context_lens_host, _query_rows(step))
+            + (4 * row + 8) * step.num_tokens + 4 * row * old_slots)
 
 
 def pmc_traffic(workload: str, per_launch_bytes: int):
@@ -151,7 +157,7 @@ def cpu_baseline(w, vals, step, budget_s: float):
     import torch
     from threadpoolctl import threadpool_limits
 
-    from oracle.attention import paged_attention
+    from oracle.attention import paged_attention, paged_attention_multi
 
     def host(t):
         if t.dtype == torch.bfloat16:
@@ -160,6 +166,7 @@ def cpu_baseline(w, vals, step, budget_s: float):
 
     tables = step.tables_host
     lens = step.context_lens_host
+    qsl = step.query_start_loc_host
     q = host(step.query)
     # host copies of each sequence's blocks (table entries renumbered)
     per_seq = []
@@ -178,7 +185,12 @@ def cpu_baseline(w, vals, step, budget_s: float):
         while t_used < budget_s:
             for s, (kc, vc, row) in enumerate(per_seq):
                 t0 = time.perf_counter()
-                paged_attention(q[s:s + 1], kc, vc, row, lens[s:s + 1], w.scale, w.dtype)
+                if step.all_queries:
+                    a, b = int(qsl[s]), int(qsl[s + 1])
+                    paged_attention_multi(q[a:b], kc, vc, row, lens[s:s + 1], [0, b - a],
+                                          w.scale, w.dtype)
+                else:
+                    paged_attention(q[s:s + 1], kc, vc, row, lens[s:s + 1], w.scale, w.dtype)
                 t_used += time.perf_counter() - t0
                 done_tokens += int(lens[s])
                 done_seqs += 1
@@ -232,7 +244,7 @@ def main():
     print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
     vals = W.make_values(w, "cuda")
     step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
-                      w.scale, part)
+                      w.scale, part, all_queries=w.extra.get("queries") == "all")
     torch.cuda.synchronize()
 
     fused = not args.unfused
@@ -269,7 +281,8 @@ def main():
     attn_avg_ms = float(np.mean(attn_ms))
 
     kv_tokens = int(step.context_lens_host.sum())
-    attn_bytes = fused_bytes(w, step) if fused else attention_bytes(w, step.context_lens_host)
+    attn_bytes = (fused_bytes(w, step) if fused
+                  else attention_bytes(w, step.context_lens_host, _query_rows(step)))
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     value = kv_tokens / (ms_per_step * 1e-3)
     result = {
@@ -300,6 +313,7 @@ def main():
             "fused_step": fused,
             "cow_copies": int(len(step.cow_pairs_host)),
             "step_tokens": int(step.num_tokens),
+            "queries_per_sequence": step.max_query_len or 1,
         },
         "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
         "attention_ms": {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),

@@ -247,6 +247,12 @@ int32_t pa_paged_attention_decode_planned(void* out, const void* query, const vo
  *                    a multiple of 16 bytes)
  *   cow_src          device int64 [num_seqs], -1 for none; may be NULL
  *   slot_mapping     device int64 [T] receiving the new tokens' slots; may be NULL
+ *   max_query_len    0: one query per sequence (query / out [num_seqs][H][D],
+ *                    the decode case); > 0: every new token is a query with
+ *                    the causal rule of pa_paged_attention_multi (query / out
+ *                    [T][H][D], at most max_query_len new tokens per
+ *                    sequence; split-K workspace sized for num_seqs x
+ *                    max_query_len rows)
  * The other arguments are those of pa_paged_attention_decode_planned.
  * ---------------------------------------------------------------------- */
 int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* value_cache,
@@ -259,7 +265,36 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        size_t workspace_bytes, const int32_t* query_start_loc,
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
-                       void* stream);
+                       int32_t max_query_len, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Several new tokens per sequence (speculative drafts, short prefill chunks;
+ * [CSDN] section 2.3 lays a step's tokens out by query_start_loc, [DEEPSONAR]
+ * section 2.5 schedules them like decode tokens).  Sequence s has n_s =
+ * query_start_loc[s+1] - query_start_loc[s] new tokens, the last n_s of its
+ * context_lens[s] tokens (already in the cache); new token i (row
+ * query_start_loc[s] + i, position L_s - n_s + i) attends to positions
+ * 0 .. L_s - n_s + i: the whole earlier context and the new tokens up to
+ * itself.  n_s = 1 everywhere is the decode call.
+ *   out, query       device [num_tokens][num_heads][head_size]
+ *   query_start_loc  device int32 [num_seqs + 1], from 0 to num_tokens
+ *   max_query_len    host bound on n_s; max_query_len x (num_heads /
+ *                    num_kv_heads) must be at most 16 for 16-bit storage and
+ *                    head_size 128 (matrix-core kernel), else at most 8
+ *   workspace        split-K only: pa_split_workspace_bytes(num_tokens, ...)
+ * Work items, shared_prefix_blocks and partition_size as in
+ * pa_paged_attention_decode_planned (items are (sequence, partition)).
+ * ---------------------------------------------------------------------- */
+int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 int64_t bt_stride, const int32_t* context_lens,
+                                 const int32_t* query_start_loc, int32_t num_seqs,
+                                 int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size, int32_t max_context_len,
+                                 float scale, int32_t dtype, int32_t partition_size,
+                                 const int32_t* work_items, int64_t num_work_items,
+                                 const int32_t* shared_prefix_blocks, void* workspace,
+                                 size_t workspace_bytes, int64_t num_tokens, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host block allocator (CPU memory only; no device calls).  Generates the

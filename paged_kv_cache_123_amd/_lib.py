@@ -45,7 +45,10 @@ SIGNATURES = {
     "pa_probe_read_blocks": (_i32, [_vp, _vp, _i64, _vp, _i32, _i32, _vp]),
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
                               _i32, _f32, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp,
-                              _i64, _i64, _vp, _vp, _vp]),
+                              _i64, _i64, _vp, _vp, _i32, _vp]),
+    "pa_paged_attention_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                        _i64, _vp, _vp, _sz, _i64, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _pi32, _c.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_add_seq": (_i32, [_vp, _i64]),

@@ -41,9 +41,16 @@ namespace {
 using namespace dev;
 
 // ---- the decode kernel ------------------------------------------------------
-// FINAL: write out[s][h][:] in storage dtype (single pass); otherwise write the
+// FINAL: write the outputs in storage dtype (single pass); otherwise write the
 // partition's (m, l, o) to the split workspace.
-template <int DT, int D, int G, int NW, bool FINAL>
+//
+// A workgroup serves NQ query vectors that share the KV head: vector v is new
+// token v >> log2_group of the sequence (one token per sequence when q_start is
+// null, the decode case) and query head kvh * G + (v & (G - 1)), G = 1 <<
+// log2_group.  Vector v sees the keys below bound[v] = L - n + (v >> log2_group)
+// + 1 for a sequence with n new tokens; vectors past the sequence's new tokens
+// see none and are not stored.
+template <int DT, int D, int NQ, int NW, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
     const void* value_cache, const int32_t* __restrict__ block_tables,
@@ -51,7 +58,8 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
     float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
-    const int32_t* __restrict__ shared_blocks) {
+    const int32_t* __restrict__ shared_blocks, int32_t log2_group,
+    const int32_t* __restrict__ q_start) {
   using S = St<DT>;
   constexpr int VEC = S::VEC;
   constexpr int LPT = D / VEC;    // lanes per token
@@ -83,16 +91,25 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     apply_appends<LPT, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
                                   static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * LPT,
                                   static_cast<int64_t>(kvh) * (1 << log2_block) * LPT);
-  const int32_t h0 = kvh * G;
+  const int32_t h0 = kvh << log2_group;
+  const int gmask = (1 << log2_group) - 1;
+  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
+  const int64_t qrow0 = q_start ? q_start[s] : s;
 
-  typename S::QReg q[G];
+  typename S::QReg q[NQ];
+  int bound[NQ];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
-    q[j] = S::load_q(query, (static_cast<int64_t>(s) * num_heads + h0 + j) * D + sub * VEC);
+  for (int j = 0; j < NQ; ++j) {
+    const int qi = j >> log2_group;
+    bound[j] = qi < qlen ? L - qlen + qi + 1 : 0;
+    q[j] = S::zero_q();
+    if (qi < qlen)
+      q[j] = S::load_q(query, ((qrow0 + qi) * num_heads + h0 + (j & gmask)) * D + sub * VEC);
+  }
 
-  float m[G], l[G], acc[G][VEC];
+  float m[NQ], l[NQ], acc[NQ][VEC];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
+  for (int j = 0; j < NQ; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.0f;
 #pragma unroll
@@ -143,22 +160,22 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     };
     auto consume = [&](int it, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
       const int t0 = c0 + (wave + it * NW) * kTile;
-      // scores of this lane group's U tokens for all G heads (log2 domain)
-      float x[G][U];
+      // scores of this lane group's U tokens for all NQ vectors (log2 domain)
+      float x[NQ][U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool valid = t0 + u * TPL + lg < c1;
+        const int t = t0 + u * TPL + lg;
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
+        for (int j = 0; j < NQ; ++j) {
           const float d = group_sum<LPT>(S::dot(q[j], kr[u]));
-          x[j][u] = valid ? d * scale_log2 : -INFINITY;
+          x[j][u] = (t < c1 && t < bound[j]) ? d * scale_log2 : -INFINITY;
         }
       }
       float vf[U][VEC];
 #pragma unroll
       for (int u = 0; u < U; ++u) S::to_float(vr[u], vf[u]);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < NQ; ++j) {
         float mt = m[j];
 #pragma unroll
         for (int u = 0; u < U; ++u) mt = fmaxf(mt, x[j][u]);
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < NQ; ++j) {
       const float mo = __shfl_xor(m[j], off);
       const float lo = __shfl_xor(l[j], off);
       const float mt = fmaxf(m[j], mo);
@@ -218,12 +235,12 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   }
 
   // ---- merge the waves through LDS, in wave order ----
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
+  __shared__ float sm_m[NW][NQ];
+  __shared__ float sm_l[NW][NQ];
+  __shared__ float sm_acc[NW][NQ][D];
   if (lg == 0) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < NQ; ++j) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) sm_acc[wave][j][sub * VEC + e] = acc[j][e];
       if (sub == 0) {
@@ -233,24 +250,27 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += NW * 64) {
+  for (int i = threadIdx.x; i < NQ * D; i += NW * 64) {
     const int j = i / D, d = i % D;
+    const int qi = j >> log2_group;
+    if (qi >= qlen) continue;  // a vector past this sequence's new tokens
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
+    const float Ms = M == -INFINITY ? 0.0f : M;  // no visible key in this range
     float lsum = 0.0f, a = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float c = __builtin_amdgcn_exp2f(sm_m[w][j] - M);  // idle wave: exp2(-inf) = 0
+      const float c = __builtin_amdgcn_exp2f(sm_m[w][j] - Ms);  // idle wave: exp2(-inf) = 0
       lsum = fmaf(sm_l[w][j], c, lsum);
       a = fmaf(sm_acc[w][j][d], c, a);
     }
-    const int64_t row = static_cast<int64_t>(s) * num_heads + h0 + j;
+    const int64_t row = (qrow0 + qi) * num_heads + h0 + (j & gmask);
     if constexpr (FINAL) {
       S::store(out, row * D + d, a / lsum);
     } else {
       const int64_t slot = row * num_partitions + p;
-      ws_out[slot * D + d] = a / lsum;
+      ws_out[slot * D + d] = lsum > 0.0f ? a / lsum : 0.0f;  // empty range: weight 0
       if (d == 0) {
         ws_max[slot] = M * kLn2;
         ws_sum[slot] = lsum;
@@ -268,7 +288,8 @@ template <int DT, int D>
 __global__ __launch_bounds__(D) void split_reduce_kernel(
     void* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t num_heads,
     int32_t partition_size, int32_t num_partitions, const float* __restrict__ ws_max,
-    const float* __restrict__ ws_sum, const float* __restrict__ ws_out) {
+    const float* __restrict__ ws_sum, const float* __restrict__ ws_out,
+    const int32_t* __restrict__ q_start) {
   constexpr int kChunk = 256;
   constexpr int NWV = D / 64;
   __shared__ float sw[kChunk];
@@ -278,7 +299,11 @@ __global__ __launch_bounds__(D) void split_reduce_kernel(
   const int d = threadIdx.x;
   const int L = context_lens[s];
   const int np = min((L + partition_size - 1) / partition_size, num_partitions);
-  const int64_t row = static_cast<int64_t>(s) * num_heads + h;
+  // one output row per new token of the sequence (one row when q_start is null)
+  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
+  const int64_t qrow0 = q_start ? q_start[s] : s;
+  for (int qi = 0; qi < qlen; ++qi) {
+  const int64_t row = (qrow0 + qi) * num_heads + h;
   const float* mrow = ws_max + row * num_partitions;
   const float* lrow = ws_sum + row * num_partitions;
   const float* orow = ws_out + row * num_partitions * D;
@@ -313,32 +338,39 @@ __global__ __launch_bounds__(D) void split_reduce_kernel(
     for (int k = 0; k < cn; ++k) wsum += sw[k];
   }
   St<DT>::store(out, row * D + d, a / wsum);
+  __syncthreads();  // red and sw are reused by the next row
+  }
 }
 
-template <int DT, int D, int G, bool FINAL, int NW>
+template <int DT, int D, int NQ, bool FINAL, int NW>
 hipError_t launch_decode_nw(const DecodeArgs& a, hipStream_t stream) {
   int log2_block = 0;
   while ((1 << log2_block) < a.block_size) ++log2_block;
+  int log2_group = 0;
+  while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))
                             : dim3(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, NW, FINAL>), grid, dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((paged_decode_kernel<DT, D, NQ, NW, FINAL>), grid, dim3(NW * 64), 0, stream,
                      a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
                      a.context_lens, a.num_heads, a.num_kv_heads, log2_block, a.partition_size,
                      a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum, a.ws_out,
                      reinterpret_cast<const int2*>(a.items), a.append,
-                     a.shared_blocks);
+                     a.shared_blocks, log2_group, a.q_start);
   return hipGetLastError();
 }
 
-template <int DT, int D, int G, bool FINAL>
+template <int DT, int D, int NQ, bool FINAL>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  return a.shared_blocks ? launch_decode_nw<DT, D, G, FINAL, PA_VALU_WAVES_SHARED>(a, stream)
-                         : launch_decode_nw<DT, D, G, FINAL, PA_VALU_WAVES>(a, stream);
+  // many query vectors of a wide head need more registers than 8-wave
+  // workgroups leave each wave: those keep the shared-case wave count
+  constexpr int kWaves = NQ * D > 512 ? PA_VALU_WAVES_SHARED : PA_VALU_WAVES;
+  return a.shared_blocks ? launch_decode_nw<DT, D, NQ, FINAL, PA_VALU_WAVES_SHARED>(a, stream)
+                         : launch_decode_nw<DT, D, NQ, FINAL, kWaves>(a, stream);
 }
 
 template <int DT, int D, bool FINAL>
 hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.num_heads / a.num_kv_heads) {
+  switch (query_vectors(a)) {
     case 1: return launch_decode_t<DT, D, 1, FINAL>(a, stream);
     case 2: return launch_decode_t<DT, D, 2, FINAL>(a, stream);
     case 4: return launch_decode_t<DT, D, 4, FINAL>(a, stream);
@@ -368,7 +400,7 @@ template <int DT, int D>
 hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((split_reduce_kernel<DT, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
                      stream, a.out, a.context_lens, a.num_heads, a.partition_size,
-                     a.num_partitions, a.ws_max, a.ws_sum, a.ws_out);
+                     a.num_partitions, a.ws_max, a.ws_sum, a.ws_out, a.q_start);
   return hipGetLastError();
 }
 
@@ -400,9 +432,15 @@ int set_decode_kernel(int mode) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int mode = decode_kernel_mode();
-  const int group = a.num_heads / a.num_kv_heads;
-  const bool mfma = decode_mfma_supported(a) && (mode == 2 || (mode == 0 && group >= 2));
+  const int nq = query_vectors(a);
+  const bool can_mfma = decode_mfma_supported(a);
+  const bool can_valu = nq <= 8;
+  // automatic: matrix cores as soon as a workgroup serves several query vectors
+  const bool mfma = mode == 1 ? (!can_valu && can_mfma)
+                  : mode == 2 ? can_mfma
+                              : (can_mfma && nq >= 2);
   if (mfma) return launch_decode_mfma(a, stream);
+  if (!can_valu) return hipErrorInvalidValue;
   return a.partition_size == 0 ? dispatch_decode<true>(a, stream)
                                : dispatch_decode<false>(a, stream);
 }

@@ -45,7 +45,10 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int DT, int G, int NW, bool FINAL>
+// Column c of the 16 MFMA columns is query vector c (c < NQ): new token
+// c >> log2_group of the sequence (one per sequence when q_start is null) and
+// query head kvh * G + (c & (G - 1)); it sees the keys below its causal bound.
+template <int DT, int NQ, int NW, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
     const void* value_cache, const int32_t* __restrict__ block_tables,
@@ -53,14 +56,15 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     int32_t num_kv_heads, int32_t log2_block, int32_t partition_size, int32_t num_partitions,
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
     float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
-    const int32_t* __restrict__ shared_blocks) {
+    const int32_t* __restrict__ shared_blocks, int32_t log2_group,
+    const int32_t* __restrict__ q_start) {
   constexpr int D = 128;
   constexpr int DV = D / 8;   // 16-byte vectors per token row
   constexpr int NK = D / 32;  // score MFMAs per tile
   constexpr int NE = 8;       // value MFMAs per tile (dims 8m + e)
   constexpr int U = 4;        // token-major V loads per tile
   using MM = Mma<DT>;
-  static_assert(G >= 1 && G <= 16, "head group must fit the 16 MFMA columns");
+  static_assert(NQ >= 1 && NQ <= 16, "query vectors must fit the 16 MFMA columns");
 
   const WorkUnit wu = work_unit(items, num_kv_heads);
   const int p = wu.p;
@@ -85,16 +89,22 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     apply_appends<DV, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
                                   static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * DV,
                                   static_cast<int64_t>(kvh) * (1 << log2_block) * DV);
-  const int h0 = kvh * G;
+  const int h0 = kvh << log2_group;
+  const int gmask = (1 << log2_group) - 1;
+  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
+  const int64_t qrow0 = q_start ? q_start[s] : s;
+  const int my_qi = col >> log2_group;
+  const bool my_valid = col < NQ && my_qi < qlen;
+  const int bound = my_valid ? L - qlen + my_qi + 1 : 0;  // keys this column sees
 
   uint4 qv[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     qv[k] = make_uint4(0, 0, 0, 0);
-    if (col < G)
+    if (my_valid)
       qv[k] = *reinterpret_cast<const uint4*>(
           static_cast<const uint16_t*>(query) +
-          (static_cast<int64_t>(s) * num_heads + h0 + col) * D + k * 32 + grp * 8);
+          ((qrow0 + my_qi) * num_heads + h0 + (col & gmask)) * D + k * 32 + grp * 8);
   }
 
   f32x4 o[NE];
@@ -145,15 +155,19 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
       for (int k = 0; k < NK; ++k) sc = MM::k32(kr[k], qv[k], sc);
       float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = t0 + grp + 4 * j < c1 ? sc[j] * scale_log2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + grp + 4 * j;
+        x[j] = (t < c1 && t < bound) ? sc[j] * scale_log2 : -INFINITY;
+      }
       float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);  // finite: token t0 is always valid
-      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      const float mn = fmaxf(m, mt);
+      const float ms = mn == -INFINITY ? 0.0f : mn;  // a column with no visible key yet
+      const float corr = __builtin_amdgcn_exp2f(m - ms);
       float pr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - mn);
+      for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - ms);
       lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
 #pragma unroll
       for (int e = 0; e < NE; ++e) o[e] *= corr;
@@ -200,10 +214,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
-  if (col < G) {
+  __shared__ float sm_m[NW][NQ];
+  __shared__ float sm_l[NW][NQ];
+  __shared__ float sm_acc[NW][NQ][D];
+  if (col < NQ) {
     if (grp == 0) {
       sm_m[wave][col] = m;
       sm_l[wave][col] = lsum;
@@ -214,24 +228,27 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
       for (int j = 0; j < 4; ++j) sm_acc[wave][col][32 * grp + 8 * j + e] = o[e][j];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += NW * 64) {
+  for (int i = threadIdx.x; i < NQ * D; i += NW * 64) {
     const int j = i / D, d = i % D;
+    const int qi = j >> log2_group;
+    if (qi >= qlen) continue;  // a column past this sequence's new tokens
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
+    const float Ms = M == -INFINITY ? 0.0f : M;  // no visible key in this range
     float l = 0.0f, a = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float c = __builtin_amdgcn_exp2f(sm_m[w][j] - M);
+      const float c = __builtin_amdgcn_exp2f(sm_m[w][j] - Ms);
       l = fmaf(sm_l[w][j], c, l);
       a = fmaf(sm_acc[w][j][d], c, a);
     }
-    const int64_t row = static_cast<int64_t>(s) * num_heads + h0 + j;
+    const int64_t row = (qrow0 + qi) * num_heads + h0 + (j & gmask);
     if constexpr (FINAL) {
       St<DT>::store(out, row * D + d, a / l);
     } else {
       const int64_t slot = row * num_partitions + p;
-      ws_out[slot * D + d] = a / l;
+      ws_out[slot * D + d] = l > 0.0f ? a / l : 0.0f;  // empty range: weight 0
       if (d == 0) {
         ws_max[slot] = M * kLn2;
         ws_sum[slot] = l;
@@ -240,29 +257,32 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
   }
 }
 
-template <int DT, int G, bool FINAL>
+template <int DT, int NQ, bool FINAL>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   int log2_block = 0;
   while ((1 << log2_block) < a.block_size) ++log2_block;
+  int log2_group = 0;
+  while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))
                             : dim3(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<DT, G, NW, FINAL>), grid, dim3(NW * 64), 0,
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<DT, NQ, NW, FINAL>), grid, dim3(NW * 64), 0,
                      stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
                      a.partition_size, a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum,
                      a.ws_out, reinterpret_cast<const int2*>(a.items), a.append,
-                     a.shared_blocks);
+                     a.shared_blocks, log2_group, a.q_start);
   return hipGetLastError();
 }
 
 template <int DT, bool FINAL>
 hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.num_heads / a.num_kv_heads) {
+  switch (query_vectors(a)) {
     case 1: return launch_t<DT, 1, FINAL>(a, stream);
     case 2: return launch_t<DT, 2, FINAL>(a, stream);
     case 4: return launch_t<DT, 4, FINAL>(a, stream);
     case 8: return launch_t<DT, 8, FINAL>(a, stream);
+    case 16: return launch_t<DT, 16, FINAL>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -270,7 +290,8 @@ hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool decode_mfma_supported(const DecodeArgs& a) {
-  return (a.dtype == PA_F16 || a.dtype == PA_BF16) && a.head_size == 128;
+  return (a.dtype == PA_F16 || a.dtype == PA_BF16) && a.head_size == 128 &&
+         query_vectors(a) <= 16;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {

@@ -64,6 +64,21 @@ int32_t check_decode(const char* who, void* out, const void* query, const void* 
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Every new token of a sequence is a query: the query vectors of one work item
+// (max_query_len x heads per KV head) must fit one workgroup.
+int32_t check_query_capacity(const char* who, int32_t max_query_len, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_size, int32_t dtype) {
+  if (max_query_len < 1)
+    return fail(PA_EINVAL, (std::string(who) + ": max_query_len must be >= 1").c_str());
+  const int64_t nq = static_cast<int64_t>(max_query_len) * (num_heads / num_kv_heads);
+  const bool matrix = (dtype == PA_F16 || dtype == PA_BF16) && head_size == 128;
+  if (nq > (matrix ? 16 : 8))
+    return fail(PA_EINVAL, (std::string(who) + ": max_query_len x (num_heads / num_kv_heads) "
+                            "must be at most 16 (16-bit storage, head_size 128) or 8")
+                               .c_str());
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,7 +277,7 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        size_t workspace_bytes, const int32_t* query_start_loc,
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
-                       void* stream) {
+                       int32_t max_query_len, void* stream) {
   const char* who = "pa_decode_step";
   int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
                             context_lens, num_seqs, num_heads, num_kv_heads, head_size,
@@ -288,17 +303,29 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                                  value_stride * eb / 16, static_cast<uint4*>(key_cache),
                                  static_cast<uint4*>(value_cache), slot_mapping};
   a.shared_blocks = shared_prefix_blocks;
+  if (max_query_len > 0) {  // every new token is a query
+    st = check_query_capacity(who, max_query_len, num_heads, num_kv_heads, head_size, dtype);
+    if (st != PA_OK) return st;
+    a.q_start = query_start_loc;
+    a.max_query_len = max_query_len;
+  } else if (max_query_len < 0) {
+    return fail(PA_EINVAL, "pa_decode_step: max_query_len must be >= 0");
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
       partition_size % block_size != 0)
     return fail(PA_EINVAL, "pa_decode_step: bad partition_size");
-  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
-                                               partition_size);
+  // workspace rows: one per sequence, or num_seqs x max_query_len when every
+  // new token is a query
+  const int64_t out_rows = static_cast<int64_t>(num_seqs) * (max_query_len > 0 ? max_query_len : 1);
+  if (out_rows > 0x7fffffff) return fail(PA_EINVAL, "pa_decode_step: too many query rows");
+  const size_t need = pa_split_workspace_bytes(static_cast<int32_t>(out_rows), num_heads,
+                                               head_size, max_context_len, partition_size);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PA_EINVAL, "pa_decode_step: workspace missing, too small or misaligned");
   const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  const size_t rows = static_cast<size_t>(out_rows) * num_heads * np;
   char* ws = static_cast<char*>(workspace);
   a.partition_size = partition_size;
   a.num_partitions = np;
@@ -308,6 +335,57 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
   st = launched(pa::launch_decode(a, s), "pa_decode_step (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_decode_step (reduce)");
+}
+
+int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 int64_t bt_stride, const int32_t* context_lens,
+                                 const int32_t* query_start_loc, int32_t num_seqs,
+                                 int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size, int32_t max_context_len,
+                                 float scale, int32_t dtype, int32_t partition_size,
+                                 const int32_t* work_items, int64_t num_work_items,
+                                 const int32_t* shared_prefix_blocks, void* workspace,
+                                 size_t workspace_bytes, int64_t num_tokens, void* stream) {
+  const char* who = "pa_paged_attention_multi";
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (!query_start_loc || num_tokens < 1)
+    return fail(PA_EINVAL, "pa_paged_attention_multi: NULL query_start_loc or num_tokens < 1");
+  st = check_query_capacity(who, max_query_len, num_heads, num_kv_heads, head_size, dtype);
+  if (st != PA_OK) return st;
+  if (!work_items || num_work_items < 1 ||
+      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, "pa_paged_attention_multi: bad work list");
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, work_items, num_work_items};
+  a.shared_blocks = shared_prefix_blocks;
+  a.q_start = query_start_loc;
+  a.max_query_len = max_query_len;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, "pa_paged_attention_multi: bad partition_size");
+  if (num_tokens > 0x7fffffff) return fail(PA_EINVAL, "pa_paged_attention_multi: too many tokens");
+  const size_t need = pa_split_workspace_bytes(static_cast<int32_t>(num_tokens), num_heads,
+                                               head_size, max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL, "pa_paged_attention_multi: workspace missing, too small or misaligned");
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(num_tokens) * num_heads * np;
+  char* ws = static_cast<char*>(workspace);
+  a.partition_size = partition_size;
+  a.num_partitions = np;
+  a.ws_max = reinterpret_cast<float*>(ws);
+  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  st = launched(pa::launch_decode(a, s), "pa_paged_attention_multi (partition)");
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_multi (reduce)");
 }
 
 }  // extern "C"

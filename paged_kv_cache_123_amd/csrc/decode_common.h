@@ -68,6 +68,7 @@ struct St<PA_F32> {
   __device__ static QReg load_q(const void* p, int64_t idx) {
     return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
   }
+  __device__ static QReg zero_q() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
   __device__ static float dot(const QReg& q, const uint4& k) {
     float s = q.x * __uint_as_float(k.x);
     s = fmaf(q.y, __uint_as_float(k.y), s);
@@ -96,6 +97,7 @@ struct St<PA_F16> {
   __device__ static QReg load_q(const void* p, int64_t idx) {
     return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
   }
+  __device__ static QReg zero_q() { return make_uint4(0, 0, 0, 0); }
   __device__ static float d2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
                                   c, false);
@@ -128,6 +130,7 @@ struct St<PA_BF16> {
   __device__ static QReg load_q(const void* p, int64_t idx) {
     return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
   }
+  __device__ static QReg zero_q() { return make_uint4(0, 0, 0, 0); }
   __device__ static float d2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
                                            __builtin_bit_cast(bf162_t, b), c, false);

@@ -46,7 +46,19 @@ struct DecodeArgs {
   int64_t num_items;
   dev::AppendArgs append;    // the step's cache writes (append.qsl == nullptr: none)
   const int32_t* shared_blocks;  // [S] leading blocks shared with other sequences, or nullptr
+  const int32_t* q_start;    // [S+1] new-token rows when every new token is a query, or nullptr
+  int32_t max_query_len;     // bound on q_start[s+1] - q_start[s] (host)
 };
+
+// Query vectors one workgroup serves: (new tokens per sequence) x (query heads
+// per KV head), rounded up to a power of two.
+inline int query_vectors(const DecodeArgs& a) {
+  const int per_seq = a.q_start ? (a.max_query_len > 0 ? a.max_query_len : 1) : 1;
+  const int n = per_seq * (a.num_heads / a.num_kv_heads);
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
 
 // Paged decode attention (single pass when partition_size == 0, else the
 // partition kernel).  Picks the matrix-core kernel for grouped-query heads

@@ -264,12 +264,22 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                 context_lens: torch.Tensor, scale: float, max_context_len: int,
                 partition_size: int, work_items: torch.Tensor, query_start_loc: torch.Tensor,
                 key: torch.Tensor, value: torch.Tensor, cow_src=None, slot_mapping=None,
-                workspace=None, shared_prefix_blocks=None) -> None:
+                workspace=None, shared_prefix_blocks=None, max_query_len: int = 0) -> None:
     """The whole decode step in one launch: copy-on-write of the old slots of
     fresh tail blocks (``cow_src`` int64 [num_seqs], -1 for none), the new
     tokens' K/V (rows of ``key``/``value`` per ``query_start_loc``) into their
-    slots, and planned attention over the updated caches."""
-    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
+    slots, and planned attention over the updated caches.  ``max_query_len``
+    > 0 makes every new token a query (query/out [num_tokens, H, D])."""
+    if max_query_len > 0:
+        S = block_tables.shape[0]
+        _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+        nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+        if out.shape != query.shape or query.dim() != 3 or query.shape[2] != D:
+            raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+        H = query.shape[1]
+    else:
+        S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
+                                       context_lens)
     _dev(work_items, query_start_loc, key, value)
     if query_start_loc.dtype != torch.int32 or query_start_loc.numel() < S + 1:
         raise ValueError("query_start_loc must be int32 [num_seqs + 1]")
@@ -301,4 +311,39 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
         work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
         query_start_loc.data_ptr(),
         key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None,
-        slot_ptr or None, _stream()))
+        slot_ptr or None, max_query_len, _stream()))
+
+
+def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                          value_cache: torch.Tensor, block_tables: torch.Tensor,
+                          context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                          max_query_len: int, scale: float, max_context_len: int,
+                          partition_size: int, work_items: torch.Tensor, workspace=None,
+                          shared_prefix_blocks=None) -> None:
+    """Attention of every new token (query/out [num_tokens, H, D]), causal over
+    each sequence's new tokens."""
+    _dev(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+         work_items)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if query.dim() != 3 or query.shape[2] != D or out.shape != query.shape:
+        raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+    if query.dtype != key_cache.dtype or out.dtype != key_cache.dtype:
+        raise TypeError("query/out must have the cache dtype")
+    for n, t in (("query", query), ("out", out), ("block_tables", block_tables),
+                 ("context_lens", context_lens), ("query_start_loc", query_start_loc),
+                 ("work_items", work_items)):
+        _contig(n, t)
+    S = block_tables.shape[0]
+    if query_start_loc.dtype != torch.int32 or query_start_loc.numel() < S + 1:
+        raise ValueError("query_start_loc must be int32 [num_seqs + 1]")
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().pa_paged_attention_multi(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(),
+        query_start_loc.data_ptr(), S, max_query_len, query.shape[1], hkv, D, B,
+        max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
+        work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
+        query.shape[0], _stream()))

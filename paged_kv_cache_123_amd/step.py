@@ -33,11 +33,14 @@ class DecodeStep:
     ``history``: list of ("add", s) / ("append", s, n) / ("fork", parent, child);
     ``appends``: list of (s, n) appended by the step, one per batch row, in
     batch order; ``values``: dict with key_cache, value_cache, query, new_key,
-    new_value device tensors (caches [NB, H_kv, B, D]).
+    new_value device tensors (caches [NB, H_kv, B, D]).  ``all_queries``:
+    every new token is a query (query/out [num_tokens, H, D], causal over each
+    sequence's new tokens) instead of one query per sequence.
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
-                 values: dict, scale: float, partition_size: int = 0, planned: bool = True):
+                 values: dict, scale: float, partition_size: int = 0, planned: bool = True,
+                 all_queries: bool = False):
         self.pool = Pool(num_blocks, block_size, free_order)
         for op in history:
             if op[0] == "add":
@@ -91,12 +94,18 @@ class DecodeStep:
         self.slot_mapping = torch.empty(self.num_tokens, dtype=torch.int64, device=dev)
         self.out = torch.empty_like(self.query)
         self.planned = planned
+        self.all_queries = bool(all_queries)
+        self.max_query_len = int(max(n for _, n in appends)) if all_queries else 0
+        if all_queries and not planned:
+            raise ValueError("every-token queries use the planned launch")
         self.plan_host = ops.decode_plan(lens, self.partition_size)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self.workspace = None
         if self.partition_size:
-            S, H, D = self.query.shape
-            self.workspace = ops.alloc_split_workspace(S, H, D, self.max_context_len,
+            rows, H, D = self.query.shape
+            if all_queries:  # the one-launch step sizes rows as num_seqs x max_query_len
+                rows = max(rows, len(seqs) * self.max_query_len)
+            self.workspace = ops.alloc_split_workspace(rows, H, D, self.max_context_len,
                                                        self.partition_size, dev)
 
     # ---- the step, kernel by kernel --------------------------------------
@@ -112,7 +121,13 @@ class DecodeStep:
                               self.slot_mapping)
 
     def attention(self):
-        if self.planned:
+        if self.all_queries:
+            ops.paged_attention_multi(self.out, self.query, self.key_cache, self.value_cache,
+                                      self.block_tables, self.context_lens,
+                                      self.query_start_loc, self.max_query_len, self.scale,
+                                      self.max_context_len, self.partition_size, self.plan,
+                                      self.workspace, self.shared_blocks)
+        elif self.planned:
             ops.paged_attention_decode_planned(self.out, self.query, self.key_cache,
                                                self.value_cache, self.block_tables,
                                                self.context_lens, self.scale,
@@ -135,7 +150,7 @@ class DecodeStep:
                         self.block_tables, self.context_lens, self.scale, self.max_context_len,
                         self.partition_size, self.plan, self.query_start_loc, self.new_key,
                         self.new_value, self.cow_src, self.slot_mapping, self.workspace,
-                        self.shared_blocks)
+                        self.shared_blocks, self.max_query_len)
 
     def run(self, fused: bool = False):
         """The whole step; returns ``out`` [num_seqs, num_heads, head_size].

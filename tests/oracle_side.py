@@ -7,7 +7,7 @@ from __future__ import annotations
 import numpy as np
 
 from oracle.allocator import OraclePool
-from oracle.attention import paged_attention, paged_attention_split
+from oracle.attention import paged_attention, paged_attention_multi, paged_attention_split
 from oracle.cache_ops import copy_blocks, reshape_and_cache
 from oracle.slots import compute_slot_mapping
 
@@ -71,3 +71,7 @@ class OracleStep:
     def attention_split(self, query, kc, vc, partition_size, pairs=None):
         return paged_attention_split(query, kc, vc, self.tables, self.context_lens, self.w.scale,
                                      self.w.dtype, partition_size, pairs=pairs)
+
+    def attention_multi(self, query, kc, vc):
+        return paged_attention_multi(query, kc, vc, self.tables, self.context_lens,
+                                     self.query_start_loc, self.w.scale, self.w.dtype)

@@ -200,12 +200,39 @@ def long_context_bf16(num_seqs=32, context_len=32768):
                                "split-K partitions of 512, pool +5%")
 
 
+def llama7b_spec4_fp16(num_seqs=64, drafts=4):
+    """The Llama-7B batch verifying 4 speculative tokens per sequence: every
+    sequence appends 4 tokens and each of them is a query (causal)."""
+    rng = np.random.default_rng(2)
+    lens = rng.integers(128, 2049, size=64)[:num_seqs]
+    w = custom_multi("llama7b_spec4_fp16", 2, lens, [drafts] * len(lens), dtype="f16", H=32,
+                     Hkv=32, D=128, B=16)
+    w.num_blocks = math.ceil(1.1 * _blocks_for(lens, 16))
+    w.free_order = np.random.default_rng(12).permutation(w.num_blocks).astype(np.int32)
+    w.notes = "Llama-7B layer, 64 seqs L~U[128,2048], 4 speculative tokens each, all queries"
+    return w
+
+
+def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
+    """The GQA batch verifying 2 speculative tokens per sequence (2 x 8 query
+    vectors per KV head fill the 16 matrix-core columns)."""
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal(256)[:num_seqs]
+    lens = np.clip(np.rint(np.exp(math.log(1024.0) + z)), 16, 8192).astype(np.int64)
+    w = custom_multi("qwen72b_gqa_spec2_bf16", 3, lens, [drafts] * len(lens), dtype="bf16",
+                     H=64, Hkv=8, D=128, B=16, sigma=0.5)
+    w.notes = "GQA 64q/8kv layer, 256 seqs lognormal lengths, 2 speculative tokens each"
+    return w
+
+
 CONFIGS = {
     "tiny_fp32": tiny_fp32,
     "llama7b_fp16": llama7b_fp16,
     "qwen72b_gqa_bf16": qwen72b_gqa_bf16,
     "shared_prefix_bf16": shared_prefix_bf16,
     "long_context_bf16": long_context_bf16,
+    "llama7b_spec4_fp16": llama7b_spec4_fp16,
+    "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
 }
 
 
@@ -213,12 +240,35 @@ def make(name: str, **kw) -> Workload:
     return CONFIGS[name](**kw)
 
 
+def custom_multi(name, seed, lens, new_tokens, *, dtype, H, Hkv, D, B, partition_size=0,
+                 sigma=1.0):
+    """A batch whose step appends new_tokens[s] tokens to sequence s (its
+    context_lens[s] = lens[s] counts them): speculative drafts or a short
+    prefill chunk, every new token being a query."""
+    lens = [int(L) for L in lens]
+    rng = np.random.default_rng(seed)
+    nb = _blocks_for(lens, B) + 3
+    order = rng.permutation(nb).astype(np.int32)
+    prefill, step = [], []
+    for s, (L, n) in enumerate(zip(lens, new_tokens)):
+        prefill.append(("add", s))
+        if L > n:
+            prefill.append(("append", s, L - int(n)))
+        step.append((s, int(n)))
+    return Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                    block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(D), sigma=sigma,
+                    seed=seed, free_order=order, seqs=list(range(len(lens))), prefill=prefill,
+                    step=step, context_lens=lens, partition_size=partition_size,
+                    extra={"queries": "all"})
+
+
 def make_values(w: Workload, device, chunk_elems: int = 1 << 26):
     """Seeded value tensors of a workload on ``device``.
 
-    Returns dict(key_cache, value_cache [NB, H_kv, B, D], query [S, H, D],
-    new_key, new_value [T, H_kv, D]); every element ~ N(0, sigma^2), drawn in
-    fp32 and rounded to the storage dtype.  Unused cache slots hold values
+    Returns dict(key_cache, value_cache [NB, H_kv, B, D], query [S, H, D]
+    (or [T, H, D] when every new token is a query, ``w.extra["queries"] ==
+    "all"``), new_key, new_value [T, H_kv, D]); every element ~ N(0, sigma^2),
+    drawn in fp32 and rounded to the storage dtype.  Unused cache slots hold values
     too, so nothing depends on memory the step never writes.
     """
     import torch
@@ -242,7 +292,8 @@ def make_values(w: Workload, device, chunk_elems: int = 1 << 26):
     return {
         "key_cache": draw(cache_shape),
         "value_cache": draw(cache_shape),
-        "query": draw((w.num_seqs, w.num_heads, w.head_size)),
+        "query": draw(((w.num_step_tokens if w.extra.get("queries") == "all" else w.num_seqs),
+                       w.num_heads, w.head_size)),
         "new_key": draw((w.num_step_tokens, w.num_kv_heads, w.head_size)),
         "new_value": draw((w.num_step_tokens, w.num_kv_heads, w.head_size)),
     }
