@@ -29,6 +29,15 @@ Parity status per function (what pins it is listed in each module header):
   attention.paged_attention ........... pinned (library softmax brute force,
                                         closed forms, invariances)
   attention.split_partials/merge ...... pinned (equality with single pass)
+  attention.paged_attention_multi ..... pinned (dense causal softmax)
+  slots.compute_slot_mapping_cp,
+  slots.cp_local_length ............... pinned (hand-computed interleaves, world
+                                        1 = plain mapping, every position on
+                                        one rank, local offsets in order)
+  attention.paged_attention_partials,
+  attention.merge_rank_partials ....... pinned (rank shares merge to dense
+                                        softmax attention; share partial =
+                                        partial over the owned positions)
   dtypes.decode ....................... pinned (bit patterns with known values)
 """
 

@@ -33,11 +33,22 @@ Readings where the pages are silent:
     (position L_s - n_s + i) scores the keys at positions 0 .. L_s - n_s + i
     (causal over the new tokens, the whole cached context before them).
 
+  * Context parallelism ([CSDN] §2.3 spreads a sequence's positions over the
+    ranks of a context-parallel group): every rank attends over the tokens
+    it stores and keeps (m, l, o) as for a split partition; merging the
+    ranks' triples with the split-K merge gives attention over the whole
+    context.  A rank with no token of a sequence contributes m = -inf,
+    l = 0, o = 0 and no weight.
+
 Pinned by tests/test_oracle_attention.py: brute force against a dense
 softmax attention built from scipy.special.softmax on contiguous K/V, closed
 forms (one token -> its value; equal keys or scale 0 -> mean of V), invariance
 under any permutation of physical blocks, shared-prefix identity, GQA equal to
 MHA with repeated KV heads, and split-K merge equal to the single pass.
+The context-parallel functions are pinned by tests/test_oracle_cp.py: the
+ranks' partials, built from rank-local caches written through the
+context-parallel slot mapping, merge to the single pass over the whole
+cache, and each rank's partial equals the one over the positions it owns.
 """
 
 from __future__ import annotations
@@ -196,4 +207,52 @@ def paged_attention_multi(query, key_cache, value_cache, block_tables, context_l
                     if kv_head_of(h, G) == g:
                         out[q0 + i, h] = attend(decode(query[q0 + i, h], dtype), K[:visible],
                                                 V[:visible], sc)
+    return out
+
+
+def attention_partial(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """(m, l, o) of one query over a set of keys; an empty set gives
+    (-inf, 0, zeros)."""
+    if K.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(V.shape[1])
+    x = scale * (K @ q)
+    m = x.max()
+    w = np.exp(x - m)
+    l = w.sum()
+    return m, l, (w @ V) / l
+
+
+def paged_attention_partials(query, key_cache, value_cache, block_tables, context_lens,
+                             scale: float, dtype: str):
+    """Rank-local (m [S, H], l [S, H], o [S, H, D]) over the first
+    context_lens[s] tokens of each sequence in this rank's cache (0 allowed)."""
+    S, H, D = query.shape
+    H_kv, B = key_cache.shape[1], key_cache.shape[2]
+    G = H // H_kv
+    sc = widen_scale(scale)
+    m = np.full((S, H), -np.inf)
+    l = np.zeros((S, H))
+    o = np.zeros((S, H, D))
+    for s in range(S):
+        L = int(context_lens[s])
+        for g in range(H_kv):
+            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B), dtype)
+            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B), dtype)
+            for h in range(H):
+                if kv_head_of(h, G) == g:
+                    m[s, h], l[s, h], o[s, h] = attention_partial(decode(query[s, h], dtype),
+                                                                  K, V, sc)
+    return m, l, o
+
+
+def merge_rank_partials(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """out [S, H, D] from the ranks' m, l [N, S, H] and o [N, S, H, D]; parts
+    with l = 0 carry no weight and a row without any key is 0."""
+    N, S, H, D = o.shape
+    out = np.zeros((S, H, D))
+    for s in range(S):
+        for h in range(H):
+            keep = l[:, s, h] > 0
+            if keep.any():
+                out[s, h] = merge_partials(m[keep, s, h], l[keep, s, h], o[keep, s, h])
     return out

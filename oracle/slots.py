@@ -16,8 +16,18 @@ Readings where the pages are silent:
     a PAD_ID constant but not its value), and entries from the number of
     scheduled tokens up to the buffer length are filled with it.
 
+Context parallelism ([CSDN] §2.3, the same kernel with world size > 1):
+world ranks share one block table; a virtual block holds B * world
+consecutive positions; offset o inside it belongs to rank (o div I) mod world
+(I = interleave size), which stores it in the same-numbered block of its own
+pool at local offset (o div (world * I)) * I + o mod I; on other ranks the
+token maps to the padding id.
+
 Pinned by: tests/test_oracle_slots.py (the [3, 0, 4] example, the 7-token
-growth example, and bijection onto the occupied slots of random pools).
+growth example, bijection onto the occupied slots of random pools, and for
+context parallelism: world 1 equals the plain mapping, hand-computed
+interleaves, every position on exactly one rank, each rank's local offsets
+filled in position order).
 """
 
 from __future__ import annotations
@@ -48,3 +58,39 @@ def compute_slot_mapping(query_start_loc, positions, block_tables, block_size: i
         for i in range(int(query_start_loc[r]), int(query_start_loc[r + 1])):
             out[i] = slot_of(block_tables[r], int(positions[i]), block_size)
     return out
+
+
+def cp_owner_and_offset(offset_in_virtual_block: int, world: int, interleave: int):
+    """(rank, local offset) of an offset inside a virtual block of B * world
+    positions, following the interleave of [CSDN] §2.3."""
+    o = offset_in_virtual_block
+    rank = (o // interleave) % world
+    local = (o // (world * interleave)) * interleave + o % interleave
+    return rank, local
+
+
+def compute_slot_mapping_cp(query_start_loc, positions, block_tables, block_size: int,
+                            max_num_tokens: int, world: int, rank: int, interleave: int):
+    """Rank ``rank``'s slot of every scheduled token (PAD_SLOT when another
+    rank stores it); entries past the last token are PAD_SLOT."""
+    num_reqs = len(query_start_loc) - 1
+    num_tokens = int(query_start_loc[num_reqs])
+    if num_tokens > max_num_tokens:
+        raise ValueError("more tokens than the slot buffer holds")
+    virtual = block_size * world
+    out = [PAD_SLOT] * max_num_tokens
+    for r in range(num_reqs):
+        for i in range(int(query_start_loc[r]), int(query_start_loc[r + 1])):
+            pos = int(positions[i])
+            vblock, off = divmod(pos, virtual)
+            owner, local = cp_owner_and_offset(off, world, interleave)
+            if owner == rank:
+                out[i] = int(block_tables[r][vblock]) * block_size + local
+    return out
+
+
+def cp_local_length(length: int, block_size: int, world: int, rank: int,
+                    interleave: int) -> int:
+    """How many of a sequence's first ``length`` positions rank ``rank`` holds."""
+    return sum(1 for p in range(length)
+               if cp_owner_and_offset(p % (block_size * world), world, interleave)[0] == rank)

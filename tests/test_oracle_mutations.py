@@ -15,6 +15,7 @@ import oracle.attention as attn_mod
 import oracle.slots as slots_mod
 import test_oracle_allocator as TA
 import test_oracle_attention as TT
+import test_oracle_cp as TC
 import test_oracle_slots as TS
 
 
@@ -51,6 +52,23 @@ def _merge_wrong_sign(m, l, o):
 def _merge_ignores_mass(m, l, o):
     a = np.exp(m - m.max())
     return (a @ o) / a.sum()
+
+
+def _cp_owner_ignores_interleave(o, world, interleave):
+    return o % world, (o // (world * interleave)) * interleave + o % interleave
+
+
+def _cp_local_drops_run_offset(o, world, interleave):
+    return (o // interleave) % world, (o // (world * interleave)) * interleave
+
+
+def _partial_unnormalised(q, K, V, scale):
+    if K.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(V.shape[1])
+    x = scale * (K @ q)
+    m = x.max()
+    w = np.exp(x - m)
+    return m, w.sum(), w @ V
 
 
 def _slot_transposed(table_row, pos, block_size):
@@ -151,6 +169,12 @@ MUTATIONS = [
     ("causal bound off by one", attn_mod, "visible_tokens", lambda L, n, i: L - n + i, TT),
     ("causal bound ignores the position", attn_mod, "visible_tokens", lambda L, n, i: L, TT),
     ("slot block/offset transposed", slots_mod, "slot_of", _slot_transposed, TS),
+    ("CP owner ignores the interleave", slots_mod, "cp_owner_and_offset",
+     _cp_owner_ignores_interleave, TC),
+    ("CP local offset drops the offset inside a run", slots_mod, "cp_owner_and_offset",
+     _cp_local_drops_run_offset, TC),
+    ("CP partial output not divided by its sum", attn_mod, "attention_partial",
+     _partial_unnormalised, TC),
     ("free returns blocks to the queue head", alloc_mod, "OraclePool", _PoolFreeToHead, TA),
     ("COW keeps the old reference", alloc_mod, "OraclePool", _PoolCowKeepsRef, TA),
     ("no copy-on-write", alloc_mod, "OraclePool", _PoolNoCow, TA),
@@ -162,14 +186,15 @@ MUTATIONS = [
 def test_planted_mistake_is_caught(monkeypatch, label, module, name, replacement, pins):
     monkeypatch.setattr(module, name, replacement)
     # test modules bound some names at import time: patch those bindings too
-    for mod in (TA, TT, TS):
+    for mod in (TA, TT, TS, TC):
         if hasattr(mod, name):
             monkeypatch.setattr(mod, name, replacement)
     with np.errstate(all="ignore"):
         assert _some_pin_fails(_all(pins)), f"no pin noticed: {label}"
 
 
-@pytest.mark.parametrize("pins", [TA, TT, TS], ids=["allocator", "attention", "slots"])
+@pytest.mark.parametrize("pins", [TA, TT, TS, TC],
+                         ids=["allocator", "attention", "slots", "context_parallel"])
 def test_unmutated_oracle_passes_every_pin(pins):
     """Control: the harness above reports no failure for the real oracle."""
     assert not _some_pin_fails(_all(pins))

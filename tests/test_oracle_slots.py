@@ -129,3 +129,53 @@ def test_cow_copy_then_scatter_matches_sharing_example():
         seq = np.stack([kc[table[p // B], :, p % B, :] for p in range(8)])
         assert np.array_equal(seq[:7], prompt)
         assert np.array_equal(seq[7], new_tok[s][0])
+
+
+# ---- context parallelism ------------------------------------------------------
+
+from oracle.slots import compute_slot_mapping_cp, cp_local_length, cp_owner_and_offset  # noqa: E402
+
+
+def test_cp_world_one_is_the_plain_mapping():
+    rng = np.random.default_rng(3)
+    for B, I in ((4, 1), (16, 4), (8, 8)):
+        tables = [list(rng.permutation(20)[:6]) for _ in range(3)]
+        lens = [5, 17, 23]
+        qsl = np.concatenate([[0], np.cumsum(lens)])
+        pos = np.concatenate([np.arange(L) for L in lens])
+        pos = np.minimum(pos, 6 * B - 1)
+        assert compute_slot_mapping_cp(qsl, pos, tables, B, len(pos), 1, 0, I) == \
+            compute_slot_mapping(qsl, pos, tables, B, len(pos))
+
+
+def test_cp_interleave_hand_examples():
+    # B = 4, two ranks: virtual block of 8 positions
+    # interleave 1: ranks alternate; local offsets 0,0,1,1,2,2,3,3
+    got = [cp_owner_and_offset(o, 2, 1) for o in range(8)]
+    assert got == [(0, 0), (1, 0), (0, 1), (1, 1), (0, 2), (1, 2), (0, 3), (1, 3)]
+    # interleave 2: pairs alternate; local offsets 0,1,0,1,2,3,2,3
+    got = [cp_owner_and_offset(o, 2, 2) for o in range(8)]
+    assert got == [(0, 0), (0, 1), (1, 0), (1, 1), (0, 2), (0, 3), (1, 2), (1, 3)]
+    # interleave = B: each rank takes one whole block's worth in turn
+    got = [cp_owner_and_offset(o, 2, 4) for o in range(8)]
+    assert got == [(0, 0), (0, 1), (0, 2), (0, 3), (1, 0), (1, 1), (1, 2), (1, 3)]
+
+
+@pytest.mark.parametrize("world,I,B", [(2, 1, 4), (4, 2, 8), (3, 1, 2), (8, 16, 16)])
+def test_cp_every_position_on_exactly_one_rank_in_order(world, I, B):
+    rng = np.random.default_rng(world * 100 + I)
+    L = 5 * B * world + 3
+    table = list(rng.permutation(64)[: -(-L // (B * world))])
+    pos = list(range(L))
+    owners = {}
+    for r in range(world):
+        slots = compute_slot_mapping_cp([0, L], pos, [table], B, L, world, r, I)
+        local = [(p, s) for p, s in zip(pos, slots) if s != PAD_SLOT]
+        for p, s in local:
+            assert p not in owners
+            owners[p] = (r, s)
+        # the rank's tokens fill local offsets of each (same-numbered) block in order
+        flat = [(table.index(s // B), s % B) for _, s in local]
+        assert flat == [(j // B, j % B) for j in range(len(local))]
+        assert len(local) == cp_local_length(L, B, world, r, I)
+    assert sorted(owners) == pos
