@@ -203,6 +203,192 @@ def cpu_baseline(w, vals, step, budget_s: float):
                       f"heads), float64 NumPy, 1 BLAS thread, {t_used:.1f} s"}
 
 
+def partials_bytes(w, local_lens) -> int:
+    """Algorithmic bytes of one rank's partials call: its K/V rows, q, table
+    entries and lengths (attention_bytes without the output row), plus the
+    fp32 (m, l, o) it writes for every (sequence, query head)."""
+    e = w.elem_bytes
+    out_row = w.num_seqs * w.num_heads * w.head_size * e
+    return (attention_bytes(w, local_lens) - out_row
+            + w.num_seqs * w.num_heads * (w.head_size + 2) * 4)
+
+
+def merge_bytes(w) -> int:
+    """Algorithmic bytes of the merge over the group: every rank's (m, l, o)
+    read, the output written."""
+    world = int(w.extra["cp_world"])
+    rows = w.num_seqs * w.num_heads
+    return world * rows * (w.head_size + 2) * 4 + rows * w.head_size * w.elem_bytes
+
+
+def cpu_baseline_cp(w, step, budget_s: float):
+    """Oracle rank partials (float64 NumPy, one BLAS thread) over the first
+    sequences of the rank's share, until about ``budget_s`` of CPU work."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import paged_attention_partials
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    tables = step.tables_host
+    lens = step.local_lens_host
+    q = host(step.query)
+    per_seq = []
+    for s in range(w.num_seqs):
+        used = np.unique(tables[s][tables[s] >= 0])
+        idx = torch.from_numpy(used.astype(np.int64)).to(step.key_cache.device)
+        remap = np.full(w.num_blocks, -1, dtype=np.int64)
+        remap[used] = np.arange(used.size)
+        row = np.where(tables[s:s + 1] >= 0, remap[np.maximum(tables[s:s + 1], 0)], -1)
+        per_seq.append((host(step.key_cache.index_select(0, idx)),
+                        host(step.value_cache.index_select(0, idx)), row))
+        if len(per_seq) >= 4:
+            break  # a few sequences are plenty for a bounded sample
+    done_tokens, done_seqs, t_used = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s:
+            for s, (kc, vc, row) in enumerate(per_seq):
+                t0 = time.perf_counter()
+                paged_attention_partials(q[s:s + 1], kc, vc, row, lens[s:s + 1], w.scale,
+                                         w.dtype)
+                t_used += time.perf_counter() - t0
+                done_tokens += int(lens[s])
+                done_seqs += 1
+                if t_used >= budget_s:
+                    break
+    return {"value": done_tokens / t_used, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_seqs} rank-partial passes over the first {len(per_seq)} of "
+                      f"{w.num_seqs} sequences of the rank's share ({done_tokens} KV tokens, "
+                      f"all {w.num_heads} heads), float64 NumPy, 1 BLAS thread, "
+                      f"{t_used:.1f} s"}
+
+
+def main_cp(args, w):
+    """One GPU's share of a context-parallel decode step: this rank's slot
+    mapping, scatter and partials, then the merge over the group's gathered
+    partials (the other ranks' slices are filled once, before timing, by the
+    same GPU playing those ranks; the all-gather itself is not timed)."""
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_123_amd import ops
+    from paged_kv_cache_123_amd.cp_step import CPRankStep, alloc_gathered
+
+    world, I = int(w.extra["cp_world"]), int(w.extra["cp_interleave"])
+    part = w.partition_size if args.partition_size is None else args.partition_size
+    vals = W.make_cp_values(w, "cuda")
+    g = alloc_gathered(world, w.num_seqs, w.num_heads, w.head_size, "cuda")
+    steps = []
+    for r in range(world):
+        v = {"key_cache": vals["key_caches"][r], "value_cache": vals["value_caches"][r],
+             "query": vals["query"], "new_key": vals["new_key"], "new_value": vals["new_value"]}
+        steps.append(CPRankStep(w.num_blocks, w.block_size, world, r, I, w.free_order,
+                                w.prefill, w.step, v, w.scale, part, gathered=g))
+    # the timed rank: the largest share, then the most new tokens written
+    lens = steps[0].context_lens_host
+    before = lens - np.bincount([s for s, _ in w.step], weights=[n for _, n in w.step],
+                                minlength=len(lens)).astype(np.int32)
+    def load(r):
+        got = ops.cp_local_context_lens(before, w.block_size, world, r, I)
+        return (int(steps[r].local_lens_host.sum()),
+                int((steps[r].local_lens_host - got).sum()))
+    rank = max(range(world), key=load)
+    for r in range(world):
+        if r != rank:
+            steps[r].run(merge=False)
+    st = steps[rank]
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    a_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    a_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        st.slot_mapping_kernel()
+        st.scatter()
+        a_start[i].record(stream)
+        st.partials()
+        a_end[i].record(stream)
+        st.merge()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in zip(a_start, a_end)]
+    attn_avg_ms = float(np.mean(attn_ms))
+    local_tokens = int(st.local_lens_host.sum())
+    pbytes = partials_bytes(w, st.local_lens_host)
+    achieved = pbytes / (attn_avg_ms * 1e-3) / 1e9
+    step_b = pbytes + merge_bytes(w) + 20 * st.num_tokens + 4 * w.num_kv_heads * w.head_size \
+        * w.elem_bytes * int(load(rank)[1])
+    result = {
+        "metric": METRIC,
+        "value": local_tokens / (ms_per_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "context_parallel_world": world,
+            "interleave": I,
+            "rank": rank,
+            "num_seqs": w.num_seqs,
+            "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_size": w.head_size,
+            "block_size": w.block_size,
+            "kv_tokens": local_tokens,
+            "kv_tokens_whole_group": int(lens.sum()),
+            "max_context_len": int(st.max_local_len),
+            "num_blocks": w.num_blocks,
+            "partition_size": part,
+            "attention_kernel": args.kernel,
+        },
+        "step_hbm_gbps": step_b / (ms_per_step * 1e-3) / 1e9,
+        "attention_ms": {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),
+                         "p90": float(np.percentile(attn_ms, 90))},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": ("paged_decode_mfma_kernel" if (args.kernel == "mfma" or (
+                args.kernel == "auto" and w.num_heads > w.num_kv_heads)) else "paged_decode_kernel")
+                      + " + merge_kernel (rank partials)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": pmc_traffic(w.name, pbytes),
+            "algorithmic_bytes_per_launch": pbytes,
+        },
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_read_reference:
+        ref = read_reference()
+        result["read_reference_gbps"] = ref
+        result["roofline"]["frac_of_random_4k_read"] = achieved / max(ref["random_4k"],
+                                                                      ref["random_4k_nt"])
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_cp(w, st, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +426,10 @@ def main():
         return
     ops.set_decode_kernel(args.kernel)
     w = W.make(args.workload)
+    if w.extra.get("cp_world"):
+        print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
+        main_cp(args, w)
+        return
     part = w.partition_size if args.partition_size is None else args.partition_size
     print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
     vals = W.make_values(w, "cuda")
@@ -322,7 +512,7 @@ def main():
             "bound": "hbm",
             "kernel": ("paged_decode_mfma_kernel" if (args.kernel == "mfma" or (
                 args.kernel == "auto" and w.num_heads > w.num_kv_heads)) else "paged_decode_kernel")
-                      + (" + split_reduce_kernel" if part else "")
+                      + (" + merge_kernel" if part else "")
                       + (" (one-launch step: copy-on-write + scatter + attention)" if fused
                          else ""),
             "achieved": achieved,

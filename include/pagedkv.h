@@ -80,6 +80,44 @@ int32_t pa_compute_slot_mapping(const int32_t* query_start_loc, const int64_t* p
                                 int32_t block_size, int64_t* slot_mapping, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Context-parallel slot mapping.  [CSDN] section 2.3, the same kernel with a
+ * context-parallel world of cp_world ranks: the ranks share one block table
+ * whose entry j names a virtual block of B * cp_world positions
+ * [j*B*cp_world, (j+1)*B*cp_world).  Offset o inside it is stored by rank
+ * (o / interleave) % cp_world, in that rank's own cache, in the physical
+ * block with the same number, at local offset
+ * (o / (cp_world * interleave)) * interleave + o % interleave.  This call
+ * gives rank cp_rank's slot for every scheduled token and -1 for the tokens
+ * other ranks store, so pa_reshape_and_cache on the rank's cache writes only
+ * its own tokens.  A rank's tokens fill its blocks in position order, so its
+ * share of a sequence is an ordinary paged sequence over the same table,
+ * pa_cp_local_context_lens tokens long.
+ *
+ *   Arguments as pa_compute_slot_mapping, plus
+ *   cp_world     ranks, >= 1 (1 gives pa_compute_slot_mapping's result)
+ *   cp_rank      this rank, 0 <= cp_rank < cp_world
+ *   interleave   run length dealt to one rank at a time; must divide
+ *                block_size (1: ranks alternate token by token; block_size:
+ *                each rank takes B consecutive positions in turn)
+ * Errors: as pa_compute_slot_mapping, plus PA_EINVAL for a bad cp_world,
+ * cp_rank or interleave.
+ * ---------------------------------------------------------------------- */
+int32_t pa_compute_slot_mapping_cp(const int32_t* query_start_loc, const int64_t* positions,
+                                   const int32_t* block_tables, int64_t bt_stride,
+                                   int32_t num_reqs, int64_t num_tokens, int64_t max_num_tokens,
+                                   int32_t block_size, int32_t cp_world, int32_t cp_rank,
+                                   int32_t interleave, int64_t* slot_mapping, void* stream);
+
+/* Host only: how many of the first context_lens[s] positions of each sequence
+ * rank cp_rank stores under the mapping above (the rank-local context length
+ * its attention call takes).  context_lens, local_lens: host int32
+ * [num_seqs].  Errors: PA_EINVAL for null pointers, num_seqs < 0,
+ * block_size < 1, a bad cp_world / cp_rank / interleave, a negative length. */
+int32_t pa_cp_local_context_lens(const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t block_size, int32_t cp_world, int32_t cp_rank,
+                                 int32_t interleave, int32_t* local_lens);
+
+/* ------------------------------------------------------------------------
  * Cache scatter.  [VLLBC] walk-through of paper section 4.2 and [PUFANYI]
  * "按 Block 分配": each new token's key and value rows are stored at its
  * slot, filling the tail block.  Bit copy, no arithmetic.
@@ -195,8 +233,11 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
  * order so that neighbouring sequences, e.g. forks sharing a prompt, stay
  * together.  items: host int32 [capacity][2]; *num_items receives the
  * item count.  items == NULL only queries the count.  PA_EINVAL for a null
- * context_lens/num_items, num_seqs < 1, a length < 1, partition_size < 0, or
- * a capacity below the count.
+ * context_lens/num_items, num_seqs < 1, a negative length, a length of 0
+ * with partition_size == 0, partition_size < 0, or a capacity below the
+ * count.  With partition_size > 0 a sequence of length 0 (an empty
+ * rank-local share under context parallelism) has no item; the split
+ * attention output of such a sequence is 0.
  *
  * pa_paged_attention_decode_planned: attention driven by such a list (copied
  * to the device by the caller: work_items = device int32 [num_work_items][2]).
@@ -358,6 +399,58 @@ int32_t pa_pool_ref(const pa_pool* pool, int32_t block);
 int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap);
 /* Number of copy-on-write copies performed since creation. */
 int64_t pa_pool_num_cow(const pa_pool* pool);
+
+/* ------------------------------------------------------------------------
+ * Attention partials and their merge (context parallelism, [CSDN] section
+ * 2.3).  Each rank attends over the tokens it stores and keeps, per
+ * (sequence, query head), m = max of the scaled scores x_t (natural log
+ * domain), l = sum exp(x_t - m) and o = sum exp(x_t - m) v_t / l; gathering
+ * the ranks' (m, l, o) and merging them with M = max m_r,
+ * a_r = l_r exp(m_r - M), out = sum a_r o_r / sum a_r gives attention over
+ * the whole context (the split-K merge over ranks instead of partitions).
+ * The exchange between ranks is the caller's (an all-gather of
+ * head_size + 2 floats per (sequence, query head)).
+ *
+ * pa_paged_attention_partials: the rank-local (m, l, o), fp32.
+ *   max_logits, exp_sums  device float [num_seqs][num_heads] (output)
+ *   partial_out           device float [num_seqs][num_heads][head_size]
+ *                         (output), 16-byte aligned
+ *   context_lens          device int32 [num_seqs], rank-local lengths; 0 is
+ *                         allowed and gives m = -inf, l = 0, o = 0
+ *   max_context_len       >= 0, at least every context_lens entry
+ *   partition_size        > 0, as pa_paged_attention_decode_split; the
+ *                         partitions are merged inside the call
+ *   work_items            NULL (one workgroup per (partition, KV head,
+ *                         sequence)) or a pa_decode_plan list for this
+ *                         partition_size
+ *   workspace             as pa_paged_attention_decode_split for
+ *                         max(max_context_len, 1); may be NULL when
+ *                         max_context_len == 0
+ *   Other arguments as pa_paged_attention_decode_planned.
+ *
+ * pa_merge_attention_partials: out [num_seqs][num_heads][head_size] in the
+ * storage dtype from num_parts gathered sets, rank-major:
+ *   max_logits, exp_sums  device float [num_parts][num_seqs][num_heads]
+ *   partial_out           device float [num_parts][num_seqs][num_heads][head_size]
+ * Parts with l = 0 carry no weight; a row no part has a key for is 0.
+ * Errors: PA_EINVAL for null pointers, num_parts < 1, num_seqs outside
+ * [1, 65535], num_heads < 1, head_size not 64 or 128, an unknown dtype.
+ * ---------------------------------------------------------------------- */
+int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* partial_out,
+                                    const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    int64_t bt_stride, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size,
+                                    int32_t max_context_len, float scale, int32_t dtype,
+                                    int32_t partition_size, const int32_t* work_items,
+                                    int64_t num_work_items, const int32_t* shared_prefix_blocks,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t pa_merge_attention_partials(void* out, const float* max_logits, const float* exp_sums,
+                                    const float* partial_out, int32_t num_parts,
+                                    int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                    int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostic (not part of the decode path): reads num_blocks whole 4 KiB

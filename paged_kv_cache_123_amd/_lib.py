@@ -28,6 +28,14 @@ SIGNATURES = {
     "pa_status_string": (_c.c_char_p, [_i32]),
     "pa_last_error": (_c.c_char_p, []),
     "pa_compute_slot_mapping": (_i32, [_vp, _vp, _vp, _i64, _i32, _i64, _i64, _i32, _vp, _vp]),
+    "pa_compute_slot_mapping_cp": (_i32, [_vp, _vp, _vp, _i64, _i32, _i64, _i64, _i32, _i32,
+                                          _i32, _i32, _vp, _vp]),
+    "pa_cp_local_context_lens": (_i32, [_pi32, _i32, _i32, _i32, _i32, _i32, _pi32]),
+    "pa_paged_attention_partials": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
+                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                           _i64, _vp, _vp, _sz, _vp]),
+    "pa_merge_attention_partials": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                           _vp]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                     _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),

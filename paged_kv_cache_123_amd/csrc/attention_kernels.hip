@@ -279,17 +279,19 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   }
 }
 
-// Merge of the partitions of one (sequence, head): M = max m_p,
-// a_p = l_p exp(m_p - M), out = sum a_p o_p / sum a_p, summed in partition
-// order.  One thread per output dimension; the partition weights are computed
-// once per chunk into LDS, and the o_p loads are unrolled so that eight of
-// them are in flight per thread.
+// Merge of the parts of one (row, head): M = max m_p, a_p = l_p exp(m_p - M),
+// out = sum a_p o_p / sum a_p, summed in part order.  The parts are the
+// partitions of a split launch, or the ranks of a context-parallel group.
+// One thread per output dimension; the part weights are computed once per
+// chunk into LDS, and the o_p loads are unrolled so that eight of them are in
+// flight per thread.  A part with l_p = 0 (no visible key) has weight 0; a row
+// with no key at all merges to m = -inf, l = 0, o = 0.
 template <int DT, int D>
-__global__ __launch_bounds__(D) void split_reduce_kernel(
-    void* __restrict__ out, const int32_t* __restrict__ context_lens, int32_t num_heads,
-    int32_t partition_size, int32_t num_partitions, const float* __restrict__ ws_max,
-    const float* __restrict__ ws_sum, const float* __restrict__ ws_out,
-    const int32_t* __restrict__ q_start) {
+__global__ __launch_bounds__(D) void merge_kernel(MergeDst dst, PartView src,
+                                                  const int32_t* __restrict__ context_lens,
+                                                  int32_t num_heads, int32_t partition_size,
+                                                  int32_t num_parts,
+                                                  const int32_t* __restrict__ q_start) {
   constexpr int kChunk = 256;
   constexpr int NWV = D / 64;
   __shared__ float sw[kChunk];
@@ -297,19 +299,21 @@ __global__ __launch_bounds__(D) void split_reduce_kernel(
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
-  const int L = context_lens[s];
-  const int np = min((L + partition_size - 1) / partition_size, num_partitions);
+  // split launches: only the partitions below the sequence's length exist
+  const int np = context_lens
+                     ? min((context_lens[s] + partition_size - 1) / partition_size, num_parts)
+                     : num_parts;
   // one output row per new token of the sequence (one row when q_start is null)
   const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
   for (int qi = 0; qi < qlen; ++qi) {
   const int64_t row = (qrow0 + qi) * num_heads + h;
-  const float* mrow = ws_max + row * num_partitions;
-  const float* lrow = ws_sum + row * num_partitions;
-  const float* orow = ws_out + row * num_partitions * D;
+  const float* mrow = src.m + row * src.row_ml;
+  const float* lrow = src.l + row * src.row_ml;
+  const float* orow = src.o + row * src.row_o + d;
 
   float mx = -INFINITY;
-  for (int i = d; i < np; i += D) mx = fmaxf(mx, mrow[i]);
+  for (int i = d; i < np; i += D) mx = fmaxf(mx, mrow[i * src.part_ml]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if ((d & 63) == 0) red[d >> 6] = mx;
@@ -317,27 +321,39 @@ __global__ __launch_bounds__(D) void split_reduce_kernel(
   float M = red[0];
 #pragma unroll
   for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[w]);
+  const float Ms = M == -INFINITY ? 0.0f : M;
 
   float a = 0.0f, wsum = 0.0f;
   for (int c0 = 0; c0 < np; c0 += kChunk) {
     const int cn = min(kChunk, np - c0);
     __syncthreads();  // sw is rewritten
-    for (int i = d; i < cn; i += D)
-      sw[i] = lrow[c0 + i] * __builtin_amdgcn_exp2f((mrow[c0 + i] - M) * kLog2e);
+    for (int i = d; i < cn; i += D) {
+      const int64_t k = static_cast<int64_t>(c0 + i) * src.part_ml;
+      sw[i] = lrow[k] * __builtin_amdgcn_exp2f((mrow[k] - Ms) * kLog2e);
+    }
     __syncthreads();
-    const float* o = orow + static_cast<int64_t>(c0) * D + d;
+    const float* o = orow + static_cast<int64_t>(c0) * src.part_o;
     int i = 0;
     for (; i + 8 <= cn; i += 8) {
       float v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = o[static_cast<int64_t>(i + k) * D];
+      for (int k = 0; k < 8; ++k) v[k] = o[static_cast<int64_t>(i + k) * src.part_o];
 #pragma unroll
       for (int k = 0; k < 8; ++k) a = fmaf(sw[i + k], v[k], a);
     }
-    for (; i < cn; ++i) a = fmaf(sw[i], o[static_cast<int64_t>(i) * D], a);
+    for (; i < cn; ++i) a = fmaf(sw[i], o[static_cast<int64_t>(i) * src.part_o], a);
     for (int k = 0; k < cn; ++k) wsum += sw[k];
   }
-  St<DT>::store(out, row * D + d, a / wsum);
+  const float merged = wsum > 0.0f ? a / wsum : 0.0f;
+  if (dst.out) {
+    St<DT>::store(dst.out, row * D + d, merged);
+  } else {
+    dst.o[row * D + d] = merged;
+    if (d == 0) {
+      dst.m[row] = M;
+      dst.l[row] = wsum;
+    }
+  }
   __syncthreads();  // red and sw are reused by the next row
   }
 }
@@ -397,11 +413,37 @@ hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <int DT, int D>
-hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((split_reduce_kernel<DT, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
-                     stream, a.out, a.context_lens, a.num_heads, a.partition_size,
-                     a.num_partitions, a.ws_max, a.ws_sum, a.ws_out, a.q_start);
+hipError_t launch_merge_t(const MergeDst& dst, const PartView& src, const int32_t* context_lens,
+                          int32_t num_rows, int32_t num_heads, int32_t partition_size,
+                          int32_t num_parts, const int32_t* q_start, hipStream_t stream) {
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(num_heads, num_rows), dim3(D), 0, stream, dst,
+                     src, context_lens, num_heads, partition_size, num_parts, q_start);
   return hipGetLastError();
+}
+
+hipError_t launch_merge(int32_t dtype, int32_t head_size, const MergeDst& dst,
+                        const PartView& src, const int32_t* context_lens, int32_t num_rows,
+                        int32_t num_heads, int32_t partition_size, int32_t num_parts,
+                        const int32_t* q_start, hipStream_t stream) {
+  const bool d64 = head_size == 64;
+#define PA_MERGE(DT)                                                                        \
+  return d64 ? launch_merge_t<DT, 64>(dst, src, context_lens, num_rows, num_heads,          \
+                                      partition_size, num_parts, q_start, stream)           \
+             : launch_merge_t<DT, 128>(dst, src, context_lens, num_rows, num_heads,         \
+                                       partition_size, num_parts, q_start, stream)
+  switch (dtype) {
+    case PA_F32: PA_MERGE(PA_F32);
+    case PA_F16: PA_MERGE(PA_F16);
+    case PA_BF16: PA_MERGE(PA_BF16);
+    default: return hipErrorInvalidValue;
+  }
+#undef PA_MERGE
+}
+
+// the split workspace as parts: [row][NP] for m and l, [row][NP][D] for o
+PartView split_parts(const DecodeArgs& a) {
+  return PartView{a.ws_max, a.ws_sum, a.ws_out, 1, a.num_partitions,
+                  a.head_size, static_cast<int64_t>(a.num_partitions) * a.head_size};
 }
 
 }  // namespace
@@ -446,17 +488,25 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream) {
-  const bool d64 = a.head_size == 64;
-  switch (a.dtype) {
-    case PA_F32:
-      return d64 ? launch_reduce_t<PA_F32, 64>(a, stream) : launch_reduce_t<PA_F32, 128>(a, stream);
-    case PA_F16:
-      return d64 ? launch_reduce_t<PA_F16, 64>(a, stream) : launch_reduce_t<PA_F16, 128>(a, stream);
-    case PA_BF16:
-      return d64 ? launch_reduce_t<PA_BF16, 64>(a, stream)
-                 : launch_reduce_t<PA_BF16, 128>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_merge(a.dtype, a.head_size, MergeDst{a.out, nullptr, nullptr, nullptr},
+                      split_parts(a), a.context_lens, a.num_seqs, a.num_heads, a.partition_size,
+                      a.num_partitions, a.q_start, stream);
+}
+
+hipError_t launch_split_reduce_partials(const DecodeArgs& a, float* m, float* l, float* o,
+                                        hipStream_t stream) {
+  return launch_merge(a.dtype, a.head_size, MergeDst{nullptr, m, l, o}, split_parts(a),
+                      a.context_lens, a.num_seqs, a.num_heads, a.partition_size,
+                      a.num_partitions, a.q_start, stream);
+}
+
+hipError_t launch_merge_ranks(void* out, const float* m, const float* l, const float* o,
+                              int32_t num_parts, int32_t num_seqs, int32_t num_heads,
+                              int32_t head_size, int32_t dtype, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
+  return launch_merge(dtype, head_size, MergeDst{out, nullptr, nullptr, nullptr},
+                      PartView{m, l, o, rows, 1, rows * head_size, head_size}, nullptr,
+                      num_seqs, num_heads, 1, num_parts, nullptr, stream);
 }
 
 }  // namespace pa

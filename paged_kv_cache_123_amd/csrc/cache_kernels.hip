@@ -20,19 +20,33 @@ namespace {
 // One workgroup per request: its tokens [qsl[r], qsl[r+1]) get
 // slot = table[r][pos / B] * B + pos % B.  Workgroups past num_reqs write the
 // padding entries [num_tokens, max_num_tokens) with -1.
+//
+// Context parallelism ([CSDN] section 2.3): with cp_world ranks a table entry
+// names a virtual block of B * cp_world positions.  Offset o inside it goes
+// to rank (o / interleave) % cp_world, at local offset
+// (o / (cp_world * interleave)) * interleave + o % interleave of that rank's
+// block with the same number; this rank writes -1 for tokens another rank
+// stores.  cp_world = 1, interleave = 1 is the plain mapping above.
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     const int32_t* __restrict__ qsl, const int64_t* __restrict__ positions,
     const int32_t* __restrict__ block_tables, int64_t bt_stride, int32_t num_reqs,
-    int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
-    int64_t* __restrict__ slot_mapping) {
+    int64_t num_tokens, int64_t max_num_tokens, int32_t block_size, int32_t cp_world,
+    int32_t cp_rank, int32_t interleave, int64_t* __restrict__ slot_mapping) {
   const int64_t r = blockIdx.x;
   if (r < num_reqs) {
     const int64_t begin = qsl[r], end = qsl[r + 1];
     const int32_t* row = block_tables + r * bt_stride;
+    const int64_t vbs = static_cast<int64_t>(block_size) * cp_world;
+    const int64_t stripe = static_cast<int64_t>(cp_world) * interleave;
     for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
       const int64_t pos = positions[i];
-      const int64_t blk = row[pos / block_size];
-      slot_mapping[i] = blk * block_size + pos % block_size;
+      const int64_t vb = pos / vbs;
+      const int64_t off = pos - vb * vbs;
+      int64_t slot = -1;
+      if ((off / interleave) % cp_world == cp_rank)
+        slot = static_cast<int64_t>(row[vb]) * block_size + (off / stripe) * interleave +
+               off % interleave;
+      slot_mapping[i] = slot;
     }
     return;
   }
@@ -90,13 +104,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
                                const int32_t* block_tables, int64_t bt_stride, int32_t num_reqs,
                                int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
+                               int32_t cp_world, int32_t cp_rank, int32_t interleave,
                                int64_t* slot_mapping, hipStream_t stream) {
   const int64_t pad = max_num_tokens - num_tokens;
   const int64_t pad_groups = (pad + 4095) / 4096;
   const int64_t grid = num_reqs + pad_groups;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, stream,
                      query_start_loc, positions, block_tables, bt_stride, num_reqs, num_tokens,
-                     max_num_tokens, block_size, slot_mapping);
+                     max_num_tokens, block_size, cp_world, cp_rank, interleave, slot_mapping);
   return hipGetLastError();
 }
 

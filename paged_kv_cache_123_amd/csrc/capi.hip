@@ -93,9 +93,31 @@ int32_t pa_compute_slot_mapping(const int32_t* query_start_loc, const int64_t* p
       block_size < 1)
     return fail(PA_EINVAL, "pa_compute_slot_mapping: bad sizes");
   return launched(pa::launch_slot_mapping(query_start_loc, positions, block_tables, bt_stride,
-                                          num_reqs, num_tokens, max_num_tokens, block_size,
-                                          slot_mapping, static_cast<hipStream_t>(stream)),
+                                          num_reqs, num_tokens, max_num_tokens, block_size, 1, 0,
+                                          1, slot_mapping, static_cast<hipStream_t>(stream)),
                   "pa_compute_slot_mapping");
+}
+
+int32_t pa_compute_slot_mapping_cp(const int32_t* query_start_loc, const int64_t* positions,
+                                   const int32_t* block_tables, int64_t bt_stride,
+                                   int32_t num_reqs, int64_t num_tokens, int64_t max_num_tokens,
+                                   int32_t block_size, int32_t cp_world, int32_t cp_rank,
+                                   int32_t interleave, int64_t* slot_mapping, void* stream) {
+  const char* who = "pa_compute_slot_mapping_cp";
+  if (!query_start_loc || !block_tables || !slot_mapping || (!positions && num_tokens > 0))
+    return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: NULL pointer");
+  if (num_reqs < 1 || num_tokens < 0 || max_num_tokens < num_tokens || bt_stride < 1 ||
+      block_size < 1)
+    return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: bad sizes");
+  if (cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world)
+    return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: need 0 <= cp_rank < cp_world");
+  if (interleave < 1 || block_size % interleave != 0)
+    return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: interleave must divide block_size");
+  return launched(pa::launch_slot_mapping(query_start_loc, positions, block_tables, bt_stride,
+                                          num_reqs, num_tokens, max_num_tokens, block_size,
+                                          cp_world, cp_rank, interleave, slot_mapping,
+                                          static_cast<hipStream_t>(stream)),
+                  who);
 }
 
 int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t key_stride,
@@ -386,6 +408,84 @@ int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_c
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_multi (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_multi (reduce)");
+}
+
+int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* partial_out,
+                                    const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    int64_t bt_stride, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size,
+                                    int32_t max_context_len, float scale, int32_t dtype,
+                                    int32_t partition_size, const int32_t* work_items,
+                                    int64_t num_work_items, const int32_t* shared_prefix_blocks,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pa_paged_attention_partials";
+  if (max_context_len < 0) return fail(PA_EINVAL, "pa_paged_attention_partials: bad sizes");
+  const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+  int32_t st = check_decode(who, partial_out, query, key_cache, value_cache, block_tables,
+                            bt_stride, context_lens, num_seqs, num_heads, num_kv_heads,
+                            head_size, block_size, ctx, dtype);
+  if (st != PA_OK) return st;
+  if (!max_logits || !exp_sums)
+    return fail(PA_EINVAL, "pa_paged_attention_partials: NULL max_logits or exp_sums");
+  if (num_seqs > 65535) return fail(PA_EINVAL, "pa_paged_attention_partials: num_seqs > 65535");
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_partials: partition_size must be a multiple of 16 and of "
+                "block_size, at most 4096");
+  if (work_items && (num_work_items < 0 ||
+                     num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads))
+    return fail(PA_EINVAL, "pa_paged_attention_partials: bad work list");
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::DecodeArgs a{nullptr, query, key_cache, value_cache, block_tables, bt_stride,
+                   context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                   partition_size, np, scale, dtype, nullptr, nullptr, nullptr, work_items,
+                   work_items ? num_work_items : 0};
+  a.shared_blocks = shared_prefix_blocks;
+  const bool any_work = np > 0 && (!work_items || num_work_items > 0);
+  if (any_work) {
+    const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size,
+                                                 max_context_len, partition_size);
+    if (!workspace || workspace_bytes < need ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(PA_EINVAL,
+                  "pa_paged_attention_partials: workspace missing, too small or misaligned");
+    const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_max = reinterpret_cast<float*>(ws);
+    a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+    a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+    st = launched(pa::launch_decode(a, s), "pa_paged_attention_partials (partition)");
+    if (st != PA_OK) return st;
+  } else {
+    // no key anywhere: the merge reads no part and writes (-inf, 0, 0)
+    a.num_partitions = 0;
+  }
+  return launched(pa::launch_split_reduce_partials(a, max_logits, exp_sums, partial_out, s),
+                  "pa_paged_attention_partials (merge)");
+}
+
+int32_t pa_merge_attention_partials(void* out, const float* max_logits, const float* exp_sums,
+                                    const float* partial_out, int32_t num_parts,
+                                    int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                    int32_t dtype, void* stream) {
+  const int32_t eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PA_EINVAL, "pa_merge_attention_partials: unknown dtype");
+  if (!out || !max_logits || !exp_sums || !partial_out)
+    return fail(PA_EINVAL, "pa_merge_attention_partials: NULL pointer");
+  if (num_parts < 1 || num_seqs < 1 || num_seqs > 65535 || num_heads < 1)
+    return fail(PA_EINVAL, "pa_merge_attention_partials: bad sizes");
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_EINVAL, "pa_merge_attention_partials: head_size must be 64 or 128");
+  if (reinterpret_cast<uintptr_t>(out) % eb != 0)
+    return fail(PA_EINVAL, "pa_merge_attention_partials: out not aligned to its element size");
+  return launched(pa::launch_merge_ranks(out, max_logits, exp_sums, partial_out, num_parts,
+                                         num_seqs, num_heads, head_size, dtype,
+                                         static_cast<hipStream_t>(stream)),
+                  "pa_merge_attention_partials");
 }
 
 }  // extern "C"

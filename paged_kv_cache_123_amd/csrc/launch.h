@@ -11,9 +11,11 @@
 
 namespace pa {
 
+// cp_world = 1, cp_rank = 0, interleave = 1: the plain mapping.
 hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
                                const int32_t* block_tables, int64_t bt_stride, int32_t num_reqs,
                                int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
+                               int32_t cp_world, int32_t cp_rank, int32_t interleave,
                                int64_t* slot_mapping, hipStream_t stream);
 
 // elem_bytes: storage element size; row_elems = num_kv_heads * head_size.
@@ -71,5 +73,33 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // mode: 0 automatic, 1 vector kernel, 2 matrix-core kernel; returns the previous mode.
 int set_decode_kernel(int mode);
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream);
+
+// (m, l, o) of several parts per row (split partitions, or the ranks of a
+// context-parallel group), with element strides between parts and rows.
+struct PartView {
+  const float* m;
+  const float* l;
+  const float* o;
+  int64_t part_ml, row_ml;  // strides of m and l
+  int64_t part_o, row_o;    // strides of o, in floats
+};
+// Destination of a merge: the storage-dtype output, or (out == nullptr) the
+// merged (m, l, o) in fp32, rows [rows][H] and [rows][H][D].
+struct MergeDst {
+  void* out;
+  float* m;
+  float* l;
+  float* o;
+};
+
+// The partitions of a split launch merged into one (m, l, o) per row instead
+// of the final output.
+hipError_t launch_split_reduce_partials(const DecodeArgs& a, float* m, float* l, float* o,
+                                        hipStream_t stream);
+// Rank-major parts ([num_parts][num_seqs][num_heads] and [..][head_size])
+// merged into the storage-dtype output [num_seqs][num_heads][head_size].
+hipError_t launch_merge_ranks(void* out, const float* m, const float* l, const float* o,
+                              int32_t num_parts, int32_t num_seqs, int32_t num_heads,
+                              int32_t head_size, int32_t dtype, hipStream_t stream);
 
 }  // namespace pa

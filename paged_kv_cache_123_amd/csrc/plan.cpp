@@ -26,11 +26,13 @@ extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
   std::vector<Item> v;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t L = context_lens[s];
-    if (L < 1) return pa::fail(PA_EINVAL, "pa_decode_plan: context length < 1");
+    if (L < 0 || (L == 0 && partition_size == 0))
+      return pa::fail(PA_EINVAL, "pa_decode_plan: context length < 1");
     if (partition_size == 0) {
       v.push_back({L, s, 0});
       continue;
     }
+    // a sequence with no token (a rank-local share can be empty) has no item
     for (int32_t p = 0; static_cast<int64_t>(p) * partition_size < L; ++p)
       v.push_back({std::min(partition_size, L - p * partition_size), s, p});
   }

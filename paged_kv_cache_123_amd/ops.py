@@ -82,6 +82,43 @@ def compute_slot_mapping(query_start_loc: torch.Tensor, positions: torch.Tensor,
         slot_mapping.data_ptr(), _stream()))
 
 
+def compute_slot_mapping_cp(query_start_loc: torch.Tensor, positions: torch.Tensor,
+                            block_tables: torch.Tensor, block_size: int,
+                            slot_mapping: torch.Tensor, num_tokens: int, cp_world: int,
+                            cp_rank: int, interleave: int = 1) -> None:
+    """Rank ``cp_rank``'s slots under context parallelism (-1 for the tokens
+    other ranks store, and for the padding tail)."""
+    _dev(query_start_loc, positions, block_tables, slot_mapping)
+    if query_start_loc.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise TypeError("query_start_loc and block_tables must be int32")
+    if positions.dtype != torch.int64 or slot_mapping.dtype != torch.int64:
+        raise TypeError("positions and slot_mapping must be int64")
+    for n, t in (("query_start_loc", query_start_loc), ("positions", positions),
+                 ("block_tables", block_tables), ("slot_mapping", slot_mapping)):
+        _contig(n, t)
+    num_reqs = query_start_loc.numel() - 1
+    if block_tables.dim() != 2 or block_tables.shape[0] < num_reqs:
+        raise ValueError("block_tables must be [>= num_reqs, width]")
+    if positions.numel() < num_tokens:
+        raise ValueError("positions shorter than num_tokens")
+    check(lib().pa_compute_slot_mapping_cp(
+        query_start_loc.data_ptr(), positions.data_ptr(), block_tables.data_ptr(),
+        block_tables.stride(0), num_reqs, num_tokens, slot_mapping.numel(), block_size,
+        cp_world, cp_rank, interleave, slot_mapping.data_ptr(), _stream()))
+
+
+def cp_local_context_lens(context_lens, block_size: int, cp_world: int, cp_rank: int,
+                          interleave: int = 1) -> np.ndarray:
+    """Host int32: how many positions of each sequence rank ``cp_rank`` stores."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    out = np.empty_like(lens)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    check(lib().pa_cp_local_context_lens(lens.ctypes.data_as(p32), lens.size, block_size,
+                                         cp_world, cp_rank, interleave,
+                                         out.ctypes.data_as(p32)))
+    return out
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                       value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
     """Store each new token's K/V rows at its slot (slots < 0 are skipped)."""
@@ -117,12 +154,13 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
                                _stream()))
 
 
-def _attn_common(out, query, key_cache, value_cache, block_tables, context_lens):
+def _attn_common(out, query, key_cache, value_cache, block_tables, context_lens,
+                 check_out_dtype=True):
     _dev(out, query, key_cache, value_cache, block_tables, context_lens)
     nb, hkv, B, D = _cache_shape(key_cache, value_cache)
     if query.dim() != 3 or query.shape[2] != D or out.shape != query.shape:
         raise ValueError("query/out must be [num_seqs, num_heads, head_size]")
-    if query.dtype != key_cache.dtype or out.dtype != key_cache.dtype:
+    if query.dtype != key_cache.dtype or (check_out_dtype and out.dtype != key_cache.dtype):
         raise TypeError("query/out must have the cache dtype")
     for n, t in (("query", query), ("out", out), ("block_tables", block_tables),
                  ("context_lens", context_lens)):
@@ -245,6 +283,66 @@ def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
         B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
         work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
         _stream()))
+
+
+def paged_attention_partials(max_logits: torch.Tensor, exp_sums: torch.Tensor,
+                             partial_out: torch.Tensor, query: torch.Tensor,
+                             key_cache: torch.Tensor, value_cache: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             scale: float, max_context_len: int, partition_size: int,
+                             workspace=None, work_items=None, shared_prefix_blocks=None) -> None:
+    """Rank-local attention partials: fp32 max_logits / exp_sums [S, H] and
+    partial_out [S, H, D] over the tokens of this rank's cache."""
+    S, H, hkv, D, B = _attn_common(partial_out, query, key_cache, value_cache, block_tables,
+                                   context_lens, check_out_dtype=False)
+    _dev(max_logits, exp_sums)
+    for n, t in (("max_logits", max_logits), ("exp_sums", exp_sums),
+                 ("partial_out", partial_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32")
+        _contig(n, t)
+    if max_logits.shape != (S, H) or exp_sums.shape != (S, H):
+        raise ValueError("max_logits and exp_sums must be [num_seqs, num_heads]")
+    items_ptr, n_items = None, 0
+    if work_items is not None:
+        _dev(work_items)
+        if work_items.dtype != torch.int32 or work_items.dim() != 2 or work_items.shape[1] != 2:
+            raise ValueError("work_items must be int32 [num_items, 2]")
+        _contig("work_items", work_items)
+        items_ptr, n_items = work_items.data_ptr() or None, work_items.shape[0]
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().pa_paged_attention_partials(
+        max_logits.data_ptr(), exp_sums.data_ptr(), partial_out.data_ptr(), query.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D, B, max_context_len,
+        scale, _dtype(key_cache), partition_size, items_ptr, n_items,
+        _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes, _stream()))
+
+
+def merge_attention_partials(out: torch.Tensor, max_logits: torch.Tensor,
+                             exp_sums: torch.Tensor, partial_out: torch.Tensor) -> None:
+    """out [S, H, D] from gathered rank partials: max_logits / exp_sums
+    [N, S, H], partial_out [N, S, H, D] (fp32)."""
+    _dev(out, max_logits, exp_sums, partial_out)
+    if partial_out.dim() != 4:
+        raise ValueError("partial_out must be [num_parts, num_seqs, num_heads, head_size]")
+    N, S, H, D = (int(x) for x in partial_out.shape)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [num_seqs, num_heads, head_size]")
+    for n, t in (("max_logits", max_logits), ("exp_sums", exp_sums),
+                 ("partial_out", partial_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32")
+        _contig(n, t)
+    if tuple(max_logits.shape) != (N, S, H) or tuple(exp_sums.shape) != (N, S, H):
+        raise ValueError("max_logits and exp_sums must be [num_parts, num_seqs, num_heads]")
+    _contig("out", out)
+    check(lib().pa_merge_attention_partials(
+        out.data_ptr(), max_logits.data_ptr(), exp_sums.data_ptr(), partial_out.data_ptr(), N, S,
+        H, D, _dtype(out), _stream()))
 
 
 def probe_read_blocks(buffer: torch.Tensor, block_order: torch.Tensor, sink: torch.Tensor,

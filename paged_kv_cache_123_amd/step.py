@@ -27,6 +27,35 @@ from . import ops
 from .host import Pool
 
 
+def replay(pool: Pool, history, appends):
+    """Run a batch's history and then the step's appends through ``pool``.
+
+    Returns (seqs, positions, query_start_loc, cow_pairs, cow_src): the batch
+    rows, the position of every new token, the row boundaries of the new
+    tokens, the (src, dst) copy-on-write pairs, and per row the source block
+    of its copy-on-write (-1 for none)."""
+    for op in history:
+        if op[0] == "add":
+            pool.add_seq(op[1])
+        elif op[0] == "append":
+            pool.append(op[1], op[2])
+        elif op[0] == "fork":
+            pool.fork(op[1], op[2])
+        else:
+            raise ValueError(f"unknown operation {op!r}")
+    seqs, positions, qsl, cow, cow_src = [], [], [0], [], []
+    for s, n in appends:
+        start = pool.seq_len(s)
+        _, pair = pool.append(s, n)
+        seqs.append(s)
+        positions.extend(range(start, start + n))
+        qsl.append(qsl[-1] + n)
+        cow_src.append(-1 if pair is None else pair[0])
+        if pair is not None:
+            cow.append(pair)
+    return seqs, positions, qsl, cow, cow_src
+
+
 class DecodeStep:
     """Allocator replay plus device tensors of one decode step.
 
@@ -42,25 +71,7 @@ class DecodeStep:
                  values: dict, scale: float, partition_size: int = 0, planned: bool = True,
                  all_queries: bool = False):
         self.pool = Pool(num_blocks, block_size, free_order)
-        for op in history:
-            if op[0] == "add":
-                self.pool.add_seq(op[1])
-            elif op[0] == "append":
-                self.pool.append(op[1], op[2])
-            elif op[0] == "fork":
-                self.pool.fork(op[1], op[2])
-            else:
-                raise ValueError(f"unknown operation {op!r}")
-        seqs, positions, qsl, cow, cow_src = [], [], [0], [], []
-        for s, n in appends:
-            start = self.pool.seq_len(s)
-            _, pair = self.pool.append(s, n)
-            seqs.append(s)
-            positions.extend(range(start, start + n))
-            qsl.append(qsl[-1] + n)
-            cow_src.append(-1 if pair is None else pair[0])
-            if pair is not None:
-                cow.append(pair)
+        seqs, positions, qsl, cow, cow_src = replay(self.pool, history, appends)
         self.seqs = seqs
         self.block_size = block_size
         width = max(self.pool.seq_num_blocks(s) for s in seqs)

@@ -7,9 +7,10 @@ from __future__ import annotations
 import numpy as np
 
 from oracle.allocator import OraclePool
-from oracle.attention import paged_attention, paged_attention_multi, paged_attention_split
+from oracle.attention import (merge_rank_partials, paged_attention, paged_attention_multi,
+                              paged_attention_partials, paged_attention_split)
 from oracle.cache_ops import copy_blocks, reshape_and_cache
-from oracle.slots import compute_slot_mapping
+from oracle.slots import compute_slot_mapping, compute_slot_mapping_cp, cp_local_length
 
 
 def to_host(t):
@@ -21,8 +22,13 @@ def to_host(t):
 
 
 class OracleStep:
+    """Under context parallelism (w.extra["cp_world"] > 1) the pool hands out
+    virtual blocks of block_size * cp_world positions shared by the ranks."""
+
     def __init__(self, w):
-        pool = OraclePool(w.num_blocks, w.block_size, w.free_order)
+        self.world = int(w.extra.get("cp_world", 1))
+        self.interleave = int(w.extra.get("cp_interleave", 1))
+        pool = OraclePool(w.num_blocks, w.block_size * self.world, w.free_order)
         for op in w.prefill:
             if op[0] == "add":
                 pool.add_seq(op[1])
@@ -75,3 +81,31 @@ class OracleStep:
     def attention_multi(self, query, kc, vc):
         return paged_attention_multi(query, kc, vc, self.tables, self.context_lens,
                                      self.query_start_loc, self.w.scale, self.w.dtype)
+
+    # ---- context parallelism: one rank's share ----------------------------
+    def cp_slot_mapping(self, rank, max_num_tokens=None):
+        T = self.query_start_loc[-1]
+        return compute_slot_mapping_cp(self.query_start_loc, self.positions, self.tables,
+                                       self.w.block_size, max_num_tokens or T, self.world, rank,
+                                       self.interleave)
+
+    def cp_local_lens(self, rank):
+        return np.array([cp_local_length(int(L), self.w.block_size, self.world, rank,
+                                         self.interleave) for L in self.context_lens])
+
+    def apply_cp_scatter(self, rank, kc, vc, new_key, new_value):
+        reshape_and_cache(kc, vc, new_key, new_value, self.cp_slot_mapping(rank),
+                          self.w.block_size)
+
+    def cp_partials(self, rank, query, kc, vc, tables=None, rows=None):
+        """(m, l, o) of the rank's share; ``rows`` restricts it to some sequences
+        (the other rows are left empty)."""
+        t = self.tables if tables is None else tables
+        lens = self.cp_local_lens(rank)
+        if rows is not None:
+            lens = np.where(np.isin(np.arange(len(lens)), rows), lens, 0)
+        return paged_attention_partials(query, kc, vc, t, lens, self.w.scale, self.w.dtype)
+
+    @staticmethod
+    def cp_merge(m, l, o):
+        return merge_rank_partials(np.asarray(m), np.asarray(l), np.asarray(o))

@@ -33,8 +33,14 @@ def test_plan_single_pass_orders_sequences_by_length():
     assert items == [[3, 0], [1, 0], [4, 0], [0, 0], [2, 0]]
 
 
-@pytest.mark.parametrize("lens,P", [([3, 0], 16), ([3], -1)])
+@pytest.mark.parametrize("lens,P", [([3, 0], 0), ([3, -1], 16), ([3], -1)])
 def test_plan_rejects_bad_input(lens, P):
     with pytest.raises(PagedKVError) as e:
         decode_plan(lens, P)
     assert e.value.status == PA_EINVAL
+
+
+def test_plan_gives_no_item_to_an_empty_split_sequence():
+    # a rank-local share can be empty under context parallelism
+    items = decode_plan([40, 0, 17], 16).tolist()
+    assert {tuple(x) for x in items} == {(0, 0), (0, 1), (0, 2), (2, 0), (2, 1)}

@@ -225,6 +225,42 @@ def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
     return w
 
 
+def cp_decode(name, seed, lens, *, dtype, H, Hkv, D, B, world, interleave, partition_size,
+              sigma=1.0, slack=1.0, notes=""):
+    """A decode batch spread over a context-parallel group of ``world`` ranks.
+    The allocator works in virtual blocks of B * world positions shared by
+    the ranks; ``num_blocks`` is the size of each rank's pool (every rank
+    holds B slots of each virtual block) and ``block_size`` the physical B."""
+    lens = [int(L) for L in lens]
+    nb = math.ceil(slack * _blocks_for(lens, B * world)) + 2
+    w = _decode_batch(name, seed, lens, dtype=dtype, H=H, Hkv=Hkv, D=D, B=B, num_blocks=nb,
+                      sigma=sigma, partition_size=partition_size, notes=notes)
+    w.extra = {"cp_world": int(world), "cp_interleave": int(interleave)}
+    return w
+
+
+def cp_prefill(name, seed, lens, *, dtype, H, Hkv, D, B, world, interleave, partition_size,
+               sigma=1.0):
+    """Context-parallel parity case: the step writes every token of every
+    sequence (a whole prompt, spread over the ranks by their slot mappings)
+    and the last token of each sequence is the query."""
+    lens = [int(L) for L in lens]
+    w = cp_decode(name, seed, lens, dtype=dtype, H=H, Hkv=Hkv, D=D, B=B, world=world,
+                  interleave=interleave, partition_size=partition_size, sigma=sigma)
+    w.prefill = [("add", s) for s in range(len(lens))]
+    w.step = [(s, L) for s, L in enumerate(lens)]
+    return w
+
+
+def long_context_cp8_bf16(num_seqs=32, context_len=32768):
+    """The long-context batch spread over 8 context-parallel ranks (one token
+    at a time in turn): one GPU's share is 32 x 4096 tokens."""
+    return cp_decode("long_context_cp8_bf16", 5, [context_len] * num_seqs, dtype="bf16", H=32,
+                     Hkv=32, D=128, B=64, world=8, interleave=1, partition_size=512, slack=1.05,
+                     notes=f"{num_seqs} x {context_len} tokens over 8 context-parallel ranks "
+                           "(interleave 1), 32x128 MHA bf16, B=64, partitions of 512")
+
+
 CONFIGS = {
     "tiny_fp32": tiny_fp32,
     "llama7b_fp16": llama7b_fp16,
@@ -233,6 +269,7 @@ CONFIGS = {
     "long_context_bf16": long_context_bf16,
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
+    "long_context_cp8_bf16": long_context_cp8_bf16,
 }
 
 
@@ -297,3 +334,40 @@ def make_values(w: Workload, device, chunk_elems: int = 1 << 26):
         "new_key": draw((w.num_step_tokens, w.num_kv_heads, w.head_size)),
         "new_value": draw((w.num_step_tokens, w.num_kv_heads, w.head_size)),
     }
+
+
+def make_cp_values(w: Workload, device, ranks=None):
+    """Seeded tensors of a context-parallel workload: the step's query,
+    new_key and new_value (as ``make_values``), and each listed rank's own
+    key/value cache [NB, H_kv, B, D] (``key_caches[r]``), drawn from a
+    generator seeded by (seed, rank) so that ranks can be built one at a time."""
+    import torch
+
+    world = int(w.extra["cp_world"])
+    ranks = list(range(world)) if ranks is None else list(ranks)
+    tdt = getattr(torch, TORCH_DTYPES[w.dtype])
+
+    def draw(gen, shape, chunk_rows=64):
+        out = torch.empty(shape, dtype=tdt, device=device)
+        for i in range(0, shape[0], chunk_rows):
+            j = min(shape[0], i + chunk_rows)
+            x = torch.randn((j - i,) + tuple(shape[1:]), generator=gen, device=device,
+                            dtype=torch.float32)
+            out[i:j] = (x * w.sigma).to(tdt)
+        return out
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    vals = {
+        "query": draw(gen, (w.num_seqs, w.num_heads, w.head_size)),
+        "new_key": draw(gen, (w.num_step_tokens, w.num_kv_heads, w.head_size)),
+        "new_value": draw(gen, (w.num_step_tokens, w.num_kv_heads, w.head_size)),
+        "key_caches": {}, "value_caches": {},
+    }
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_size)
+    for r in ranks:
+        g = torch.Generator(device=device)
+        g.manual_seed(w.seed * 1000 + 1 + r)
+        vals["key_caches"][r] = draw(g, shape)
+        vals["value_caches"][r] = draw(g, shape)
+    return vals
