@@ -38,6 +38,11 @@ Parity status per function (what pins it is listed in each module header):
   attention.merge_rank_partials ....... pinned (rank shares merge to dense
                                         softmax attention; share partial =
                                         partial over the owned positions)
+  slots.map_to_kernel_blocks .......... pinned (the [0,1,2] x 2 example; slots
+                                        agree under both block sizes)
+  attention.* with window > 0,
+  allocator.OraclePool.remove_skipped . pinned (banded dense softmax, closed
+                                        forms, released blocks never read)
   dtypes.decode ....................... pinned (bit patterns with known values)
 """
 

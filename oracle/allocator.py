@@ -22,6 +22,10 @@ What it follows:
     block whose count reaches zero is appended to the tail of the free queue.
   * [CSDN] §3.2.3 (touch): sharing increments the count of every shared block.
 
+  * [CSDN] §3.1.1 / §3.3.1 (sliding window): before new slots are
+    allocated, the blocks that lie wholly before the window are released;
+    their number is the count of skipped tokens divided by B, rounded down.
+
 Readings where the pages are silent or disagree:
   * The free queue is a FIFO seeded with an explicit initial order, freed
     blocks go to its tail, and there is no reserved null block ([CSDN] §2.4
@@ -30,6 +34,11 @@ Readings where the pages are silent or disagree:
     [7, 1, 3, 4, 5, 0, 2, 6] this reproduces the [VLLBC] examples exactly.
   * Only the first appended token of a shared partial tail can trigger a
     copy; a full shared tail is never copied (a new block is opened instead).
+  * Sliding window W: after N computed tokens the next query (position N)
+    sees positions N - W + 1 .. N, so max(0, N - W + 1) tokens are skipped.
+    A released block leaves a hole (None) in the table, is dropped like a
+    freed block (count down, to the queue tail at zero), and the holes are
+    released tail first, as a freed request's blocks are.
 
 Pinned by: tests/test_oracle_allocator.py against the pages' worked examples
 (tests/golden/*.txt) and by closed-form block / slot counts.
@@ -133,13 +142,33 @@ class OraclePool:
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         for blk in self.tables[child]:
-            self.ref[blk] += 1
+            if blk is not None:
+                self.ref[blk] += 1
+
+    def remove_skipped(self, seq: int, num_computed: int, window: int) -> list:
+        """Release the blocks of ``seq`` that lie wholly before the window of
+        its next query; returns the released block ids in release order."""
+        table = self.tables[seq]
+        skipped_blocks = num_skipped_tokens(num_computed, window) // self.block_size
+        released = []
+        for j in reversed(range(min(skipped_blocks, len(table)))):
+            blk = table[j]
+            if blk is None:
+                continue
+            table[j] = None
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                self.free.append(blk)
+            released.append(blk)
+        return released
 
     def free_seq(self, seq: int) -> None:
         """Drop ``seq``; blocks are released tail first."""
         table = self.tables.pop(seq)
         del self.lens[seq]
         for blk in reversed(table):
+            if blk is None:
+                continue
             self.ref[blk] -= 1
             if self.ref[blk] < 0:
                 raise AssertionError(f"block {blk} released more often than taken")
@@ -151,7 +180,8 @@ class OraclePool:
         mapped = [0] * self.num_blocks
         for table in self.tables.values():
             for blk in table:
-                mapped[blk] += 1
+                if blk is not None:
+                    mapped[blk] += 1
         assert mapped == self.ref, "reference counts differ from the table mappings"
         free = set(self.free)
         assert len(free) == len(self.free), "a block is queued twice"
@@ -159,6 +189,13 @@ class OraclePool:
             assert (blk in free) == (self.ref[blk] == 0), f"block {blk} free/referenced mismatch"
         for seq, table in self.tables.items():
             assert len(table) == -(-self.lens[seq] // self.block_size)
+
+
+def num_skipped_tokens(num_computed: int, window: int) -> int:
+    """Tokens no future query sees once ``num_computed`` tokens are computed
+    (window W: the next query, at position num_computed, starts at
+    num_computed - W + 1); 0 without a window."""
+    return max(0, num_computed - window + 1) if window > 0 else 0
 
 
 def sharing_saving(tables) -> float:

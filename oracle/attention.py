@@ -33,6 +33,11 @@ Readings where the pages are silent:
     (position L_s - n_s + i) scores the keys at positions 0 .. L_s - n_s + i
     (causal over the new tokens, the whole cached context before them).
 
+  * Sliding window ([CSDN] §3.1.1 and §3.3.1 release the blocks a sliding
+    window leaves behind, without giving the window's rule): with window W, a
+    query at position p scores only the keys at positions p - W + 1 .. p
+    (the W most recent tokens, itself included); W = 0 means no window.
+
   * Context parallelism ([CSDN] §2.3 spreads a sequence's positions over the
     ranks of a context-parallel group): every rank attends over the tokens
     it stores and keeps (m, l, o) as for a split partition; merging the
@@ -64,12 +69,20 @@ def widen_scale(scale: float) -> float:
 
 
 def gather_tokens(cache: np.ndarray, table_row, length: int, kv_head: int,
-                  block_size: int) -> np.ndarray:
-    """Rows [length, head_size] of one KV head of one sequence, read through
-    its block table: position t is (table_row[t div B], kv_head, t mod B)."""
-    t = np.arange(length)
+                  block_size: int, start: int = 0) -> np.ndarray:
+    """Rows [length - start, head_size] of one KV head of one sequence,
+    positions start .. length - 1, read through its block table: position t
+    is (table_row[t div B], kv_head, t mod B)."""
+    t = np.arange(start, length)
     blocks = np.asarray(table_row, dtype=np.int64)[t // block_size]
+    if (blocks < 0).any():
+        raise ValueError("a position to read lies in a released block")
     return cache[blocks, kv_head, t % block_size, :]
+
+
+def window_start(position: int, window: int) -> int:
+    """First key position a query at ``position`` sees (0 without a window)."""
+    return max(0, position - window + 1) if window > 0 else 0
 
 
 def kv_head_of(h: int, group: int) -> int:
@@ -86,12 +99,13 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
 
 
 def paged_attention(query, key_cache, value_cache, block_tables, context_lens,
-                    scale: float, dtype: str, pairs=None) -> np.ndarray:
+                    scale: float, dtype: str, pairs=None, window: int = 0) -> np.ndarray:
     """Decode attention of every (sequence, query head), or of ``pairs``.
 
     query: raw [S, H, D]; caches: raw [NB, H_kv, B, D]; block_tables: [S, W]
-    ints; context_lens: [S].  Returns float64 [S, H, D] (rows not in ``pairs``
-    are left zero).
+    ints; context_lens: [S].  The query is the token at position L - 1 and
+    sees keys from window_start(L - 1, window).  Returns float64 [S, H, D]
+    (rows not in ``pairs`` are left zero).
     """
     S, H, D = query.shape
     H_kv, B = key_cache.shape[1], key_cache.shape[2]
@@ -110,8 +124,9 @@ def paged_attention(query, key_cache, value_cache, block_tables, context_lens,
                      and (wanted is None or (s, h) in wanted)]
             if not heads:
                 continue
-            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B), dtype)
-            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B), dtype)
+            lo = window_start(L - 1, window)
+            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B, lo), dtype)
+            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B, lo), dtype)
             for h in heads:
                 out[s, h] = attend(decode(query[s, h], dtype), K, V, sc)
     return out
@@ -180,13 +195,15 @@ def visible_tokens(L: int, n: int, i: int) -> int:
 
 
 def paged_attention_multi(query, key_cache, value_cache, block_tables, context_lens,
-                          query_start_loc, scale: float, dtype: str) -> np.ndarray:
+                          query_start_loc, scale: float, dtype: str,
+                          window: int = 0) -> np.ndarray:
     """Attention of every new token of every sequence, causal over the new
     tokens ([CSDN] section 2.3 lays out a step's tokens by query_start_loc;
     [DEEPSONAR] section 2.5 schedules prefill chunks and speculative tokens
     the same way as decode tokens).
 
-    query: raw [T, H, D]; returns float64 [T, H, D]."""
+    query: raw [T, H, D]; returns float64 [T, H, D].  With a window, query
+    token i sees keys from window_start(L - n + i, window) on."""
     T, H, D = query.shape
     H_kv, B = key_cache.shape[1], key_cache.shape[2]
     G = H // H_kv
@@ -198,15 +215,18 @@ def paged_attention_multi(query, key_cache, value_cache, block_tables, context_l
         n = q1 - q0
         if n > L:
             raise ValueError("more new tokens than the context holds")
+        lo0 = window_start(L - n, window)  # no query of the row reads keys before it
         for g in range(H_kv):
-            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B), dtype)
-            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B), dtype)
+            K = decode(gather_tokens(key_cache, block_tables[s], L, g, B, lo0), dtype)
+            V = decode(gather_tokens(value_cache, block_tables[s], L, g, B, lo0), dtype)
             for i in range(n):
                 visible = visible_tokens(L, n, i)
+                lo = window_start(visible - 1, window)
                 for h in range(H):
                     if kv_head_of(h, G) == g:
-                        out[q0 + i, h] = attend(decode(query[q0 + i, h], dtype), K[:visible],
-                                                V[:visible], sc)
+                        out[q0 + i, h] = attend(decode(query[q0 + i, h], dtype),
+                                                K[lo - lo0:visible - lo0],
+                                                V[lo - lo0:visible - lo0], sc)
     return out
 
 

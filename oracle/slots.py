@@ -23,11 +23,16 @@ consecutive positions; offset o inside it belongs to rank (o div I) mod world
 pool at local offset (o div (world * I)) * I + o mod I; on other ranks the
 token maps to the padding id.
 
+Kernel blocks ([CSDN] §3.4, hybrid block sizes): when the allocator's blocks
+hold k smaller blocks of the attention kernel, manager block b stands for
+kernel blocks b*k .. b*k + k - 1, in order.
+
 Pinned by: tests/test_oracle_slots.py (the [3, 0, 4] example, the 7-token
 growth example, bijection onto the occupied slots of random pools, and for
 context parallelism: world 1 equals the plain mapping, hand-computed
 interleaves, every position on exactly one rank, each rank's local offsets
-filled in position order).
+filled in position order; the manager-to-kernel example [0, 1, 2] x 2 ->
+[0..5] and slot numbers that agree under both block sizes).
 """
 
 from __future__ import annotations
@@ -94,3 +99,14 @@ def cp_local_length(length: int, block_size: int, world: int, rank: int,
     """How many of a sequence's first ``length`` positions rank ``rank`` holds."""
     return sum(1 for p in range(length)
                if cp_owner_and_offset(p % (block_size * world), world, interleave)[0] == rank)
+
+
+def map_to_kernel_blocks(manager_ids, blocks_per_kv_block: int):
+    """Kernel block ids of a row of manager block ids ([CSDN] §3.4: manager
+    block b covers kernel blocks b*k .. b*k + k - 1)."""
+    k = int(blocks_per_kv_block)
+    out = []
+    for b in manager_ids:
+        for j in range(k):
+            out.append(int(b) * k + j)
+    return out

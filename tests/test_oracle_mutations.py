@@ -17,10 +17,11 @@ import test_oracle_allocator as TA
 import test_oracle_attention as TT
 import test_oracle_cp as TC
 import test_oracle_slots as TS
+import test_oracle_window as TW
 
 
-def _gather_swapped(cache, table_row, length, kv_head, block_size):
-    t = np.arange(length)
+def _gather_swapped(cache, table_row, length, kv_head, block_size, start=0):
+    t = np.arange(start, length)
     blocks = np.asarray(table_row, dtype=np.int64)[t % len(table_row)]
     return cache[blocks, kv_head, t % block_size, :]
 
@@ -69,6 +70,10 @@ def _partial_unnormalised(q, K, V, scale):
     m = x.max()
     w = np.exp(x - m)
     return m, w.sum(), w @ V
+
+
+def _kernel_blocks_strided(ids, k):
+    return [int(b) + j * len(ids) for b in ids for j in range(int(k))]
 
 
 def _slot_transposed(table_row, pos, block_size):
@@ -175,6 +180,13 @@ MUTATIONS = [
      _cp_local_drops_run_offset, TC),
     ("CP partial output not divided by its sum", attn_mod, "attention_partial",
      _partial_unnormalised, TC),
+    ("kernel blocks strided instead of consecutive", slots_mod, "map_to_kernel_blocks",
+     _kernel_blocks_strided, TS),
+    ("window start off by one", attn_mod, "window_start",
+     lambda p, w: max(0, p - w) if w > 0 else 0, TW),
+    ("window ignored", attn_mod, "window_start", lambda p, w: 0, TW),
+    ("skipped tokens off by one", alloc_mod, "num_skipped_tokens",
+     lambda n, w: max(0, n - w) if w > 0 else 0, TW),
     ("free returns blocks to the queue head", alloc_mod, "OraclePool", _PoolFreeToHead, TA),
     ("COW keeps the old reference", alloc_mod, "OraclePool", _PoolCowKeepsRef, TA),
     ("no copy-on-write", alloc_mod, "OraclePool", _PoolNoCow, TA),
@@ -186,15 +198,15 @@ MUTATIONS = [
 def test_planted_mistake_is_caught(monkeypatch, label, module, name, replacement, pins):
     monkeypatch.setattr(module, name, replacement)
     # test modules bound some names at import time: patch those bindings too
-    for mod in (TA, TT, TS, TC):
+    for mod in (TA, TT, TS, TC, TW):
         if hasattr(mod, name):
             monkeypatch.setattr(mod, name, replacement)
     with np.errstate(all="ignore"):
         assert _some_pin_fails(_all(pins)), f"no pin noticed: {label}"
 
 
-@pytest.mark.parametrize("pins", [TA, TT, TS, TC],
-                         ids=["allocator", "attention", "slots", "context_parallel"])
+@pytest.mark.parametrize("pins", [TA, TT, TS, TC, TW],
+                         ids=["allocator", "attention", "slots", "context_parallel", "window"])
 def test_unmutated_oracle_passes_every_pin(pins):
     """Control: the harness above reports no failure for the real oracle."""
     assert not _some_pin_fails(_all(pins))

@@ -179,3 +179,35 @@ def test_cp_every_position_on_exactly_one_rank_in_order(world, I, B):
         assert flat == [(j // B, j % B) for j in range(len(local))]
         assert len(local) == cp_local_length(L, B, world, r, I)
     assert sorted(owners) == pos
+
+
+# ---- kernel blocks ------------------------------------------------------------
+
+from oracle.slots import map_to_kernel_blocks  # noqa: E402
+
+
+def test_kernel_block_example():
+    g = load_golden("t_k2k")
+    k = int(g["blocks_per_kv_block"][0])
+    assert k == int(g["manager_block_size"][0]) // int(g["kernel_block_size"][0])
+    assert map_to_kernel_blocks(ints(g["manager_ids"]), k) == ints(g["kernel_ids"])
+
+
+def test_kernel_blocks_one_per_manager_block_is_identity():
+    assert map_to_kernel_blocks([7, 3, 0, 9], 1) == [7, 3, 0, 9]
+
+
+@pytest.mark.parametrize("k,Bk", [(2, 16), (4, 4), (8, 1), (3, 5)])
+def test_kernel_block_slots_equal_manager_block_slots(k, Bk):
+    """A position's slot is the same number under the manager table at block
+    size k * Bk and under the kernel table at block size Bk."""
+    rng = np.random.default_rng(k * 10 + Bk)
+    Bm = k * Bk
+    lens = [1, Bm - 1, Bm, 3 * Bm + 2, 7 * Bm]
+    tables = [list(rng.permutation(40)[: -(-L // Bm)]) for L in lens]
+    qsl = np.concatenate([[0], np.cumsum(lens)])
+    pos = np.concatenate([np.arange(L) for L in lens])
+    manager = compute_slot_mapping(qsl, pos, tables, Bm, len(pos))
+    kernel = compute_slot_mapping(qsl, pos, [map_to_kernel_blocks(t, k) for t in tables], Bk,
+                                  len(pos))
+    assert manager == kernel
