@@ -40,16 +40,34 @@ def attention_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def attention_bytes(w, context_lens, query_rows=None) -> int:
-    """Algorithmic bytes of one attention launch: every cached K and V row of
-    every (sequence, KV head) once, q in, out back (one row per sequence, or
-    ``query_rows`` when every new token is a query), the table entries and the
-    context lengths."""
+def window_of(w) -> int:
+    return int(w.extra.get("sliding_window", 0))
+
+
+def attended(w, context_lens, query_lens=None):
+    """Per sequence, the cached positions [lo, L) its queries read: all of
+    them, or with a sliding window W those from the first query's window on."""
+    W = window_of(w)
+    out = []
+    for s, L in enumerate(context_lens):
+        n = 1 if query_lens is None else int(query_lens[s])
+        lo = max(0, int(L) - n + 1 - W) if W else 0
+        out.append((lo, int(L)))
+    return out
+
+
+def attention_bytes(w, context_lens, query_rows=None, query_lens=None) -> int:
+    """Algorithmic bytes of one attention launch: every K and V row a query
+    reads, once per (sequence, KV head), q in, out back (one row per
+    sequence, or ``query_rows`` when every new token is a query), the table
+    entries of the blocks read and the context lengths."""
     e = w.elem_bytes
-    kv = int(sum(context_lens)) * 2 * w.num_kv_heads * w.head_size * e
+    B = w.extra.get("kernel_block_size", w.block_size)
+    spans = attended(w, context_lens, query_lens)
+    kv = sum(L - lo for lo, L in spans) * 2 * w.num_kv_heads * w.head_size * e
     rows = w.num_seqs if query_rows is None else query_rows
     qo = 2 * rows * w.num_heads * w.head_size * e
-    tables = 4 * int(sum(-(-int(L) // w.block_size) for L in context_lens))
+    tables = 4 * sum((L - 1) // B - lo // B + 1 for lo, L in spans if L > lo)
     return kv + qo + tables + 4 * w.num_seqs
 
 
@@ -60,13 +78,18 @@ def step_bytes(w, step) -> int:
     e = w.elem_bytes
     T = step.num_tokens
     row = w.num_kv_heads * w.head_size * e
-    blk = w.num_kv_heads * w.block_size * w.head_size * e
-    return (attention_bytes(w, step.context_lens_host, _query_rows(step)) + 20 * T
+    blk = w.num_kv_heads * step.block_size * w.head_size * e  # kernel blocks
+    return (attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step))
+            + 20 * T
             + 4 * row * T + 4 * blk * len(step.cow_pairs_host))
 
 
 def _query_rows(step):
     return step.num_tokens if step.all_queries else None
+
+
+def _query_lens(step):
+    return np.diff(step.query_start_loc_host) if step.all_queries else None
 
 
 def fused_bytes(w, step) -> int:
@@ -82,7 +105,7 @@ def fused_bytes(w, step) -> int:
         if src >= 0:
             first_new = int(step.context_lens_host[r]) - int(qsl[r + 1] - qsl[r])
             old_slots += first_new % w.block_size
-    return (attention_bytes(w, step.context_lens_host, _query_rows(step))
+    return (attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step))
             + (4 * row + 8) * step.num_tokens + 4 * row * old_slots)
 
 
@@ -188,11 +211,14 @@ def cpu_baseline(w, vals, step, budget_s: float):
                 if step.all_queries:
                     a, b = int(qsl[s]), int(qsl[s + 1])
                     paged_attention_multi(q[a:b], kc, vc, row, lens[s:s + 1], [0, b - a],
-                                          w.scale, w.dtype)
+                                          w.scale, w.dtype, window=window_of(w))
                 else:
-                    paged_attention(q[s:s + 1], kc, vc, row, lens[s:s + 1], w.scale, w.dtype)
+                    paged_attention(q[s:s + 1], kc, vc, row, lens[s:s + 1], w.scale, w.dtype,
+                                    window=window_of(w))
                 t_used += time.perf_counter() - t0
-                done_tokens += int(lens[s])
+                lo, hi = attended(w, lens[s:s + 1],
+                                  None if not step.all_queries else [int(qsl[s + 1] - qsl[s])])[0]
+                done_tokens += hi - lo
                 done_seqs += 1
                 if t_used >= budget_s:
                     break
@@ -434,7 +460,9 @@ def main():
     print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
     vals = W.make_values(w, "cuda")
     step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
-                      w.scale, part, all_queries=w.extra.get("queries") == "all")
+                      w.scale, part, all_queries=w.extra.get("queries") == "all",
+                      sliding_window=window_of(w),
+                      kernel_block_size=w.extra.get("kernel_block_size", 0))
     torch.cuda.synchronize()
 
     fused = not args.unfused
@@ -470,9 +498,11 @@ def main():
     ms_per_step = total_ms / args.steps
     attn_avg_ms = float(np.mean(attn_ms))
 
-    kv_tokens = int(step.context_lens_host.sum())
+    # KV tokens the step's queries attend to (the window's share with a window)
+    kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
     attn_bytes = (fused_bytes(w, step) if fused
-                  else attention_bytes(w, step.context_lens_host, _query_rows(step)))
+                  else attention_bytes(w, step.context_lens_host, _query_rows(step),
+                                       _query_lens(step)))
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     value = kv_tokens / (ms_per_step * 1e-3)
     result = {
@@ -504,6 +534,8 @@ def main():
             "cow_copies": int(len(step.cow_pairs_host)),
             "step_tokens": int(step.num_tokens),
             "queries_per_sequence": step.max_query_len or 1,
+            "sliding_window": window_of(w),
+            "context_tokens": int(step.context_lens_host.sum()),
         },
         "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
         "attention_ms": {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),

@@ -253,9 +253,28 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
  * are read once and are loaded as non-temporal streams.  A cache hint only:
  * results do not depend on it.  NULL = nothing shared.  The unplanned calls
  * above stream every row.
+ *
+ * Sliding window ([CSDN] sections 3.1.1 and 3.3.1 release the blocks a
+ * sliding window leaves behind; the rule itself is this library's reading):
+ * sliding_window W > 0 makes a query at position p attend only to positions
+ * p - W + 1 .. p, the W most recent tokens with itself; 0 is full attention.
+ * Only the K/V rows inside the window are read, so table entries before it
+ * may be -1 (blocks released by pa_pool_remove_skipped).  With
+ * partition_size > 0 the partitions wholly before the window have no item
+ * and are not launched or merged.
+ *
+ * pa_decode_plan_window: pa_decode_plan for windowed attention.  query_lens
+ * (host int32 [num_seqs], NULL = one query per sequence) gives each
+ * sequence's new-token count n_s, 1 <= n_s <= its length; its first query
+ * (position L_s - n_s) starts the window.  An item's size is the part of it
+ * inside the window.  sliding_window == 0 gives pa_decode_plan's list.
  * ---------------------------------------------------------------------- */
 int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
                        int32_t* items, int64_t capacity, int64_t* num_items);
+
+int32_t pa_decode_plan_window(const int32_t* context_lens, const int32_t* query_lens,
+                              int32_t num_seqs, int32_t partition_size, int32_t sliding_window,
+                              int32_t* items, int64_t capacity, int64_t* num_items);
 
 int32_t pa_paged_attention_decode_planned(void* out, const void* query, const void* key_cache,
                                           const void* value_cache, const int32_t* block_tables,
@@ -266,7 +285,8 @@ int32_t pa_paged_attention_decode_planned(void* out, const void* query, const vo
                                           float scale, int32_t dtype, int32_t partition_size,
                                           const int32_t* work_items, int64_t num_work_items,
                                           const int32_t* shared_prefix_blocks, void* workspace,
-                                          size_t workspace_bytes, void* stream);
+                                          size_t workspace_bytes, int32_t sliding_window,
+                                          void* stream);
 
 /* ------------------------------------------------------------------------
  * One decode step in one launch (plus the reduce when partition_size > 0).
@@ -294,7 +314,10 @@ int32_t pa_paged_attention_decode_planned(void* out, const void* query, const vo
  *                    [T][H][D], at most max_query_len new tokens per
  *                    sequence; split-K workspace sized for num_seqs x
  *                    max_query_len rows)
- * The other arguments are those of pa_paged_attention_decode_planned.
+ * The other arguments are those of pa_paged_attention_decode_planned
+ * (sliding_window included: the copy-on-write rows and new tokens are written
+ * whatever the window, since they lie in the partition of the first new
+ * token, which is always inside it).
  * ---------------------------------------------------------------------- */
 int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* value_cache,
                        const int32_t* block_tables, int64_t bt_stride,
@@ -306,7 +329,7 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        size_t workspace_bytes, const int32_t* query_start_loc,
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
-                       int32_t max_query_len, void* stream);
+                       int32_t max_query_len, int32_t sliding_window, void* stream);
 
 /* ------------------------------------------------------------------------
  * Several new tokens per sequence (speculative drafts, short prefill chunks;
@@ -323,8 +346,9 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
  *                    num_kv_heads) must be at most 16 for 16-bit storage and
  *                    head_size 128 (matrix-core kernel), else at most 8
  *   workspace        split-K only: pa_split_workspace_bytes(num_tokens, ...)
- * Work items, shared_prefix_blocks and partition_size as in
- * pa_paged_attention_decode_planned (items are (sequence, partition)).
+ * Work items, shared_prefix_blocks, partition_size and sliding_window as in
+ * pa_paged_attention_decode_planned (items are (sequence, partition), from
+ * pa_decode_plan_window with the query lengths when a window is used).
  * ---------------------------------------------------------------------- */
 int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_cache,
                                  const void* value_cache, const int32_t* block_tables,
@@ -335,7 +359,8 @@ int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_c
                                  float scale, int32_t dtype, int32_t partition_size,
                                  const int32_t* work_items, int64_t num_work_items,
                                  const int32_t* shared_prefix_blocks, void* workspace,
-                                 size_t workspace_bytes, int64_t num_tokens, void* stream);
+                                 size_t workspace_bytes, int64_t num_tokens,
+                                 int32_t sliding_window, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host block allocator (CPU memory only; no device calls).  Generates the
@@ -388,7 +413,9 @@ int32_t pa_pool_block_tables(const pa_pool* pool, const int64_t* seqs, int32_t n
                              int32_t* out, int32_t width, int32_t* context_lens_out);
 /* For each of num_seqs sequences, the number of leading blocks of its table
  * whose reference count is above 1 (blocks other sequences share), into
- * host int32 out[num_seqs].  PA_EINVAL for an unknown sequence. */
+ * host int32 out[num_seqs]; released entries (-1) may sit inside that
+ * prefix, which ends after its last shared block.  PA_EINVAL for an unknown
+ * sequence. */
 int32_t pa_pool_shared_prefix_blocks(const pa_pool* pool, const int64_t* seqs, int32_t num_seqs,
                                      int32_t* out);
 /* Number of free blocks; reference count of one block (-1 if out of range). */
@@ -399,6 +426,33 @@ int32_t pa_pool_ref(const pa_pool* pool, int32_t block);
 int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap);
 /* Number of copy-on-write copies performed since creation. */
 int64_t pa_pool_num_cow(const pa_pool* pool);
+/* Sliding window ([CSDN] sections 3.1.1 and 3.3.1: before allocating, the
+ * blocks outside the window are released).  With num_computed_tokens N
+ * computed, the next query (position N) sees positions N - W + 1 .. N (the
+ * reading pa_paged_attention_decode_planned documents), so
+ * max(0, N - W + 1) tokens are skipped and the first floor of that over B
+ * blocks of seq are released: tail first, counts down, blocks reaching 0 to
+ * the queue tail.  Their table entries become -1 (pa_pool_block_tables
+ * reports them; windowed attention never reads them); the length is
+ * unchanged.  sliding_window == 0 releases nothing.  *num_released (may be
+ * NULL) receives how many blocks this call released.  PA_EINVAL for an
+ * unknown sequence or a negative argument. */
+int32_t pa_pool_remove_skipped(pa_pool* pool, int64_t seq, int64_t num_computed_tokens,
+                               int32_t sliding_window, int32_t* num_released);
+
+/* Kernel blocks ([CSDN] section 3.4, hybrid block sizes): when the
+ * allocator's blocks hold k = blocks_per_kv_block smaller blocks of the
+ * kernels, manager block b stands for kernel blocks b*k .. b*k + k - 1.
+ * Host only: kernel_ids (host int32 [n * k]) receives the mapping of
+ * manager_ids (host int32 [n]); -1 entries map to k entries of -1.  The
+ * kernels then take the mapped table with block size B / k and a cache of
+ * num_blocks * k kernel blocks [..][num_kv_heads][B / k][head_size]; slot
+ * numbers are the same under both tables.  Copy-on-write pairs map the same
+ * way, pair by pair.  PA_EINVAL for null pointers with n > 0, n < 0,
+ * blocks_per_kv_block < 1 or an id whose kernel ids overflow int32 (then
+ * nothing is written). */
+int32_t pa_map_to_kernel_blocks(const int32_t* manager_ids, int64_t n,
+                                int32_t blocks_per_kv_block, int32_t* kernel_ids);
 
 /* ------------------------------------------------------------------------
  * Attention partials and their merge (context parallelism, [CSDN] section

@@ -47,16 +47,17 @@ SIGNATURES = {
                                                _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                _sz, _vp]),
     "pa_decode_plan": (_i32, [_pi32, _i32, _i32, _pi32, _i64, _pi64]),
+    "pa_decode_plan_window": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32, _i64, _pi64]),
     "pa_paged_attention_decode_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
-                                                 _i64, _vp, _vp, _sz, _vp]),
+                                                 _i64, _vp, _vp, _sz, _i32, _vp]),
     "pa_probe_read_blocks": (_i32, [_vp, _vp, _i64, _vp, _i32, _i32, _vp]),
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
                               _i32, _f32, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp,
-                              _i64, _i64, _vp, _vp, _i32, _vp]),
+                              _i64, _i64, _vp, _vp, _i32, _i32, _vp]),
     "pa_paged_attention_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
-                                        _i64, _vp, _vp, _sz, _i64, _vp]),
+                                        _i64, _vp, _vp, _sz, _i64, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _pi32, _c.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_add_seq": (_i32, [_vp, _i64]),
@@ -71,6 +72,8 @@ SIGNATURES = {
     "pa_pool_ref": (_i32, [_vp, _i32]),
     "pa_pool_free_queue": (_i32, [_vp, _pi32, _i32]),
     "pa_pool_num_cow": (_i64, [_vp]),
+    "pa_pool_remove_skipped": (_i32, [_vp, _i64, _i64, _i32, _pi32]),
+    "pa_map_to_kernel_blocks": (_i32, [_pi32, _i64, _i32, _pi32]),
 }
 
 _LIB = None

@@ -49,7 +49,9 @@ using namespace dev;
 // null, the decode case) and query head kvh * G + (v & (G - 1)), G = 1 <<
 // log2_group.  Vector v sees the keys below bound[v] = L - n + (v >> log2_group)
 // + 1 for a sequence with n new tokens; vectors past the sequence's new tokens
-// see none and are not stored.
+// see none and are not stored.  With a sliding window W > 0 it sees only the
+// last W of them, positions from bound[v] - W on: reading starts at the first
+// vector's window, and a partition wholly before it has no work.
 template <int DT, int D, int NQ, int NW, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
     float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
     const int32_t* __restrict__ shared_blocks, int32_t log2_group,
-    const int32_t* __restrict__ q_start) {
+    const int32_t* __restrict__ q_start, int32_t window) {
   using S = St<DT>;
   constexpr int VEC = S::VEC;
   constexpr int LPT = D / VEC;    // lanes per token
@@ -75,6 +77,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const int t_begin = FINAL ? 0 : p * partition_size;
   if (t_begin >= L) return;  // empty partition: the reduce never reads it
   const int t_end = FINAL ? L : min(L, t_begin + partition_size);
+  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
+  // first key any vector of this sequence sees (the first new token's window)
+  const int lo_min = window > 0 ? max(0, L - qlen + 1 - window) : 0;
+  if (t_end <= lo_min) return;  // wholly before the window: the merge skips it
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -93,15 +99,15 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
                                   static_cast<int64_t>(kvh) * (1 << log2_block) * LPT);
   const int32_t h0 = kvh << log2_group;
   const int gmask = (1 << log2_group) - 1;
-  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
 
   typename S::QReg q[NQ];
-  int bound[NQ];
+  int bound[NQ], lo[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int qi = j >> log2_group;
     bound[j] = qi < qlen ? L - qlen + qi + 1 : 0;
+    lo[j] = window > 0 ? max(0, bound[j] - window) : 0;
     q[j] = S::zero_q();
     if (qi < qlen)
       q[j] = S::load_q(query, ((qrow0 + qi) * num_heads + h0 + (j & gmask)) * D + sub * VEC);
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
   const uint4* kc = static_cast<const uint4*>(key_cache);
   const uint4* vc = static_cast<const uint4*>(value_cache);
 
-  for (int c0 = t_begin; c0 < t_end; c0 += kChunkTokens) {
+  for (int c0 = max(t_begin, lo_min); c0 < t_end; c0 += kChunkTokens) {
     const int c1 = min(c0 + kChunkTokens, t_end);
     const int b0 = c0 >> log2_block;
     const int nb = ((c1 - 1) >> log2_block) - b0 + 1;
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
           const float d = group_sum<LPT>(S::dot(q[j], kr[u]));
-          x[j][u] = (t < c1 && t < bound[j]) ? d * scale_log2 : -INFINITY;
+          x[j][u] = (t < c1 && t < bound[j] && t >= lo[j]) ? d * scale_log2 : -INFINITY;
         }
       }
       float vf[U][VEC];
@@ -291,7 +297,8 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeDst dst, PartView src,
                                                   const int32_t* __restrict__ context_lens,
                                                   int32_t num_heads, int32_t partition_size,
                                                   int32_t num_parts,
-                                                  const int32_t* __restrict__ q_start) {
+                                                  const int32_t* __restrict__ q_start,
+                                                  int32_t window) {
   constexpr int kChunk = 256;
   constexpr int NWV = D / 64;
   __shared__ float sw[kChunk];
@@ -300,20 +307,23 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeDst dst, PartView src,
   const int s = blockIdx.y;
   const int d = threadIdx.x;
   // split launches: only the partitions below the sequence's length exist
-  const int np = context_lens
-                     ? min((context_lens[s] + partition_size - 1) / partition_size, num_parts)
-                     : num_parts;
+  const int L = context_lens ? context_lens[s] : 0;
+  const int np = context_lens ? min((L + partition_size - 1) / partition_size, num_parts)
+                              : num_parts;
   // one output row per new token of the sequence (one row when q_start is null)
   const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
   for (int qi = 0; qi < qlen; ++qi) {
   const int64_t row = (qrow0 + qi) * num_heads + h;
-  const float* mrow = src.m + row * src.row_ml;
-  const float* lrow = src.l + row * src.row_ml;
-  const float* orow = src.o + row * src.row_o + d;
+  // with a sliding window, partitions before this row's window hold nothing
+  const int p0 = window > 0 ? max(0, L - qlen + qi + 1 - window) / partition_size : 0;
+  const float* mrow = src.m + row * src.row_ml + static_cast<int64_t>(p0) * src.part_ml;
+  const float* lrow = src.l + row * src.row_ml + static_cast<int64_t>(p0) * src.part_ml;
+  const float* orow = src.o + row * src.row_o + static_cast<int64_t>(p0) * src.part_o + d;
+  const int nrow = np - p0;  // parts this row merges
 
   float mx = -INFINITY;
-  for (int i = d; i < np; i += D) mx = fmaxf(mx, mrow[i * src.part_ml]);
+  for (int i = d; i < nrow; i += D) mx = fmaxf(mx, mrow[i * src.part_ml]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if ((d & 63) == 0) red[d >> 6] = mx;
@@ -324,8 +334,8 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeDst dst, PartView src,
   const float Ms = M == -INFINITY ? 0.0f : M;
 
   float a = 0.0f, wsum = 0.0f;
-  for (int c0 = 0; c0 < np; c0 += kChunk) {
-    const int cn = min(kChunk, np - c0);
+  for (int c0 = 0; c0 < nrow; c0 += kChunk) {
+    const int cn = min(kChunk, nrow - c0);
     __syncthreads();  // sw is rewritten
     for (int i = d; i < cn; i += D) {
       const int64_t k = static_cast<int64_t>(c0 + i) * src.part_ml;
@@ -371,7 +381,7 @@ hipError_t launch_decode_nw(const DecodeArgs& a, hipStream_t stream) {
                      a.context_lens, a.num_heads, a.num_kv_heads, log2_block, a.partition_size,
                      a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum, a.ws_out,
                      reinterpret_cast<const int2*>(a.items), a.append,
-                     a.shared_blocks, log2_group, a.q_start);
+                     a.shared_blocks, log2_group, a.q_start, a.window);
   return hipGetLastError();
 }
 
@@ -415,22 +425,23 @@ hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t stream) {
 template <int DT, int D>
 hipError_t launch_merge_t(const MergeDst& dst, const PartView& src, const int32_t* context_lens,
                           int32_t num_rows, int32_t num_heads, int32_t partition_size,
-                          int32_t num_parts, const int32_t* q_start, hipStream_t stream) {
+                          int32_t num_parts, const int32_t* q_start, int32_t window,
+                          hipStream_t stream) {
   hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(num_heads, num_rows), dim3(D), 0, stream, dst,
-                     src, context_lens, num_heads, partition_size, num_parts, q_start);
+                     src, context_lens, num_heads, partition_size, num_parts, q_start, window);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(int32_t dtype, int32_t head_size, const MergeDst& dst,
                         const PartView& src, const int32_t* context_lens, int32_t num_rows,
                         int32_t num_heads, int32_t partition_size, int32_t num_parts,
-                        const int32_t* q_start, hipStream_t stream) {
+                        const int32_t* q_start, int32_t window, hipStream_t stream) {
   const bool d64 = head_size == 64;
 #define PA_MERGE(DT)                                                                        \
   return d64 ? launch_merge_t<DT, 64>(dst, src, context_lens, num_rows, num_heads,          \
-                                      partition_size, num_parts, q_start, stream)           \
+                                      partition_size, num_parts, q_start, window, stream)   \
              : launch_merge_t<DT, 128>(dst, src, context_lens, num_rows, num_heads,         \
-                                       partition_size, num_parts, q_start, stream)
+                                       partition_size, num_parts, q_start, window, stream)
   switch (dtype) {
     case PA_F32: PA_MERGE(PA_F32);
     case PA_F16: PA_MERGE(PA_F16);
@@ -490,14 +501,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream) {
   return launch_merge(a.dtype, a.head_size, MergeDst{a.out, nullptr, nullptr, nullptr},
                       split_parts(a), a.context_lens, a.num_seqs, a.num_heads, a.partition_size,
-                      a.num_partitions, a.q_start, stream);
+                      a.num_partitions, a.q_start, a.window, stream);
 }
 
 hipError_t launch_split_reduce_partials(const DecodeArgs& a, float* m, float* l, float* o,
                                         hipStream_t stream) {
   return launch_merge(a.dtype, a.head_size, MergeDst{nullptr, m, l, o}, split_parts(a),
                       a.context_lens, a.num_seqs, a.num_heads, a.partition_size,
-                      a.num_partitions, a.q_start, stream);
+                      a.num_partitions, a.q_start, a.window, stream);
 }
 
 hipError_t launch_merge_ranks(void* out, const float* m, const float* l, const float* o,
@@ -506,7 +517,7 @@ hipError_t launch_merge_ranks(void* out, const float* m, const float* l, const f
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
   return launch_merge(dtype, head_size, MergeDst{out, nullptr, nullptr, nullptr},
                       PartView{m, l, o, rows, 1, rows * head_size, head_size}, nullptr,
-                      num_seqs, num_heads, 1, num_parts, nullptr, stream);
+                      num_seqs, num_heads, 1, num_parts, nullptr, 0, stream);
 }
 
 }  // namespace pa

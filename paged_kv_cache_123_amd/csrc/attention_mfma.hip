@@ -47,7 +47,8 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
 
 // Column c of the 16 MFMA columns is query vector c (c < NQ): new token
 // c >> log2_group of the sequence (one per sequence when q_start is null) and
-// query head kvh * G + (c & (G - 1)); it sees the keys below its causal bound.
+// query head kvh * G + (c & (G - 1)); it sees the keys below its causal bound,
+// only the last W of them with a sliding window W > 0.
 template <int DT, int NQ, int NW, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
     float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
     const int32_t* __restrict__ shared_blocks, int32_t log2_group,
-    const int32_t* __restrict__ q_start) {
+    const int32_t* __restrict__ q_start, int32_t window) {
   constexpr int D = 128;
   constexpr int DV = D / 8;   // 16-byte vectors per token row
   constexpr int NK = D / 32;  // score MFMAs per tile
@@ -74,6 +75,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
   const int t_begin = FINAL ? 0 : p * partition_size;
   if (t_begin >= L) return;
   const int t_end = FINAL ? L : min(L, t_begin + partition_size);
+  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
+  // first key any column of this sequence sees (the first new token's window)
+  const int lo_min = window > 0 ? max(0, L - qlen + 1 - window) : 0;
+  if (t_end <= lo_min) return;  // wholly before the window: the merge skips it
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -91,11 +96,11 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
                                   static_cast<int64_t>(kvh) * (1 << log2_block) * DV);
   const int h0 = kvh << log2_group;
   const int gmask = (1 << log2_group) - 1;
-  const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
   const int my_qi = col >> log2_group;
   const bool my_valid = col < NQ && my_qi < qlen;
   const int bound = my_valid ? L - qlen + my_qi + 1 : 0;  // keys this column sees
+  const int lo = window > 0 ? max(0, bound - window) : 0;   // ... from here on
 
   uint4 qv[NK];
 #pragma unroll
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
   const uint4* vc = static_cast<const uint4*>(value_cache);
   const int k_tok = (col >> 2) + 4 * (col & 3);  // token of this lane's K row
 
-  for (int c0 = t_begin; c0 < t_end; c0 += kChunkTokens) {
+  for (int c0 = max(t_begin, lo_min); c0 < t_end; c0 += kChunkTokens) {
     const int c1 = min(c0 + kChunkTokens, t_end);
     const int b0 = c0 >> log2_block;
     const int nb = ((c1 - 1) >> log2_block) - b0 + 1;
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = t0 + grp + 4 * j;
-        x[j] = (t < c1 && t < bound) ? sc[j] * scale_log2 : -INFINITY;
+        x[j] = (t < c1 && t < bound && t >= lo) ? sc[j] * scale_log2 : -INFINITY;
       }
       float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -271,7 +276,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
                      a.partition_size, a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum,
                      a.ws_out, reinterpret_cast<const int2*>(a.items), a.append,
-                     a.shared_blocks, log2_group, a.q_start);
+                     a.shared_blocks, log2_group, a.q_start, a.window);
   return hipGetLastError();
 }
 

@@ -3,9 +3,13 @@
 //
 // Semantics ([PUFANYI] "按 Block 分配"; [CSDN] sections 3.1.2, 3.2.1, 3.2.3,
 // 3.2.4; [VLLBC] paper section 4.4 / Fig. 8) are described in pagedkv.h.
+// With a sliding window, the blocks a sequence's next query can no longer see
+// are released early ([CSDN] sections 3.1.1 and 3.3.1); they leave holes (-1)
+// at the front of its table.
 // Design: the free queue is an intrusive doubly linked list over block ids
 // (prev/next arrays), so taking the head, appending at the tail and removing
 // an arbitrary block are all O(1) with no allocation after creation.
+#include <algorithm>
 #include <cstdint>
 #include <string>
 #include <unordered_map>
@@ -108,7 +112,8 @@ int32_t pa_pool_fork(pa_pool* pool, int64_t parent, int64_t child) {
   if (it == pool->seqs.end()) return pa::fail(PA_EINVAL, "pa_pool_fork: unknown parent");
   if (pool->seqs.count(child)) return pa::fail(PA_EINVAL, "pa_pool_fork: child exists");
   Seq c = it->second;
-  for (int32_t b : c.blocks) pool->ref[b] += 1;
+  for (int32_t b : c.blocks)
+    if (b >= 0) pool->ref[b] += 1;
   pool->seqs.emplace(child, std::move(c));
   return PA_OK;
 }
@@ -152,9 +157,34 @@ int32_t pa_pool_free_seq(pa_pool* pool, int64_t seq) {
   if (it == pool->seqs.end()) return pa::fail(PA_EINVAL, "pa_pool_free_seq: unknown sequence");
   const std::vector<int32_t>& blocks = it->second.blocks;
   for (auto b = blocks.rbegin(); b != blocks.rend(); ++b) {
-    if (--pool->ref[*b] == 0) pool->push_tail(*b);
+    if (*b >= 0 && --pool->ref[*b] == 0) pool->push_tail(*b);
   }
   pool->seqs.erase(it);
+  return PA_OK;
+}
+
+int32_t pa_pool_remove_skipped(pa_pool* pool, int64_t seq, int64_t num_computed_tokens,
+                               int32_t sliding_window, int32_t* num_released) {
+  if (!pool || num_computed_tokens < 0 || sliding_window < 0)
+    return pa::fail(PA_EINVAL, "pa_pool_remove_skipped: bad argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return pa::fail(PA_EINVAL, "pa_pool_remove_skipped: unknown sequence");
+  std::vector<int32_t>& blocks = it->second.blocks;
+  // the next query (position num_computed_tokens) sees the last W positions
+  const int64_t skipped =
+      sliding_window > 0 ? std::max<int64_t>(0, num_computed_tokens - sliding_window + 1) : 0;
+  const int64_t n = std::min<int64_t>(skipped / pool->block_size,
+                                      static_cast<int64_t>(blocks.size()));
+  int32_t released = 0;
+  for (int64_t j = n - 1; j >= 0; --j) {  // tail first, as a freed request
+    const int32_t b = blocks[j];
+    if (b < 0) continue;
+    blocks[j] = -1;
+    if (--pool->ref[b] == 0) pool->push_tail(b);
+    ++released;
+  }
+  if (num_released) *num_released = released;
   return PA_OK;
 }
 
@@ -205,10 +235,14 @@ int32_t pa_pool_shared_prefix_blocks(const pa_pool* pool, const int64_t* seqs, i
     auto it = pool->seqs.find(seqs[r]);
     if (it == pool->seqs.end())
       return pa::fail(PA_EINVAL, "pa_pool_shared_prefix_blocks: unknown sequence");
-    int32_t n = 0;
+    // holes (released blocks) are never read: they may sit inside the prefix,
+    // which ends after its last shared block
+    int32_t n = 0, j = 0;
     for (int32_t b : it->second.blocks) {
+      ++j;
+      if (b < 0) continue;
       if (pool->ref[b] <= 1) break;
-      ++n;
+      n = j;
     }
     out[r] = n;
   }
@@ -230,5 +264,21 @@ int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap) {
 }
 
 int64_t pa_pool_num_cow(const pa_pool* pool) { return pool ? pool->num_cow : -1; }
+
+int32_t pa_map_to_kernel_blocks(const int32_t* manager_ids, int64_t n,
+                                int32_t blocks_per_kv_block, int32_t* kernel_ids) {
+  if ((n > 0 && (!manager_ids || !kernel_ids)) || n < 0 || blocks_per_kv_block < 1)
+    return pa::fail(PA_EINVAL, "pa_map_to_kernel_blocks: bad argument");
+  const int64_t k = blocks_per_kv_block;
+  for (int64_t i = 0; i < n; ++i)
+    if (manager_ids[i] > (static_cast<int64_t>(INT32_MAX) - k + 1) / k)
+      return pa::fail(PA_EINVAL, "pa_map_to_kernel_blocks: kernel block id overflows int32");
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t b = manager_ids[i];
+    for (int64_t j = 0; j < k; ++j)
+      kernel_ids[i * k + j] = b < 0 ? -1 : static_cast<int32_t>(b * k + j);
+  }
+  return PA_OK;
+}
 
 }  // extern "C"

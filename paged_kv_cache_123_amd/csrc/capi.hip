@@ -247,8 +247,11 @@ int32_t pa_paged_attention_decode_planned(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
     int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
     int32_t partition_size, const int32_t* work_items, int64_t num_work_items,
-    const int32_t* shared_prefix_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+    const int32_t* shared_prefix_blocks, void* workspace, size_t workspace_bytes,
+    int32_t sliding_window, void* stream) {
   const char* who = "pa_paged_attention_decode_planned";
+  if (sliding_window < 0)
+    return fail(PA_EINVAL, "pa_paged_attention_decode_planned: sliding_window < 0");
   int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
                             context_lens, num_seqs, num_heads, num_kv_heads, head_size,
                             block_size, max_context_len, dtype);
@@ -262,6 +265,7 @@ int32_t pa_paged_attention_decode_planned(
                      num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale,
                      dtype, nullptr, nullptr, nullptr, work_items, num_work_items};
     a.shared_blocks = shared_prefix_blocks;
+    a.window = sliding_window;
     return launched(pa::launch_decode(a, s), who);
   }
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
@@ -284,6 +288,7 @@ int32_t pa_paged_attention_decode_planned(
                    reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float))),
                    work_items, num_work_items};
   a.shared_blocks = shared_prefix_blocks;
+  a.window = sliding_window;
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_planned (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_planned (reduce)");
@@ -299,8 +304,10 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        size_t workspace_bytes, const int32_t* query_start_loc,
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
-                       int32_t max_query_len, void* stream) {
+                       int32_t max_query_len, int32_t sliding_window, void* stream) {
   const char* who = "pa_decode_step";
+  if (sliding_window < 0)
+    return fail(PA_EINVAL, "pa_decode_step: sliding_window < 0");
   int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
                             context_lens, num_seqs, num_heads, num_kv_heads, head_size,
                             block_size, max_context_len, dtype);
@@ -325,6 +332,7 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                                  value_stride * eb / 16, static_cast<uint4*>(key_cache),
                                  static_cast<uint4*>(value_cache), slot_mapping};
   a.shared_blocks = shared_prefix_blocks;
+  a.window = sliding_window;
   if (max_query_len > 0) {  // every new token is a query
     st = check_query_capacity(who, max_query_len, num_heads, num_kv_heads, head_size, dtype);
     if (st != PA_OK) return st;
@@ -368,8 +376,11 @@ int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_c
                                  float scale, int32_t dtype, int32_t partition_size,
                                  const int32_t* work_items, int64_t num_work_items,
                                  const int32_t* shared_prefix_blocks, void* workspace,
-                                 size_t workspace_bytes, int64_t num_tokens, void* stream) {
+                                 size_t workspace_bytes, int64_t num_tokens,
+                                 int32_t sliding_window, void* stream) {
   const char* who = "pa_paged_attention_multi";
+  if (sliding_window < 0)
+    return fail(PA_EINVAL, "pa_paged_attention_multi: sliding_window < 0");
   int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
                             context_lens, num_seqs, num_heads, num_kv_heads, head_size,
                             block_size, max_context_len, dtype);
@@ -387,6 +398,7 @@ int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_c
   a.shared_blocks = shared_prefix_blocks;
   a.q_start = query_start_loc;
   a.max_query_len = max_query_len;
+  a.window = sliding_window;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||

@@ -50,6 +50,7 @@ struct DecodeArgs {
   const int32_t* shared_blocks;  // [S] leading blocks shared with other sequences, or nullptr
   const int32_t* q_start;    // [S+1] new-token rows when every new token is a query, or nullptr
   int32_t max_query_len;     // bound on q_start[s+1] - q_start[s] (host)
+  int32_t window;            // sliding window in tokens, 0 for none
 };
 
 // Query vectors one workgroup serves: (new tokens per sequence) x (query heads

@@ -4,6 +4,8 @@
 // compared in buckets of kGranule tokens and equal buckets keep batch order,
 // so sequences that share blocks (forks of one prompt sit next to each other
 // in a batch) still run close together in time and reuse cached blocks.
+// With a sliding window an item's size is the part of it inside the window,
+// and partitions wholly before the window are left out.
 #include <algorithm>
 #include <cstdint>
 #include <vector>
@@ -15,10 +17,11 @@ namespace {
 constexpr int32_t kGranule = 256;
 }
 
-extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
-                                  int32_t partition_size, int32_t* items, int64_t capacity,
-                                  int64_t* num_items) {
-  if (!context_lens || !num_items || num_seqs < 1 || partition_size < 0)
+extern "C" int32_t pa_decode_plan_window(const int32_t* context_lens,
+                                         const int32_t* query_lens, int32_t num_seqs,
+                                         int32_t partition_size, int32_t sliding_window,
+                                         int32_t* items, int64_t capacity, int64_t* num_items) {
+  if (!context_lens || !num_items || num_seqs < 1 || partition_size < 0 || sliding_window < 0)
     return pa::fail(PA_EINVAL, "pa_decode_plan: bad argument");
   struct Item {
     int32_t tokens, s, p;
@@ -28,13 +31,21 @@ extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
     const int32_t L = context_lens[s];
     if (L < 0 || (L == 0 && partition_size == 0))
       return pa::fail(PA_EINVAL, "pa_decode_plan: context length < 1");
+    const int32_t n = query_lens ? query_lens[s] : 1;
+    if (L > 0 && (n < 1 || n > L))
+      return pa::fail(PA_EINVAL, "pa_decode_plan: query length outside [1, context length]");
+    // first key the sequence's first query sees under the window
+    const int32_t lo = sliding_window > 0 ? std::max(0, L - n + 1 - sliding_window) : 0;
     if (partition_size == 0) {
-      v.push_back({L, s, 0});
+      v.push_back({L - lo, s, 0});
       continue;
     }
-    // a sequence with no token (a rank-local share can be empty) has no item
-    for (int32_t p = 0; static_cast<int64_t>(p) * partition_size < L; ++p)
-      v.push_back({std::min(partition_size, L - p * partition_size), s, p});
+    // a sequence with no token (a rank-local share can be empty) has no item;
+    // partitions wholly before the window have none either
+    for (int32_t p = lo / partition_size; static_cast<int64_t>(p) * partition_size < L; ++p) {
+      const int32_t begin = std::max(p * partition_size, lo);
+      v.push_back({std::min((p + 1) * partition_size, L) - begin, s, p});
+    }
   }
   *num_items = static_cast<int64_t>(v.size());
   if (!items) return PA_OK;  // size query
@@ -48,4 +59,11 @@ extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
     items[2 * i + 1] = v[i].p;
   }
   return PA_OK;
+}
+
+extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t partition_size, int32_t* items, int64_t capacity,
+                                  int64_t* num_items) {
+  return pa_decode_plan_window(context_lens, nullptr, num_seqs, partition_size, 0, items,
+                               capacity, num_items);
 }

@@ -64,6 +64,14 @@ class Pool:
     def free_seq(self, seq: int) -> None:
         check(lib().pa_pool_free_seq(self._h, seq))
 
+    def remove_skipped(self, seq: int, num_computed_tokens: int, sliding_window: int) -> int:
+        """Release the blocks of ``seq`` wholly before its next query's
+        window; returns how many were released (their entries become -1)."""
+        n = ctypes.c_int32(0)
+        check(lib().pa_pool_remove_skipped(self._h, seq, num_computed_tokens, sliding_window,
+                                           ctypes.byref(n)))
+        return n.value
+
     def seq_len(self, seq: int) -> int:
         out = ctypes.c_int64()
         check(lib().pa_pool_seq_len(self._h, seq, ctypes.byref(out)))
@@ -84,6 +92,7 @@ class Pool:
         return out, lens
 
     def block_table(self, seq: int) -> list:
+        """Physical blocks of ``seq`` in logical order; released ones are -1."""
         n = self.seq_num_blocks(seq)
         t, _ = self.block_tables([seq], max(n, 1))
         return [int(b) for b in t[0, :n]]

@@ -246,18 +246,47 @@ def _shared_ptr(shared_prefix_blocks, S):
     return shared_prefix_blocks.data_ptr()
 
 
-def decode_plan(context_lens, partition_size: int) -> np.ndarray:
+def decode_plan(context_lens, partition_size: int, sliding_window: int = 0,
+                query_lens=None) -> np.ndarray:
     """Host work plan: int32 [num_items, 2] of (sequence, partition), every
-    non-empty item once, largest first (partition_size 0: one per sequence)."""
+    non-empty item once, largest first (partition_size 0: one per sequence).
+    With a sliding window, only the items inside each sequence's window;
+    ``query_lens`` (new tokens per sequence) place its first query."""
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     n = ctypes.c_int64(0)
     p32 = ctypes.POINTER(ctypes.c_int32)
-    check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size, None, 0,
-                               ctypes.byref(n)))
+    if sliding_window == 0 and query_lens is None:
+        check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size, None, 0,
+                                   ctypes.byref(n)))
+        items = np.empty((n.value, 2), dtype=np.int32)
+        check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size,
+                                   items.ctypes.data_as(p32), n.value, ctypes.byref(n)))
+        return items
+    qlens = None
+    if query_lens is not None:
+        qlens = np.ascontiguousarray(np.asarray(query_lens, dtype=np.int32))
+        if qlens.size != lens.size:
+            raise ValueError("query_lens must have one entry per sequence")
+    qp = None if qlens is None else qlens.ctypes.data_as(p32)
+    check(lib().pa_decode_plan_window(lens.ctypes.data_as(p32), qp, lens.size, partition_size,
+                                      sliding_window, None, 0, ctypes.byref(n)))
     items = np.empty((n.value, 2), dtype=np.int32)
-    check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size,
-                               items.ctypes.data_as(p32), n.value, ctypes.byref(n)))
+    check(lib().pa_decode_plan_window(lens.ctypes.data_as(p32), qp, lens.size, partition_size,
+                                      sliding_window, items.ctypes.data_as(p32), n.value,
+                                      ctypes.byref(n)))
     return items
+
+
+def map_to_kernel_blocks(manager_ids, blocks_per_kv_block: int) -> np.ndarray:
+    """Host int32 kernel block ids of manager block ids (any shape; the last
+    axis grows by ``blocks_per_kv_block``); -1 entries stay -1."""
+    ids = np.ascontiguousarray(np.asarray(manager_ids, dtype=np.int32))
+    out = np.empty(ids.shape[:-1] + (ids.shape[-1] * blocks_per_kv_block,) if ids.ndim else
+                   (blocks_per_kv_block,), dtype=np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    check(lib().pa_map_to_kernel_blocks(ids.ctypes.data_as(p32), ids.size, blocks_per_kv_block,
+                                        out.ctypes.data_as(p32)))
+    return out
 
 
 def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
@@ -265,9 +294,10 @@ def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
                                    block_tables: torch.Tensor, context_lens: torch.Tensor,
                                    scale: float, max_context_len: int, partition_size: int,
                                    work_items: torch.Tensor, workspace=None,
-                                   shared_prefix_blocks=None) -> None:
+                                   shared_prefix_blocks=None, sliding_window: int = 0) -> None:
     """Attention driven by a work plan (device int32 [num_items, 2]).
-    ``shared_prefix_blocks``: optional device int32 [num_seqs] cache hint."""
+    ``shared_prefix_blocks``: optional device int32 [num_seqs] cache hint;
+    ``sliding_window``: attend to the last W tokens only (0: all)."""
     S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables, context_lens)
     _dev(work_items)
     if work_items.dtype != torch.int32 or work_items.dim() != 2 or work_items.shape[1] != 2:
@@ -282,7 +312,7 @@ def paged_attention_decode_planned(out: torch.Tensor, query: torch.Tensor,
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
         work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
-        _stream()))
+        sliding_window, _stream()))
 
 
 def paged_attention_partials(max_logits: torch.Tensor, exp_sums: torch.Tensor,
@@ -362,7 +392,8 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                 context_lens: torch.Tensor, scale: float, max_context_len: int,
                 partition_size: int, work_items: torch.Tensor, query_start_loc: torch.Tensor,
                 key: torch.Tensor, value: torch.Tensor, cow_src=None, slot_mapping=None,
-                workspace=None, shared_prefix_blocks=None, max_query_len: int = 0) -> None:
+                workspace=None, shared_prefix_blocks=None, max_query_len: int = 0,
+                sliding_window: int = 0) -> None:
     """The whole decode step in one launch: copy-on-write of the old slots of
     fresh tail blocks (``cow_src`` int64 [num_seqs], -1 for none), the new
     tokens' K/V (rows of ``key``/``value`` per ``query_start_loc``) into their
@@ -409,7 +440,7 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
         work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
         query_start_loc.data_ptr(),
         key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None,
-        slot_ptr or None, max_query_len, _stream()))
+        slot_ptr or None, max_query_len, sliding_window, _stream()))
 
 
 def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
@@ -417,7 +448,7 @@ def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: tor
                           context_lens: torch.Tensor, query_start_loc: torch.Tensor,
                           max_query_len: int, scale: float, max_context_len: int,
                           partition_size: int, work_items: torch.Tensor, workspace=None,
-                          shared_prefix_blocks=None) -> None:
+                          shared_prefix_blocks=None, sliding_window: int = 0) -> None:
     """Attention of every new token (query/out [num_tokens, H, D]), causal over
     each sequence's new tokens."""
     _dev(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc,
@@ -444,4 +475,4 @@ def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: tor
         query_start_loc.data_ptr(), S, max_query_len, query.shape[1], hkv, D, B,
         max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
         work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
-        query.shape[0], _stream()))
+        query.shape[0], sliding_window, _stream()))

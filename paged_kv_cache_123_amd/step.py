@@ -27,8 +27,10 @@ from . import ops
 from .host import Pool
 
 
-def replay(pool: Pool, history, appends):
+def replay(pool: Pool, history, appends, sliding_window: int = 0):
     """Run a batch's history and then the step's appends through ``pool``.
+    With a sliding window, each row first releases the blocks its next query
+    can no longer see ([CSDN] sections 3.1.1 and 3.3.1).
 
     Returns (seqs, positions, query_start_loc, cow_pairs, cow_src): the batch
     rows, the position of every new token, the row boundaries of the new
@@ -46,6 +48,8 @@ def replay(pool: Pool, history, appends):
     seqs, positions, qsl, cow, cow_src = [], [], [0], [], []
     for s, n in appends:
         start = pool.seq_len(s)
+        if sliding_window:
+            pool.remove_skipped(s, start, sliding_window)
         _, pair = pool.append(s, n)
         seqs.append(s)
         positions.extend(range(start, start + n))
@@ -65,22 +69,42 @@ class DecodeStep:
     new_value device tensors (caches [NB, H_kv, B, D]).  ``all_queries``:
     every new token is a query (query/out [num_tokens, H, D], causal over each
     sequence's new tokens) instead of one query per sequence.
+    ``sliding_window``: attention sees the last W tokens only, and blocks
+    outside every query's window are released before the step's appends.
+    ``kernel_block_size``: the allocator hands out blocks of ``block_size``
+    tokens that the kernels see as block_size / kernel_block_size blocks of
+    kernel_block_size tokens ([CSDN] section 3.4): tables and copy-on-write
+    pairs are mapped, and the caches hold num_blocks * k kernel blocks.
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
                  values: dict, scale: float, partition_size: int = 0, planned: bool = True,
-                 all_queries: bool = False):
+                 all_queries: bool = False, sliding_window: int = 0,
+                 kernel_block_size: int = 0):
         self.pool = Pool(num_blocks, block_size, free_order)
-        seqs, positions, qsl, cow, cow_src = replay(self.pool, history, appends)
+        self.sliding_window = int(sliding_window)
+        seqs, positions, qsl, cow, cow_src = replay(self.pool, history, appends,
+                                                    self.sliding_window)
         self.seqs = seqs
-        self.block_size = block_size
+        kb = int(kernel_block_size) or block_size
+        if block_size % kb:
+            raise ValueError("kernel_block_size must divide block_size")
+        k = block_size // kb
+        self.block_size = kb
+        self.kernel_blocks_per_block = k
         width = max(self.pool.seq_num_blocks(s) for s in seqs)
         tables, lens = self.pool.block_tables(seqs, width)
+        self.manager_tables_host = tables
+        if k > 1:
+            tables = ops.map_to_kernel_blocks(tables, k)
+            cow = [(src * k + j, dst * k + j) for src, dst in cow for j in range(k)]
+            cow_src = [-1 if c < 0 else None for c in cow_src]  # no one-launch copy
         self.tables_host = tables
         self.context_lens_host = lens
         self.cow_pairs_host = np.asarray(cow, dtype=np.int64).reshape(-1, 2)
-        self.cow_src_host = np.asarray(cow_src, dtype=np.int64)
-        self.shared_blocks_host = self.pool.shared_prefix_blocks(seqs)
+        self.fused_ok = all(c is not None for c in cow_src)
+        self.cow_src_host = np.asarray([-1 if c is None else c for c in cow_src], dtype=np.int64)
+        self.shared_blocks_host = self.pool.shared_prefix_blocks(seqs) * k  # in kernel blocks
         self.positions_host = np.asarray(positions, dtype=np.int64)
         self.query_start_loc_host = np.asarray(qsl, dtype=np.int32)
         self.num_tokens = int(qsl[-1])
@@ -109,7 +133,11 @@ class DecodeStep:
         self.max_query_len = int(max(n for _, n in appends)) if all_queries else 0
         if all_queries and not planned:
             raise ValueError("every-token queries use the planned launch")
-        self.plan_host = ops.decode_plan(lens, self.partition_size)
+        if self.sliding_window and not planned:
+            raise ValueError("a sliding window uses the planned launch")
+        query_lens = [n for _, n in appends] if all_queries else None
+        self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
+                                         query_lens)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self.workspace = None
         if self.partition_size:
@@ -137,13 +165,14 @@ class DecodeStep:
                                       self.block_tables, self.context_lens,
                                       self.query_start_loc, self.max_query_len, self.scale,
                                       self.max_context_len, self.partition_size, self.plan,
-                                      self.workspace, self.shared_blocks)
+                                      self.workspace, self.shared_blocks, self.sliding_window)
         elif self.planned:
             ops.paged_attention_decode_planned(self.out, self.query, self.key_cache,
                                                self.value_cache, self.block_tables,
                                                self.context_lens, self.scale,
                                                self.max_context_len, self.partition_size,
-                                               self.plan, self.workspace, self.shared_blocks)
+                                               self.plan, self.workspace, self.shared_blocks,
+                                               self.sliding_window)
         elif self.partition_size:
             ops.paged_attention_decode_split(self.out, self.query, self.key_cache,
                                              self.value_cache, self.block_tables,
@@ -157,11 +186,14 @@ class DecodeStep:
 
     def fused(self):
         """The whole step as one launch (pa_decode_step)."""
+        if not self.fused_ok:
+            raise ValueError("a copy-on-write of a block of several kernel blocks needs "
+                             "copy_blocks: run the step unfused")
         ops.decode_step(self.out, self.query, self.key_cache, self.value_cache,
                         self.block_tables, self.context_lens, self.scale, self.max_context_len,
                         self.partition_size, self.plan, self.query_start_loc, self.new_key,
                         self.new_value, self.cow_src, self.slot_mapping, self.workspace,
-                        self.shared_blocks, self.max_query_len)
+                        self.shared_blocks, self.max_query_len, self.sliding_window)
 
     def run(self, fused: bool = False):
         """The whole step; returns ``out`` [num_seqs, num_heads, head_size].

@@ -10,7 +10,8 @@ from oracle.allocator import OraclePool
 from oracle.attention import (merge_rank_partials, paged_attention, paged_attention_multi,
                               paged_attention_partials, paged_attention_split)
 from oracle.cache_ops import copy_blocks, reshape_and_cache
-from oracle.slots import compute_slot_mapping, compute_slot_mapping_cp, cp_local_length
+from oracle.slots import (compute_slot_mapping, compute_slot_mapping_cp, cp_local_length,
+                          map_to_kernel_blocks)
 
 
 def to_host(t):
@@ -23,11 +24,18 @@ def to_host(t):
 
 class OracleStep:
     """Under context parallelism (w.extra["cp_world"] > 1) the pool hands out
-    virtual blocks of block_size * cp_world positions shared by the ranks."""
+    virtual blocks of block_size * cp_world positions shared by the ranks.
+    With w.extra["sliding_window"] each row releases the blocks outside its
+    next query's window before the step appends; with
+    w.extra["kernel_block_size"] the pool's blocks are split into kernel
+    blocks for the tables, copies and cache accesses."""
 
     def __init__(self, w):
         self.world = int(w.extra.get("cp_world", 1))
         self.interleave = int(w.extra.get("cp_interleave", 1))
+        self.window = int(w.extra.get("sliding_window", 0))
+        self.kb = int(w.extra.get("kernel_block_size", 0)) or w.block_size
+        k = w.block_size // self.kb
         pool = OraclePool(w.num_blocks, w.block_size * self.world, w.free_order)
         for op in w.prefill:
             if op[0] == "add":
@@ -39,6 +47,7 @@ class OracleStep:
         positions, qsl, cow, slots = [], [0], [], []
         for s, n in w.step:
             start = pool.seq_len(s)
+            pool.remove_skipped(s, start, self.window)
             sl, c = pool.append(s, n)
             slots += sl
             cow += c
@@ -46,11 +55,14 @@ class OracleStep:
             qsl.append(qsl[-1] + n)
         self.pool = pool
         self.seqs = [s for s, _ in w.step]
-        width = max(len(pool.block_table(s)) for s in self.seqs)
+        width = max(len(pool.block_table(s)) for s in self.seqs) * k
         self.tables = np.full((len(self.seqs), width), -1, dtype=np.int64)
         for r, s in enumerate(self.seqs):
-            t = pool.block_table(s)
+            t = []
+            for b in pool.block_table(s):  # released blocks stay holes
+                t += [-1] * k if b is None else map_to_kernel_blocks([b], k)
             self.tables[r, :len(t)] = t
+        cow = [(a * k + j, b * k + j) for a, b in cow for j in range(k)]
         self.context_lens = np.array([pool.seq_len(s) for s in self.seqs], dtype=np.int64)
         self.positions = positions
         self.query_start_loc = qsl
@@ -61,26 +73,28 @@ class OracleStep:
     def slot_mapping(self, max_num_tokens=None):
         T = self.query_start_loc[-1]
         return compute_slot_mapping(self.query_start_loc, self.positions, self.tables,
-                                    self.w.block_size, max_num_tokens or T)
+                                    self.kb, max_num_tokens or T)
 
     def apply_copies(self, kc, vc):
         copy_blocks(kc, vc, self.cow_pairs)
 
     def apply_scatter(self, kc, vc, new_key, new_value):
-        reshape_and_cache(kc, vc, new_key, new_value, self.slot_mapping(), self.w.block_size)
+        reshape_and_cache(kc, vc, new_key, new_value, self.slot_mapping(), self.kb)
 
     def attention(self, query, kc, vc, pairs=None, tables=None):
         t = self.tables if tables is None else tables
         return paged_attention(query, kc, vc, t, self.context_lens, self.w.scale, self.w.dtype,
-                               pairs=pairs)
+                               pairs=pairs, window=self.window)
 
     def attention_split(self, query, kc, vc, partition_size, pairs=None):
+        assert self.window == 0, "the split oracle has no window"
         return paged_attention_split(query, kc, vc, self.tables, self.context_lens, self.w.scale,
                                      self.w.dtype, partition_size, pairs=pairs)
 
     def attention_multi(self, query, kc, vc):
         return paged_attention_multi(query, kc, vc, self.tables, self.context_lens,
-                                     self.query_start_loc, self.w.scale, self.w.dtype)
+                                     self.query_start_loc, self.w.scale, self.w.dtype,
+                                     window=self.window)
 
     # ---- context parallelism: one rank's share ----------------------------
     def cp_slot_mapping(self, rank, max_num_tokens=None):

@@ -57,7 +57,10 @@ def _step(w, vals, partition_size=None, planned=True):
     from paged_kv_cache_123_amd.step import DecodeStep
     ps = w.partition_size if partition_size is None else partition_size
     return DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
-                      w.scale, ps, planned=planned)
+                      w.scale, ps, planned=planned,
+                      all_queries=w.extra.get("queries") == "all",
+                      sliding_window=w.extra.get("sliding_window", 0),
+                      kernel_block_size=w.extra.get("kernel_block_size", 0))
 
 
 def full_parity(w, partition_size=None, planned=True):

@@ -44,3 +44,27 @@ def test_plan_gives_no_item_to_an_empty_split_sequence():
     # a rank-local share can be empty under context parallelism
     items = decode_plan([40, 0, 17], 16).tolist()
     assert {tuple(x) for x in items} == {(0, 0), (0, 1), (0, 2), (2, 0), (2, 1)}
+
+
+@pytest.mark.parametrize("P", [0, 16, 64])
+@pytest.mark.parametrize("W", [1, 7, 100, 5000])
+def test_window_plan_covers_the_window_only(P, W):
+    rng = np.random.default_rng(P + W)
+    lens = rng.integers(1, 3000, size=23).tolist()
+    qlens = [int(min(L, x)) for L, x in zip(lens, rng.integers(1, 5, size=23))]
+    items = decode_plan(lens, P, W, qlens).tolist()
+    want = set()
+    for s, (L, n) in enumerate(zip(lens, qlens)):
+        lo = max(0, L - n + 1 - W)
+        if P == 0:
+            want.add((s, 0))
+        else:
+            want |= {(s, p) for p in range(-(-L // P)) if (p + 1) * P > lo}
+    assert len(items) == len(want) and {tuple(x) for x in items} == want
+    # window 0 and no query lengths: the plain plan
+    assert decode_plan(lens, P, 0, None).tolist() == decode_plan(lens, P).tolist()
+
+
+def test_window_plan_rejects_a_query_longer_than_its_context():
+    with pytest.raises(PagedKVError):
+        decode_plan([5, 3], 16, 4, [1, 4])

@@ -92,17 +92,27 @@ def _decode_batch(name, seed, lens, *, dtype, H, Hkv, D, B, num_blocks, sigma,
                     partition_size=partition_size, notes=notes)
 
 
+def _options(w, sliding_window=0, kernel_block_size=0):
+    """Record a sliding window and a kernel block size on a workload."""
+    if sliding_window:
+        w.extra["sliding_window"] = int(sliding_window)
+    if kernel_block_size and kernel_block_size != w.block_size:
+        w.extra["kernel_block_size"] = int(kernel_block_size)
+    return w
+
+
 def custom_decode(name, seed, lens, *, dtype, H, Hkv, D, B, num_blocks=None, sigma=1.0,
-                  partition_size=0):
+                  partition_size=0, sliding_window=0, kernel_block_size=0):
     """A decode batch with the given context lengths (edge-case tests)."""
     lens = [int(L) for L in lens]
     nb = num_blocks if num_blocks is not None else _blocks_for(lens, B) + 3
-    return _decode_batch(name, seed, lens, dtype=dtype, H=H, Hkv=Hkv, D=D, B=B,
-                         num_blocks=nb, sigma=sigma, partition_size=partition_size)
+    w = _decode_batch(name, seed, lens, dtype=dtype, H=H, Hkv=Hkv, D=D, B=B,
+                      num_blocks=nb, sigma=sigma, partition_size=partition_size)
+    return _options(w, sliding_window, kernel_block_size)
 
 
 def custom_forks(name, seed, prompts, samples, appends, *, dtype, H, Hkv, D, B,
-                 partition_size=0, sigma=1.0):
+                 partition_size=0, sigma=1.0, sliding_window=0, kernel_block_size=0):
     """Parallel-sampling batch for edge-case tests: prompt g is prefilled once
     and forked into ``samples`` sequences; sample j of group g then appends
     appends[g][j] tokens (several tokens per sample, across block and
@@ -120,10 +130,11 @@ def custom_forks(name, seed, prompts, samples, appends, *, dtype, H, Hkv, D, B,
             lens.append(int(P) + int(appends[g][j]))
     nb = _blocks_for(prompts, B) + sum(-(-int(a) // B) + 1 for row in appends for a in row) + 4
     order = rng.permutation(nb).astype(np.int32)
-    return Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
-                    block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(D), sigma=sigma,
-                    seed=seed, free_order=order, seqs=seqs, prefill=prefill, step=step,
-                    context_lens=lens, partition_size=partition_size)
+    w = Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                 block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(D), sigma=sigma,
+                 seed=seed, free_order=order, seqs=seqs, prefill=prefill, step=step,
+                 context_lens=lens, partition_size=partition_size)
+    return _options(w, sliding_window, kernel_block_size)
 
 
 def _blocks_for(lens, B) -> int:
@@ -225,6 +236,21 @@ def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
     return w
 
 
+def mistral7b_swa_bf16(num_seqs=64, window=4096):
+    """A Mistral-7B-style layer (32 query heads sharing 8 KV heads, head 128)
+    with a 4096-token sliding window over contexts up to 16k: attention reads
+    the last 4096 tokens of each sequence, and the blocks before the window
+    are released before the step."""
+    rng = np.random.default_rng(6)
+    lens = rng.integers(2048, 16385, size=64)[:num_seqs]
+    w = _decode_batch("mistral7b_swa_bf16", 6, lens, dtype="bf16", H=32, Hkv=8, D=128, B=16,
+                      num_blocks=math.ceil(1.05 * _blocks_for(lens, 16)), sigma=1.0,
+                      partition_size=0, rng=rng,
+                      notes=f"{num_seqs} seqs L~U[2048,16384], 32q/8kv x 128 bf16, B=16, "
+                            f"sliding window {window}, single pass")
+    return _options(w, sliding_window=window)
+
+
 def cp_decode(name, seed, lens, *, dtype, H, Hkv, D, B, world, interleave, partition_size,
               sigma=1.0, slack=1.0, notes=""):
     """A decode batch spread over a context-parallel group of ``world`` ranks.
@@ -270,6 +296,7 @@ CONFIGS = {
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
+    "mistral7b_swa_bf16": mistral7b_swa_bf16,
 }
 
 
@@ -278,7 +305,7 @@ def make(name: str, **kw) -> Workload:
 
 
 def custom_multi(name, seed, lens, new_tokens, *, dtype, H, Hkv, D, B, partition_size=0,
-                 sigma=1.0):
+                 sigma=1.0, sliding_window=0):
     """A batch whose step appends new_tokens[s] tokens to sequence s (its
     context_lens[s] = lens[s] counts them): speculative drafts or a short
     prefill chunk, every new token being a query."""
@@ -292,11 +319,12 @@ def custom_multi(name, seed, lens, new_tokens, *, dtype, H, Hkv, D, B, partition
         if L > n:
             prefill.append(("append", s, L - int(n)))
         step.append((s, int(n)))
-    return Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
-                    block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(D), sigma=sigma,
-                    seed=seed, free_order=order, seqs=list(range(len(lens))), prefill=prefill,
-                    step=step, context_lens=lens, partition_size=partition_size,
-                    extra={"queries": "all"})
+    w = Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                 block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(D), sigma=sigma,
+                 seed=seed, free_order=order, seqs=list(range(len(lens))), prefill=prefill,
+                 step=step, context_lens=lens, partition_size=partition_size,
+                 extra={"queries": "all"})
+    return _options(w, sliding_window)
 
 
 def make_values(w: Workload, device, chunk_elems: int = 1 << 26):
@@ -325,7 +353,8 @@ def make_values(w: Workload, device, chunk_elems: int = 1 << 26):
             flat[i:j] = (x * w.sigma).to(tdt)
         return out
 
-    cache_shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_size)
+    kb = w.extra.get("kernel_block_size", w.block_size)  # kernel blocks of the cache
+    cache_shape = (w.num_blocks * (w.block_size // kb), w.num_kv_heads, kb, w.head_size)
     return {
         "key_cache": draw(cache_shape),
         "value_cache": draw(cache_shape),
