@@ -43,9 +43,12 @@ Parity status per function (what pins it is listed in each module header):
   attention.* with window > 0,
   allocator.OraclePool.remove_skipped . pinned (banded dense softmax, closed
                                         forms, released blocks never read)
+  prefix_cache.* ...................... pinned (FIPS 180 digests, chaining,
+                                        first-miss stop, n - 1 cap, full
+                                        blocks only, LRU eviction, touch)
   dtypes.decode ....................... pinned (bit patterns with known values)
 """
 
-from . import allocator, attention, cache_ops, dtypes, slots  # noqa: F401
+from . import allocator, attention, cache_ops, dtypes, prefix_cache, slots  # noqa: F401
 
-__all__ = ["allocator", "attention", "cache_ops", "dtypes", "slots"]
+__all__ = ["allocator", "attention", "cache_ops", "dtypes", "prefix_cache", "slots"]

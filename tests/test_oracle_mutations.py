@@ -12,11 +12,13 @@ import pytest
 
 import oracle.allocator as alloc_mod
 import oracle.attention as attn_mod
+import oracle.prefix_cache as pc_mod
 import oracle.slots as slots_mod
 import test_oracle_allocator as TA
 import test_oracle_attention as TT
 import test_oracle_cp as TC
 import test_oracle_slots as TS
+import test_oracle_prefix_cache as TP
 import test_oracle_window as TW
 
 
@@ -70,6 +72,28 @@ def _partial_unnormalised(q, K, V, scale):
     m = x.max()
     w = np.exp(x - m)
     return m, w.sum(), w @ V
+
+
+class _PrefixSkipsMisses(pc_mod.OraclePrefixPool):
+    def longest_hit(self, keys, max_length):
+        return [self.cached[k] for k in keys[:max_length // self.block_size] if k in self.cached]
+
+
+class _PrefixNoLastTokenCap(pc_mod.OraclePrefixPool):
+    def longest_hit(self, keys, max_length):
+        return super().longest_hit(keys, max_length + 1)
+
+
+class _PrefixNoEviction(pc_mod.OraclePrefixPool):
+    def _take(self):
+        return alloc_mod.OraclePool._take(self)
+
+
+_block_key = pc_mod.block_key
+
+
+def _key_without_parent(parent, tokens, extra=b""):
+    return _block_key(pc_mod.ROOT_KEY, tokens, extra)
 
 
 def _kernel_blocks_strided(ids, k):
@@ -187,6 +211,11 @@ MUTATIONS = [
     ("window ignored", attn_mod, "window_start", lambda p, w: 0, TW),
     ("skipped tokens off by one", alloc_mod, "num_skipped_tokens",
      lambda n, w: max(0, n - w) if w > 0 else 0, TW),
+    ("block key ignores the parent key", pc_mod, "block_key", _key_without_parent, TP),
+    ("prefix lookup skips misses", pc_mod, "OraclePrefixPool", _PrefixSkipsMisses, TP),
+    ("prefix lookup may cover the last token", pc_mod, "OraclePrefixPool",
+     _PrefixNoLastTokenCap, TP),
+    ("reused blocks keep their cache key", pc_mod, "OraclePrefixPool", _PrefixNoEviction, TP),
     ("free returns blocks to the queue head", alloc_mod, "OraclePool", _PoolFreeToHead, TA),
     ("COW keeps the old reference", alloc_mod, "OraclePool", _PoolCowKeepsRef, TA),
     ("no copy-on-write", alloc_mod, "OraclePool", _PoolNoCow, TA),
@@ -198,15 +227,16 @@ MUTATIONS = [
 def test_planted_mistake_is_caught(monkeypatch, label, module, name, replacement, pins):
     monkeypatch.setattr(module, name, replacement)
     # test modules bound some names at import time: patch those bindings too
-    for mod in (TA, TT, TS, TC, TW):
+    for mod in (TA, TT, TS, TC, TW, TP):
         if hasattr(mod, name):
             monkeypatch.setattr(mod, name, replacement)
     with np.errstate(all="ignore"):
         assert _some_pin_fails(_all(pins)), f"no pin noticed: {label}"
 
 
-@pytest.mark.parametrize("pins", [TA, TT, TS, TC, TW],
-                         ids=["allocator", "attention", "slots", "context_parallel", "window"])
+@pytest.mark.parametrize("pins", [TA, TT, TS, TC, TW, TP],
+                         ids=["allocator", "attention", "slots", "context_parallel", "window",
+                              "prefix_cache"])
 def test_unmutated_oracle_passes_every_pin(pins):
     """Control: the harness above reports no failure for the real oracle."""
     assert not _some_pin_fails(_all(pins))
