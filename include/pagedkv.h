@@ -440,6 +440,55 @@ int64_t pa_pool_num_cow(const pa_pool* pool);
 int32_t pa_pool_remove_skipped(pa_pool* pool, int64_t seq, int64_t num_computed_tokens,
                                int32_t sliding_window, int32_t* num_released);
 
+/* ------------------------------------------------------------------------
+ * Prefix caching on the host ([DEEPSONAR] section 2.4; [CSDN] sections
+ * 3.2.1-3.2.3, 5.2 and 5.3; [PUFANYI] "共享前缀，分叉时 Copy-on-write").
+ * Every full block of a request is keyed by a chained SHA-256 over the
+ * parent block's key, the block's token ids and the request's extra key
+ * bytes (e.g. an adapter id), so equal keys mean equal whole prefixes.
+ * Message layout (this library's reading; the pages name the three inputs
+ * only): parent key (32 bytes) || token ids as little-endian int32 ||
+ * extra bytes; the first block's parent key is 32 zero bytes.
+ *
+ * A new request takes over its longest run of cached blocks from the start
+ * of its prompt, stopping at the first key that is not cached and at
+ * (prompt length - 1) / B blocks: the last prompt token is always computed
+ * again.  Taken-over blocks gain a holder (one with none leaves the free
+ * queue).  Freed cached blocks keep their key while they wait in the free
+ * queue, which is the LRU order: a block taken from its head for new tokens
+ * loses its key (eviction).  A key already held by another block keeps that
+ * block.
+ *
+ * pa_pool_enable_prefix_caching: switch the cache on; only before the first
+ *   sequence.  PA_EINVAL otherwise.
+ * pa_pool_add_seq_cached: new sequence for a prompt of host int32 token ids;
+ *   *num_computed_tokens receives how many prompt tokens came from the cache
+ *   (a multiple of B); the caller appends the rest with
+ *   pa_pool_append_tokens.  PA_EINVAL when caching is off, the sequence
+ *   exists or an argument is bad.
+ * pa_pool_append_tokens: pa_pool_append that also records the token ids
+ *   (host int32 [n]); plain pa_pool_append stops a sequence's recording and
+ *   then pa_pool_cache_full_blocks refuses it.
+ * pa_pool_cache_full_blocks: key every full block of seq that has no key yet
+ *   (after its K/V were written); *num_cached (may be NULL) receives how many
+ *   blocks were added to the cache.
+ * pa_pool_num_cached_blocks / pa_pool_num_evicted: cache size and evictions
+ *   so far (-1 for a null pool).
+ * pa_block_keys (host only): the key chain of a token sequence, 32 bytes per
+ *   full block into keys_out [num_tokens / block_size][32].
+ * ---------------------------------------------------------------------- */
+int32_t pa_pool_enable_prefix_caching(pa_pool* pool);
+int32_t pa_pool_add_seq_cached(pa_pool* pool, int64_t seq, const int32_t* prompt,
+                               int64_t num_prompt_tokens, const void* extra,
+                               int32_t extra_bytes, int64_t* num_computed_tokens);
+int32_t pa_pool_append_tokens(pa_pool* pool, int64_t seq, const int32_t* tokens, int32_t n,
+                              int64_t* slots_out, int64_t* cow_pair_out, int32_t* n_cow_out);
+int32_t pa_pool_cache_full_blocks(pa_pool* pool, int64_t seq, int32_t* num_cached);
+int64_t pa_pool_num_cached_blocks(const pa_pool* pool);
+int64_t pa_pool_num_evicted(const pa_pool* pool);
+int32_t pa_block_keys(const int32_t* tokens, int64_t num_tokens, int32_t block_size,
+                      const void* extra, int32_t extra_bytes, uint8_t* keys_out);
+
 /* Kernel blocks ([CSDN] section 3.4, hybrid block sizes): when the
  * allocator's blocks hold k = blocks_per_kv_block smaller blocks of the
  * kernels, manager block b stands for kernel blocks b*k .. b*k + k - 1.

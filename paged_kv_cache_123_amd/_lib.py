@@ -74,6 +74,13 @@ SIGNATURES = {
     "pa_pool_num_cow": (_i64, [_vp]),
     "pa_pool_remove_skipped": (_i32, [_vp, _i64, _i64, _i32, _pi32]),
     "pa_map_to_kernel_blocks": (_i32, [_pi32, _i64, _i32, _pi32]),
+    "pa_pool_enable_prefix_caching": (_i32, [_vp]),
+    "pa_pool_add_seq_cached": (_i32, [_vp, _i64, _pi32, _i64, _vp, _i32, _pi64]),
+    "pa_pool_append_tokens": (_i32, [_vp, _i64, _pi32, _i32, _pi64, _pi64, _pi32]),
+    "pa_pool_cache_full_blocks": (_i32, [_vp, _i64, _pi32]),
+    "pa_pool_num_cached_blocks": (_i64, [_vp]),
+    "pa_pool_num_evicted": (_i64, [_vp]),
+    "pa_block_keys": (_i32, [_pi32, _i64, _i32, _vp, _i32, _vp]),
 }
 
 _LIB = None

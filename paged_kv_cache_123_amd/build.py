@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 HIP_SOURCES = ["cache_kernels.hip", "attention_kernels.hip", "attention_mfma.hip", "capi.hip",
                "probe_kernels.hip"]
-CXX_SOURCES = ["context_parallel.cpp", "block_pool.cpp", "plan.cpp", "status.cpp"]
+CXX_SOURCES = ["context_parallel.cpp", "sha256.cpp", "block_pool.cpp", "plan.cpp", "status.cpp"]
 
 # Packed-fp32 instructions are kept out of every HIP build.
 HIPCC_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -1,5 +1,9 @@
 // Host block allocator: physical block pool with reference counts and
-// copy-on-write, producing the block tables and slots the kernels consume.
+// copy-on-write, producing the block tables and slots the kernels consume,
+// with an optional prefix cache over its blocks ([DEEPSONAR] section 2.4;
+// [CSDN] sections 3.2.1-3.2.3 and 5.2-5.3): full blocks are keyed by a
+// chained SHA-256, a new request takes over its longest cached prefix, and
+// the free queue is the LRU list whose head is evicted when reused.
 //
 // Semantics ([PUFANYI] "按 Block 分配"; [CSDN] sections 3.1.2, 3.2.1, 3.2.3,
 // 3.2.4; [VLLBC] paper section 4.4 / Fig. 8) are described in pagedkv.h.
@@ -11,11 +15,13 @@
 // an arbitrary block are all O(1) with no allocation after creation.
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <string>
 #include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
+#include "sha256.h"
 #include "status.h"
 
 namespace {
@@ -23,7 +29,47 @@ namespace {
 struct Seq {
   std::vector<int32_t> blocks;
   int64_t len = 0;
+  // prefix caching: the token ids behind the blocks (tracked == false once
+  // tokens were appended without ids) and the request's extra key bytes
+  bool tracked = false;
+  std::vector<int32_t> tokens;
+  std::string extra;
 };
+
+struct DigestHash {
+  size_t operator()(const pa::Digest& d) const {
+    size_t h;
+    std::memcpy(&h, d.data(), sizeof h);
+    return h;
+  }
+};
+
+// Key of one full block: SHA-256 of parent key || int32 LE token ids || extra.
+pa::Digest block_key(const pa::Digest& parent, const int32_t* tokens, int32_t n,
+                     const std::string& extra) {
+  std::vector<uint8_t> tok(static_cast<size_t>(n) * 4);
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t v = static_cast<uint32_t>(tokens[i]);
+    for (int b = 0; b < 4; ++b) tok[4 * i + b] = static_cast<uint8_t>(v >> (8 * b));
+  }
+  const uint8_t* parts[3] = {parent.data(), tok.data(),
+                             reinterpret_cast<const uint8_t*>(extra.data())};
+  const size_t sizes[3] = {parent.size(), tok.size(), extra.size()};
+  return pa::sha256(parts, sizes, 3);
+}
+
+// Keys of the full blocks of a token sequence, each chained on the one before;
+// the first block's parent is 32 zero bytes.
+std::vector<pa::Digest> key_chain(const int32_t* tokens, int64_t n, int32_t block_size,
+                                  const std::string& extra) {
+  std::vector<pa::Digest> keys;
+  pa::Digest parent{};
+  for (int64_t j = 0; (j + 1) * block_size <= n; ++j) {
+    parent = block_key(parent, tokens + j * block_size, block_size, extra);
+    keys.push_back(parent);
+  }
+  return keys;
+}
 
 }  // namespace
 
@@ -38,6 +84,12 @@ struct pa_pool {
   int32_t head = kNone, tail = kNone, num_free = 0;
   std::unordered_map<int64_t, Seq> seqs;
   int64_t num_cow = 0;
+  // prefix cache: key of each cached block, and key -> block
+  bool caching = false;
+  std::vector<pa::Digest> key_of;
+  std::vector<uint8_t> has_key;
+  std::unordered_map<pa::Digest, int32_t, DigestHash> cached;
+  int64_t num_evicted = 0;
 
   void push_tail(int32_t b) {
     prev[b] = tail;
@@ -56,10 +108,27 @@ struct pa_pool {
     --num_free;
     return b;
   }
+  void unlink(int32_t b) {  // take b out of the free queue wherever it is
+    if (prev[b] != kNone) next[prev[b]] = next[b]; else head = next[b];
+    if (next[b] != kNone) prev[next[b]] = prev[b]; else tail = prev[b];
+    prev[b] = next[b] = kNone;
+    queued[b] = 0;
+    --num_free;
+  }
   int32_t take() {  // caller checked num_free
     int32_t b = pop_head();
+    if (caching && has_key[b]) {  // the LRU head still holds cached content
+      auto it = cached.find(key_of[b]);
+      if (it != cached.end() && it->second == b) cached.erase(it);
+      has_key[b] = 0;
+      ++num_evicted;
+    }
     ref[b] = 1;
     return b;
+  }
+  void touch(int32_t b) {  // a cache hit: a block without holders leaves the queue
+    if (ref[b] == 0) unlink(b);
+    ref[b] += 1;
   }
   int64_t fresh_blocks_needed(const Seq& s, int32_t n) const {
     const int64_t B = block_size;
@@ -148,6 +217,7 @@ int32_t pa_pool_append(pa_pool* pool, int64_t seq, int32_t n, int64_t* slots_out
     slots_out[i] = static_cast<int64_t>(s.blocks[s.len / B]) * B + s.len % B;
     s.len += 1;
   }
+  s.tracked = false;  // token ids unknown from here on: no longer cacheable
   return PA_OK;
 }
 
@@ -264,6 +334,104 @@ int32_t pa_pool_free_queue(const pa_pool* pool, int32_t* out, int32_t cap) {
 }
 
 int64_t pa_pool_num_cow(const pa_pool* pool) { return pool ? pool->num_cow : -1; }
+
+int32_t pa_pool_enable_prefix_caching(pa_pool* pool) {
+  if (!pool) return pa::fail(PA_EINVAL, "pa_pool_enable_prefix_caching: pool is NULL");
+  if (!pool->seqs.empty())
+    return pa::fail(PA_EINVAL, "pa_pool_enable_prefix_caching: the pool already has sequences");
+  pool->caching = true;
+  pool->key_of.assign(pool->num_blocks, pa::Digest{});
+  pool->has_key.assign(pool->num_blocks, 0);
+  return PA_OK;
+}
+
+int32_t pa_pool_add_seq_cached(pa_pool* pool, int64_t seq, const int32_t* prompt,
+                               int64_t num_prompt_tokens, const void* extra,
+                               int32_t extra_bytes, int64_t* num_computed_tokens) {
+  if (!pool || (!prompt && num_prompt_tokens > 0) || num_prompt_tokens < 0 || extra_bytes < 0 ||
+      (!extra && extra_bytes > 0) || !num_computed_tokens)
+    return pa::fail(PA_EINVAL, "pa_pool_add_seq_cached: bad argument");
+  if (!pool->caching)
+    return pa::fail(PA_EINVAL, "pa_pool_add_seq_cached: prefix caching is not enabled");
+  if (pool->seqs.count(seq)) return pa::fail(PA_EINVAL, "pa_pool_add_seq_cached: sequence exists");
+  Seq s;
+  s.tracked = true;
+  if (extra_bytes > 0) s.extra.assign(static_cast<const char*>(extra), extra_bytes);
+  // the last prompt token is always computed again: at most n - 1 from the cache
+  const int64_t max_blocks = num_prompt_tokens > 0 ? (num_prompt_tokens - 1) / pool->block_size : 0;
+  const std::vector<pa::Digest> keys =
+      key_chain(prompt, max_blocks * pool->block_size, pool->block_size, s.extra);
+  for (const pa::Digest& k : keys) {  // stop at the first miss
+    auto it = pool->cached.find(k);
+    if (it == pool->cached.end()) break;
+    s.blocks.push_back(it->second);
+  }
+  for (int32_t b : s.blocks) pool->touch(b);
+  s.len = static_cast<int64_t>(s.blocks.size()) * pool->block_size;
+  s.tokens.assign(prompt, prompt + s.len);
+  *num_computed_tokens = s.len;
+  pool->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+int32_t pa_pool_append_tokens(pa_pool* pool, int64_t seq, const int32_t* tokens, int32_t n,
+                              int64_t* slots_out, int64_t* cow_pair_out, int32_t* n_cow_out) {
+  if (!pool || !tokens) return pa::fail(PA_EINVAL, "pa_pool_append_tokens: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return pa::fail(PA_EINVAL, "pa_pool_append_tokens: unknown sequence");
+  const bool tracked = it->second.tracked;
+  const int32_t st = pa_pool_append(pool, seq, n, slots_out, cow_pair_out, n_cow_out);
+  if (st != PA_OK) return st;
+  Seq& s = pool->seqs.find(seq)->second;
+  s.tracked = tracked;
+  if (tracked) s.tokens.insert(s.tokens.end(), tokens, tokens + n);
+  return PA_OK;
+}
+
+int32_t pa_pool_cache_full_blocks(pa_pool* pool, int64_t seq, int32_t* num_cached) {
+  if (!pool) return pa::fail(PA_EINVAL, "pa_pool_cache_full_blocks: pool is NULL");
+  if (!pool->caching)
+    return pa::fail(PA_EINVAL, "pa_pool_cache_full_blocks: prefix caching is not enabled");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return pa::fail(PA_EINVAL, "pa_pool_cache_full_blocks: unknown sequence");
+  Seq& s = it->second;
+  if (!s.tracked)
+    return pa::fail(PA_EINVAL, "pa_pool_cache_full_blocks: the sequence's token ids are unknown");
+  const std::vector<pa::Digest> keys =
+      key_chain(s.tokens.data(), s.len, pool->block_size, s.extra);
+  int32_t n = 0;
+  for (size_t j = 0; j < keys.size(); ++j) {
+    const int32_t b = s.blocks[j];
+    if (b < 0 || pool->has_key[b]) continue;
+    if (pool->cached.count(keys[j])) continue;  // another block holds this content
+    pool->key_of[b] = keys[j];
+    pool->has_key[b] = 1;
+    pool->cached.emplace(keys[j], b);
+    ++n;
+  }
+  if (num_cached) *num_cached = n;
+  return PA_OK;
+}
+
+int64_t pa_pool_num_cached_blocks(const pa_pool* pool) {
+  return pool ? static_cast<int64_t>(pool->cached.size()) : -1;
+}
+
+int64_t pa_pool_num_evicted(const pa_pool* pool) { return pool ? pool->num_evicted : -1; }
+
+int32_t pa_block_keys(const int32_t* tokens, int64_t num_tokens, int32_t block_size,
+                      const void* extra, int32_t extra_bytes, uint8_t* keys_out) {
+  if ((!tokens && num_tokens > 0) || num_tokens < 0 || block_size < 1 || extra_bytes < 0 ||
+      (!extra && extra_bytes > 0) || (!keys_out && num_tokens >= block_size))
+    return pa::fail(PA_EINVAL, "pa_block_keys: bad argument");
+  std::string x;
+  if (extra_bytes > 0) x.assign(static_cast<const char*>(extra), extra_bytes);
+  const std::vector<pa::Digest> keys = key_chain(tokens, num_tokens, block_size, x);
+  for (size_t j = 0; j < keys.size(); ++j) std::memcpy(keys_out + 32 * j, keys[j].data(), 32);
+  return PA_OK;
+}
 
 int32_t pa_map_to_kernel_blocks(const int32_t* manager_ids, int64_t n,
                                 int32_t blocks_per_kv_block, int32_t* kernel_ids) {

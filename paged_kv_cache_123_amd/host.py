@@ -117,3 +117,52 @@ class Pool:
 
     def num_cow(self) -> int:
         return int(lib().pa_pool_num_cow(self._h))
+
+    # ---- prefix caching ----------------------------------------------------
+    def enable_prefix_caching(self) -> None:
+        check(lib().pa_pool_enable_prefix_caching(self._h))
+
+    def add_seq_cached(self, seq: int, prompt, extra: bytes = b"") -> int:
+        """New sequence for ``prompt`` (token ids); returns how many of its
+        tokens were taken over from the cache."""
+        toks = np.ascontiguousarray(np.asarray(prompt, dtype=np.int32))
+        done = ctypes.c_int64(0)
+        check(lib().pa_pool_add_seq_cached(self._h, seq, _p32(toks), toks.size,
+                                           extra if extra else None, len(extra),
+                                           ctypes.byref(done)))
+        return done.value
+
+    def append_tokens(self, seq: int, tokens):
+        """append() that records the token ids for later caching."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        n = toks.size
+        slots = np.empty(n, dtype=np.int64)
+        cow = np.empty(2, dtype=np.int64)
+        n_cow = ctypes.c_int32(0)
+        st = lib().pa_pool_append_tokens(self._h, seq, _p32(toks), n, _p64(slots), _p64(cow),
+                                         ctypes.byref(n_cow))
+        if st == PA_ENOMEM:
+            raise PoolExhausted(st, lib().pa_last_error().decode())
+        check(st)
+        return slots, ((int(cow[0]), int(cow[1])) if n_cow.value else None)
+
+    def cache_full_blocks(self, seq: int) -> int:
+        n = ctypes.c_int32(0)
+        check(lib().pa_pool_cache_full_blocks(self._h, seq, ctypes.byref(n)))
+        return n.value
+
+    def num_cached_blocks(self) -> int:
+        return int(lib().pa_pool_num_cached_blocks(self._h))
+
+    def num_evicted(self) -> int:
+        return int(lib().pa_pool_num_evicted(self._h))
+
+
+def block_keys(tokens, block_size: int, extra: bytes = b"") -> list:
+    """Chained keys (32 bytes each) of the full blocks of a token sequence."""
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    nk = toks.size // block_size
+    out = np.zeros((max(nk, 1), 32), dtype=np.uint8)
+    check(lib().pa_block_keys(_p32(toks), toks.size, block_size, extra if extra else None,
+                              len(extra), out.ctypes.data))
+    return [bytes(out[j]) for j in range(nk)]
