@@ -109,6 +109,37 @@ def fused_bytes(w, step) -> int:
             + (4 * row + 8) * step.num_tokens + 4 * row * old_slots)
 
 
+def time_prefix_cache(w, min_seconds: float = 0.3) -> dict:
+    """Host cost of serving the workload's requests through the prefix cache
+    (lookup, appends and caching of full blocks on a fresh C++ pool),
+    repeated for at least ``min_seconds``."""
+    from paged_kv_cache_123_amd.host import Pool
+
+    reqs = [op for op in w.prefill if op[0] == "request"]
+    prompt_tokens = sum(len(op[2]) for op in reqs)
+    runs, elapsed, hit_tokens = 0, 0.0, 0
+    while elapsed < min_seconds:
+        pool = Pool(w.num_blocks, w.block_size, w.free_order)
+        pool.enable_prefix_caching()
+        hit_tokens = 0
+        t0 = time.perf_counter()
+        for op in w.prefill:
+            if op[0] == "request":
+                _, s, prompt, extra = op
+                done = pool.add_seq_cached(s, prompt, extra)
+                pool.append_tokens(s, prompt[done:])
+                pool.cache_full_blocks(s)
+                hit_tokens += done
+            elif op[0] == "free":
+                pool.free_seq(op[1])
+        elapsed += time.perf_counter() - t0
+        runs += 1
+    return {"requests": len(reqs), "prompt_tokens": prompt_tokens, "hit_tokens": hit_tokens,
+            "hit_fraction": hit_tokens / max(prompt_tokens, 1),
+            "us_per_request": elapsed / (runs * max(len(reqs), 1)) * 1e6,
+            "note": "C++ allocator through ctypes, one host thread"}
+
+
 def pmc_traffic(workload: str, per_launch_bytes: int):
     """HBM traffic of the attention kernel from a committed rocprofv3 counter
     summary, if it was taken on the current kernel source."""
@@ -556,6 +587,8 @@ def main():
         },
         "wall_s_timed_region": wall,
     }
+    if any(op[0] == "request" for op in w.prefill):
+        result["host_prefix_cache"] = time_prefix_cache(w)
     if not args.no_read_reference:
         ref = read_reference()
         result["read_reference_gbps"] = ref

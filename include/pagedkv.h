@@ -263,18 +263,24 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
  * partition_size > 0 the partitions wholly before the window have no item
  * and are not launched or merged.
  *
- * pa_decode_plan_window: pa_decode_plan for windowed attention.  query_lens
- * (host int32 [num_seqs], NULL = one query per sequence) gives each
- * sequence's new-token count n_s, 1 <= n_s <= its length; its first query
- * (position L_s - n_s) starts the window.  An item's size is the part of it
- * inside the window.  sliding_window == 0 gives pa_decode_plan's list.
+ * pa_decode_plan_window: pa_decode_plan for windowed attention and grouped
+ * readers.  query_lens (host int32 [num_seqs], NULL = one query per
+ * sequence) gives each sequence's new-token count n_s, 1 <= n_s <= its
+ * length; its first query (position L_s - n_s) starts the window.  An
+ * item's size is the part of it inside the window.  group_keys (host int32
+ * [num_seqs], may be NULL = the sequence index) order the items of one size
+ * bucket by key, then by (sequence, partition): sequences that read one
+ * shared prefix (e.g. key = the prefix's first block) then run together
+ * wherever they sit in the batch.  sliding_window == 0 and NULL query_lens
+ * and group_keys give pa_decode_plan's list.
  * ---------------------------------------------------------------------- */
 int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t partition_size,
                        int32_t* items, int64_t capacity, int64_t* num_items);
 
 int32_t pa_decode_plan_window(const int32_t* context_lens, const int32_t* query_lens,
-                              int32_t num_seqs, int32_t partition_size, int32_t sliding_window,
-                              int32_t* items, int64_t capacity, int64_t* num_items);
+                              const int32_t* group_keys, int32_t num_seqs,
+                              int32_t partition_size, int32_t sliding_window, int32_t* items,
+                              int64_t capacity, int64_t* num_items);
 
 int32_t pa_paged_attention_decode_planned(void* out, const void* query, const void* key_cache,
                                           const void* value_cache, const int32_t* block_tables,

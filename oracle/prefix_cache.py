@@ -13,7 +13,9 @@ What it follows:
     block and stop at the first key that is not cached; at most
     max_length // B blocks.  §5.3: max_length is the prompt length minus one
     (the last token is always computed again), only full blocks are cached
-    (cache_full_blocks), and a block records its key when it is cached.
+    (cache_full_blocks) and only those past the request's count of blocks
+    already cached (the blocks it took over count as cached), and a block
+    records its key when it is cached.
   * [CSDN] §3.2.1 / §3.2.2: a block taken from the free queue loses its key
     (eviction); §3.2.3 (touch): a hit on a block with no holder takes it out
     of the free queue and counts it.
@@ -70,6 +72,7 @@ class OraclePrefixPool(OraclePool):
         self.cached = {}                    # key -> block
         self.tokens: dict[int, list] = {}
         self.extra: dict[int, bytes] = {}
+        self.num_cached_blocks: dict[int, int] = {}  # per request
         self.num_evicted = 0
 
     def _take(self) -> int:
@@ -107,6 +110,7 @@ class OraclePrefixPool(OraclePool):
         for blk in hit:
             self._touch(blk)
         self.tables[seq] = list(hit)
+        self.num_cached_blocks[seq] = len(hit)
         n = len(hit) * self.block_size
         self.lens[seq] = n
         self.tokens[seq] = list(prompt[:n])
@@ -122,18 +126,23 @@ class OraclePrefixPool(OraclePool):
         super().fork(parent, child)
         self.tokens[child] = list(self.tokens.get(parent, []))
         self.extra[child] = self.extra.get(parent, b"")
+        self.num_cached_blocks[child] = self.num_cached_blocks.get(parent, 0)
 
     def free_seq(self, seq: int) -> None:
         super().free_seq(seq)
         self.tokens.pop(seq, None)
         self.extra.pop(seq, None)
+        self.num_cached_blocks.pop(seq, None)
 
     def cache_full_blocks(self, seq: int) -> int:
-        """Register every full block of ``seq`` under its key; returns how
-        many blocks were newly cached."""
+        """Register the full blocks of ``seq`` past its count of cached blocks
+        under their keys; returns how many blocks were newly cached."""
         keys = key_chain(self.tokens[seq], self.block_size, self.extra[seq])
         n = 0
-        for j, key in enumerate(keys):
+        start = self.num_cached_blocks[seq]
+        self.num_cached_blocks[seq] = max(start, len(keys))
+        for j in range(start, len(keys)):
+            key = keys[j]
             blk = self.tables[seq][j]
             if blk is None or self.key_of[blk] is not None:
                 continue

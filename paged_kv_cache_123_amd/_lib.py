@@ -47,7 +47,8 @@ SIGNATURES = {
                                                _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                _sz, _vp]),
     "pa_decode_plan": (_i32, [_pi32, _i32, _i32, _pi32, _i64, _pi64]),
-    "pa_decode_plan_window": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32, _i64, _pi64]),
+    "pa_decode_plan_window": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _i32, _pi32, _i64,
+                                     _pi64]),
     "pa_paged_attention_decode_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                  _i64, _vp, _vp, _sz, _i32, _vp]),

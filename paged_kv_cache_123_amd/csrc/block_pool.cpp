@@ -34,6 +34,8 @@ struct Seq {
   bool tracked = false;
   std::vector<int32_t> tokens;
   std::string extra;
+  std::vector<pa::Digest> keys;  // keys of the first keys.size() full blocks
+  size_t registered = 0;         // full blocks already offered to the cache
 };
 
 struct DigestHash {
@@ -58,17 +60,14 @@ pa::Digest block_key(const pa::Digest& parent, const int32_t* tokens, int32_t n,
   return pa::sha256(parts, sizes, 3);
 }
 
-// Keys of the full blocks of a token sequence, each chained on the one before;
-// the first block's parent is 32 zero bytes.
-std::vector<pa::Digest> key_chain(const int32_t* tokens, int64_t n, int32_t block_size,
-                                  const std::string& extra) {
-  std::vector<pa::Digest> keys;
-  pa::Digest parent{};
-  for (int64_t j = 0; (j + 1) * block_size <= n; ++j) {
-    parent = block_key(parent, tokens + j * block_size, block_size, extra);
-    keys.push_back(parent);
+// Extend a chain of block keys to the full blocks of tokens[0, n): each key
+// chains on the one before, the first block's parent being 32 zero bytes.
+void extend_keys(std::vector<pa::Digest>& keys, const int32_t* tokens, int64_t n,
+                 int32_t block_size, const std::string& extra) {
+  for (int64_t j = static_cast<int64_t>(keys.size()); (j + 1) * block_size <= n; ++j) {
+    const pa::Digest parent = j > 0 ? keys[j - 1] : pa::Digest{};
+    keys.push_back(block_key(parent, tokens + j * block_size, block_size, extra));
   }
-  return keys;
 }
 
 }  // namespace
@@ -357,15 +356,17 @@ int32_t pa_pool_add_seq_cached(pa_pool* pool, int64_t seq, const int32_t* prompt
   Seq s;
   s.tracked = true;
   if (extra_bytes > 0) s.extra.assign(static_cast<const char*>(extra), extra_bytes);
-  // the last prompt token is always computed again: at most n - 1 from the cache
-  const int64_t max_blocks = num_prompt_tokens > 0 ? (num_prompt_tokens - 1) / pool->block_size : 0;
-  const std::vector<pa::Digest> keys =
-      key_chain(prompt, max_blocks * pool->block_size, pool->block_size, s.extra);
-  for (const pa::Digest& k : keys) {  // stop at the first miss
-    auto it = pool->cached.find(k);
+  // the last prompt token is always computed again: at most n - 1 from the
+  // cache; keys are hashed block by block up to the first miss
+  const int64_t B = pool->block_size;
+  const int64_t max_blocks = num_prompt_tokens > 0 ? (num_prompt_tokens - 1) / B : 0;
+  for (int64_t j = 0; j < max_blocks; ++j) {
+    extend_keys(s.keys, prompt, (j + 1) * B, pool->block_size, s.extra);
+    auto it = pool->cached.find(s.keys[j]);
     if (it == pool->cached.end()) break;
     s.blocks.push_back(it->second);
   }
+  s.registered = s.blocks.size();  // taken-over blocks are cached already
   for (int32_t b : s.blocks) pool->touch(b);
   s.len = static_cast<int64_t>(s.blocks.size()) * pool->block_size;
   s.tokens.assign(prompt, prompt + s.len);
@@ -399,18 +400,19 @@ int32_t pa_pool_cache_full_blocks(pa_pool* pool, int64_t seq, int32_t* num_cache
   Seq& s = it->second;
   if (!s.tracked)
     return pa::fail(PA_EINVAL, "pa_pool_cache_full_blocks: the sequence's token ids are unknown");
-  const std::vector<pa::Digest> keys =
-      key_chain(s.tokens.data(), s.len, pool->block_size, s.extra);
+  extend_keys(s.keys, s.tokens.data(), s.len, pool->block_size, s.extra);
+  const size_t full = static_cast<size_t>(s.len / pool->block_size);
   int32_t n = 0;
-  for (size_t j = 0; j < keys.size(); ++j) {
+  for (size_t j = s.registered; j < full; ++j) {
     const int32_t b = s.blocks[j];
     if (b < 0 || pool->has_key[b]) continue;
-    if (pool->cached.count(keys[j])) continue;  // another block holds this content
-    pool->key_of[b] = keys[j];
+    if (pool->cached.count(s.keys[j])) continue;  // another block holds this content
+    pool->key_of[b] = s.keys[j];
     pool->has_key[b] = 1;
-    pool->cached.emplace(keys[j], b);
+    pool->cached.emplace(s.keys[j], b);
     ++n;
   }
+  s.registered = std::max(s.registered, full);
   if (num_cached) *num_cached = n;
   return PA_OK;
 }
@@ -428,7 +430,8 @@ int32_t pa_block_keys(const int32_t* tokens, int64_t num_tokens, int32_t block_s
     return pa::fail(PA_EINVAL, "pa_block_keys: bad argument");
   std::string x;
   if (extra_bytes > 0) x.assign(static_cast<const char*>(extra), extra_bytes);
-  const std::vector<pa::Digest> keys = key_chain(tokens, num_tokens, block_size, x);
+  std::vector<pa::Digest> keys;
+  extend_keys(keys, tokens, num_tokens, block_size, x);
   for (size_t j = 0; j < keys.size(); ++j) std::memcpy(keys_out + 32 * j, keys[j].data(), 32);
   return PA_OK;
 }

@@ -5,7 +5,9 @@
 // so sequences that share blocks (forks of one prompt sit next to each other
 // in a batch) still run close together in time and reuse cached blocks.
 // With a sliding window an item's size is the part of it inside the window,
-// and partitions wholly before the window are left out.
+// and partitions wholly before the window are left out.  Group keys (e.g. the
+// first block of a shared prefix) order the items of one bucket by group, so
+// the readers of one prefix run together wherever they sit in the batch.
 #include <algorithm>
 #include <cstdint>
 #include <vector>
@@ -18,13 +20,14 @@ constexpr int32_t kGranule = 256;
 }
 
 extern "C" int32_t pa_decode_plan_window(const int32_t* context_lens,
-                                         const int32_t* query_lens, int32_t num_seqs,
-                                         int32_t partition_size, int32_t sliding_window,
-                                         int32_t* items, int64_t capacity, int64_t* num_items) {
+                                         const int32_t* query_lens, const int32_t* group_keys,
+                                         int32_t num_seqs, int32_t partition_size,
+                                         int32_t sliding_window, int32_t* items,
+                                         int64_t capacity, int64_t* num_items) {
   if (!context_lens || !num_items || num_seqs < 1 || partition_size < 0 || sliding_window < 0)
     return pa::fail(PA_EINVAL, "pa_decode_plan: bad argument");
   struct Item {
-    int32_t tokens, s, p;
+    int32_t tokens, group, s, p;
   };
   std::vector<Item> v;
   for (int32_t s = 0; s < num_seqs; ++s) {
@@ -36,15 +39,17 @@ extern "C" int32_t pa_decode_plan_window(const int32_t* context_lens,
       return pa::fail(PA_EINVAL, "pa_decode_plan: query length outside [1, context length]");
     // first key the sequence's first query sees under the window
     const int32_t lo = sliding_window > 0 ? std::max(0, L - n + 1 - sliding_window) : 0;
+    // sequences with one group key (readers of one shared prefix) run together
+    const int32_t g = group_keys ? group_keys[s] : s;
     if (partition_size == 0) {
-      v.push_back({L - lo, s, 0});
+      v.push_back({L - lo, g, s, 0});
       continue;
     }
     // a sequence with no token (a rank-local share can be empty) has no item;
     // partitions wholly before the window have none either
     for (int32_t p = lo / partition_size; static_cast<int64_t>(p) * partition_size < L; ++p) {
       const int32_t begin = std::max(p * partition_size, lo);
-      v.push_back({std::min((p + 1) * partition_size, L) - begin, s, p});
+      v.push_back({std::min((p + 1) * partition_size, L) - begin, g, s, p});
     }
   }
   *num_items = static_cast<int64_t>(v.size());
@@ -52,7 +57,9 @@ extern "C" int32_t pa_decode_plan_window(const int32_t* context_lens,
   if (capacity < static_cast<int64_t>(v.size()))
     return pa::fail(PA_EINVAL, "pa_decode_plan: capacity smaller than the number of items");
   std::stable_sort(v.begin(), v.end(), [](const Item& a, const Item& b) {
-    return (a.tokens + kGranule - 1) / kGranule > (b.tokens + kGranule - 1) / kGranule;
+    const int32_t ba = (a.tokens + kGranule - 1) / kGranule;
+    const int32_t bb = (b.tokens + kGranule - 1) / kGranule;
+    return ba != bb ? ba > bb : a.group < b.group;
   });
   for (size_t i = 0; i < v.size(); ++i) {
     items[2 * i] = v[i].s;
@@ -64,6 +71,6 @@ extern "C" int32_t pa_decode_plan_window(const int32_t* context_lens,
 extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
                                   int32_t partition_size, int32_t* items, int64_t capacity,
                                   int64_t* num_items) {
-  return pa_decode_plan_window(context_lens, nullptr, num_seqs, partition_size, 0, items,
-                               capacity, num_items);
+  return pa_decode_plan_window(context_lens, nullptr, nullptr, num_seqs, partition_size, 0,
+                               items, capacity, num_items);
 }

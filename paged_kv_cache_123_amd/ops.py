@@ -247,33 +247,33 @@ def _shared_ptr(shared_prefix_blocks, S):
 
 
 def decode_plan(context_lens, partition_size: int, sliding_window: int = 0,
-                query_lens=None) -> np.ndarray:
+                query_lens=None, group_keys=None) -> np.ndarray:
     """Host work plan: int32 [num_items, 2] of (sequence, partition), every
     non-empty item once, largest first (partition_size 0: one per sequence).
     With a sliding window, only the items inside each sequence's window;
-    ``query_lens`` (new tokens per sequence) place its first query."""
+    ``query_lens`` (new tokens per sequence) place its first query.
+    ``group_keys``: items of one size bucket run in key order (readers of a
+    shared prefix together)."""
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     n = ctypes.c_int64(0)
     p32 = ctypes.POINTER(ctypes.c_int32)
-    if sliding_window == 0 and query_lens is None:
-        check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size, None, 0,
-                                   ctypes.byref(n)))
-        items = np.empty((n.value, 2), dtype=np.int32)
-        check(lib().pa_decode_plan(lens.ctypes.data_as(p32), lens.size, partition_size,
-                                   items.ctypes.data_as(p32), n.value, ctypes.byref(n)))
-        return items
-    qlens = None
-    if query_lens is not None:
-        qlens = np.ascontiguousarray(np.asarray(query_lens, dtype=np.int32))
-        if qlens.size != lens.size:
-            raise ValueError("query_lens must have one entry per sequence")
-    qp = None if qlens is None else qlens.ctypes.data_as(p32)
-    check(lib().pa_decode_plan_window(lens.ctypes.data_as(p32), qp, lens.size, partition_size,
-                                      sliding_window, None, 0, ctypes.byref(n)))
+
+    def opt(x):
+        if x is None:
+            return None, None
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+        if a.size != lens.size:
+            raise ValueError("per-sequence arrays must have one entry per sequence")
+        return a, a.ctypes.data_as(p32)
+
+    qlens, qp = opt(query_lens)
+    gkeys, gp = opt(group_keys)
+    check(lib().pa_decode_plan_window(lens.ctypes.data_as(p32), qp, gp, lens.size,
+                                      partition_size, sliding_window, None, 0, ctypes.byref(n)))
     items = np.empty((n.value, 2), dtype=np.int32)
-    check(lib().pa_decode_plan_window(lens.ctypes.data_as(p32), qp, lens.size, partition_size,
-                                      sliding_window, items.ctypes.data_as(p32), n.value,
-                                      ctypes.byref(n)))
+    check(lib().pa_decode_plan_window(lens.ctypes.data_as(p32), qp, gp, lens.size,
+                                      partition_size, sliding_window,
+                                      items.ctypes.data_as(p32), n.value, ctypes.byref(n)))
     return items
 
 

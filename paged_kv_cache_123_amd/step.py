@@ -30,7 +30,11 @@ from .host import Pool
 def replay(pool: Pool, history, appends, sliding_window: int = 0):
     """Run a batch's history and then the step's appends through ``pool``.
     With a sliding window, each row first releases the blocks its next query
-    can no longer see ([CSDN] sections 3.1.1 and 3.3.1).
+    can no longer see ([CSDN] sections 3.1.1 and 3.3.1).  History operations:
+    ("add", s), ("append", s, n), ("fork", parent, child), ("free", s), and
+    ("request", s, prompt_token_ids, extra_key_bytes): a request served
+    through the prefix cache (its longest cached prefix is taken over, the
+    rest of the prompt appended, and its full blocks cached).
 
     Returns (seqs, positions, query_start_loc, cow_pairs, cow_src): the batch
     rows, the position of every new token, the row boundaries of the new
@@ -43,6 +47,13 @@ def replay(pool: Pool, history, appends, sliding_window: int = 0):
             pool.append(op[1], op[2])
         elif op[0] == "fork":
             pool.fork(op[1], op[2])
+        elif op[0] == "free":
+            pool.free_seq(op[1])
+        elif op[0] == "request":
+            _, s, prompt, extra = op
+            done = pool.add_seq_cached(s, prompt, extra)
+            pool.append_tokens(s, prompt[done:])
+            pool.cache_full_blocks(s)
         else:
             raise ValueError(f"unknown operation {op!r}")
     seqs, positions, qsl, cow, cow_src = [], [], [0], [], []
@@ -82,6 +93,8 @@ class DecodeStep:
                  all_queries: bool = False, sliding_window: int = 0,
                  kernel_block_size: int = 0):
         self.pool = Pool(num_blocks, block_size, free_order)
+        if any(op[0] == "request" for op in history):
+            self.pool.enable_prefix_caching()
         self.sliding_window = int(sliding_window)
         seqs, positions, qsl, cow, cow_src = replay(self.pool, history, appends,
                                                     self.sliding_window)
@@ -136,8 +149,12 @@ class DecodeStep:
         if self.sliding_window and not planned:
             raise ValueError("a sliding window uses the planned launch")
         query_lens = [n for _, n in appends] if all_queries else None
+        # readers of one shared prefix (same first live block) run together
+        first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
+        groups = np.where(self.shared_blocks_host > 0, first,
+                          self.pool.num_blocks * k + np.arange(len(seqs)))
         self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
-                                         query_lens)
+                                         query_lens, groups)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self.workspace = None
         if self.partition_size:

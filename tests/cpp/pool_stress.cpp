@@ -157,9 +157,9 @@ int main() {
       q[i] = 1 + static_cast<int32_t>(rng() % std::min(lens[i], 8));
     }
     int64_t n = 0;
-    CHECK(pa_decode_plan_window(lens.data(), q.data(), S, P, W, nullptr, 0, &n) == PA_OK);
+    CHECK(pa_decode_plan_window(lens.data(), q.data(), nullptr, S, P, W, nullptr, 0, &n) == PA_OK);
     std::vector<int32_t> items(2 * n + 2);
-    CHECK(pa_decode_plan_window(lens.data(), q.data(), S, P, W, items.data(), n, &n) == PA_OK);
+    CHECK(pa_decode_plan_window(lens.data(), q.data(), lens.data(), S, P, W, items.data(), n, &n) == PA_OK);
     const int32_t world = 1 + static_cast<int32_t>(rng() % 8);
     int64_t total = 0;
     for (int32_t r = 0; r < world; ++r) {

@@ -10,6 +10,7 @@ from oracle.allocator import OraclePool
 from oracle.attention import (merge_rank_partials, paged_attention, paged_attention_multi,
                               paged_attention_partials, paged_attention_split)
 from oracle.cache_ops import copy_blocks, reshape_and_cache
+from oracle.prefix_cache import OraclePrefixPool
 from oracle.slots import (compute_slot_mapping, compute_slot_mapping_cp, cp_local_length,
                           map_to_kernel_blocks)
 
@@ -36,14 +37,23 @@ class OracleStep:
         self.window = int(w.extra.get("sliding_window", 0))
         self.kb = int(w.extra.get("kernel_block_size", 0)) or w.block_size
         k = w.block_size // self.kb
-        pool = OraclePool(w.num_blocks, w.block_size * self.world, w.free_order)
+        caching = any(op[0] == "request" for op in w.prefill)
+        pool = (OraclePrefixPool if caching else OraclePool)(
+            w.num_blocks, w.block_size * self.world, w.free_order)
         for op in w.prefill:
             if op[0] == "add":
                 pool.add_seq(op[1])
             elif op[0] == "append":
                 pool.append(op[1], op[2])
-            else:
+            elif op[0] == "fork":
                 pool.fork(op[1], op[2])
+            elif op[0] == "free":
+                pool.free_seq(op[1])
+            else:  # a request through the prefix cache
+                _, s, prompt, extra = op
+                done = pool.add_seq_cached(s, prompt, extra)
+                pool.append_tokens(s, prompt[done:])
+                pool.cache_full_blocks(s)
         positions, qsl, cow, slots = [], [0], [], []
         for s, n in w.step:
             start = pool.seq_len(s)

@@ -68,3 +68,13 @@ def test_window_plan_covers_the_window_only(P, W):
 def test_window_plan_rejects_a_query_longer_than_its_context():
     with pytest.raises(PagedKVError):
         decode_plan([5, 3], 16, 4, [1, 4])
+
+
+def test_group_keys_order_items_inside_a_bucket():
+    lens = [300, 310, 305, 320, 290]  # one 256-token bucket (257..512)
+    groups = [9, 4, 9, 4, 1]
+    items = decode_plan(lens, 0, 0, None, groups).tolist()
+    assert items == [[4, 0], [1, 0], [3, 0], [0, 0], [2, 0]]
+    # buckets still come first: a longer sequence leads whatever its key
+    items = decode_plan([300, 900, 305], 0, 0, None, [0, 5, 0]).tolist()
+    assert items == [[1, 0], [0, 0], [2, 0]]

@@ -236,6 +236,56 @@ def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
     return w
 
 
+def custom_prefix(name, seed, systems, requests, *, dtype, H, Hkv, D, B, num_blocks=None,
+                  finished=(), partition_size=0, sigma=1.0, vocab=32000):
+    """Requests served through the prefix cache.  ``systems``: lengths of the
+    shared system prompts; ``requests``: (system index or -1, suffix length)
+    per request, in arrival order; ``finished``: requests that end before the
+    decode step (freed right after the next request arrives, so their cached
+    blocks wait in the LRU queue).  Every other request then decodes one
+    token.  Token ids are drawn from ``vocab``."""
+    rng = np.random.default_rng(seed)
+    prompts = [rng.integers(0, vocab, size=int(n)).astype(np.int32) for n in systems]
+    prefill, step, seqs, lens = [], [], [], []
+    pending = []
+    for r, (g, suffix) in enumerate(requests):
+        prompt = np.concatenate([prompts[g] if g >= 0 else np.zeros(0, np.int32),
+                                 rng.integers(0, vocab, size=int(suffix)).astype(np.int32)])
+        prefill.append(("request", r, prompt, b""))
+        for f in pending:
+            prefill.append(("free", f))
+        pending = [r] if r in finished else []
+        if r not in finished:
+            step.append((r, 1))
+            seqs.append(r)
+            lens.append(len(prompt) + 1)
+    prefill += [("free", f) for f in pending]
+    if num_blocks is None:
+        num_blocks = _blocks_for([len(op[2]) + 1 for op in prefill if op[0] == "request"], B) + 4
+    order = rng.permutation(num_blocks).astype(np.int32)
+    return Workload(name=name, dtype=dtype, num_heads=H, num_kv_heads=Hkv, head_size=D,
+                    block_size=B, num_blocks=num_blocks, scale=1.0 / math.sqrt(D), sigma=sigma,
+                    seed=seed, free_order=order, seqs=seqs, prefill=prefill, step=step,
+                    context_lens=lens, partition_size=partition_size)
+
+
+def prefix_cache_bf16(num_systems=16, per_system=8):
+    """Requests that share 16 system prompts of ~1k tokens, each with a
+    private question of 16-256 tokens, arriving round-robin over the system
+    prompts: the first request of each prompt computes it, the other seven
+    take over its full blocks from the prefix cache; then all 128 decode one
+    token (32x128 MHA bf16, B=16)."""
+    rng = np.random.default_rng(7)
+    systems = (1000 + rng.integers(0, 64, size=num_systems)).tolist()
+    requests = [(g, int(rng.integers(16, 257))) for _ in range(per_system)
+                for g in range(num_systems)]
+    w = custom_prefix("prefix_cache_bf16", 7, systems, requests, dtype="bf16", H=32, Hkv=32,
+                      D=128, B=16)
+    w.notes = (f"{len(requests)} requests over {num_systems} cached system prompts of ~1k "
+               "tokens + 16-256 private tokens, one decode token each; 32x128 MHA bf16, B=16")
+    return w
+
+
 def mistral7b_swa_bf16(num_seqs=64, window=4096):
     """A Mistral-7B-style layer (32 query heads sharing 8 KV heads, head 128)
     with a 4096-token sliding window over contexts up to 16k: attention reads
@@ -297,6 +347,7 @@ CONFIGS = {
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
     "mistral7b_swa_bf16": mistral7b_swa_bf16,
+    "prefix_cache_bf16": prefix_cache_bf16,
 }
 
 
