@@ -383,6 +383,8 @@ def main_cp(args, w):
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in zip(a_start, a_end)]
     attn_avg_ms = float(np.mean(attn_ms))
+    attn_stats = {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),
+                  "p90": float(np.percentile(attn_ms, 90))}
     local_tokens = int(st.local_lens_host.sum())
     pbytes = partials_bytes(w, st.local_lens_host)
     achieved = pbytes / (attn_avg_ms * 1e-3) / 1e9
@@ -419,8 +421,7 @@ def main_cp(args, w):
             "attention_kernel": args.kernel,
         },
         "step_hbm_gbps": step_b / (ms_per_step * 1e-3) / 1e9,
-        "attention_ms": {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),
-                         "p90": float(np.percentile(attn_ms, 90))},
+        "attention_ms": attn_stats,
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_decode_mfma_kernel" if (args.kernel == "mfma" or (
@@ -497,6 +498,10 @@ def main():
     torch.cuda.synchronize()
 
     fused = not args.unfused
+    # A one-launch step without partitions is a single kernel: its average
+    # launch duration is the timed region over K, and per-launch events would
+    # only add their own gaps.  Otherwise events bracket every attention launch.
+    per_launch = not (fused and part == 0)
     for _ in range(args.warmup):
         step.run(fused=fused)
     torch.cuda.synchronize()
@@ -511,9 +516,11 @@ def main():
     t_start.record(stream)
     for i in range(args.steps):
         if fused:
-            a_start[i].record(stream)
+            if per_launch:
+                a_start[i].record(stream)
             step.fused()
-            a_end[i].record(stream)
+            if per_launch:
+                a_end[i].record(stream)
         else:
             step.copy_blocks()
             step.slot_mapping_kernel()
@@ -525,11 +532,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    attn_ms = [a.elapsed_time(b) for a, b in zip(a_start, a_end)]
     ms_per_step = total_ms / args.steps
-    attn_avg_ms = float(np.mean(attn_ms))
+    if per_launch:
+        attn_ms = [a.elapsed_time(b) for a, b in zip(a_start, a_end)]
+        attn_stats = {"mean": float(np.mean(attn_ms)), "p10": float(np.percentile(attn_ms, 10)),
+                      "p90": float(np.percentile(attn_ms, 90))}
+    else:
+        attn_stats = {"mean": ms_per_step, "p10": None, "p90": None,
+                      "note": "one kernel launch per step: the timed region over the steps"}
+    attn_avg_ms = attn_stats["mean"]
 
-    # KV tokens the step's queries attend to (the window's share with a window)
     kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
     attn_bytes = (fused_bytes(w, step) if fused
                   else attention_bytes(w, step.context_lens_host, _query_rows(step),
@@ -569,8 +581,7 @@ def main():
             "context_tokens": int(step.context_lens_host.sum()),
         },
         "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
-        "attention_ms": {"mean": attn_avg_ms, "p10": float(np.percentile(attn_ms, 10)),
-                         "p90": float(np.percentile(attn_ms, 90))},
+        "attention_ms": attn_stats,
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_decode_mfma_kernel" if (args.kernel == "mfma" or (

@@ -138,6 +138,25 @@ int32_t pa_reshape_and_cache(const void* key, const void* value, int64_t key_str
                              int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Table check.  The kernels trust device-resident tables and lengths; this
+ * call checks them on the device, for tests and debugging: a sequence is
+ * invalid when its length is negative, when ceil(length / B) exceeds
+ * bt_stride, or when a table entry the attention reads is outside
+ * [0, num_blocks).  With sliding_window W > 0 the entries before the decode
+ * query's window (positions below length - W) are not checked, since they
+ * are never read and may be -1 (released); for several new tokens per
+ * sequence pass W + max_query_len - 1.
+ *   result  device int32 [2] (output): {number of invalid sequences, the
+ *           smallest invalid sequence or INT32_MAX when none}; written by the
+ *           call's own kernels (no prior initialisation needed)
+ * Errors: PA_EINVAL for null pointers or sizes < 1 (sliding_window < 0).
+ * ---------------------------------------------------------------------- */
+int32_t pa_validate_tables(const int32_t* block_tables, int64_t bt_stride,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           int32_t num_blocks, int32_t sliding_window, int32_t* result,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Block copy for copy-on-write.  [VLLBC] paper section 4.4 / Fig. 8 and
  * [PUFANYI] "共享前缀，分叉时 Copy-on-write": before a writer appends to a
  * shared, partly filled tail block, the whole physical block (all KV heads,

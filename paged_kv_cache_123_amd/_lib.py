@@ -39,6 +39,7 @@ SIGNATURES = {
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                     _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
+    "pa_validate_tables": (_i32, [_vp, _i64, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pa_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _f32, _i32, _vp]),
     "pa_set_decode_kernel": (_i32, [_i32]),

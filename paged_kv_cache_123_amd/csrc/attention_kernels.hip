@@ -35,6 +35,10 @@
 #include "launch.h"
 #include "pagedkv.h"
 
+#ifndef PA_VALU_OCCUPANCY
+#define PA_VALU_OCCUPANCY
+#endif
+
 namespace pa {
 namespace {
 
@@ -53,7 +57,7 @@ using namespace dev;
 // last W of them, positions from bound[v] - W on: reading starts at the first
 // vector's window, and a partition wholly before it has no work.
 template <int DT, int D, int NQ, int NW, bool FINAL>
-__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
+__global__ __launch_bounds__(NW * 64) PA_VALU_OCCUPANCY void paged_decode_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
     const void* value_cache, const int32_t* __restrict__ block_tables,
     int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,
@@ -177,27 +181,33 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(
           x[j][u] = (t < c1 && t < bound[j] && t >= lo[j]) ? d * scale_log2 : -INFINITY;
         }
       }
-      float vf[U][VEC];
-#pragma unroll
-      for (int u = 0; u < U; ++u) S::to_float(vr[u], vf[u]);
+      // new running maximum of every vector; rescale what it has so far
+      float ms[NQ];
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         float mt = m[j];
 #pragma unroll
         for (int u = 0; u < U; ++u) mt = fmaxf(mt, x[j][u]);
-        const float ms = mt == -INFINITY ? 0.0f : mt;
-        const float c = __builtin_amdgcn_exp2f(m[j] - ms);
+        ms[j] = mt == -INFINITY ? 0.0f : mt;
+        const float c = __builtin_amdgcn_exp2f(m[j] - ms[j]);
         l[j] *= c;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[j][e] *= c;
+        m[j] = mt;
+      }
+      // accumulate token by token: one V row piece is converted at a time,
+      // which keeps the live registers (and so the occupancy) down
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float pr = __builtin_amdgcn_exp2f(x[j][u] - ms);
+      for (int u = 0; u < U; ++u) {
+        float vf[VEC];
+        S::to_float(vr[u], vf);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+          const float pr = __builtin_amdgcn_exp2f(x[j][u] - ms[j]);
           l[j] += pr;
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pr, vf[u][e], acc[j][e]);
+          for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pr, vf[e], acc[j][e]);
         }
-        m[j] = mt;
       }
     };
     constexpr int NBUF = kPrefetch + 1;

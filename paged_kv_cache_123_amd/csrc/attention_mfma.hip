@@ -36,6 +36,10 @@
 #include "launch.h"
 #include "pagedkv.h"
 
+#ifndef PA_MFMA_OCCUPANCY
+#define PA_MFMA_OCCUPANCY
+#endif
+
 namespace pa {
 namespace {
 
@@ -50,7 +54,7 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
 // query head kvh * G + (c & (G - 1)); it sees the keys below its causal bound,
 // only the last W of them with a sliding window W > 0.
 template <int DT, int NQ, int NW, bool FINAL>
-__global__ __launch_bounds__(NW * 64) void paged_decode_mfma_kernel(
+__global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
     const void* value_cache, const int32_t* __restrict__ block_tables,
     int64_t bt_stride, const int32_t* __restrict__ context_lens, int32_t num_heads,

@@ -99,6 +99,45 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   }
 }
 
+// Table validation: result[0] counts the sequences whose length or table
+// entries are invalid, result[1] receives the smallest such sequence (or
+// INT32_MAX when none).  The entries read are only those the attention reads
+// (blocks [lo / B, ceil(L / B)), lo the window start), after the row width is
+// checked, so a bad length is reported rather than followed.
+__global__ void validate_init_kernel(int32_t* __restrict__ result) {
+  if (threadIdx.x == 0) {
+    result[0] = 0;
+    result[1] = INT32_MAX;
+  }
+}
+
+__global__ __launch_bounds__(256) void validate_tables_kernel(
+    const int32_t* __restrict__ block_tables, int64_t bt_stride,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t block_size,
+    int32_t num_blocks, int32_t window, int32_t* __restrict__ result) {
+  __shared__ int bad;
+  const int32_t s = blockIdx.x;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int64_t L = context_lens[s];
+  const int64_t nb = (L + block_size - 1) / block_size;
+  if (L < 0 || nb > bt_stride) {
+    if (threadIdx.x == 0) bad = 1;
+  } else {
+    const int64_t lo = window > 0 ? (L - window > 0 ? L - window : 0) : 0;
+    const int32_t* row = block_tables + static_cast<int64_t>(s) * bt_stride;
+    for (int64_t j = lo / block_size + threadIdx.x; j < nb; j += blockDim.x) {
+      const int32_t b = row[j];
+      if (b < 0 || b >= num_blocks) bad = 1;  // benign race: every writer stores 1
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && bad) {
+    atomicAdd(&result[0], 1);
+    atomicMin(&result[1], s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
@@ -167,4 +206,18 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int64_t*
   return hipGetLastError();
 }
 
+hipError_t launch_validate_tables(const int32_t* block_tables, int64_t bt_stride,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t block_size, int32_t num_blocks, int32_t window,
+                                  int32_t* result, hipStream_t stream) {
+  hipLaunchKernelGGL(validate_init_kernel, dim3(1), dim3(64), 0, stream, result);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(validate_tables_kernel, dim3(static_cast<uint32_t>(num_seqs)), dim3(256), 0,
+                     stream, block_tables, bt_stride, context_lens, num_seqs, block_size,
+                     num_blocks, window, result);
+  return hipGetLastError();
+}
+
 }  // namespace pa
+

@@ -500,4 +500,18 @@ int32_t pa_merge_attention_partials(void* out, const float* max_logits, const fl
                   "pa_merge_attention_partials");
 }
 
+int32_t pa_validate_tables(const int32_t* block_tables, int64_t bt_stride,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           int32_t num_blocks, int32_t sliding_window, int32_t* result,
+                           void* stream) {
+  if (!block_tables || !context_lens || !result)
+    return fail(PA_EINVAL, "pa_validate_tables: NULL pointer");
+  if (num_seqs < 1 || bt_stride < 1 || block_size < 1 || num_blocks < 1 || sliding_window < 0)
+    return fail(PA_EINVAL, "pa_validate_tables: bad sizes");
+  return launched(pa::launch_validate_tables(block_tables, bt_stride, context_lens, num_seqs,
+                                             block_size, num_blocks, sliding_window, result,
+                                             static_cast<hipStream_t>(stream)),
+                  "pa_validate_tables");
+}
+
 }  // extern "C"

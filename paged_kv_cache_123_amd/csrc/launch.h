@@ -28,6 +28,12 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, int64_t 
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
                               int64_t num_pairs, int64_t block_bytes, hipStream_t stream);
 
+// result: device int32 [2] = {invalid sequences, smallest invalid sequence or INT32_MAX}
+hipError_t launch_validate_tables(const int32_t* block_tables, int64_t bt_stride,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t block_size, int32_t num_blocks, int32_t window,
+                                  int32_t* result, hipStream_t stream);
+
 struct DecodeArgs {
   void* out;                 // final output (single pass) or nullptr
   const void* query;

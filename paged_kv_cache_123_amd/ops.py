@@ -139,6 +139,28 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
         _dtype(key_cache), _stream()))
 
 
+def validate_tables(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
+                    num_blocks: int, sliding_window: int = 0, result=None):
+    """Device check of tables and lengths; returns (invalid sequences, the
+    smallest invalid sequence or None).  Synchronises the stream."""
+    _dev(block_tables, context_lens)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    _contig("context_lens", context_lens)
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [num_seqs, width] with unit column stride")
+    S = context_lens.numel()
+    if block_tables.shape[0] < S:
+        raise ValueError("block_tables has fewer rows than context_lens")
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=block_tables.device)
+    check(lib().pa_validate_tables(block_tables.data_ptr(), block_tables.stride(0),
+                                   context_lens.data_ptr(), S, block_size, num_blocks,
+                                   sliding_window, result.data_ptr(), _stream()))
+    bad, first = (int(x) for x in result.cpu())
+    return bad, (None if bad == 0 else first)
+
+
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
                 block_mapping: torch.Tensor) -> None:
     """cache[dst] = cache[src] for every (src, dst) row, key and value."""

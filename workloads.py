@@ -332,9 +332,10 @@ def long_context_cp8_bf16(num_seqs=32, context_len=32768):
     """The long-context batch spread over 8 context-parallel ranks (one token
     at a time in turn): one GPU's share is 32 x 4096 tokens."""
     return cp_decode("long_context_cp8_bf16", 5, [context_len] * num_seqs, dtype="bf16", H=32,
-                     Hkv=32, D=128, B=64, world=8, interleave=1, partition_size=512, slack=1.05,
+                     Hkv=32, D=128, B=64, world=8, interleave=1, partition_size=4096,
+                     slack=1.05,
                      notes=f"{num_seqs} x {context_len} tokens over 8 context-parallel ranks "
-                           "(interleave 1), 32x128 MHA bf16, B=64, partitions of 512")
+                           "(interleave 1), 32x128 MHA bf16, B=64, partitions of 4096")
 
 
 CONFIGS = {
