@@ -38,6 +38,9 @@
 #ifndef PA_VALU_OCCUPANCY
 #define PA_VALU_OCCUPANCY
 #endif
+#ifndef PA_VALU_PIPELINE_BARRIER
+#define PA_VALU_PIPELINE_BARRIER 1
+#endif
 
 namespace pa {
 namespace {
@@ -147,29 +150,19 @@ __global__ __launch_bounds__(NW * 64) PA_VALU_OCCUPANCY void paged_decode_kernel
       return static_cast<int64_t>(phys) * blk_stride_v + head_off_v + off * LPT;
     };
 
-    // This wave's tiles are wave, wave + NW, ...; kPrefetch of them are in
-    // flight while one is consumed (a ring of kPrefetch + 1 register slots).
-    const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
-    auto load_tile = [&](int it, uint4 (&kd)[U], uint4 (&vd)[U]) {
-      const int t0 = c0 + (wave + it * NW) * kTile;
-      if (t0 >= shared_tokens) {
+    // Tile i covers tokens c0 + 16 i ..; wave w takes tiles w, w + NW, ...
+    auto load_tile = [&](auto kind, int i, uint4 (&kd)[U], uint4 (&vd)[U]) {
+      constexpr bool NT = decltype(kind)::streaming;
+      const int t0 = c0 + i * kTile;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t idx = vec_index(t0 + u * TPL + lg);
-          kd[u] = load_stream(kc + idx);
-          vd[u] = load_stream(vc + idx);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t idx = vec_index(t0 + u * TPL + lg);
-          kd[u] = load_cached(kc + idx);
-          vd[u] = load_cached(vc + idx);
-        }
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = vec_index(t0 + u * TPL + lg);
+        kd[u] = load_kv<NT>(kc + idx);
+        vd[u] = load_kv<NT>(vc + idx);
       }
     };
-    auto consume = [&](int it, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
-      const int t0 = c0 + (wave + it * NW) * kTile;
+    auto consume = [&](int i, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+      const int t0 = c0 + i * kTile;
       // scores of this lane group's U tokens for all NQ vectors (log2 domain)
       float x[NQ][U];
 #pragma unroll
@@ -210,18 +203,74 @@ __global__ __launch_bounds__(NW * 64) PA_VALU_OCCUPANCY void paged_decode_kernel
         }
       }
     };
+    // A wave's tiles of one load kind, through a ring of kPrefetch + 1
+    // register slots: tile k + kPrefetch is requested before tile k is
+    // consumed.  The steady-state loop requests unconditionally, so the wait
+    // before each consume leaves the prefetched loads in flight; the last
+    // tiles drain without prefetch.
     constexpr int NBUF = kPrefetch + 1;
-    uint4 kb[NBUF][U], vb[NBUF][U];
+    auto run = [&](auto kind, int lo, int hi) {
+      int first, my;
+      wave_tiles(lo, hi, wave, NW, first, my);
+      uint4 kb[NBUF][U], vb[NBUF][U];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j)
-      if (j < my_tiles) load_tile(j, kb[j], vb[j]);
-    for (int it = 0; it < my_tiles; it += NBUF) {
+      for (int j = 0; j < kPrefetch; ++j)
+        if (j < my) load_tile(kind, first + j * NW, kb[j], vb[j]);
+      int k = 0;
+      for (; k + NBUF - 1 + kPrefetch < my; k += NBUF) {
 #pragma unroll
-      for (int j = 0; j < NBUF; ++j) {
-        if (it + j < my_tiles) {
-          if (it + j + kPrefetch < my_tiles)
-            load_tile(it + j + kPrefetch, kb[(j + kPrefetch) % NBUF], vb[(j + kPrefetch) % NBUF]);
-          consume(it + j, kb[j], vb[j]);
+        for (int j = 0; j < NBUF; ++j) {
+          load_tile(kind, first + (k + j + kPrefetch) * NW, kb[(j + kPrefetch) % NBUF],
+                    vb[(j + kPrefetch) % NBUF]);
+#if PA_VALU_PIPELINE_BARRIER
+          // keep the scheduler from sinking these loads below the consume
+          __builtin_amdgcn_sched_barrier(0);
+#endif
+          consume(first + (k + j) * NW, kb[j], vb[j]);
+        }
+      }
+      for (; k < my; k += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          if (k + j < my) {
+            if (k + j + kPrefetch < my)
+              load_tile(kind, first + (k + j + kPrefetch) * NW, kb[(j + kPrefetch) % NBUF],
+                        vb[(j + kPrefetch) % NBUF]);
+            consume(first + (k + j) * NW, kb[j], vb[j]);
+          }
+        }
+      }
+    };
+    // Tiles that start below shared_tokens read shared blocks: cached loads;
+    // the rest stream.  Each wave still takes its tiles in index order.
+    // Measured choice of loop: the two-kind pipeline for one bf16 or fp32
+    // query vector (long context 2600 vs 2654 us); for fp16 it needs 128+
+    // VGPRs and loses to the single loop below, which keeps 4 waves per SIMD
+    // (Llama-7B 186.2 vs 185.5 us); several query vectors would spill in it.
+    if constexpr (NQ == 1 && DT != PA_F16) {
+      const int n_cached = min(ntiles, max(0, (shared_tokens - c0 + kTile - 1) / kTile));
+      run(LoadKind<false>{}, 0, n_cached);
+      run(LoadKind<true>{}, n_cached, ntiles);
+    } else {
+      // one loop with the load kind chosen per tile
+      const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
+      auto load_any = [&](int it, uint4 (&kd)[U], uint4 (&vd)[U]) {
+        const int i = wave + it * NW;
+        if (c0 + i * kTile >= shared_tokens) load_tile(LoadKind<true>{}, i, kd, vd);
+        else load_tile(LoadKind<false>{}, i, kd, vd);
+      };
+      uint4 kb[NBUF][U], vb[NBUF][U];
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j)
+        if (j < my_tiles) load_any(j, kb[j], vb[j]);
+      for (int it = 0; it < my_tiles; it += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          if (it + j < my_tiles) {
+            if (it + j + kPrefetch < my_tiles)
+              load_any(it + j + kPrefetch, kb[(j + kPrefetch) % NBUF], vb[(j + kPrefetch) % NBUF]);
+            consume(wave + (it + j) * NW, kb[j], vb[j]);
+          }
         }
       }
     }

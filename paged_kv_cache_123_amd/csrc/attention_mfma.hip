@@ -141,23 +141,17 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
       return static_cast<int64_t>(phys) * blk_stride_v + head_off_v + off * DV + vec;
     };
 
-    const int my_tiles = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
-    auto load_tile = [&](int it, uint4 (&kd)[NK], uint4 (&vd)[U]) {
-      const int t0 = c0 + (wave + it * NW) * kTile;
-      if (t0 >= shared_tokens) {
+    // Tile i covers tokens c0 + 16 i ..; wave w takes tiles w, w + NW, ...
+    auto load_tile = [&](auto kind, int i, uint4 (&kd)[NK], uint4 (&vd)[U]) {
+      constexpr bool NT = decltype(kind)::streaming;
+      const int t0 = c0 + i * kTile;
 #pragma unroll
-        for (int k = 0; k < NK; ++k) kd[k] = load_stream(kc + vec_index(t0 + k_tok, k * 4 + grp));
+      for (int k = 0; k < NK; ++k) kd[k] = load_kv<NT>(kc + vec_index(t0 + k_tok, k * 4 + grp));
 #pragma unroll
-        for (int u = 0; u < U; ++u) vd[u] = load_stream(vc + vec_index(t0 + grp + 4 * u, col));
-      } else {
-#pragma unroll
-        for (int k = 0; k < NK; ++k) kd[k] = load_cached(kc + vec_index(t0 + k_tok, k * 4 + grp));
-#pragma unroll
-        for (int u = 0; u < U; ++u) vd[u] = load_cached(vc + vec_index(t0 + grp + 4 * u, col));
-      }
+      for (int u = 0; u < U; ++u) vd[u] = load_kv<NT>(vc + vec_index(t0 + grp + 4 * u, col));
     };
-    auto consume = [&](int it, const uint4 (&kr)[NK], const uint4 (&vr)[U]) {
-      const int t0 = c0 + (wave + it * NW) * kTile;
+    auto consume = [&](int i, const uint4 (&kr)[NK], const uint4 (&vr)[U]) {
+      const int t0 = c0 + i * kTile;
       // scores of tokens grp + 4j for head col
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -201,21 +195,43 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
         o[e] = MM::k16(a, plo, o[e]);
       }
     };
+    // A wave's tiles of one load kind, through a ring of kPrefetch + 1
+    // register slots (the same pipeline as the vector kernel's).
     constexpr int NBUF = kPrefetch + 1;
-    uint4 kb[NBUF][NK], vb[NBUF][U];
+    auto run = [&](auto kind, int lo_tile, int hi_tile) {
+      int first, my;
+      wave_tiles(lo_tile, hi_tile, wave, NW, first, my);
+      uint4 kb[NBUF][NK], vb[NBUF][U];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j)
-      if (j < my_tiles) load_tile(j, kb[j], vb[j]);
-    for (int it = 0; it < my_tiles; it += NBUF) {
+      for (int j = 0; j < kPrefetch; ++j)
+        if (j < my) load_tile(kind, first + j * NW, kb[j], vb[j]);
+      int k = 0;
+      for (; k + NBUF - 1 + kPrefetch < my; k += NBUF) {
 #pragma unroll
-      for (int j = 0; j < NBUF; ++j) {
-        if (it + j < my_tiles) {
-          if (it + j + kPrefetch < my_tiles)
-            load_tile(it + j + kPrefetch, kb[(j + kPrefetch) % NBUF], vb[(j + kPrefetch) % NBUF]);
-          consume(it + j, kb[j], vb[j]);
+        for (int j = 0; j < NBUF; ++j) {
+          load_tile(kind, first + (k + j + kPrefetch) * NW, kb[(j + kPrefetch) % NBUF],
+                    vb[(j + kPrefetch) % NBUF]);
+          // keep the scheduler from sinking these loads below the consume
+          __builtin_amdgcn_sched_barrier(0);
+          consume(first + (k + j) * NW, kb[j], vb[j]);
         }
       }
-    }
+      for (; k < my; k += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          if (k + j < my) {
+            if (k + j + kPrefetch < my)
+              load_tile(kind, first + (k + j + kPrefetch) * NW, kb[(j + kPrefetch) % NBUF],
+                        vb[(j + kPrefetch) % NBUF]);
+            consume(first + (k + j) * NW, kb[j], vb[j]);
+          }
+        }
+      }
+    };
+    // tiles that start below shared_tokens read shared blocks: cached loads
+    const int n_cached = min(ntiles, max(0, (shared_tokens - c0 + kTile - 1) / kTile));
+    run(LoadKind<false>{}, 0, n_cached);
+    run(LoadKind<true>{}, n_cached, ntiles);
     __syncthreads();
   }
 

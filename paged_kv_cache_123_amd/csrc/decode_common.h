@@ -52,6 +52,26 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 #endif
 }
 
+// Load kind of a run of tiles, as a type so that each kind gets its own loop.
+template <bool NT>
+struct LoadKind {
+  static constexpr bool streaming = NT;
+};
+template <bool NT>
+__device__ __forceinline__ uint4 load_kv(const uint4* p) {
+  if constexpr (NT) return load_stream(p);
+  else return load_cached(p);
+}
+
+// First tile >= lo that wave `wave` of `nw` owns when tiles are dealt
+// round-robin (tile i belongs to wave i mod nw), and how many of its tiles lie
+// below hi.
+__device__ __forceinline__ void wave_tiles(int lo, int hi, int wave, int nw, int& first,
+                                           int& count) {
+  first = lo + ((wave - lo) % nw + nw) % nw;
+  count = first < hi ? (hi - first + nw - 1) / nw : 0;
+}
+
 constexpr int kTile = 16;          // tokens per tile
 constexpr int kChunkTokens = 2048;  // tokens whose table entries are staged at once
 constexpr float kLog2e = 1.4426950408889634f;

@@ -211,6 +211,20 @@ def long_context_bf16(num_seqs=32, context_len=32768):
                                "split-K partitions of 512, pool +5%")
 
 
+def qwen72b_gqa_tp8_bf16(num_seqs=256, partition_size=1024):
+    """One GPU's share of the GQA layer under 8-way tensor parallelism: the
+    same 256 sequences and lengths with 8 query heads and 1 KV head.  With one
+    KV head a single pass has only 256 workgroups, so the share is split into
+    partitions of 1024 tokens."""
+    w = qwen72b_gqa_bf16(num_seqs)
+    w.name = "qwen72b_gqa_tp8_bf16"
+    w.num_heads, w.num_kv_heads = 8, 1
+    w.partition_size = partition_size
+    w.notes = ("GQA layer's share on one of 8 tensor-parallel GPUs: 256 seqs lognormal lengths, "
+               "8 query heads sharing 1 KV head, head 128, bf16, B=16")
+    return w
+
+
 def llama7b_spec4_fp16(num_seqs=64, drafts=4):
     """The Llama-7B batch verifying 4 speculative tokens per sequence: every
     sequence appends 4 tokens and each of them is a query (causal)."""
@@ -347,6 +361,7 @@ CONFIGS = {
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
+    "qwen72b_gqa_tp8_bf16": qwen72b_gqa_tp8_bf16,
     "mistral7b_swa_bf16": mistral7b_swa_bf16,
     "prefix_cache_bf16": prefix_cache_bf16,
 }
