@@ -113,8 +113,8 @@ __global__ void validate_init_kernel(int32_t* __restrict__ result) {
 
 __global__ __launch_bounds__(256) void validate_tables_kernel(
     const int32_t* __restrict__ block_tables, int64_t bt_stride,
-    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t block_size,
-    int32_t num_blocks, int32_t window, int32_t* __restrict__ result) {
+    const int32_t* __restrict__ context_lens, int32_t block_size, int32_t num_blocks,
+    int32_t window, int32_t* __restrict__ result) {
   __shared__ int bad;
   const int32_t s = blockIdx.x;
   if (threadIdx.x == 0) bad = 0;
@@ -214,8 +214,8 @@ hipError_t launch_validate_tables(const int32_t* block_tables, int64_t bt_stride
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(validate_tables_kernel, dim3(static_cast<uint32_t>(num_seqs)), dim3(256), 0,
-                     stream, block_tables, bt_stride, context_lens, num_seqs, block_size,
-                     num_blocks, window, result);
+                     stream, block_tables, bt_stride, context_lens, block_size, num_blocks,
+                     window, result);
   return hipGetLastError();
 }
 

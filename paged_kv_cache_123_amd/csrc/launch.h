@@ -52,11 +52,11 @@ struct DecodeArgs {
   float* ws_out;
   const int32_t* items;      // work list [num_items][2] = (seq, partition), or nullptr
   int64_t num_items;
-  dev::AppendArgs append;    // the step's cache writes (append.qsl == nullptr: none)
-  const int32_t* shared_blocks;  // [S] leading blocks shared with other sequences, or nullptr
-  const int32_t* q_start;    // [S+1] new-token rows when every new token is a query, or nullptr
-  int32_t max_query_len;     // bound on q_start[s+1] - q_start[s] (host)
-  int32_t window;            // sliding window in tokens, 0 for none
+  dev::AppendArgs append{};  // the step's cache writes (append.qsl == nullptr: none)
+  const int32_t* shared_blocks = nullptr;  // [S] leading blocks shared with other sequences
+  const int32_t* q_start = nullptr;  // [S+1] new-token rows when every new token is a query
+  int32_t max_query_len = 0;  // bound on q_start[s+1] - q_start[s] (host)
+  int32_t window = 0;         // sliding window in tokens, 0 for none
 };
 
 // Query vectors one workgroup serves: (new tokens per sequence) x (query heads
