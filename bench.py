@@ -260,6 +260,66 @@ def cpu_baseline(w, vals, step, budget_s: float):
                       f"heads), float64 NumPy, 1 BLAS thread, {t_used:.1f} s"}
 
 
+def _cpu_worker(job):
+    """One CPU worker of the multi-core oracle baseline: builds host inputs for
+    its sequences from the workload recipe (values drawn on the CPU with the
+    workload's distribution; each sequence's blocks numbered 0..n-1) and runs
+    the oracle over them, one sequence at a time, until its budget is spent."""
+    name, rows, budget, seed = job
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle.attention import paged_attention
+
+    w = W.make(name)
+    rng = np.random.default_rng([seed, rows[0]])
+    B, hkv, D, H = w.block_size, w.num_kv_heads, w.head_size, w.num_heads
+    raw = {"f32": np.float32, "f16": np.float16}.get(w.dtype)
+
+    def draw(shape):
+        x = (rng.standard_normal(shape, dtype=np.float32) * w.sigma)
+        if raw is not None:
+            return x.astype(raw)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)  # bf16 bits (truncated)
+
+    seqs = []
+    for r in rows:
+        L = int(w.context_lens[r])
+        lo, hi = attended(w, [L])[0]
+        nb = -(-L // B)
+        seqs.append((draw((1, H, D)), draw((nb, hkv, B, D)), draw((nb, hkv, B, D)),
+                     np.arange(nb)[None, :], L, hi - lo))
+    done, used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while used < budget:
+            for q, kc, vc, table, L, n in seqs:
+                t0 = time.perf_counter()
+                paged_attention(q, kc, vc, table, [L], w.scale, w.dtype, window=window_of(w))
+                used += time.perf_counter() - t0
+                done += n
+                if used >= budget:
+                    break
+    return done, used
+
+
+def cpu_baseline_pool(w, pool, workers: int, budget_s: float):
+    """The oracle on ``workers`` processes in parallel over the sequences
+    (each with one BLAS thread): aggregate KV tokens per second."""
+    rows = [r for r in range(w.num_seqs)]
+    jobs = [(w.name, rows[i::workers], budget_s, 1234) for i in range(workers)
+            if rows[i::workers]]
+    t0 = time.perf_counter()
+    res = pool.map(_cpu_worker, jobs)
+    wall = time.perf_counter() - t0
+    done = sum(r[0] for r in res)
+    return {"value": done / max(r[1] for r in res), "unit": "KV tokens/s", "cores": len(jobs),
+            "kind": "oracle",
+            "sample": f"{len(jobs)} processes over the {w.num_seqs} sequences, each {budget_s:.0f} s "
+                      f"of float64 NumPy with one BLAS thread ({done} KV tokens in {wall:.1f} s "
+                      "wall); inputs drawn on the host with the workload's shapes and "
+                      "distribution"}
+
+
 def partials_bytes(w, local_lens) -> int:
     """Algorithmic bytes of one rank's partials call: its K/V rows, q, table
     entries and lengths (attention_bytes without the output row), plus the
@@ -462,6 +522,9 @@ def main():
                          "instead of the one-launch step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-workers", type=int, default=None,
+                    help="processes of the multi-core oracle baseline (default: the usable "
+                         "cores, at most 16; 0 = single core only)")
     ap.add_argument("--no-read-reference", action="store_true")
     ap.add_argument("--calibrate-counters", action="store_true",
                     help="only run kernels of known byte count (for rocprofv3 --pmc scaling)")
@@ -471,6 +534,16 @@ def main():
               "(sharding across GPUs is a design note, not code); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    # The multi-core oracle baseline's processes are forked here, before
+    # anything touches the GPU; they wait until the GPU timing is done.
+    pool, workers = None, 0
+    if not args.no_cpu_baseline and not args.calibrate_counters:
+        import multiprocessing
+        usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 1
+        workers = min(16, usable) if args.cpu_workers is None else args.cpu_workers
+        if workers > 1:
+            pool = multiprocessing.get_context("fork").Pool(workers)
 
     import torch
 
@@ -486,6 +559,9 @@ def main():
     w = W.make(args.workload)
     if w.extra.get("cp_world"):
         print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
+        if pool is not None:  # the context-parallel baseline is single-core
+            pool.close()
+            pool.join()
         main_cp(args, w)
         return
     part = w.partition_size if args.partition_size is None else args.partition_size
@@ -607,7 +683,15 @@ def main():
         result["roofline"]["frac_of_random_4k_read"] = achieved / best
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, vals, step, args.cpu_budget)
+        single = cpu_baseline(w, vals, step, args.cpu_budget)
+        if pool is not None and not step.all_queries:
+            result["cpu_baseline"] = cpu_baseline_pool(w, pool, workers, args.cpu_budget)
+            result["cpu_baseline"]["single_core"] = single
+        else:
+            result["cpu_baseline"] = single
+    if pool is not None:
+        pool.close()
+        pool.join()
     print(json.dumps(result), flush=True)
 
 
