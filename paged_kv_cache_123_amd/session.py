@@ -1,0 +1,113 @@
+"""A paged KV cache that lives across decode steps.
+
+`PagedKVCache` keeps the host block pool and the device K/V caches of one
+attention layer and runs one step at a time: every listed sequence appends
+its new tokens (a whole prompt, a decode token, or a few speculative tokens),
+and the step returns the attention output of each sequence's last new token
+over its whole context ([VLLBC] paper sections 4.2 and 4.4; [PUFANYI]
+"按 Block 分配" and "共享前缀，分叉时 Copy-on-write").  Sequences can fork
+(sharing every block, copy-on-write on the next append) and be freed; with a
+sliding window each step first releases the blocks the window has left
+([CSDN] sections 3.1.1 and 3.3.1).
+
+Host bookkeeping runs in the C++ allocator; every device computation is one
+`pa_decode_step` launch (copy-on-write of the old slots, scatter of the new
+rows, planned attention; plus the merge launch with partitions).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import ops
+from .host import Pool
+
+_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+class PagedKVCache:
+    """K/V caches [num_blocks, num_kv_heads, block_size, head_size] of one
+    layer plus the host allocator that hands out their blocks."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
+                 dtype: str = "f16", device="cuda", free_order=None, sliding_window: int = 0,
+                 partition_size: int = 0):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.num_kv_heads, self.head_size = int(num_kv_heads), int(head_size)
+        self.dtype = _TORCH[dtype]
+        self.device = torch.device(device)
+        self.sliding_window = int(sliding_window)
+        self.partition_size = int(partition_size)
+        self.pool = Pool(self.num_blocks, self.block_size, free_order)
+        shape = (self.num_blocks, self.num_kv_heads, self.block_size, self.head_size)
+        self.key_cache = torch.zeros(shape, dtype=self.dtype, device=self.device)
+        self.value_cache = torch.zeros(shape, dtype=self.dtype, device=self.device)
+        self._seqs: set = set()
+
+    # ---- sequences ------------------------------------------------------
+    def add(self, seq: int) -> None:
+        """A new, empty sequence (its prompt arrives with the next step)."""
+        self.pool.add_seq(seq)
+        self._seqs.add(seq)
+
+    def fork(self, parent: int, child: int) -> None:
+        """``child`` shares all of ``parent``'s blocks."""
+        self.pool.fork(parent, child)
+        self._seqs.add(child)
+
+    def free(self, seq: int) -> None:
+        self.pool.free_seq(seq)
+        self._seqs.discard(seq)
+
+    def length(self, seq: int) -> int:
+        return self.pool.seq_len(seq)
+
+    # ---- one step ---------------------------------------------------------
+    def step(self, seqs, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+             new_tokens, scale: float) -> torch.Tensor:
+        """Append new_tokens[i] tokens to seqs[i] (their K/V rows are the
+        consecutive rows of ``key`` / ``value``, [T, num_kv_heads, head_size])
+        and attend with query[i] ([S, num_heads, head_size], the last new
+        token of each sequence).  Returns out [S, num_heads, head_size]."""
+        seqs = [int(s) for s in seqs]
+        n = [int(x) for x in new_tokens]
+        if len(n) != len(seqs) or query.shape[0] != len(seqs):
+            raise ValueError("one query and one new-token count per sequence")
+        T = sum(n)
+        if key.shape[0] != T or value.shape[0] != T:
+            raise ValueError("key/value must hold the new tokens of every sequence in order")
+        # host: release what the window left behind, then allocate
+        qsl, cow_src = [0], []
+        for s, k in zip(seqs, n):
+            if k < 1:
+                raise ValueError("every sequence of a step appends at least one token")
+            start = self.pool.seq_len(s)
+            if self.sliding_window:
+                self.pool.remove_skipped(s, start, self.sliding_window)
+            _, pair = self.pool.append(s, k)
+            qsl.append(qsl[-1] + k)
+            cow_src.append(-1 if pair is None else pair[0])
+        width = max(self.pool.seq_num_blocks(s) for s in seqs)
+        tables, lens = self.pool.block_tables(seqs, width)
+        shared = self.pool.shared_prefix_blocks(seqs)
+        dev = self.device
+        # readers of one shared prefix (same first live block) run together
+        first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
+        groups = np.where(shared > 0, first, self.num_blocks + np.arange(len(seqs)))
+        plan = ops.decode_plan(lens, self.partition_size, self.sliding_window, None, groups)
+        t = {name: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for name, a in (
+            ("tables", tables), ("lens", lens), ("qsl", np.asarray(qsl, dtype=np.int32)),
+            ("cow_src", np.asarray(cow_src, dtype=np.int64)), ("plan", plan))}
+        out = torch.empty_like(query)
+        workspace = None
+        if self.partition_size:
+            workspace = ops.alloc_split_workspace(len(seqs), query.shape[1], self.head_size,
+                                                  int(lens.max()), self.partition_size, dev)
+        shared_dev = torch.from_numpy(shared).to(dev) if shared.any() else None
+        ops.decode_step(out, query, self.key_cache, self.value_cache, t["tables"], t["lens"],
+                        scale, int(lens.max()), self.partition_size, t["plan"], t["qsl"], key,
+                        value, t["cow_src"], None, workspace, shared_dev, 0,
+                        self.sliding_window)
+        self.last_tables, self.last_lens = tables, lens
+        return out
