@@ -559,10 +559,12 @@ int32_t pa_map_to_kernel_blocks(const int32_t* manager_ids, int64_t n,
  * pa_merge_attention_partials: out [num_seqs][num_heads][head_size] in the
  * storage dtype from num_parts gathered sets, rank-major:
  *   max_logits, exp_sums  device float [num_parts][num_seqs][num_heads]
- *   partial_out           device float [num_parts][num_seqs][num_heads][head_size]
+ *   partial_out           device float [num_parts][num_seqs][num_heads][head_size],
+ *                         8-byte aligned
  * Parts with l = 0 carry no weight; a row no part has a key for is 0.
  * Errors: PA_EINVAL for null pointers, num_parts < 1, num_seqs outside
- * [1, 65535], num_heads < 1, head_size not 64 or 128, an unknown dtype.
+ * [1, 65535], num_heads < 1, head_size not 64 or 128, an unknown dtype,
+ * out not aligned to its element size, partial_out not 8-byte aligned.
  * ---------------------------------------------------------------------- */
 int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* partial_out,
                                     const void* query, const void* key_cache,

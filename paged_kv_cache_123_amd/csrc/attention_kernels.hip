@@ -345,26 +345,49 @@ __global__ __launch_bounds__(NW * 64) PA_VALU_OCCUPANCY void paged_decode_kernel
 }
 
 // Merge of the parts of one (row, head): M = max m_p, a_p = l_p exp(m_p - M),
-// out = sum a_p o_p / sum a_p, summed in part order.  The parts are the
-// partitions of a split launch, or the ranks of a context-parallel group.
-// One thread per output dimension; the part weights are computed once per
-// chunk into LDS, and the o_p loads are unrolled so that eight of them are in
-// flight per thread.  A part with l_p = 0 (no visible key) has weight 0; a row
-// with no key at all merges to m = -inf, l = 0, o = 0.
+// out = sum a_p o_p / sum a_p.  The parts are the partitions of a split
+// launch, or the ranks of a context-parallel group.
+//
+// One wave per (row, head), four heads per workgroup, nothing shared between
+// waves.  Parts are taken in chunks of 64: lane i loads m and l of part
+// c0 + i, the wave reduces the maximum and the weight sum with shuffles, and
+// each lane accumulates its D/64 dims of o over the chunk, the weight of part
+// p read from lane p.  The o loads do not depend on the weights, so the first
+// kMergeBatch of them are issued before the weights are computed; a load
+// past the chunk's last part re-reads that part and gets weight 0.  A later
+// chunk rescales what was accumulated when the maximum grows.  A part with
+// l_p = 0 (no visible key) has weight 0; a row with no key at all merges to
+// m = -inf, l = 0, o = 0.
+constexpr int kMergeBatch = 16;
+
+template <int D>
+__device__ __forceinline__ void load_parts(float (&v)[kMergeBatch][D / 64], const float* o,
+                                           int64_t part_o, int i, int cn) {
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const float* q = o + static_cast<int64_t>(min(i + k, cn - 1)) * part_o;
+    if constexpr (D == 128) {
+      const float2 t = *reinterpret_cast<const float2*>(q);
+      v[k][0] = t.x;
+      v[k][1] = t.y;
+    } else {
+      v[k][0] = *q;
+    }
+  }
+}
+
 template <int DT, int D>
-__global__ __launch_bounds__(D) void merge_kernel(MergeDst dst, PartView src,
-                                                  const int32_t* __restrict__ context_lens,
-                                                  int32_t num_heads, int32_t partition_size,
-                                                  int32_t num_parts,
-                                                  const int32_t* __restrict__ q_start,
-                                                  int32_t window) {
-  constexpr int kChunk = 256;
-  constexpr int NWV = D / 64;
-  __shared__ float sw[kChunk];
-  __shared__ float red[NWV];
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(256) void merge_kernel(MergeDst dst, PartView src,
+                                                    const int32_t* __restrict__ context_lens,
+                                                    int32_t num_heads, int32_t partition_size,
+                                                    int32_t num_parts,
+                                                    const int32_t* __restrict__ q_start,
+                                                    int32_t window) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int s = blockIdx.y;
-  const int d = threadIdx.x;
+  if (h >= num_heads) return;  // no barrier below
   // split launches: only the partitions below the sequence's length exist
   const int L = context_lens ? context_lens[s] : 0;
   const int np = context_lens ? min((L + partition_size - 1) / partition_size, num_parts)
@@ -373,57 +396,64 @@ __global__ __launch_bounds__(D) void merge_kernel(MergeDst dst, PartView src,
   const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
   for (int qi = 0; qi < qlen; ++qi) {
-  const int64_t row = (qrow0 + qi) * num_heads + h;
-  // with a sliding window, partitions before this row's window hold nothing
-  const int p0 = window > 0 ? max(0, L - qlen + qi + 1 - window) / partition_size : 0;
-  const float* mrow = src.m + row * src.row_ml + static_cast<int64_t>(p0) * src.part_ml;
-  const float* lrow = src.l + row * src.row_ml + static_cast<int64_t>(p0) * src.part_ml;
-  const float* orow = src.o + row * src.row_o + static_cast<int64_t>(p0) * src.part_o + d;
-  const int nrow = np - p0;  // parts this row merges
-
-  float mx = -INFINITY;
-  for (int i = d; i < nrow; i += D) mx = fmaxf(mx, mrow[i * src.part_ml]);
+    const int64_t row = (qrow0 + qi) * num_heads + h;
+    // with a sliding window, partitions before this row's window hold nothing
+    const int p0 = window > 0 ? max(0, L - qlen + qi + 1 - window) / partition_size : 0;
+    const float* mrow = src.m + row * src.row_ml;
+    const float* lrow = src.l + row * src.row_ml;
+    const float* orow = src.o + row * src.row_o + lane * DPL;
+    float M = -INFINITY, wsum = 0.0f;
+    float acc[DPL];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((d & 63) == 0) red[d >> 6] = mx;
-  __syncthreads();
-  float M = red[0];
+    for (int j = 0; j < DPL; ++j) acc[j] = 0.0f;
+    for (int c0 = p0; c0 < np; c0 += 64) {
+      const int cn = min(64, np - c0);
+      const float* o = orow + static_cast<int64_t>(c0) * src.part_o;
+      float v[kMergeBatch][DPL];
+      load_parts<D>(v, o, src.part_o, 0, cn);
+      const int64_t k = static_cast<int64_t>(c0 + min(lane, cn - 1)) * src.part_ml;
+      const float mv = lane < cn ? mrow[k] : -INFINITY;
+      const float lv = lane < cn ? lrow[k] : 0.0f;
+      float mc = mv;
 #pragma unroll
-  for (int w = 1; w < NWV; ++w) M = fmaxf(M, red[w]);
-  const float Ms = M == -INFINITY ? 0.0f : M;
-
-  float a = 0.0f, wsum = 0.0f;
-  for (int c0 = 0; c0 < nrow; c0 += kChunk) {
-    const int cn = min(kChunk, nrow - c0);
-    __syncthreads();  // sw is rewritten
-    for (int i = d; i < cn; i += D) {
-      const int64_t k = static_cast<int64_t>(c0 + i) * src.part_ml;
-      sw[i] = lrow[k] * __builtin_amdgcn_exp2f((mrow[k] - Ms) * kLog2e);
+      for (int off = 32; off >= 1; off >>= 1) mc = fmaxf(mc, __shfl_xor(mc, off));
+      const float Mn = fmaxf(M, mc);
+      const float Ms = Mn == -INFINITY ? 0.0f : Mn;
+      // rescale the earlier chunks (nothing to rescale before the first)
+      const float corr = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((M - Ms) * kLog2e);
+      M = Mn;
+      const float w = lv * __builtin_amdgcn_exp2f((mv - Ms) * kLog2e);
+      float ws = w;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
+      wsum = wsum * corr + ws;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[j] *= corr;
+      for (int i = 0;;) {
+#pragma unroll
+        for (int kk = 0; kk < kMergeBatch; ++kk) {
+          const float wk = i + kk < cn ? __shfl(w, i + kk) : 0.0f;
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) acc[j] = fmaf(wk, v[kk][j], acc[j]);
+        }
+        i += kMergeBatch;
+        if (i >= cn) break;
+        load_parts<D>(v, o, src.part_o, i, cn);
+      }
     }
-    __syncthreads();
-    const float* o = orow + static_cast<int64_t>(c0) * src.part_o;
-    int i = 0;
-    for (; i + 8 <= cn; i += 8) {
-      float v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = o[static_cast<int64_t>(i + k) * src.part_o];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) a = fmaf(sw[i + k], v[k], a);
+    for (int j = 0; j < DPL; ++j) {
+      const float merged = wsum > 0.0f ? acc[j] / wsum : 0.0f;
+      const int64_t e = row * D + lane * DPL + j;
+      if (dst.out)
+        St<DT>::store(dst.out, e, merged);
+      else
+        dst.o[e] = merged;
     }
-    for (; i < cn; ++i) a = fmaf(sw[i], o[static_cast<int64_t>(i) * src.part_o], a);
-    for (int k = 0; k < cn; ++k) wsum += sw[k];
-  }
-  const float merged = wsum > 0.0f ? a / wsum : 0.0f;
-  if (dst.out) {
-    St<DT>::store(dst.out, row * D + d, merged);
-  } else {
-    dst.o[row * D + d] = merged;
-    if (d == 0) {
+    if (!dst.out && lane == 0) {
       dst.m[row] = M;
       dst.l[row] = wsum;
     }
-  }
-  __syncthreads();  // red and sw are reused by the next row
   }
 }
 
@@ -486,8 +516,9 @@ hipError_t launch_merge_t(const MergeDst& dst, const PartView& src, const int32_
                           int32_t num_rows, int32_t num_heads, int32_t partition_size,
                           int32_t num_parts, const int32_t* q_start, int32_t window,
                           hipStream_t stream) {
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(num_heads, num_rows), dim3(D), 0, stream, dst,
-                     src, context_lens, num_heads, partition_size, num_parts, q_start, window);
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((num_heads + 3) / 4, num_rows), dim3(256), 0,
+                     stream, dst, src, context_lens, num_heads, partition_size, num_parts, q_start,
+                     window);
   return hipGetLastError();
 }
 

@@ -494,6 +494,8 @@ int32_t pa_merge_attention_partials(void* out, const float* max_logits, const fl
     return fail(PA_EINVAL, "pa_merge_attention_partials: head_size must be 64 or 128");
   if (reinterpret_cast<uintptr_t>(out) % eb != 0)
     return fail(PA_EINVAL, "pa_merge_attention_partials: out not aligned to its element size");
+  if (reinterpret_cast<uintptr_t>(partial_out) % 8 != 0)
+    return fail(PA_EINVAL, "pa_merge_attention_partials: partial_out not 8-byte aligned");
   return launched(pa::launch_merge_ranks(out, max_logits, exp_sums, partial_out, num_parts,
                                          num_seqs, num_heads, head_size, dtype,
                                          static_cast<hipStream_t>(stream)),
