@@ -172,8 +172,12 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
 #pragma unroll
       for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - ms);
       lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      // corr is exactly 1 in a column whose maximum did not grow (and its
+      // accumulators are 0 while it has seen no key): rescale only if some did
+      if (__any(mn > m)) {
 #pragma unroll
-      for (int e = 0; e < NE; ++e) o[e] *= corr;
+        for (int e = 0; e < NE; ++e) o[e] *= corr;
+      }
       m = mn;
       uint32_t hi[4], lo[4];
 #pragma unroll
