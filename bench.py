@@ -109,6 +109,29 @@ def fused_bytes(w, step) -> int:
             + (4 * row + 8) * step.num_tokens + 4 * row * old_slots)
 
 
+def cascade_bytes(w, step) -> int:
+    """Algorithmic bytes of the one-launch step over a cascade plan: the K/V
+    rows its items read (a group item's partition once for all its members),
+    q in and out back, the table entries of the blocks read, the lengths, the
+    fp32 (m, l, o) of every (row, head, partition) written and read back by the
+    merge, and the step's cache writes as in fused_bytes."""
+    e = w.elem_bytes
+    P, B = step.partition_size, step.block_size
+    items = step.plan_host[:2 * step.num_items].reshape(-1, 2)
+    lens = step.context_lens_host
+    tokens, entries = 0, 0
+    for s, p in items.tolist():
+        n = P if s < 0 else min(P, int(lens[s]) - p * P)
+        tokens += n
+        entries += -(-n // B)
+    kv = tokens * 2 * w.num_kv_heads * w.head_size * e
+    qo = 2 * w.num_seqs * w.num_heads * w.head_size * e
+    parts = int(sum(-(-int(L) // P) for L in lens))
+    partials = 2 * parts * w.num_heads * (w.head_size + 2) * 4
+    writes = fused_bytes(w, step) - attention_bytes(w, lens)
+    return kv + qo + 4 * entries * w.num_kv_heads + 4 * w.num_seqs + partials + writes
+
+
 def time_prefix_cache(w, min_seconds: float = 0.3) -> dict:
     """Host cost of serving the workload's requests through the prefix cache
     (lookup, appends and caching of full blocks on a fresh C++ pool),
@@ -478,6 +501,9 @@ def main_cp(args, w):
             "max_context_len": int(st.max_local_len),
             "num_blocks": w.num_blocks,
             "partition_size": part,
+            "cascade_group": cascade,
+            "cascade_group_items": int((step.plan_host[:2 * step.num_items:2] < 0).sum())
+            if cascade else 0,
             "attention_kernel": args.kernel,
         },
         "step_hbm_gbps": step_b / (ms_per_step * 1e-3) / 1e9,
@@ -517,6 +543,9 @@ def main():
                     help="override the workload's split-K partition (0 = single pass)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"],
                     help="attention kernel (auto: matrix cores for grouped-query heads)")
+    ap.add_argument("--cascade", type=int, default=None,
+                    help="cascade plan with groups of at most N sharers (0: off; default: "
+                         "the workload's)")
     ap.add_argument("--unfused", action="store_true",
                     help="time copy_blocks, slot mapping, scatter and attention as four launches "
                          "instead of the one-launch step")
@@ -565,15 +594,20 @@ def main():
         main_cp(args, w)
         return
     part = w.partition_size if args.partition_size is None else args.partition_size
+    cascade = int(w.extra.get("cascade", 0) if args.cascade is None else args.cascade)
+    if cascade and not part:
+        sys.exit("a cascade plan needs --partition-size > 0")
     print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
     vals = W.make_values(w, "cuda")
     step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
                       w.scale, part, all_queries=w.extra.get("queries") == "all",
                       sliding_window=window_of(w),
-                      kernel_block_size=w.extra.get("kernel_block_size", 0))
+                      kernel_block_size=w.extra.get("kernel_block_size", 0), cascade=cascade)
     torch.cuda.synchronize()
 
     fused = not args.unfused
+    if cascade and not fused:
+        sys.exit("a cascade plan runs in the one-launch step")
     # A one-launch step without partitions is a single kernel: its average
     # launch duration is the timed region over K, and per-launch events would
     # only add their own gaps.  Otherwise events bracket every attention launch.
@@ -619,7 +653,8 @@ def main():
     attn_avg_ms = attn_stats["mean"]
 
     kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
-    attn_bytes = (fused_bytes(w, step) if fused
+    attn_bytes = (cascade_bytes(w, step) if cascade
+                  else fused_bytes(w, step) if fused
                   else attention_bytes(w, step.context_lens_host, _query_rows(step),
                                        _query_lens(step)))
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -660,9 +695,10 @@ def main():
         "attention_ms": attn_stats,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_decode_mfma_kernel" if (args.kernel == "mfma" or (
+            "kernel": ("paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
                 args.kernel == "auto" and w.num_heads > w.num_kv_heads)) else "paged_decode_kernel")
                       + (" + merge_kernel" if part else "")
+                      + (" (cascade plan)" if cascade else "")
                       + (" (one-launch step: copy-on-write + scatter + attention)" if fused
                          else ""),
             "achieved": achieved,

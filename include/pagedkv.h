@@ -301,6 +301,43 @@ int32_t pa_decode_plan_window(const int32_t* context_lens, const int32_t* query_
                               int32_t partition_size, int32_t sliding_window, int32_t* items,
                               int64_t capacity, int64_t* num_items);
 
+/* ------------------------------------------------------------------------
+ * Cascade plan (host): a decode batch in which several sequences read one
+ * prefix of physical blocks (the samples of one prompt, [VLLBC] paper
+ * section 4.4; requests that share cached prefix blocks) computes the
+ * partitions lying wholly inside that prefix once per group of sharers
+ * instead of once per sequence.  The result is the same attention: a
+ * sequence's partitions are merged exactly as in the split launch, whether a
+ * group item or its own item wrote them.
+ *   context_lens   host int32 [num_seqs], lengths after the step
+ *   block_tables   host int32 [num_seqs][bt_stride], the step's tables
+ *   new_tokens     host int32 [num_seqs] (NULL = 1 each): rows written during
+ *                  the step, the last new_tokens[s] positions of sequence s
+ * Sequences whose first table entry is the same block form a candidate
+ * group.  Its prefix is the run of leading entries every member has, cut to
+ * full blocks that end before any member's first new token; the partitions
+ * (partition_size tokens, a multiple of block_size) wholly inside it become
+ * group items, split into chunks of at most max_group_size members.  Output
+ * `plan` (host int32, capacity entries), plan_len entries in all:
+ *   [2 * num_items]  items (sequence, partition), largest first as in
+ *                    pa_decode_plan; a group item is (-1 - c, partition) for
+ *                    chunk c
+ *   [1]              number of chunks C
+ *   [C + 1]          offsets of the chunks' member lists
+ *   [offsets[C]]     members (batch rows)
+ * max_members receives the widest chunk (0 when no group formed; the plan is
+ * then an ordinary item list followed by an empty group section).  plan ==
+ * NULL returns only num_items, plan_len and max_members.
+ * Errors: PA_EINVAL for null outputs, sizes < 1, a partition_size that is not
+ * a multiple of block_size, new tokens outside [1, length], a table row
+ * shorter than its length, or capacity < plan_len.
+ * ---------------------------------------------------------------------- */
+int32_t pa_decode_plan_cascade(const int32_t* context_lens, const int32_t* block_tables,
+                               int64_t bt_stride, const int32_t* new_tokens, int32_t num_seqs,
+                               int32_t block_size, int32_t partition_size,
+                               int32_t max_group_size, int32_t* plan, int64_t capacity,
+                               int64_t* num_items, int64_t* plan_len, int32_t* max_members);
+
 int32_t pa_paged_attention_decode_planned(void* out, const void* query, const void* key_cache,
                                           const void* value_cache, const int32_t* block_tables,
                                           int64_t bt_stride, const int32_t* context_lens,
@@ -355,6 +392,34 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
                        int32_t max_query_len, int32_t sliding_window, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode_step over a cascade plan (pa_decode_plan_cascade): one query per
+ * sequence, split-K (partition_size > 0, the plan's), no sliding window.  A
+ * group item reads each K/V tile of its shared partition once for all its
+ * members (their queries are the columns of the matrix-core tiles) and
+ * writes every member's partial to that member's workspace slot; the rest is
+ * pa_decode_step.
+ *   plan            device int32, the whole cascade plan (items and group
+ *                   section), unchanged during the call
+ *   num_items       its item count
+ *   max_group_size  its max_members (0: no group item)
+ * Needs 16-bit storage, head_size 128 and max_group_size x (num_heads /
+ * num_kv_heads) <= 16.  Errors: those of pa_decode_step, plus PA_EINVAL for
+ * partition_size == 0, another dtype or head size, or a group too wide.
+ * ---------------------------------------------------------------------- */
+int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, void* value_cache,
+                               const int32_t* block_tables, int64_t bt_stride,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                               int32_t block_size, int32_t max_context_len, float scale,
+                               int32_t dtype, int32_t partition_size, const int32_t* plan,
+                               int64_t num_items, int32_t max_group_size,
+                               const int32_t* shared_prefix_blocks, void* workspace,
+                               size_t workspace_bytes, const int32_t* query_start_loc,
+                               const void* key, const void* value, int64_t key_stride,
+                               int64_t value_stride, const int64_t* cow_src,
+                               int64_t* slot_mapping, void* stream);
 
 /* ------------------------------------------------------------------------
  * Several new tokens per sequence (speculative drafts, short prefill chunks;

@@ -50,6 +50,8 @@ SIGNATURES = {
     "pa_decode_plan": (_i32, [_pi32, _i32, _i32, _pi32, _i64, _pi64]),
     "pa_decode_plan_window": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _i32, _pi32, _i64,
                                      _pi64]),
+    "pa_decode_plan_cascade": (_i32, [_pi32, _pi32, _i64, _pi32, _i32, _i32, _i32, _i32, _pi32,
+                                      _i64, _pi64, _pi64, _pi32]),
     "pa_paged_attention_decode_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                  _i64, _vp, _vp, _sz, _i32, _vp]),
@@ -57,6 +59,9 @@ SIGNATURES = {
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
                               _i32, _f32, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp,
                               _i64, _i64, _vp, _vp, _i32, _i32, _vp]),
+    "pa_decode_step_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _f32, _i32, _i32, _vp, _i64, _i32, _vp, _vp,
+                                      _sz, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "pa_paged_attention_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                         _i64, _vp, _vp, _sz, _i64, _i32, _vp]),

@@ -577,6 +577,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int mode = decode_kernel_mode();
   const int nq = query_vectors(a);
   const bool can_mfma = decode_mfma_supported(a);
+  // group items (cascade plans) exist only in the matrix-core kernel
+  if (a.max_group > 0) return can_mfma ? launch_decode_mfma(a, stream) : hipErrorInvalidValue;
   const bool can_valu = nq <= 8;
   // automatic: matrix cores as soon as a workgroup serves several query vectors
   const bool mfma = mode == 1 ? (!can_valu && can_mfma)

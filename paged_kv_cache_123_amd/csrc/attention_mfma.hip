@@ -62,7 +62,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
     float scale_log2, float* __restrict__ ws_max, float* __restrict__ ws_sum,
     float* __restrict__ ws_out, const int2* __restrict__ items, AppendArgs ap,
     const int32_t* __restrict__ shared_blocks, int32_t log2_group,
-    const int32_t* __restrict__ q_start, int32_t window) {
+    const int32_t* __restrict__ q_start, int32_t window, int64_t num_items) {
   constexpr int D = 128;
   constexpr int DV = D / 8;   // 16-byte vectors per token row
   constexpr int NK = D / 32;  // score MFMAs per tile
@@ -74,12 +74,27 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
   const WorkUnit wu = work_unit(items, num_kv_heads);
   const int p = wu.p;
   const int kvh = wu.kvh;
-  const int s = wu.s;
+  // A group item (sequence field < 0) serves the members of chunk -1 - s of
+  // the plan's group section, which follows its items: column c holds member
+  // c >> log2_group's decode query, and the partition lies in the prefix the
+  // members share, read through the first member's table.  Split launches
+  // only (each member's partial goes to its own workspace slot).
+  const int32_t* gmem = nullptr;
+  int gn = 0;
+  if (wu.s < 0) {
+    const int32_t* gsec = reinterpret_cast<const int32_t*>(items + num_items);
+    const int c = -1 - wu.s;
+    const int m0 = gsec[1 + c];
+    gn = gsec[2 + c] - m0;
+    gmem = gsec + 2 + gsec[0] + m0;
+  }
+  const int s = gmem ? gmem[0] : wu.s;
   const int L = context_lens[s];
   const int t_begin = FINAL ? 0 : p * partition_size;
   if (t_begin >= L) return;
   const int t_end = FINAL ? L : min(L, t_begin + partition_size);
   const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
+  const int nrows = gmem ? gn : qlen;  // query rows: the members, or the new tokens
   // first key any column of this sequence sees (the first new token's window)
   const int lo_min = window > 0 ? max(0, L - qlen + 1 - window) : 0;
   if (t_end <= lo_min) return;  // wholly before the window: the merge skips it
@@ -92,9 +107,10 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
   const int64_t head_off_v = static_cast<int64_t>(kvh) * B * DV;
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
-  // tokens of the leading blocks other sequences share (cached loads)
-  const int shared_tokens = shared_blocks ? (shared_blocks[s] << log2_block) : 0;
-  if (ap.qsl)
+  // tokens of the leading blocks other sequences share (cached loads); a
+  // group item reads its prefix once (streaming loads)
+  const int shared_tokens = shared_blocks && !gmem ? (shared_blocks[s] << log2_block) : 0;
+  if (ap.qsl && !gmem)
     apply_appends<DV, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
                                   static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * DV,
                                   static_cast<int64_t>(kvh) * (1 << log2_block) * DV);
@@ -102,8 +118,10 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
   const int gmask = (1 << log2_group) - 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
   const int my_qi = col >> log2_group;
-  const bool my_valid = col < NQ && my_qi < qlen;
-  const int bound = my_valid ? L - qlen + my_qi + 1 : 0;  // keys this column sees
+  const bool my_valid = col < NQ && my_qi < nrows;
+  const int64_t my_row = gmem ? gmem[my_valid ? my_qi : 0] : qrow0 + my_qi;
+  // keys this column sees (a member sees the whole shared prefix)
+  const int bound = !my_valid ? 0 : gmem ? t_end : L - qlen + my_qi + 1;
   const int lo = window > 0 ? max(0, bound - window) : 0;   // ... from here on
 
   uint4 qv[NK];
@@ -113,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
     if (my_valid)
       qv[k] = *reinterpret_cast<const uint4*>(
           static_cast<const uint16_t*>(query) +
-          ((qrow0 + my_qi) * num_heads + h0 + (col & gmask)) * D + k * 32 + grp * 8);
+          (my_row * num_heads + h0 + (col & gmask)) * D + k * 32 + grp * 8);
   }
 
   f32x4 o[NE];
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
   for (int i = threadIdx.x; i < NQ * D; i += NW * 64) {
     const int j = i / D, d = i % D;
     const int qi = j >> log2_group;
-    if (qi >= qlen) continue;  // a column past this sequence's new tokens
+    if (qi >= nrows) continue;  // a column past the sequence's new tokens or the members
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
@@ -272,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
       l = fmaf(sm_l[w][j], c, l);
       a = fmaf(sm_acc[w][j][d], c, a);
     }
-    const int64_t row = (qrow0 + qi) * num_heads + h0 + (j & gmask);
+    const int64_t row = (gmem ? gmem[qi] : qrow0 + qi) * num_heads + h0 + (j & gmask);
     if constexpr (FINAL) {
       St<DT>::store(out, row * D + d, a / l);
     } else {
@@ -300,7 +318,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
                      a.partition_size, a.num_partitions, a.scale * kLog2e, a.ws_max, a.ws_sum,
                      a.ws_out, reinterpret_cast<const int2*>(a.items), a.append,
-                     a.shared_blocks, log2_group, a.q_start, a.window);
+                     a.shared_blocks, log2_group, a.q_start, a.window, a.num_items);
   return hipGetLastError();
 }
 

@@ -294,6 +294,85 @@ int32_t pa_paged_attention_decode_planned(
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_planned (reduce)");
 }
 
+static int32_t decode_step_impl(const char* who, int32_t max_group, void* out,
+                                const void* query, void* key_cache, void* value_cache,
+                                const int32_t* block_tables, int64_t bt_stride,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                int32_t block_size, int32_t max_context_len, float scale,
+                                int32_t dtype, int32_t partition_size,
+                                const int32_t* work_items, int64_t num_work_items,
+                                const int32_t* shared_prefix_blocks, void* workspace,
+                                size_t workspace_bytes, const int32_t* query_start_loc,
+                                const void* key, const void* value, int64_t key_stride,
+                                int64_t value_stride, const int64_t* cow_src,
+                                int64_t* slot_mapping, int32_t max_query_len,
+                                int32_t sliding_window, void* stream) {
+  if (sliding_window < 0)
+    return fail(PA_EINVAL, (std::string(who) + ": sliding_window < 0").c_str());
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (!work_items || num_work_items < 1 ||
+      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, (std::string(who) + ": bad work list").c_str());
+  if (!query_start_loc || !key || !value)
+    return fail(PA_EINVAL, (std::string(who) + ": NULL query_start_loc, key or value").c_str());
+  const int32_t eb = elem_bytes(dtype);
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_size;
+  if (key_stride < row || value_stride < row || (key_stride * eb) % 16 != 0 ||
+      (value_stride * eb) % 16 != 0 || !aligned16(key) || !aligned16(value))
+    return fail(PA_EINVAL, (std::string(who) +
+                            ": key/value rows must be 16-byte aligned with a stride of at "
+                            "least num_kv_heads * head_size elements")
+                               .c_str());
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, work_items, num_work_items};
+  a.append = pa::dev::AppendArgs{query_start_loc, cow_src, static_cast<const uint4*>(key),
+                                 static_cast<const uint4*>(value), key_stride * eb / 16,
+                                 value_stride * eb / 16, static_cast<uint4*>(key_cache),
+                                 static_cast<uint4*>(value_cache), slot_mapping};
+  a.shared_blocks = shared_prefix_blocks;
+  a.window = sliding_window;
+  a.max_group = max_group;
+  if (max_query_len > 0) {  // every new token is a query
+    st = check_query_capacity(who, max_query_len, num_heads, num_kv_heads, head_size, dtype);
+    if (st != PA_OK) return st;
+    a.q_start = query_start_loc;
+    a.max_query_len = max_query_len;
+  } else if (max_query_len < 0) {
+    return fail(PA_EINVAL, (std::string(who) + ": max_query_len must be >= 0").c_str());
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, (std::string(who) + ": bad partition_size").c_str());
+  // workspace rows: one per sequence, or num_seqs x max_query_len when every
+  // new token is a query
+  const int64_t out_rows = static_cast<int64_t>(num_seqs) * (max_query_len > 0 ? max_query_len : 1);
+  if (out_rows > 0x7fffffff)
+    return fail(PA_EINVAL, (std::string(who) + ": too many query rows").c_str());
+  const size_t need = pa_split_workspace_bytes(static_cast<int32_t>(out_rows), num_heads,
+                                               head_size, max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL,
+                (std::string(who) + ": workspace missing, too small or misaligned").c_str());
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(out_rows) * num_heads * np;
+  char* ws = static_cast<char*>(workspace);
+  a.partition_size = partition_size;
+  a.num_partitions = np;
+  a.ws_max = reinterpret_cast<float*>(ws);
+  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  st = launched(pa::launch_decode(a, s), (std::string(who) + " (partition)").c_str());
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), (std::string(who) + " (reduce)").c_str());
+}
+
 int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* value_cache,
                        const int32_t* block_tables, int64_t bt_stride,
                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -305,66 +384,44 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
                        int32_t max_query_len, int32_t sliding_window, void* stream) {
-  const char* who = "pa_decode_step";
-  if (sliding_window < 0)
-    return fail(PA_EINVAL, "pa_decode_step: sliding_window < 0");
-  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
-                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
-                            block_size, max_context_len, dtype);
-  if (st != PA_OK) return st;
-  if (!work_items || num_work_items < 1 ||
-      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
-    return fail(PA_EINVAL, "pa_decode_step: bad work list");
-  if (!query_start_loc || !key || !value)
-    return fail(PA_EINVAL, "pa_decode_step: NULL query_start_loc, key or value");
-  const int32_t eb = elem_bytes(dtype);
-  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_size;
-  if (key_stride < row || value_stride < row || (key_stride * eb) % 16 != 0 ||
-      (value_stride * eb) % 16 != 0 || !aligned16(key) || !aligned16(value))
+  return decode_step_impl("pa_decode_step", 0, out, query, key_cache, value_cache, block_tables,
+                          bt_stride, context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                          block_size, max_context_len, scale, dtype, partition_size, work_items,
+                          num_work_items, shared_prefix_blocks, workspace, workspace_bytes,
+                          query_start_loc, key, value, key_stride, value_stride, cow_src,
+                          slot_mapping, max_query_len, sliding_window, stream);
+}
+
+int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, void* value_cache,
+                               const int32_t* block_tables, int64_t bt_stride,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                               int32_t block_size, int32_t max_context_len, float scale,
+                               int32_t dtype, int32_t partition_size, const int32_t* plan,
+                               int64_t num_items, int32_t max_group_size,
+                               const int32_t* shared_prefix_blocks, void* workspace,
+                               size_t workspace_bytes, const int32_t* query_start_loc,
+                               const void* key, const void* value, int64_t key_stride,
+                               int64_t value_stride, const int64_t* cow_src,
+                               int64_t* slot_mapping, void* stream) {
+  const char* who = "pa_decode_step_cascade";
+  if (max_group_size < 0)
+    return fail(PA_EINVAL, "pa_decode_step_cascade: max_group_size < 0");
+  if (partition_size == 0)
+    return fail(PA_EINVAL, "pa_decode_step_cascade: needs partition_size > 0");
+  if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
     return fail(PA_EINVAL,
-                "pa_decode_step: key/value rows must be 16-byte aligned with a stride of at least "
-                "num_kv_heads * head_size elements");
-  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
-                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
-                   nullptr, nullptr, nullptr, work_items, num_work_items};
-  a.append = pa::dev::AppendArgs{query_start_loc, cow_src, static_cast<const uint4*>(key),
-                                 static_cast<const uint4*>(value), key_stride * eb / 16,
-                                 value_stride * eb / 16, static_cast<uint4*>(key_cache),
-                                 static_cast<uint4*>(value_cache), slot_mapping};
-  a.shared_blocks = shared_prefix_blocks;
-  a.window = sliding_window;
-  if (max_query_len > 0) {  // every new token is a query
-    st = check_query_capacity(who, max_query_len, num_heads, num_kv_heads, head_size, dtype);
-    if (st != PA_OK) return st;
-    a.q_start = query_start_loc;
-    a.max_query_len = max_query_len;
-  } else if (max_query_len < 0) {
-    return fail(PA_EINVAL, "pa_decode_step: max_query_len must be >= 0");
-  }
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
-  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
-      partition_size % block_size != 0)
-    return fail(PA_EINVAL, "pa_decode_step: bad partition_size");
-  // workspace rows: one per sequence, or num_seqs x max_query_len when every
-  // new token is a query
-  const int64_t out_rows = static_cast<int64_t>(num_seqs) * (max_query_len > 0 ? max_query_len : 1);
-  if (out_rows > 0x7fffffff) return fail(PA_EINVAL, "pa_decode_step: too many query rows");
-  const size_t need = pa_split_workspace_bytes(static_cast<int32_t>(out_rows), num_heads,
-                                               head_size, max_context_len, partition_size);
-  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(PA_EINVAL, "pa_decode_step: workspace missing, too small or misaligned");
-  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(out_rows) * num_heads * np;
-  char* ws = static_cast<char*>(workspace);
-  a.partition_size = partition_size;
-  a.num_partitions = np;
-  a.ws_max = reinterpret_cast<float*>(ws);
-  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
-  st = launched(pa::launch_decode(a, s), "pa_decode_step (partition)");
-  if (st != PA_OK) return st;
-  return launched(pa::launch_split_reduce(a, s), "pa_decode_step (reduce)");
+                "pa_decode_step_cascade: group items need 16-bit storage and head_size 128");
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
+      static_cast<int64_t>(max_group_size) * (num_heads / num_kv_heads) > 16)
+    return fail(PA_EINVAL,
+                "pa_decode_step_cascade: max_group_size x (num_heads / num_kv_heads) exceeds 16");
+  return decode_step_impl(who, max_group_size, out, query, key_cache, value_cache, block_tables,
+                          bt_stride, context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                          block_size, max_context_len, scale, dtype, partition_size, plan,
+                          num_items, shared_prefix_blocks, workspace, workspace_bytes,
+                          query_start_loc, key, value, key_stride, value_stride, cow_src,
+                          slot_mapping, 0, 0, stream);
 }
 
 int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_cache,

@@ -57,13 +57,15 @@ struct DecodeArgs {
   const int32_t* q_start = nullptr;  // [S+1] new-token rows when every new token is a query
   int32_t max_query_len = 0;  // bound on q_start[s+1] - q_start[s] (host)
   int32_t window = 0;         // sliding window in tokens, 0 for none
+  int32_t max_group = 0;      // members of the widest group item (cascade plan), 0 for none
 };
 
 // Query vectors one workgroup serves: (new tokens per sequence) x (query heads
 // per KV head), rounded up to a power of two.
 inline int query_vectors(const DecodeArgs& a) {
   const int per_seq = a.q_start ? (a.max_query_len > 0 ? a.max_query_len : 1) : 1;
-  const int n = per_seq * (a.num_heads / a.num_kv_heads);
+  const int rows = a.max_group > per_seq ? a.max_group : per_seq;
+  const int n = rows * (a.num_heads / a.num_kv_heads);
   int p = 1;
   while (p < n) p <<= 1;
   return p;

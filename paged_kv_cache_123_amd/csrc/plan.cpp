@@ -74,3 +74,120 @@ extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
   return pa_decode_plan_window(context_lens, nullptr, nullptr, num_seqs, partition_size, 0,
                                items, capacity, num_items);
 }
+
+// Cascade plan: the partitions that lie wholly inside a prefix several
+// sequences share are computed once per group of sharers instead of once per
+// sequence.  Sequences are candidates for one group when their first table
+// entry is the same block; the group's prefix is the run of leading table
+// entries all members agree on, cut to full blocks that end before any
+// member's first new token (no row of it is written during the step).  A
+// group is split into chunks of at most max_group_size members; chunk c and
+// partition p (wholly inside the prefix) make the item (-1 - c, p).  Every
+// other (sequence, partition) pair keeps its own item.  Layout of `plan`:
+//   [2 * num_items]           the items, largest first as in pa_decode_plan
+//   [1]                       number of chunks C
+//   [C + 1]                   offsets of each chunk's members
+//   [offsets[C]]              members (batch rows), in batch order per chunk
+extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
+                                          const int32_t* block_tables, int64_t bt_stride,
+                                          const int32_t* new_tokens, int32_t num_seqs,
+                                          int32_t block_size, int32_t partition_size,
+                                          int32_t max_group_size, int32_t* plan,
+                                          int64_t capacity, int64_t* num_items,
+                                          int64_t* plan_len, int32_t* max_members) {
+  if (!context_lens || !block_tables || !num_items || !plan_len || !max_members ||
+      num_seqs < 1 || block_size < 1 || partition_size < 1 || max_group_size < 1 ||
+      partition_size % block_size != 0 || bt_stride < 1)
+    return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: bad argument");
+  std::vector<int32_t> first_new(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = context_lens[s];
+    const int32_t n = new_tokens ? new_tokens[s] : 1;
+    if (L < 1 || n < 1 || n > L)
+      return pa::fail(PA_EINVAL,
+                      "pa_decode_plan_cascade: need 1 <= new tokens <= context length");
+    if ((static_cast<int64_t>(L) + block_size - 1) / block_size > bt_stride)
+      return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: table row shorter than the length");
+    first_new[s] = L - n;
+  }
+  auto row = [&](int32_t s) { return block_tables + static_cast<int64_t>(s) * bt_stride; };
+  // candidates: sequences with the same first block, in batch order
+  std::vector<int32_t> order(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) order[s] = s;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return row(a)[0] < row(b)[0]; });
+  std::vector<int32_t> prefix_parts(num_seqs, 0);  // partitions a group item covers
+  std::vector<int32_t> chunk_off{0}, members;
+  std::vector<int32_t> chunk_parts;
+  for (size_t i = 0; i < order.size();) {
+    size_t j = i + 1;
+    while (j < order.size() && row(order[j])[0] == row(order[i])[0]) ++j;
+    if (j - i >= 2 && row(order[i])[0] >= 0) {
+      // common leading entries, full blocks before every member's first new token
+      int32_t limit = INT32_MAX;
+      for (size_t k = i; k < j; ++k) limit = std::min(limit, first_new[order[k]] / block_size);
+      int32_t common = 0;
+      while (common < limit) {
+        const int32_t b = row(order[i])[common];
+        bool same = b >= 0;
+        for (size_t k = i + 1; k < j && same; ++k) same = row(order[k])[common] == b;
+        if (!same) break;
+        ++common;
+      }
+      const int32_t parts = static_cast<int32_t>(
+          static_cast<int64_t>(common) * block_size / partition_size);
+      if (parts > 0) {
+        std::vector<int32_t> grp(order.begin() + i, order.begin() + j);
+        std::sort(grp.begin(), grp.end());
+        for (size_t c = 0; c < grp.size(); c += max_group_size) {
+          const size_t e = std::min(grp.size(), c + max_group_size);
+          if (e - c < 2) break;  // a lone member keeps its own items
+          for (size_t k = c; k < e; ++k) {
+            members.push_back(grp[k]);
+            prefix_parts[grp[k]] = parts;
+          }
+          chunk_off.push_back(static_cast<int32_t>(members.size()));
+          chunk_parts.push_back(parts);
+        }
+      }
+    }
+    i = j;
+  }
+  struct Item {
+    int32_t tokens, key, s, p;
+  };
+  std::vector<Item> v;
+  const int32_t num_chunks = static_cast<int32_t>(chunk_parts.size());
+  for (int32_t c = 0; c < num_chunks; ++c)
+    for (int32_t p = 0; p < chunk_parts[c]; ++p)
+      v.push_back({partition_size, members[chunk_off[c]], -1 - c, p});
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = context_lens[s];
+    for (int32_t p = prefix_parts[s]; static_cast<int64_t>(p) * partition_size < L; ++p)
+      v.push_back({std::min((p + 1) * partition_size, L) - p * partition_size, s, s, p});
+  }
+  int32_t widest = 0;
+  for (int32_t c = 0; c < num_chunks; ++c)
+    widest = std::max(widest, chunk_off[c + 1] - chunk_off[c]);
+  *num_items = static_cast<int64_t>(v.size());
+  *plan_len = 2 * static_cast<int64_t>(v.size()) + 1 + (num_chunks + 1) +
+              static_cast<int64_t>(members.size());
+  *max_members = widest;
+  if (!plan) return PA_OK;  // size query
+  if (capacity < *plan_len)
+    return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: capacity smaller than the plan");
+  std::stable_sort(v.begin(), v.end(), [](const Item& a, const Item& b) {
+    const int32_t ba = (a.tokens + kGranule - 1) / kGranule;
+    const int32_t bb = (b.tokens + kGranule - 1) / kGranule;
+    return ba != bb ? ba > bb : a.key < b.key;
+  });
+  int64_t w = 0;
+  for (const Item& it : v) {
+    plan[w++] = it.s;
+    plan[w++] = it.p;
+  }
+  plan[w++] = num_chunks;
+  for (int32_t o : chunk_off) plan[w++] = o;
+  for (int32_t m : members) plan[w++] = m;
+  return PA_OK;
+}

@@ -299,6 +299,35 @@ def decode_plan(context_lens, partition_size: int, sliding_window: int = 0,
     return items
 
 
+def decode_plan_cascade(block_tables, context_lens, block_size: int, partition_size: int,
+                        max_group_size: int, new_tokens=None):
+    """Host cascade plan (pa_decode_plan_cascade): partitions wholly inside a
+    prefix several sequences share become one group item per chunk of at most
+    ``max_group_size`` sharers.  Returns (plan int32 1-D: items then the group
+    section, num_items, max_members)."""
+    tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if tables.ndim != 2 or tables.shape[0] != lens.size:
+        raise ValueError("block_tables must be [num_seqs, width]")
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    newp = None
+    if new_tokens is not None:
+        new = np.ascontiguousarray(np.asarray(new_tokens, dtype=np.int32))
+        if new.size != lens.size:
+            raise ValueError("new_tokens must have one entry per sequence")
+        newp = new.ctypes.data_as(p32)
+    n, plen, widest = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    args = (lens.ctypes.data_as(p32), tables.ctypes.data_as(p32), tables.shape[1], newp,
+            lens.size, block_size, partition_size, max_group_size)
+    check(lib().pa_decode_plan_cascade(*args, None, 0, ctypes.byref(n), ctypes.byref(plen),
+                                       ctypes.byref(widest)))
+    plan = np.empty(plen.value, dtype=np.int32)
+    check(lib().pa_decode_plan_cascade(*args, plan.ctypes.data_as(p32), plan.size,
+                                       ctypes.byref(n), ctypes.byref(plen),
+                                       ctypes.byref(widest)))
+    return plan, n.value, widest.value
+
+
 def map_to_kernel_blocks(manager_ids, blocks_per_kv_block: int) -> np.ndarray:
     """Host int32 kernel block ids of manager block ids (any shape; the last
     axis grows by ``blocks_per_kv_block``); -1 entries stay -1."""
@@ -463,6 +492,54 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
         query_start_loc.data_ptr(),
         key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None,
         slot_ptr or None, max_query_len, sliding_window, _stream()))
+
+
+def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_context_len: int,
+                        partition_size: int, plan: torch.Tensor, num_items: int,
+                        max_group_size: int, query_start_loc: torch.Tensor, key: torch.Tensor,
+                        value: torch.Tensor, cow_src=None, slot_mapping=None, workspace=None,
+                        shared_prefix_blocks=None) -> None:
+    """decode_step over a cascade plan (decode_plan_cascade, uploaded as a
+    device int32 tensor): the prefix partitions of each group of sharers are
+    computed once for all of them."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
+                                   context_lens)
+    _dev(plan, query_start_loc, key, value)
+    if plan.dtype != torch.int32 or plan.dim() != 1 or plan.numel() < 2 * num_items + 2:
+        raise ValueError("plan must be the int32 cascade plan")
+    _contig("plan", plan)
+    if query_start_loc.dtype != torch.int32 or query_start_loc.numel() < S + 1:
+        raise ValueError("query_start_loc must be int32 [num_seqs + 1]")
+    for n, t in (("key", key), ("value", value)):
+        if t.dtype != key_cache.dtype or t.dim() != 3 or tuple(t.shape[1:]) != (hkv, D):
+            raise ValueError(f"{n} must be [num_tokens, num_kv_heads, head_size] in cache dtype")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{n} rows must be contiguous [num_kv_heads, head_size]")
+    cow_ptr = 0
+    if cow_src is not None:
+        _dev(cow_src)
+        if cow_src.dtype != torch.int64 or cow_src.numel() < S:
+            raise ValueError("cow_src must be int64 [num_seqs]")
+        cow_ptr = cow_src.data_ptr()
+    slot_ptr = 0
+    if slot_mapping is not None:
+        _dev(slot_mapping)
+        if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < key.shape[0]:
+            raise ValueError("slot_mapping must be int64 [num_tokens]")
+        slot_ptr = slot_mapping.data_ptr()
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().pa_decode_step_cascade(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), partition_size, plan.data_ptr(),
+        num_items, max_group_size, _shared_ptr(shared_prefix_blocks, S), ws_ptr or None,
+        ws_bytes, query_start_loc.data_ptr(), key.data_ptr(), value.data_ptr(), key.stride(0),
+        value.stride(0), cow_ptr or None, slot_ptr or None, _stream()))
 
 
 def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

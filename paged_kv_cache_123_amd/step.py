@@ -86,12 +86,16 @@ class DecodeStep:
     tokens that the kernels see as block_size / kernel_block_size blocks of
     kernel_block_size tokens ([CSDN] section 3.4): tables and copy-on-write
     pairs are mapped, and the caches hold num_blocks * k kernel blocks.
+    ``cascade``: build a cascade plan (partitions inside a prefix several
+    sequences share run once per group of sharers) with groups of at most
+    ``cascade`` members, for the one-launch step; needs partitions, one query
+    per sequence and no window.
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
                  values: dict, scale: float, partition_size: int = 0, planned: bool = True,
                  all_queries: bool = False, sliding_window: int = 0,
-                 kernel_block_size: int = 0):
+                 kernel_block_size: int = 0, cascade: int = 0):
         self.pool = Pool(num_blocks, block_size, free_order)
         if any(op[0] == "request" for op in history):
             self.pool.enable_prefix_caching()
@@ -153,8 +157,17 @@ class DecodeStep:
         first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
         groups = np.where(self.shared_blocks_host > 0, first,
                           self.pool.num_blocks * k + np.arange(len(seqs)))
-        self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
-                                         query_lens, groups)
+        self.cascade = int(cascade)
+        self.num_items, self.max_group = 0, 0
+        if self.cascade:
+            if not self.partition_size or all_queries or self.sliding_window or k > 1:
+                raise ValueError("a cascade plan needs partitions, one query per sequence, "
+                                 "no window and kernel blocks equal to the allocator's")
+            self.plan_host, self.num_items, self.max_group = ops.decode_plan_cascade(
+                tables, lens, kb, self.partition_size, self.cascade, [n for _, n in appends])
+        else:
+            self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
+                                             query_lens, groups)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self.workspace = None
         if self.partition_size:
@@ -177,6 +190,8 @@ class DecodeStep:
                               self.slot_mapping)
 
     def attention(self):
+        if self.cascade:
+            raise ValueError("a cascade plan runs in the one-launch step (fused=True)")
         if self.all_queries:
             ops.paged_attention_multi(self.out, self.query, self.key_cache, self.value_cache,
                                       self.block_tables, self.context_lens,
@@ -206,6 +221,14 @@ class DecodeStep:
         if not self.fused_ok:
             raise ValueError("a copy-on-write of a block of several kernel blocks needs "
                              "copy_blocks: run the step unfused")
+        if self.cascade:
+            ops.decode_step_cascade(self.out, self.query, self.key_cache, self.value_cache,
+                                    self.block_tables, self.context_lens, self.scale,
+                                    self.max_context_len, self.partition_size, self.plan,
+                                    self.num_items, self.max_group, self.query_start_loc,
+                                    self.new_key, self.new_value, self.cow_src,
+                                    self.slot_mapping, self.workspace, self.shared_blocks)
+            return
         ops.decode_step(self.out, self.query, self.key_cache, self.value_cache,
                         self.block_tables, self.context_lens, self.scale, self.max_context_len,
                         self.partition_size, self.plan, self.query_start_loc, self.new_key,

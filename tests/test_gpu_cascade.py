@@ -1,0 +1,106 @@
+"""GPU parity of the cascade step: partitions inside a prefix several
+sequences share are computed once per group of sharers.
+
+Checked against the oracle (tables, slots and every readable cache slot
+bit-exact; attention within the stated tolerances), and against the ordinary
+split step on the matrix-core kernel with the same partition size, which must
+give identical bits: a group item computes each member's column with the same
+arithmetic as that member's own item would.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle_side import OracleStep, to_host
+from test_gpu_parity import _dead_cow_slots, _require_gpu, check_attention
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _steps(w, part, group):
+    from paged_kv_cache_123_amd import ops
+    from paged_kv_cache_123_amd.step import DecodeStep
+    vals = W.make_values(w, DEV)
+    host = {k: to_host(v) for k, v in vals.items()}
+    plain_vals = {k: v.clone() for k, v in vals.items()}
+    casc = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals, w.scale,
+                      part, cascade=group)
+    prev = ops.set_decode_kernel("mfma")
+    try:
+        plain = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step,
+                           plain_vals, w.scale, part)
+        plain.run(fused=True)
+    finally:
+        ops.set_decode_kernel(prev)
+    casc.slot_mapping.fill_(-7)
+    out = casc.run(fused=True)
+    torch.cuda.synchronize()
+    return casc, plain, out, host
+
+
+def _check(w, part, group, expect_groups=True):
+    casc, plain, out, host = _steps(w, part, group)
+    if expect_groups:
+        assert casc.max_group >= 2, "the batch should form groups"
+    ora = OracleStep(w)
+    assert np.array_equal(casc.tables_host.astype(np.int64), ora.tables)
+    assert to_host(casc.slot_mapping).tolist() == ora.slot_mapping()
+    kc, vc = host["key_cache"], host["value_cache"]
+    ora.apply_copies(kc, vc)
+    ora.apply_scatter(kc, vc, host["new_key"], host["new_value"])
+    gk, gv = to_host(casc.key_cache), to_host(casc.value_cache)
+    for blk, off in _dead_cow_slots(ora, w):
+        gk[blk, :, off, :] = kc[blk, :, off, :]
+        gv[blk, :, off, :] = vc[blk, :, off, :]
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    want = ora.attention(host["query"], kc, vc)
+    check_attention(to_host(out), want, w.dtype, f"cascade P={part} group={group}")
+    assert torch.equal(out.view(torch.int16), plain.out.view(torch.int16)), \
+        "cascade and plain split steps differ"
+
+
+@pytest.mark.parametrize("part,group", [(256, 8), (512, 8), (256, 3), (1024, 16)])
+def test_shared_prefix_batch_full_size(part, group):
+    """16 prompts x 8 samples sharing 1024-token prefixes (the shared-prefix
+    configuration)."""
+    _require_gpu()
+    print(f"[cascade] shared prefix P={part} group={group}", flush=True)
+    _check(W.shared_prefix_bf16(), part, group)
+
+
+FORK_CASES = [
+    # dtype, B, G, partition, group, prompts, samples, appends (per sample, cycled)
+    ("bf16", 16, 1, 64, 8, [300, 77, 129], 5, [1, 3, 17, 2, 40]),
+    ("f16", 16, 2, 32, 8, [200, 33], 4, [1, 1, 9, 16]),
+    ("bf16", 32, 4, 64, 4, [500, 64, 65], 3, [2, 31, 1]),
+    ("bf16", 64, 8, 128, 2, [700], 6, [1, 5, 64, 3, 2, 9]),
+    ("f16", 128, 1, 256, 16, [1000, 257], 8, [1, 2, 3, 4, 5, 6, 7, 130]),
+    ("bf16", 16, 1, 16, 2, [48, 49, 15], 3, [1, 16, 2]),
+]
+
+
+@pytest.mark.parametrize("dtype,B,G,part,group,prompts,samples,appends", FORK_CASES,
+                         ids=[f"{c[0]}-B{c[1]}-G{c[2]}-P{c[3]}-g{c[4]}" for c in FORK_CASES])
+def test_forks(dtype, B, G, part, group, prompts, samples, appends):
+    """Forked samples of several prompts, several new tokens per sample,
+    copy-on-write tails, prefixes that end inside a partition."""
+    _require_gpu()
+    print(f"[cascade] forks {dtype} B={B} G={G} P={part} group={group}", flush=True)
+    rows = [[appends[(g + j) % len(appends)] for j in range(samples)]
+            for g in range(len(prompts))]
+    w = W.custom_forks("cascade", 41, prompts, samples, rows, dtype=dtype, H=2 * G, Hkv=2,
+                       D=128, B=B, partition_size=part)
+    _check(w, part, group)
+
+
+def test_no_sharing_runs_as_the_plain_step():
+    _require_gpu()
+    w = W.custom_decode("cascade_none", 43, [1, 17, 300, 1025, 64], dtype="bf16", H=8, Hkv=2,
+                        D=128, B=16, partition_size=64)
+    _check(w, 64, 4, expect_groups=False)
