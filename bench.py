@@ -501,9 +501,6 @@ def main_cp(args, w):
             "max_context_len": int(st.max_local_len),
             "num_blocks": w.num_blocks,
             "partition_size": part,
-            "cascade_group": cascade,
-            "cascade_group_items": int((step.plan_host[:2 * step.num_items:2] < 0).sum())
-            if cascade else 0,
             "attention_kernel": args.kernel,
         },
         "step_hbm_gbps": step_b / (ms_per_step * 1e-3) / 1e9,
@@ -683,6 +680,9 @@ def main():
             "max_context_len": int(step.max_context_len),
             "num_blocks": w.num_blocks,
             "partition_size": part,
+            "cascade_group": cascade,
+            "cascade_group_items": int((step.plan_host[:2 * step.num_items:2] < 0).sum())
+            if cascade else 0,
             "attention_kernel": args.kernel,
             "fused_step": fused,
             "cow_copies": int(len(step.cow_pairs_host)),

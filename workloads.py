@@ -202,6 +202,18 @@ def shared_prefix_bf16(num_groups=16):
                     extra={"unique_blocks": unique, "prompts": prompts.tolist()})
 
 
+def shared_prefix_cascade_bf16(num_groups=16, partition_size=1024, group=8):
+    """The shared-prefix batch run through a cascade plan: partitions of
+    ``partition_size`` tokens lying wholly inside a prompt's shared blocks are
+    computed once for groups of up to ``group`` samples."""
+    w = shared_prefix_bf16(num_groups)
+    w.name = "shared_prefix_cascade_bf16"
+    w.partition_size = int(partition_size)
+    w.extra["cascade"] = int(group)
+    w.notes += f"; cascade plan: partitions of {partition_size}, groups of up to {group}"
+    return w
+
+
 def long_context_bf16(num_seqs=32, context_len=32768):
     lens = [context_len] * num_seqs
     nb = math.ceil(1.05 * _blocks_for(lens, 64))
@@ -358,6 +370,7 @@ CONFIGS = {
     "qwen72b_gqa_bf16": qwen72b_gqa_bf16,
     "shared_prefix_bf16": shared_prefix_bf16,
     "long_context_bf16": long_context_bf16,
+    "shared_prefix_cascade_bf16": shared_prefix_cascade_bf16,
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
