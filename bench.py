@@ -79,8 +79,9 @@ def step_bytes(w, step) -> int:
     T = step.num_tokens
     row = w.num_kv_heads * w.head_size * e
     blk = w.num_kv_heads * step.block_size * w.head_size * e  # kernel blocks
-    return (attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step))
-            + 20 * T
+    attn = (cascade_bytes(w, step, with_writes=False) if step.cascade else
+            attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step)))
+    return (attn + 20 * T
             + 4 * row * T + 4 * blk * len(step.cow_pairs_host))
 
 
@@ -92,43 +93,65 @@ def _query_lens(step):
     return np.diff(step.query_start_loc_host) if step.all_queries else None
 
 
-def fused_bytes(w, step) -> int:
-    """Algorithmic bytes of the one-launch step: attention, plus the new
-    tokens' K/V rows read and written (4 * row bytes per token), their slots
-    (8 B each), and the copy-on-write of the slots before each fork's first new
-    token (read + write of K and V)."""
-    e = w.elem_bytes
-    row = w.num_kv_heads * w.head_size * e
-    old_slots = 0
+def _cow_old_slots(w, step) -> int:
+    """Slots before each fork's first new token in its fresh copy-on-write
+    tail block: the rows the one-launch step copies."""
+    old = 0
     qsl = step.query_start_loc_host
     for r, src in enumerate(step.cow_src_host):
         if src >= 0:
             first_new = int(step.context_lens_host[r]) - int(qsl[r + 1] - qsl[r])
-            old_slots += first_new % w.block_size
+            old += first_new % w.block_size
+    return old
+
+
+def write_bytes(w, step) -> int:
+    """The step's cache writes at their minimum: each new token's K/V rows
+    written (its read is the attention's read of that token) and its slot (8
+    B), and the copied old slots of each copy-on-write tail written (their
+    read is the attention's read of those tokens)."""
+    row = w.num_kv_heads * w.head_size * w.elem_bytes
+    return (2 * row + 8) * step.num_tokens + 2 * row * _cow_old_slots(w, step)
+
+
+def fused_bytes(w, step) -> int:
+    """Algorithmic bytes of the one-launch step: attention (which reads every
+    context token once, the new ones included) plus the step's writes."""
     return (attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step))
-            + (4 * row + 8) * step.num_tokens + 4 * row * old_slots)
+            + write_bytes(w, step))
 
 
-def cascade_bytes(w, step) -> int:
-    """Algorithmic bytes of the one-launch step over a cascade plan: the K/V
-    rows its items read (a group item's partition once for all its members),
-    q in and out back, the table entries of the blocks read, the lengths, the
-    fp32 (m, l, o) of every (row, head, partition) written and read back by the
-    merge, and the step's cache writes as in fused_bytes."""
+def cascade_bytes(w, step, with_writes: bool = True) -> int:
+    """Algorithmic bytes of a launch over a cascade plan: the K/V rows its
+    items read (a group's shared prefix once for all its members: per shared
+    partition, or in the single-pass item before each member's own tokens), q
+    in and out back, the table entries of the blocks read, the lengths, with
+    partitions the fp32 (m, l, o) of every (row, head, partition) written and
+    read back by the merge, and (``with_writes``, the one-launch step) the
+    step's writes."""
     e = w.elem_bytes
     P, B = step.partition_size, step.block_size
-    items = step.plan_host[:2 * step.num_items].reshape(-1, 2)
+    n = step.num_items
+    items = step.plan_host[:2 * n].reshape(-1, 2)
+    sec = step.plan_host[2 * n:]
+    nc = int(sec[0])
+    offs, members = sec[1:2 + nc], sec[2 + nc:]
     lens = step.context_lens_host
     tokens, entries = 0, 0
     for s, p in items.tolist():
-        n = P if s < 0 else min(P, int(lens[s]) - p * P)
-        tokens += n
-        entries += -(-n // B)
+        if P == 0:  # single pass: (chunk, prefix tokens) or (sequence, 0)
+            spans = ([p] + [int(lens[m]) - p for m in members[offs[-1 - s]:offs[-s]]]
+                     if s < 0 else [int(lens[s])])
+        else:
+            spans = [P if s < 0 else min(P, int(lens[s]) - p * P)]
+        for t in spans:
+            tokens += t
+            entries += -(-t // B)
     kv = tokens * 2 * w.num_kv_heads * w.head_size * e
     qo = 2 * w.num_seqs * w.num_heads * w.head_size * e
-    parts = int(sum(-(-int(L) // P) for L in lens))
+    parts = int(sum(-(-int(L) // P) for L in lens)) if P else 0
     partials = 2 * parts * w.num_heads * (w.head_size + 2) * 4
-    writes = fused_bytes(w, step) - attention_bytes(w, lens)
+    writes = write_bytes(w, step) if with_writes else 0
     return kv + qo + 4 * entries * w.num_kv_heads + 4 * w.num_seqs + partials + writes
 
 
@@ -592,8 +615,6 @@ def main():
         return
     part = w.partition_size if args.partition_size is None else args.partition_size
     cascade = int(w.extra.get("cascade", 0) if args.cascade is None else args.cascade)
-    if cascade and not part:
-        sys.exit("a cascade plan needs --partition-size > 0")
     print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
     vals = W.make_values(w, "cuda")
     step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
@@ -603,8 +624,6 @@ def main():
     torch.cuda.synchronize()
 
     fused = not args.unfused
-    if cascade and not fused:
-        sys.exit("a cascade plan runs in the one-launch step")
     # A one-launch step without partitions is a single kernel: its average
     # launch duration is the timed region over K, and per-launch events would
     # only add their own gaps.  Otherwise events bracket every attention launch.
@@ -650,7 +669,7 @@ def main():
     attn_avg_ms = attn_stats["mean"]
 
     kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
-    attn_bytes = (cascade_bytes(w, step) if cascade
+    attn_bytes = (cascade_bytes(w, step, with_writes=fused) if cascade
                   else fused_bytes(w, step) if fused
                   else attention_bytes(w, step.context_lens_host, _query_rows(step),
                                        _query_lens(step)))
@@ -695,8 +714,10 @@ def main():
         "attention_ms": attn_stats,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
-                args.kernel == "auto" and w.num_heads > w.num_kv_heads)) else "paged_decode_kernel")
+            "kernel": ("cascade_decode_kernel" if cascade and not part else
+                       "paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
+                           args.kernel == "auto" and w.num_heads > w.num_kv_heads))
+                       else "paged_decode_kernel")
                       + (" + merge_kernel" if part else "")
                       + (" (cascade plan)" if cascade else "")
                       + (" (one-launch step: copy-on-write + scatter + attention)" if fused

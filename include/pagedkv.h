@@ -315,20 +315,24 @@ int32_t pa_decode_plan_window(const int32_t* context_lens, const int32_t* query_
  *                  the step, the last new_tokens[s] positions of sequence s
  * Sequences whose first table entry is the same block form a candidate
  * group.  Its prefix is the run of leading entries every member has, cut to
- * full blocks that end before any member's first new token; the partitions
- * (partition_size tokens, a multiple of block_size) wholly inside it become
- * group items, split into chunks of at most max_group_size members.  Output
- * `plan` (host int32, capacity entries), plan_len entries in all:
- *   [2 * num_items]  items (sequence, partition), largest first as in
- *                    pa_decode_plan; a group item is (-1 - c, partition) for
- *                    chunk c
+ * full blocks that end before any member's first new token; the group is
+ * split into chunks of at most max_group_size members.  With partition_size
+ * > 0 (a multiple of block_size) the partitions wholly inside the prefix
+ * become group items (-1 - c, partition) of chunk c, and every other
+ * (sequence, partition) pair keeps its own item.  With partition_size == 0
+ * (single pass) chunk c has the one item (-1 - c, prefix tokens), which
+ * reads the prefix once and then each member's own tokens, and every
+ * sequence outside a chunk has the item (s, 0).  Output `plan` (host int32,
+ * capacity entries), plan_len entries in all:
+ *   [2 * num_items]  items, largest first as in pa_decode_plan (by the
+ *                    tokens they read)
  *   [1]              number of chunks C
  *   [C + 1]          offsets of the chunks' member lists
  *   [offsets[C]]     members (batch rows)
  * max_members receives the widest chunk (0 when no group formed; the plan is
  * then an ordinary item list followed by an empty group section).  plan ==
  * NULL returns only num_items, plan_len and max_members.
- * Errors: PA_EINVAL for null outputs, sizes < 1, a partition_size that is not
+ * Errors: PA_EINVAL for null outputs, sizes < 1, a partition_size < 0 or not
  * a multiple of block_size, new tokens outside [1, length], a table row
  * shorter than its length, or capacity < plan_len.
  * ---------------------------------------------------------------------- */
@@ -395,10 +399,16 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
 
 /* ------------------------------------------------------------------------
  * pa_decode_step over a cascade plan (pa_decode_plan_cascade): one query per
- * sequence, split-K (partition_size > 0, the plan's), no sliding window.  A
- * group item reads each K/V tile of its shared partition once for all its
- * members (their queries are the columns of the matrix-core tiles) and
- * writes every member's partial to that member's workspace slot; the rest is
+ * sequence, no sliding window, partition_size the plan's.  A group item
+ * reads each K/V tile of its shared prefix once for all its members (their
+ * queries are the columns of the matrix-core tiles).  Split plans
+ * (partition_size > 0): it writes every member's partial to that member's
+ * workspace slot, merged as in the split launch.  Single-pass plans
+ * (partition_size == 0, workspace may be NULL): it goes on with each
+ * member's own tokens and writes every member's output; it also writes the
+ * new rows of all its members first, which serializes those writes on a few
+ * workgroups (pa_paged_attention_cascade after pa_copy_blocks and
+ * pa_reshape_and_cache spreads them over the whole GPU).  The rest is
  * pa_decode_step.
  *   plan            device int32, the whole cascade plan (items and group
  *                   section), unchanged during the call
@@ -406,7 +416,7 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
  *   max_group_size  its max_members (0: no group item)
  * Needs 16-bit storage, head_size 128 and max_group_size x (num_heads /
  * num_kv_heads) <= 16.  Errors: those of pa_decode_step, plus PA_EINVAL for
- * partition_size == 0, another dtype or head size, or a group too wide.
+ * another dtype or head size, or a group too wide.
  * ---------------------------------------------------------------------- */
 int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, void* value_cache,
                                const int32_t* block_tables, int64_t bt_stride,
@@ -420,6 +430,26 @@ int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, vo
                                const void* key, const void* value, int64_t key_stride,
                                int64_t value_stride, const int64_t* cow_src,
                                int64_t* slot_mapping, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention alone over a cascade plan (pa_decode_plan_cascade), on caches that
+ * already hold the step's rows: pa_paged_attention_decode_planned's
+ * arguments, with the plan (device int32, whole: items and group section),
+ * its num_items and max_group_size (its max_members) in place of the work
+ * list.  partition_size == 0: single pass, workspace may be NULL;
+ * partition_size > 0: partition kernel plus merge, workspace as for
+ * pa_paged_attention_decode_split.  Same requirements and errors as
+ * pa_decode_step_cascade, without its cache-write arguments.
+ * ---------------------------------------------------------------------- */
+int32_t pa_paged_attention_cascade(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int64_t bt_stride, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size,
+                                   int32_t max_context_len, float scale, int32_t dtype,
+                                   int32_t partition_size, const int32_t* plan,
+                                   int64_t num_items, int32_t max_group_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Several new tokens per sequence (speculative drafts, short prefill chunks;

@@ -62,6 +62,9 @@ SIGNATURES = {
     "pa_decode_step_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _f32, _i32, _i32, _vp, _i64, _i32, _vp, _vp,
                                       _sz, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "pa_paged_attention_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _f32, _i32, _i32, _vp, _i64, _i32,
+                                          _vp, _sz, _vp]),
     "pa_paged_attention_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                         _i64, _vp, _vp, _sz, _i64, _i32, _vp]),

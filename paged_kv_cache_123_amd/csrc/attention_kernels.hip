@@ -100,10 +100,12 @@ __global__ __launch_bounds__(NW * 64) PA_VALU_OCCUPANCY void paged_decode_kernel
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
   // tokens of the leading blocks other sequences share (cached loads)
   const int shared_tokens = shared_blocks ? (shared_blocks[s] << log2_block) : 0;
-  if (ap.qsl)
+  if (ap.qsl) {
     apply_appends<LPT, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
-                                  static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * LPT,
-                                  static_cast<int64_t>(kvh) * (1 << log2_block) * LPT);
+                                static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * LPT,
+                                static_cast<int64_t>(kvh) * (1 << log2_block) * LPT);
+    __syncthreads();  // the rows written above are read by other waves below
+  }
   const int32_t h0 = kvh << log2_group;
   const int gmask = (1 << log2_group) - 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
@@ -577,8 +579,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int mode = decode_kernel_mode();
   const int nq = query_vectors(a);
   const bool can_mfma = decode_mfma_supported(a);
-  // group items (cascade plans) exist only in the matrix-core kernel
-  if (a.max_group > 0) return can_mfma ? launch_decode_mfma(a, stream) : hipErrorInvalidValue;
+  // group items (cascade plans) exist only in the matrix-core kernels: the
+  // partition kernel, or the single-pass cascade kernel
+  if (a.max_group > 0) {
+    if (!can_mfma) return hipErrorInvalidValue;
+    return a.partition_size == 0 ? launch_cascade_single(a, stream)
+                                 : launch_decode_mfma(a, stream);
+  }
   const bool can_valu = nq <= 8;
   // automatic: matrix cores as soon as a workgroup serves several query vectors
   const bool mfma = mode == 1 ? (!can_valu && can_mfma)

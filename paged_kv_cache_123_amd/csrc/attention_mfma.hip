@@ -110,10 +110,12 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
   // tokens of the leading blocks other sequences share (cached loads); a
   // group item reads its prefix once (streaming loads)
   const int shared_tokens = shared_blocks && !gmem ? (shared_blocks[s] << log2_block) : 0;
-  if (ap.qsl && !gmem)
+  if (ap.qsl && !gmem) {
     apply_appends<DV, NW * 64>(ap, s, kvh, L, t_begin, t_end, bt_row, log2_block,
-                                  static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * DV,
-                                  static_cast<int64_t>(kvh) * (1 << log2_block) * DV);
+                                static_cast<int64_t>(num_kv_heads) * (1 << log2_block) * DV,
+                                static_cast<int64_t>(kvh) * (1 << log2_block) * DV);
+    __syncthreads();  // the rows written above are read by other waves below
+  }
   const int h0 = kvh << log2_group;
   const int gmask = (1 << log2_group) - 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
@@ -334,11 +336,416 @@ hipError_t dispatch_g(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+// ---- single-pass cascade ----------------------------------------------------
+// One workgroup per (item, KV head) of a single-pass cascade plan.  A group
+// item (s < 0) serves the members of chunk -1 - s of the plan's group section
+// (column c holds member c >> log2_group's query): it reads the prefix of
+// it.y tokens once through the first member's table with every member's
+// columns live, then each member's own tokens [prefix, L_m) through that
+// member's table with only that member's columns live, and stores every
+// member's output.  An item (s, 0) reads sequence s alone.
+//
+// The step's cache writes of every member ride on the attention's loads:
+// tiles that hold a member's new tokens take those rows from key/value, and
+// the old slots of a copy-on-write tail from the source block; every lane
+// then stores what it loaded to the cache slot the row belongs to (and the
+// new tokens' slots).  No workgroup reads a row written during the launch,
+// so the writes need no barrier and cost no extra loads.
+//
+// Tokens go in rounds of at most kChunkTokens.  A round is a list of pieces
+// (a run of the prefix or of one member's own tokens); thread 0 lists them,
+// then the workgroup stages their table entries in LDS and describes their
+// 16-token tiles (owner, first token, piece end, table base), and the waves
+// take the round's tiles round-robin.  Tile boundaries depend only on logical
+// positions, so the result does not depend on where the blocks lie.
+#ifndef PA_CASCADE_PREFETCH
+#define PA_CASCADE_PREFETCH 1
+#endif
+constexpr int kCascadePrefetch = PA_CASCADE_PREFETCH;  // tiles in flight per wave
+constexpr int kMaxMembers = 16;
+constexpr int kMaxPieces = kMaxMembers + 1;
+constexpr int kRoundTiles = kChunkTokens / kTile + kMaxPieces;
+
+template <int DT, int NQ, int NW>
+__global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kernel(
+    void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
+    const void* value_cache, const int32_t* __restrict__ block_tables, int64_t bt_stride,
+    const int32_t* __restrict__ context_lens, int32_t num_heads, int32_t num_kv_heads,
+    int32_t log2_block, float scale_log2, const int2* __restrict__ items, int64_t num_items,
+    AppendArgs ap, int32_t log2_group) {
+  constexpr int D = 128;
+  constexpr int DV = D / 8;
+  constexpr int NK = D / 32;
+  constexpr int NE = 8;
+  constexpr int U = 4;
+  using MM = Mma<DT>;
+  static_assert(NQ >= 1 && NQ <= 16, "query vectors must fit the 16 MFMA columns");
+
+  const int2 it = items[blockIdx.x / num_kv_heads];
+  const int kvh = static_cast<int>(blockIdx.x % num_kv_heads);
+  __shared__ int32_t sm_mem[kMaxMembers];  // members (batch rows)
+  __shared__ int32_t sm_len[kMaxMembers];  // their context lengths
+  // the step's writes per member: first new position (INT_MAX: none), first
+  // position written (the copied tail's block start, or the first new
+  // position), copy-on-write source block (-1: none), input row of p0
+  __shared__ int32_t sm_p0[kMaxMembers];
+  __shared__ int32_t sm_touch[kMaxMembers];
+  __shared__ int32_t sm_cow[kMaxMembers];
+  __shared__ int32_t sm_q0[kMaxMembers];
+  int nmem = 1;
+  const int32_t* gm = nullptr;
+  if (it.x < 0) {
+    const int32_t* gsec = reinterpret_cast<const int32_t*>(items + num_items);
+    const int c = -1 - it.x;
+    const int m0 = gsec[1 + c];
+    nmem = min(gsec[2 + c] - m0, kMaxMembers);
+    gm = gsec + 2 + gsec[0] + m0;
+  }
+  if (static_cast<int>(threadIdx.x) < nmem) {
+    const int32_t r = gm ? gm[threadIdx.x] : it.x;
+    const int L = context_lens[r];
+    int p0 = INT_MAX, touch = INT_MAX, cow = -1, q0 = 0;
+    if (ap.qsl) {
+      q0 = ap.qsl[r];
+      const int n = ap.qsl[r + 1] - q0;
+      if (n > 0) {
+        p0 = L - n;
+        touch = p0;
+        if (ap.cow_src && ap.cow_src[r] >= 0) {
+          cow = static_cast<int32_t>(ap.cow_src[r]);
+          touch = (p0 >> log2_block) << log2_block;
+        }
+      }
+    }
+    sm_mem[threadIdx.x] = r;
+    sm_len[threadIdx.x] = L;
+    sm_p0[threadIdx.x] = p0;
+    sm_touch[threadIdx.x] = touch;
+    sm_cow[threadIdx.x] = cow;
+    sm_q0[threadIdx.x] = q0;
+  }
+  const int prefix = gm ? it.y : 0;
+  __syncthreads();
+
+  const int B = 1 << log2_block;
+  const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
+  const int64_t head_off_v = static_cast<int64_t>(kvh) * B * DV;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int h0 = kvh << log2_group;
+  const int gmask = (1 << log2_group) - 1;
+  const int my_m = col >> log2_group;  // member of this column
+  const bool my_valid = col < NQ && my_m < nmem;
+  const int64_t my_row = sm_mem[my_valid ? my_m : 0];
+
+  uint4 qv[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    qv[k] = make_uint4(0, 0, 0, 0);
+    if (my_valid)
+      qv[k] = *reinterpret_cast<const uint4*>(
+          static_cast<const uint16_t*>(query) +
+          (my_row * num_heads + h0 + (col & gmask)) * D + k * 32 + grp * 8);
+  }
+
+  f32x4 o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, lsum = 0.0f;
+
+  __shared__ int32_t sm_bt[kChunkTokens + kMaxPieces];
+  __shared__ int4 sm_piece[kMaxPieces];  // {first token, end, owner (-1: all), first entry}
+  __shared__ int32_t sm_ptile[kMaxPieces + 1];  // first tile of each piece
+  __shared__ int4 sm_tile[kRoundTiles];  // {owner, first token, piece end, table base}
+  __shared__ int32_t sm_round[4];        // {pieces, next segment, next token, entries}
+  const uint4* kc = static_cast<const uint4*>(key_cache);
+  const uint4* vc = static_cast<const uint4*>(value_cache);
+  const int k_tok = (col >> 2) + 4 * (col & 3);  // token of this lane's K row
+
+  // segment g: the prefix (g == 0 when there is one), else a member's own tokens
+  const int nseg = (prefix > 0 ? 1 : 0) + nmem;
+  auto segment = [&](int g, int& a, int& b, int& owner) {
+    if (prefix > 0 && g == 0) {
+      a = 0;
+      b = prefix;
+      owner = -1;
+    } else {
+      owner = g - (prefix > 0 ? 1 : 0);
+      a = prefix;
+      b = sm_len[owner];
+    }
+  };
+  auto table_row = [&](int owner) {
+    return block_tables + static_cast<int64_t>(sm_mem[owner < 0 ? 0 : owner]) * bt_stride;
+  };
+  int seg = 0, pos = 0;
+  {
+    int a, b, ow;
+    segment(0, a, b, ow);
+    pos = a;
+  }
+  while (seg < nseg) {
+    if (threadIdx.x == 0) {  // list this round's pieces
+      int np = 0, tok = 0, ent = 0, tiles = 0, g = seg, q = pos;
+      while (g < nseg && tok < kChunkTokens && np < kMaxPieces) {
+        int a, b, ow;
+        segment(g, a, b, ow);
+        const int e = max(q, min(b, q + (kChunkTokens - tok)));
+        sm_piece[np] = make_int4(q, e, ow, ent);
+        sm_ptile[np] = tiles;
+        if (e > q) {
+          ent += ((e - 1) >> log2_block) - (q >> log2_block) + 1;
+          tiles += (e - q + kTile - 1) / kTile;
+          tok += e - q;
+        }
+        ++np;
+        if (e >= b) {
+          if (++g < nseg) segment(g, q, b, ow);
+        } else {
+          q = e;
+        }
+      }
+      sm_ptile[np] = tiles;
+      sm_round[0] = np;
+      sm_round[1] = g;
+      sm_round[2] = q;
+      sm_round[3] = ent;
+    }
+    __syncthreads();
+    const int np = sm_round[0];
+    const int ntiles = sm_ptile[np];
+    const int nent = sm_round[3];
+    // table entries and tile descriptors of the round
+    for (int i = threadIdx.x; i < nent; i += NW * 64) {
+      int k = 0;  // the last non-empty piece whose entries start at or below i
+      for (int j = 1; j < np; ++j)
+        if (sm_piece[j].w <= i && sm_piece[j].y > sm_piece[j].x) k = j;
+      const int4 pc = sm_piece[k];
+      sm_bt[i] = table_row(pc.z)[(pc.x >> log2_block) + (i - pc.w)];
+    }
+    for (int i = threadIdx.x; i < ntiles; i += NW * 64) {
+      int k = 0;  // the last non-empty piece whose tiles start at or below i
+      for (int j = 1; j < np; ++j)
+        if (sm_ptile[j] <= i && sm_ptile[j + 1] > sm_ptile[j]) k = j;
+      const int4 pc = sm_piece[k];
+      sm_tile[i] = make_int4(pc.z, pc.x + (i - sm_ptile[k]) * kTile, pc.y,
+                             pc.w - (pc.x >> log2_block));
+    }
+    __syncthreads();
+
+    auto vec_index = [&](const int4& d, int t, int vec) -> int64_t {
+      const int tc = min(t, d.z - 1);  // tail lanes read a real row of the piece
+      const int32_t phys = sm_bt[d.w + (tc >> log2_block)];
+      const int off = tc & (B - 1);
+      return static_cast<int64_t>(phys) * blk_stride_v + head_off_v + off * DV + vec;
+    };
+    // a tile of member tokens the step writes (new rows or a copied tail)
+    auto writes_rows = [&](const int4& d) { return d.x >= 0 && d.y + kTile > sm_touch[d.x]; };
+    // where token t of such a tile is read: its new row in key/value, the
+    // copy-on-write source block, or the cache
+    auto source = [&](const int4& d, int t, int vec, const uint4* cache, const uint4* rows,
+                      int64_t row_stride) -> const uint4* {
+      const int tc = min(t, d.z - 1);
+      const int p0 = sm_p0[d.x];
+      if (tc >= p0) return rows + (sm_q0[d.x] + (tc - p0)) * row_stride + kvh * DV + vec;
+      if (sm_cow[d.x] >= 0 && (tc >> log2_block) == (p0 >> log2_block))
+        return cache + static_cast<int64_t>(sm_cow[d.x]) * blk_stride_v + head_off_v +
+               (tc & (B - 1)) * DV + vec;
+      return cache + vec_index(d, t, vec);
+    };
+    // the cache slot of token t receives what the lane loaded for it, if the
+    // step writes t (in this piece, at or past the first written position)
+    auto store_row = [&](const int4& d, int t, int vec, const uint4& v, uint4* cache) {
+      if (t < d.z && t >= sm_touch[d.x]) cache[vec_index(d, t, vec)] = v;
+    };
+    auto load_tile = [&](int i, uint4 (&kd)[NK], uint4 (&vd)[U]) {
+      const int4 d = sm_tile[i];
+      if (writes_rows(d)) {
+        const uint4* kp = source(d, d.y + k_tok, grp, kc, ap.key, ap.key_stride_v);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) kd[k] = load_cached(kp + k * 4);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          vd[u] = load_cached(source(d, d.y + grp + 4 * u, col, vc, ap.value, ap.value_stride_v));
+        return;
+      }
+#pragma unroll
+      for (int k = 0; k < NK; ++k) kd[k] = load_stream(kc + vec_index(d, d.y + k_tok, k * 4 + grp));
+#pragma unroll
+      for (int u = 0; u < U; ++u) vd[u] = load_stream(vc + vec_index(d, d.y + grp + 4 * u, col));
+    };
+    auto consume = [&](int i, const uint4 (&kr)[NK], const uint4 (&vr)[U]) {
+      const int4 d = sm_tile[i];
+      if (writes_rows(d)) {
+        const int t = d.y + k_tok;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) store_row(d, t, k * 4 + grp, kr[k], ap.key_cache);
+#pragma unroll
+        for (int u = 0; u < U; ++u) store_row(d, d.y + grp + 4 * u, col, vr[u], ap.value_cache);
+        if (kvh == 0 && grp == 0 && ap.slot_mapping && t < d.z && t >= sm_p0[d.x]) {
+          const int64_t phys = sm_bt[d.w + (t >> log2_block)];
+          ap.slot_mapping[sm_q0[d.x] + (t - sm_p0[d.x])] = phys * B + (t & (B - 1));
+        }
+      }
+      const bool live = my_valid && (d.x < 0 || d.x == my_m);
+      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < NK; ++k) sc = MM::k32(kr[k], qv[k], sc);
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = d.y + grp + 4 * j;
+        x[j] = (live && t < d.z) ? sc[j] * scale_log2 : -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float ms = mn == -INFINITY ? 0.0f : mn;
+      const float corr = __builtin_amdgcn_exp2f(m - ms);
+      float pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - ms);
+      lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      if (__any(mn > m)) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o[e] *= corr;
+      }
+      m = mn;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float back, unused;
+        hi[j] = MM::round16(pr[j], back);
+        lo[j] = MM::round16(pr[j] - back, unused);
+      }
+      const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int w = e >> 1;
+        uint2 a;
+        a.x = __builtin_amdgcn_perm(dword(vr[1], w), dword(vr[0], w), sel);
+        a.y = __builtin_amdgcn_perm(dword(vr[3], w), dword(vr[2], w), sel);
+        o[e] = MM::k16(a, phi, o[e]);
+        o[e] = MM::k16(a, plo, o[e]);
+      }
+    };
+    // this wave's tiles of the round through a ring of kCascadePrefetch + 1 slots
+    constexpr int NBUF = kCascadePrefetch + 1;
+    int first, my;
+    wave_tiles(0, ntiles, wave, NW, first, my);
+    uint4 kb[NBUF][NK], vb[NBUF][U];
+#pragma unroll
+    for (int j = 0; j < kCascadePrefetch; ++j)
+      if (j < my) load_tile(first + j * NW, kb[j], vb[j]);
+    int k = 0;
+    for (; k + NBUF - 1 + kCascadePrefetch < my; k += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        load_tile(first + (k + j + kCascadePrefetch) * NW, kb[(j + kCascadePrefetch) % NBUF],
+                  vb[(j + kCascadePrefetch) % NBUF]);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(first + (k + j) * NW, kb[j], vb[j]);
+      }
+    }
+    for (; k < my; k += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        if (k + j < my) {
+          if (k + j + kCascadePrefetch < my)
+            load_tile(first + (k + j + kCascadePrefetch) * NW, kb[(j + kCascadePrefetch) % NBUF],
+                      vb[(j + kCascadePrefetch) % NBUF]);
+          consume(first + (k + j) * NW, kb[j], vb[j]);
+        }
+      }
+    }
+    seg = sm_round[1];
+    pos = sm_round[2];
+    __syncthreads();  // the round's LDS is rewritten by the next one
+  }
+
+  // per-head sum of the four lane groups (disjoint token slots)
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  __shared__ float sm_m[NW][NQ];
+  __shared__ float sm_l[NW][NQ];
+  __shared__ float sm_acc[NW][NQ][D];
+  if (col < NQ) {
+    if (grp == 0) {
+      sm_m[wave][col] = m;
+      sm_l[wave][col] = lsum;
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_acc[wave][col][32 * grp + 8 * j + e] = o[e][j];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NQ * D; i += NW * 64) {
+    const int j = i / D, dd = i % D;
+    const int qi = j >> log2_group;
+    if (qi >= nmem) continue;  // a column past the members
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
+    const float Ms = M == -INFINITY ? 0.0f : M;
+    float l = 0.0f, a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = __builtin_amdgcn_exp2f(sm_m[w][j] - Ms);
+      l = fmaf(sm_l[w][j], c, l);
+      a = fmaf(sm_acc[w][j][dd], c, a);
+    }
+    const int64_t row = static_cast<int64_t>(sm_mem[qi]) * num_heads + h0 + (j & gmask);
+    St<DT>::store(out, row * D + dd, a / l);
+  }
+}
+
+template <int DT, int NQ>
+hipError_t launch_cascade_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int NW = PA_MFMA_WAVES;
+  int log2_block = 0;
+  while ((1 << log2_block) < a.block_size) ++log2_block;
+  int log2_group = 0;
+  while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
+  hipLaunchKernelGGL((cascade_decode_kernel<DT, NQ, NW>),
+                     dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads)), dim3(NW * 64), 0,
+                     stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
+                     a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
+                     a.scale * kLog2e, reinterpret_cast<const int2*>(a.items), a.num_items,
+                     a.append, log2_group);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_cascade(const DecodeArgs& a, hipStream_t stream) {
+  switch (query_vectors(a)) {
+    case 1: return launch_cascade_t<DT, 1>(a, stream);
+    case 2: return launch_cascade_t<DT, 2>(a, stream);
+    case 4: return launch_cascade_t<DT, 4>(a, stream);
+    case 8: return launch_cascade_t<DT, 8>(a, stream);
+    case 16: return launch_cascade_t<DT, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 bool decode_mfma_supported(const DecodeArgs& a) {
   return (a.dtype == PA_F16 || a.dtype == PA_BF16) && a.head_size == 128 &&
          query_vectors(a) <= 16;
+}
+
+hipError_t launch_cascade_single(const DecodeArgs& a, hipStream_t stream) {
+  if (!a.items || a.num_items < 1 || a.partition_size != 0) return hipErrorInvalidValue;
+  return a.dtype == PA_BF16 ? dispatch_cascade<PA_BF16>(a, stream)
+                            : dispatch_cascade<PA_F16>(a, stream);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {

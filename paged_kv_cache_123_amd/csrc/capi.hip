@@ -407,8 +407,6 @@ int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, vo
   const char* who = "pa_decode_step_cascade";
   if (max_group_size < 0)
     return fail(PA_EINVAL, "pa_decode_step_cascade: max_group_size < 0");
-  if (partition_size == 0)
-    return fail(PA_EINVAL, "pa_decode_step_cascade: needs partition_size > 0");
   if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
     return fail(PA_EINVAL,
                 "pa_decode_step_cascade: group items need 16-bit storage and head_size 128");
@@ -422,6 +420,58 @@ int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, vo
                           num_items, shared_prefix_blocks, workspace, workspace_bytes,
                           query_start_loc, key, value, key_stride, value_stride, cow_src,
                           slot_mapping, 0, 0, stream);
+}
+
+int32_t pa_paged_attention_cascade(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int64_t bt_stride, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size,
+                                   int32_t max_context_len, float scale, int32_t dtype,
+                                   int32_t partition_size, const int32_t* plan,
+                                   int64_t num_items, int32_t max_group_size, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const char* who = "pa_paged_attention_cascade";
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (max_group_size < 0)
+    return fail(PA_EINVAL, "pa_paged_attention_cascade: max_group_size < 0");
+  if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_cascade: group items need 16-bit storage and head_size 128");
+  if (static_cast<int64_t>(max_group_size) * (num_heads / num_kv_heads) > 16)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_cascade: max_group_size x (num_heads / num_kv_heads) exceeds "
+                "16");
+  if (!plan || num_items < 1 || num_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, "pa_paged_attention_cascade: bad plan");
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, plan, num_items};
+  a.max_group = max_group_size;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, "pa_paged_attention_cascade: bad partition_size");
+  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                               partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_cascade: workspace missing, too small or misaligned");
+  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  char* ws = static_cast<char*>(workspace);
+  a.partition_size = partition_size;
+  a.num_partitions = np;
+  a.ws_max = reinterpret_cast<float*>(ws);
+  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  st = launched(pa::launch_decode(a, s), "pa_paged_attention_cascade (partition)");
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_cascade (reduce)");
 }
 
 int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_cache,

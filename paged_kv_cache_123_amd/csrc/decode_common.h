@@ -250,13 +250,12 @@ __device__ void apply_appends(const AppendArgs& ap, int s, int kvh, int L, int t
     const int jb = p0 >> log2_block;
     const int bstart = jb << log2_block;
     if (src >= 0 && bstart >= t_begin && bstart < t_end) {
-      const int64_t dst = bt_row[jb];
+      const int64_t from = src * blk_stride_v + head_off_v;
+      const int64_t to = static_cast<int64_t>(bt_row[jb]) * blk_stride_v + head_off_v;
       const int units = (p0 - bstart) * LPT;  // old slots of the copied block
       for (int u = threadIdx.x; u < units; u += NT) {
-        ap.key_cache[dst * blk_stride_v + head_off_v + u] =
-            ap.key_cache[src * blk_stride_v + head_off_v + u];
-        ap.value_cache[dst * blk_stride_v + head_off_v + u] =
-            ap.value_cache[src * blk_stride_v + head_off_v + u];
+        ap.key_cache[to + u] = ap.key_cache[from + u];
+        ap.value_cache[to + u] = ap.value_cache[from + u];
       }
     }
   }
@@ -272,7 +271,7 @@ __device__ void apply_appends(const AppendArgs& ap, int s, int kvh, int L, int t
     ap.value_cache[dst] = ap.value[i * ap.value_stride_v + kvh * LPT + e];
     if (kvh == 0 && e == 0 && ap.slot_mapping) ap.slot_mapping[i] = phys * B + off;
   }
-  __syncthreads();  // the rows written above are read by other waves below
+  // the caller passes a barrier before any wave reads these rows
 }
 
 // ---- matrix-core helpers (16-bit storage only) ---------------------------

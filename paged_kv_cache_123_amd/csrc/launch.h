@@ -79,6 +79,9 @@ inline int query_vectors(const DecodeArgs& a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// Single-pass cascade plan (items and group section as pa_decode_plan_cascade
+// writes them with partition_size 0): matrix cores, 16-bit storage, D = 128.
+hipError_t launch_cascade_single(const DecodeArgs& a, hipStream_t stream);
 // mode: 0 automatic, 1 vector kernel, 2 matrix-core kernel; returns the previous mode.
 int set_decode_kernel(int mode);
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream);

@@ -9,6 +9,7 @@
 // first block of a shared prefix) order the items of one bucket by group, so
 // the readers of one prefix run together wherever they sit in the batch.
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <vector>
 
@@ -83,7 +84,12 @@ extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
 // member's first new token (no row of it is written during the step).  A
 // group is split into chunks of at most max_group_size members; chunk c and
 // partition p (wholly inside the prefix) make the item (-1 - c, p).  Every
-// other (sequence, partition) pair keeps its own item.  Layout of `plan`:
+// other (sequence, partition) pair keeps its own item.
+// With partition_size == 0 (single pass) a chunk's item is (-1 - c, prefix
+// tokens): one workgroup per KV head reads the prefix once for all members
+// and then every member's own tokens past it; every other sequence s keeps
+// the item (s, 0).  Items are ordered by the tokens they read.  Layout of
+// `plan`:
 //   [2 * num_items]           the items, largest first as in pa_decode_plan
 //   [1]                       number of chunks C
 //   [C + 1]                   offsets of each chunk's members
@@ -96,7 +102,7 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
                                           int64_t capacity, int64_t* num_items,
                                           int64_t* plan_len, int32_t* max_members) {
   if (!context_lens || !block_tables || !num_items || !plan_len || !max_members ||
-      num_seqs < 1 || block_size < 1 || partition_size < 1 || max_group_size < 1 ||
+      num_seqs < 1 || block_size < 1 || partition_size < 0 || max_group_size < 1 ||
       partition_size % block_size != 0 || bt_stride < 1)
     return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: bad argument");
   std::vector<int32_t> first_new(num_seqs);
@@ -116,9 +122,12 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
   for (int32_t s = 0; s < num_seqs; ++s) order[s] = s;
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t a, int32_t b) { return row(a)[0] < row(b)[0]; });
-  std::vector<int32_t> prefix_parts(num_seqs, 0);  // partitions a group item covers
+  const bool single = partition_size == 0;
+  // partitions a group item covers (single pass: 1 once the sequence is in a
+  // chunk, whose item reads all of it)
+  std::vector<int32_t> prefix_parts(num_seqs, 0);
   std::vector<int32_t> chunk_off{0}, members;
-  std::vector<int32_t> chunk_parts;
+  std::vector<int32_t> chunk_parts;  // split: shared partitions; single pass: prefix tokens
   for (size_t i = 0; i < order.size();) {
     size_t j = i + 1;
     while (j < order.size() && row(order[j])[0] == row(order[i])[0]) ++j;
@@ -134,8 +143,10 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
         if (!same) break;
         ++common;
       }
-      const int32_t parts = static_cast<int32_t>(
-          static_cast<int64_t>(common) * block_size / partition_size);
+      const int32_t parts =
+          single ? common * block_size
+                 : static_cast<int32_t>(static_cast<int64_t>(common) * block_size /
+                                        partition_size);
       if (parts > 0) {
         std::vector<int32_t> grp(order.begin() + i, order.begin() + j);
         std::sort(grp.begin(), grp.end());
@@ -144,7 +155,7 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
           if (e - c < 2) break;  // a lone member keeps its own items
           for (size_t k = c; k < e; ++k) {
             members.push_back(grp[k]);
-            prefix_parts[grp[k]] = parts;
+            prefix_parts[grp[k]] = single ? 1 : parts;
           }
           chunk_off.push_back(static_cast<int32_t>(members.size()));
           chunk_parts.push_back(parts);
@@ -158,11 +169,25 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
   };
   std::vector<Item> v;
   const int32_t num_chunks = static_cast<int32_t>(chunk_parts.size());
-  for (int32_t c = 0; c < num_chunks; ++c)
+  for (int32_t c = 0; c < num_chunks; ++c) {
+    if (single) {  // the prefix once, then each member's own tokens
+      const int32_t prefix = chunk_parts[c];
+      int64_t tokens = prefix;
+      for (int32_t k = chunk_off[c]; k < chunk_off[c + 1]; ++k)
+        tokens += context_lens[members[k]] - prefix;
+      v.push_back({static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)),
+                   members[chunk_off[c]], -1 - c, prefix});
+      continue;
+    }
     for (int32_t p = 0; p < chunk_parts[c]; ++p)
       v.push_back({partition_size, members[chunk_off[c]], -1 - c, p});
+  }
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t L = context_lens[s];
+    if (single) {
+      if (!prefix_parts[s]) v.push_back({L, s, s, 0});
+      continue;
+    }
     for (int32_t p = prefix_parts[s]; static_cast<int64_t>(p) * partition_size < L; ++p)
       v.push_back({std::min((p + 1) * partition_size, L) - p * partition_size, s, s, p});
   }

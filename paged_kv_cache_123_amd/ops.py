@@ -303,8 +303,9 @@ def decode_plan_cascade(block_tables, context_lens, block_size: int, partition_s
                         max_group_size: int, new_tokens=None):
     """Host cascade plan (pa_decode_plan_cascade): partitions wholly inside a
     prefix several sequences share become one group item per chunk of at most
-    ``max_group_size`` sharers.  Returns (plan int32 1-D: items then the group
-    section, num_items, max_members)."""
+    ``max_group_size`` sharers; with ``partition_size`` 0, one single-pass item
+    per chunk (prefix once, then each member's own tokens).  Returns (plan
+    int32 1-D: items then the group section, num_items, max_members)."""
     tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     if tables.ndim != 2 or tables.shape[0] != lens.size:
@@ -502,8 +503,9 @@ def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch
                         value: torch.Tensor, cow_src=None, slot_mapping=None, workspace=None,
                         shared_prefix_blocks=None) -> None:
     """decode_step over a cascade plan (decode_plan_cascade, uploaded as a
-    device int32 tensor): the prefix partitions of each group of sharers are
-    computed once for all of them."""
+    device int32 tensor): the prefix of each group of sharers is read once
+    for all of them (per shared partition, or in one single-pass item when
+    ``partition_size`` is 0)."""
     S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
                                    context_lens)
     _dev(plan, query_start_loc, key, value)
@@ -540,6 +542,30 @@ def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch
         num_items, max_group_size, _shared_ptr(shared_prefix_blocks, S), ws_ptr or None,
         ws_bytes, query_start_loc.data_ptr(), key.data_ptr(), value.data_ptr(), key.stride(0),
         value.stride(0), cow_ptr or None, slot_ptr or None, _stream()))
+
+
+def paged_attention_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                            value_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, scale: float, max_context_len: int,
+                            partition_size: int, plan: torch.Tensor, num_items: int,
+                            max_group_size: int, workspace=None) -> None:
+    """Attention alone over a cascade plan (pa_paged_attention_cascade), on
+    caches that already hold the step's rows."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
+                                   context_lens)
+    _dev(plan)
+    if plan.dtype != torch.int32 or plan.dim() != 1 or plan.numel() < 2 * num_items + 2:
+        raise ValueError("plan must be the int32 cascade plan")
+    _contig("plan", plan)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().pa_paged_attention_cascade(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), partition_size, plan.data_ptr(),
+        num_items, max_group_size, ws_ptr or None, ws_bytes, _stream()))
 
 
 def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

@@ -86,10 +86,11 @@ class DecodeStep:
     tokens that the kernels see as block_size / kernel_block_size blocks of
     kernel_block_size tokens ([CSDN] section 3.4): tables and copy-on-write
     pairs are mapped, and the caches hold num_blocks * k kernel blocks.
-    ``cascade``: build a cascade plan (partitions inside a prefix several
-    sequences share run once per group of sharers) with groups of at most
-    ``cascade`` members, for the one-launch step; needs partitions, one query
-    per sequence and no window.
+    ``cascade``: build a cascade plan with groups of at most ``cascade``
+    members, for the one-launch step: with partitions, those inside a prefix
+    several sequences share run once per group of sharers; without, one
+    workgroup per group and KV head reads the prefix once and then every
+    member's own tokens.  Needs one query per sequence and no window.
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
@@ -160,9 +161,9 @@ class DecodeStep:
         self.cascade = int(cascade)
         self.num_items, self.max_group = 0, 0
         if self.cascade:
-            if not self.partition_size or all_queries or self.sliding_window or k > 1:
-                raise ValueError("a cascade plan needs partitions, one query per sequence, "
-                                 "no window and kernel blocks equal to the allocator's")
+            if all_queries or self.sliding_window or k > 1:
+                raise ValueError("a cascade plan needs one query per sequence, no window and "
+                                 "kernel blocks equal to the allocator's")
             self.plan_host, self.num_items, self.max_group = ops.decode_plan_cascade(
                 tables, lens, kb, self.partition_size, self.cascade, [n for _, n in appends])
         else:
@@ -191,8 +192,11 @@ class DecodeStep:
 
     def attention(self):
         if self.cascade:
-            raise ValueError("a cascade plan runs in the one-launch step (fused=True)")
-        if self.all_queries:
+            ops.paged_attention_cascade(self.out, self.query, self.key_cache, self.value_cache,
+                                        self.block_tables, self.context_lens, self.scale,
+                                        self.max_context_len, self.partition_size, self.plan,
+                                        self.num_items, self.max_group, self.workspace)
+        elif self.all_queries:
             ops.paged_attention_multi(self.out, self.query, self.key_cache, self.value_cache,
                                       self.block_tables, self.context_lens,
                                       self.query_start_loc, self.max_query_len, self.scale,

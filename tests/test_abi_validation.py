@@ -61,6 +61,29 @@ CASES = [
                                     0, None], "key/value rows must be 16-byte aligned"),
     ("pa_decode_step", _decode() + [0, P, 3, None, None, 0, P, P, P, 256, 256, None, None, 0, -3,
                                     None], "sliding_window < 0"),
+    ("pa_paged_attention_cascade", _decode() + [0, P, 3, -1, None, 0, None],
+     "max_group_size < 0"),
+    ("pa_paged_attention_cascade", _decode(dtype=F32) + [0, P, 3, 2, None, 0, None],
+     "16-bit storage and head_size 128"),
+    ("pa_paged_attention_cascade", _decode(D=64) + [0, P, 3, 2, None, 0, None],
+     "16-bit storage and head_size 128"),
+    ("pa_paged_attention_cascade", _decode() + [0, P, 3, 9, None, 0, None], "exceeds 16"),
+    ("pa_paged_attention_cascade", _decode() + [0, None, 3, 2, None, 0, None], "bad plan"),
+    ("pa_paged_attention_cascade", _decode() + [0, P, 0, 2, None, 0, None], "bad plan"),
+    ("pa_paged_attention_cascade", _decode() + [24, P, 3, 2, P, 1 << 20, None],
+     "bad partition_size"),
+    ("pa_paged_attention_cascade", _decode() + [32, P, 3, 2, None, 0, None],
+     "workspace missing, too small or misaligned"),
+    ("pa_decode_step_cascade", _decode() + [0, P, 3, -1, None, None, 0, P, P, P, 256, 256, None,
+                                            None, None], "max_group_size < 0"),
+    ("pa_decode_step_cascade", _decode(D=64) + [0, P, 3, 2, None, None, 0, P, P, P, 128, 128,
+                                                None, None, None],
+     "16-bit storage and head_size 128"),
+    ("pa_decode_step_cascade", _decode() + [0, P, 3, 9, None, None, 0, P, P, P, 256, 256, None,
+                                            None, None], "exceeds 16"),
+    ("pa_decode_step_cascade", _decode() + [0, P, 3, 2, None, None, 0, None, P, P, 256, 256,
+                                            None, None, None],
+     "NULL query_start_loc, key or value"),
     ("pa_paged_attention_multi",
      [P, P, P, P, P, 8, P, None, 2, 2, 4, 2, 128, 16, 100, 1.0, F16, 0, P, 3, None, P, 1 << 20,
       4, 0, None], "NULL query_start_loc or num_tokens < 1"),

@@ -1,11 +1,15 @@
-"""GPU parity of the cascade step: partitions inside a prefix several
-sequences share are computed once per group of sharers.
+"""GPU parity of the cascade step: a prefix several sequences share is read
+once per group of sharers, per shared partition (split plans) or in one
+single-pass item per group that then reads every member's own tokens.
 
 Checked against the oracle (tables, slots and every readable cache slot
-bit-exact; attention within the stated tolerances), and against the ordinary
-split step on the matrix-core kernel with the same partition size, which must
-give identical bits: a group item computes each member's column with the same
-arithmetic as that member's own item would.
+bit-exact; attention within the stated tolerances).  A split cascade step is
+also checked against the ordinary split step on the matrix-core kernel with
+the same partition size, which must give identical bits: a group item
+computes each member's column with the same arithmetic as that member's own
+item would.  A single-pass cascade step accumulates the prefix and the
+member's own tokens in another order than a plain single pass, so there the
+oracle alone decides; running it again must give identical bits.
 """
 
 from __future__ import annotations
@@ -23,7 +27,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _steps(w, part, group):
+def _steps(w, part, group, fused=True):
     from paged_kv_cache_123_amd import ops
     from paged_kv_cache_123_amd.step import DecodeStep
     vals = W.make_values(w, DEV)
@@ -39,13 +43,15 @@ def _steps(w, part, group):
     finally:
         ops.set_decode_kernel(prev)
     casc.slot_mapping.fill_(-7)
-    out = casc.run(fused=True)
+    out = casc.run(fused=fused)
     torch.cuda.synchronize()
     return casc, plain, out, host
 
 
-def _check(w, part, group, expect_groups=True):
-    casc, plain, out, host = _steps(w, part, group)
+def _check(w, part, group, expect_groups=True, fused=True):
+    """``fused``: the one-launch step; else copy_blocks, slot mapping, scatter
+    and the cascade attention as separate launches."""
+    casc, plain, out, host = _steps(w, part, group, fused)
     if expect_groups:
         assert casc.max_group >= 2, "the batch should form groups"
     ora = OracleStep(w)
@@ -61,17 +67,26 @@ def _check(w, part, group, expect_groups=True):
     assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
     want = ora.attention(host["query"], kc, vc)
     check_attention(to_host(out), want, w.dtype, f"cascade P={part} group={group}")
-    assert torch.equal(out.view(torch.int16), plain.out.view(torch.int16)), \
-        "cascade and plain split steps differ"
+    if part:
+        assert torch.equal(out.view(torch.int16), plain.out.view(torch.int16)), \
+            "cascade and plain split steps differ"
+    else:
+        first = out.clone()
+        casc.run(fused=not fused)  # writes the same rows again, the other way
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), casc.out.view(torch.int16)), \
+            "single-pass cascade: one launch and separate calls differ"
 
 
-@pytest.mark.parametrize("part,group", [(256, 8), (512, 8), (256, 3), (1024, 16)])
-def test_shared_prefix_batch_full_size(part, group):
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "calls"])
+@pytest.mark.parametrize("part,group", [(256, 8), (512, 8), (256, 3), (1024, 16), (0, 8),
+                                        (0, 3), (0, 16)])
+def test_shared_prefix_batch_full_size(part, group, fused):
     """16 prompts x 8 samples sharing 1024-token prefixes (the shared-prefix
     configuration)."""
     _require_gpu()
-    print(f"[cascade] shared prefix P={part} group={group}", flush=True)
-    _check(W.shared_prefix_bf16(), part, group)
+    print(f"[cascade] shared prefix P={part} group={group} fused={fused}", flush=True)
+    _check(W.shared_prefix_bf16(), part, group, fused=fused)
 
 
 FORK_CASES = [
@@ -85,22 +100,48 @@ FORK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("single", [False, True], ids=["split", "single"])
 @pytest.mark.parametrize("dtype,B,G,part,group,prompts,samples,appends", FORK_CASES,
                          ids=[f"{c[0]}-B{c[1]}-G{c[2]}-P{c[3]}-g{c[4]}" for c in FORK_CASES])
-def test_forks(dtype, B, G, part, group, prompts, samples, appends):
+def test_forks(dtype, B, G, part, group, prompts, samples, appends, single):
     """Forked samples of several prompts, several new tokens per sample,
     copy-on-write tails, prefixes that end inside a partition."""
     _require_gpu()
+    part = 0 if single else part
     print(f"[cascade] forks {dtype} B={B} G={G} P={part} group={group}", flush=True)
     rows = [[appends[(g + j) % len(appends)] for j in range(samples)]
             for g in range(len(prompts))]
     w = W.custom_forks("cascade", 41, prompts, samples, rows, dtype=dtype, H=2 * G, Hkv=2,
                        D=128, B=B, partition_size=part)
-    _check(w, part, group)
+    _check(w, part, group, fused=not single)
 
 
-def test_no_sharing_runs_as_the_plain_step():
+@pytest.mark.parametrize("part", [64, 0])
+def test_no_sharing_runs_as_the_plain_step(part):
     _require_gpu()
     w = W.custom_decode("cascade_none", 43, [1, 17, 300, 1025, 64], dtype="bf16", H=8, Hkv=2,
-                        D=128, B=16, partition_size=64)
-    _check(w, 64, 4, expect_groups=False)
+                        D=128, B=16, partition_size=part)
+    _check(w, part, 4, expect_groups=False)
+
+
+ROUND_CASES = [
+    # B, G, group, prompts, samples, appends: prefixes and own tokens longer
+    # than one round of the single-pass kernel (2048 tokens), pieces cut
+    # inside a member's tokens
+    (16, 1, 16, [4500, 2100], 16, [300, 1, 257, 64, 129, 2, 33, 200]),
+    (4, 2, 8, [2049, 40], 8, [1, 700, 3, 2047]),
+    (128, 4, 4, [6000], 4, [1, 128, 129, 5]),
+    (1, 1, 8, [2100], 5, [3, 1, 2, 40, 9]),
+]
+
+
+@pytest.mark.parametrize("B,G,group,prompts,samples,appends", ROUND_CASES,
+                         ids=[f"B{c[0]}-G{c[1]}-g{c[2]}-{c[3][0]}" for c in ROUND_CASES])
+def test_single_pass_rounds(B, G, group, prompts, samples, appends):
+    _require_gpu()
+    print(f"[cascade] rounds B={B} G={G} group={group} prompts={prompts}", flush=True)
+    rows = [[appends[(g + j) % len(appends)] for j in range(samples)]
+            for g in range(len(prompts))]
+    w = W.custom_forks("cascade_rounds", 47, prompts, samples, rows, dtype="bf16", H=2 * G,
+                       Hkv=2, D=128, B=B, partition_size=0)
+    _check(w, 0, group)

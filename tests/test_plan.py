@@ -120,6 +120,41 @@ def _check_cascade(tables, lens, new, B, P, G):
     return items, chunks
 
 
+def _check_cascade_single(tables, lens, new, B, G):
+    """Single-pass cascade plan: every sequence in exactly one item; a group
+    item's prefix is the longest run of full blocks all members share before
+    their first new token; items ordered by the tokens they read."""
+    from paged_kv_cache_123_amd import ops
+    plan, n, widest = ops.decode_plan_cascade(tables, lens, B, 0, G, new)
+    items, chunks = _parse_cascade(plan, n)
+    assert widest == max([len(c) for c in chunks], default=0)
+    seen, sizes = [], []
+    for s, p in items.tolist():
+        if s < 0:
+            rows = chunks[-1 - s]
+            assert 2 <= len(rows) <= G and p > 0 and p % B == 0
+            nblk = p // B
+            for r in rows:
+                assert p <= lens[r] - new[r]
+                assert list(tables[r][:nblk]) == list(tables[rows[0]][:nblk])
+            # longest over every sequence that starts with the same block (the
+            # group, before it is cut into chunks): the next block differs
+            # somewhere, or is not full before some first new token
+            cand = [r for r in range(len(lens)) if tables[r][0] == tables[rows[0]][0]]
+            limit = min((int(lens[r]) - int(new[r])) // B for r in cand)
+            assert nblk == limit or len({int(tables[r][nblk]) for r in cand}) > 1
+            sizes.append(p + sum(int(lens[r]) - p for r in rows))
+        else:
+            assert p == 0
+            rows = [s]
+            sizes.append(int(lens[s]))
+        seen += rows
+    assert sorted(seen) == list(range(len(lens))), "every sequence in exactly one item"
+    buckets = [-(-x // 256) for x in sizes]
+    assert buckets == sorted(buckets, reverse=True)
+    return items, chunks
+
+
 def test_cascade_plan_groups_samples_of_one_prompt():
     from paged_kv_cache_123_amd.host import Pool
     B, P = 16, 256
@@ -151,6 +186,13 @@ def test_cascade_plan_groups_samples_of_one_prompt():
     by_first = {seqs[c[0]] // 10: sorted(ps) for c, ps in parts.items()}
     assert by_first == {0: [0, 1, 2, 3], 1: [0, 1], 3: [0, 1, 2, 3]}
     assert sorted(len(c) for c in chunks) == [2, 2, 2, 3, 3, 3]
+    # single pass: the 40-token prompt's two full blocks form groups too; the
+    # prefixes are the full prompt blocks (1031 -> 64 blocks, 700 -> 43,
+    # 40 -> 2, 1024 -> 64)
+    items, chunks = _check_cascade_single(tables, lens, new, B, 3)
+    prefix = {seqs[chunks[-1 - s][0]] // 10: p for s, p in items.tolist() if s < 0}
+    assert prefix == {0: 1024, 1: 688, 2: 32, 3: 1024}
+    assert sorted(len(c) for c in chunks) == [2] * 4 + [3] * 4
 
 
 def test_cascade_plan_without_sharing_is_the_plain_plan():
@@ -170,6 +212,9 @@ def test_cascade_plan_without_sharing_is_the_plain_plan():
     assert chunks == []
     plain = ops.decode_plan(lens, P)
     assert sorted(map(tuple, items.tolist())) == sorted(map(tuple, plain.tolist()))
+    items, chunks = _check_cascade_single(tables, lens, new, B, 8)
+    assert chunks == []
+    assert sorted(map(tuple, items.tolist())) == [(s, 0) for s in range(20)]
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -200,7 +245,9 @@ def test_cascade_plan_random_forest(seed):
         pool.append(s, k)
     width = max(pool.seq_num_blocks(s) for s in live)
     tables, lens = pool.block_tables(live, width)
-    _check_cascade(tables, lens, new, B, P, int(rng.integers(2, 9)))
+    G = int(rng.integers(2, 9))
+    _check_cascade(tables, lens, new, B, P, G)
+    _check_cascade_single(tables, lens, new, B, G)
 
 
 def test_cascade_plan_rejects_bad_arguments():
@@ -209,6 +256,8 @@ def test_cascade_plan_rejects_bad_arguments():
     lens = np.array([10, 64], dtype=np.int32)
     with pytest.raises(PagedKVError):
         ops.decode_plan_cascade(tables, lens, 16, 24, 4)  # partition not a multiple of B
+    with pytest.raises(PagedKVError):
+        ops.decode_plan_cascade(tables, lens, 16, -16, 4)  # negative partition
     with pytest.raises(PagedKVError):
         ops.decode_plan_cascade(tables, lens, 16, 32, 4, [11, 1])  # more new tokens than length
     with pytest.raises(PagedKVError):

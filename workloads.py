@@ -202,15 +202,18 @@ def shared_prefix_bf16(num_groups=16):
                     extra={"unique_blocks": unique, "prompts": prompts.tolist()})
 
 
-def shared_prefix_cascade_bf16(num_groups=16, partition_size=1024, group=8):
-    """The shared-prefix batch run through a cascade plan: partitions of
-    ``partition_size`` tokens lying wholly inside a prompt's shared blocks are
-    computed once for groups of up to ``group`` samples."""
+def shared_prefix_cascade_bf16(num_groups=16, partition_size=0, group=8):
+    """The shared-prefix batch run through a cascade plan for groups of up to
+    ``group`` samples: single pass (``partition_size`` 0: one workgroup per
+    group and KV head reads the shared prompt blocks once, then each sample's
+    own tokens), or partitions of ``partition_size`` tokens lying wholly inside
+    the shared blocks computed once per group."""
     w = shared_prefix_bf16(num_groups)
     w.name = "shared_prefix_cascade_bf16"
     w.partition_size = int(partition_size)
     w.extra["cascade"] = int(group)
-    w.notes += f"; cascade plan: partitions of {partition_size}, groups of up to {group}"
+    w.notes += (f"; cascade plan, groups of up to {group}, "
+                + (f"partitions of {partition_size}" if partition_size else "single pass"))
     return w
 
 
