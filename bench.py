@@ -56,15 +56,28 @@ def attended(w, context_lens, query_lens=None):
     return out
 
 
-def attention_bytes(w, context_lens, query_rows=None, query_lens=None) -> int:
+def attended_rows(spans, tables, B) -> int:
+    """Distinct cache rows (slots) the queries attend: a block that several
+    sequences share counts once."""
+    slots = [tables[s, np.arange(lo, L) // B].astype(np.int64) * B + np.arange(lo, L) % B
+             for s, (lo, L) in enumerate(spans) if L > lo]
+    return int(np.unique(np.concatenate(slots)).size) if slots else 0
+
+
+def attention_bytes(w, context_lens, query_rows=None, query_lens=None, tables=None) -> int:
     """Algorithmic bytes of one attention launch: every K and V row a query
-    reads, once per (sequence, KV head), q in, out back (one row per
-    sequence, or ``query_rows`` when every new token is a query), the table
-    entries of the blocks read and the context lengths."""
+    reads, once per KV head (with ``tables``, each distinct cache row once,
+    however many sequences share its block; else once per sequence), q in,
+    out back (one row per sequence, or ``query_rows`` when every new token is
+    a query), the table entries of the blocks read and the context lengths.
+    The plan does not change it: a cascade plan only reads closer to it, and
+    split-K workspace traffic is overhead."""
     e = w.elem_bytes
     B = w.extra.get("kernel_block_size", w.block_size)
     spans = attended(w, context_lens, query_lens)
-    kv = sum(L - lo for lo, L in spans) * 2 * w.num_kv_heads * w.head_size * e
+    rows_read = (attended_rows(spans, tables, B) if tables is not None
+                 else sum(L - lo for lo, L in spans))
+    kv = rows_read * 2 * w.num_kv_heads * w.head_size * e
     rows = w.num_seqs if query_rows is None else query_rows
     qo = 2 * rows * w.num_heads * w.head_size * e
     tables = 4 * sum((L - 1) // B - lo // B + 1 for lo, L in spans if L > lo)
@@ -79,8 +92,8 @@ def step_bytes(w, step) -> int:
     T = step.num_tokens
     row = w.num_kv_heads * w.head_size * e
     blk = w.num_kv_heads * step.block_size * w.head_size * e  # kernel blocks
-    attn = (cascade_bytes(w, step, with_writes=False) if step.cascade else
-            attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step)))
+    attn = attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step),
+                           step.tables_host)
     return (attn + 20 * T
             + 4 * row * T + 4 * blk * len(step.cow_pairs_host))
 
@@ -116,43 +129,10 @@ def write_bytes(w, step) -> int:
 
 def fused_bytes(w, step) -> int:
     """Algorithmic bytes of the one-launch step: attention (which reads every
-    context token once, the new ones included) plus the step's writes."""
-    return (attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step))
+    attended row once, the new ones included) plus the step's writes."""
+    return (attention_bytes(w, step.context_lens_host, _query_rows(step), _query_lens(step),
+                            step.tables_host)
             + write_bytes(w, step))
-
-
-def cascade_bytes(w, step, with_writes: bool = True) -> int:
-    """Algorithmic bytes of a launch over a cascade plan: the K/V rows its
-    items read (a group's shared prefix once for all its members: per shared
-    partition, or in the single-pass item before each member's own tokens), q
-    in and out back, the table entries of the blocks read, the lengths, with
-    partitions the fp32 (m, l, o) of every (row, head, partition) written and
-    read back by the merge, and (``with_writes``, the one-launch step) the
-    step's writes."""
-    e = w.elem_bytes
-    P, B = step.partition_size, step.block_size
-    n = step.num_items
-    items = step.plan_host[:2 * n].reshape(-1, 2)
-    sec = step.plan_host[2 * n:]
-    nc = int(sec[0])
-    offs, members = sec[1:2 + nc], sec[2 + nc:]
-    lens = step.context_lens_host
-    tokens, entries = 0, 0
-    for s, p in items.tolist():
-        if P == 0:  # single pass: (chunk, prefix tokens) or (sequence, 0)
-            spans = ([p] + [int(lens[m]) - p for m in members[offs[-1 - s]:offs[-s]]]
-                     if s < 0 else [int(lens[s])])
-        else:
-            spans = [P if s < 0 else min(P, int(lens[s]) - p * P)]
-        for t in spans:
-            tokens += t
-            entries += -(-t // B)
-    kv = tokens * 2 * w.num_kv_heads * w.head_size * e
-    qo = 2 * w.num_seqs * w.num_heads * w.head_size * e
-    parts = int(sum(-(-int(L) // P) for L in lens)) if P else 0
-    partials = 2 * parts * w.num_heads * (w.head_size + 2) * 4
-    writes = write_bytes(w, step) if with_writes else 0
-    return kv + qo + 4 * entries * w.num_kv_heads + 4 * w.num_seqs + partials + writes
 
 
 def time_prefix_cache(w, min_seconds: float = 0.3) -> dict:
@@ -669,10 +649,9 @@ def main():
     attn_avg_ms = attn_stats["mean"]
 
     kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
-    attn_bytes = (cascade_bytes(w, step, with_writes=fused) if cascade
-                  else fused_bytes(w, step) if fused
+    attn_bytes = (fused_bytes(w, step) if fused
                   else attention_bytes(w, step.context_lens_host, _query_rows(step),
-                                       _query_lens(step)))
+                                       _query_lens(step), step.tables_host))
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     value = kv_tokens / (ms_per_step * 1e-3)
     result = {

@@ -145,3 +145,26 @@ def test_single_pass_rounds(B, G, group, prompts, samples, appends):
     w = W.custom_forks("cascade_rounds", 47, prompts, samples, rows, dtype="bf16", H=2 * G,
                        Hkv=2, D=128, B=B, partition_size=0)
     _check(w, 0, group)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "calls"])
+def test_prefix_cache_batch_single_pass(fused):
+    """128 requests over 16 cached system prompts: the prompt blocks the
+    prefix cache hands to each prompt's requests form the groups."""
+    _require_gpu()
+    print(f"[cascade] prefix-cache batch fused={fused}", flush=True)
+    _check(W.prefix_cache_bf16(), 0, 8, fused=fused)
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_prefix_cache_hits_and_evictions(part):
+    """A tight pool: finished requests' cached blocks are evicted while other
+    requests still hit theirs."""
+    _require_gpu()
+    B = 16
+    systems = [3 * B + 5, 5 * B, 2 * B + 1]
+    requests = [(0, 7), (1, 3), (0, 2 * B), (2, 1), (-1, 4 * B), (1, B), (0, 9), (2, 3 * B),
+                (1, 2), (0, 1)]
+    w = W.custom_prefix("cascade_prefix", 53, systems, requests, dtype="bf16", H=8, Hkv=2,
+                        D=128, B=B, finished={0, 3, 4, 6}, partition_size=part, num_blocks=24)
+    _check(w, part, 4, expect_groups=False)

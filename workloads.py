@@ -315,6 +315,17 @@ def prefix_cache_bf16(num_systems=16, per_system=8):
     return w
 
 
+def prefix_cache_cascade_bf16(num_systems=16, per_system=8, group=8):
+    """The prefix-cache batch run through a single-pass cascade plan: the
+    cached system-prompt blocks that a prompt's requests share are read once
+    per group of up to ``group`` requests, then each request's own tokens."""
+    w = prefix_cache_bf16(num_systems, per_system)
+    w.name = "prefix_cache_cascade_bf16"
+    w.extra["cascade"] = int(group)
+    w.notes += f"; single-pass cascade plan, groups of up to {group}"
+    return w
+
+
 def mistral7b_swa_bf16(num_seqs=64, window=4096):
     """A Mistral-7B-style layer (32 query heads sharing 8 KV heads, head 128)
     with a 4096-token sliding window over contexts up to 16k: attention reads
@@ -380,6 +391,7 @@ CONFIGS = {
     "qwen72b_gqa_tp8_bf16": qwen72b_gqa_tp8_bf16,
     "mistral7b_swa_bf16": mistral7b_swa_bf16,
     "prefix_cache_bf16": prefix_cache_bf16,
+    "prefix_cache_cascade_bf16": prefix_cache_cascade_bf16,
 }
 
 
