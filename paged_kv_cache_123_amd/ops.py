@@ -451,6 +451,31 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     tokens' K/V (rows of ``key``/``value`` per ``query_start_loc``) into their
     slots, and planned attention over the updated caches.  ``max_query_len``
     > 0 makes every new token a query (query/out [num_tokens, H, D])."""
+    launch_prepared(prepare_decode_step(
+        out, query, key_cache, value_cache, block_tables, context_lens, scale,
+        max_context_len, partition_size, work_items, query_start_loc, key, value, cow_src,
+        slot_mapping, workspace, shared_prefix_blocks, max_query_len, sliding_window))
+
+
+def launch_prepared(prepared) -> None:
+    """Launch a call prepared by prepare_decode_step or
+    prepare_decode_step_cascade on the current stream: the tensors it names
+    must still be alive and unchanged in shape."""
+    fn, args = prepared
+    check(fn(*args, _stream()))
+
+
+def prepare_decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_context_len: int,
+                        partition_size: int, work_items: torch.Tensor,
+                        query_start_loc: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                        cow_src=None, slot_mapping=None, workspace=None,
+                        shared_prefix_blocks=None, max_query_len: int = 0,
+                        sliding_window: int = 0):
+    """decode_step's checks and argument marshalling, done once: returns what
+    launch_prepared takes (the C function and its arguments but the stream),
+    for a step launched repeatedly on the same tensors."""
     if max_query_len > 0:
         S = block_tables.shape[0]
         _dev(out, query, key_cache, value_cache, block_tables, context_lens)
@@ -485,14 +510,14 @@ def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     if workspace is not None:
         _dev(workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check(lib().pa_decode_step(
+    return lib().pa_decode_step, (
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, work_items.data_ptr(),
         work_items.shape[0], _shared_ptr(shared_prefix_blocks, S), ws_ptr or None, ws_bytes,
         query_start_loc.data_ptr(),
         key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None,
-        slot_ptr or None, max_query_len, sliding_window, _stream()))
+        slot_ptr or None, max_query_len, sliding_window)
 
 
 def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
@@ -506,6 +531,22 @@ def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch
     device int32 tensor): the prefix of each group of sharers is read once
     for all of them (per shared partition, or in one single-pass item when
     ``partition_size`` is 0)."""
+    launch_prepared(prepare_decode_step_cascade(
+        out, query, key_cache, value_cache, block_tables, context_lens, scale,
+        max_context_len, partition_size, plan, num_items, max_group_size, query_start_loc,
+        key, value, cow_src, slot_mapping, workspace, shared_prefix_blocks))
+
+
+def prepare_decode_step_cascade(out: torch.Tensor, query: torch.Tensor,
+                                key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                scale: float, max_context_len: int, partition_size: int,
+                                plan: torch.Tensor, num_items: int, max_group_size: int,
+                                query_start_loc: torch.Tensor, key: torch.Tensor,
+                                value: torch.Tensor, cow_src=None, slot_mapping=None,
+                                workspace=None, shared_prefix_blocks=None):
+    """decode_step_cascade's checks and argument marshalling, done once (see
+    prepare_decode_step)."""
     S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
                                    context_lens)
     _dev(plan, query_start_loc, key, value)
@@ -535,13 +576,13 @@ def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch
     if workspace is not None:
         _dev(workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check(lib().pa_decode_step_cascade(
+    return lib().pa_decode_step_cascade, (
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, plan.data_ptr(),
         num_items, max_group_size, _shared_ptr(shared_prefix_blocks, S), ws_ptr or None,
         ws_bytes, query_start_loc.data_ptr(), key.data_ptr(), value.data_ptr(), key.stride(0),
-        value.stride(0), cow_ptr or None, slot_ptr or None, _stream()))
+        value.stride(0), cow_ptr or None, slot_ptr or None)
 
 
 def paged_attention_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

@@ -170,6 +170,7 @@ class DecodeStep:
             self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
                                              query_lens, groups)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
+        self._fused_call = None  # the one-launch step's marshalled arguments
         self.workspace = None
         if self.partition_size:
             rows, H, D = self.query.shape
@@ -221,23 +222,28 @@ class DecodeStep:
                                        self.max_context_len)
 
     def fused(self):
-        """The whole step as one launch (pa_decode_step)."""
+        """The whole step as one launch (pa_decode_step).  The arguments are
+        checked and marshalled on the first call; later calls launch them on
+        the current stream."""
         if not self.fused_ok:
             raise ValueError("a copy-on-write of a block of several kernel blocks needs "
                              "copy_blocks: run the step unfused")
-        if self.cascade:
-            ops.decode_step_cascade(self.out, self.query, self.key_cache, self.value_cache,
-                                    self.block_tables, self.context_lens, self.scale,
-                                    self.max_context_len, self.partition_size, self.plan,
-                                    self.num_items, self.max_group, self.query_start_loc,
-                                    self.new_key, self.new_value, self.cow_src,
-                                    self.slot_mapping, self.workspace, self.shared_blocks)
-            return
-        ops.decode_step(self.out, self.query, self.key_cache, self.value_cache,
-                        self.block_tables, self.context_lens, self.scale, self.max_context_len,
-                        self.partition_size, self.plan, self.query_start_loc, self.new_key,
-                        self.new_value, self.cow_src, self.slot_mapping, self.workspace,
-                        self.shared_blocks, self.max_query_len, self.sliding_window)
+        if self._fused_call is None:
+            if self.cascade:
+                self._fused_call = ops.prepare_decode_step_cascade(
+                    self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
+                    self.context_lens, self.scale, self.max_context_len, self.partition_size,
+                    self.plan, self.num_items, self.max_group, self.query_start_loc,
+                    self.new_key, self.new_value, self.cow_src, self.slot_mapping,
+                    self.workspace, self.shared_blocks)
+            else:
+                self._fused_call = ops.prepare_decode_step(
+                    self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
+                    self.context_lens, self.scale, self.max_context_len, self.partition_size,
+                    self.plan, self.query_start_loc, self.new_key, self.new_value,
+                    self.cow_src, self.slot_mapping, self.workspace, self.shared_blocks,
+                    self.max_query_len, self.sliding_window)
+        ops.launch_prepared(self._fused_call)
 
     def run(self, fused: bool = False):
         """The whole step; returns ``out`` [num_seqs, num_heads, head_size].
