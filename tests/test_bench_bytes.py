@@ -69,3 +69,16 @@ def test_attention_bytes_formula():
     qo = 2 * 2 * 4 * 8 * 2
     entries = 4 * (2 + 1)
     assert got == kv + qo + entries + 4 * 2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """Only one GPU's share is measured: --gpus N > 1 exits with a message,
+    before anything touches a GPU."""
+    import subprocess
+    import sys
+
+    from conftest import REPO
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=REPO,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
