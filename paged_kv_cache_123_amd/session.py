@@ -12,7 +12,10 @@ sliding window each step first releases the blocks the window has left
 
 Host bookkeeping runs in the C++ allocator; every device computation is one
 `pa_decode_step` launch (copy-on-write of the old slots, scatter of the new
-rows, planned attention; plus the merge launch with partitions).
+rows, planned attention; plus the merge launch with partitions).  With
+``cascade`` > 0 a step runs over a cascade plan instead
+(`pa_decode_step_cascade`): sequences that share leading blocks, such as the
+forks of one prompt, read them once per group of at most ``cascade``.
 """
 
 from __future__ import annotations
@@ -32,13 +35,16 @@ class PagedKVCache:
 
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
                  dtype: str = "f16", device="cuda", free_order=None, sliding_window: int = 0,
-                 partition_size: int = 0):
+                 partition_size: int = 0, cascade: int = 0):
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.num_kv_heads, self.head_size = int(num_kv_heads), int(head_size)
         self.dtype = _TORCH[dtype]
         self.device = torch.device(device)
         self.sliding_window = int(sliding_window)
         self.partition_size = int(partition_size)
+        self.cascade = int(cascade)
+        if self.cascade and (self.sliding_window or dtype == "f32" or self.head_size != 128):
+            raise ValueError("cascade plans need 16-bit storage, head_size 128 and no window")
         self.pool = Pool(self.num_blocks, self.block_size, free_order)
         shape = (self.num_blocks, self.num_kv_heads, self.block_size, self.head_size)
         self.key_cache = torch.zeros(shape, dtype=self.dtype, device=self.device)
@@ -95,7 +101,12 @@ class PagedKVCache:
         # readers of one shared prefix (same first live block) run together
         first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
         groups = np.where(shared > 0, first, self.num_blocks + np.arange(len(seqs)))
-        plan = ops.decode_plan(lens, self.partition_size, self.sliding_window, None, groups)
+        widest = 0  # members of the widest cascade group of the step
+        if self.cascade:
+            plan, num_items, widest = ops.decode_plan_cascade(
+                tables, lens, self.block_size, self.partition_size, self.cascade, n)
+        else:
+            plan = ops.decode_plan(lens, self.partition_size, self.sliding_window, None, groups)
         t = {name: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for name, a in (
             ("tables", tables), ("lens", lens), ("qsl", np.asarray(qsl, dtype=np.int32)),
             ("cow_src", np.asarray(cow_src, dtype=np.int64)), ("plan", plan))}
@@ -105,9 +116,15 @@ class PagedKVCache:
             workspace = ops.alloc_split_workspace(len(seqs), query.shape[1], self.head_size,
                                                   int(lens.max()), self.partition_size, dev)
         shared_dev = torch.from_numpy(shared).to(dev) if shared.any() else None
-        ops.decode_step(out, query, self.key_cache, self.value_cache, t["tables"], t["lens"],
-                        scale, int(lens.max()), self.partition_size, t["plan"], t["qsl"], key,
-                        value, t["cow_src"], None, workspace, shared_dev, 0,
-                        self.sliding_window)
-        self.last_tables, self.last_lens = tables, lens
+        if self.cascade:
+            ops.decode_step_cascade(out, query, self.key_cache, self.value_cache, t["tables"],
+                                    t["lens"], scale, int(lens.max()), self.partition_size,
+                                    t["plan"], num_items, widest, t["qsl"], key, value,
+                                    t["cow_src"], None, workspace, shared_dev)
+        else:
+            ops.decode_step(out, query, self.key_cache, self.value_cache, t["tables"],
+                            t["lens"], scale, int(lens.max()), self.partition_size, t["plan"],
+                            t["qsl"], key, value, t["cow_src"], None, workspace, shared_dev, 0,
+                            self.sliding_window)
+        self.last_tables, self.last_lens, self.last_group = tables, lens, widest
         return out

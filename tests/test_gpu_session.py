@@ -1,6 +1,7 @@
 """Many steps of one cache: prompts, decode tokens, a few tokens at once,
-forks and frees, with and without a sliding window and partitions, each step
-against the oracle replaying the same history on host copies of the caches."""
+forks and frees, with and without a sliding window, partitions or cascade
+plans, each step against the oracle replaying the same history on host copies
+of the caches."""
 
 from __future__ import annotations
 
@@ -24,11 +25,12 @@ def _draw(gen, shape, dtype):
     return torch.randn(shape, generator=gen, dtype=torch.float32).to(TORCH[dtype])
 
 
-@pytest.mark.parametrize("dtype,B,G,window,part", [
-    ("f16", 16, 1, 0, 0), ("bf16", 4, 4, 0, 32), ("f32", 8, 2, 0, 0),
-    ("bf16", 16, 8, 24, 0), ("f16", 8, 1, 9, 16),
+@pytest.mark.parametrize("dtype,B,G,window,part,cascade", [
+    ("f16", 16, 1, 0, 0, 0), ("bf16", 4, 4, 0, 32, 0), ("f32", 8, 2, 0, 0, 0),
+    ("bf16", 16, 8, 24, 0, 0), ("f16", 8, 1, 9, 16, 0),
+    ("bf16", 8, 1, 0, 0, 8), ("f16", 4, 2, 0, 16, 4), ("bf16", 16, 8, 0, 0, 2),
 ])
-def test_many_steps_against_the_oracle(dtype, B, G, window, part):
+def test_many_steps_against_the_oracle(dtype, B, G, window, part, cascade):
     _require_gpu()
     from paged_kv_cache_123_amd.session import PagedKVCache
     hkv, D, nb = 2, 128, 96
@@ -36,13 +38,14 @@ def test_many_steps_against_the_oracle(dtype, B, G, window, part):
     rng = np.random.default_rng(B * 10 + G + window)
     order = rng.permutation(nb)
     cache = PagedKVCache(nb, B, hkv, D, dtype, DEV, free_order=order, sliding_window=window,
-                         partition_size=part)
+                         partition_size=part, cascade=cascade)
     pool = OraclePool(nb, B, order)
     kc = to_host(cache.key_cache).copy()
     vc = to_host(cache.value_cache).copy()
     gen = torch.Generator().manual_seed(7)
     live = []
     scale = 1.0 / np.sqrt(D)
+    widest = []  # widest cascade group of every step
 
     def run_step(seqs, counts, label):
         T = sum(counts)
@@ -51,6 +54,7 @@ def test_many_steps_against_the_oracle(dtype, B, G, window, part):
         v = _draw(gen, (T, hkv, D), dtype)
         out = cache.step(seqs, q.to(DEV), k.to(DEV), v.to(DEV), counts, scale)
         torch.cuda.synchronize()
+        widest.append(cache.last_group)
         # the oracle: window release, allocation, copies, scatter, attention
         slots, pairs = [], []
         for s, n in zip(seqs, counts):
@@ -103,3 +107,5 @@ def test_many_steps_against_the_oracle(dtype, B, G, window, part):
         run_step(list(live), counts, f"step {it}")
     pool.check_invariants()
     assert cache.pool.num_free() == pool.num_free()
+    if cascade:
+        assert max(widest) >= 2, "forks sharing full blocks should form cascade groups"
