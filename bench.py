@@ -26,6 +26,9 @@ sys.path.insert(0, REPO)
 
 METRIC = "paged decode attention: KV tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+# dense matrix-core peaks of MI355X (TFLOP/s) by storage dtype; fp32 is the
+# vector peak (the fp32 path runs on the vector ALUs)
+MATRIX_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "llama7b_fp16"
 CSRC = os.path.join(REPO, "paged_kv_cache_123_amd", "csrc")
 ATTN_SRCS = [os.path.join(CSRC, f) for f in ("attention_kernels.hip", "attention_mfma.hip",
@@ -82,6 +85,21 @@ def attention_bytes(w, context_lens, query_rows=None, query_lens=None, tables=No
     qo = 2 * rows * w.num_heads * w.head_size * e
     tables = 4 * sum((L - 1) // B - lo // B + 1 for lo, L in spans if L > lo)
     return kv + qo + tables + 4 * w.num_seqs
+
+
+def attention_flops(w, context_lens, query_lens=None) -> int:
+    """Algorithmic flops of one attention launch: for every (query token,
+    visible key) pair and query head, 2*D for q.k and 2*D for the weighted
+    sum of v (exps and the softmax sums are not counted)."""
+    W = window_of(w)
+    pairs = 0
+    for s, L in enumerate(context_lens):
+        n = 1 if query_lens is None else int(query_lens[s])
+        for i in range(n):
+            hi = int(L) - n + i + 1
+            lo = max(0, hi - W) if W else 0
+            pairs += hi - lo
+    return pairs * w.num_heads * 4 * w.head_size
 
 
 def step_bytes(w, step) -> int:
@@ -603,7 +621,10 @@ def main():
                       kernel_block_size=w.extra.get("kernel_block_size", 0), cascade=cascade)
     torch.cuda.synchronize()
 
-    fused = not args.unfused
+    # steps whose cache writes must precede the attention (query blocks of a
+    # prefill chunk; copy-on-write of blocks of several kernel blocks) run as
+    # separate calls
+    fused = not args.unfused and step.fused_ok
     # A one-launch step without partitions is a single kernel: its average
     # launch duration is the timed region over K, and per-launch events would
     # only add their own gaps.  Otherwise events bracket every attention launch.
@@ -654,6 +675,11 @@ def main():
                                        _query_lens(step), step.tables_host))
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     value = kv_tokens / (ms_per_step * 1e-3)
+    # the bound: HBM, or the matrix cores when the flops per algorithmic byte
+    # exceed the ridge (several queries per token row: prefill chunks)
+    flops = attention_flops(w, step.context_lens_host, _query_lens(step))
+    mpeak = MATRIX_PEAK_TFLOPS[w.dtype]
+    compute_bound = flops / attn_bytes > mpeak * 1e12 / (HBM_PEAK_GBPS * 1e9)
     result = {
         "metric": METRIC,
         "value": value,
@@ -692,7 +718,7 @@ def main():
         "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
         "attention_ms": attn_stats,
         "roofline": {
-            "bound": "hbm",
+            "bound": "mfma" if compute_bound else "hbm",
             "kernel": ("cascade_decode_kernel" if cascade and not part else
                        "paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
                            args.kernel == "auto" and w.num_heads > w.num_kv_heads))
@@ -707,9 +733,15 @@ def main():
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": pmc_traffic(w.name, attn_bytes),
             "algorithmic_bytes_per_launch": attn_bytes,
+            "algorithmic_flops_per_launch": flops,
         },
         "wall_s_timed_region": wall,
     }
+    if compute_bound:
+        tflops = flops / (attn_avg_ms * 1e-3) / 1e12
+        result["roofline"].update({
+            "achieved": tflops, "peak": mpeak, "unit": "TFLOP/s", "frac": tflops / mpeak,
+            "hbm_gbps": achieved, "hbm_frac": achieved / HBM_PEAK_GBPS})
     if any(op[0] == "request" for op in w.prefill):
         result["host_prefix_cache"] = time_prefix_cache(w)
     if not args.no_read_reference:

@@ -432,6 +432,32 @@ int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, vo
                                int64_t* slot_mapping, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Query blocks (host) for steps whose sequences bring more new tokens than
+ * one workgroup holds as query vectors (max_query_len x (num_heads /
+ * num_kv_heads) above 16, or 8 for the vector kernel): a prefill chunk
+ * ([DEEPSONAR] section 2.5 schedules prefill chunks like decode tokens;
+ * [CSDN] section 2.3 lays a step's tokens out by query_start_loc).  Sequence
+ * s's n_s new tokens are cut into blocks of at most max_block tokens; block j
+ * is a row of its own for pa_paged_attention_multi, over sequence s's table
+ * row, with the new tokens rows [query_start_loc[s] + j*max_block, ...) and
+ * the context length L_s - n_s + (end of the block), so every token keeps its
+ * causal bound.  Output rows keep the step's token order.  Blocks of one
+ * sequence read each other's new rows, so the cache writes of such a step go
+ * first (pa_reshape_and_cache), not inside the attention launch.
+ *   context_lens, query_start_loc  host int32 [num_seqs], [num_seqs + 1]
+ *   row_seq, row_lens              host int32 [capacity] (outputs): source
+ *                                  sequence and context length of each row
+ *   row_qsl                        host int32 [capacity + 1] (output)
+ * row_seq == NULL returns only num_rows.  Errors: PA_EINVAL for null
+ * arguments, num_seqs or max_block < 1, new tokens outside [1, length],
+ * capacity < num_rows.
+ * ---------------------------------------------------------------------- */
+int32_t pa_query_blocks(const int32_t* context_lens, const int32_t* query_start_loc,
+                        int32_t num_seqs, int32_t max_block, int32_t* row_seq,
+                        int32_t* row_lens, int32_t* row_qsl, int64_t capacity,
+                        int64_t* num_rows);
+
+/* ------------------------------------------------------------------------
  * Attention alone over a cascade plan (pa_decode_plan_cascade), on caches that
  * already hold the step's rows: pa_paged_attention_decode_planned's
  * arguments, with the plan (device int32, whole: items and group section),

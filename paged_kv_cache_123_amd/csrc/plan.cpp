@@ -216,3 +216,44 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
   for (int32_t m : members) plan[w++] = m;
   return PA_OK;
 }
+
+// Query blocks: sequence s's n_s new tokens (rows [qsl[s], qsl[s+1]) of the
+// step's queries, positions [L_s - n_s, L_s)) are cut into blocks of at most
+// max_block tokens.  Block j becomes a row of its own for the multi-query
+// attention: its tokens are rows [qsl[s] + j*max_block, ...) and it sees the
+// sequence's positions up to its last token, so its context length is
+// L_s - n_s + (end of the block) and its causal bounds are those of the
+// tokens in the whole sequence.
+extern "C" int32_t pa_query_blocks(const int32_t* context_lens, const int32_t* query_start_loc,
+                                   int32_t num_seqs, int32_t max_block, int32_t* row_seq,
+                                   int32_t* row_lens, int32_t* row_qsl, int64_t capacity,
+                                   int64_t* num_rows) {
+  if (!context_lens || !query_start_loc || !num_rows || num_seqs < 1 || max_block < 1)
+    return pa::fail(PA_EINVAL, "pa_query_blocks: bad argument");
+  int64_t rows = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t n = query_start_loc[s + 1] - query_start_loc[s];
+    if (n < 1 || n > context_lens[s])
+      return pa::fail(PA_EINVAL, "pa_query_blocks: need 1 <= new tokens <= context length");
+    rows += (n + max_block - 1) / max_block;
+  }
+  *num_rows = rows;
+  if (!row_seq) return PA_OK;  // size query
+  if (!row_lens || !row_qsl || capacity < rows)
+    return pa::fail(PA_EINVAL, "pa_query_blocks: outputs missing or capacity too small");
+  int64_t r = 0;
+  row_qsl[0] = query_start_loc[0];
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t q0 = query_start_loc[s];
+    const int32_t n = query_start_loc[s + 1] - q0;
+    const int32_t first = context_lens[s] - n;  // position of the first new token
+    for (int32_t j = 0; j < n; j += max_block) {
+      const int32_t e = std::min(n, j + max_block);
+      row_seq[r] = s;
+      row_lens[r] = first + e;
+      row_qsl[r + 1] = q0 + e;
+      ++r;
+    }
+  }
+  return PA_OK;
+}

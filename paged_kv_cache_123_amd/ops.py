@@ -329,6 +329,29 @@ def decode_plan_cascade(block_tables, context_lens, block_size: int, partition_s
     return plan, n.value, widest.value
 
 
+def query_blocks(context_lens, query_start_loc, max_block: int):
+    """Host query blocks (pa_query_blocks): each sequence's new tokens cut into
+    rows of at most ``max_block`` tokens.  Returns (row_seq, row_lens, row_qsl)
+    as int32 arrays."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    qsl = np.ascontiguousarray(np.asarray(query_start_loc, dtype=np.int32))
+    if qsl.size != lens.size + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    rows = ctypes.c_int64(0)
+    check(lib().pa_query_blocks(lens.ctypes.data_as(p32), qsl.ctypes.data_as(p32), lens.size,
+                                max_block, None, None, None, 0, ctypes.byref(rows)))
+    n = rows.value
+    row_seq = np.empty(n, np.int32)
+    row_lens = np.empty(n, np.int32)
+    row_qsl = np.empty(n + 1, np.int32)
+    check(lib().pa_query_blocks(lens.ctypes.data_as(p32), qsl.ctypes.data_as(p32), lens.size,
+                                max_block, row_seq.ctypes.data_as(p32),
+                                row_lens.ctypes.data_as(p32), row_qsl.ctypes.data_as(p32), n,
+                                ctypes.byref(rows)))
+    return row_seq, row_lens, row_qsl
+
+
 def map_to_kernel_blocks(manager_ids, blocks_per_kv_block: int) -> np.ndarray:
     """Host int32 kernel block ids of manager block ids (any shape; the last
     axis grows by ``blocks_per_kv_block``); -1 entries stay -1."""

@@ -79,7 +79,10 @@ class DecodeStep:
     batch order; ``values``: dict with key_cache, value_cache, query, new_key,
     new_value device tensors (caches [NB, H_kv, B, D]).  ``all_queries``:
     every new token is a query (query/out [num_tokens, H, D], causal over each
-    sequence's new tokens) instead of one query per sequence.
+    sequence's new tokens) instead of one query per sequence; a sequence with
+    more new tokens than one workgroup holds as query vectors (a prefill
+    chunk) is attended as several query blocks (pa_query_blocks), after the
+    step's cache writes (the step then runs as separate launches).
     ``sliding_window``: attention sees the last W tokens only, and blocks
     outside every query's window are released before the step's appends.
     ``kernel_block_size``: the allocator hands out blocks of ``block_size``
@@ -169,6 +172,36 @@ class DecodeStep:
         else:
             self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
                                              query_lens, groups)
+        # the rows the multi-query attention runs over: the sequences, or their
+        # query blocks when a sequence brings more tokens than a workgroup holds
+        self.attn_tables, self.attn_lens = self.block_tables, self.context_lens
+        self.attn_qsl, self.attn_max_query_len = self.query_start_loc, self.max_query_len
+        self.attn_shared = self.shared_blocks
+        self.query_blocks = False
+        if all_queries:
+            H, D = self.query.shape[1], self.query.shape[2]
+            G = H // values["key_cache"].shape[1]
+            matrix = self.query.dtype != torch.float32 and D == 128
+            block = (16 if matrix else 8) // G
+            if block < 1:
+                raise ValueError("one new token's query heads exceed a workgroup's query vectors")
+            if self.max_query_len > block:
+                self.query_blocks = True
+                self.fused_ok = False  # blocks of one sequence read each other's new rows
+                row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl, block)
+                row_tables = np.ascontiguousarray(tables[row_seq])
+                rows_per_seq = np.bincount(row_seq, minlength=len(seqs))
+                # every block of a sequence cut into several rows is read by all
+                # of them: cached loads
+                row_shared = np.where(rows_per_seq[row_seq] > 1,
+                                      -(-row_lens // kb), self.shared_blocks_host[row_seq])
+                self.plan_host = ops.decode_plan(row_lens, self.partition_size,
+                                                 self.sliding_window, np.diff(row_qsl), row_seq)
+                self.attn_tables = torch.from_numpy(row_tables).to(dev)
+                self.attn_lens = torch.from_numpy(row_lens).to(dev)
+                self.attn_qsl = torch.from_numpy(row_qsl).to(dev)
+                self.attn_max_query_len = int(np.diff(row_qsl).max())
+                self.attn_shared = torch.from_numpy(row_shared.astype(np.int32)).to(dev)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self._fused_call = None  # the one-launch step's marshalled arguments
         self.workspace = None
@@ -199,10 +232,10 @@ class DecodeStep:
                                         self.num_items, self.max_group, self.workspace)
         elif self.all_queries:
             ops.paged_attention_multi(self.out, self.query, self.key_cache, self.value_cache,
-                                      self.block_tables, self.context_lens,
-                                      self.query_start_loc, self.max_query_len, self.scale,
+                                      self.attn_tables, self.attn_lens, self.attn_qsl,
+                                      self.attn_max_query_len, self.scale,
                                       self.max_context_len, self.partition_size, self.plan,
-                                      self.workspace, self.shared_blocks, self.sliding_window)
+                                      self.workspace, self.attn_shared, self.sliding_window)
         elif self.planned:
             ops.paged_attention_decode_planned(self.out, self.query, self.key_cache,
                                                self.value_cache, self.block_tables,
@@ -226,8 +259,9 @@ class DecodeStep:
         checked and marshalled on the first call; later calls launch them on
         the current stream."""
         if not self.fused_ok:
-            raise ValueError("a copy-on-write of a block of several kernel blocks needs "
-                             "copy_blocks: run the step unfused")
+            raise ValueError("a copy-on-write of a block of several kernel blocks, or query "
+                             "blocks that read each other's new rows, need the separate "
+                             "calls: run the step unfused")
         if self._fused_call is None:
             if self.cascade:
                 self._fused_call = ops.prepare_decode_step_cascade(

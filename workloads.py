@@ -253,6 +253,20 @@ def llama7b_spec4_fp16(num_seqs=64, drafts=4):
     return w
 
 
+def llama7b_prefill512_fp16(num_seqs=16, chunk=512):
+    """Chunked prefill on the Llama-7B layer: each sequence has a cached
+    prefix of U[0, 1536] tokens and appends a ``chunk``-token prefill chunk
+    in the step, every new token a query (causal over the chunk)."""
+    rng = np.random.default_rng(8)
+    prefix = rng.integers(0, 1537, size=num_seqs)
+    lens = [int(p) + chunk for p in prefix]
+    w = custom_multi("llama7b_prefill512_fp16", 8, lens, [chunk] * num_seqs, dtype="f16",
+                     H=32, Hkv=32, D=128, B=16)
+    w.notes = (f"{num_seqs} sequences, cached prefix U[0,1536] + a {chunk}-token prefill chunk "
+               "(every new token a query, causal); 32x128 MHA fp16, B=16")
+    return w
+
+
 def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
     """The GQA batch verifying 2 speculative tokens per sequence (2 x 8 query
     vectors per KV head fill the 16 matrix-core columns)."""
@@ -386,6 +400,7 @@ CONFIGS = {
     "long_context_bf16": long_context_bf16,
     "shared_prefix_cascade_bf16": shared_prefix_cascade_bf16,
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
+    "llama7b_prefill512_fp16": llama7b_prefill512_fp16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
     "qwen72b_gqa_tp8_bf16": qwen72b_gqa_tp8_bf16,
