@@ -32,7 +32,7 @@ MATRIX_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "llama7b_fp16"
 CSRC = os.path.join(REPO, "paged_kv_cache_123_amd", "csrc")
 ATTN_SRCS = [os.path.join(CSRC, f) for f in ("attention_kernels.hip", "attention_mfma.hip",
-                                             "decode_common.h")]
+                                             "attention_prefill.hip", "decode_common.h")]
 
 
 def attention_source_hash() -> str:
@@ -564,6 +564,8 @@ def main():
     ap.add_argument("--cascade", type=int, default=None,
                     help="cascade plan with groups of at most N sharers (0: off; default: "
                          "the workload's)")
+    ap.add_argument("--no-prefill-kernel", action="store_true",
+                    help="attend prefill chunks as 16-token query blocks on the decode kernels")
     ap.add_argument("--unfused", action="store_true",
                     help="time copy_blocks, slot mapping, scatter and attention as four launches "
                          "instead of the one-launch step")
@@ -618,7 +620,8 @@ def main():
     step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
                       w.scale, part, all_queries=w.extra.get("queries") == "all",
                       sliding_window=window_of(w),
-                      kernel_block_size=w.extra.get("kernel_block_size", 0), cascade=cascade)
+                      kernel_block_size=w.extra.get("kernel_block_size", 0), cascade=cascade,
+                      prefill_kernel=not args.no_prefill_kernel)
     torch.cuda.synchronize()
 
     # steps whose cache writes must precede the attention (query blocks of a
@@ -719,7 +722,8 @@ def main():
         "attention_ms": attn_stats,
         "roofline": {
             "bound": "mfma" if compute_bound else "hbm",
-            "kernel": ("cascade_decode_kernel" if cascade and not part else
+            "kernel": ("prefill_kernel (query blocks)" if step.prefill_rows else
+                       "cascade_decode_kernel" if cascade and not part else
                        "paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
                            args.kernel == "auto" and w.num_heads > w.num_kv_heads))
                        else "paged_decode_kernel")

@@ -458,6 +458,49 @@ int32_t pa_query_blocks(const int32_t* context_lens, const int32_t* query_start_
                         int64_t* num_rows);
 
 /* ------------------------------------------------------------------------
+ * Prefill attention over query blocks on the matrix cores (16-bit storage,
+ * head_size 128, single pass): the result of pa_paged_attention_multi for
+ * the rows of pa_query_blocks, computed with each key/value tile loaded once
+ * into LDS for all query vectors of a block instead of once per 16 of them.
+ *
+ * pa_prefill_block_tokens (host): *tokens receives the max_block to give
+ * pa_query_blocks, 64 / (num_heads / num_kv_heads) new tokens per block.
+ * PA_EINVAL for a null tokens or a head ratio other than 1, 2, 4 or 8.
+ *
+ * pa_paged_attention_prefill: one workgroup per (row, KV head).
+ *   out, query          device [num_tokens][num_heads][128], the step's tokens
+ *   block_tables        device int32 [num_seqs][bt_stride], indexed by row_seq
+ *   row_seq, row_lens   device int32 [num_rows]: each row's table row and its
+ *                       context length (that of the row's last token)
+ *   row_qsl             device int32 [num_rows + 1]: row r's tokens are the
+ *                       query rows row_qsl[r] .. row_qsl[r + 1] - 1, at most
+ *                       pa_prefill_block_tokens of them (tokens past that
+ *                       leave their outputs undefined)
+ *   work_items          device int32 [num_rows][2], may be NULL: launch order,
+ *                       (row, 0) for every row once, e.g. pa_decode_plan_window
+ *                       over row_lens (largest first); NULL = the last row
+ *                       first, so that a sequence's rows run together
+ *   max_context_len     host bound on row_lens, checked against bt_stride
+ *   sliding_window      as for pa_paged_attention_multi
+ * Every key a row sees, its own new tokens included, must already be in the
+ * caches (pa_reshape_and_cache before this call).  Errors: as
+ * pa_paged_attention_multi's checks of sizes, pointers and alignment, plus
+ * PA_EINVAL for f32 storage, head_size 64, null row arrays, num_rows < 1 or
+ * a scale that is not positive and finite.
+ * ---------------------------------------------------------------------- */
+int32_t pa_prefill_block_tokens(int32_t num_heads, int32_t num_kv_heads, int32_t* tokens);
+
+int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int64_t bt_stride, const int32_t* row_seq,
+                                   const int32_t* row_lens, const int32_t* row_qsl,
+                                   int32_t num_rows, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size,
+                                   int32_t max_context_len, float scale, int32_t dtype,
+                                   const int32_t* work_items, int32_t sliding_window,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * Attention alone over a cascade plan (pa_decode_plan_cascade), on caches that
  * already hold the step's rows: pa_paged_attention_decode_planned's
  * arguments, with the plan (device int32, whole: items and group section),

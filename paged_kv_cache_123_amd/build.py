@@ -16,14 +16,19 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["cache_kernels.hip", "attention_kernels.hip", "attention_mfma.hip", "capi.hip",
-               "probe_kernels.hip"]
+HIP_SOURCES = ["cache_kernels.hip", "attention_kernels.hip", "attention_mfma.hip",
+               "attention_prefill.hip", "capi.hip", "probe_kernels.hip"]
 CXX_SOURCES = ["context_parallel.cpp", "sha256.cpp", "block_pool.cpp", "plan.cpp", "status.cpp"]
 
 # Packed-fp32 instructions are kept out of every HIP build.
 HIPCC_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Matrix-core kernels keep their accumulators in ordinary VGPRs: with the
+# default accumulation-register form the compiler moves every accumulator
+# into and out of AGPRs around each MFMA once the softmax rescales it.
+MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"attention_prefill.hip": MFMA_FLAGS, "attention_mfma.hip": MFMA_FLAGS}
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
@@ -43,11 +48,13 @@ def build(verbose: bool = False, defines=(), out: str = LIB, obj_dir: str = OBJ)
     (tuning constants of the kernels); ``out``/``obj_dir``: where to put the
     library and objects (defaults: in-tree)."""
     os.makedirs(obj_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     dflags = [f"-D{d}" for d in defines]
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
-        jobs.append(["hipcc", *HIPCC_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["hipcc", *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *dflags, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-I/opt/rocm/include", "-c", os.path.join(CSRC, src),

@@ -1,0 +1,314 @@
+// Paged attention for prefill chunks on the matrix cores: every new token of
+// a sequence is a query, causal over the new tokens ([DEEPSONAR] section 2.5
+// schedules prefill chunks like decode tokens; [CSDN] section 2.3 lays a
+// step's tokens out by query_start_loc).  The result is that of
+// pa_paged_attention_multi; only the work layout differs.
+//
+// The host cuts each sequence's new tokens into query blocks of 64/G tokens
+// (pa_query_blocks): with G query heads per KV head, a block holds 64 query
+// vectors (token, head).  One workgroup of four waves serves one (block, KV
+// head); wave w owns query vectors 16w .. 16w+15, the 16 columns of its
+// matrix-core tiles.  The workgroup walks the keys the block sees in tiles of
+// 64 tokens, double-buffered in LDS: the next tile's rows are loaded into
+// registers while the waves score and accumulate the current one from LDS,
+// so each K/V row is read once per 64 queries.  Every wave sees every tile,
+// keeps the online softmax of its own columns (mfma_tile_update) and writes
+// its outputs itself: no merge across waves.  LDS rows are padded to 17
+// 16-byte units so that the K operand reads (16 tokens of one dim chunk)
+// fall into different banks.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "decode_common.h"
+#include "launch.h"
+#include "pagedkv.h"
+
+namespace pa {
+namespace {
+
+using namespace dev;
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillTile = 64;  // key tokens per LDS tile
+
+// Maximum over the four lane groups of a column (lanes 16 and 32 apart):
+// each permlane swap trades rows of 16 lanes between its two results, so
+// their maximum is that of the lane and its partner.
+__device__ __forceinline__ float column_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int DT>
+__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
+    void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
+    const void* value_cache, const int32_t* __restrict__ block_tables, int64_t bt_stride,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_lens,
+    const int32_t* __restrict__ row_qsl, const int32_t* __restrict__ work_items,
+    int32_t num_rows, int32_t num_heads, int32_t num_kv_heads, int32_t log2_block,
+    int32_t log2_group, float scale_log2, int32_t window) {
+  constexpr int NW = kPrefillWaves;
+  constexpr int NT = NW * 64;
+  constexpr int D = 128;
+  constexpr int DV = D / 8;        // 16-byte units per token row
+  constexpr int NK = D / 32;       // score MFMAs per 16-token sub-tile
+  constexpr int NE = 8;            // value MFMA chunks
+  constexpr int KT = kPrefillTile;
+  constexpr int ROW = DV + 1;      // padded LDS row, in 16-byte units
+  constexpr int PER = KT * DV / NT;  // units of each cache a thread moves per tile
+  static_assert(KT * DV % NT == 0 && KT % 16 == 0, "tile shape");
+  using MM = Mma<DT>;
+
+  __shared__ uint4 sk[2][KT * ROW];
+  __shared__ uint4 sv[2][KT * ROW];
+  __shared__ int32_t sm_bt[kChunkTokens];
+
+  // without a list, the last row first: the rows of a sequence run together,
+  // its longest first
+  const int item = static_cast<int>(blockIdx.x / num_kv_heads);
+  const int r = work_items ? work_items[2 * item] : num_rows - 1 - item;
+  const int kvh = static_cast<int>(blockIdx.x % num_kv_heads);
+  const int s = row_seq[r];
+  const int L = row_lens[r];
+  const int q0 = row_qsl[r];
+  const int qlen = row_qsl[r + 1] - q0;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int gmask = (1 << log2_group) - 1;
+  const int v = wave * 16 + col;    // query vector of this lane's column
+  const int qi = v >> log2_group;   // its token within the block
+  const bool valid = qi < qlen;
+  const int h = (kvh << log2_group) + (v & gmask);
+  // keys this column sees: [lo, bound)
+  const int bound = valid ? L - qlen + qi + 1 : 0;
+  const int lo = !valid ? INT_MAX : window > 0 ? max(0, bound - window) : 0;
+  // the block's first visible key, and this wave's key range (wave-uniform)
+  const int lo_min = window > 0 ? max(0, L - qlen + 1 - window) : 0;
+  // and the keys every column of it sees: [wlo_max, whi_min) (empty when a
+  // column has no query)
+  int whi = bound, wlo = lo, whi_min = valid ? bound : 0, wlo_max = valid ? lo : INT_MAX;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    whi = max(whi, __shfl_xor(whi, off));
+    wlo = min(wlo, __shfl_xor(wlo, off));
+    whi_min = min(whi_min, __shfl_xor(whi_min, off));
+    wlo_max = max(wlo_max, __shfl_xor(wlo_max, off));
+  }
+
+  uint4 qv[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    qv[k] = make_uint4(0, 0, 0, 0);
+    if (valid)
+      qv[k] = *reinterpret_cast<const uint4*>(
+          static_cast<const uint16_t*>(query) +
+          (static_cast<int64_t>(q0 + qi) * num_heads + h) * D + k * 32 + grp * 8);
+  }
+  f32x4 o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, lsum = 0.0f;
+
+  const int B = 1 << log2_block;
+  const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
+  const int64_t head_off_v = static_cast<int64_t>(kvh) * B * DV;
+  const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
+  const uint4* kc = static_cast<const uint4*>(key_cache);
+  const uint4* vc = static_cast<const uint4*>(value_cache);
+
+  for (int c0 = lo_min; c0 < L; c0 += kChunkTokens) {
+    const int c1 = min(c0 + kChunkTokens, L);
+    const int b0 = c0 >> log2_block;
+    const int nb = ((c1 - 1) >> log2_block) - b0 + 1;
+    for (int i = tid; i < nb; i += NT) sm_bt[i] = bt_row[b0 + i];
+    __syncthreads();
+    const int ntiles = (c1 - c0 + KT - 1) / KT;
+    // rows of tile t into registers; rows past the chunk repeat its last row,
+    // so tiles beyond the last are loaded too (unconditional loads keep the
+    // wait counts of the pipeline static) and hit that one row
+    auto gload = [&](int t, uint4 (&pk)[PER], uint4 (&pv)[PER]) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int u = tid + j * NT;
+        const int tok = min(c0 + t * KT + u / DV, c1 - 1);
+        const int64_t idx = static_cast<int64_t>(sm_bt[(tok >> log2_block) - b0]) * blk_stride_v +
+                            head_off_v + (tok & (B - 1)) * DV + u % DV;
+        pk[j] = load_cached(kc + idx);  // the sequence's other blocks read these rows too
+        pv[j] = load_cached(vc + idx);
+      }
+    };
+    auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int u = tid + j * NT;
+        sk[buf][(u / DV) * ROW + u % DV] = pk[j];
+        sv[buf][(u / DV) * ROW + u % DV] = pv[j];
+      }
+    };
+    auto tile = [&](int t, int buf) {
+      const int t0 = c0 + t * KT;
+      if (t0 < whi && t0 + KT > wlo) {
+        // scores of the whole tile first (independent MFMA chains): lane
+        // (col, grp) gets those of keys 16 st + 4 grp + j of its column
+        constexpr int NS = KT / 16;
+        f32x4 sc[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          sc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k = 0; k < NK; ++k)
+            sc[st] = MM::k32(sk[buf][(st * 16 + col) * ROW + k * 4 + grp], qv[k], sc[st]);
+        }
+        // a tile inside every column's keys needs no mask (wave-uniform)
+        if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
+#pragma unroll
+          for (int st = 0; st < NS; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int tt = t0 + st * 16 + 4 * grp + j;
+              const bool vis = (tt < bound) & (tt >= lo) & (tt < c1);
+              sc[st][j] = vis ? sc[st][j] : -INFINITY;
+            }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+          mt = fmaxf(mt, fmaxf(fmaxf(sc[st][0], sc[st][1]), fmaxf(sc[st][2], sc[st][3])));
+        mt = column_max(mt) * scale_log2;
+        // The reference maximum moves only when the tile's maximum exceeds it
+        // by more than 2^8: probabilities stay below 256 and the
+        // accumulators are rescaled only on such rare jumps.
+        const float mref = mt > m + 8.0f ? mt : m;
+        const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
+        const float corr = __builtin_amdgcn_exp2f(m - ms);
+        float p[NS][4];
+        float tsum = 0.0f;
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[st][j] = __builtin_amdgcn_exp2f(fmaf(sc[st][j], scale_log2, -ms));
+            tsum += p[st][j];
+          }
+        lsum = lsum * corr + tsum;
+        if (__any(mref != m)) {
+#pragma unroll
+          for (int e = 0; e < NE; ++e) o[e] *= corr;
+        }
+        m = mref;
+        // value products over pairs of sub-tiles (K = 32 keys per MFMA):
+        // probabilities as a 16-bit head plus its remainder
+#pragma unroll
+        for (int sp = 0; sp < NS; sp += 2) {
+          uint32_t hi[8], rem[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float back, unused;
+              hi[4 * h + j] = MM::round16(p[sp + h][j], back);
+              rem[4 * h + j] = MM::round16(p[sp + h][j] - back, unused);
+            }
+          const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                       hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+          const uint4 plo = make_uint4(rem[0] | (rem[1] << 16), rem[2] | (rem[3] << 16),
+                                       rem[4] | (rem[5] << 16), rem[6] | (rem[7] << 16));
+          // rows 4 grp + u of both sub-tiles, dims 8 col .. 8 col + 7
+          uint4 vr[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            vr[u] = sv[buf][((sp + (u >> 2)) * 16 + 4 * grp + (u & 3)) * ROW + col];
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
+            // dim 8 col + e of the eight keys, in the order of phi
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const int w = e >> 1;
+            uint4 a;
+            a.x = __builtin_amdgcn_perm(dword(vr[1], w), dword(vr[0], w), sel);
+            a.y = __builtin_amdgcn_perm(dword(vr[3], w), dword(vr[2], w), sel);
+            a.z = __builtin_amdgcn_perm(dword(vr[5], w), dword(vr[4], w), sel);
+            a.w = __builtin_amdgcn_perm(dword(vr[7], w), dword(vr[6], w), sel);
+            o[e] = MM::k32(a, phi, o[e]);
+            o[e] = MM::k32(a, plo, o[e]);
+          }
+        }
+      }
+    };
+    // LDS holds tile t and t + 1 alternately; registers A and B carry the
+    // loads of the next two tiles, so two tiles' rows are in flight while
+    // one is computed
+    uint4 ak[PER], av[PER], bk[PER], bv[PER];
+    gload(0, ak, av);
+    lstore(0, ak, av);
+    gload(1, ak, av);
+    gload(2, bk, bv);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(t, 0);
+      lstore(1, ak, av);  // tile t + 1
+      __syncthreads();
+      gload(t + 3, ak, av);
+      if (t + 1 >= ntiles) break;
+      tile(t + 1, 1);
+      lstore(0, bk, bv);  // tile t + 2
+      __syncthreads();
+      gload(t + 4, bk, bv);
+    }
+  }
+
+  // per-column sum over the four lane groups (disjoint key slots)
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (!valid) return;
+  // lane (col, grp) holds dims 32 grp + 8 j + e of its column: 8 contiguous
+  // dims per j, stored as one 16-byte unit
+  uint16_t* dst = static_cast<uint16_t*>(out) +
+                  (static_cast<int64_t>(q0 + qi) * num_heads + h) * D + 32 * grp;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < NE; e += 2) {
+      float back;
+      const uint32_t a = MM::round16(o[e][j] / lsum, back);
+      const uint32_t b = MM::round16(o[e + 1][j] / lsum, back);
+      w[e / 2] = a | (b << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+}  // namespace
+
+int prefill_block_tokens(int group) { return kPrefillWaves * 16 / group; }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  int log2_block = 0;
+  while ((1 << log2_block) < a.block_size) ++log2_block;
+  int log2_group = 0;
+  while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_rows) * a.num_kv_heads));
+  const float sl2 = a.scale * kLog2e;
+  if (a.dtype == PA_BF16)
+    hipLaunchKernelGGL(prefill_kernel<PA_BF16>, grid, dim3(kPrefillWaves * 64), 0, stream, a.out,
+                       a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
+                       a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,
+                       a.num_kv_heads, log2_block, log2_group, sl2, a.window);
+  else
+    hipLaunchKernelGGL(prefill_kernel<PA_F16>, grid, dim3(kPrefillWaves * 64), 0, stream, a.out,
+                       a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
+                       a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,
+                       a.num_kv_heads, log2_block, log2_group, sl2, a.window);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -2,6 +2,7 @@
 // validation, then the launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <string>
 
@@ -607,6 +608,45 @@ int32_t pa_merge_attention_partials(void* out, const float* max_logits, const fl
                                          num_seqs, num_heads, head_size, dtype,
                                          static_cast<hipStream_t>(stream)),
                   "pa_merge_attention_partials");
+}
+
+int32_t pa_prefill_block_tokens(int32_t num_heads, int32_t num_kv_heads, int32_t* tokens) {
+  if (!tokens || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "pa_prefill_block_tokens: bad arguments");
+  const int32_t g = num_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_EINVAL, "pa_prefill_block_tokens: num_heads / num_kv_heads must be 1, 2, 4 or 8");
+  *tokens = pa::prefill_block_tokens(g);
+  return PA_OK;
+}
+
+int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int64_t bt_stride, const int32_t* row_seq,
+                                   const int32_t* row_lens, const int32_t* row_qsl,
+                                   int32_t num_rows, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size,
+                                   int32_t max_context_len, float scale, int32_t dtype,
+                                   const int32_t* work_items, int32_t sliding_window,
+                                   void* stream) {
+  const char* who = "pa_paged_attention_prefill";
+  if (sliding_window < 0) return fail(PA_EINVAL, "pa_paged_attention_prefill: sliding_window < 0");
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            row_lens, num_rows, num_heads, num_kv_heads, head_size, block_size,
+                            max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (!row_seq || !row_qsl) return fail(PA_EINVAL, "pa_paged_attention_prefill: NULL row arrays");
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(PA_EINVAL, "pa_paged_attention_prefill: scale must be positive and finite");
+  if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_prefill: needs 16-bit storage and head_size 128");
+  if (static_cast<int64_t>(num_rows) * num_kv_heads > 0x7fffffff)
+    return fail(PA_EINVAL, "pa_paged_attention_prefill: too many rows");
+  pa::PrefillArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, row_seq,
+                    row_lens, row_qsl, work_items, num_rows, num_heads, num_kv_heads,
+                    block_size, scale, dtype, sliding_window};
+  return launched(pa::launch_prefill(a, static_cast<hipStream_t>(stream)), who);
 }
 
 int32_t pa_validate_tables(const int32_t* block_tables, int64_t bt_stride,

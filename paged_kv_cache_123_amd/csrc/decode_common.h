@@ -323,5 +323,64 @@ struct Mma<PA_F16> {
   }
 };
 
+__device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One 16-token tile of one wave: scores S^T = K Q^T on the matrix cores, the
+// online softmax of every head column (vis[j]: whether this lane's column
+// sees token grp + 4j of the tile), and O^T += V^T P^T with P split into a
+// 16-bit head and remainder.  (m, lsum) are the column's running maximum
+// (log2 domain) and the lane's partial sum; o its accumulator chunks.
+template <int DT>
+__device__ __forceinline__ void mfma_tile_update(const uint4 (&kr)[4], const uint4 (&vr)[4],
+                                                 const uint4 (&qv)[4], const bool (&vis)[4],
+                                                 float scale_log2, float& m, float& lsum,
+                                                 f32x4 (&o)[8]) {
+  using MM = Mma<DT>;
+  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sc = MM::k32(kr[k], qv[k], sc);
+  float x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = vis[j] ? sc[j] * scale_log2 : -INFINITY;
+  float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float mn = fmaxf(m, mt);
+  const float ms = mn == -INFINITY ? 0.0f : mn;  // a column with no visible key yet
+  const float corr = __builtin_amdgcn_exp2f(m - ms);
+  float pr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - ms);
+  lsum = lsum * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  // corr is exactly 1 in a column whose maximum did not grow (and its
+  // accumulators are 0 while it has seen no key): rescale only if some did
+  if (__any(mn > m)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= corr;
+  }
+  m = mn;
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float back, unused;
+    hi[j] = MM::round16(pr[j], back);
+    lo[j] = MM::round16(pr[j] - back, unused);
+  }
+  const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+  const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    const int w = e >> 1;
+    uint2 a;
+    a.x = __builtin_amdgcn_perm(dword(vr[1], w), dword(vr[0], w), sel);
+    a.y = __builtin_amdgcn_perm(dword(vr[3], w), dword(vr[2], w), sel);
+    o[e] = MM::k16(a, phi, o[e]);
+    o[e] = MM::k16(a, plo, o[e]);
+  }
+}
+
 }  // namespace dev
 }  // namespace pa

@@ -82,6 +82,26 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Single-pass cascade plan (items and group section as pa_decode_plan_cascade
 // writes them with partition_size 0): matrix cores, 16-bit storage, D = 128.
 hipError_t launch_cascade_single(const DecodeArgs& a, hipStream_t stream);
+// Prefill chunks on the matrix cores (16-bit storage, head_size 128): rows
+// are query blocks of at most prefill_block_tokens(G) tokens (pa_query_blocks).
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  int64_t bt_stride;
+  const int32_t* row_seq;    // [num_rows] sequence of each row (its table row)
+  const int32_t* row_lens;   // [num_rows] context length up to the row's last token
+  const int32_t* row_qsl;    // [num_rows + 1] the rows' query rows
+  const int32_t* work_items; // [num_rows][2] launch order (row, 0), or nullptr
+  int32_t num_rows, num_heads, num_kv_heads, block_size;
+  float scale;
+  int32_t dtype;
+  int32_t window;
+};
+int prefill_block_tokens(int group);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // mode: 0 automatic, 1 vector kernel, 2 matrix-core kernel; returns the previous mode.
 int set_decode_kernel(int mode);
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream);

@@ -352,6 +352,13 @@ def query_blocks(context_lens, query_start_loc, max_block: int):
     return row_seq, row_lens, row_qsl
 
 
+def prefill_block_tokens(num_heads: int, num_kv_heads: int) -> int:
+    """New tokens per query block of the prefill kernel (pa_prefill_block_tokens)."""
+    t = ctypes.c_int32(0)
+    check(lib().pa_prefill_block_tokens(num_heads, num_kv_heads, ctypes.byref(t)))
+    return t.value
+
+
 def map_to_kernel_blocks(manager_ids, blocks_per_kv_block: int) -> np.ndarray:
     """Host int32 kernel block ids of manager block ids (any shape; the last
     axis grows by ``blocks_per_kv_block``); -1 entries stay -1."""
@@ -630,6 +637,42 @@ def paged_attention_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: t
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, plan.data_ptr(),
         num_items, max_group_size, ws_ptr or None, ws_bytes, _stream()))
+
+
+def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                            value_cache: torch.Tensor, block_tables: torch.Tensor,
+                            row_seq: torch.Tensor, row_lens: torch.Tensor, row_qsl: torch.Tensor,
+                            scale: float, max_context_len: int, work_items=None,
+                            sliding_window: int = 0) -> None:
+    """Attention of every new token over query blocks (pa_paged_attention_prefill):
+    row_seq/row_lens/row_qsl as from query_blocks with prefill_block_tokens;
+    the step's cache writes must have run."""
+    _dev(out, query, key_cache, value_cache, block_tables, row_seq, row_lens, row_qsl)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if query.dim() != 3 or query.shape[2] != D or out.shape != query.shape:
+        raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+    if query.dtype != key_cache.dtype or out.dtype != key_cache.dtype:
+        raise TypeError("query/out must have the cache dtype")
+    for n, t in (("query", query), ("out", out), ("block_tables", block_tables),
+                 ("row_seq", row_seq), ("row_lens", row_lens), ("row_qsl", row_qsl)):
+        _contig(n, t)
+    R = row_seq.numel()
+    for n, t, size in (("row_seq", row_seq, R), ("row_lens", row_lens, R),
+                       ("row_qsl", row_qsl, R + 1)):
+        if t.dtype != torch.int32 or t.numel() != size:
+            raise ValueError(f"{n} must be int32 with {size} entries")
+    items = 0
+    if work_items is not None:
+        _dev(work_items)
+        _contig("work_items", work_items)
+        if work_items.dtype != torch.int32 or work_items.shape != (R, 2):
+            raise ValueError("work_items must be int32 [num_rows, 2]")
+        items = work_items.data_ptr()
+    check(lib().pa_paged_attention_prefill(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), row_seq.data_ptr(), row_lens.data_ptr(),
+        row_qsl.data_ptr(), R, query.shape[1], hkv, D, B, max_context_len, scale,
+        _dtype(key_cache), items or None, sliding_window, _stream()))
 
 
 def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

@@ -82,7 +82,10 @@ class DecodeStep:
     sequence's new tokens) instead of one query per sequence; a sequence with
     more new tokens than one workgroup holds as query vectors (a prefill
     chunk) is attended as several query blocks (pa_query_blocks), after the
-    step's cache writes (the step then runs as separate launches).
+    step's cache writes (the step then runs as separate launches); with
+    16-bit storage, head_size 128 and no partitions the blocks hold 64 query
+    vectors and run on the prefill kernel (pa_paged_attention_prefill) unless
+    ``prefill_kernel`` is False.
     ``sliding_window``: attention sees the last W tokens only, and blocks
     outside every query's window are released before the step's appends.
     ``kernel_block_size``: the allocator hands out blocks of ``block_size``
@@ -99,7 +102,7 @@ class DecodeStep:
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
                  values: dict, scale: float, partition_size: int = 0, planned: bool = True,
                  all_queries: bool = False, sliding_window: int = 0,
-                 kernel_block_size: int = 0, cascade: int = 0):
+                 kernel_block_size: int = 0, cascade: int = 0, prefill_kernel: bool = True):
         self.pool = Pool(num_blocks, block_size, free_order)
         if any(op[0] == "request" for op in history):
             self.pool.enable_prefix_caching()
@@ -178,6 +181,7 @@ class DecodeStep:
         self.attn_qsl, self.attn_max_query_len = self.query_start_loc, self.max_query_len
         self.attn_shared = self.shared_blocks
         self.query_blocks = False
+        self.prefill_rows = False
         if all_queries:
             H, D = self.query.shape[1], self.query.shape[2]
             G = H // values["key_cache"].shape[1]
@@ -188,6 +192,11 @@ class DecodeStep:
             if self.max_query_len > block:
                 self.query_blocks = True
                 self.fused_ok = False  # blocks of one sequence read each other's new rows
+                # single pass on the matrix cores: the prefill kernel's larger
+                # blocks, each K/V tile staged once in LDS for the whole block
+                self.prefill_rows = prefill_kernel and matrix and not self.partition_size
+                if self.prefill_rows:
+                    block = ops.prefill_block_tokens(H, values["key_cache"].shape[1])
                 row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl, block)
                 row_tables = np.ascontiguousarray(tables[row_seq])
                 rows_per_seq = np.bincount(row_seq, minlength=len(seqs))
@@ -202,6 +211,7 @@ class DecodeStep:
                 self.attn_qsl = torch.from_numpy(row_qsl).to(dev)
                 self.attn_max_query_len = int(np.diff(row_qsl).max())
                 self.attn_shared = torch.from_numpy(row_shared.astype(np.int32)).to(dev)
+                self.row_seq = torch.from_numpy(row_seq).to(dev)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self._fused_call = None  # the one-launch step's marshalled arguments
         self.workspace = None
@@ -230,6 +240,11 @@ class DecodeStep:
                                         self.block_tables, self.context_lens, self.scale,
                                         self.max_context_len, self.partition_size, self.plan,
                                         self.num_items, self.max_group, self.workspace)
+        elif self.prefill_rows:
+            ops.paged_attention_prefill(self.out, self.query, self.key_cache, self.value_cache,
+                                        self.block_tables, self.row_seq, self.attn_lens,
+                                        self.attn_qsl, self.scale, self.max_context_len,
+                                        None, self.sliding_window)
         elif self.all_queries:
             ops.paged_attention_multi(self.out, self.query, self.key_cache, self.value_cache,
                                       self.attn_tables, self.attn_lens, self.attn_qsl,

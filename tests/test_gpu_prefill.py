@@ -32,25 +32,37 @@ CASES = [
     ("bf16", 128, 1, 4, [70, 33], [70, 20], 32, 0),
     ("bf16", 128, 16, 1, [900, 400], [200, 400], 0, 128),
     ("f16", 64, 32, 1, [2100, 2048], [300, 1], 512, 0),
+    # contexts over one 2048-token table chunk; 16- and 8-token prefill blocks
+    ("f16", 128, 16, 4, [3000, 520], [700, 520], 0, 0),
+    ("bf16", 128, 32, 2, [2500, 96], [96, 96], 0, 1000),
+    ("bf16", 128, 1, 1, [150, 65], [130, 65], 0, 0),
+    ("f16", 128, 128, 8, [1000, 300], [300, 64], 0, 0),
 ]
 
 
 @BOTH
+@pytest.mark.parametrize("prefill_kernel", [False, True], ids=["decode-kernels", "prefill-kernel"])
 @pytest.mark.parametrize("dtype,D,B,G,lens,new,part,window", CASES,
                          ids=[f"{c[0]}-D{c[1]}-B{c[2]}-G{c[3]}-n{max(c[5])}-P{c[6]}-W{c[7]}"
                               for c in CASES])
-def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window, decode_kernel):
+def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window, prefill_kernel,
+                                        decode_kernel):
     _require_gpu()
     from paged_kv_cache_123_amd.step import DecodeStep
+    matrix = dtype != "f32" and D == 128
+    if prefill_kernel and (decode_kernel == "valu" or not matrix or part):
+        pytest.skip("the prefill kernel runs 16-bit, head_size 128, single pass; once")
     print(f"[prefill] {dtype} D={D} B={B} G={G} new={new} P={part} W={window} "
-          f"kernel={decode_kernel}", flush=True)
+          f"kernel={'prefill' if prefill_kernel else decode_kernel}", flush=True)
     w = W.custom_multi("prefill", 31, lens, new, dtype=dtype, H=2 * G, Hkv=2, D=D, B=B,
                        partition_size=part, sliding_window=window)
     vals = W.make_values(w, DEV)
     host = {k: to_host(v) for k, v in vals.items()}
     step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals, w.scale,
-                      part, all_queries=True, sliding_window=window)
+                      part, all_queries=True, sliding_window=window,
+                      prefill_kernel=prefill_kernel)
     assert step.query_blocks, "the chunks should need several query blocks"
+    assert step.prefill_rows == (prefill_kernel and matrix and not part)
     with pytest.raises(ValueError):
         step.fused()  # blocks of one sequence read each other's new rows
     out = step.run()
@@ -63,3 +75,32 @@ def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window,
         assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
     want = ora.attention_multi(host["query"], kc, vc)
     check_attention(to_host(out), want, w.dtype, f"prefill {dtype} G={G} P={part} W={window}")
+
+
+def test_prefill_kernel_launch_order_does_not_change_results():
+    """pa_paged_attention_prefill with a work list (largest rows first) and
+    without one (last row first): each (row, KV head) is one workgroup's, so
+    the outputs are bit-identical."""
+    _require_gpu()
+    from paged_kv_cache_123_amd import ops
+    from paged_kv_cache_123_amd.step import DecodeStep
+    print("[prefill] launch order", flush=True)
+    w = W.custom_multi("prefill-order", 5, [900, 300, 1500], [300, 200, 129], dtype="f16", H=8,
+                       Hkv=2, D=128, B=16)
+    vals = W.make_values(w, DEV)
+    step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals, w.scale,
+                      0, all_queries=True)
+    assert step.prefill_rows
+    step.copy_blocks()
+    step.slot_mapping_kernel()
+    step.scatter()
+    outs = []
+    for items in (step.plan, None):
+        out = torch.full_like(step.query, float("nan"))
+        ops.paged_attention_prefill(out, step.query, step.key_cache, step.value_cache,
+                                    step.block_tables, step.row_seq, step.attn_lens,
+                                    step.attn_qsl, step.scale, step.max_context_len, items)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1])
