@@ -45,6 +45,17 @@ __device__ __forceinline__ float column_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Transposed value tile: row d (one dim) holds the tile's 64 keys of that
+// dim, 128 bytes = 8 units of 16 bytes.  Unit k of a row holds the eight keys
+// one lane passes to a K = 32 value MFMA (keys 32 (k/4) + 4 (k%4) + 0..3 and
+// the same plus 16, the order of the probabilities of lane group k%4), and it
+// is stored at unit k ^ (d ^ d/8) % 8: the 16 dims one MFMA reads (16 e ..
+// 16 e + 15) fall into distinct units, and so, two by two, do the 16 dims of
+// one 8-byte store instruction.
+__device__ __forceinline__ int value_slot(int d, int k) {
+  return d * 8 + (k ^ ((d ^ (d >> 3)) & 7));
+}
+
 template <int DT>
 __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
@@ -61,12 +72,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   constexpr int NE = 8;            // value MFMA chunks
   constexpr int KT = kPrefillTile;
   constexpr int ROW = DV + 1;      // padded LDS row, in 16-byte units
-  constexpr int PER = KT * DV / NT;  // units of each cache a thread moves per tile
-  static_assert(KT * DV % NT == 0 && KT % 16 == 0, "tile shape");
+  constexpr int PER = 4;           // keys of each cache a thread moves per tile
+  static_assert(KT * DV == NT * PER && KT % 32 == 0, "tile shape");
   using MM = Mma<DT>;
+  constexpr bool kSplitP = DT == PA_BF16;  // probabilities as head + remainder
 
   __shared__ uint4 sk[2][KT * ROW];
-  __shared__ uint4 sv[2][KT * ROW];
+  // values transposed: 128 dims x 64 keys of 16 bits per buffer, keys in
+  // MFMA operand order and 16-byte units XOR-swizzled by the dim (value_slot)
+  __shared__ uint4 sv[2][D * KT / 8];
   __shared__ int32_t sm_bt[kChunkTokens];
 
   // without a list, the last row first: the rows of a sequence run together,
@@ -91,15 +105,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   // keys this column sees: [lo, bound)
   const int bound = valid ? L - qlen + qi + 1 : 0;
   const int lo = !valid ? INT_MAX : window > 0 ? max(0, bound - window) : 0;
-  // the block's first visible key, and this wave's key range (wave-uniform)
+  // the block's first visible key
   const int lo_min = window > 0 ? max(0, L - qlen + 1 - window) : 0;
-  // and the keys every column of it sees: [wlo_max, whi_min) (empty when a
-  // column has no query)
-  int whi = bound, wlo = lo, whi_min = valid ? bound : 0, wlo_max = valid ? lo : INT_MAX;
+  // and the keys every column of this wave sees: [wlo_max, whi_min) (empty
+  // when a column has no query)
+  int whi_min = valid ? bound : 0, wlo_max = valid ? lo : INT_MAX;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    whi = max(whi, __shfl_xor(whi, off));
-    wlo = min(wlo, __shfl_xor(wlo, off));
     whi_min = min(whi_min, __shfl_xor(whi_min, off));
     wlo_max = max(wlo_max, __shfl_xor(wlo_max, off));
   }
@@ -118,6 +130,17 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   for (int e = 0; e < NE; ++e) o[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m = -INFINITY, lsum = 0.0f;
 
+  // this thread's share of each tile's loads, and where its four keys of
+  // each of its eight dims go in the transposed value tile (8-byte units):
+  // keys 4 my_keys .. + 3 = 32 a + 16 b + 4 g + 0..3 sit in unit 4 a + g,
+  // half b
+  const int my_unit = tid & 15, my_keys = tid >> 4;
+  int v_store[8];
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd)
+    v_store[dd] = 2 * value_slot(8 * my_unit + dd, 4 * (my_keys >> 3) + (my_keys & 3)) +
+                  ((my_keys >> 2) & 1);
+
   const int B = 1 << log2_block;
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
   const int64_t head_off_v = static_cast<int64_t>(kvh) * B * DV;
@@ -135,111 +158,117 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     // rows of tile t into registers; rows past the chunk repeat its last row,
     // so tiles beyond the last are loaded too (unconditional loads keep the
     // wait counts of the pipeline static) and hit that one row
+    // thread (my_keys, my_unit) moves keys 4 my_keys .. + 3, dims 8 my_unit
+    // .. + 7 of each tile
     auto gload = [&](int t, uint4 (&pk)[PER], uint4 (&pv)[PER]) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const int u = tid + j * NT;
-        const int tok = min(c0 + t * KT + u / DV, c1 - 1);
+        const int tok = min(c0 + t * KT + 4 * my_keys + j, c1 - 1);
         const int64_t idx = static_cast<int64_t>(sm_bt[(tok >> log2_block) - b0]) * blk_stride_v +
-                            head_off_v + (tok & (B - 1)) * DV + u % DV;
+                            head_off_v + (tok & (B - 1)) * DV + my_unit;
         pk[j] = load_cached(kc + idx);  // the sequence's other blocks read these rows too
         pv[j] = load_cached(vc + idx);
       }
     };
     auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int u = tid + j * NT;
-        sk[buf][(u / DV) * ROW + u % DV] = pk[j];
-        sv[buf][(u / DV) * ROW + u % DV] = pv[j];
+      for (int j = 0; j < PER; ++j) sk[buf][(4 * my_keys + j) * ROW + my_unit] = pk[j];
+      // each dim's four keys as one 8-byte piece
+      uint2* vt = reinterpret_cast<uint2*>(sv[buf]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = dword(pv[0], w), x1 = dword(pv[1], w);
+        const uint32_t x2 = dword(pv[2], w), x3 = dword(pv[3], w);
+        vt[v_store[2 * w]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u),
+                                        __builtin_amdgcn_perm(x3, x2, 0x05040100u));
+        vt[v_store[2 * w + 1]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u),
+                                            __builtin_amdgcn_perm(x3, x2, 0x07060302u));
       }
     };
-    auto tile = [&](int t, int buf) {
+    // One tile in two halves: scores and softmax, then the value products.
+    // Between them the pipeline stores the next tile and issues the loads of
+    // a later one, so that their instructions interleave with the MFMAs.
+    // Tiles outside a wave's keys run too (their probabilities are 0).
+    constexpr int NS = KT / 16;
+    auto scores = [&](int t, int buf, uint4 (&phi)[NS / 2], uint4 (&plo)[NS / 2]) {
       const int t0 = c0 + t * KT;
-      if (t0 < whi && t0 + KT > wlo) {
-        // scores of the whole tile first (independent MFMA chains): lane
-        // (col, grp) gets those of keys 16 st + 4 grp + j of its column
-        constexpr int NS = KT / 16;
-        f32x4 sc[NS];
+      // scores of the whole tile first (independent MFMA chains): lane
+      // (col, grp) gets those of keys 16 st + 4 grp + j of its column
+      f32x4 sc[NS];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          sc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int st = 0; st < NS; ++st) {
+        sc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int k = 0; k < NK; ++k)
-            sc[st] = MM::k32(sk[buf][(st * 16 + col) * ROW + k * 4 + grp], qv[k], sc[st]);
-        }
-        // a tile inside every column's keys needs no mask (wave-uniform)
-        if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
-#pragma unroll
-          for (int st = 0; st < NS; ++st)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int tt = t0 + st * 16 + 4 * grp + j;
-              const bool vis = (tt < bound) & (tt >= lo) & (tt < c1);
-              sc[st][j] = vis ? sc[st][j] : -INFINITY;
-            }
-        }
-        float mt = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < NS; ++st)
-          mt = fmaxf(mt, fmaxf(fmaxf(sc[st][0], sc[st][1]), fmaxf(sc[st][2], sc[st][3])));
-        mt = column_max(mt) * scale_log2;
-        // The reference maximum moves only when the tile's maximum exceeds it
-        // by more than 2^8: probabilities stay below 256 and the
-        // accumulators are rescaled only on such rare jumps.
-        const float mref = mt > m + 8.0f ? mt : m;
-        const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
-        const float corr = __builtin_amdgcn_exp2f(m - ms);
-        float p[NS][4];
-        float tsum = 0.0f;
+        for (int k = 0; k < NK; ++k)
+          sc[st] = MM::k32(sk[buf][(st * 16 + col) * ROW + k * 4 + grp], qv[k], sc[st]);
+      }
+      // a tile inside every column's keys needs no mask (wave-uniform)
+      if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[st][j] = __builtin_amdgcn_exp2f(fmaf(sc[st][j], scale_log2, -ms));
-            tsum += p[st][j];
+            const int tt = t0 + st * 16 + 4 * grp + j;
+            const bool vis = (tt < bound) & (tt >= lo) & (tt < c1);
+            sc[st][j] = vis ? sc[st][j] : -INFINITY;
           }
-        lsum = lsum * corr + tsum;
-        if (__any(mref != m)) {
+      }
+      float mt = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < NE; ++e) o[e] *= corr;
+      for (int st = 0; st < NS; ++st)
+        mt = fmaxf(mt, fmaxf(fmaxf(sc[st][0], sc[st][1]), fmaxf(sc[st][2], sc[st][3])));
+      mt = column_max(mt) * scale_log2;
+      // The reference maximum moves only when the tile's maximum exceeds it
+      // by more than 2^8: probabilities stay below 256 and the
+      // accumulators are rescaled only on such rare jumps.
+      const float mref = mt > m + 8.0f ? mt : m;
+      const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
+      const float corr = __builtin_amdgcn_exp2f(m - ms);
+      float p[NS][4];
+      float tsum = 0.0f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[st][j] = __builtin_amdgcn_exp2f(fmaf(sc[st][j], scale_log2, -ms));
+          tsum += p[st][j];
         }
-        m = mref;
-        // value products over pairs of sub-tiles (K = 32 keys per MFMA):
-        // probabilities as a 16-bit head plus its remainder
+      lsum = lsum * corr + tsum;
+      if (__any(mref != m)) {
 #pragma unroll
-        for (int sp = 0; sp < NS; sp += 2) {
-          uint32_t hi[8], rem[8];
+        for (int e = 0; e < NE; ++e) o[e] *= corr;
+      }
+      m = mref;
+      // probabilities in 16 bits for the value products over pairs of
+      // sub-tiles (K = 32 keys per MFMA).  bf16 keeps 8 significant bits, so
+      // its rounding remainder goes into a second product; fp16 rounding
+      // (11 bits) is already at the level of the output's own.
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+      for (int sp = 0; sp < NS; sp += 2) {
+        uint32_t hi[8], rem[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float back, unused;
-              hi[4 * h + j] = MM::round16(p[sp + h][j], back);
-              rem[4 * h + j] = MM::round16(p[sp + h][j] - back, unused);
-            }
-          const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                       hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-          const uint4 plo = make_uint4(rem[0] | (rem[1] << 16), rem[2] | (rem[3] << 16),
-                                       rem[4] | (rem[5] << 16), rem[6] | (rem[7] << 16));
-          // rows 4 grp + u of both sub-tiles, dims 8 col .. 8 col + 7
-          uint4 vr[8];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            vr[u] = sv[buf][((sp + (u >> 2)) * 16 + 4 * grp + (u & 3)) * ROW + col];
-#pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            // dim 8 col + e of the eight keys, in the order of phi
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const int w = e >> 1;
-            uint4 a;
-            a.x = __builtin_amdgcn_perm(dword(vr[1], w), dword(vr[0], w), sel);
-            a.y = __builtin_amdgcn_perm(dword(vr[3], w), dword(vr[2], w), sel);
-            a.z = __builtin_amdgcn_perm(dword(vr[5], w), dword(vr[4], w), sel);
-            a.w = __builtin_amdgcn_perm(dword(vr[7], w), dword(vr[6], w), sel);
-            o[e] = MM::k32(a, phi, o[e]);
-            o[e] = MM::k32(a, plo, o[e]);
+          for (int j = 0; j < 4; ++j) {
+            float back, unused;
+            hi[4 * h + j] = MM::round16(p[sp + h][j], back);
+            rem[4 * h + j] = kSplitP ? MM::round16(p[sp + h][j] - back, unused) : 0u;
           }
+        phi[sp / 2] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                 hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+        plo[sp / 2] = make_uint4(rem[0] | (rem[1] << 16), rem[2] | (rem[3] << 16),
+                                 rem[4] | (rem[5] << 16), rem[6] | (rem[7] << 16));
+      }
+    };
+    auto values = [&](int buf, const uint4 (&phi)[NS / 2], const uint4 (&plo)[NS / 2]) {
+#pragma unroll
+      for (int sp = 0; sp < NS; sp += 2) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          // dim 16 e + col of the eight keys, in the order of phi
+          const uint4 a = sv[buf][value_slot(16 * e + col, 2 * sp + grp)];
+          o[e] = MM::k32(a, phi[sp / 2], o[e]);
+          if constexpr (kSplitP) o[e] = MM::k32(a, plo[sp / 2], o[e]);
         }
       }
     };
@@ -252,16 +281,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     gload(1, ak, av);
     gload(2, bk, bv);
     __syncthreads();
+    uint4 phi[NS / 2], plo[NS / 2];
     for (int t = 0; t < ntiles; t += 2) {
-      tile(t, 0);
+      scores(t, 0, phi, plo);
       lstore(1, ak, av);  // tile t + 1
-      __syncthreads();
       gload(t + 3, ak, av);
-      if (t + 1 >= ntiles) break;
-      tile(t + 1, 1);
-      lstore(0, bk, bv);  // tile t + 2
+      values(0, phi, plo);
       __syncthreads();
+      if (t + 1 >= ntiles) break;
+      scores(t + 1, 1, phi, plo);
+      lstore(0, bk, bv);  // tile t + 2
       gload(t + 4, bk, bv);
+      values(1, phi, plo);
+      __syncthreads();
     }
   }
 
@@ -269,21 +301,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (!valid) return;
-  // lane (col, grp) holds dims 32 grp + 8 j + e of its column: 8 contiguous
-  // dims per j, stored as one 16-byte unit
+  // lane (col, grp) holds dims 16 e + 4 grp + j of its column: four
+  // contiguous dims per e, stored as one 8-byte piece
   uint16_t* dst = static_cast<uint16_t*>(out) +
-                  (static_cast<int64_t>(q0 + qi) * num_heads + h) * D + 32 * grp;
+                  (static_cast<int64_t>(q0 + qi) * num_heads + h) * D + 4 * grp;
+  const float inv = 1.0f / lsum;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int e = 0; e < NE; ++e) {
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < NE; e += 2) {
+    for (int j = 0; j < 4; ++j) {
       float back;
-      const uint32_t a = MM::round16(o[e][j] / lsum, back);
-      const uint32_t b = MM::round16(o[e + 1][j] / lsum, back);
-      w[e / 2] = a | (b << 16);
+      w[j] = MM::round16(o[e][j] * inv, back);
     }
-    *reinterpret_cast<uint4*>(dst + 8 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint2*>(dst + 16 * e) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
   }
 }
 
