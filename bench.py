@@ -31,8 +31,10 @@ HBM_PEAK_GBPS = 8000.0
 MATRIX_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "llama7b_fp16"
 CSRC = os.path.join(REPO, "paged_kv_cache_123_amd", "csrc")
+# the attention kernels' sources and the build script that sets their flags
 ATTN_SRCS = [os.path.join(CSRC, f) for f in ("attention_kernels.hip", "attention_mfma.hip",
-                                             "attention_prefill.hip", "decode_common.h")]
+                                             "attention_prefill.hip", "decode_common.h")] + [
+    os.path.join(REPO, "paged_kv_cache_123_amd", "build.py")]
 
 
 def attention_source_hash() -> str:
@@ -725,7 +727,8 @@ def main():
             "kernel": ("prefill_kernel (query blocks)" if step.prefill_rows else
                        "cascade_decode_kernel" if cascade and not part else
                        "paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
-                           args.kernel == "auto" and w.num_heads > w.num_kv_heads))
+                           args.kernel == "auto" and w.dtype != "f32" and w.head_size == 128
+                           and (w.num_heads > w.num_kv_heads or step.attn_max_query_len > 1)))
                        else "paged_decode_kernel")
                       + (" + merge_kernel" if part else "")
                       + (" (cascade plan)" if cascade else "")
