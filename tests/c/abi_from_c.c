@@ -50,6 +50,16 @@ int main(void) {
   uint8_t key[32];
   CHECK(pa_block_keys(toks, 4, 4, NULL, 0, key) == PA_OK);
   CHECK(strcmp(pa_status_string(PA_ENOMEM), "") != 0);
+
+  /* a prefill chunk cut into the prefill kernel's query blocks */
+  const int32_t qlens[2] = {100, 30};
+  const int32_t qsl[3] = {0, 70, 80};
+  int32_t tokens = 0, rseq[8], rlen[8], rqsl[9];
+  int64_t rows = 0;
+  CHECK(pa_prefill_block_tokens(32, 8, &tokens) == PA_OK && tokens == 16);
+  CHECK(pa_query_blocks(qlens, qsl, 2, tokens, rseq, rlen, rqsl, 8, &rows) == PA_OK && rows == 6);
+  CHECK(rlen[0] == 46 && rlen[4] == 100 && rseq[4] == 0 && rseq[5] == 1 && rlen[5] == 30);
+  CHECK(rqsl[4] == 64 && rqsl[5] == 70 && rqsl[6] == 80);
   printf("abi_from_c ok %s\n", pa_version());
   return 0;
 }

@@ -37,6 +37,9 @@ CASES = [
     ("bf16", 128, 32, 2, [2500, 96], [96, 96], 0, 1000),
     ("bf16", 128, 1, 1, [150, 65], [130, 65], 0, 0),
     ("f16", 128, 128, 8, [1000, 300], [300, 64], 0, 0),
+    # a window whose start falls inside a table chunk; whole prompts as one chunk
+    ("bf16", 128, 16, 4, [5000, 700], [300, 700], 0, 2500),
+    ("f16", 128, 32, 2, [640, 64], [640, 64], 0, 0),
 ]
 
 
