@@ -71,20 +71,31 @@ class PagedKVCache:
 
     # ---- one step ---------------------------------------------------------
     def step(self, seqs, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
-             new_tokens, scale: float) -> torch.Tensor:
+             new_tokens, scale: float, all_queries: bool = False) -> torch.Tensor:
         """Append new_tokens[i] tokens to seqs[i] (their K/V rows are the
         consecutive rows of ``key`` / ``value``, [T, num_kv_heads, head_size])
         and attend with query[i] ([S, num_heads, head_size], the last new
-        token of each sequence).  Returns out [S, num_heads, head_size]."""
+        token of each sequence).  Returns out [S, num_heads, head_size].
+
+        ``all_queries``: every new token is a query (query/out [T, num_heads,
+        head_size] in the order of ``key``), causal over its sequence's new
+        tokens: speculative drafts, or prompts and prefill chunks.  A sequence
+        with more new tokens than one workgroup holds as query vectors is
+        attended as query blocks after the step's cache writes (separate
+        launches; the prefill kernel with 16-bit storage, head_size 128 and
+        no partitions)."""
         seqs = [int(s) for s in seqs]
         n = [int(x) for x in new_tokens]
-        if len(n) != len(seqs) or query.shape[0] != len(seqs):
-            raise ValueError("one query and one new-token count per sequence")
         T = sum(n)
+        if len(n) != len(seqs) or query.shape[0] != (T if all_queries else len(seqs)):
+            raise ValueError("one query per sequence, or per new token with all_queries, and "
+                             "one new-token count per sequence")
+        if all_queries and self.cascade:
+            raise ValueError("cascade plans take one query per sequence")
         if key.shape[0] != T or value.shape[0] != T:
             raise ValueError("key/value must hold the new tokens of every sequence in order")
         # host: release what the window left behind, then allocate
-        qsl, cow_src = [0], []
+        qsl, cow_src, cow_pairs, positions = [0], [], [], []
         for s, k in zip(seqs, n):
             if k < 1:
                 raise ValueError("every sequence of a step appends at least one token")
@@ -94,6 +105,9 @@ class PagedKVCache:
             _, pair = self.pool.append(s, k)
             qsl.append(qsl[-1] + k)
             cow_src.append(-1 if pair is None else pair[0])
+            if pair is not None:
+                cow_pairs.append(pair)
+            positions.extend(range(start, start + k))
         width = max(self.pool.seq_num_blocks(s) for s in seqs)
         tables, lens = self.pool.block_tables(seqs, width)
         shared = self.pool.shared_prefix_blocks(seqs)
@@ -102,19 +116,32 @@ class PagedKVCache:
         first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
         groups = np.where(shared > 0, first, self.num_blocks + np.arange(len(seqs)))
         widest = 0  # members of the widest cascade group of the step
+        if all_queries:
+            H, D = query.shape[1], query.shape[2]
+            G = H // self.num_kv_heads
+            matrix = self.dtype != torch.float32 and D == 128
+            if max(n) * G > (16 if matrix else 8):  # more than one workgroup's query vectors
+                out = self._query_blocks(query, key, value, tables, lens, qsl, cow_pairs,
+                                         positions, scale, shared, matrix)
+                self.last_tables, self.last_lens, self.last_group = tables, lens, 0
+                return out
         if self.cascade:
             plan, num_items, widest = ops.decode_plan_cascade(
                 tables, lens, self.block_size, self.partition_size, self.cascade, n)
         else:
-            plan = ops.decode_plan(lens, self.partition_size, self.sliding_window, None, groups)
+            plan = ops.decode_plan(lens, self.partition_size, self.sliding_window,
+                                   n if all_queries else None, groups)
         t = {name: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for name, a in (
             ("tables", tables), ("lens", lens), ("qsl", np.asarray(qsl, dtype=np.int32)),
             ("cow_src", np.asarray(cow_src, dtype=np.int64)), ("plan", plan))}
         out = torch.empty_like(query)
         workspace = None
         if self.partition_size:
-            workspace = ops.alloc_split_workspace(len(seqs), query.shape[1], self.head_size,
-                                                  int(lens.max()), self.partition_size, dev)
+            # the one-launch step sizes multi-query rows as num_seqs x max_query_len
+            rows = len(seqs) * max(n) if all_queries else len(seqs)
+            workspace = ops.alloc_split_workspace(max(rows, query.shape[0]), query.shape[1],
+                                                  self.head_size, int(lens.max()),
+                                                  self.partition_size, dev)
         shared_dev = torch.from_numpy(shared).to(dev) if shared.any() else None
         if self.cascade:
             ops.decode_step_cascade(out, query, self.key_cache, self.value_cache, t["tables"],
@@ -124,7 +151,57 @@ class PagedKVCache:
         else:
             ops.decode_step(out, query, self.key_cache, self.value_cache, t["tables"],
                             t["lens"], scale, int(lens.max()), self.partition_size, t["plan"],
-                            t["qsl"], key, value, t["cow_src"], None, workspace, shared_dev, 0,
-                            self.sliding_window)
+                            t["qsl"], key, value, t["cow_src"], None, workspace, shared_dev,
+                            max(n) if all_queries else 0, self.sliding_window)
         self.last_tables, self.last_lens, self.last_group = tables, lens, widest
+        return out
+
+    def _query_blocks(self, query, key, value, tables, lens, qsl, cow_pairs, positions, scale,
+                      shared, matrix):
+        """A step whose sequences bring more new tokens than a workgroup holds:
+        the cache writes (copy-on-write, slot mapping, scatter) first, then the
+        attention over query blocks (pa_query_blocks)."""
+        dev = self.device
+        T = len(positions)
+        tab = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+        qsl_host = np.asarray(qsl, dtype=np.int32)
+        if cow_pairs:
+            ops.copy_blocks(self.key_cache, self.value_cache,
+                            torch.tensor(cow_pairs, dtype=torch.int64, device=dev))
+        slots = torch.empty(T, dtype=torch.int64, device=dev)
+        ops.compute_slot_mapping(torch.from_numpy(qsl_host).to(dev),
+                                 torch.tensor(positions, dtype=torch.int64, device=dev), tab,
+                                 self.block_size, slots, T)
+        ops.reshape_and_cache(key, value, self.key_cache, self.value_cache, slots)
+        out = torch.empty_like(query)
+        H = query.shape[1]
+        max_len = int(lens.max())
+        if matrix and not self.partition_size:
+            row_seq, row_lens, row_qsl = ops.query_blocks(
+                lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
+            ops.paged_attention_prefill(out, query, self.key_cache, self.value_cache, tab,
+                                        torch.from_numpy(row_seq).to(dev),
+                                        torch.from_numpy(row_lens).to(dev),
+                                        torch.from_numpy(row_qsl).to(dev), scale, max_len,
+                                        None, self.sliding_window)
+            return out
+        block = (16 if matrix else 8) // (H // self.num_kv_heads)
+        row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl_host, block)
+        rows_per_seq = np.bincount(row_seq, minlength=len(lens))
+        # a sequence cut into several rows has all of its blocks read by each
+        row_shared = np.where(rows_per_seq[row_seq] > 1, -(-row_lens // self.block_size),
+                              shared[row_seq]).astype(np.int32)
+        plan = ops.decode_plan(row_lens, self.partition_size, self.sliding_window,
+                               np.diff(row_qsl), row_seq)
+        workspace = None
+        if self.partition_size:
+            workspace = ops.alloc_split_workspace(T, H, self.head_size, max_len,
+                                                  self.partition_size, dev)
+        ops.paged_attention_multi(out, query, self.key_cache, self.value_cache,
+                                  torch.from_numpy(np.ascontiguousarray(tables[row_seq])).to(dev),
+                                  torch.from_numpy(row_lens).to(dev),
+                                  torch.from_numpy(row_qsl).to(dev), int(np.diff(row_qsl).max()),
+                                  scale, max_len, self.partition_size,
+                                  torch.from_numpy(plan).to(dev), workspace,
+                                  torch.from_numpy(row_shared).to(dev), self.sliding_window)
         return out

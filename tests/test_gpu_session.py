@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle.allocator import OraclePool
-from oracle.attention import paged_attention
+from oracle.attention import paged_attention, paged_attention_multi
 from oracle.cache_ops import copy_blocks, reshape_and_cache
 from oracle_side import to_host
 from test_gpu_parity import _require_gpu, check_attention
@@ -109,3 +109,71 @@ def test_many_steps_against_the_oracle(dtype, B, G, window, part, cascade):
     assert cache.pool.num_free() == pool.num_free()
     if cascade:
         assert max(widest) >= 2, "forks sharing full blocks should form cascade groups"
+
+
+@pytest.mark.parametrize("dtype,B,G,window,part", [
+    ("f16", 16, 1, 0, 0), ("bf16", 16, 4, 0, 0), ("bf16", 8, 2, 40, 0), ("f32", 8, 2, 0, 0),
+    ("f16", 16, 2, 0, 32),
+])
+def test_every_new_token_a_query_over_many_steps(dtype, B, G, window, part):
+    """Prompts and prefill chunks with every new token a query (query blocks,
+    on the prefill kernel where it applies), speculative drafts (one launch)
+    and plain decodes on one cache, with a fork whose tail is copied inside a
+    prefill step; each step against the oracle."""
+    _require_gpu()
+    from paged_kv_cache_123_amd.session import PagedKVCache
+    hkv, D, nb = 2, 128, 160
+    H = hkv * G
+    rng = np.random.default_rng(B + G + window + part)
+    order = rng.permutation(nb)
+    cache = PagedKVCache(nb, B, hkv, D, dtype, DEV, free_order=order, sliding_window=window,
+                         partition_size=part)
+    pool = OraclePool(nb, B, order)
+    kc = to_host(cache.key_cache).copy()
+    vc = to_host(cache.value_cache).copy()
+    gen = torch.Generator().manual_seed(11)
+    scale = 1.0 / np.sqrt(D)
+
+    def run_step(seqs, counts, all_queries, label):
+        print(f"[session] {label} {dtype} B={B} G={G} W={window} P={part}", flush=True)
+        T = sum(counts)
+        q = _draw(gen, (T if all_queries else len(seqs), H, D), dtype)
+        k = _draw(gen, (T, hkv, D), dtype)
+        v = _draw(gen, (T, hkv, D), dtype)
+        out = cache.step(seqs, q.to(DEV), k.to(DEV), v.to(DEV), counts, scale,
+                         all_queries=all_queries)
+        torch.cuda.synchronize()
+        slots, pairs = [], []
+        for s, n in zip(seqs, counts):
+            pool.remove_skipped(s, pool.seq_len(s), window)
+            sl, cow = pool.append(s, n)
+            slots += sl
+            pairs += cow
+        copy_blocks(kc, vc, pairs)
+        reshape_and_cache(kc, vc, to_host(k), to_host(v), slots, B)
+        tables = [[-1 if b is None else b for b in pool.block_table(s)] for s in seqs]
+        width = max(len(t) for t in tables)
+        tables = np.array([t + [-1] * (width - len(t)) for t in tables])
+        lens = [pool.seq_len(s) for s in seqs]
+        assert np.array_equal(cache.last_tables, tables), label
+        if all_queries:
+            qsl = np.concatenate([[0], np.cumsum(counts)])
+            want = paged_attention_multi(to_host(q), kc, vc, tables, lens, qsl, scale, dtype,
+                                         window=window)
+        else:
+            want = paged_attention(to_host(q), kc, vc, tables, lens, scale, dtype,
+                                   window=window)
+        check_attention(to_host(out), want, dtype, label)
+
+    for s in range(3):
+        cache.add(s)
+        pool.add_seq(s)
+    run_step([0, 1, 2], [150, 70, 5], True, "prompts as prefill")
+    run_step([0, 1, 2], [1, 1, 1], False, "decode")
+    cache.fork(0, 3)
+    pool.fork(0, 3)
+    run_step([0, 1, 2, 3], [4, 2, 3, 4], True, "drafts")
+    run_step([0, 1, 2, 3], [100, 1, 40, 20], True, "prefill chunks")
+    run_step([0, 1, 2, 3], [1, 1, 1, 1], False, "decode after the chunks")
+    pool.check_invariants()
+    assert cache.pool.num_free() == pool.num_free()
