@@ -501,6 +501,40 @@ int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key
                                    void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_prefill_step: pa_paged_attention_prefill with the step's cache writes
+ * in the same launch (the prefill counterpart of pa_decode_step): the
+ * copy-on-write of the old slots of each fresh tail block, the new tokens'
+ * K/V rows into their slots, and their slots into slot_mapping.  The
+ * attention reads keys from a sequence's first new position on from the
+ * key/value rows and the old slots of a copied tail from its source block,
+ * so no workgroup reads a slot the launch writes, and the result is that of
+ * the separate calls (copy_blocks, compute_slot_mapping, reshape_and_cache,
+ * pa_paged_attention_prefill), bit for bit.
+ *   query_start_loc  device int32 [num_seqs + 1]: sequence s's new tokens are
+ *                    the rows query_start_loc[s] .. [s + 1] - 1 of query, key
+ *                    and value; row_seq indexes these sequences and row_qsl
+ *                    the same token rows
+ *   key, value       device [num_tokens][...], rows key_stride / value_stride
+ *                    elements apart (>= num_kv_heads * head_size, 16-byte
+ *                    aligned), head kvh at kvh * head_size
+ *   cow_src          device int64 [num_seqs]: the block whose first slots
+ *                    sequence s's last block copies, or -1; NULL = none
+ *   slot_mapping     device int64 [num_tokens] output, or NULL
+ * block_tables must hold each sequence's blocks after the step's
+ * allocation.  Errors: those of pa_paged_attention_prefill, plus PA_EINVAL
+ * for a NULL query_start_loc, key or value and misaligned rows or strides.
+ * ---------------------------------------------------------------------- */
+int32_t pa_prefill_step(void* out, const void* query, void* key_cache, void* value_cache,
+                        const int32_t* block_tables, int64_t bt_stride, const int32_t* row_seq,
+                        const int32_t* row_lens, const int32_t* row_qsl, int32_t num_rows,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                        int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+                        const int32_t* work_items, int32_t sliding_window,
+                        const int32_t* query_start_loc, const void* key, const void* value,
+                        int64_t key_stride, int64_t value_stride, const int64_t* cow_src,
+                        int64_t* slot_mapping, void* stream);
+
+/* ------------------------------------------------------------------------
  * Attention alone over a cascade plan (pa_decode_plan_cascade), on caches that
  * already hold the step's rows: pa_paged_attention_decode_planned's
  * arguments, with the plan (device int32, whole: items and group section),

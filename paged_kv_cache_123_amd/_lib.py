@@ -67,6 +67,9 @@ SIGNATURES = {
     "pa_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,
                                           _vp]),
+    "pa_prefill_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32,
+                               _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _vp, _vp, _i64,
+                               _i64, _vp, _vp, _vp]),
     "pa_paged_attention_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _f32, _i32, _i32, _vp, _i64, _i32,
                                           _vp, _sz, _vp]),

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_lens,
     const int32_t* __restrict__ row_qsl, const int32_t* __restrict__ work_items,
     int32_t num_rows, int32_t num_heads, int32_t num_kv_heads, int32_t log2_block,
-    int32_t log2_group, float scale_log2, int32_t window) {
+    int32_t log2_group, float scale_log2, int32_t window, AppendArgs ap) {
   constexpr int NW = kPrefillWaves;
   constexpr int NT = NW * 64;
   constexpr int D = 128;
@@ -148,6 +148,30 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   const uint4* kc = static_cast<const uint4*>(key_cache);
   const uint4* vc = static_cast<const uint4*>(value_cache);
 
+  // The step's cache writes, in the same launch: no workgroup reads a slot
+  // written here.  Keys from the sequence's first new position p0 on come
+  // from the step's key/value rows, the old slots of a copied tail block
+  // from its source block.  Each row stores the rows of its own tokens as
+  // its tiles load them (and, for KV head 0, their slots); the sequence's
+  // first row copies the old slots here.
+  int p0 = INT_MAX, seq_q0 = 0, special = INT_MAX;
+  int64_t cow = -1;
+  if (ap.qsl) {
+    seq_q0 = ap.qsl[s];
+    p0 = L - qlen - (q0 - seq_q0);
+    cow = ap.cow_src ? ap.cow_src[s] : -1;
+    special = cow >= 0 ? (p0 >> log2_block) << log2_block : p0;  // first key read elsewhere
+    if (cow >= 0 && q0 == seq_q0) {
+      const int jb = p0 >> log2_block;
+      const int64_t from = cow * blk_stride_v + head_off_v;
+      const int64_t to = static_cast<int64_t>(bt_row[jb]) * blk_stride_v + head_off_v;
+      for (int i = tid; i < (p0 - (jb << log2_block)) * DV; i += NT) {
+        ap.key_cache[to + i] = ap.key_cache[from + i];
+        ap.value_cache[to + i] = ap.value_cache[from + i];
+      }
+    }
+  }
+
   for (int c0 = lo_min; c0 < L; c0 += kChunkTokens) {
     const int c1 = min(c0 + kChunkTokens, L);
     const int b0 = c0 >> log2_block;
@@ -164,15 +188,41 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int tok = min(c0 + t * KT + 4 * my_keys + j, c1 - 1);
-        const int64_t idx = static_cast<int64_t>(sm_bt[(tok >> log2_block) - b0]) * blk_stride_v +
-                            head_off_v + (tok & (B - 1)) * DV + my_unit;
-        pk[j] = load_cached(kc + idx);  // the sequence's other blocks read these rows too
-        pv[j] = load_cached(vc + idx);
+        const uint4 *ks, *vs;
+        if (tok < special) {  // the sequence's other blocks read these rows too: cached loads
+          const int64_t idx = static_cast<int64_t>(sm_bt[(tok >> log2_block) - b0]) *
+                              blk_stride_v + head_off_v + (tok & (B - 1)) * DV;
+          ks = kc + idx;
+          vs = vc + idx;
+        } else if (tok >= p0) {  // a new row of the step
+          ks = ap.key + (seq_q0 + tok - p0) * ap.key_stride_v + kvh * DV;
+          vs = ap.value + (seq_q0 + tok - p0) * ap.value_stride_v + kvh * DV;
+        } else {  // an old slot of the copied tail block
+          const int64_t idx = cow * blk_stride_v + head_off_v + (tok & (B - 1)) * DV;
+          ks = kc + idx;
+          vs = vc + idx;
+        }
+        pk[j] = load_cached(ks + my_unit);
+        pv[j] = load_cached(vs + my_unit);
       }
     };
-    auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
+    auto lstore = [&](int t, int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) sk[buf][(4 * my_keys + j) * ROW + my_unit] = pk[j];
+      if (ap.qsl) {  // this row's own tokens go to their cache slots
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int tok = c0 + t * KT + 4 * my_keys + j;
+          if (tok >= L - qlen && tok < c1) {
+            const int64_t phys = sm_bt[(tok >> log2_block) - b0];
+            const int64_t dst = phys * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + my_unit;
+            ap.key_cache[dst] = pk[j];
+            ap.value_cache[dst] = pv[j];
+            if (ap.slot_mapping && kvh == 0 && my_unit == 0)
+              ap.slot_mapping[q0 + tok - (L - qlen)] = phys * B + (tok & (B - 1));
+          }
+        }
+      }
       // each dim's four keys as one 8-byte piece
       uint2* vt = reinterpret_cast<uint2*>(sv[buf]);
 #pragma unroll
@@ -277,20 +327,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     // one is computed
     uint4 ak[PER], av[PER], bk[PER], bv[PER];
     gload(0, ak, av);
-    lstore(0, ak, av);
+    lstore(0, 0, ak, av);
     gload(1, ak, av);
     gload(2, bk, bv);
     __syncthreads();
     uint4 phi[NS / 2], plo[NS / 2];
     for (int t = 0; t < ntiles; t += 2) {
       scores(t, 0, phi, plo);
-      lstore(1, ak, av);  // tile t + 1
+      lstore(t + 1, 1, ak, av);
       gload(t + 3, ak, av);
       values(0, phi, plo);
       __syncthreads();
       if (t + 1 >= ntiles) break;
       scores(t + 1, 1, phi, plo);
-      lstore(0, bk, bv);  // tile t + 2
+      lstore(t + 2, 0, bk, bv);
       gload(t + 4, bk, bv);
       values(1, phi, plo);
       __syncthreads();
@@ -333,12 +383,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(prefill_kernel<PA_BF16>, grid, dim3(kPrefillWaves * 64), 0, stream, a.out,
                        a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
                        a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,
-                       a.num_kv_heads, log2_block, log2_group, sl2, a.window);
+                       a.num_kv_heads, log2_block, log2_group, sl2, a.window, a.append);
   else
     hipLaunchKernelGGL(prefill_kernel<PA_F16>, grid, dim3(kPrefillWaves * 64), 0, stream, a.out,
                        a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
                        a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,
-                       a.num_kv_heads, log2_block, log2_group, sl2, a.window);
+                       a.num_kv_heads, log2_block, log2_group, sl2, a.window, a.append);
   return hipGetLastError();
 }
 

@@ -620,6 +620,25 @@ int32_t pa_prefill_block_tokens(int32_t num_heads, int32_t num_kv_heads, int32_t
   return PA_OK;
 }
 
+// Shared checks of the prefill entry points; fills the launch arguments.
+static int32_t check_prefill(const char* who, pa::PrefillArgs& a, int64_t bt_stride,
+                             int32_t head_size, int32_t max_context_len) {
+  const std::string w(who);
+  if (a.window < 0) return fail(PA_EINVAL, (w + ": sliding_window < 0").c_str());
+  int32_t st = check_decode(who, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
+                            bt_stride, a.row_lens, a.num_rows, a.num_heads, a.num_kv_heads,
+                            head_size, a.block_size, max_context_len, a.dtype);
+  if (st != PA_OK) return st;
+  if (!a.row_seq || !a.row_qsl) return fail(PA_EINVAL, (w + ": NULL row arrays").c_str());
+  if (!(a.scale > 0.0f) || !std::isfinite(a.scale))
+    return fail(PA_EINVAL, (w + ": scale must be positive and finite").c_str());
+  if ((a.dtype != PA_F16 && a.dtype != PA_BF16) || head_size != 128)
+    return fail(PA_EINVAL, (w + ": needs 16-bit storage and head_size 128").c_str());
+  if (static_cast<int64_t>(a.num_rows) * a.num_kv_heads > 0x7fffffff)
+    return fail(PA_EINVAL, (w + ": too many rows").c_str());
+  return PA_OK;
+}
+
 int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key_cache,
                                    const void* value_cache, const int32_t* block_tables,
                                    int64_t bt_stride, const int32_t* row_seq,
@@ -630,22 +649,41 @@ int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key
                                    const int32_t* work_items, int32_t sliding_window,
                                    void* stream) {
   const char* who = "pa_paged_attention_prefill";
-  if (sliding_window < 0) return fail(PA_EINVAL, "pa_paged_attention_prefill: sliding_window < 0");
-  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
-                            row_lens, num_rows, num_heads, num_kv_heads, head_size, block_size,
-                            max_context_len, dtype);
-  if (st != PA_OK) return st;
-  if (!row_seq || !row_qsl) return fail(PA_EINVAL, "pa_paged_attention_prefill: NULL row arrays");
-  if (!(scale > 0.0f) || !std::isfinite(scale))
-    return fail(PA_EINVAL, "pa_paged_attention_prefill: scale must be positive and finite");
-  if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
-    return fail(PA_EINVAL,
-                "pa_paged_attention_prefill: needs 16-bit storage and head_size 128");
-  if (static_cast<int64_t>(num_rows) * num_kv_heads > 0x7fffffff)
-    return fail(PA_EINVAL, "pa_paged_attention_prefill: too many rows");
   pa::PrefillArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, row_seq,
                     row_lens, row_qsl, work_items, num_rows, num_heads, num_kv_heads,
                     block_size, scale, dtype, sliding_window};
+  const int32_t st = check_prefill(who, a, bt_stride, head_size, max_context_len);
+  if (st != PA_OK) return st;
+  return launched(pa::launch_prefill(a, static_cast<hipStream_t>(stream)), who);
+}
+
+int32_t pa_prefill_step(void* out, const void* query, void* key_cache, void* value_cache,
+                        const int32_t* block_tables, int64_t bt_stride, const int32_t* row_seq,
+                        const int32_t* row_lens, const int32_t* row_qsl, int32_t num_rows,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                        int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+                        const int32_t* work_items, int32_t sliding_window,
+                        const int32_t* query_start_loc, const void* key, const void* value,
+                        int64_t key_stride, int64_t value_stride, const int64_t* cow_src,
+                        int64_t* slot_mapping, void* stream) {
+  const char* who = "pa_prefill_step";
+  pa::PrefillArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, row_seq,
+                    row_lens, row_qsl, work_items, num_rows, num_heads, num_kv_heads,
+                    block_size, scale, dtype, sliding_window};
+  int32_t st = check_prefill(who, a, bt_stride, head_size, max_context_len);
+  if (st != PA_OK) return st;
+  if (!query_start_loc || !key || !value)
+    return fail(PA_EINVAL, "pa_prefill_step: NULL query_start_loc, key or value");
+  const int32_t eb = elem_bytes(dtype);
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_size;
+  if (key_stride < row || value_stride < row || (key_stride * eb) % 16 != 0 ||
+      (value_stride * eb) % 16 != 0 || !aligned16(key) || !aligned16(value))
+    return fail(PA_EINVAL, "pa_prefill_step: key/value rows must be 16-byte aligned with a "
+                           "stride of at least num_kv_heads * head_size elements");
+  a.append = pa::dev::AppendArgs{query_start_loc, cow_src, static_cast<const uint4*>(key),
+                                 static_cast<const uint4*>(value), key_stride * eb / 16,
+                                 value_stride * eb / 16, static_cast<uint4*>(key_cache),
+                                 static_cast<uint4*>(value_cache), slot_mapping};
   return launched(pa::launch_prefill(a, static_cast<hipStream_t>(stream)), who);
 }
 

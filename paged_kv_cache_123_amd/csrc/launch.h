@@ -99,6 +99,7 @@ struct PrefillArgs {
   float scale;
   int32_t dtype;
   int32_t window;
+  dev::AppendArgs append{};  // the step's cache writes (append.qsl == nullptr: none)
 };
 int prefill_block_tokens(int group);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -675,6 +675,71 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: t
         _dtype(key_cache), items or None, sliding_window, _stream()))
 
 
+def prepare_prefill_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, block_tables: torch.Tensor,
+                         row_seq: torch.Tensor, row_lens: torch.Tensor, row_qsl: torch.Tensor,
+                         scale: float, max_context_len: int, query_start_loc: torch.Tensor,
+                         key: torch.Tensor, value: torch.Tensor, cow_src=None,
+                         slot_mapping=None, work_items=None, sliding_window: int = 0):
+    """Check and marshal a pa_prefill_step call (prefill attention over query
+    blocks with the step's copy-on-write and scatter in the same launch);
+    launch it with launch_prepared."""
+    _dev(out, query, key_cache, value_cache, block_tables, row_seq, row_lens, row_qsl,
+         query_start_loc, key, value)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if query.dim() != 3 or query.shape[2] != D or out.shape != query.shape:
+        raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+    for n, t in (("query", query), ("out", out), ("key", key), ("value", value)):
+        if t.dtype != key_cache.dtype:
+            raise TypeError(f"{n} must have the cache dtype")
+    for n, t in (("query", query), ("out", out), ("block_tables", block_tables),
+                 ("row_seq", row_seq), ("row_lens", row_lens), ("row_qsl", row_qsl),
+                 ("query_start_loc", query_start_loc)):
+        _contig(n, t)
+    R = row_seq.numel()
+    for n, t, size in (("row_seq", row_seq, R), ("row_lens", row_lens, R),
+                       ("row_qsl", row_qsl, R + 1),
+                       ("query_start_loc", query_start_loc, block_tables.shape[0] + 1)):
+        if t.dtype != torch.int32 or t.numel() != size:
+            raise ValueError(f"{n} must be int32 with {size} entries")
+    T = query.shape[0]
+    if key.shape != (T, hkv, D) or value.shape != (T, hkv, D):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_size]")
+    if key.stride(1) != D or key.stride(2) != 1 or value.stride(1) != D or value.stride(2) != 1:
+        raise ValueError("key/value rows must be dense [num_kv_heads, head_size]")
+    cow = 0
+    if cow_src is not None:
+        _dev(cow_src)
+        if cow_src.dtype != torch.int64 or cow_src.numel() != block_tables.shape[0]:
+            raise ValueError("cow_src must be int64 [num_seqs]")
+        cow = cow_src.data_ptr()
+    slots = 0
+    if slot_mapping is not None:
+        _dev(slot_mapping)
+        if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < T:
+            raise ValueError("slot_mapping must be int64 [num_tokens]")
+        slots = slot_mapping.data_ptr()
+    items = 0
+    if work_items is not None:
+        _dev(work_items)
+        _contig("work_items", work_items)
+        if work_items.dtype != torch.int32 or work_items.shape != (R, 2):
+            raise ValueError("work_items must be int32 [num_rows, 2]")
+        items = work_items.data_ptr()
+    return lib().pa_prefill_step, (
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), row_seq.data_ptr(), row_lens.data_ptr(),
+        row_qsl.data_ptr(), R, query.shape[1], hkv, D, B, max_context_len, scale,
+        _dtype(key_cache), items or None, sliding_window, query_start_loc.data_ptr(),
+        key.data_ptr(), value.data_ptr(), key.stride(0), value.stride(0), cow or None,
+        slots or None)
+
+
+def prefill_step(*args, **kw) -> None:
+    """pa_prefill_step on the current stream (arguments as prepare_prefill_step)."""
+    launch_prepared(prepare_prefill_step(*args, **kw))
+
+
 def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                           value_cache: torch.Tensor, block_tables: torch.Tensor,
                           context_lens: torch.Tensor, query_start_loc: torch.Tensor,

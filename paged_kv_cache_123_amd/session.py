@@ -81,9 +81,9 @@ class PagedKVCache:
         head_size] in the order of ``key``), causal over its sequence's new
         tokens: speculative drafts, or prompts and prefill chunks.  A sequence
         with more new tokens than one workgroup holds as query vectors is
-        attended as query blocks after the step's cache writes (separate
-        launches; the prefill kernel with 16-bit storage, head_size 128 and
-        no partitions)."""
+        attended as query blocks: in one launch on the prefill kernel (16-bit
+        storage, head_size 128, no partitions), else after the step's cache
+        writes on the decode kernels."""
         seqs = [int(s) for s in seqs]
         n = [int(x) for x in new_tokens]
         T = sum(n)
@@ -121,8 +121,8 @@ class PagedKVCache:
             G = H // self.num_kv_heads
             matrix = self.dtype != torch.float32 and D == 128
             if max(n) * G > (16 if matrix else 8):  # more than one workgroup's query vectors
-                out = self._query_blocks(query, key, value, tables, lens, qsl, cow_pairs,
-                                         positions, scale, shared, matrix)
+                out = self._query_blocks(query, key, value, tables, lens, qsl, cow_src,
+                                         cow_pairs, positions, scale, shared, matrix)
                 self.last_tables, self.last_lens, self.last_group = tables, lens, 0
                 return out
         if self.cascade:
@@ -156,15 +156,29 @@ class PagedKVCache:
         self.last_tables, self.last_lens, self.last_group = tables, lens, widest
         return out
 
-    def _query_blocks(self, query, key, value, tables, lens, qsl, cow_pairs, positions, scale,
-                      shared, matrix):
-        """A step whose sequences bring more new tokens than a workgroup holds:
-        the cache writes (copy-on-write, slot mapping, scatter) first, then the
-        attention over query blocks (pa_query_blocks)."""
+    def _query_blocks(self, query, key, value, tables, lens, qsl, cow_src, cow_pairs, positions,
+                      scale, shared, matrix):
+        """A step whose sequences bring more new tokens than a workgroup holds,
+        attended over query blocks (pa_query_blocks): on the prefill kernel
+        with the cache writes in the same launch (pa_prefill_step), else the
+        cache writes (copy-on-write, slot mapping, scatter) first."""
         dev = self.device
         T = len(positions)
         tab = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
         qsl_host = np.asarray(qsl, dtype=np.int32)
+        out = torch.empty_like(query)
+        H = query.shape[1]
+        max_len = int(lens.max())
+        if matrix and not self.partition_size:
+            row_seq, row_lens, row_qsl = ops.query_blocks(
+                lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
+            ops.prefill_step(out, query, self.key_cache, self.value_cache, tab,
+                             torch.from_numpy(row_seq).to(dev), torch.from_numpy(row_lens).to(dev),
+                             torch.from_numpy(row_qsl).to(dev), scale, max_len,
+                             torch.from_numpy(qsl_host).to(dev), key, value,
+                             torch.tensor(cow_src, dtype=torch.int64, device=dev), None, None,
+                             self.sliding_window)
+            return out
         if cow_pairs:
             ops.copy_blocks(self.key_cache, self.value_cache,
                             torch.tensor(cow_pairs, dtype=torch.int64, device=dev))
@@ -173,18 +187,6 @@ class PagedKVCache:
                                  torch.tensor(positions, dtype=torch.int64, device=dev), tab,
                                  self.block_size, slots, T)
         ops.reshape_and_cache(key, value, self.key_cache, self.value_cache, slots)
-        out = torch.empty_like(query)
-        H = query.shape[1]
-        max_len = int(lens.max())
-        if matrix and not self.partition_size:
-            row_seq, row_lens, row_qsl = ops.query_blocks(
-                lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
-            ops.paged_attention_prefill(out, query, self.key_cache, self.value_cache, tab,
-                                        torch.from_numpy(row_seq).to(dev),
-                                        torch.from_numpy(row_lens).to(dev),
-                                        torch.from_numpy(row_qsl).to(dev), scale, max_len,
-                                        None, self.sliding_window)
-            return out
         block = (16 if matrix else 8) // (H // self.num_kv_heads)
         row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl_host, block)
         rows_per_seq = np.bincount(row_seq, minlength=len(lens))

@@ -81,11 +81,12 @@ class DecodeStep:
     every new token is a query (query/out [num_tokens, H, D], causal over each
     sequence's new tokens) instead of one query per sequence; a sequence with
     more new tokens than one workgroup holds as query vectors (a prefill
-    chunk) is attended as several query blocks (pa_query_blocks), after the
-    step's cache writes (the step then runs as separate launches); with
-    16-bit storage, head_size 128 and no partitions the blocks hold 64 query
-    vectors and run on the prefill kernel (pa_paged_attention_prefill) unless
-    ``prefill_kernel`` is False.
+    chunk) is attended as several query blocks (pa_query_blocks): with 16-bit
+    storage, head_size 128 and no partitions the blocks hold 64 query vectors
+    and run on the prefill kernel (pa_paged_attention_prefill, or
+    pa_prefill_step with the cache writes in the same launch) unless
+    ``prefill_kernel`` is False; otherwise on the decode kernels after the
+    step's cache writes (separate launches).
     ``sliding_window``: attention sees the last W tokens only, and blocks
     outside every query's window are released before the step's appends.
     ``kernel_block_size``: the allocator hands out blocks of ``block_size``
@@ -191,10 +192,13 @@ class DecodeStep:
                 raise ValueError("one new token's query heads exceed a workgroup's query vectors")
             if self.max_query_len > block:
                 self.query_blocks = True
-                self.fused_ok = False  # blocks of one sequence read each other's new rows
                 # single pass on the matrix cores: the prefill kernel's larger
-                # blocks, each K/V tile staged once in LDS for the whole block
+                # blocks, each K/V tile staged once in LDS for the whole block;
+                # it reads the step's new rows from their inputs, so the step
+                # can run as one launch.  On the decode kernels, blocks of one
+                # sequence read each other's new rows from the cache.
                 self.prefill_rows = prefill_kernel and matrix and not self.partition_size
+                self.fused_ok = self.fused_ok and self.prefill_rows
                 if self.prefill_rows:
                     block = ops.prefill_block_tokens(H, values["key_cache"].shape[1])
                 row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl, block)
@@ -270,15 +274,22 @@ class DecodeStep:
                                        self.max_context_len)
 
     def fused(self):
-        """The whole step as one launch (pa_decode_step).  The arguments are
+        """The whole step as one launch (pa_decode_step, or pa_prefill_step for
+        query blocks on the prefill kernel).  The arguments are
         checked and marshalled on the first call; later calls launch them on
         the current stream."""
         if not self.fused_ok:
             raise ValueError("a copy-on-write of a block of several kernel blocks, or query "
-                             "blocks that read each other's new rows, need the separate "
-                             "calls: run the step unfused")
+                             "blocks on the decode kernels (they read each other's new rows "
+                             "from the cache), need the separate calls: run the step unfused")
         if self._fused_call is None:
-            if self.cascade:
+            if self.prefill_rows:
+                self._fused_call = ops.prepare_prefill_step(
+                    self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
+                    self.row_seq, self.attn_lens, self.attn_qsl, self.scale,
+                    self.max_context_len, self.query_start_loc, self.new_key, self.new_value,
+                    self.cow_src, self.slot_mapping, None, self.sliding_window)
+            elif self.cascade:
                 self._fused_call = ops.prepare_decode_step_cascade(
                     self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
                     self.context_lens, self.scale, self.max_context_len, self.partition_size,

@@ -66,9 +66,10 @@ def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window,
                       prefill_kernel=prefill_kernel)
     assert step.query_blocks, "the chunks should need several query blocks"
     assert step.prefill_rows == (prefill_kernel and matrix and not part)
-    with pytest.raises(ValueError):
-        step.fused()  # blocks of one sequence read each other's new rows
-    out = step.run()
+    if not step.prefill_rows:
+        with pytest.raises(ValueError):
+            step.fused()  # blocks of one sequence read each other's new rows from the cache
+    out = step.run().clone()
     torch.cuda.synchronize()
     ora = OracleStep(w)
     kc, vc = host["key_cache"], host["value_cache"]
@@ -78,6 +79,18 @@ def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window,
         assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
     want = ora.attention_multi(host["query"], kc, vc)
     check_attention(to_host(out), want, w.dtype, f"prefill {dtype} G={G} P={part} W={window}")
+    if step.prefill_rows:
+        # the one-launch step (pa_prefill_step) on a fresh copy of the caches
+        # before the step: the same caches, slots and output, bit for bit
+        vals2 = W.make_values(w, DEV)
+        step2 = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals2,
+                           w.scale, part, all_queries=True, sliding_window=window)
+        out2 = step2.run(fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(step2.key_cache, step.key_cache)
+        assert torch.equal(step2.value_cache, step.value_cache)
+        assert np.array_equal(to_host(step2.slot_mapping), ora.slot_mapping())
+        assert torch.equal(out2, out)
 
 
 def test_prefill_kernel_launch_order_does_not_change_results():
