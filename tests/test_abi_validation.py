@@ -145,6 +145,20 @@ CASES = [
     ("pa_paged_attention_prefill", _prefill(scale=float("inf")),
      "scale must be positive and finite"),
     ("pa_paged_attention_prefill", _prefill(bt_stride=6), "bt_stride smaller"),
+    ("pa_prefill_step", _prefill()[:-1] + [None, P, P, 256, 256, None, None, None],
+     "NULL query_start_loc, key or value"),
+    ("pa_prefill_step", _prefill()[:-1] + [P, P, None, 256, 256, None, None, None],
+     "NULL query_start_loc, key or value"),
+    ("pa_prefill_step", _prefill()[:-1] + [P, P, P, 128, 256, None, None, None],
+     "key/value rows must be 16-byte aligned"),
+    ("pa_prefill_step", _prefill()[:-1] + [P, P + 2, P, 256, 256, None, None, None],
+     "key/value rows must be 16-byte aligned"),
+    ("pa_prefill_step", _prefill()[:-1] + [P, P, P, 260, 256, None, None, None],
+     "key/value rows must be 16-byte aligned"),
+    ("pa_prefill_step", _prefill(dtype=F32)[:-1] + [P, P, P, 256, 256, None, None, None],
+     "needs 16-bit storage and head_size 128"),
+    ("pa_prefill_step", _prefill(window=-1)[:-1] + [P, P, P, 256, 256, None, None, None],
+     "sliding_window < 0"),
     ("pa_validate_tables", [None, 8, P, 2, 16, 100, 0, P, None], "NULL pointer"),
     ("pa_validate_tables", [P, 8, P, 0, 16, 100, 0, P, None], "bad sizes"),
     ("pa_validate_tables", [P, 8, P, 2, 16, 100, -1, P, None], "bad sizes"),
