@@ -267,6 +267,21 @@ def llama7b_prefill512_fp16(num_seqs=16, chunk=512):
     return w
 
 
+def qwen72b_prefill512_bf16(num_seqs=16, chunk=512):
+    """Chunked prefill on the Qwen2.5-72B-style GQA layer (64 query / 8 KV
+    heads, bf16): the Llama-7B prefill batch's prefixes and chunks, where one
+    K/V row serves 8 query heads of every chunk token (above the matrix-core
+    ridge: bound by the MFMA rate, not HBM)."""
+    rng = np.random.default_rng(8)
+    prefix = rng.integers(0, 1537, size=num_seqs)
+    lens = [int(p) + chunk for p in prefix]
+    w = custom_multi("qwen72b_prefill512_bf16", 9, lens, [chunk] * num_seqs, dtype="bf16",
+                     H=64, Hkv=8, D=128, B=16, sigma=0.5)
+    w.notes = (f"{num_seqs} sequences, cached prefix U[0,1536] + a {chunk}-token prefill chunk "
+               "(every new token a query, causal); GQA 64q/8kv x 128 bf16, B=16")
+    return w
+
+
 def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
     """The GQA batch verifying 2 speculative tokens per sequence (2 x 8 query
     vectors per KV head fill the 16 matrix-core columns)."""
@@ -401,6 +416,7 @@ CONFIGS = {
     "shared_prefix_cascade_bf16": shared_prefix_cascade_bf16,
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "llama7b_prefill512_fp16": llama7b_prefill512_fp16,
+    "qwen72b_prefill512_bf16": qwen72b_prefill512_bf16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
     "qwen72b_gqa_tp8_bf16": qwen72b_gqa_tp8_bf16,
