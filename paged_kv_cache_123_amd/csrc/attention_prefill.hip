@@ -9,13 +9,19 @@
 // vectors (token, head).  One workgroup of four waves serves one (block, KV
 // head); wave w owns query vectors 16w .. 16w+15, the 16 columns of its
 // matrix-core tiles.  The workgroup walks the keys the block sees in tiles of
-// 64 tokens, double-buffered in LDS: the next tile's rows are loaded into
-// registers while the waves score and accumulate the current one from LDS,
-// so each K/V row is read once per 64 queries.  Every wave sees every tile,
-// keeps the online softmax of its own columns (mfma_tile_update) and writes
-// its outputs itself: no merge across waves.  LDS rows are padded to 17
-// 16-byte units so that the K operand reads (16 tokens of one dim chunk)
-// fall into different banks.
+// 64 tokens, double-buffered in LDS, with the loads of the next two tiles in
+// registers while one is computed, so each K/V row is read once per 64
+// query vectors.  Every wave sees every tile, keeps the online softmax of
+// its own columns and writes its outputs itself: no merge across waves.  K
+// rows sit in LDS as stored, padded to 17 16-byte units so that the 16 rows
+// one score MFMA reads fall into different banks; V is transposed into the
+// value MFMA's operand order (value_slot).
+//
+// With the step's cache writes in the same launch (pa_prefill_step), keys
+// from a sequence's first new position on are read from the step's key/value
+// rows and the old slots of a copied tail block from its source block, so no
+// workgroup reads a slot the launch writes; each row stores its own tokens'
+// rows as its tiles bring them through the registers.
 #include <hip/hip_runtime.h>
 
 #include <climits>
