@@ -71,8 +71,10 @@ const char* pa_last_error(void);
  *   slot_mapping     device int64 [max_num_tokens] (output); entries
  *                    [num_tokens, max_num_tokens) are set to -1 (padding)
  *   num_tokens must equal query_start_loc[num_reqs].
+ * One thread per slot_mapping entry finds its request by a binary search of
+ * query_start_loc.
  * Errors: PA_EINVAL for null pointers, num_reqs < 1, num_tokens < 0,
- * max_num_tokens < num_tokens, bt_stride < 1, block_size < 1.
+ * max_num_tokens < num_tokens or > INT32_MAX, bt_stride < 1, block_size < 1.
  * ---------------------------------------------------------------------- */
 int32_t pa_compute_slot_mapping(const int32_t* query_start_loc, const int64_t* positions,
                                 const int32_t* block_tables, int64_t bt_stride,
@@ -187,7 +189,10 @@ int32_t pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_
  *   context_lens     device int32 [num_seqs], each in [1, max_context_len]
  *   max_context_len  host bound on context_lens (used to size launches)
  * Errors: PA_EINVAL for null pointers, unsupported shapes or dtype,
- * num_heads % num_kv_heads != 0, max_context_len < 1.
+ * num_heads % num_kv_heads != 0, max_context_len < 1, or more workgroups
+ * than one launch holds (num_seqs x num_kv_heads, or num_seqs x
+ * ceil(num_heads / 4) for a merge, above INT32_MAX); every attention call
+ * shares these checks.
  * ---------------------------------------------------------------------- */
 int32_t pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
                                   const void* value_cache, const int32_t* block_tables,
@@ -228,6 +233,14 @@ int32_t pa_set_decode_kernel(int32_t mode);
  * ---------------------------------------------------------------------- */
 size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                 int32_t max_context_len, int32_t partition_size);
+/* Host: where the three sections of that workspace start, for a caller that
+ * reads the partials.  offsets_out (host int64 [3]) receives the byte offsets
+ * of max_logits, exp_sums and tmp_out; *num_partitions_out receives NP.
+ * num_seqs counts the workspace's rows (sequences, or new tokens when every
+ * new token is a query).  PA_EINVAL for null outputs or sizes < 1. */
+int32_t pa_split_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                  int32_t max_context_len, int32_t partition_size,
+                                  int64_t* offsets_out, int32_t* num_partitions_out);
 
 int32_t pa_paged_attention_decode_split(void* out, const void* query, const void* key_cache,
                                         const void* value_cache, const int32_t* block_tables,
@@ -456,6 +469,20 @@ int32_t pa_query_blocks(const int32_t* context_lens, const int32_t* query_start_
                         int32_t num_seqs, int32_t max_block, int32_t* row_seq,
                         int32_t* row_lens, int32_t* row_qsl, int64_t capacity,
                         int64_t* num_rows);
+/* pa_query_block_hints (host): the shared-block cache hint
+ * (shared_prefix_blocks of pa_paged_attention_multi) of query-block rows.
+ * The rows of a sequence cut into several blocks all read every block of its
+ * context, so such a row's hint covers its whole context,
+ * ceil(row_lens[r] / block_size) blocks; a sequence left in one row keeps
+ * its own hint seq_shared_blocks[row_seq[r]] (NULL: 0).
+ *   row_seq, row_lens   host int32 [num_rows], as pa_query_blocks wrote them
+ *   seq_shared_blocks   host int32 [num_seqs] or NULL
+ *   row_shared_out      host int32 [num_rows] (output)
+ * PA_EINVAL for null arrays, sizes < 1, or a row whose sequence is outside
+ * [0, num_seqs) or whose length is negative. */
+int32_t pa_query_block_hints(const int32_t* row_seq, const int32_t* row_lens, int32_t num_rows,
+                             const int32_t* seq_shared_blocks, int32_t num_seqs,
+                             int32_t block_size, int32_t* row_shared_out);
 
 /* ------------------------------------------------------------------------
  * Prefill attention over query blocks on the matrix cores (16-bit storage,
@@ -662,6 +689,47 @@ int64_t pa_pool_num_cow(const pa_pool* pool);
  * unknown sequence or a negative argument. */
 int32_t pa_pool_remove_skipped(pa_pool* pool, int64_t seq, int64_t num_computed_tokens,
                                int32_t sliding_window, int32_t* num_released);
+/* The appends of one step, as a whole or not at all ([CSDN] section 3.2.1:
+ * a request that does not fit is refused without side effects; sections
+ * 3.1.1 and 3.3.1: blocks outside the window are released before the
+ * allocation; section 3.4: the kernels' smaller blocks).  Row r appends
+ * num_new[r] tokens to seqs[r]: with sliding_window > 0 it first releases
+ * what its next query no longer sees (pa_pool_remove_skipped at its current
+ * length), then appends (pa_pool_append), rows in order.
+ * Before anything changes, every row is checked (a known sequence, listed
+ * once, num_new >= 1) and the free queue is followed through the rows in
+ * order, counting the blocks earlier rows release, copy and take: PA_EINVAL
+ * or PA_ENOMEM then leave the pool exactly as it was.
+ * Outputs (host buffers; T = the sum of num_new, k = blocks_per_kv_block,
+ * 1 when the allocator's blocks are the kernels' blocks):
+ *   positions_out        int64 [T]: position of each new token, rows in order
+ *   query_start_loc_out  int32 [num_seqs + 1]: row r's tokens are
+ *                        [qsl[r], qsl[r+1])
+ *   slots_out            int64 [T] or NULL: slot of each new token (the same
+ *                        number under manager and kernel blocks)
+ *   cow_src_out          int64 [num_seqs]: the manager block row r's shared
+ *                        tail was copied from, -1 if none
+ *   cow_pairs_out        int64 [num_seqs * k][2]: the copies for
+ *                        pa_copy_blocks in kernel blocks: manager pair
+ *                        (src, dst) gives (src*k + j, dst*k + j), j < k
+ *   num_cow_pairs_out    number of pairs written
+ *   shared_blocks_out    int32 [num_seqs] or NULL: after the appends, the
+ *                        leading shared blocks of each table
+ *                        (pa_pool_shared_prefix_blocks) in kernel blocks
+ *   group_keys_out       int32 [num_seqs] or NULL: a key for
+ *                        pa_decode_plan_window that rows reading the same
+ *                        shared prefix have in common (its first live kernel
+ *                        block); a row without shared blocks gets
+ *                        num_blocks * k + r.
+ * PA_EINVAL also for null required pointers, num_seqs < 1, a negative
+ * window, k < 1 or kernel block ids past int32. */
+int32_t pa_pool_append_batch(pa_pool* pool, const int64_t* seqs, const int32_t* num_new,
+                             int32_t num_seqs, int32_t sliding_window,
+                             int32_t blocks_per_kv_block, int64_t* positions_out,
+                             int32_t* query_start_loc_out, int64_t* slots_out,
+                             int64_t* cow_src_out, int64_t* cow_pairs_out,
+                             int32_t* num_cow_pairs_out, int32_t* shared_blocks_out,
+                             int32_t* group_keys_out);
 
 /* ------------------------------------------------------------------------
  * Prefix caching on the host ([DEEPSONAR] section 2.4; [CSDN] sections
@@ -760,9 +828,10 @@ int32_t pa_map_to_kernel_blocks(const int32_t* manager_ids, int64_t n,
  *   partial_out           device float [num_parts][num_seqs][num_heads][head_size],
  *                         8-byte aligned
  * Parts with l = 0 carry no weight; a row no part has a key for is 0.
- * Errors: PA_EINVAL for null pointers, num_parts < 1, num_seqs outside
- * [1, 65535], num_heads < 1, head_size not 64 or 128, an unknown dtype,
- * out not aligned to its element size, partial_out not 8-byte aligned.
+ * Errors: PA_EINVAL for null pointers, num_parts < 1, num_seqs < 1,
+ * num_heads < 1, num_seqs x ceil(num_heads / 4) above INT32_MAX (the merge's
+ * workgroups), head_size not 64 or 128, an unknown dtype, out not aligned to
+ * its element size, partial_out not 8-byte aligned.
  * ---------------------------------------------------------------------- */
 int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* partial_out,
                                     const void* query, const void* key_cache,

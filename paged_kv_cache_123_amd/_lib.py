@@ -44,6 +44,7 @@ SIGNATURES = {
                                          _i32, _i32, _i32, _f32, _i32, _vp]),
     "pa_set_decode_kernel": (_i32, [_i32]),
     "pa_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_split_workspace_layout": (_i32, [_i32, _i32, _i32, _i32, _i32, _pi64, _pi32]),
     "pa_paged_attention_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                _sz, _vp]),
@@ -63,6 +64,7 @@ SIGNATURES = {
                                       _i32, _i32, _f32, _i32, _i32, _vp, _i64, _i32, _vp, _vp,
                                       _sz, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "pa_query_blocks": (_i32, [_pi32, _pi32, _i32, _i32, _pi32, _pi32, _pi32, _i64, _pi64]),
+    "pa_query_block_hints": (_i32, [_pi32, _pi32, _i32, _pi32, _i32, _i32, _pi32]),
     "pa_prefill_block_tokens": (_i32, [_i32, _i32, _pi32]),
     "pa_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,
@@ -91,6 +93,8 @@ SIGNATURES = {
     "pa_pool_free_queue": (_i32, [_vp, _pi32, _i32]),
     "pa_pool_num_cow": (_i64, [_vp]),
     "pa_pool_remove_skipped": (_i32, [_vp, _i64, _i64, _i32, _pi32]),
+    "pa_pool_append_batch": (_i32, [_vp, _pi64, _pi32, _i32, _i32, _i32, _pi64, _pi32, _pi64,
+                                    _pi64, _pi64, _pi32, _pi32, _pi32]),
     "pa_map_to_kernel_blocks": (_i32, [_pi32, _i64, _i32, _pi32]),
     "pa_pool_enable_prefix_caching": (_i32, [_vp]),
     "pa_pool_add_seq_cached": (_i32, [_vp, _i64, _pi32, _i64, _vp, _i32, _pi64]),

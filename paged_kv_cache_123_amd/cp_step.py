@@ -20,7 +20,6 @@ virtual block.  One rank's step, in order on one stream:
 
 from __future__ import annotations
 
-import numpy as np
 import torch
 
 from . import ops
@@ -55,7 +54,8 @@ class CPRankStep:
         self.world, self.rank, self.interleave = int(world), int(rank), int(interleave)
         self.block_size = int(block_size)
         self.pool = Pool(num_blocks, block_size * world, free_order)
-        seqs, positions, qsl, cow, _ = replay(self.pool, history, appends)
+        batch = replay(self.pool, history, appends)
+        seqs = [s for s, _ in appends]
         width = max(max(self.pool.seq_num_blocks(s) for s in seqs), 1)
         tables, lens = self.pool.block_tables(seqs, width)
         self.seqs = seqs
@@ -63,10 +63,10 @@ class CPRankStep:
         self.context_lens_host = lens            # whole sequences
         self.local_lens_host = ops.cp_local_context_lens(lens, block_size, world, rank,
                                                          interleave)
-        self.cow_pairs_host = np.asarray(cow, dtype=np.int64).reshape(-1, 2)
-        self.positions_host = np.asarray(positions, dtype=np.int64)
-        self.query_start_loc_host = np.asarray(qsl, dtype=np.int32)
-        self.num_tokens = int(qsl[-1])
+        self.cow_pairs_host = batch.cow_pairs
+        self.positions_host = batch.positions
+        self.query_start_loc_host = batch.query_start_loc
+        self.num_tokens = int(batch.query_start_loc[-1])
         self.max_local_len = int(self.local_lens_host.max())
         self.scale = float(scale)
         self.partition_size = int(partition_size)

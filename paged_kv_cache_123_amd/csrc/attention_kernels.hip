@@ -76,7 +76,7 @@ __global__ __launch_bounds__(NW * 64) PA_VALU_OCCUPANCY void paged_decode_kernel
   constexpr int U = kTile / TPL;  // loads per tile per cache
   static_assert(LPT >= 8 && LPT <= 32 && U >= 1, "unsupported head size");
 
-  const WorkUnit wu = work_unit(items, num_kv_heads);
+  const WorkUnit wu = work_unit(items, num_kv_heads, FINAL ? 1 : num_partitions);
   const int p = wu.p;
   const int kvh = wu.kvh;
   const int s = wu.s;
@@ -387,8 +387,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeDst dst, PartView src,
                                                     int32_t window) {
   constexpr int DPL = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int s = blockIdx.y;
+  const int head_groups = (num_heads + 3) / 4;  // four heads (waves) per workgroup
+  const int h = static_cast<int>(blockIdx.x % head_groups) * 4 + (threadIdx.x >> 6);
+  const int s = static_cast<int>(blockIdx.x / head_groups);
   if (h >= num_heads) return;  // no barrier below
   // split launches: only the partitions below the sequence's length exist
   const int L = context_lens ? context_lens[s] : 0;
@@ -466,7 +467,9 @@ hipError_t launch_decode_nw(const DecodeArgs& a, hipStream_t stream) {
   int log2_group = 0;
   while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))
-                            : dim3(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
+                            : dim3(static_cast<uint32_t>((FINAL ? 1 : a.num_partitions) *
+                                                         static_cast<int64_t>(a.num_kv_heads) *
+                                                         a.num_seqs));
   hipLaunchKernelGGL((paged_decode_kernel<DT, D, NQ, NW, FINAL>), grid, dim3(NW * 64), 0, stream,
                      a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
                      a.context_lens, a.num_heads, a.num_kv_heads, log2_block, a.partition_size,
@@ -518,7 +521,8 @@ hipError_t launch_merge_t(const MergeDst& dst, const PartView& src, const int32_
                           int32_t num_rows, int32_t num_heads, int32_t partition_size,
                           int32_t num_parts, const int32_t* q_start, int32_t window,
                           hipStream_t stream) {
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((num_heads + 3) / 4, num_rows), dim3(256), 0,
+  const int64_t grid = static_cast<int64_t>((num_heads + 3) / 4) * num_rows;
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
                      stream, dst, src, context_lens, num_heads, partition_size, num_parts, q_start,
                      window);
   return hipGetLastError();

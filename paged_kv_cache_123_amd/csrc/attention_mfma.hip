@@ -67,7 +67,7 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void paged_decode_mfma_k
   constexpr int U = 4;        // token-major V loads per tile
   static_assert(NQ >= 1 && NQ <= 16, "query vectors must fit the 16 MFMA columns");
 
-  const WorkUnit wu = work_unit(items, num_kv_heads);
+  const WorkUnit wu = work_unit(items, num_kv_heads, FINAL ? 1 : num_partitions);
   const int p = wu.p;
   const int kvh = wu.kvh;
   // A group item (sequence field < 0) serves the members of chunk -1 - s of
@@ -271,7 +271,9 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   int log2_group = 0;
   while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid = a.items ? dim3(static_cast<uint32_t>(a.num_items * a.num_kv_heads))
-                            : dim3(FINAL ? 1 : a.num_partitions, a.num_kv_heads, a.num_seqs);
+                            : dim3(static_cast<uint32_t>((FINAL ? 1 : a.num_partitions) *
+                                                         static_cast<int64_t>(a.num_kv_heads) *
+                                                         a.num_seqs));
   hipLaunchKernelGGL((paged_decode_mfma_kernel<DT, NQ, NW, FINAL>), grid, dim3(NW * 64), 0,
                      stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,

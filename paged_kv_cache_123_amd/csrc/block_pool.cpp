@@ -257,6 +257,115 @@ int32_t pa_pool_remove_skipped(pa_pool* pool, int64_t seq, int64_t num_computed_
   return PA_OK;
 }
 
+int32_t pa_pool_append_batch(pa_pool* pool, const int64_t* seqs, const int32_t* num_new,
+                             int32_t num_seqs, int32_t sliding_window,
+                             int32_t blocks_per_kv_block, int64_t* positions_out,
+                             int32_t* query_start_loc_out, int64_t* slots_out,
+                             int64_t* cow_src_out, int64_t* cow_pairs_out,
+                             int32_t* num_cow_pairs_out, int32_t* shared_blocks_out,
+                             int32_t* group_keys_out) {
+  if (!pool || !seqs || !num_new || !positions_out || !query_start_loc_out || !cow_src_out ||
+      !cow_pairs_out || !num_cow_pairs_out)
+    return pa::fail(PA_EINVAL, "pa_pool_append_batch: NULL argument");
+  if (num_seqs < 1 || sliding_window < 0 || blocks_per_kv_block < 1)
+    return pa::fail(PA_EINVAL, "pa_pool_append_batch: bad num_seqs, sliding_window or "
+                               "blocks_per_kv_block");
+  const int64_t k = blocks_per_kv_block;
+  if (static_cast<int64_t>(pool->num_blocks) * k > INT32_MAX)
+    return pa::fail(PA_EINVAL, "pa_pool_append_batch: kernel block ids overflow int32");
+  // Dry run: every row is checked and the free queue is followed row by row
+  // (window releases first, then the copy of a shared tail and the fresh
+  // blocks) on an overlay of the reference counts, so that a step either
+  // fits as a whole or leaves the pool untouched.
+  std::unordered_map<int64_t, int32_t> row_of;
+  std::unordered_map<int32_t, int32_t> ref_now;  // counts the dry run changed
+  auto ref_of = [&](int32_t b) {
+    auto it = ref_now.find(b);
+    return it != ref_now.end() ? it->second : pool->ref[b];
+  };
+  const int64_t B = pool->block_size;
+  int64_t free_now = pool->num_free, total = 0;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    auto it = pool->seqs.find(seqs[r]);
+    if (it == pool->seqs.end())
+      return pa::fail(PA_EINVAL, "pa_pool_append_batch: unknown sequence");
+    if (!row_of.emplace(seqs[r], r).second)
+      return pa::fail(PA_EINVAL, "pa_pool_append_batch: a sequence is listed twice");
+    if (num_new[r] < 1)
+      return pa::fail(PA_EINVAL, "pa_pool_append_batch: every row appends at least one token");
+    total += num_new[r];
+    if (total > INT32_MAX) return pa::fail(PA_EINVAL, "pa_pool_append_batch: too many tokens");
+    const Seq& s = it->second;
+    if (sliding_window > 0) {
+      const int64_t skipped = std::max<int64_t>(0, s.len - sliding_window + 1);
+      const int64_t n = std::min<int64_t>(skipped / B, static_cast<int64_t>(s.blocks.size()));
+      for (int64_t j = n - 1; j >= 0; --j) {
+        const int32_t b = s.blocks[j];
+        if (b < 0) continue;
+        const int32_t c = ref_of(b) - 1;
+        ref_now[b] = c;
+        if (c == 0) ++free_now;
+      }
+    }
+    if (s.len % B != 0) {
+      const int32_t tail = s.blocks.back();
+      if (ref_of(tail) > 1) {  // copy-on-write: one fresh block, one holder less
+        ref_now[tail] = ref_of(tail) - 1;
+        --free_now;
+      }
+    }
+    free_now -= (s.len + num_new[r] + B - 1) / B - (s.len + B - 1) / B;
+    if (free_now < 0) return pa::fail(PA_ENOMEM, "pa_pool_append_batch: not enough free blocks");
+  }
+  // The step itself: each row releases, then appends (cannot fail now).
+  int64_t t = 0;
+  int32_t pairs = 0;
+  query_start_loc_out[0] = 0;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    const int64_t start = pool->seqs.find(seqs[r])->second.len;
+    if (sliding_window > 0) pa_pool_remove_skipped(pool, seqs[r], start, sliding_window, nullptr);
+    int64_t pair[2];
+    int32_t copied = 0;
+    std::vector<int64_t> row_slots;
+    int64_t* sl = slots_out ? slots_out + t : (row_slots.resize(num_new[r]), row_slots.data());
+    const int32_t st = pa_pool_append(pool, seqs[r], num_new[r], sl, pair, &copied);
+    if (st != PA_OK) return st;  // unreachable after the dry run
+    for (int32_t i = 0; i < num_new[r]; ++i) positions_out[t + i] = start + i;
+    t += num_new[r];
+    query_start_loc_out[r + 1] = static_cast<int32_t>(t);
+    cow_src_out[r] = copied ? pair[0] : -1;
+    if (copied) {
+      for (int64_t j = 0; j < k; ++j) {
+        cow_pairs_out[2 * pairs] = pair[0] * k + j;
+        cow_pairs_out[2 * pairs + 1] = pair[1] * k + j;
+        ++pairs;
+      }
+    }
+  }
+  *num_cow_pairs_out = pairs;
+  if (shared_blocks_out || group_keys_out) {
+    std::vector<int32_t> shared(num_seqs);
+    pa_pool_shared_prefix_blocks(pool, seqs, num_seqs, shared.data());
+    for (int32_t r = 0; r < num_seqs; ++r) {
+      if (shared_blocks_out) shared_blocks_out[r] = static_cast<int32_t>(shared[r] * k);
+      if (!group_keys_out) continue;
+      // readers of one shared prefix share a key: its first live block, in
+      // kernel blocks; a row without shared blocks gets a key of its own
+      int32_t key = static_cast<int32_t>(pool->num_blocks * k + r);
+      if (shared[r] > 0) {
+        for (int32_t b : pool->seqs.find(seqs[r])->second.blocks) {
+          if (b >= 0) {
+            key = static_cast<int32_t>(b * k);
+            break;
+          }
+        }
+      }
+      group_keys_out[r] = key;
+    }
+  }
+  return PA_OK;
+}
+
 int32_t pa_pool_seq_len(const pa_pool* pool, int64_t seq, int64_t* len_out) {
   if (!pool || !len_out) return pa::fail(PA_EINVAL, "pa_pool_seq_len: NULL argument");
   auto it = pool->seqs.find(seq);

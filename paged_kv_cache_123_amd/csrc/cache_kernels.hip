@@ -17,42 +17,51 @@
 namespace pa {
 namespace {
 
-// One workgroup per request: its tokens [qsl[r], qsl[r+1]) get
-// slot = table[r][pos / B] * B + pos % B.  Workgroups past num_reqs write the
-// padding entries [num_tokens, max_num_tokens) with -1.
+// Slot of one token position under one table row ([PUFANYI] "按 Block 分配":
+// logical block pos / B, physical block row[pos / B], offset pos % B).
 //
-// Context parallelism ([CSDN] section 2.3): with cp_world ranks a table entry
-// names a virtual block of B * cp_world positions.  Offset o inside it goes
-// to rank (o / interleave) % cp_world, at local offset
-// (o / (cp_world * interleave)) * interleave + o % interleave of that rank's
-// block with the same number; this rank writes -1 for tokens another rank
-// stores.  cp_world = 1, interleave = 1 is the plain mapping above.
+// Context parallelism ([CSDN] section 2.3 describes the placement): the
+// ranks of a group share a table whose entries name virtual blocks of
+// B * cp_world positions.  Inside a virtual block, runs of `interleave`
+// consecutive positions are dealt to the ranks in turn; a rank keeps its
+// runs in order, so its k-th run fills local offsets [k * interleave,
+// (k + 1) * interleave) of the block with the same number in its own cache.
+// Positions dealt to another rank give -1.  cp_world = interleave = 1 is the
+// plain mapping.
+__device__ __forceinline__ int64_t slot_of(const int32_t* __restrict__ row, int64_t pos,
+                                           int32_t block_size, int32_t cp_world,
+                                           int32_t cp_rank, int32_t interleave) {
+  const int64_t span = static_cast<int64_t>(block_size) * cp_world;
+  const int64_t vblock = pos / span;
+  const int64_t within = pos - vblock * span;
+  const int64_t run = within / interleave;  // index of the run inside the block
+  if (run % cp_world != cp_rank) return -1;
+  const int64_t local = (run / cp_world) * interleave + (within - run * interleave);
+  return static_cast<int64_t>(row[vblock]) * block_size + local;
+}
+
+// One thread per entry of slot_mapping[0, max_num_tokens).  Token i <
+// num_tokens belongs to the last request r with qsl[r] <= i (a binary search
+// over the request offsets, so empty requests are skipped); entries from
+// num_tokens on are padding and get -1.
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     const int32_t* __restrict__ qsl, const int64_t* __restrict__ positions,
     const int32_t* __restrict__ block_tables, int64_t bt_stride, int32_t num_reqs,
     int64_t num_tokens, int64_t max_num_tokens, int32_t block_size, int32_t cp_world,
     int32_t cp_rank, int32_t interleave, int64_t* __restrict__ slot_mapping) {
-  const int64_t r = blockIdx.x;
-  if (r < num_reqs) {
-    const int64_t begin = qsl[r], end = qsl[r + 1];
-    const int32_t* row = block_tables + r * bt_stride;
-    const int64_t vbs = static_cast<int64_t>(block_size) * cp_world;
-    const int64_t stripe = static_cast<int64_t>(cp_world) * interleave;
-    for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
-      const int64_t pos = positions[i];
-      const int64_t vb = pos / vbs;
-      const int64_t off = pos - vb * vbs;
-      int64_t slot = -1;
-      if ((off / interleave) % cp_world == cp_rank)
-        slot = static_cast<int64_t>(row[vb]) * block_size + (off / stripe) * interleave +
-               off % interleave;
-      slot_mapping[i] = slot;
-    }
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= max_num_tokens) return;
+  if (i >= num_tokens) {
+    slot_mapping[i] = -1;
     return;
   }
-  const int64_t pad_begin = num_tokens + (r - num_reqs) * 4096;
-  const int64_t pad_end = pad_begin + 4096 < max_num_tokens ? pad_begin + 4096 : max_num_tokens;
-  for (int64_t i = pad_begin + threadIdx.x; i < pad_end; i += blockDim.x) slot_mapping[i] = -1;
+  int32_t lo = 0, hi = num_reqs;  // invariant: qsl[lo] <= i < qsl[hi]
+  while (hi - lo > 1) {
+    const int32_t mid = lo + (hi - lo) / 2;
+    if (qsl[mid] <= i) lo = mid; else hi = mid;
+  }
+  slot_mapping[i] = slot_of(block_tables + static_cast<int64_t>(lo) * bt_stride, positions[i],
+                            block_size, cp_world, cp_rank, interleave);
 }
 
 // One workgroup per token.  Unit = 16 bytes when every row start is 16-byte
@@ -145,10 +154,9 @@ hipError_t launch_slot_mapping(const int32_t* query_start_loc, const int64_t* po
                                int64_t num_tokens, int64_t max_num_tokens, int32_t block_size,
                                int32_t cp_world, int32_t cp_rank, int32_t interleave,
                                int64_t* slot_mapping, hipStream_t stream) {
-  const int64_t pad = max_num_tokens - num_tokens;
-  const int64_t pad_groups = (pad + 4095) / 4096;
-  const int64_t grid = num_reqs + pad_groups;
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, stream,
+  if (max_num_tokens == 0) return hipSuccess;
+  const int64_t grid = (max_num_tokens + 255) / 256;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
                      query_start_loc, positions, block_tables, bt_stride, num_reqs, num_tokens,
                      max_num_tokens, block_size, cp_world, cp_rank, interleave, slot_mapping);
   return hipGetLastError();

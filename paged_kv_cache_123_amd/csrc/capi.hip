@@ -2,6 +2,7 @@
 // validation, then the launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -60,10 +61,55 @@ int32_t check_decode(const char* who, void* out, const void* query, const void* 
     return fail(PA_EINVAL, (w + ": bt_stride smaller than ceil(max_context_len / B)").c_str());
   if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
     return fail(PA_EINVAL, (w + ": out, query and caches must be 16-byte aligned").c_str());
+  // every grid is one-dimensional: (sequence, KV head) workgroups of a
+  // launch without a work list, (sequence, four heads) of the merge
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads > INT32_MAX ||
+      static_cast<int64_t>(num_seqs) * ((num_heads + 3) / 4) > INT32_MAX)
+    return fail(PA_EINVAL, (w + ": num_seqs x heads exceeds one launch's workgroups").c_str());
+  return PA_OK;
+}
+
+// A split launch without a work list has a workgroup per (sequence, KV head,
+// partition), whether the partition holds tokens or not.
+int32_t check_split_grid(const char* who, int32_t num_seqs, int32_t num_kv_heads,
+                         int32_t max_context_len, int32_t partition_size) {
+  const int64_t np = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  if (np * num_kv_heads * num_seqs > INT32_MAX)
+    return fail(PA_EINVAL, (std::string(who) + ": num_seqs x num_kv_heads x partitions exceeds "
+                            "one launch's workgroups")
+                               .c_str());
   return PA_OK;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Sections of a split workspace: max_logits and exp_sums [rows][H][NP], then
+// tmp_out [rows][H][NP][D], each starting on a 256-byte boundary.
+struct SplitLayout {
+  int32_t np;
+  size_t sum_off, out_off, bytes;
+};
+
+SplitLayout split_layout(int64_t rows, int32_t num_heads, int32_t head_size,
+                         int32_t max_context_len, int32_t partition_size) {
+  SplitLayout w{};
+  w.np = (max_context_len + partition_size - 1) / partition_size;
+  const size_t parts = static_cast<size_t>(rows) * num_heads * w.np;
+  w.sum_off = align256(parts * sizeof(float));
+  w.out_off = 2 * w.sum_off;
+  w.bytes = w.out_off + align256(parts * head_size * sizeof(float));
+  return w;
+}
+
+// Points the launch arguments at the sections of a checked workspace.
+void set_split(pa::DecodeArgs& a, void* workspace, const SplitLayout& w, int32_t partition_size) {
+  char* ws = static_cast<char*>(workspace);
+  a.partition_size = partition_size;
+  a.num_partitions = w.np;
+  a.ws_max = reinterpret_cast<float*>(ws);
+  a.ws_sum = reinterpret_cast<float*>(ws + w.sum_off);
+  a.ws_out = reinterpret_cast<float*>(ws + w.out_off);
+}
 
 // Every new token of a sequence is a query: the query vectors of one work item
 // (max_query_len x heads per KV head) must fit one workgroup.
@@ -90,8 +136,8 @@ int32_t pa_compute_slot_mapping(const int32_t* query_start_loc, const int64_t* p
                                 int32_t block_size, int64_t* slot_mapping, void* stream) {
   if (!query_start_loc || !block_tables || !slot_mapping || (!positions && num_tokens > 0))
     return fail(PA_EINVAL, "pa_compute_slot_mapping: NULL pointer");
-  if (num_reqs < 1 || num_tokens < 0 || max_num_tokens < num_tokens || bt_stride < 1 ||
-      block_size < 1)
+  if (num_reqs < 1 || num_tokens < 0 || max_num_tokens < num_tokens ||
+      max_num_tokens > INT32_MAX || bt_stride < 1 || block_size < 1)
     return fail(PA_EINVAL, "pa_compute_slot_mapping: bad sizes");
   return launched(pa::launch_slot_mapping(query_start_loc, positions, block_tables, bt_stride,
                                           num_reqs, num_tokens, max_num_tokens, block_size, 1, 0,
@@ -107,8 +153,8 @@ int32_t pa_compute_slot_mapping_cp(const int32_t* query_start_loc, const int64_t
   const char* who = "pa_compute_slot_mapping_cp";
   if (!query_start_loc || !block_tables || !slot_mapping || (!positions && num_tokens > 0))
     return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: NULL pointer");
-  if (num_reqs < 1 || num_tokens < 0 || max_num_tokens < num_tokens || bt_stride < 1 ||
-      block_size < 1)
+  if (num_reqs < 1 || num_tokens < 0 || max_num_tokens < num_tokens ||
+      max_num_tokens > INT32_MAX || bt_stride < 1 || block_size < 1)
     return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: bad sizes");
   if (cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world)
     return fail(PA_EINVAL, "pa_compute_slot_mapping_cp: need 0 <= cp_rank < cp_world");
@@ -198,9 +244,22 @@ size_t pa_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t hea
   if (num_seqs < 1 || num_heads < 1 || head_size < 1 || max_context_len < 1 ||
       partition_size < 1)
     return 0;
-  const size_t np = (static_cast<size_t>(max_context_len) + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * head_size * sizeof(float));
+  return split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size).bytes;
+}
+
+int32_t pa_split_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                  int32_t max_context_len, int32_t partition_size,
+                                  int64_t* offsets_out, int32_t* num_partitions_out) {
+  if (!offsets_out || !num_partitions_out || num_seqs < 1 || num_heads < 1 || head_size < 1 ||
+      max_context_len < 1 || partition_size < 1)
+    return fail(PA_EINVAL, "pa_split_workspace_layout: bad argument");
+  const SplitLayout w =
+      split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size);
+  offsets_out[0] = 0;
+  offsets_out[1] = static_cast<int64_t>(w.sum_off);
+  offsets_out[2] = static_cast<int64_t>(w.out_off);
+  *num_partitions_out = w.np;
+  return PA_OK;
 }
 
 int32_t pa_paged_attention_decode_split(void* out, const void* query, const void* key_cache,
@@ -227,15 +286,15 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
     return fail(PA_EINVAL, "pa_paged_attention_decode_split: workspace missing or too small");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PA_EINVAL, "pa_paged_attention_decode_split: workspace must be 256-byte aligned");
-  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
-  char* ws = static_cast<char*>(workspace);
-  float* ws_max = reinterpret_cast<float*>(ws);
-  float* ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-  float* ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  st = check_split_grid("pa_paged_attention_decode_split", num_seqs, num_kv_heads,
+                        max_context_len, partition_size);
+  if (st != PA_OK) return st;
   pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
-                   num_seqs, num_heads, num_kv_heads, head_size, block_size, partition_size,
-                   np, scale, dtype, ws_max, ws_sum, ws_out, nullptr, 0};
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale,
+                   dtype, nullptr, nullptr, nullptr, nullptr, 0};
+  set_split(a, workspace,
+            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_split (partition)");
   if (st != PA_OK) return st;
@@ -279,15 +338,12 @@ int32_t pa_paged_attention_decode_planned(
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PA_EINVAL,
                 "pa_paged_attention_decode_planned: workspace missing, too small or misaligned");
-  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
-  char* ws = static_cast<char*>(workspace);
   pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
-                   num_seqs, num_heads, num_kv_heads, head_size, block_size, partition_size, np,
-                   scale, dtype, reinterpret_cast<float*>(ws),
-                   reinterpret_cast<float*>(ws + align256(rows * sizeof(float))),
-                   reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float))),
-                   work_items, num_work_items};
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, work_items, num_work_items};
+  set_split(a, workspace,
+            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
   a.shared_blocks = shared_prefix_blocks;
   a.window = sliding_window;
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_planned (partition)");
@@ -361,14 +417,9 @@ static int32_t decode_step_impl(const char* who, int32_t max_group, void* out,
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PA_EINVAL,
                 (std::string(who) + ": workspace missing, too small or misaligned").c_str());
-  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(out_rows) * num_heads * np;
-  char* ws = static_cast<char*>(workspace);
-  a.partition_size = partition_size;
-  a.num_partitions = np;
-  a.ws_max = reinterpret_cast<float*>(ws);
-  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  set_split(a, workspace,
+            split_layout(out_rows, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
   st = launched(pa::launch_decode(a, s), (std::string(who) + " (partition)").c_str());
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), (std::string(who) + " (reduce)").c_str());
@@ -462,14 +513,9 @@ int32_t pa_paged_attention_cascade(void* out, const void* query, const void* key
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PA_EINVAL,
                 "pa_paged_attention_cascade: workspace missing, too small or misaligned");
-  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
-  char* ws = static_cast<char*>(workspace);
-  a.partition_size = partition_size;
-  a.num_partitions = np;
-  a.ws_max = reinterpret_cast<float*>(ws);
-  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  set_split(a, workspace,
+            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_cascade (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_cascade (reduce)");
@@ -517,14 +563,9 @@ int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_c
                                                head_size, max_context_len, partition_size);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PA_EINVAL, "pa_paged_attention_multi: workspace missing, too small or misaligned");
-  const int32_t np = (max_context_len + partition_size - 1) / partition_size;
-  const size_t rows = static_cast<size_t>(num_tokens) * num_heads * np;
-  char* ws = static_cast<char*>(workspace);
-  a.partition_size = partition_size;
-  a.num_partitions = np;
-  a.ws_max = reinterpret_cast<float*>(ws);
-  a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-  a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  set_split(a, workspace,
+            split_layout(num_tokens, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
   st = launched(pa::launch_decode(a, s), "pa_paged_attention_multi (partition)");
   if (st != PA_OK) return st;
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_multi (reduce)");
@@ -549,7 +590,6 @@ int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* p
   if (st != PA_OK) return st;
   if (!max_logits || !exp_sums)
     return fail(PA_EINVAL, "pa_paged_attention_partials: NULL max_logits or exp_sums");
-  if (num_seqs > 65535) return fail(PA_EINVAL, "pa_paged_attention_partials: num_seqs > 65535");
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
       partition_size % block_size != 0)
     return fail(PA_EINVAL,
@@ -558,6 +598,10 @@ int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* p
   if (work_items && (num_work_items < 0 ||
                      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads))
     return fail(PA_EINVAL, "pa_paged_attention_partials: bad work list");
+  if (!work_items) {
+    st = check_split_grid(who, num_seqs, num_kv_heads, ctx, partition_size);
+    if (st != PA_OK) return st;
+  }
   const int32_t np = (max_context_len + partition_size - 1) / partition_size;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   pa::DecodeArgs a{nullptr, query, key_cache, value_cache, block_tables, bt_stride,
@@ -573,11 +617,9 @@ int32_t pa_paged_attention_partials(float* max_logits, float* exp_sums, float* p
         reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return fail(PA_EINVAL,
                   "pa_paged_attention_partials: workspace missing, too small or misaligned");
-    const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
-    char* ws = static_cast<char*>(workspace);
-    a.ws_max = reinterpret_cast<float*>(ws);
-    a.ws_sum = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-    a.ws_out = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+    set_split(a, workspace,
+              split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
+              partition_size);
     st = launched(pa::launch_decode(a, s), "pa_paged_attention_partials (partition)");
     if (st != PA_OK) return st;
   } else {
@@ -596,8 +638,11 @@ int32_t pa_merge_attention_partials(void* out, const float* max_logits, const fl
   if (eb == 0) return fail(PA_EINVAL, "pa_merge_attention_partials: unknown dtype");
   if (!out || !max_logits || !exp_sums || !partial_out)
     return fail(PA_EINVAL, "pa_merge_attention_partials: NULL pointer");
-  if (num_parts < 1 || num_seqs < 1 || num_seqs > 65535 || num_heads < 1)
+  if (num_parts < 1 || num_seqs < 1 || num_heads < 1)
     return fail(PA_EINVAL, "pa_merge_attention_partials: bad sizes");
+  if (static_cast<int64_t>(num_seqs) * ((num_heads + 3) / 4) > INT32_MAX)
+    return fail(PA_EINVAL, "pa_merge_attention_partials: num_seqs x heads exceeds one launch's "
+                           "workgroups");
   if (head_size != 64 && head_size != 128)
     return fail(PA_EINVAL, "pa_merge_attention_partials: head_size must be 64 or 128");
   if (reinterpret_cast<uintptr_t>(out) % eb != 0)

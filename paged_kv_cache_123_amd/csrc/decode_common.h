@@ -202,19 +202,23 @@ __device__ __forceinline__ float group_sum(float x) {
 // ---- work units -------------------------------------------------------------
 // (sequence, KV head, partition) of this workgroup.  With a work list,
 // workgroup b serves item b / H_kv, KV head b % H_kv (items are (sequence,
-// partition) pairs, largest first); without one the grid is
-// (partition, KV head, sequence).
+// partition) pairs, largest first); without one, workgroup b serves
+// partition b % grid_parts, KV head (b / grid_parts) % H_kv and sequence
+// b / (grid_parts * H_kv), all on grid.x (no 65535 limit of grid.y / z).
 struct WorkUnit {
   int s, kvh, p;
 };
 
-__device__ __forceinline__ WorkUnit work_unit(const int2* items, int num_kv_heads) {
+__device__ __forceinline__ WorkUnit work_unit(const int2* items, int num_kv_heads,
+                                              int grid_parts) {
+  const uint32_t b = blockIdx.x;
   if (items) {
-    const int2 it = items[blockIdx.x / num_kv_heads];
-    return {it.x, static_cast<int>(blockIdx.x % num_kv_heads), it.y};
+    const int2 it = items[b / num_kv_heads];
+    return {it.x, static_cast<int>(b % num_kv_heads), it.y};
   }
-  return {static_cast<int>(blockIdx.z), static_cast<int>(blockIdx.y),
-          static_cast<int>(blockIdx.x)};
+  const uint32_t sh = b / grid_parts;
+  return {static_cast<int>(sh / num_kv_heads), static_cast<int>(sh % num_kv_heads),
+          static_cast<int>(b % grid_parts)};
 }
 
 // ---- the step's cache writes, fused into the attention launch ---------------

@@ -257,3 +257,29 @@ extern "C" int32_t pa_query_blocks(const int32_t* context_lens, const int32_t* q
   }
   return PA_OK;
 }
+
+// A sequence cut into several rows has every block of its context read by
+// each of them, so all of a row's blocks are shared then; a sequence with one
+// row keeps its own shared prefix.
+extern "C" int32_t pa_query_block_hints(const int32_t* row_seq, const int32_t* row_lens,
+                                        int32_t num_rows, const int32_t* seq_shared_blocks,
+                                        int32_t num_seqs, int32_t block_size,
+                                        int32_t* row_shared_out) {
+  if (!row_seq || !row_lens || !row_shared_out || num_rows < 1 || num_seqs < 1 ||
+      block_size < 1)
+    return pa::fail(PA_EINVAL, "pa_query_block_hints: bad argument");
+  std::vector<int32_t> rows_of(num_seqs, 0);
+  for (int32_t r = 0; r < num_rows; ++r) {
+    if (row_seq[r] < 0 || row_seq[r] >= num_seqs || row_lens[r] < 0)
+      return pa::fail(PA_EINVAL, "pa_query_block_hints: row sequence or length out of range");
+    ++rows_of[row_seq[r]];
+  }
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const int32_t s = row_seq[r];
+    row_shared_out[r] = rows_of[s] > 1
+                            ? static_cast<int32_t>((static_cast<int64_t>(row_lens[r]) +
+                                                    block_size - 1) / block_size)
+                            : (seq_shared_blocks ? seq_shared_blocks[s] : 0);
+  }
+  return PA_OK;
+}

@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import ctypes
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -19,6 +20,18 @@ def _p32(a: np.ndarray):
 
 def _p64(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+@dataclass
+class StepAppends:
+    """What pa_pool_append_batch hands back for one step (host arrays)."""
+    positions: np.ndarray        # int64 [T]
+    query_start_loc: np.ndarray  # int32 [S + 1]
+    slots: np.ndarray            # int64 [T]
+    cow_src: np.ndarray          # int64 [S], -1: no copy
+    cow_pairs: np.ndarray        # int64 [P, 2], kernel blocks
+    shared_blocks: np.ndarray    # int32 [S], kernel blocks
+    group_keys: np.ndarray       # int32 [S]
 
 
 class Pool:
@@ -60,6 +73,41 @@ class Pool:
             raise PoolExhausted(st, lib().pa_last_error().decode())
         check(st)
         return slots, ((int(cow[0]), int(cow[1])) if n_cow.value else None)
+
+    def append_batch(self, seqs, num_new, sliding_window: int = 0,
+                     blocks_per_kv_block: int = 1) -> "StepAppends":
+        """The appends of one step, all or nothing (pa_pool_append_batch):
+        row r releases what its window left (sliding_window > 0), then appends
+        num_new[r] tokens to seqs[r].  Raises PoolExhausted (or PagedKVError
+        for an unknown or repeated sequence, or a count < 1) with the pool
+        unchanged."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = np.ascontiguousarray(np.asarray(num_new, dtype=np.int32))
+        if ids.ndim != 1 or n.shape != ids.shape or ids.size < 1:
+            raise ValueError("one new-token count per sequence, at least one sequence")
+        k = int(blocks_per_kv_block)
+        total = int(n.astype(np.int64).sum()) if (n >= 1).all() else 0
+        out = StepAppends(
+            positions=np.empty(max(total, 1), dtype=np.int64),
+            query_start_loc=np.empty(ids.size + 1, dtype=np.int32),
+            slots=np.empty(max(total, 1), dtype=np.int64),
+            cow_src=np.empty(ids.size, dtype=np.int64),
+            cow_pairs=np.empty((ids.size * max(k, 1), 2), dtype=np.int64),
+            shared_blocks=np.empty(ids.size, dtype=np.int32),
+            group_keys=np.empty(ids.size, dtype=np.int32))
+        n_pairs = ctypes.c_int32(0)
+        st = lib().pa_pool_append_batch(
+            self._h, _p64(ids), _p32(n), ids.size, int(sliding_window), k,
+            _p64(out.positions), _p32(out.query_start_loc), _p64(out.slots), _p64(out.cow_src),
+            _p64(out.cow_pairs), ctypes.byref(n_pairs), _p32(out.shared_blocks),
+            _p32(out.group_keys))
+        if st == PA_ENOMEM:
+            raise PoolExhausted(st, lib().pa_last_error().decode())
+        check(st)
+        out.positions = out.positions[:total]
+        out.slots = out.slots[:total]
+        out.cow_pairs = out.cow_pairs[:n_pairs.value]
+        return out
 
     def free_seq(self, seq: int) -> None:
         check(lib().pa_pool_free_seq(self._h, seq))

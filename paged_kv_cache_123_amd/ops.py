@@ -249,14 +249,21 @@ def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head
                     max_context_len: int, partition_size: int):
     """(max_logits [S,H,NP], exp_sums [S,H,NP], tmp_out [S,H,NP,D]) views of a
     split workspace, in the layout pagedkv.h documents."""
-    np_ = -(-max_context_len // partition_size)
-    rows = num_seqs * num_heads * np_
-    sec = -(-rows * 4 // 256) * 256
+    offs = np.zeros(3, dtype=np.int64)
+    nparts = ctypes.c_int32(0)
+    check(lib().pa_split_workspace_layout(num_seqs, num_heads, head_size, max_context_len,
+                                          partition_size,
+                                          offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                          ctypes.byref(nparts)))
+    shape = (num_seqs, num_heads, nparts.value)
     f = workspace.view(torch.uint8)
-    mx = f[:rows * 4].view(torch.float32).view(num_seqs, num_heads, np_)
-    sm = f[sec:sec + rows * 4].view(torch.float32).view(num_seqs, num_heads, np_)
-    to = f[2 * sec:2 * sec + rows * head_size * 4].view(torch.float32)
-    return mx, sm, to.view(num_seqs, num_heads, np_, head_size)
+
+    def section(i, per_part):
+        n = int(np.prod(shape)) * per_part * 4
+        return f[int(offs[i]):int(offs[i]) + n].view(torch.float32)
+
+    return (section(0, 1).view(shape), section(1, 1).view(shape),
+            section(2, head_size).view(*shape, head_size))
 
 
 def _shared_ptr(shared_prefix_blocks, S):
@@ -350,6 +357,20 @@ def query_blocks(context_lens, query_start_loc, max_block: int):
                                 row_lens.ctypes.data_as(p32), row_qsl.ctypes.data_as(p32), n,
                                 ctypes.byref(rows)))
     return row_seq, row_lens, row_qsl
+
+
+def query_block_hints(row_seq, row_lens, seq_shared_blocks, block_size: int) -> np.ndarray:
+    """Shared-block cache hints of query-block rows (pa_query_block_hints):
+    int32 [num_rows]."""
+    rs = np.ascontiguousarray(np.asarray(row_seq, dtype=np.int32))
+    rl = np.ascontiguousarray(np.asarray(row_lens, dtype=np.int32))
+    sh = np.ascontiguousarray(np.asarray(seq_shared_blocks, dtype=np.int32))
+    out = np.empty(rs.size, dtype=np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    check(lib().pa_query_block_hints(rs.ctypes.data_as(p32), rl.ctypes.data_as(p32), rs.size,
+                                     sh.ctypes.data_as(p32), sh.size, block_size,
+                                     out.ctypes.data_as(p32)))
+    return out
 
 
 def prefill_block_tokens(num_heads: int, num_kv_heads: int) -> int:

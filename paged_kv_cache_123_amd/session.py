@@ -94,27 +94,24 @@ class PagedKVCache:
             raise ValueError("cascade plans take one query per sequence")
         if key.shape[0] != T or value.shape[0] != T:
             raise ValueError("key/value must hold the new tokens of every sequence in order")
-        # host: release what the window left behind, then allocate
-        qsl, cow_src, cow_pairs, positions = [0], [], [], []
-        for s, k in zip(seqs, n):
-            if k < 1:
-                raise ValueError("every sequence of a step appends at least one token")
-            start = self.pool.seq_len(s)
-            if self.sliding_window:
-                self.pool.remove_skipped(s, start, self.sliding_window)
-            _, pair = self.pool.append(s, k)
-            qsl.append(qsl[-1] + k)
-            cow_src.append(-1 if pair is None else pair[0])
-            if pair is not None:
-                cow_pairs.append(pair)
-            positions.extend(range(start, start + k))
+        for name, t in (("key", key), ("value", value)):
+            if tuple(t.shape[1:]) != (self.num_kv_heads, self.head_size) or t.dtype != self.dtype:
+                raise ValueError(f"{name} must be [T, num_kv_heads, head_size] of the cache dtype")
+        if (query.dim() != 3 or query.shape[2] != self.head_size or query.dtype != self.dtype
+                or query.shape[1] % self.num_kv_heads):
+            raise ValueError("query must be [rows, num_heads, head_size] of the cache dtype, "
+                             "num_heads a multiple of num_kv_heads")
+        # host: every row releases what its window left behind, then
+        # allocates; the batch fits as a whole or leaves the pool unchanged
+        batch = self.pool.append_batch(seqs, n, self.sliding_window)
+        qsl, cow_src, cow_pairs = batch.query_start_loc, batch.cow_src, batch.cow_pairs
+        positions = batch.positions
         width = max(self.pool.seq_num_blocks(s) for s in seqs)
         tables, lens = self.pool.block_tables(seqs, width)
-        shared = self.pool.shared_prefix_blocks(seqs)
+        shared = batch.shared_blocks
         dev = self.device
-        # readers of one shared prefix (same first live block) run together
-        first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
-        groups = np.where(shared > 0, first, self.num_blocks + np.arange(len(seqs)))
+        # readers of one shared prefix run together (a key per prefix)
+        groups = batch.group_keys
         widest = 0  # members of the widest cascade group of the step
         if all_queries:
             H, D = query.shape[1], query.shape[2]
@@ -132,8 +129,8 @@ class PagedKVCache:
             plan = ops.decode_plan(lens, self.partition_size, self.sliding_window,
                                    n if all_queries else None, groups)
         t = {name: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for name, a in (
-            ("tables", tables), ("lens", lens), ("qsl", np.asarray(qsl, dtype=np.int32)),
-            ("cow_src", np.asarray(cow_src, dtype=np.int64)), ("plan", plan))}
+            ("tables", tables), ("lens", lens), ("qsl", qsl), ("cow_src", cow_src),
+            ("plan", plan))}
         out = torch.empty_like(query)
         workspace = None
         if self.partition_size:
@@ -165,7 +162,7 @@ class PagedKVCache:
         dev = self.device
         T = len(positions)
         tab = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
-        qsl_host = np.asarray(qsl, dtype=np.int32)
+        qsl_host = qsl
         out = torch.empty_like(query)
         H = query.shape[1]
         max_len = int(lens.max())
@@ -176,23 +173,20 @@ class PagedKVCache:
                              torch.from_numpy(row_seq).to(dev), torch.from_numpy(row_lens).to(dev),
                              torch.from_numpy(row_qsl).to(dev), scale, max_len,
                              torch.from_numpy(qsl_host).to(dev), key, value,
-                             torch.tensor(cow_src, dtype=torch.int64, device=dev), None, None,
+                             torch.from_numpy(cow_src).to(dev), None, None,
                              self.sliding_window)
             return out
-        if cow_pairs:
-            ops.copy_blocks(self.key_cache, self.value_cache,
-                            torch.tensor(cow_pairs, dtype=torch.int64, device=dev))
+        if len(cow_pairs):
+            ops.copy_blocks(self.key_cache, self.value_cache, torch.from_numpy(cow_pairs).to(dev))
         slots = torch.empty(T, dtype=torch.int64, device=dev)
         ops.compute_slot_mapping(torch.from_numpy(qsl_host).to(dev),
-                                 torch.tensor(positions, dtype=torch.int64, device=dev), tab,
-                                 self.block_size, slots, T)
+                                 torch.from_numpy(positions).to(dev), tab, self.block_size, slots,
+                                 T)
         ops.reshape_and_cache(key, value, self.key_cache, self.value_cache, slots)
         block = (16 if matrix else 8) // (H // self.num_kv_heads)
         row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl_host, block)
-        rows_per_seq = np.bincount(row_seq, minlength=len(lens))
         # a sequence cut into several rows has all of its blocks read by each
-        row_shared = np.where(rows_per_seq[row_seq] > 1, -(-row_lens // self.block_size),
-                              shared[row_seq]).astype(np.int32)
+        row_shared = ops.query_block_hints(row_seq, row_lens, shared, self.block_size)
         plan = ops.decode_plan(row_lens, self.partition_size, self.sliding_window,
                                np.diff(row_qsl), row_seq)
         workspace = None

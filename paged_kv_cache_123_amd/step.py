@@ -27,19 +27,20 @@ from . import ops
 from .host import Pool
 
 
-def replay(pool: Pool, history, appends, sliding_window: int = 0):
+def replay(pool: Pool, history, appends, sliding_window: int = 0,
+           blocks_per_kv_block: int = 1):
     """Run a batch's history and then the step's appends through ``pool``.
-    With a sliding window, each row first releases the blocks its next query
-    can no longer see ([CSDN] sections 3.1.1 and 3.3.1).  History operations:
-    ("add", s), ("append", s, n), ("fork", parent, child), ("free", s), and
-    ("request", s, prompt_token_ids, extra_key_bytes): a request served
-    through the prefix cache (its longest cached prefix is taken over, the
-    rest of the prompt appended, and its full blocks cached).
+    History operations: ("add", s), ("append", s, n), ("fork", parent, child),
+    ("free", s), and ("request", s, prompt_token_ids, extra_key_bytes): a
+    request served through the prefix cache (its longest cached prefix is
+    taken over, the rest of the prompt appended, and its full blocks cached).
+    The step's appends, (s, n) per batch row, go through the allocator as one
+    batch (pa_pool_append_batch): with a sliding window each row first
+    releases the blocks its next query can no longer see ([CSDN] sections
+    3.1.1 and 3.3.1), and the batch fits as a whole or changes nothing.
 
-    Returns (seqs, positions, query_start_loc, cow_pairs, cow_src): the batch
-    rows, the position of every new token, the row boundaries of the new
-    tokens, the (src, dst) copy-on-write pairs, and per row the source block
-    of its copy-on-write (-1 for none)."""
+    Returns the batch's StepAppends (positions, row boundaries, slots, copy
+    sources and kernel-block copy pairs, shared-prefix hints and group keys)."""
     for op in history:
         if op[0] == "add":
             pool.add_seq(op[1])
@@ -56,19 +57,8 @@ def replay(pool: Pool, history, appends, sliding_window: int = 0):
             pool.cache_full_blocks(s)
         else:
             raise ValueError(f"unknown operation {op!r}")
-    seqs, positions, qsl, cow, cow_src = [], [], [0], [], []
-    for s, n in appends:
-        start = pool.seq_len(s)
-        if sliding_window:
-            pool.remove_skipped(s, start, sliding_window)
-        _, pair = pool.append(s, n)
-        seqs.append(s)
-        positions.extend(range(start, start + n))
-        qsl.append(qsl[-1] + n)
-        cow_src.append(-1 if pair is None else pair[0])
-        if pair is not None:
-            cow.append(pair)
-    return seqs, positions, qsl, cow, cow_src
+    return pool.append_batch([s for s, _ in appends], [n for _, n in appends], sliding_window,
+                             blocks_per_kv_block)
 
 
 class DecodeStep:
@@ -108,13 +98,13 @@ class DecodeStep:
         if any(op[0] == "request" for op in history):
             self.pool.enable_prefix_caching()
         self.sliding_window = int(sliding_window)
-        seqs, positions, qsl, cow, cow_src = replay(self.pool, history, appends,
-                                                    self.sliding_window)
-        self.seqs = seqs
         kb = int(kernel_block_size) or block_size
         if block_size % kb:
             raise ValueError("kernel_block_size must divide block_size")
         k = block_size // kb
+        batch = replay(self.pool, history, appends, self.sliding_window, k)
+        seqs = [s for s, _ in appends]
+        self.seqs = seqs
         self.block_size = kb
         self.kernel_blocks_per_block = k
         width = max(self.pool.seq_num_blocks(s) for s in seqs)
@@ -122,17 +112,17 @@ class DecodeStep:
         self.manager_tables_host = tables
         if k > 1:
             tables = ops.map_to_kernel_blocks(tables, k)
-            cow = [(src * k + j, dst * k + j) for src, dst in cow for j in range(k)]
-            cow_src = [-1 if c < 0 else None for c in cow_src]  # no one-launch copy
         self.tables_host = tables
         self.context_lens_host = lens
-        self.cow_pairs_host = np.asarray(cow, dtype=np.int64).reshape(-1, 2)
-        self.fused_ok = all(c is not None for c in cow_src)
-        self.cow_src_host = np.asarray([-1 if c is None else c for c in cow_src], dtype=np.int64)
-        self.shared_blocks_host = self.pool.shared_prefix_blocks(seqs) * k  # in kernel blocks
-        self.positions_host = np.asarray(positions, dtype=np.int64)
-        self.query_start_loc_host = np.asarray(qsl, dtype=np.int32)
-        self.num_tokens = int(qsl[-1])
+        self.cow_pairs_host = batch.cow_pairs
+        # the one-launch step copies a row's tail from one source block: a
+        # manager block of several kernel blocks needs pa_copy_blocks
+        self.fused_ok = k == 1 or not (batch.cow_src >= 0).any()
+        self.cow_src_host = batch.cow_src if k == 1 else np.full(len(seqs), -1, dtype=np.int64)
+        self.shared_blocks_host = batch.shared_blocks  # in kernel blocks
+        self.positions_host = batch.positions
+        self.query_start_loc_host = batch.query_start_loc
+        self.num_tokens = int(batch.query_start_loc[-1])
         self.max_context_len = int(lens.max())
         self.scale = float(scale)
         self.partition_size = int(partition_size)
@@ -161,10 +151,8 @@ class DecodeStep:
         if self.sliding_window and not planned:
             raise ValueError("a sliding window uses the planned launch")
         query_lens = [n for _, n in appends] if all_queries else None
-        # readers of one shared prefix (same first live block) run together
-        first = tables[np.arange(len(seqs)), np.argmax(tables >= 0, axis=1)]
-        groups = np.where(self.shared_blocks_host > 0, first,
-                          self.pool.num_blocks * k + np.arange(len(seqs)))
+        # readers of one shared prefix run together (a key per prefix)
+        groups = batch.group_keys
         self.cascade = int(cascade)
         self.num_items, self.max_group = 0, 0
         if self.cascade:
@@ -203,18 +191,15 @@ class DecodeStep:
                     block = ops.prefill_block_tokens(H, values["key_cache"].shape[1])
                 row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl, block)
                 row_tables = np.ascontiguousarray(tables[row_seq])
-                rows_per_seq = np.bincount(row_seq, minlength=len(seqs))
-                # every block of a sequence cut into several rows is read by all
-                # of them: cached loads
-                row_shared = np.where(rows_per_seq[row_seq] > 1,
-                                      -(-row_lens // kb), self.shared_blocks_host[row_seq])
+                row_shared = ops.query_block_hints(row_seq, row_lens, self.shared_blocks_host,
+                                                   kb)
                 self.plan_host = ops.decode_plan(row_lens, self.partition_size,
                                                  self.sliding_window, np.diff(row_qsl), row_seq)
                 self.attn_tables = torch.from_numpy(row_tables).to(dev)
                 self.attn_lens = torch.from_numpy(row_lens).to(dev)
                 self.attn_qsl = torch.from_numpy(row_qsl).to(dev)
                 self.attn_max_query_len = int(np.diff(row_qsl).max())
-                self.attn_shared = torch.from_numpy(row_shared.astype(np.int32)).to(dev)
+                self.attn_shared = torch.from_numpy(row_shared).to(dev)
                 self.row_seq = torch.from_numpy(row_seq).to(dev)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self._fused_call = None  # the one-launch step's marshalled arguments

@@ -51,6 +51,12 @@ CASES = [
     ("pa_paged_attention_decode_split", _decode() + [4112, P, 1 << 20, None], "at most 4096"),
     ("pa_paged_attention_decode_split", _decode() + [32, None, 0, None], "missing or too small"),
     ("pa_paged_attention_decode_split", _decode() + [32, P, 64, None], "missing or too small"),
+    ("pa_paged_attention_decode_split", _decode(S=1 << 26, H=8, Hkv=8) + [16, P, 1 << 62, None],
+     "num_seqs x num_kv_heads x partitions"),
+    ("pa_paged_attention_decode", _decode(S=1 << 30, H=16, Hkv=2) + [None],
+     "num_seqs x heads exceeds one launch's workgroups"),
+    ("pa_merge_attention_partials", [P, P, P, P, 8, 1 << 30, 16, 128, F16, None],
+     "exceeds one launch's workgroups"),
     ("pa_paged_attention_decode_split", _decode() + [32, P + 16, 1 << 20, None],
      "256-byte aligned"),
     ("pa_paged_attention_decode_planned", _decode() + [0, P, 3, None, P, 1 << 20, -1, None],
@@ -104,8 +110,11 @@ CASES = [
      [P, P, P, P, P, 8, P, P, 2, 9, 4, 2, 128, 16, 100, 1.0, F16, 0, P, 3, None, P, 1 << 20, 4,
       0, None], "max_query_len x (num_heads / num_kv_heads)"),
     ("pa_paged_attention_partials",
-     [P, P, P, P, P, P, P, 8, P, 70000, 4, 2, 128, 16, 100, 1.0, F16, 32, None, 0, None, P,
-      1 << 30, None], "num_seqs > 65535"),
+     [P, P, P, P, P, P, P, 8, P, 1 << 30, 16, 2, 128, 16, 100, 1.0, F16, 32, None, 0, None, P,
+      1 << 30, None], "num_seqs x heads exceeds one launch's workgroups"),
+    ("pa_paged_attention_partials",
+     [P, P, P, P, P, P, P, 8, P, 1 << 26, 8, 8, 128, 16, 100, 1.0, F16, 16, None, 0, None, P,
+      1 << 30, None], "num_seqs x num_kv_heads x partitions"),
     ("pa_paged_attention_partials",
      [None, P, P, P, P, P, P, 8, P, 2, 4, 2, 128, 16, 100, 1.0, F16, 32, None, 0, None, P,
       1 << 30, None], "NULL max_logits or exp_sums"),

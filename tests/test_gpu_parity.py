@@ -135,6 +135,43 @@ def test_growth_example_on_device():
         assert pool.block_table(0) == want_table
 
 
+@pytest.mark.parametrize("world,rank,interleave", [(1, 0, 1), (2, 1, 1), (4, 2, 4), (8, 7, 2)])
+def test_slot_mapping_with_empty_requests_and_padding(world, rank, interleave):
+    """One thread per entry finds its request by a binary search over
+    query_start_loc: requests without tokens (runs of them, first and last
+    included) are skipped, several workgroups of tokens and the padding tail
+    are covered; bit-exact against the oracle's plain and context-parallel
+    mappings."""
+    _require_gpu()
+    from oracle.slots import compute_slot_mapping, compute_slot_mapping_cp
+    from paged_kv_cache_123_amd import ops
+    rng = np.random.default_rng(31 + world)
+    B, S, width = 16, 97, 40
+    counts = rng.integers(0, 12, size=S)
+    counts[:3] = 0
+    counts[-2:] = 0
+    counts[40:50] = 0
+    qsl = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(qsl[-1])
+    tables = rng.permutation(S * width).reshape(S, width).astype(np.int32)
+    positions = np.concatenate(
+        [np.sort(rng.choice(B * width * world, size=c, replace=False)) for c in counts]
+    ).astype(np.int64)
+    print(f"[slots] world={world} rank={rank} I={interleave} T={T}", flush=True)
+    dev = {n: torch.from_numpy(a).to(DEV) for n, a in
+           (("qsl", qsl), ("pos", positions), ("tables", tables))}
+    slots = torch.full((T + 300,), 12345, dtype=torch.int64, device=DEV)
+    if world == 1:
+        ops.compute_slot_mapping(dev["qsl"], dev["pos"], dev["tables"], B, slots, T)
+        want = compute_slot_mapping(qsl, positions, tables, B, T + 300)
+    else:
+        ops.compute_slot_mapping_cp(dev["qsl"], dev["pos"], dev["tables"], B, slots, T, world,
+                                    rank, interleave)
+        want = compute_slot_mapping_cp(qsl, positions, tables, B, T + 300, world, rank,
+                                       interleave)
+    assert to_host(slots).tolist() == want
+
+
 @BOTH
 def test_llama7b_fp16_full_step(decode_kernel):
     full_parity(W.llama7b_fp16())
