@@ -189,7 +189,8 @@ class DecodeStep:
                 self.fused_ok = self.fused_ok and self.prefill_rows
                 if self.prefill_rows:
                     block = ops.prefill_block_tokens(H, values["key_cache"].shape[1])
-                row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl, block)
+                row_seq, row_lens, row_qsl = ops.query_blocks(lens, self.query_start_loc_host,
+                                                              block)
                 row_tables = np.ascontiguousarray(tables[row_seq])
                 row_shared = ops.query_block_hints(row_seq, row_lens, self.shared_blocks_host,
                                                    kb)
