@@ -252,6 +252,32 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pa_paged_attention_decode_split without the workspace arguments.  The
+ * split workspace is a static device array of PA_NOALLOC_WORKSPACE_BYTES
+ * inside the library (each GPU the library runs on holds one until the
+ * process ends); the call allocates nothing and calls no allocating routine.
+ * The caller still passes inputs and outputs, as for
+ * pa_paged_attention_decode_split, and gets the same result bit for bit.
+ * The array keeps the last call's partials; nothing needs clearing (every
+ * partition a merge reads is written first).  Calls that overlap on one GPU
+ * (two streams, or two threads) share the array and race: serialise them.
+ * Errors: as pa_paged_attention_decode_split, plus PA_EINVAL when
+ * pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+ * partition_size) exceeds PA_NOALLOC_WORKSPACE_BYTES (checked before any
+ * device call) or the current device index is 64 or more; PA_ELAUNCH when
+ * the array's device address cannot be found on the current device.
+ * ---------------------------------------------------------------------- */
+#define PA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int32_t pa_paged_attention_decode_split_noalloc(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t partition_size, void* stream);
+
+/* ------------------------------------------------------------------------
  * Planned launch (load balance).  The two calls above launch one workgroup
  * per (sequence, KV head[, partition]) in index order, including partitions
  * past a sequence's end.  With lengths that vary a lot, a launch that starts

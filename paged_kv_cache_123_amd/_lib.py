@@ -48,6 +48,9 @@ SIGNATURES = {
     "pa_paged_attention_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                                _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                _sz, _vp]),
+    "pa_paged_attention_decode_split_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
+                                                       _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                                       _i32, _vp]),
     "pa_decode_plan": (_i32, [_pi32, _i32, _i32, _pi32, _i64, _pi64]),
     "pa_decode_plan_window": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _i32, _pi32, _i64,
                                      _pi64]),

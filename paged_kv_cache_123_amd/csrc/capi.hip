@@ -5,6 +5,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -123,6 +124,35 @@ int32_t check_query_capacity(const char* who, int32_t max_query_len, int32_t num
     return fail(PA_EINVAL, (std::string(who) + ": max_query_len x (num_heads / num_kv_heads) "
                             "must be at most 16 (16-bit storage, head_size 128) or 8")
                                .c_str());
+  return PA_OK;
+}
+
+// Split-K workspace of pa_paged_attention_decode_split_noalloc: a static
+// device array, so that launch needs no allocation.  Each GPU the library
+// runs on holds its own copy until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in): the
+// device address of the current GPU's copy is looked up once per device
+// with hipGetSymbolAddress and kept here.
+static __device__ __align__(256) char scratch[PA_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t noalloc_workspace(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launched(e, who);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_EINVAL, (std::string(who) + ": device index beyond 63").c_str());
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return launched(e != hipSuccess ? e : hipErrorInvalidSymbol, who);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return PA_OK;
 }
 
@@ -262,6 +292,53 @@ int32_t pa_split_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t h
   return PA_OK;
 }
 
+static int32_t decode_split_impl(const char* who, void* out, const void* query,
+                                 const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, int64_t bt_stride,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                 int32_t block_size, int32_t max_context_len, float scale,
+                                 int32_t dtype, int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, bool static_workspace, void* stream) {
+  const std::string w(who);
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, (w + ": partition_size must be a multiple of 16 and of block_size, "
+                                "at most 4096").c_str());
+  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                               partition_size);
+  if (static_workspace) {
+    if (need > PA_NOALLOC_WORKSPACE_BYTES)
+      return fail(PA_EINVAL, (w + ": the split workspace of this launch exceeds the library's "
+                                  "static PA_NOALLOC_WORKSPACE_BYTES").c_str());
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_EINVAL, (w + ": workspace missing or too small").c_str());
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(PA_EINVAL, (w + ": workspace must be 256-byte aligned").c_str());
+  }
+  st = check_split_grid(who, num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (st != PA_OK) return st;
+  if (static_workspace) {  // every host check passed: now the device's array
+    st = noalloc_workspace(who, &workspace);
+    if (st != PA_OK) return st;
+  }
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale,
+                   dtype, nullptr, nullptr, nullptr, nullptr, 0};
+  set_split(a, workspace,
+            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launched(pa::launch_decode(a, s), (w + " (partition)").c_str());
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), (w + " (reduce)").c_str());
+}
+
 int32_t pa_paged_attention_decode_split(void* out, const void* query, const void* key_cache,
                                         const void* value_cache, const int32_t* block_tables,
                                         int64_t bt_stride, const int32_t* context_lens,
@@ -270,35 +347,22 @@ int32_t pa_paged_attention_decode_split(void* out, const void* query, const void
                                         int32_t block_size, int32_t max_context_len,
                                         float scale, int32_t dtype, int32_t partition_size,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  int32_t st = check_decode("pa_paged_attention_decode_split", out, query, key_cache,
-                            value_cache, block_tables, bt_stride, context_lens, num_seqs,
-                            num_heads, num_kv_heads, head_size, block_size, max_context_len,
-                            dtype);
-  if (st != PA_OK) return st;
-  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
-      partition_size % block_size != 0)
-    return fail(PA_EINVAL,
-                "pa_paged_attention_decode_split: partition_size must be a multiple of 16 and "
-                "of block_size, at most 4096");
-  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
-                                               partition_size);
-  if (!workspace || workspace_bytes < need)
-    return fail(PA_EINVAL, "pa_paged_attention_decode_split: workspace missing or too small");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(PA_EINVAL, "pa_paged_attention_decode_split: workspace must be 256-byte aligned");
-  st = check_split_grid("pa_paged_attention_decode_split", num_seqs, num_kv_heads,
-                        max_context_len, partition_size);
-  if (st != PA_OK) return st;
-  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
-                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale,
-                   dtype, nullptr, nullptr, nullptr, nullptr, 0};
-  set_split(a, workspace,
-            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
-            partition_size);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launched(pa::launch_decode(a, s), "pa_paged_attention_decode_split (partition)");
-  if (st != PA_OK) return st;
-  return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_split (reduce)");
+  return decode_split_impl("pa_paged_attention_decode_split", out, query, key_cache, value_cache,
+                           block_tables, bt_stride, context_lens, num_seqs, num_heads,
+                           num_kv_heads, head_size, block_size, max_context_len, scale, dtype,
+                           partition_size, workspace, workspace_bytes, false, stream);
+}
+
+int32_t pa_paged_attention_decode_split_noalloc(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t partition_size, void* stream) {
+  return decode_split_impl("pa_paged_attention_decode_split_noalloc", out, query, key_cache,
+                           value_cache, block_tables, bt_stride, context_lens, num_seqs,
+                           num_heads, num_kv_heads, head_size, block_size, max_context_len, scale,
+                           dtype, partition_size, nullptr, 0, true, stream);
 }
 
 int32_t pa_paged_attention_decode_planned(

@@ -245,6 +245,21 @@ def paged_attention_decode_split(out: torch.Tensor, query: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream()))
 
 
+def paged_attention_decode_split_noalloc(out: torch.Tensor, query: torch.Tensor,
+                                         key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                         block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                         scale: float, max_context_len: int,
+                                         partition_size: int) -> None:
+    """Split-K decode whose workspace is the library's static device array
+    (pa_paged_attention_decode_split_noalloc): nothing is allocated."""
+    S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
+                                   context_lens)
+    check(lib().pa_paged_attention_decode_split_noalloc(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
+        B, max_context_len, scale, _dtype(key_cache), partition_size, _stream()))
+
+
 def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head_size: int,
                     max_context_len: int, partition_size: int):
     """(max_logits [S,H,NP], exp_sums [S,H,NP], tmp_out [S,H,NP,D]) views of a

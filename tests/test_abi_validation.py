@@ -53,6 +53,11 @@ CASES = [
     ("pa_paged_attention_decode_split", _decode() + [32, P, 64, None], "missing or too small"),
     ("pa_paged_attention_decode_split", _decode(S=1 << 26, H=8, Hkv=8) + [16, P, 1 << 62, None],
      "num_seqs x num_kv_heads x partitions"),
+    ("pa_paged_attention_decode_split_noalloc",
+     _decode(S=512, H=64, Hkv=8, max_len=32768, bt_stride=2048) + [512, None],
+     "exceeds the library's static PA_NOALLOC_WORKSPACE_BYTES"),
+    ("pa_paged_attention_decode_split_noalloc", _decode() + [24, None],
+     "partition_size must be a multiple of 16"),
     ("pa_paged_attention_decode", _decode(S=1 << 30, H=16, Hkv=2) + [None],
      "num_seqs x heads exceeds one launch's workgroups"),
     ("pa_merge_attention_partials", [P, P, P, P, 8, 1 << 30, 16, 128, F16, None],
