@@ -553,6 +553,255 @@ def main_cp(args, w):
     print(json.dumps(result), flush=True)
 
 
+# The default run also times these workloads after the metric's own, each
+# with its own timed region and roofline (extra keys of the one JSON line):
+# the other decode configuration the roofline target names, the long-context
+# split-K batch and the shared-prefix batch (on the plan the step chooses).
+EXTRA_WORKLOADS = ("qwen72b_gqa_bf16", "long_context_bf16", "shared_prefix_bf16")
+# Residency control: a step whose working set is below this many bytes is
+# timed on several device copies of its pool and tables in turn, so that no
+# repetition finds the previous one's rows in the 256 MB Infinity Cache.
+RESIDENCY_BYTES = 1 << 30
+DISTRIBUTION_LAUNCHES = 50
+
+
+def replicas(step, n: int):
+    """``n`` steps over independent device copies of the same pool, tables
+    and inputs (the first is ``step`` itself)."""
+    import copy
+
+    import torch
+    out = [step]
+    for _ in range(n - 1):
+        c = copy.copy(step)
+        memo = {}
+        for name, t in vars(step).items():
+            if isinstance(t, torch.Tensor):
+                # tensors that alias each other in the step alias in the copy
+                key = (t.data_ptr(), tuple(t.shape), t.dtype)
+                if key not in memo:
+                    memo[key] = t.clone()
+                setattr(c, name, memo[key])
+        c._fused_call = None
+        out.append(c)
+    return out
+
+
+def num_replicas(working_set: int) -> int:
+    if working_set >= 2 * RESIDENCY_BYTES:
+        return 1
+    return max(2, -(-RESIDENCY_BYTES // max(working_set, 1)))
+
+
+def time_step(steps, fused: bool, K: int, warmup: int):
+    """Warm-up, then K timed steps (HIP events around the whole region, no
+    events between steps), then a distribution pass of at least
+    DISTRIBUTION_LAUNCHES steps with HIP events around each launch (the
+    one-launch step, or the attention call of the separate calls).  Steps
+    cycle over the replicas.  Returns (ms per step, wall seconds of the timed
+    region, per-launch milliseconds of the distribution pass)."""
+    import torch
+
+    R = len(steps)
+
+    def one(i, ev=None):
+        st = steps[i % R]
+        if fused:
+            if ev is not None:
+                ev[0].record()
+            st.fused()
+            if ev is not None:
+                ev[1].record()
+        else:
+            st.copy_blocks()
+            st.slot_mapping_kernel()
+            st.scatter()
+            if ev is not None:
+                ev[0].record()
+            st.attention()
+            if ev is not None:
+                ev[1].record()
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        one(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / K
+    n = max(K, DISTRIBUTION_LAUNCHES)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        one(i, evs[i])
+    torch.cuda.synchronize()
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    return ms_per_step, wall, launch_ms
+
+
+def kernel_label(w, step, args, part, fused) -> str:
+    cascade = step.cascade
+    return (("prefill_kernel (query blocks)" if step.prefill_rows else
+             "cascade_decode_kernel" if cascade and not part else
+             "paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
+                 args.kernel == "auto" and w.dtype != "f32" and w.head_size == 128
+                 and (w.num_heads > w.num_kv_heads or step.attn_max_query_len > 1)))
+             else "paged_decode_kernel")
+            + (" + merge_kernel" if part else "")
+            + (" (cascade plan)" if cascade else "")
+            + (" (one-launch step: copy-on-write + scatter + attention)" if fused else ""))
+
+
+def measure(args, w, cascade_arg=None):
+    """One workload's step on resident inputs: returns (result dict, step,
+    values) where the result holds value, ms_per_step, roofline and the
+    per-launch statistics."""
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_123_amd.step import DecodeStep
+
+    part = w.partition_size if args.partition_size is None else args.partition_size
+    vals = W.make_values(w, "cuda")
+    step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
+                      w.scale, part, all_queries=w.extra.get("queries") == "all",
+                      sliding_window=window_of(w),
+                      kernel_block_size=w.extra.get("kernel_block_size", 0),
+                      cascade=cascade_arg, prefill_kernel=not args.no_prefill_kernel)
+    torch.cuda.synchronize()
+    # steps whose cache writes must precede the attention (query blocks of a
+    # prefill chunk on the decode kernels; copy-on-write of blocks of several
+    # kernel blocks) run as separate calls
+    fused = not args.unfused and step.fused_ok
+    attn_bytes = (fused_bytes(w, step) if fused
+                  else attention_bytes(w, step.context_lens_host, _query_rows(step),
+                                       _query_lens(step), step.tables_host))
+    R = 1 if args.no_residency_control else num_replicas(step_bytes(w, step))
+    steps = replicas(step, R)
+    torch.cuda.synchronize()
+    ms_per_step, wall, launch_ms = time_step(steps, fused, args.steps, args.warmup)
+    # A one-launch step without partitions is a single kernel: its mean
+    # launch duration is the timed region over K, which has no events between
+    # launches.  Otherwise the mean of the per-launch events.
+    single_kernel = fused and part == 0
+    attn_avg_ms = ms_per_step if single_kernel else float(np.mean(launch_ms))
+    attn_stats = {
+        "mean": attn_avg_ms,
+        "median": float(np.median(launch_ms)),
+        "p10": float(np.percentile(launch_ms, 10)),
+        "p90": float(np.percentile(launch_ms, 90)),
+        "launches": len(launch_ms),
+        "mean_of_launch_events": float(np.mean(launch_ms)),
+        "note": ("mean: the timed region over the steps (one kernel launch per step); median, "
+                 "p10, p90: HIP events around each launch of a separate pass"
+                 if single_kernel else
+                 "HIP events around each attention launch of a separate pass"),
+    }
+    kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    flops = attention_flops(w, step.context_lens_host, _query_lens(step))
+    mpeak = MATRIX_PEAK_TFLOPS[w.dtype]
+    # the bound: HBM, or the matrix cores when the flops per algorithmic byte
+    # exceed the ridge (several queries per token row: prefill chunks)
+    compute_bound = flops / attn_bytes > mpeak * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    cascade = step.cascade
+    result = {
+        "value": kv_tokens / (ms_per_step * 1e-3),
+        "unit": "KV tokens/s",
+        "ms_per_step": ms_per_step,
+        "dtype": w.dtype,
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_size": w.head_size,
+            "block_size": w.block_size,
+            "kv_tokens": kv_tokens,
+            "max_context_len": int(step.max_context_len),
+            "num_blocks": w.num_blocks,
+            "partition_size": part,
+            "cascade_group": cascade,
+            "cascade_group_items": int((step.plan_host[:2 * step.num_items:2] < 0).sum())
+            if cascade else 0,
+            "attention_kernel": args.kernel,
+            "fused_step": fused,
+            "cow_copies": int(len(step.cow_pairs_host)),
+            "step_tokens": int(step.num_tokens),
+            "queries_per_sequence": step.max_query_len or 1,
+            "sliding_window": window_of(w),
+            "context_tokens": int(step.context_lens_host.sum()),
+            "pool_copies_in_rotation": R,
+        },
+        "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
+        "attention_ms": attn_stats,
+        "roofline": {
+            "bound": "mfma" if compute_bound else "hbm",
+            "kernel": kernel_label(w, step, args, part, fused),
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": pmc_traffic(w.name, attn_bytes),
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "algorithmic_flops_per_launch": flops,
+        },
+        "wall_s_timed_region": wall,
+    }
+    if compute_bound:
+        tflops = flops / (attn_avg_ms * 1e-3) / 1e12
+        result["roofline"].update({
+            "achieved": tflops, "peak": mpeak, "unit": "TFLOP/s", "frac": tflops / mpeak,
+            "hbm_gbps": achieved, "hbm_frac": achieved / HBM_PEAK_GBPS})
+    del steps
+    return result, step, vals
+
+
+def cache_kernels(step, w, reps: int = 50) -> dict:
+    """The integer and copy kernels of a step on their own (slot mapping,
+    scatter, copy_blocks), each timed with HIP events over ``reps`` launches:
+    GB/s over their algorithmic bytes (slot mapping 20 B per token: position,
+    table entry and slot; scatter a read and a write of each new K/V row;
+    copy_blocks a read and a write of every K and V block of each pair)."""
+    import torch
+    T = step.num_tokens
+    row = w.num_kv_heads * w.head_size * w.elem_bytes
+    blk = w.num_kv_heads * step.block_size * w.head_size * w.elem_bytes
+    jobs = {"compute_slot_mapping": (step.slot_mapping_kernel, 20 * T, f"{T} tokens"),
+            "reshape_and_cache": (step.scatter, 4 * row * T, f"{T} tokens x {row * 2} B"),
+            "copy_blocks": (step.copy_blocks, 4 * blk * len(step.cow_pairs_host),
+                            f"{len(step.cow_pairs_host)} pairs of {blk} B blocks")}
+    out = {}
+    for name, (fn, nbytes, what) in jobs.items():
+        if nbytes == 0:
+            continue
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        out[name] = {"us": us, "algorithmic_bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
+                     "frac_of_8tbps": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "what": what}
+    return out
+
+
+def compact(res: dict) -> dict:
+    """The keys of an extra workload's entry in the JSON line."""
+    keep = ("value", "unit", "ms_per_step", "dtype", "config", "step_hbm_gbps", "attention_ms",
+            "roofline", "cache_kernels")
+    return {k: res[k] for k in keep if k in res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -565,12 +814,17 @@ def main():
                     help="attention kernel (auto: matrix cores for grouped-query heads)")
     ap.add_argument("--cascade", type=int, default=None,
                     help="cascade plan with groups of at most N sharers (0: off; default: "
-                         "the workload's)")
+                         "the workload's, else the step's own choice)")
     ap.add_argument("--no-prefill-kernel", action="store_true",
                     help="attend prefill chunks as 16-token query blocks on the decode kernels")
     ap.add_argument("--unfused", action="store_true",
                     help="time copy_blocks, slot mapping, scatter and attention as four launches "
                          "instead of the one-launch step")
+    ap.add_argument("--no-residency-control", action="store_true",
+                    help="time one copy of the pool even when its working set fits the caches")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only --workload (the default run also times the extra "
+                         "workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cpu-workers", type=int, default=None,
@@ -600,7 +854,6 @@ def main():
 
     import workloads as W
     from paged_kv_cache_123_amd import ops
-    from paged_kv_cache_123_amd.step import DecodeStep
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_counters:
@@ -615,147 +868,24 @@ def main():
             pool.join()
         main_cp(args, w)
         return
-    part = w.partition_size if args.partition_size is None else args.partition_size
-    cascade = int(w.extra.get("cascade", 0) if args.cascade is None else args.cascade)
+    cascade_arg = w.extra.get("cascade") if args.cascade is None else args.cascade
     print(f"[bench] workload {w.name}: {w.notes}", file=sys.stderr, flush=True)
-    vals = W.make_values(w, "cuda")
-    step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
-                      w.scale, part, all_queries=w.extra.get("queries") == "all",
-                      sliding_window=window_of(w),
-                      kernel_block_size=w.extra.get("kernel_block_size", 0), cascade=cascade,
-                      prefill_kernel=not args.no_prefill_kernel)
-    torch.cuda.synchronize()
-
-    # steps whose cache writes must precede the attention (query blocks of a
-    # prefill chunk; copy-on-write of blocks of several kernel blocks) run as
-    # separate calls
-    fused = not args.unfused and step.fused_ok
-    # A one-launch step without partitions is a single kernel: its average
-    # launch duration is the timed region over K, and per-launch events would
-    # only add their own gaps.  Otherwise events bracket every attention launch.
-    per_launch = not (fused and part == 0)
-    for _ in range(args.warmup):
-        step.run(fused=fused)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    a_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    a_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        if fused:
-            if per_launch:
-                a_start[i].record(stream)
-            step.fused()
-            if per_launch:
-                a_end[i].record(stream)
-        else:
-            step.copy_blocks()
-            step.slot_mapping_kernel()
-            step.scatter()
-            a_start[i].record(stream)
-            step.attention()
-            a_end[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    if per_launch:
-        attn_ms = [a.elapsed_time(b) for a, b in zip(a_start, a_end)]
-        attn_stats = {"mean": float(np.mean(attn_ms)), "p10": float(np.percentile(attn_ms, 10)),
-                      "p90": float(np.percentile(attn_ms, 90))}
-    else:
-        attn_stats = {"mean": ms_per_step, "p10": None, "p90": None,
-                      "note": "one kernel launch per step: the timed region over the steps"}
-    attn_avg_ms = attn_stats["mean"]
-
-    kv_tokens = sum(L - lo for lo, L in attended(w, step.context_lens_host, _query_lens(step)))
-    attn_bytes = (fused_bytes(w, step) if fused
-                  else attention_bytes(w, step.context_lens_host, _query_rows(step),
-                                       _query_lens(step), step.tables_host))
-    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
-    value = kv_tokens / (ms_per_step * 1e-3)
-    # the bound: HBM, or the matrix cores when the flops per algorithmic byte
-    # exceed the ridge (several queries per token row: prefill chunks)
-    flops = attention_flops(w, step.context_lens_host, _query_lens(step))
-    mpeak = MATRIX_PEAK_TFLOPS[w.dtype]
-    compute_bound = flops / attn_bytes > mpeak * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    result = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "KV tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "num_seqs": w.num_seqs,
-            "num_heads": w.num_heads,
-            "num_kv_heads": w.num_kv_heads,
-            "head_size": w.head_size,
-            "block_size": w.block_size,
-            "kv_tokens": kv_tokens,
-            "max_context_len": int(step.max_context_len),
-            "num_blocks": w.num_blocks,
-            "partition_size": part,
-            "cascade_group": cascade,
-            "cascade_group_items": int((step.plan_host[:2 * step.num_items:2] < 0).sum())
-            if cascade else 0,
-            "attention_kernel": args.kernel,
-            "fused_step": fused,
-            "cow_copies": int(len(step.cow_pairs_host)),
-            "step_tokens": int(step.num_tokens),
-            "queries_per_sequence": step.max_query_len or 1,
-            "sliding_window": window_of(w),
-            "context_tokens": int(step.context_lens_host.sum()),
-        },
-        "step_hbm_gbps": step_bytes(w, step) / (ms_per_step * 1e-3) / 1e9,
-        "attention_ms": attn_stats,
-        "roofline": {
-            "bound": "mfma" if compute_bound else "hbm",
-            "kernel": ("prefill_kernel (query blocks)" if step.prefill_rows else
-                       "cascade_decode_kernel" if cascade and not part else
-                       "paged_decode_mfma_kernel" if (cascade or args.kernel == "mfma" or (
-                           args.kernel == "auto" and w.dtype != "f32" and w.head_size == 128
-                           and (w.num_heads > w.num_kv_heads or step.attn_max_query_len > 1)))
-                       else "paged_decode_kernel")
-                      + (" + merge_kernel" if part else "")
-                      + (" (cascade plan)" if cascade else "")
-                      + (" (one-launch step: copy-on-write + scatter + attention)" if fused
-                         else ""),
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": pmc_traffic(w.name, attn_bytes),
-            "algorithmic_bytes_per_launch": attn_bytes,
-            "algorithmic_flops_per_launch": flops,
-        },
-        "wall_s_timed_region": wall,
-    }
-    if compute_bound:
-        tflops = flops / (attn_avg_ms * 1e-3) / 1e12
-        result["roofline"].update({
-            "achieved": tflops, "peak": mpeak, "unit": "TFLOP/s", "frac": tflops / mpeak,
-            "hbm_gbps": achieved, "hbm_frac": achieved / HBM_PEAK_GBPS})
+    res, step, vals = measure(args, w, cascade_arg)
+    result = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": res["dtype"], "data": "synthetic"}
+    result.update({k: v for k, v in res.items() if k not in result and k != "unit"})
     if any(op[0] == "request" for op in w.prefill):
         result["host_prefix_cache"] = time_prefix_cache(w)
+    if step.num_tokens > w.num_seqs or len(step.cow_pairs_host):
+        result["cache_kernels"] = cache_kernels(step, w)
     if not args.no_read_reference:
         ref = read_reference()
         result["read_reference_gbps"] = ref
         best = max(ref["random_4k"], ref["random_4k_nt"])
-        result["roofline"]["frac_of_random_4k_read"] = achieved / best
+        result["roofline"]["frac_of_random_4k_read"] = result["roofline"]["achieved"] / best \
+            if result["roofline"]["unit"] == "GB/s" else None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         single = cpu_baseline(w, vals, step, args.cpu_budget)
@@ -767,6 +897,20 @@ def main():
     if pool is not None:
         pool.close()
         pool.join()
+    del step, vals
+    torch.cuda.empty_cache()
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extras:
+        extras = {}
+        for name in EXTRA_WORKLOADS:
+            we = W.make(name)
+            print(f"[bench] extra workload {we.name}: {we.notes}", file=sys.stderr, flush=True)
+            r, st, v = measure(args, we, we.extra.get("cascade"))
+            if st.num_tokens > we.num_seqs or len(st.cow_pairs_host):
+                r["cache_kernels"] = cache_kernels(st, we)
+            extras[name] = compact(r)
+            del st, v
+            torch.cuda.empty_cache()
+        result["extra_workloads"] = extras
     print(json.dumps(result), flush=True)
 
 

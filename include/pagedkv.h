@@ -380,6 +380,13 @@ int32_t pa_decode_plan_cascade(const int32_t* context_lens, const int32_t* block
                                int32_t block_size, int32_t partition_size,
                                int32_t max_group_size, int32_t* plan, int64_t capacity,
                                int64_t* num_items, int64_t* plan_len, int32_t* max_members);
+/* Host: the widest max_group_size the cascade calls take for this shape,
+ * members x (num_heads / num_kv_heads) <= 16 (the matrix cores' columns of a
+ * group item), at most 8; 0 for fp32 storage or a head_size other than 128,
+ * which have no group-item kernels.  *group receives it.  PA_EINVAL for a
+ * null group or bad head counts. */
+int32_t pa_cascade_max_group(int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                             int32_t dtype, int32_t* group);
 
 int32_t pa_paged_attention_decode_planned(void* out, const void* query, const void* key_cache,
                                           const void* value_cache, const int32_t* block_tables,

@@ -283,3 +283,17 @@ extern "C" int32_t pa_query_block_hints(const int32_t* row_seq, const int32_t* r
   }
   return PA_OK;
 }
+
+// Members whose decode queries fill the matrix cores' 16 columns of a group
+// item: 16 / (num_heads / num_kv_heads), at most 8; 0 where the group items'
+// kernels do not exist (fp32 storage, head_size other than 128).
+extern "C" int32_t pa_cascade_max_group(int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_size, int32_t dtype, int32_t* group) {
+  if (!group || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0)
+    return pa::fail(PA_EINVAL, "pa_cascade_max_group: bad arguments");
+  const int32_t g = num_heads / num_kv_heads;
+  *group = ((dtype == PA_F16 || dtype == PA_BF16) && head_size == 128 && g <= 16)
+               ? std::min(8, 16 / g)
+               : 0;
+  return PA_OK;
+}

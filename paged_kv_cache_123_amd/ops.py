@@ -374,6 +374,17 @@ def query_blocks(context_lens, query_start_loc, max_block: int):
     return row_seq, row_lens, row_qsl
 
 
+def cascade_max_group(num_heads: int, num_kv_heads: int, head_size: int, dtype) -> int:
+    """Widest group a cascade plan may take for this shape (pa_cascade_max_group);
+    ``dtype`` is a torch dtype or "f32" / "f16" / "bf16"."""
+    code = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}.get(dtype) if isinstance(
+        dtype, str) else {torch.float32: PA_F32, torch.float16: PA_F16,
+                          torch.bfloat16: PA_BF16}[dtype]
+    g = ctypes.c_int32(0)
+    check(lib().pa_cascade_max_group(num_heads, num_kv_heads, head_size, code, ctypes.byref(g)))
+    return g.value
+
+
 def query_block_hints(row_seq, row_lens, seq_shared_blocks, block_size: int) -> np.ndarray:
     """Shared-block cache hints of query-block rows (pa_query_block_hints):
     int32 [num_rows]."""

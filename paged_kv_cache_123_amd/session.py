@@ -15,7 +15,11 @@ Host bookkeeping runs in the C++ allocator; every device computation is one
 rows, planned attention; plus the merge launch with partitions).  With
 ``cascade`` > 0 a step runs over a cascade plan instead
 (`pa_decode_step_cascade`): sequences that share leading blocks, such as the
-forks of one prompt, read them once per group of at most ``cascade``.
+forks of one prompt, read them once per group of at most ``cascade``.  With
+``cascade`` None (the default) each step chooses: a cascade plan as wide as
+the matrix cores allow when the allocator reports shared blocks, one query
+per sequence is asked for and the shape has a cascade kernel; 0 never builds
+one.
 """
 
 from __future__ import annotations
@@ -25,6 +29,7 @@ import torch
 
 from . import ops
 from .host import Pool
+from .step import auto_cascade_group
 
 _TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -35,14 +40,14 @@ class PagedKVCache:
 
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
                  dtype: str = "f16", device="cuda", free_order=None, sliding_window: int = 0,
-                 partition_size: int = 0, cascade: int = 0):
+                 partition_size: int = 0, cascade=None):
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.num_kv_heads, self.head_size = int(num_kv_heads), int(head_size)
         self.dtype = _TORCH[dtype]
         self.device = torch.device(device)
         self.sliding_window = int(sliding_window)
         self.partition_size = int(partition_size)
-        self.cascade = int(cascade)
+        self.cascade = None if cascade is None else int(cascade)
         if self.cascade and (self.sliding_window or dtype == "f32" or self.head_size != 128):
             raise ValueError("cascade plans need 16-bit storage, head_size 128 and no window")
         self.pool = Pool(self.num_blocks, self.block_size, free_order)
@@ -113,6 +118,11 @@ class PagedKVCache:
         # readers of one shared prefix run together (a key per prefix)
         groups = batch.group_keys
         widest = 0  # members of the widest cascade group of the step
+        cascade = self.cascade
+        if cascade is None:  # chosen per step
+            cascade = (auto_cascade_group(query.shape[1], self.num_kv_heads, self.head_size,
+                                          self.dtype)
+                       if shared.any() and not all_queries and not self.sliding_window else 0)
         if all_queries:
             H, D = query.shape[1], query.shape[2]
             G = H // self.num_kv_heads
@@ -122,9 +132,9 @@ class PagedKVCache:
                                          cow_pairs, positions, scale, shared, matrix)
                 self.last_tables, self.last_lens, self.last_group = tables, lens, 0
                 return out
-        if self.cascade:
+        if cascade:
             plan, num_items, widest = ops.decode_plan_cascade(
-                tables, lens, self.block_size, self.partition_size, self.cascade, n)
+                tables, lens, self.block_size, self.partition_size, cascade, n)
         else:
             plan = ops.decode_plan(lens, self.partition_size, self.sliding_window,
                                    n if all_queries else None, groups)
@@ -140,7 +150,7 @@ class PagedKVCache:
                                                   self.head_size, int(lens.max()),
                                                   self.partition_size, dev)
         shared_dev = torch.from_numpy(shared).to(dev) if shared.any() else None
-        if self.cascade:
+        if cascade:
             ops.decode_step_cascade(out, query, self.key_cache, self.value_cache, t["tables"],
                                     t["lens"], scale, int(lens.max()), self.partition_size,
                                     t["plan"], num_items, widest, t["qsl"], key, value,

@@ -61,6 +61,16 @@ def replay(pool: Pool, history, appends, sliding_window: int = 0,
                              blocks_per_kv_block)
 
 
+def auto_cascade_group(num_heads: int, num_kv_heads: int, head_size: int, dtype) -> int:
+    """Group width of the cascade plan a step takes on its own when sequences
+    share blocks: members x query heads per KV head fill the matrix cores' 16
+    columns, at most 8 members (pa_cascade_max_group).  0, i.e. per-sequence
+    work, where the group would hold fewer than 4 members (8 query heads per
+    KV head) or the shape has no cascade kernel (fp32, head_size 64)."""
+    group = ops.cascade_max_group(num_heads, num_kv_heads, head_size, dtype)
+    return group if group >= 4 else 0
+
+
 class DecodeStep:
     """Allocator replay plus device tensors of one decode step.
 
@@ -88,12 +98,15 @@ class DecodeStep:
     several sequences share run once per group of sharers; without, one
     workgroup per group and KV head reads the prefix once and then every
     member's own tokens.  Needs one query per sequence and no window.
+    None (the default) chooses: a cascade plan as wide as the matrix-core
+    columns allow (``auto_cascade_group``) when the allocator reports blocks
+    several sequences share and the shape allows one; 0 never builds one.
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
                  values: dict, scale: float, partition_size: int = 0, planned: bool = True,
                  all_queries: bool = False, sliding_window: int = 0,
-                 kernel_block_size: int = 0, cascade: int = 0, prefill_kernel: bool = True):
+                 kernel_block_size: int = 0, cascade=None, prefill_kernel: bool = True):
         self.pool = Pool(num_blocks, block_size, free_order)
         if any(op[0] == "request" for op in history):
             self.pool.enable_prefix_caching()
@@ -153,6 +166,11 @@ class DecodeStep:
         query_lens = [n for _, n in appends] if all_queries else None
         # readers of one shared prefix run together (a key per prefix)
         groups = batch.group_keys
+        if cascade is None:
+            cascade = (auto_cascade_group(self.query.shape[1], self.key_cache.shape[1],
+                                          self.query.shape[2], self.query.dtype)
+                       if (self.shared_blocks_host.any() and planned and not all_queries
+                           and not self.sliding_window and k == 1) else 0)
         self.cascade = int(cascade)
         self.num_items, self.max_group = 0, 0
         if self.cascade:

@@ -53,24 +53,26 @@ def check_attention(got_raw, want, dtype, what=""):
     return err, rel
 
 
-def _step(w, vals, partition_size=None, planned=True):
+def _step(w, vals, partition_size=None, planned=True, cascade=0):
+    """The workload's step; per-sequence work unless ``cascade`` asks for a
+    cascade plan (None: the step's own choice)."""
     from paged_kv_cache_123_amd.step import DecodeStep
     ps = w.partition_size if partition_size is None else partition_size
     return DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
                       w.scale, ps, planned=planned,
                       all_queries=w.extra.get("queries") == "all",
                       sliding_window=w.extra.get("sliding_window", 0),
-                      kernel_block_size=w.extra.get("kernel_block_size", 0))
+                      kernel_block_size=w.extra.get("kernel_block_size", 0), cascade=cascade)
 
 
-def full_parity(w, partition_size=None, planned=True):
+def full_parity(w, partition_size=None, planned=True, cascade=0):
     """Every kernel of the step, checked one after the other."""
     _require_gpu()
     print(f"[parity] {w.name} S={w.num_seqs} NB={w.num_blocks} part={partition_size} "
           f"planned={planned}", flush=True)
     vals = W.make_values(w, DEV)
     host = {k: to_host(v) for k, v in vals.items()}
-    step = _step(w, vals, partition_size, planned)
+    step = _step(w, vals, partition_size, planned, cascade)
     ora = OracleStep(w)
     # host allocators: C++ library vs oracle, bit-exact
     assert np.array_equal(step.tables_host.astype(np.int64), ora.tables)
@@ -209,6 +211,16 @@ def test_qwen72b_gqa_bf16_split(decode_kernel):
 def test_shared_prefix_bf16_full_step(decode_kernel):
     step, ora, _ = full_parity(W.shared_prefix_bf16())
     assert len(ora.cow_pairs) == 16 * 7  # the first 7 writers of each group copy
+
+
+@pytest.mark.parametrize("partition_size", [0, 512])
+def test_shared_prefix_bf16_takes_a_cascade_plan_by_itself(partition_size):
+    """With no cascade argument the step sees the shared blocks the allocator
+    reports and builds a cascade plan (groups of 8 forks, the 16 matrix-core
+    columns at one query head per KV head): the full step against the oracle."""
+    step, ora, _ = full_parity(W.shared_prefix_bf16(), partition_size=partition_size,
+                               cascade=None)
+    assert step.cascade == 8 and step.max_group == 8
 
 
 @BOTH

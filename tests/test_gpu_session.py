@@ -29,6 +29,7 @@ def _draw(gen, shape, dtype):
     ("f16", 16, 1, 0, 0, 0), ("bf16", 4, 4, 0, 32, 0), ("f32", 8, 2, 0, 0, 0),
     ("bf16", 16, 8, 24, 0, 0), ("f16", 8, 1, 9, 16, 0),
     ("bf16", 8, 1, 0, 0, 8), ("f16", 4, 2, 0, 16, 4), ("bf16", 16, 8, 0, 0, 2),
+    ("bf16", 16, 1, 0, 0, None), ("f16", 8, 4, 0, 32, None),
 ])
 def test_many_steps_against_the_oracle(dtype, B, G, window, part, cascade):
     _require_gpu()
