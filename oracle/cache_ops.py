@@ -17,8 +17,9 @@ Both functions move raw storage elements (bit copies); they reject inputs
 whose result would depend on the order of writes (a slot written twice, a
 copy destination that repeats or is also a source).
 
-Pinned by: tests/test_oracle_cache_ops.py (gather of written slots returns the
-input bytes, untouched rows unchanged, copied block byte-equal to its source).
+Pinned by: tests/test_oracle_slots.py (gather of written slots returns the
+input bytes, untouched rows unchanged, copied block byte-equal to its source,
+order-dependent inputs rejected, the Fig. 8 sharing example replayed on data).
 """
 
 from __future__ import annotations
