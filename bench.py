@@ -652,7 +652,7 @@ def kernel_label(w, step, args, part, fused) -> str:
                  args.kernel == "auto" and w.dtype != "f32" and w.head_size == 128
                  and (w.num_heads > w.num_kv_heads or step.attn_max_query_len > 1)))
              else "paged_decode_kernel")
-            + (" + merge_kernel" if part else "")
+            + (" + merge_kernel" if part or step.cascade_chunk else "")
             + (" (cascade plan)" if cascade else "")
             + (" (one-launch step: copy-on-write + scatter + attention)" if fused else ""))
 
@@ -672,7 +672,9 @@ def measure(args, w, cascade_arg=None):
                       w.scale, part, all_queries=w.extra.get("queries") == "all",
                       sliding_window=window_of(w),
                       kernel_block_size=w.extra.get("kernel_block_size", 0),
-                      cascade=cascade_arg, prefill_kernel=not args.no_prefill_kernel)
+                      cascade=cascade_arg, prefill_kernel=not args.no_prefill_kernel,
+                      **({} if args.cascade_chunk is None
+                         else {"cascade_chunk": args.cascade_chunk}))
     torch.cuda.synchronize()
     # steps whose cache writes must precede the attention (query blocks of a
     # prefill chunk on the decode kernels; copy-on-write of blocks of several
@@ -688,7 +690,7 @@ def measure(args, w, cascade_arg=None):
     # A one-launch step without partitions is a single kernel: its mean
     # launch duration is the timed region over K, which has no events between
     # launches.  Otherwise the mean of the per-launch events.
-    single_kernel = fused and part == 0
+    single_kernel = fused and part == 0 and not step.cascade_chunk
     attn_avg_ms = ms_per_step if single_kernel else float(np.mean(launch_ms))
     attn_stats = {
         "mean": attn_avg_ms,
@@ -727,6 +729,7 @@ def measure(args, w, cascade_arg=None):
             "num_blocks": w.num_blocks,
             "partition_size": part,
             "cascade_group": cascade,
+            "cascade_chunk": step.cascade_chunk,
             "cascade_group_items": int((step.plan_host[:2 * step.num_items:2] < 0).sum())
             if cascade else 0,
             "attention_kernel": args.kernel,
@@ -815,6 +818,9 @@ def main():
     ap.add_argument("--cascade", type=int, default=None,
                     help="cascade plan with groups of at most N sharers (0: off; default: "
                          "the workload's, else the step's own choice)")
+    ap.add_argument("--cascade-chunk", type=int, default=None,
+                    help="chunked cascade plan: pieces of N prefix tokens per workgroup (0: "
+                         "one workgroup per group; default: the step's own choice)")
     ap.add_argument("--no-prefill-kernel", action="store_true",
                     help="attend prefill chunks as 16-token query blocks on the decode kernels")
     ap.add_argument("--unfused", action="store_true",

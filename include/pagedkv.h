@@ -478,6 +478,71 @@ int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, vo
                                int64_t* slot_mapping, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Chunked cascade plans: the single-pass cascade's workgroup per (group, KV
+ * head) reads a whole shared prefix, so a batch of few groups is one round
+ * of long workgroups.  A chunked plan cuts each group's prefix into pieces of
+ * chunk_tokens (a multiple of block_size and of 16, at most 4096), each read
+ * once for all members by a workgroup of its own, and gives the group one
+ * more item that reads the rest of the prefix once and then every member's
+ * own tokens (the step's writes happen there, as in the single-pass
+ * cascade).  Every item writes (m, l, o) partials; the split merge over
+ * ceil(L / chunk_tokens) parts per sequence gives the same attention
+ * ([VLLBC] paper section 4.4 / Fig. 8: the samples of one prompt share its
+ * blocks; the result is the plain attention of each sequence).
+ *
+ * pa_decode_plan_cascade_chunked (host): groups as pa_decode_plan_cascade
+ * forms them.  Items, largest first:
+ *   (-1 - c, j), j < pf_c = prefix_c / chunk_tokens: chunk c's prefix tokens
+ *        [j * chunk_tokens, (j + 1) * chunk_tokens), written to slot j
+ *   (-1 - c, pf_c): tokens [pf_c * chunk_tokens, prefix_c) for all members,
+ *        then each member's [prefix_c, L_m), written to slot pf_c (the
+ *        member's later slots are marked empty)
+ *   (s, p) for a sequence outside every chunk: tokens [p * chunk_tokens,
+ *        min((p + 1) * chunk_tokens, L_s)), written to slot p
+ * Layout of plan: [2 * num_items] items, [1] C, [C + 1] member offsets, [C]
+ * prefix tokens of each chunk, members.  Arguments and errors as
+ * pa_decode_plan_cascade, with chunk_tokens >= 1 in place of partition_size.
+ *
+ * pa_decode_step_cascade_chunked: pa_decode_step_cascade over such a plan,
+ * chunk_tokens in place of partition_size, workspace as for
+ * pa_paged_attention_decode_split with partition_size = chunk_tokens; the
+ * cascade launch plus the merge launch.  pa_paged_attention_cascade_chunked:
+ * the attention alone (caches already written).  Errors as their unchunked
+ * counterparts, plus PA_EINVAL for chunk_tokens == 0.
+ * ---------------------------------------------------------------------- */
+/* pa_cascade_auto_chunk (host): the chunk_tokens a step would take on its
+ * own: 2048 when the single-pass plan gives fewer than 512 (item, KV head)
+ * workgroups (one round at two per compute unit) and some group's prefix
+ * spans at least 4096 tokens, else 0 (the single-pass plan).  Arguments as
+ * pa_decode_plan_cascade, plus num_kv_heads; *chunk_tokens receives it. */
+int32_t pa_cascade_auto_chunk(const int32_t* context_lens, const int32_t* block_tables,
+                              int64_t bt_stride, const int32_t* new_tokens, int32_t num_seqs,
+                              int32_t block_size, int32_t max_group_size, int32_t num_kv_heads,
+                              int32_t* chunk_tokens);
+int32_t pa_decode_plan_cascade_chunked(const int32_t* context_lens, const int32_t* block_tables,
+                                       int64_t bt_stride, const int32_t* new_tokens,
+                                       int32_t num_seqs, int32_t block_size,
+                                       int32_t chunk_tokens, int32_t max_group_size,
+                                       int32_t* plan, int64_t capacity, int64_t* num_items,
+                                       int64_t* plan_len, int32_t* max_members);
+int32_t pa_decode_step_cascade_chunked(
+    void* out, const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t chunk_tokens, const int32_t* plan, int64_t num_items, int32_t max_group_size,
+    void* workspace, size_t workspace_bytes, const int32_t* query_start_loc, const void* key,
+    const void* value, int64_t key_stride, int64_t value_stride, const int64_t* cow_src,
+    int64_t* slot_mapping, void* stream);
+int32_t pa_paged_attention_cascade_chunked(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t chunk_tokens, const int32_t* plan, int64_t num_items, int32_t max_group_size,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Query blocks (host) for steps whose sequences bring more new tokens than
  * one workgroup holds as query vectors (max_query_len x (num_heads /
  * num_kv_heads) above 16, or 8 for the vector kernel): a prefill chunk

@@ -67,6 +67,16 @@ SIGNATURES = {
                                       _i32, _i32, _f32, _i32, _i32, _vp, _i64, _i32, _vp, _vp,
                                       _sz, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "pa_cascade_max_group": (_i32, [_i32, _i32, _i32, _i32, _pi32]),
+    "pa_cascade_auto_chunk": (_i32, [_pi32, _pi32, _i64, _pi32, _i32, _i32, _i32, _i32, _pi32]),
+    "pa_decode_plan_cascade_chunked": (_i32, [_pi32, _pi32, _i64, _pi32, _i32, _i32, _i32,
+                                              _i32, _pi32, _i64, _pi64, _pi64, _pi32]),
+    "pa_decode_step_cascade_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                              _i64, _i32, _vp, _sz, _vp, _vp, _vp, _i64, _i64,
+                                              _vp, _vp, _vp]),
+    "pa_paged_attention_cascade_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                                  _vp, _i64, _i32, _vp, _sz, _vp]),
     "pa_query_blocks": (_i32, [_pi32, _pi32, _i32, _i32, _pi32, _pi32, _pi32, _i64, _pi64]),
     "pa_query_block_hints": (_i32, [_pi32, _pi32, _i32, _pi32, _i32, _i32, _pi32]),
     "pa_prefill_block_tokens": (_i32, [_i32, _i32, _pi32]),

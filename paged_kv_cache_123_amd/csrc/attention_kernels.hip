@@ -587,8 +587,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   // partition kernel, or the single-pass cascade kernel
   if (a.max_group > 0) {
     if (!can_mfma) return hipErrorInvalidValue;
-    return a.partition_size == 0 ? launch_cascade_single(a, stream)
-                                 : launch_decode_mfma(a, stream);
+    return a.partition_size == 0 || a.cascade_chunked ? launch_cascade_single(a, stream)
+                                                      : launch_decode_mfma(a, stream);
   }
   const bool can_valu = nq <= 8;
   // automatic: matrix cores as soon as a workgroup serves several query vectors

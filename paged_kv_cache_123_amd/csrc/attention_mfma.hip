@@ -331,7 +331,8 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
     const void* value_cache, const int32_t* __restrict__ block_tables, int64_t bt_stride,
     const int32_t* __restrict__ context_lens, int32_t num_heads, int32_t num_kv_heads,
     int32_t log2_block, float scale_log2, const int2* __restrict__ items, int64_t num_items,
-    AppendArgs ap, int32_t log2_group) {
+    AppendArgs ap, int32_t log2_group, int32_t partition_size, int32_t num_partitions,
+    float* __restrict__ ws_max, float* __restrict__ ws_sum, float* __restrict__ ws_out) {
   constexpr int D = 128;
   constexpr int DV = D / 8;
   constexpr int NK = D / 32;
@@ -350,14 +351,20 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
   __shared__ int32_t sm_touch[kMaxMembers];
   __shared__ int32_t sm_cow[kMaxMembers];
   __shared__ int32_t sm_q0[kMaxMembers];
+  // chunked plans (partition_size > 0) keep each chunk's prefix length after
+  // the member offsets; single-pass plans carry it in the item
+  const bool chunked = partition_size > 0;
   int nmem = 1;
   const int32_t* gm = nullptr;
+  int prefix = 0;
   if (it.x < 0) {
     const int32_t* gsec = reinterpret_cast<const int32_t*>(items + num_items);
+    const int nc = gsec[0];
     const int c = -1 - it.x;
     const int m0 = gsec[1 + c];
     nmem = min(gsec[2 + c] - m0, kMaxMembers);
-    gm = gsec + 2 + gsec[0] + m0;
+    gm = gsec + 2 + nc + (chunked ? nc : 0) + m0;
+    prefix = chunked ? gsec[2 + nc + c] : it.y;
   }
   if (static_cast<int>(threadIdx.x) < nmem) {
     const int32_t r = gm ? gm[threadIdx.x] : it.x;
@@ -382,8 +389,35 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
     sm_cow[threadIdx.x] = cow;
     sm_q0[threadIdx.x] = q0;
   }
-  const int prefix = gm ? it.y : 0;
   __syncthreads();
+  // What the item reads: a run [sa, sb) of the shared prefix with every
+  // member's columns live, then (with_members) each member's own tokens
+  // [ma, min(L_m, me)) with only that member's columns live.  out_part: the
+  // slot of the partials it writes (chunked plans), or -1 for the output.
+  //   single pass, group:  [0, prefix), then [prefix, L_m)
+  //   single pass, alone:  [0, L)
+  //   chunked, group j < prefix / P:  [jP, (j + 1)P) of the prefix, slot j
+  //   chunked, group j = prefix / P:  [jP, prefix), then [prefix, L_m), slot j
+  //   chunked, alone (s, p):  [pP, min((p + 1)P, L)), slot p
+  int sa = 0, sb = 0, ma = 0, me = INT_MAX, out_part = -1;
+  bool with_members = true;
+  if (gm) {
+    ma = prefix;
+    sb = prefix;
+    if (chunked) {
+      const int pf = prefix / partition_size;
+      out_part = it.y;
+      sa = it.y * partition_size;
+      if (it.y < pf) {
+        sb = sa + partition_size;
+        with_members = false;
+      }
+    }
+  } else if (chunked) {
+    out_part = it.y;
+    ma = it.y * partition_size;
+    me = ma + partition_size;
+  }
 
   const int B = 1 << log2_block;
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
@@ -423,17 +457,18 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
   const uint4* vc = static_cast<const uint4*>(value_cache);
   const int k_tok = (col >> 2) + 4 * (col & 3);  // token of this lane's K row
 
-  // segment g: the prefix (g == 0 when there is one), else a member's own tokens
-  const int nseg = (prefix > 0 ? 1 : 0) + nmem;
+  // segment g: the shared run (g == 0 when there is one), else a member's own tokens
+  const bool has_shared = sb > sa;
+  const int nseg = (has_shared ? 1 : 0) + (with_members ? nmem : 0);
   auto segment = [&](int g, int& a, int& b, int& owner) {
-    if (prefix > 0 && g == 0) {
-      a = 0;
-      b = prefix;
+    if (has_shared && g == 0) {
+      a = sa;
+      b = sb;
       owner = -1;
     } else {
-      owner = g - (prefix > 0 ? 1 : 0);
-      a = prefix;
-      b = sm_len[owner];
+      owner = g - (has_shared ? 1 : 0);
+      a = ma;
+      b = min(sm_len[owner], me);
     }
   };
   auto table_row = [&](int owner) {
@@ -622,7 +657,36 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
       a = fmaf(sm_acc[w][j][dd], c, a);
     }
     const int64_t row = static_cast<int64_t>(sm_mem[qi]) * num_heads + h0 + (j & gmask);
-    St<DT>::store(out, row * D + dd, a / l);
+    if (out_part < 0) {
+      St<DT>::store(out, row * D + dd, a / l);
+    } else {
+      const int64_t slot = row * num_partitions + out_part;
+      ws_out[slot * D + dd] = l > 0.0f ? a / l : 0.0f;
+      if (dd == 0) {
+        ws_max[slot] = M * kLn2;
+        ws_sum[slot] = l;
+      }
+    }
+  }
+  // A chunked group's last item read each member's tokens past the prefix,
+  // which may reach into later slots: those hold nothing for the merge.
+  if (out_part >= 0 && gm && with_members) {
+    const int G = 1 << log2_group;
+    for (int qi = 0; qi < nmem; ++qi) {
+      const int np = (sm_len[qi] + partition_size - 1) / partition_size;
+      const int n = (np - out_part - 1) * G * D;
+      for (int i = threadIdx.x; i < n; i += NW * 64) {
+        const int dd = i % D, part = out_part + 1 + (i / D) % (np - out_part - 1);
+        const int hh = i / (D * (np - out_part - 1));
+        const int64_t slot =
+            (static_cast<int64_t>(sm_mem[qi]) * num_heads + h0 + hh) * num_partitions + part;
+        ws_out[slot * D + dd] = 0.0f;
+        if (dd == 0) {
+          ws_max[slot] = -INFINITY;
+          ws_sum[slot] = 0.0f;
+        }
+      }
+    }
   }
 }
 
@@ -638,7 +702,8 @@ hipError_t launch_cascade_t(const DecodeArgs& a, hipStream_t stream) {
                      stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,
                      a.bt_stride, a.context_lens, a.num_heads, a.num_kv_heads, log2_block,
                      a.scale * kLog2e, reinterpret_cast<const int2*>(a.items), a.num_items,
-                     a.append, log2_group);
+                     a.append, log2_group, a.cascade_chunked ? a.partition_size : 0,
+                     a.num_partitions, a.ws_max, a.ws_sum, a.ws_out);
   return hipGetLastError();
 }
 
@@ -662,7 +727,8 @@ bool decode_mfma_supported(const DecodeArgs& a) {
 }
 
 hipError_t launch_cascade_single(const DecodeArgs& a, hipStream_t stream) {
-  if (!a.items || a.num_items < 1 || a.partition_size != 0) return hipErrorInvalidValue;
+  if (!a.items || a.num_items < 1 || (a.partition_size != 0) != a.cascade_chunked)
+    return hipErrorInvalidValue;
   return a.dtype == PA_BF16 ? dispatch_cascade<PA_BF16>(a, stream)
                             : dispatch_cascade<PA_F16>(a, stream);
 }

@@ -415,7 +415,7 @@ int32_t pa_paged_attention_decode_planned(
   return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_decode_planned (reduce)");
 }
 
-static int32_t decode_step_impl(const char* who, int32_t max_group, void* out,
+static int32_t decode_step_impl(const char* who, int32_t max_group, bool chunked, void* out,
                                 const void* query, void* key_cache, void* value_cache,
                                 const int32_t* block_tables, int64_t bt_stride,
                                 const int32_t* context_lens, int32_t num_seqs,
@@ -458,6 +458,7 @@ static int32_t decode_step_impl(const char* who, int32_t max_group, void* out,
   a.shared_blocks = shared_prefix_blocks;
   a.window = sliding_window;
   a.max_group = max_group;
+  a.cascade_chunked = chunked;
   if (max_query_len > 0) {  // every new token is a query
     st = check_query_capacity(who, max_query_len, num_heads, num_kv_heads, head_size, dtype);
     if (st != PA_OK) return st;
@@ -467,7 +468,7 @@ static int32_t decode_step_impl(const char* who, int32_t max_group, void* out,
     return fail(PA_EINVAL, (std::string(who) + ": max_query_len must be >= 0").c_str());
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
+  if (partition_size == 0 && !chunked) return launched(pa::launch_decode(a, s), who);
   if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
       partition_size % block_size != 0)
     return fail(PA_EINVAL, (std::string(who) + ": bad partition_size").c_str());
@@ -500,12 +501,42 @@ int32_t pa_decode_step(void* out, const void* query, void* key_cache, void* valu
                        const void* key, const void* value, int64_t key_stride,
                        int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping,
                        int32_t max_query_len, int32_t sliding_window, void* stream) {
-  return decode_step_impl("pa_decode_step", 0, out, query, key_cache, value_cache, block_tables,
+  return decode_step_impl("pa_decode_step", 0, false, out, query, key_cache, value_cache,
+                          block_tables,
                           bt_stride, context_lens, num_seqs, num_heads, num_kv_heads, head_size,
                           block_size, max_context_len, scale, dtype, partition_size, work_items,
                           num_work_items, shared_prefix_blocks, workspace, workspace_bytes,
                           query_start_loc, key, value, key_stride, value_stride, cow_src,
                           slot_mapping, max_query_len, sliding_window, stream);
+}
+
+static int32_t decode_step_cascade_impl(
+    const char* who, bool chunked, void* out, const void* query, void* key_cache,
+    void* value_cache, const int32_t* block_tables, int64_t bt_stride,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t partition_size, const int32_t* plan, int64_t num_items, int32_t max_group_size,
+    const int32_t* shared_prefix_blocks, void* workspace, size_t workspace_bytes,
+    const int32_t* query_start_loc, const void* key, const void* value, int64_t key_stride,
+    int64_t value_stride, const int64_t* cow_src, int64_t* slot_mapping, void* stream) {
+  const std::string w(who);
+  if (max_group_size < 0) return fail(PA_EINVAL, (w + ": max_group_size < 0").c_str());
+  if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
+    return fail(PA_EINVAL,
+                (w + ": group items need 16-bit storage and head_size 128").c_str());
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
+      static_cast<int64_t>(max_group_size) * (num_heads / num_kv_heads) > 16)
+    return fail(PA_EINVAL,
+                (w + ": max_group_size x (num_heads / num_kv_heads) exceeds 16").c_str());
+  if (chunked && partition_size == 0)
+    return fail(PA_EINVAL, (w + ": a chunked plan needs its chunk_tokens as partition_size")
+                               .c_str());
+  return decode_step_impl(who, max_group_size, chunked, out, query, key_cache, value_cache,
+                          block_tables, bt_stride, context_lens, num_seqs, num_heads,
+                          num_kv_heads, head_size, block_size, max_context_len, scale, dtype,
+                          partition_size, plan, num_items, shared_prefix_blocks, workspace,
+                          workspace_bytes, query_start_loc, key, value, key_stride,
+                          value_stride, cow_src, slot_mapping, 0, 0, stream);
 }
 
 int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, void* value_cache,
@@ -520,22 +551,78 @@ int32_t pa_decode_step_cascade(void* out, const void* query, void* key_cache, vo
                                const void* key, const void* value, int64_t key_stride,
                                int64_t value_stride, const int64_t* cow_src,
                                int64_t* slot_mapping, void* stream) {
-  const char* who = "pa_decode_step_cascade";
-  if (max_group_size < 0)
-    return fail(PA_EINVAL, "pa_decode_step_cascade: max_group_size < 0");
+  return decode_step_cascade_impl(
+      "pa_decode_step_cascade", false, out, query, key_cache, value_cache, block_tables,
+      bt_stride, context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+      max_context_len, scale, dtype, partition_size, plan, num_items, max_group_size,
+      shared_prefix_blocks, workspace, workspace_bytes, query_start_loc, key, value, key_stride,
+      value_stride, cow_src, slot_mapping, stream);
+}
+
+int32_t pa_decode_step_cascade_chunked(
+    void* out, const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t chunk_tokens, const int32_t* plan, int64_t num_items, int32_t max_group_size,
+    void* workspace, size_t workspace_bytes, const int32_t* query_start_loc, const void* key,
+    const void* value, int64_t key_stride, int64_t value_stride, const int64_t* cow_src,
+    int64_t* slot_mapping, void* stream) {
+  return decode_step_cascade_impl(
+      "pa_decode_step_cascade_chunked", true, out, query, key_cache, value_cache, block_tables,
+      bt_stride, context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+      max_context_len, scale, dtype, chunk_tokens, plan, num_items, max_group_size, nullptr,
+      workspace, workspace_bytes, query_start_loc, key, value, key_stride, value_stride, cow_src,
+      slot_mapping, stream);
+}
+
+static int32_t attention_cascade_impl(const char* who, bool chunked, void* out,
+                                      const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      int64_t bt_stride, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_size, int32_t block_size,
+                                      int32_t max_context_len, float scale, int32_t dtype,
+                                      int32_t partition_size, const int32_t* plan,
+                                      int64_t num_items, int32_t max_group_size,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const std::string w(who);
+  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
+                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (max_group_size < 0) return fail(PA_EINVAL, (w + ": max_group_size < 0").c_str());
   if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
     return fail(PA_EINVAL,
-                "pa_decode_step_cascade: group items need 16-bit storage and head_size 128");
-  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
-      static_cast<int64_t>(max_group_size) * (num_heads / num_kv_heads) > 16)
+                (w + ": group items need 16-bit storage and head_size 128").c_str());
+  if (static_cast<int64_t>(max_group_size) * (num_heads / num_kv_heads) > 16)
     return fail(PA_EINVAL,
-                "pa_decode_step_cascade: max_group_size x (num_heads / num_kv_heads) exceeds 16");
-  return decode_step_impl(who, max_group_size, out, query, key_cache, value_cache, block_tables,
-                          bt_stride, context_lens, num_seqs, num_heads, num_kv_heads, head_size,
-                          block_size, max_context_len, scale, dtype, partition_size, plan,
-                          num_items, shared_prefix_blocks, workspace, workspace_bytes,
-                          query_start_loc, key, value, key_stride, value_stride, cow_src,
-                          slot_mapping, 0, 0, stream);
+                (w + ": max_group_size x (num_heads / num_kv_heads) exceeds 16").c_str());
+  if (!plan || num_items < 1 || num_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, (w + ": bad plan").c_str());
+  if (chunked && partition_size == 0)
+    return fail(PA_EINVAL, (w + ": a chunked plan needs its chunk_tokens as partition_size")
+                               .c_str());
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
+                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, plan, num_items};
+  a.max_group = max_group_size;
+  a.cascade_chunked = chunked;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, (w + ": bad partition_size").c_str());
+  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                               partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL, (w + ": workspace missing, too small or misaligned").c_str());
+  set_split(a, workspace,
+            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
+            partition_size);
+  st = launched(pa::launch_decode(a, s), (w + " (partition)").c_str());
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(a, s), (w + " (reduce)").c_str());
 }
 
 int32_t pa_paged_attention_cascade(void* out, const void* query, const void* key_cache,
@@ -547,42 +634,25 @@ int32_t pa_paged_attention_cascade(void* out, const void* query, const void* key
                                    int32_t partition_size, const int32_t* plan,
                                    int64_t num_items, int32_t max_group_size, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  const char* who = "pa_paged_attention_cascade";
-  int32_t st = check_decode(who, out, query, key_cache, value_cache, block_tables, bt_stride,
-                            context_lens, num_seqs, num_heads, num_kv_heads, head_size,
-                            block_size, max_context_len, dtype);
-  if (st != PA_OK) return st;
-  if (max_group_size < 0)
-    return fail(PA_EINVAL, "pa_paged_attention_cascade: max_group_size < 0");
-  if ((dtype != PA_F16 && dtype != PA_BF16) || head_size != 128)
-    return fail(PA_EINVAL,
-                "pa_paged_attention_cascade: group items need 16-bit storage and head_size 128");
-  if (static_cast<int64_t>(max_group_size) * (num_heads / num_kv_heads) > 16)
-    return fail(PA_EINVAL,
-                "pa_paged_attention_cascade: max_group_size x (num_heads / num_kv_heads) exceeds "
-                "16");
-  if (!plan || num_items < 1 || num_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
-    return fail(PA_EINVAL, "pa_paged_attention_cascade: bad plan");
-  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, context_lens,
-                   num_seqs, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
-                   nullptr, nullptr, nullptr, plan, num_items};
-  a.max_group = max_group_size;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (partition_size == 0) return launched(pa::launch_decode(a, s), who);
-  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
-      partition_size % block_size != 0)
-    return fail(PA_EINVAL, "pa_paged_attention_cascade: bad partition_size");
-  const size_t need = pa_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
-                                               partition_size);
-  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(PA_EINVAL,
-                "pa_paged_attention_cascade: workspace missing, too small or misaligned");
-  set_split(a, workspace,
-            split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size),
-            partition_size);
-  st = launched(pa::launch_decode(a, s), "pa_paged_attention_cascade (partition)");
-  if (st != PA_OK) return st;
-  return launched(pa::launch_split_reduce(a, s), "pa_paged_attention_cascade (reduce)");
+  return attention_cascade_impl("pa_paged_attention_cascade", false, out, query, key_cache,
+                                value_cache, block_tables, bt_stride, context_lens, num_seqs,
+                                num_heads, num_kv_heads, head_size, block_size, max_context_len,
+                                scale, dtype, partition_size, plan, num_items, max_group_size,
+                                workspace, workspace_bytes, stream);
+}
+
+int32_t pa_paged_attention_cascade_chunked(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_context_len, float scale, int32_t dtype,
+    int32_t chunk_tokens, const int32_t* plan, int64_t num_items, int32_t max_group_size,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_cascade_impl("pa_paged_attention_cascade_chunked", true, out, query,
+                                key_cache, value_cache, block_tables, bt_stride, context_lens,
+                                num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                                max_context_len, scale, dtype, chunk_tokens, plan, num_items,
+                                max_group_size, workspace, workspace_bytes, stream);
 }
 
 int32_t pa_paged_attention_multi(void* out, const void* query, const void* key_cache,

@@ -58,6 +58,8 @@ struct DecodeArgs {
   int32_t max_query_len = 0;  // bound on q_start[s+1] - q_start[s] (host)
   int32_t window = 0;         // sliding window in tokens, 0 for none
   int32_t max_group = 0;      // members of the widest group item (cascade plan), 0 for none
+  bool cascade_chunked = false;  // a chunked cascade plan on the single-pass kernel,
+                                 // writing partials of partition_size-token slots
 };
 
 // Query vectors one workgroup serves: (new tokens per sequence) x (query heads
@@ -80,7 +82,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Single-pass cascade plan (items and group section as pa_decode_plan_cascade
-// writes them with partition_size 0): matrix cores, 16-bit storage, D = 128.
+// writes them with partition_size 0), or a chunked one
+// (pa_decode_plan_cascade_chunked, cascade_chunked set: partials for the split
+// merge): matrix cores, 16-bit storage, D = 128.
 hipError_t launch_cascade_single(const DecodeArgs& a, hipStream_t stream);
 // Prefill chunks on the matrix cores (16-bit storage, head_size 128): rows
 // are query blocks of at most prefill_block_tokens(G) tokens (pa_query_blocks).

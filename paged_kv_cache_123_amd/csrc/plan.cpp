@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <string>
 #include <vector>
 
 #include "pagedkv.h"
@@ -94,45 +95,44 @@ extern "C" int32_t pa_decode_plan(const int32_t* context_lens, int32_t num_seqs,
 //   [1]                       number of chunks C
 //   [C + 1]                   offsets of each chunk's members
 //   [offsets[C]]              members (batch rows), in batch order per chunk
-extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
-                                          const int32_t* block_tables, int64_t bt_stride,
-                                          const int32_t* new_tokens, int32_t num_seqs,
-                                          int32_t block_size, int32_t partition_size,
-                                          int32_t max_group_size, int32_t* plan,
-                                          int64_t capacity, int64_t* num_items,
-                                          int64_t* plan_len, int32_t* max_members) {
-  if (!context_lens || !block_tables || !num_items || !plan_len || !max_members ||
-      num_seqs < 1 || block_size < 1 || partition_size < 0 || max_group_size < 1 ||
-      partition_size % block_size != 0 || bt_stride < 1)
-    return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: bad argument");
+namespace {
+
+// Groups of sharers, as both cascade plans form them: sequences whose first
+// table entry is the same block are candidates; the group's prefix is the run
+// of leading entries all of them agree on, cut to full blocks that end before
+// any member's first new token; a group is split into chunks of at most
+// max_group_size members (a lone member is left out).
+struct CascadeGroups {
+  std::vector<int32_t> off{0};   // chunk c's members: members[off[c] .. off[c+1])
+  std::vector<int32_t> members;  // batch rows
+  std::vector<int32_t> prefix;   // shared prefix tokens of each chunk
+  std::vector<uint8_t> grouped;  // per sequence: in a chunk
+};
+
+int32_t form_groups(const char* who, const int32_t* context_lens, const int32_t* block_tables,
+                    int64_t bt_stride, const int32_t* new_tokens, int32_t num_seqs,
+                    int32_t block_size, int32_t max_group_size, CascadeGroups& g) {
   std::vector<int32_t> first_new(num_seqs);
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t L = context_lens[s];
     const int32_t n = new_tokens ? new_tokens[s] : 1;
     if (L < 1 || n < 1 || n > L)
       return pa::fail(PA_EINVAL,
-                      "pa_decode_plan_cascade: need 1 <= new tokens <= context length");
+                      (std::string(who) + ": need 1 <= new tokens <= context length").c_str());
     if ((static_cast<int64_t>(L) + block_size - 1) / block_size > bt_stride)
-      return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: table row shorter than the length");
+      return pa::fail(PA_EINVAL, (std::string(who) + ": table row shorter than the length").c_str());
     first_new[s] = L - n;
   }
   auto row = [&](int32_t s) { return block_tables + static_cast<int64_t>(s) * bt_stride; };
-  // candidates: sequences with the same first block, in batch order
   std::vector<int32_t> order(num_seqs);
   for (int32_t s = 0; s < num_seqs; ++s) order[s] = s;
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t a, int32_t b) { return row(a)[0] < row(b)[0]; });
-  const bool single = partition_size == 0;
-  // partitions a group item covers (single pass: 1 once the sequence is in a
-  // chunk, whose item reads all of it)
-  std::vector<int32_t> prefix_parts(num_seqs, 0);
-  std::vector<int32_t> chunk_off{0}, members;
-  std::vector<int32_t> chunk_parts;  // split: shared partitions; single pass: prefix tokens
+  g.grouped.assign(num_seqs, 0);
   for (size_t i = 0; i < order.size();) {
     size_t j = i + 1;
     while (j < order.size() && row(order[j])[0] == row(order[i])[0]) ++j;
     if (j - i >= 2 && row(order[i])[0] >= 0) {
-      // common leading entries, full blocks before every member's first new token
       int32_t limit = INT32_MAX;
       for (size_t k = i; k < j; ++k) limit = std::min(limit, first_new[order[k]] / block_size);
       int32_t common = 0;
@@ -143,78 +143,218 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
         if (!same) break;
         ++common;
       }
-      const int32_t parts =
-          single ? common * block_size
-                 : static_cast<int32_t>(static_cast<int64_t>(common) * block_size /
-                                        partition_size);
-      if (parts > 0) {
+      if (common > 0) {
         std::vector<int32_t> grp(order.begin() + i, order.begin() + j);
         std::sort(grp.begin(), grp.end());
         for (size_t c = 0; c < grp.size(); c += max_group_size) {
           const size_t e = std::min(grp.size(), c + max_group_size);
           if (e - c < 2) break;  // a lone member keeps its own items
           for (size_t k = c; k < e; ++k) {
-            members.push_back(grp[k]);
-            prefix_parts[grp[k]] = single ? 1 : parts;
+            g.members.push_back(grp[k]);
+            g.grouped[grp[k]] = 1;
           }
-          chunk_off.push_back(static_cast<int32_t>(members.size()));
-          chunk_parts.push_back(parts);
+          g.off.push_back(static_cast<int32_t>(g.members.size()));
+          g.prefix.push_back(common * block_size);
         }
       }
     }
     i = j;
   }
-  struct Item {
-    int32_t tokens, key, s, p;
-  };
-  std::vector<Item> v;
-  const int32_t num_chunks = static_cast<int32_t>(chunk_parts.size());
-  for (int32_t c = 0; c < num_chunks; ++c) {
-    if (single) {  // the prefix once, then each member's own tokens
-      const int32_t prefix = chunk_parts[c];
-      int64_t tokens = prefix;
-      for (int32_t k = chunk_off[c]; k < chunk_off[c + 1]; ++k)
-        tokens += context_lens[members[k]] - prefix;
-      v.push_back({static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)),
-                   members[chunk_off[c]], -1 - c, prefix});
-      continue;
-    }
-    for (int32_t p = 0; p < chunk_parts[c]; ++p)
-      v.push_back({partition_size, members[chunk_off[c]], -1 - c, p});
-  }
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t L = context_lens[s];
-    if (single) {
-      if (!prefix_parts[s]) v.push_back({L, s, s, 0});
-      continue;
-    }
-    for (int32_t p = prefix_parts[s]; static_cast<int64_t>(p) * partition_size < L; ++p)
-      v.push_back({std::min((p + 1) * partition_size, L) - p * partition_size, s, s, p});
-  }
+  return PA_OK;
+}
+
+struct PlanItem {
+  int32_t tokens, key, s, p;
+};
+
+// Items largest first (by tokens read, in buckets), then the plan's group
+// section: C, the C + 1 member offsets, optionally the C prefix lengths, the
+// members.
+int32_t write_plan(const char* who, std::vector<PlanItem>& v, const CascadeGroups& g,
+                   bool with_prefix, int32_t* plan, int64_t capacity, int64_t* num_items,
+                   int64_t* plan_len, int32_t* max_members) {
+  const int32_t num_chunks = static_cast<int32_t>(g.prefix.size());
   int32_t widest = 0;
-  for (int32_t c = 0; c < num_chunks; ++c)
-    widest = std::max(widest, chunk_off[c + 1] - chunk_off[c]);
+  for (int32_t c = 0; c < num_chunks; ++c) widest = std::max(widest, g.off[c + 1] - g.off[c]);
   *num_items = static_cast<int64_t>(v.size());
   *plan_len = 2 * static_cast<int64_t>(v.size()) + 1 + (num_chunks + 1) +
-              static_cast<int64_t>(members.size());
+              (with_prefix ? num_chunks : 0) + static_cast<int64_t>(g.members.size());
   *max_members = widest;
   if (!plan) return PA_OK;  // size query
   if (capacity < *plan_len)
-    return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: capacity smaller than the plan");
-  std::stable_sort(v.begin(), v.end(), [](const Item& a, const Item& b) {
+    return pa::fail(PA_EINVAL, (std::string(who) + ": capacity smaller than the plan").c_str());
+  std::stable_sort(v.begin(), v.end(), [](const PlanItem& a, const PlanItem& b) {
     const int32_t ba = (a.tokens + kGranule - 1) / kGranule;
     const int32_t bb = (b.tokens + kGranule - 1) / kGranule;
     return ba != bb ? ba > bb : a.key < b.key;
   });
   int64_t w = 0;
-  for (const Item& it : v) {
+  for (const PlanItem& it : v) {
     plan[w++] = it.s;
     plan[w++] = it.p;
   }
   plan[w++] = num_chunks;
-  for (int32_t o : chunk_off) plan[w++] = o;
-  for (int32_t m : members) plan[w++] = m;
+  for (int32_t o : g.off) plan[w++] = o;
+  if (with_prefix)
+    for (int32_t t : g.prefix) plan[w++] = t;
+  for (int32_t m : g.members) plan[w++] = m;
   return PA_OK;
+}
+
+}  // namespace
+
+// Cascade plan: the partitions that lie wholly inside a prefix several
+// sequences share are computed once per group of sharers instead of once per
+// sequence (groups as form_groups makes them).  Chunk c and partition p
+// (wholly inside the prefix) make the item (-1 - c, p).  Every other
+// (sequence, partition) pair keeps its own item.
+// With partition_size == 0 (single pass) a chunk's item is (-1 - c, prefix
+// tokens): one workgroup per KV head reads the prefix once for all members
+// and then every member's own tokens past it; every other sequence s keeps
+// the item (s, 0).  Items are ordered by the tokens they read.  Layout of
+// `plan`:
+//   [2 * num_items]           the items, largest first as in pa_decode_plan
+//   [1]                       number of chunks C
+//   [C + 1]                   offsets of each chunk's members
+//   [offsets[C]]              members (batch rows), in batch order per chunk
+extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
+                                          const int32_t* block_tables, int64_t bt_stride,
+                                          const int32_t* new_tokens, int32_t num_seqs,
+                                          int32_t block_size, int32_t partition_size,
+                                          int32_t max_group_size, int32_t* plan,
+                                          int64_t capacity, int64_t* num_items,
+                                          int64_t* plan_len, int32_t* max_members) {
+  const char* who = "pa_decode_plan_cascade";
+  if (!context_lens || !block_tables || !num_items || !plan_len || !max_members ||
+      num_seqs < 1 || block_size < 1 || partition_size < 0 || max_group_size < 1 ||
+      partition_size % block_size != 0 || bt_stride < 1)
+    return pa::fail(PA_EINVAL, "pa_decode_plan_cascade: bad argument");
+  CascadeGroups g;
+  int32_t st = form_groups(who, context_lens, block_tables, bt_stride, new_tokens, num_seqs,
+                           block_size, max_group_size, g);
+  if (st != PA_OK) return st;
+  const bool single = partition_size == 0;
+  // split plans keep only chunks with a whole partition inside the prefix
+  if (!single) {
+    CascadeGroups kept;
+    kept.grouped.assign(num_seqs, 0);
+    for (size_t c = 0; c + 1 < g.off.size(); ++c) {
+      if (g.prefix[c] / partition_size == 0) continue;
+      for (int32_t k = g.off[c]; k < g.off[c + 1]; ++k) {
+        kept.members.push_back(g.members[k]);
+        kept.grouped[g.members[k]] = 1;
+      }
+      kept.off.push_back(static_cast<int32_t>(kept.members.size()));
+      kept.prefix.push_back(g.prefix[c]);
+    }
+    g = std::move(kept);
+  }
+  std::vector<PlanItem> v;
+  const int32_t num_chunks = static_cast<int32_t>(g.prefix.size());
+  for (int32_t c = 0; c < num_chunks; ++c) {
+    if (single) {  // the prefix once, then each member's own tokens
+      const int32_t prefix = g.prefix[c];
+      int64_t tokens = prefix;
+      for (int32_t k = g.off[c]; k < g.off[c + 1]; ++k)
+        tokens += context_lens[g.members[k]] - prefix;
+      v.push_back({static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)),
+                   g.members[g.off[c]], -1 - c, prefix});
+      continue;
+    }
+    for (int32_t p = 0; p < g.prefix[c] / partition_size; ++p)
+      v.push_back({partition_size, g.members[g.off[c]], -1 - c, p});
+  }
+  // split: a member's own items start after its chunk's prefix partitions
+  std::vector<int32_t> own_from(num_seqs, 0);
+  if (!single)
+    for (int32_t c = 0; c < num_chunks; ++c)
+      for (int32_t k = g.off[c]; k < g.off[c + 1]; ++k)
+        own_from[g.members[k]] = g.prefix[c] / partition_size;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = context_lens[s];
+    if (single) {
+      if (!g.grouped[s]) v.push_back({L, s, s, 0});
+      continue;
+    }
+    for (int32_t p = own_from[s]; static_cast<int64_t>(p) * partition_size < L; ++p)
+      v.push_back({std::min((p + 1) * partition_size, L) - p * partition_size, s, s, p});
+  }
+  return write_plan(who, v, g, false, plan, capacity, num_items, plan_len, max_members);
+}
+
+// Chunk size of a step's cascade plan: a single-pass plan runs one
+// workgroup per (item, KV head); when that is less than one round of the
+// chip (kRoundWorkgroups, two per compute unit) and some prefix spans at
+// least two pieces of kAutoChunk tokens, the chunked plan spreads the
+// prefixes over more workgroups.  0: the single-pass plan.
+extern "C" int32_t pa_cascade_auto_chunk(const int32_t* context_lens,
+                                         const int32_t* block_tables, int64_t bt_stride,
+                                         const int32_t* new_tokens, int32_t num_seqs,
+                                         int32_t block_size, int32_t max_group_size,
+                                         int32_t num_kv_heads, int32_t* chunk_tokens) {
+  constexpr int64_t kRoundWorkgroups = 512;
+  constexpr int32_t kAutoChunk = 2048;
+  const char* who = "pa_cascade_auto_chunk";
+  if (!context_lens || !block_tables || !chunk_tokens || num_seqs < 1 || block_size < 1 ||
+      max_group_size < 1 || num_kv_heads < 1 || bt_stride < 1)
+    return pa::fail(PA_EINVAL, "pa_cascade_auto_chunk: bad argument");
+  *chunk_tokens = 0;
+  CascadeGroups g;
+  const int32_t st = form_groups(who, context_lens, block_tables, bt_stride, new_tokens,
+                                 num_seqs, block_size, max_group_size, g);
+  if (st != PA_OK) return st;
+  int64_t items = static_cast<int64_t>(g.prefix.size());
+  for (int32_t s = 0; s < num_seqs; ++s) items += g.grouped[s] ? 0 : 1;
+  int32_t longest = 0;
+  for (int32_t t : g.prefix) longest = std::max(longest, t);
+  if (items * num_kv_heads < kRoundWorkgroups && longest >= 2 * kAutoChunk &&
+      kAutoChunk % block_size == 0)
+    *chunk_tokens = kAutoChunk;
+  return PA_OK;
+}
+
+// Chunked cascade plan (single-pass kernel, split into pieces of at most
+// chunk_tokens): a chunk's shared prefix is cut into chunk_tokens pieces, each
+// an item (-1 - c, j) for j < pf = prefix / chunk_tokens that reads its piece
+// once for all members; the item (-1 - c, pf) reads the rest of the prefix
+// [pf * chunk_tokens, prefix) once for all members and then every member's
+// own tokens.  A sequence outside every chunk has the items (s, p), tokens
+// [p * chunk_tokens, min((p + 1) * chunk_tokens, L)).  Every item writes
+// partials that a merge over ceil(L / chunk_tokens) parts per sequence
+// finishes.  Layout as pa_decode_plan_cascade, with the C prefix lengths
+// after the member offsets.
+extern "C" int32_t pa_decode_plan_cascade_chunked(
+    const int32_t* context_lens, const int32_t* block_tables, int64_t bt_stride,
+    const int32_t* new_tokens, int32_t num_seqs, int32_t block_size, int32_t chunk_tokens,
+    int32_t max_group_size, int32_t* plan, int64_t capacity, int64_t* num_items,
+    int64_t* plan_len, int32_t* max_members) {
+  const char* who = "pa_decode_plan_cascade_chunked";
+  if (!context_lens || !block_tables || !num_items || !plan_len || !max_members ||
+      num_seqs < 1 || block_size < 1 || chunk_tokens < 1 || max_group_size < 1 ||
+      chunk_tokens % block_size != 0 || bt_stride < 1)
+    return pa::fail(PA_EINVAL, "pa_decode_plan_cascade_chunked: bad argument");
+  CascadeGroups g;
+  const int32_t st = form_groups(who, context_lens, block_tables, bt_stride, new_tokens,
+                                 num_seqs, block_size, max_group_size, g);
+  if (st != PA_OK) return st;
+  std::vector<PlanItem> v;
+  const int32_t num_chunks = static_cast<int32_t>(g.prefix.size());
+  for (int32_t c = 0; c < num_chunks; ++c) {
+    const int32_t prefix = g.prefix[c], pf = prefix / chunk_tokens;
+    const int32_t key = g.members[g.off[c]];
+    for (int32_t j = 0; j < pf; ++j) v.push_back({chunk_tokens, key, -1 - c, j});
+    int64_t tokens = prefix - static_cast<int64_t>(pf) * chunk_tokens;
+    for (int32_t k = g.off[c]; k < g.off[c + 1]; ++k)
+      tokens += context_lens[g.members[k]] - prefix;
+    v.push_back({static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)), key, -1 - c, pf});
+  }
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (g.grouped[s]) continue;
+    const int32_t L = context_lens[s];
+    for (int32_t p = 0; static_cast<int64_t>(p) * chunk_tokens < L; ++p)
+      v.push_back({std::min((p + 1) * chunk_tokens, L) - p * chunk_tokens, s, s, p});
+  }
+  return write_plan(who, v, g, true, plan, capacity, num_items, plan_len, max_members);
 }
 
 // Query blocks: sequence s's n_s new tokens (rows [qsl[s], qsl[s+1]) of the

@@ -322,12 +322,16 @@ def decode_plan(context_lens, partition_size: int, sliding_window: int = 0,
 
 
 def decode_plan_cascade(block_tables, context_lens, block_size: int, partition_size: int,
-                        max_group_size: int, new_tokens=None):
+                        max_group_size: int, new_tokens=None, chunk_tokens: int = 0):
     """Host cascade plan (pa_decode_plan_cascade): partitions wholly inside a
     prefix several sequences share become one group item per chunk of at most
     ``max_group_size`` sharers; with ``partition_size`` 0, one single-pass item
-    per chunk (prefix once, then each member's own tokens).  Returns (plan
-    int32 1-D: items then the group section, num_items, max_members)."""
+    per chunk (prefix once, then each member's own tokens).  With
+    ``chunk_tokens`` > 0 (``partition_size`` ignored) the chunked plan
+    (pa_decode_plan_cascade_chunked): each prefix in pieces of chunk_tokens
+    plus one item for the rest and the members' own tokens, all writing
+    partials.  Returns (plan int32 1-D: items then the group section,
+    num_items, max_members)."""
     tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     if tables.ndim != 2 or tables.shape[0] != lens.size:
@@ -340,15 +344,34 @@ def decode_plan_cascade(block_tables, context_lens, block_size: int, partition_s
             raise ValueError("new_tokens must have one entry per sequence")
         newp = new.ctypes.data_as(p32)
     n, plen, widest = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    fn = lib().pa_decode_plan_cascade_chunked if chunk_tokens else lib().pa_decode_plan_cascade
     args = (lens.ctypes.data_as(p32), tables.ctypes.data_as(p32), tables.shape[1], newp,
-            lens.size, block_size, partition_size, max_group_size)
-    check(lib().pa_decode_plan_cascade(*args, None, 0, ctypes.byref(n), ctypes.byref(plen),
-                                       ctypes.byref(widest)))
+            lens.size, block_size, chunk_tokens or partition_size, max_group_size)
+    check(fn(*args, None, 0, ctypes.byref(n), ctypes.byref(plen), ctypes.byref(widest)))
     plan = np.empty(plen.value, dtype=np.int32)
-    check(lib().pa_decode_plan_cascade(*args, plan.ctypes.data_as(p32), plan.size,
-                                       ctypes.byref(n), ctypes.byref(plen),
-                                       ctypes.byref(widest)))
+    check(fn(*args, plan.ctypes.data_as(p32), plan.size, ctypes.byref(n), ctypes.byref(plen),
+             ctypes.byref(widest)))
     return plan, n.value, widest.value
+
+
+def cascade_auto_chunk(block_tables, context_lens, block_size: int, max_group_size: int,
+                       num_kv_heads: int, new_tokens=None) -> int:
+    """The chunk_tokens a cascade step takes on its own (pa_cascade_auto_chunk):
+    0 for the single-pass plan."""
+    tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if tables.ndim != 2 or tables.shape[0] != lens.size:
+        raise ValueError("block_tables must be [num_seqs, width]")
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    newp = None
+    if new_tokens is not None:
+        new = np.ascontiguousarray(np.asarray(new_tokens, dtype=np.int32))
+        newp = new.ctypes.data_as(p32)
+    out = ctypes.c_int32(0)
+    check(lib().pa_cascade_auto_chunk(lens.ctypes.data_as(p32), tables.ctypes.data_as(p32),
+                                      tables.shape[1], newp, lens.size, block_size,
+                                      max_group_size, num_kv_heads, ctypes.byref(out)))
+    return out.value
 
 
 def query_blocks(context_lens, query_start_loc, max_block: int):
@@ -603,15 +626,16 @@ def decode_step_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch
                         partition_size: int, plan: torch.Tensor, num_items: int,
                         max_group_size: int, query_start_loc: torch.Tensor, key: torch.Tensor,
                         value: torch.Tensor, cow_src=None, slot_mapping=None, workspace=None,
-                        shared_prefix_blocks=None) -> None:
+                        shared_prefix_blocks=None, chunked: bool = False) -> None:
     """decode_step over a cascade plan (decode_plan_cascade, uploaded as a
     device int32 tensor): the prefix of each group of sharers is read once
     for all of them (per shared partition, or in one single-pass item when
-    ``partition_size`` is 0)."""
+    ``partition_size`` is 0).  ``chunked``: a chunked plan, whose chunk_tokens
+    is ``partition_size`` (pa_decode_step_cascade_chunked)."""
     launch_prepared(prepare_decode_step_cascade(
         out, query, key_cache, value_cache, block_tables, context_lens, scale,
         max_context_len, partition_size, plan, num_items, max_group_size, query_start_loc,
-        key, value, cow_src, slot_mapping, workspace, shared_prefix_blocks))
+        key, value, cow_src, slot_mapping, workspace, shared_prefix_blocks, chunked))
 
 
 def prepare_decode_step_cascade(out: torch.Tensor, query: torch.Tensor,
@@ -621,7 +645,8 @@ def prepare_decode_step_cascade(out: torch.Tensor, query: torch.Tensor,
                                 plan: torch.Tensor, num_items: int, max_group_size: int,
                                 query_start_loc: torch.Tensor, key: torch.Tensor,
                                 value: torch.Tensor, cow_src=None, slot_mapping=None,
-                                workspace=None, shared_prefix_blocks=None):
+                                workspace=None, shared_prefix_blocks=None,
+                                chunked: bool = False):
     """decode_step_cascade's checks and argument marshalling, done once (see
     prepare_decode_step)."""
     S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
@@ -653,22 +678,26 @@ def prepare_decode_step_cascade(out: torch.Tensor, query: torch.Tensor,
     if workspace is not None:
         _dev(workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    return lib().pa_decode_step_cascade, (
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
-        B, max_context_len, scale, _dtype(key_cache), partition_size, plan.data_ptr(),
-        num_items, max_group_size, _shared_ptr(shared_prefix_blocks, S), ws_ptr or None,
-        ws_bytes, query_start_loc.data_ptr(), key.data_ptr(), value.data_ptr(), key.stride(0),
-        value.stride(0), cow_ptr or None, slot_ptr or None)
+    common = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+              block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H,
+              hkv, D, B, max_context_len, scale, _dtype(key_cache), partition_size,
+              plan.data_ptr(), num_items, max_group_size)
+    rest = (ws_ptr or None, ws_bytes, query_start_loc.data_ptr(), key.data_ptr(),
+            value.data_ptr(), key.stride(0), value.stride(0), cow_ptr or None, slot_ptr or None)
+    if chunked:
+        return lib().pa_decode_step_cascade_chunked, common + rest
+    return lib().pa_decode_step_cascade, common + (_shared_ptr(shared_prefix_blocks, S),) + rest
 
 
 def paged_attention_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                             value_cache: torch.Tensor, block_tables: torch.Tensor,
                             context_lens: torch.Tensor, scale: float, max_context_len: int,
                             partition_size: int, plan: torch.Tensor, num_items: int,
-                            max_group_size: int, workspace=None) -> None:
-    """Attention alone over a cascade plan (pa_paged_attention_cascade), on
-    caches that already hold the step's rows."""
+                            max_group_size: int, workspace=None, chunked: bool = False) -> None:
+    """Attention alone over a cascade plan (pa_paged_attention_cascade, or
+    pa_paged_attention_cascade_chunked with ``chunked``, ``partition_size``
+    then being the plan's chunk_tokens), on caches that already hold the
+    step's rows."""
     S, H, hkv, D, B = _attn_common(out, query, key_cache, value_cache, block_tables,
                                    context_lens)
     _dev(plan)
@@ -679,7 +708,8 @@ def paged_attention_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: t
     if workspace is not None:
         _dev(workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check(lib().pa_paged_attention_cascade(
+    fn = lib().pa_paged_attention_cascade_chunked if chunked else lib().pa_paged_attention_cascade
+    check(fn(
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(), S, H, hkv, D,
         B, max_context_len, scale, _dtype(key_cache), partition_size, plan.data_ptr(),

@@ -132,9 +132,14 @@ class PagedKVCache:
                                          cow_pairs, positions, scale, shared, matrix)
                 self.last_tables, self.last_lens, self.last_group = tables, lens, 0
                 return out
+        chunk = 0  # a chunked cascade plan's piece size (the step's own choice)
+        if cascade and not self.partition_size:
+            chunk = ops.cascade_auto_chunk(tables, lens, self.block_size, cascade,
+                                           self.num_kv_heads, n)
         if cascade:
             plan, num_items, widest = ops.decode_plan_cascade(
-                tables, lens, self.block_size, self.partition_size, cascade, n)
+                tables, lens, self.block_size, self.partition_size, cascade, n,
+                chunk_tokens=chunk)
         else:
             plan = ops.decode_plan(lens, self.partition_size, self.sliding_window,
                                    n if all_queries else None, groups)
@@ -143,18 +148,19 @@ class PagedKVCache:
             ("plan", plan))}
         out = torch.empty_like(query)
         workspace = None
-        if self.partition_size:
+        if self.partition_size or chunk:
             # the one-launch step sizes multi-query rows as num_seqs x max_query_len
             rows = len(seqs) * max(n) if all_queries else len(seqs)
             workspace = ops.alloc_split_workspace(max(rows, query.shape[0]), query.shape[1],
                                                   self.head_size, int(lens.max()),
-                                                  self.partition_size, dev)
+                                                  self.partition_size or chunk, dev)
         shared_dev = torch.from_numpy(shared).to(dev) if shared.any() else None
         if cascade:
             ops.decode_step_cascade(out, query, self.key_cache, self.value_cache, t["tables"],
-                                    t["lens"], scale, int(lens.max()), self.partition_size,
-                                    t["plan"], num_items, widest, t["qsl"], key, value,
-                                    t["cow_src"], None, workspace, shared_dev)
+                                    t["lens"], scale, int(lens.max()),
+                                    self.partition_size or chunk, t["plan"], num_items, widest,
+                                    t["qsl"], key, value, t["cow_src"], None, workspace,
+                                    shared_dev, chunked=bool(chunk))
         else:
             ops.decode_step(out, query, self.key_cache, self.value_cache, t["tables"],
                             t["lens"], scale, int(lens.max()), self.partition_size, t["plan"],

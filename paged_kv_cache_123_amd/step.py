@@ -101,12 +101,18 @@ class DecodeStep:
     None (the default) chooses: a cascade plan as wide as the matrix-core
     columns allow (``auto_cascade_group``) when the allocator reports blocks
     several sequences share and the shape allows one; 0 never builds one.
+    ``cascade_chunk``: with a cascade plan and no partitions, cut each shared
+    prefix into pieces of this many tokens, each read once for the group by a
+    workgroup of its own, plus one item for the rest of the prefix and the
+    members' own tokens; partials merged as in split-K (0: one workgroup per
+    group and KV head; None: the step's choice, pa_cascade_auto_chunk).
     """
 
     def __init__(self, num_blocks: int, block_size: int, free_order, history, appends,
                  values: dict, scale: float, partition_size: int = 0, planned: bool = True,
                  all_queries: bool = False, sliding_window: int = 0,
-                 kernel_block_size: int = 0, cascade=None, prefill_kernel: bool = True):
+                 kernel_block_size: int = 0, cascade=None, prefill_kernel: bool = True,
+                 cascade_chunk=None):
         self.pool = Pool(num_blocks, block_size, free_order)
         if any(op[0] == "request" for op in history):
             self.pool.enable_prefix_caching()
@@ -172,13 +178,20 @@ class DecodeStep:
                        if (self.shared_blocks_host.any() and planned and not all_queries
                            and not self.sliding_window and k == 1) else 0)
         self.cascade = int(cascade)
+        if self.cascade and not self.partition_size and cascade_chunk is None:
+            cascade_chunk = ops.cascade_auto_chunk(tables, lens, kb, self.cascade,
+                                                   self.key_cache.shape[1],
+                                                   [n for _, n in appends])
+        self.cascade_chunk = (int(cascade_chunk or 0) if self.cascade and not self.partition_size
+                              else 0)
         self.num_items, self.max_group = 0, 0
         if self.cascade:
             if all_queries or self.sliding_window or k > 1:
                 raise ValueError("a cascade plan needs one query per sequence, no window and "
                                  "kernel blocks equal to the allocator's")
             self.plan_host, self.num_items, self.max_group = ops.decode_plan_cascade(
-                tables, lens, kb, self.partition_size, self.cascade, [n for _, n in appends])
+                tables, lens, kb, self.partition_size, self.cascade, [n for _, n in appends],
+                chunk_tokens=self.cascade_chunk)
         else:
             self.plan_host = ops.decode_plan(lens, self.partition_size, self.sliding_window,
                                              query_lens, groups)
@@ -223,12 +236,13 @@ class DecodeStep:
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self._fused_call = None  # the one-launch step's marshalled arguments
         self.workspace = None
-        if self.partition_size:
+        if self.partition_size or self.cascade_chunk:
             rows, H, D = self.query.shape
             if all_queries:  # the one-launch step sizes rows as num_seqs x max_query_len
                 rows = max(rows, len(seqs) * self.max_query_len)
             self.workspace = ops.alloc_split_workspace(rows, H, D, self.max_context_len,
-                                                       self.partition_size, dev)
+                                                       self.partition_size or self.cascade_chunk,
+                                                       dev)
 
     # ---- the step, kernel by kernel --------------------------------------
     def copy_blocks(self):
@@ -246,8 +260,10 @@ class DecodeStep:
         if self.cascade:
             ops.paged_attention_cascade(self.out, self.query, self.key_cache, self.value_cache,
                                         self.block_tables, self.context_lens, self.scale,
-                                        self.max_context_len, self.partition_size, self.plan,
-                                        self.num_items, self.max_group, self.workspace)
+                                        self.max_context_len,
+                                        self.partition_size or self.cascade_chunk, self.plan,
+                                        self.num_items, self.max_group, self.workspace,
+                                        chunked=bool(self.cascade_chunk))
         elif self.prefill_rows:
             ops.paged_attention_prefill(self.out, self.query, self.key_cache, self.value_cache,
                                         self.block_tables, self.row_seq, self.attn_lens,
@@ -296,10 +312,11 @@ class DecodeStep:
             elif self.cascade:
                 self._fused_call = ops.prepare_decode_step_cascade(
                     self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
-                    self.context_lens, self.scale, self.max_context_len, self.partition_size,
-                    self.plan, self.num_items, self.max_group, self.query_start_loc,
-                    self.new_key, self.new_value, self.cow_src, self.slot_mapping,
-                    self.workspace, self.shared_blocks)
+                    self.context_lens, self.scale, self.max_context_len,
+                    self.partition_size or self.cascade_chunk, self.plan, self.num_items,
+                    self.max_group, self.query_start_loc, self.new_key, self.new_value,
+                    self.cow_src, self.slot_mapping, self.workspace, self.shared_blocks,
+                    chunked=bool(self.cascade_chunk))
             else:
                 self._fused_call = ops.prepare_decode_step(
                     self.out, self.query, self.key_cache, self.value_cache, self.block_tables,

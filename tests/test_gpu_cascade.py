@@ -27,14 +27,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _steps(w, part, group, fused=True):
+def _steps(w, part, group, fused=True, chunk=0):
     from paged_kv_cache_123_amd import ops
     from paged_kv_cache_123_amd.step import DecodeStep
     vals = W.make_values(w, DEV)
     host = {k: to_host(v) for k, v in vals.items()}
     plain_vals = {k: v.clone() for k, v in vals.items()}
     casc = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals, w.scale,
-                      part, cascade=group)
+                      part, cascade=group, cascade_chunk=chunk)
+    assert casc.cascade_chunk == chunk
     prev = ops.set_decode_kernel("mfma")
     try:
         plain = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step,
@@ -48,10 +49,11 @@ def _steps(w, part, group, fused=True):
     return casc, plain, out, host
 
 
-def _check(w, part, group, expect_groups=True, fused=True):
+def _check(w, part, group, expect_groups=True, fused=True, chunk=0):
     """``fused``: the one-launch step; else copy_blocks, slot mapping, scatter
-    and the cascade attention as separate launches."""
-    casc, plain, out, host = _steps(w, part, group, fused)
+    and the cascade attention as separate launches.  ``chunk``: a chunked
+    single-pass plan with pieces of that many tokens (partials and a merge)."""
+    casc, plain, out, host = _steps(w, part, group, fused, chunk)
     if expect_groups:
         assert casc.max_group >= 2, "the batch should form groups"
     ora = OracleStep(w)
@@ -66,7 +68,7 @@ def _check(w, part, group, expect_groups=True, fused=True):
         gv[blk, :, off, :] = vc[blk, :, off, :]
     assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
     want = ora.attention(host["query"], kc, vc)
-    check_attention(to_host(out), want, w.dtype, f"cascade P={part} group={group}")
+    check_attention(to_host(out), want, w.dtype, f"cascade P={part} group={group} chunk={chunk}")
     if part:
         assert torch.equal(out.view(torch.int16), plain.out.view(torch.int16)), \
             "cascade and plain split steps differ"
@@ -76,6 +78,19 @@ def _check(w, part, group, expect_groups=True, fused=True):
         torch.cuda.synchronize()
         assert torch.equal(first.view(torch.int16), casc.out.view(torch.int16)), \
             "single-pass cascade: one launch and separate calls differ"
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "calls"])
+@pytest.mark.parametrize("chunk,group", [(256, 8), (512, 8), (1024, 8), (128, 3), (32, 16)])
+def test_shared_prefix_batch_chunked(chunk, group, fused):
+    """The shared-prefix configuration on a chunked plan: each 1024-token
+    prefix in pieces of ``chunk`` tokens, one workgroup per piece and KV head,
+    the rest of the prefix and the samples' own tokens in the group's last
+    item, partials merged."""
+    _require_gpu()
+    print(f"[cascade] shared prefix chunked chunk={chunk} group={group} fused={fused}",
+          flush=True)
+    _check(W.shared_prefix_bf16(), 0, group, fused=fused, chunk=chunk)
 
 
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "calls"])
@@ -100,28 +115,32 @@ FORK_CASES = [
 ]
 
 
-@pytest.mark.parametrize("single", [False, True], ids=["split", "single"])
+@pytest.mark.parametrize("mode", ["split", "single", "chunked"])
 @pytest.mark.parametrize("dtype,B,G,part,group,prompts,samples,appends", FORK_CASES,
                          ids=[f"{c[0]}-B{c[1]}-G{c[2]}-P{c[3]}-g{c[4]}" for c in FORK_CASES])
-def test_forks(dtype, B, G, part, group, prompts, samples, appends, single):
+def test_forks(dtype, B, G, part, group, prompts, samples, appends, mode):
     """Forked samples of several prompts, several new tokens per sample,
-    copy-on-write tails, prefixes that end inside a partition."""
+    copy-on-write tails, prefixes that end inside a partition; chunked plans
+    use pieces of the case's partition size, so own tokens reach past the
+    group's last slot (marked empty for the merge)."""
     _require_gpu()
-    part = 0 if single else part
-    print(f"[cascade] forks {dtype} B={B} G={G} P={part} group={group}", flush=True)
+    chunk = part if mode == "chunked" else 0
+    part = part if mode == "split" else 0
+    print(f"[cascade] forks {dtype} B={B} G={G} P={part} chunk={chunk} group={group}",
+          flush=True)
     rows = [[appends[(g + j) % len(appends)] for j in range(samples)]
             for g in range(len(prompts))]
     w = W.custom_forks("cascade", 41, prompts, samples, rows, dtype=dtype, H=2 * G, Hkv=2,
                        D=128, B=B, partition_size=part)
-    _check(w, part, group, fused=not single)
+    _check(w, part, group, fused=mode != "single", chunk=chunk)
 
 
-@pytest.mark.parametrize("part", [64, 0])
-def test_no_sharing_runs_as_the_plain_step(part):
+@pytest.mark.parametrize("part,chunk", [(64, 0), (0, 0), (0, 64)])
+def test_no_sharing_runs_as_the_plain_step(part, chunk):
     _require_gpu()
     w = W.custom_decode("cascade_none", 43, [1, 17, 300, 1025, 64], dtype="bf16", H=8, Hkv=2,
                         D=128, B=16, partition_size=part)
-    _check(w, part, 4, expect_groups=False)
+    _check(w, part, 4, expect_groups=False, chunk=chunk)
 
 
 ROUND_CASES = [
@@ -135,29 +154,34 @@ ROUND_CASES = [
 ]
 
 
+@pytest.mark.parametrize("chunk", [0, 512])
 @pytest.mark.parametrize("B,G,group,prompts,samples,appends", ROUND_CASES,
                          ids=[f"B{c[0]}-G{c[1]}-g{c[2]}-{c[3][0]}" for c in ROUND_CASES])
-def test_single_pass_rounds(B, G, group, prompts, samples, appends):
+def test_single_pass_rounds(B, G, group, prompts, samples, appends, chunk):
+    """Also chunked: the group's last item then reads several rounds of the
+    members' own tokens, reaching many slots past its own."""
     _require_gpu()
-    print(f"[cascade] rounds B={B} G={G} group={group} prompts={prompts}", flush=True)
+    print(f"[cascade] rounds B={B} G={G} group={group} prompts={prompts} chunk={chunk}",
+          flush=True)
     rows = [[appends[(g + j) % len(appends)] for j in range(samples)]
             for g in range(len(prompts))]
     w = W.custom_forks("cascade_rounds", 47, prompts, samples, rows, dtype="bf16", H=2 * G,
                        Hkv=2, D=128, B=B, partition_size=0)
-    _check(w, 0, group)
+    _check(w, 0, group, chunk=chunk)
 
 
+@pytest.mark.parametrize("chunk", [0, 256])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "calls"])
-def test_prefix_cache_batch_single_pass(fused):
+def test_prefix_cache_batch_single_pass(fused, chunk):
     """128 requests over 16 cached system prompts: the prompt blocks the
     prefix cache hands to each prompt's requests form the groups."""
     _require_gpu()
-    print(f"[cascade] prefix-cache batch fused={fused}", flush=True)
-    _check(W.prefix_cache_bf16(), 0, 8, fused=fused)
+    print(f"[cascade] prefix-cache batch fused={fused} chunk={chunk}", flush=True)
+    _check(W.prefix_cache_bf16(), 0, 8, fused=fused, chunk=chunk)
 
 
-@pytest.mark.parametrize("part", [0, 64])
-def test_prefix_cache_hits_and_evictions(part):
+@pytest.mark.parametrize("part,chunk", [(0, 0), (64, 0), (0, 32)])
+def test_prefix_cache_hits_and_evictions(part, chunk):
     """A tight pool: finished requests' cached blocks are evicted while other
     requests still hit theirs."""
     _require_gpu()
@@ -167,4 +191,30 @@ def test_prefix_cache_hits_and_evictions(part):
                 (1, 2), (0, 1)]
     w = W.custom_prefix("cascade_prefix", 53, systems, requests, dtype="bf16", H=8, Hkv=2,
                         D=128, B=B, finished={0, 3, 4, 6}, partition_size=part, num_blocks=24)
-    _check(w, part, 4, expect_groups=False)
+    _check(w, part, 4, expect_groups=False, chunk=chunk)
+
+
+def test_long_prompts_take_a_chunked_plan_by_themselves():
+    """Two prompts of ~9k tokens forked 8 ways on a 32q/8kv layer: the step
+    chooses 2048-token pieces (the single-pass plan would have 32
+    workgroups); one launch and separate calls against the oracle, and
+    bit-identical to each other."""
+    _require_gpu()
+    from paged_kv_cache_123_amd.step import DecodeStep
+    w = W.shared_long_prompt_bf16(num_groups=2, prompt=9000)
+    print(f"[cascade] {w.notes}", flush=True)
+    vals = W.make_values(w, DEV)
+    host = {k: to_host(v) for k, v in vals.items()}
+    step = DecodeStep(w.num_blocks, w.block_size, w.free_order, w.prefill, w.step, vals,
+                      w.scale, 0)
+    assert step.cascade == 4 and step.cascade_chunk == 2048
+    out = step.run(fused=True).clone()
+    torch.cuda.synchronize()
+    ora = OracleStep(w)
+    kc, vc = host["key_cache"], host["value_cache"]
+    ora.apply_copies(kc, vc)
+    ora.apply_scatter(kc, vc, host["new_key"], host["new_value"])
+    check_attention(to_host(out), ora.attention(host["query"], kc, vc), w.dtype, w.name)
+    step.run(fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), step.out.view(torch.int16))

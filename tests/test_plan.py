@@ -155,6 +155,66 @@ def _check_cascade_single(tables, lens, new, B, G):
     return items, chunks
 
 
+def _check_cascade_chunked(tables, lens, new, B, P, G):
+    """Chunked cascade plan: its groups and prefixes are the single-pass
+    plan's; every position of every sequence is read by exactly one item;
+    each (sequence, slot) the merge reads, ceil(L / P) slots, is written by
+    exactly one item, or marked empty by the group's last item; shared runs
+    lie in blocks all members hold before their first new token."""
+    from paged_kv_cache_123_amd import ops
+    plan, n, widest = ops.decode_plan_cascade(tables, lens, B, 0, G, new, chunk_tokens=P)
+    items = plan[:2 * n].reshape(-1, 2)
+    sec = plan[2 * n:]
+    nc = int(sec[0])
+    offs = sec[1:2 + nc]
+    prefixes = [int(x) for x in sec[2 + nc:2 + 2 * nc]]
+    mem = sec[2 + 2 * nc:]
+    assert len(mem) == offs[-1]
+    chunks = [list(mem[offs[c]:offs[c + 1]]) for c in range(nc)]
+    assert widest == max([len(c) for c in chunks], default=0)
+    single, sn = ops.decode_plan_cascade(tables, lens, B, 0, G, new)[:2]
+    s_items, s_chunks = _parse_cascade(single, sn)
+    assert sorted(map(sorted, s_chunks)) == sorted(map(sorted, chunks))
+    s_prefix = {tuple(s_chunks[-1 - x]): y for x, y in s_items.tolist() if x < 0}
+    assert {tuple(chunks[c]): prefixes[c] for c in range(nc)} == s_prefix
+    read = {s: np.zeros(int(L), np.int32) for s, L in enumerate(lens)}
+    slots, sizes = {}, []
+    for x, j in items.tolist():
+        if x < 0:
+            rows, prefix = chunks[-1 - x], prefixes[-1 - x]
+            pf = prefix // P
+            assert 0 <= j <= pf and 2 <= len(rows) <= G
+            a = j * P
+            b = a + P if j < pf else prefix
+            nblk = -(-b // B)
+            for r in rows:
+                assert b <= lens[r] - new[r]
+                assert list(tables[r][:nblk]) == list(tables[rows[0]][:nblk])
+                read[r][a:b] += 1
+                if j == pf:
+                    read[r][prefix:] += 1
+                    for q in range(pf + 1, -(-int(lens[r]) // P)):  # marked empty
+                        assert (r, q) not in slots
+                        slots[(r, q)] = "empty"
+                assert (r, j) not in slots
+                slots[(r, j)] = x
+            sizes.append(b - a + (sum(int(lens[r]) - prefix for r in rows) if j == pf else 0))
+        else:
+            L = int(lens[x])
+            assert 0 <= j * P < L
+            read[x][j * P:min((j + 1) * P, L)] += 1
+            assert (x, j) not in slots
+            slots[(x, j)] = x
+            sizes.append(min((j + 1) * P, L) - j * P)
+    for s_, r in read.items():
+        assert (r == 1).all(), f"sequence {s_}: a position read {set(r.tolist())} times"
+    want = {(s_, q) for s_ in range(len(lens)) for q in range(-(-int(lens[s_]) // P))}
+    assert set(slots) == want
+    buckets = [-(-x // 256) for x in sizes]
+    assert buckets == sorted(buckets, reverse=True)
+    return items, chunks
+
+
 def test_cascade_plan_groups_samples_of_one_prompt():
     from paged_kv_cache_123_amd.host import Pool
     B, P = 16, 256
@@ -193,6 +253,10 @@ def test_cascade_plan_groups_samples_of_one_prompt():
     prefix = {seqs[chunks[-1 - s][0]] // 10: p for s, p in items.tolist() if s < 0}
     assert prefix == {0: 1024, 1: 688, 2: 32, 3: 1024}
     assert sorted(len(c) for c in chunks) == [2] * 4 + [3] * 4
+    # chunked: the 1024-token prefixes in pieces of 256, the others with a
+    # remainder read by the group's last item
+    for chunk in (16, 256, 512, 48):
+        _check_cascade_chunked(tables, lens, new, B, chunk, 3)
 
 
 def test_cascade_plan_without_sharing_is_the_plain_plan():
@@ -248,6 +312,15 @@ def test_cascade_plan_random_forest(seed):
     G = int(rng.integers(2, 9))
     _check_cascade(tables, lens, new, B, P, G)
     _check_cascade_single(tables, lens, new, B, G)
+    _check_cascade_chunked(tables, lens, new, B, P, G)
+
+
+def test_chunked_cascade_plan_without_sharing_splits_every_sequence():
+    lens = np.array([1, 17, 300, 513], dtype=np.int32)
+    B = 16
+    tables = np.arange(4 * 40, dtype=np.int32).reshape(4, 40)
+    items, chunks = _check_cascade_chunked(tables, lens, np.ones(4, np.int32), B, 64, 8)
+    assert chunks == [] and len(items) == 1 + 1 + 5 + 9
 
 
 def test_cascade_plan_rejects_bad_arguments():
@@ -262,6 +335,8 @@ def test_cascade_plan_rejects_bad_arguments():
         ops.decode_plan_cascade(tables, lens, 16, 32, 4, [11, 1])  # more new tokens than length
     with pytest.raises(PagedKVError):
         ops.decode_plan_cascade(tables[:, :3], np.array([10, 64], np.int32), 16, 32, 4)
+    with pytest.raises(PagedKVError):
+        ops.decode_plan_cascade(tables, lens, 16, 0, 4, chunk_tokens=24)  # not a multiple of B
 
 
 # ---- query blocks ---------------------------------------------------------------

@@ -202,6 +202,40 @@ def shared_prefix_bf16(num_groups=16):
                     extra={"unique_blocks": unique, "prompts": prompts.tolist()})
 
 
+def shared_long_prompt_bf16(num_groups=2, prompt=16384, samples=8):
+    """Parallel sampling over long prompts on a grouped-query layer: each of a
+    few prompts of ``prompt`` + U{1..15} tokens is shared by ``samples``
+    samples that each append U{1..64} tokens; 32 query heads over 8 KV heads,
+    bf16, B = 16.  Few groups over long prefixes: a cascade plan with one
+    workgroup per group and KV head has few workgroups."""
+    rng = np.random.default_rng(10)
+    B = 16
+    prompts = prompt + rng.integers(1, 16, size=num_groups)
+    appends = rng.integers(1, 65, size=(num_groups, samples))
+    prefill, step, seqs, lens = [], [], [], []
+    for g in range(num_groups):
+        lead = g * samples
+        prefill += [("add", lead), ("append", lead, int(prompts[g]))]
+        for j in range(1, samples):
+            prefill.append(("fork", lead, lead + j))
+        for j in range(samples):
+            step.append((lead + j, int(appends[g, j])))
+            seqs.append(lead + j)
+            lens.append(int(prompts[g] + appends[g, j]))
+    own = sum(-(-int(prompts[g] + appends[g, j]) // B) - int(prompts[g]) // B
+              for g in range(num_groups) for j in range(samples))
+    unique = sum(int(p) // B for p in prompts) + own
+    nb = math.ceil(1.1 * unique)
+    order = rng.permutation(nb).astype(np.int32)
+    return Workload(name="shared_long_prompt_bf16", dtype="bf16", num_heads=32, num_kv_heads=8,
+                    head_size=128, block_size=B, num_blocks=nb, scale=1.0 / math.sqrt(128),
+                    sigma=1.0, seed=10, free_order=order, seqs=seqs, prefill=prefill, step=step,
+                    context_lens=lens,
+                    notes=f"{num_groups} prompts of {prompt}+U[1,15] tokens x {samples} samples, "
+                          "each appends U[1,64]; 32q/8kv x128 bf16, B=16",
+                    extra={"unique_blocks": unique, "prompts": prompts.tolist()})
+
+
 def shared_prefix_cascade_bf16(num_groups=16, partition_size=0, group=8):
     """The shared-prefix batch run through a cascade plan for groups of up to
     ``group`` samples: single pass (``partition_size`` 0: one workgroup per
@@ -414,6 +448,7 @@ CONFIGS = {
     "shared_prefix_bf16": shared_prefix_bf16,
     "long_context_bf16": long_context_bf16,
     "shared_prefix_cascade_bf16": shared_prefix_cascade_bf16,
+    "shared_long_prompt_bf16": shared_long_prompt_bf16,
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "llama7b_prefill512_fp16": llama7b_prefill512_fp16,
     "qwen72b_prefill512_bf16": qwen72b_prefill512_bf16,
