@@ -411,8 +411,10 @@ int32_t pa_paged_attention_decode_planned(void* out, const void* query, const vo
  * position L_s - n_s (a fresh copy-on-write block, [VLLBC] paper section
  * 4.4 / Fig. 8) first receives the slots before that position from block
  * cow_src[s].  Each attention workgroup writes the rows it then reads, so
- * the caches, slot_mapping and out end exactly as with the four separate
- * calls.
+ * slot_mapping, out and every cache slot below L_s end exactly as with the
+ * four separate calls.  The slots at or past L_s of a copied block, which
+ * pa_copy_blocks fills from the source block, are left unspecified here
+ * (no step reads a slot before writing it).
  *   key_cache, value_cache  written in place
  *   query_start_loc  device int32 [num_seqs + 1]
  *   key, value       device, 16-byte aligned rows [T][num_kv_heads][head_size]
@@ -634,7 +636,10 @@ int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key
  * key/value rows and the old slots of a copied tail from its source block,
  * so no workgroup reads a slot the launch writes, and the result is that of
  * the separate calls (copy_blocks, compute_slot_mapping, reshape_and_cache,
- * pa_paged_attention_prefill), bit for bit.
+ * pa_paged_attention_prefill), bit for bit, in out, slot_mapping and every
+ * cache slot below a sequence's length.  The slots at or past that length
+ * of a copied block, which copy_blocks fills from the source block, are left
+ * unspecified.
  *   query_start_loc  device int32 [num_seqs + 1]: sequence s's new tokens are
  *                    the rows query_start_loc[s] .. [s + 1] - 1 of query, key
  *                    and value; row_seq indexes these sequences and row_qsl
@@ -647,7 +652,8 @@ int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key
  *   slot_mapping     device int64 [num_tokens] output, or NULL
  * block_tables must hold each sequence's blocks after the step's
  * allocation.  Errors: those of pa_paged_attention_prefill, plus PA_EINVAL
- * for a NULL query_start_loc, key or value and misaligned rows or strides.
+ * for a NULL query_start_loc, key or value, misaligned rows or strides, and
+ * strides of 2^35 bytes or more.
  * ---------------------------------------------------------------------- */
 int32_t pa_prefill_step(void* out, const void* query, void* key_cache, void* value_cache,
                         const int32_t* block_tables, int64_t bt_stride, const int32_t* row_seq,

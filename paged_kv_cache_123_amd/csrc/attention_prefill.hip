@@ -26,6 +26,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "decode_common.h"
 #include "launch.h"
@@ -62,7 +63,10 @@ __device__ __forceinline__ int value_slot(int d, int k) {
   return d * 8 + (k ^ ((d ^ (d >> 3)) & 7));
 }
 
-template <int DT>
+// BIG_B: blocks of at least 4 tokens, so that the four keys a thread moves
+// per tile share one block.  APPEND: the step's cache writes ride in the
+// launch (pa_prefill_step).
+template <int DT, bool BIG_B, bool APPEND>
 __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
     const void* value_cache, const int32_t* __restrict__ block_tables, int64_t bt_stride,
@@ -81,7 +85,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   constexpr int PER = 4;           // keys of each cache a thread moves per tile
   static_assert(KT * DV == NT * PER && KT % 32 == 0, "tile shape");
   using MM = Mma<DT>;
-  constexpr bool kSplitP = DT == PA_BF16;  // probabilities as head + remainder
 
   __shared__ uint4 sk[2][KT * ROW];
   // values transposed: 128 dims x 64 keys of 16 bits per buffer, keys in
@@ -111,8 +114,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   // keys this column sees: [lo, bound)
   const int bound = valid ? L - qlen + qi + 1 : 0;
   const int lo = !valid ? INT_MAX : window > 0 ? max(0, bound - window) : 0;
-  // the block's first visible key
-  const int lo_min = window > 0 ? max(0, L - qlen + 1 - window) : 0;
+  // the block's first visible key, rounded down to a multiple of 4 with
+  // blocks of 4 or more keys (the keys before it are masked and lie in its
+  // block): a thread's four keys of a tile then share one block
+  const int lo_first = window > 0 ? max(0, L - qlen + 1 - window) : 0;
+  const int lo_min = BIG_B ? lo_first & ~3 : lo_first;
   // and the keys every column of this wave sees: [wlo_max, whi_min) (empty
   // when a column has no query)
   int whi_min = valid ? bound : 0, wlo_max = valid ? lo : INT_MAX;
@@ -153,19 +159,34 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * bt_stride;
   const uint4* kc = static_cast<const uint4*>(key_cache);
   const uint4* vc = static_cast<const uint4*>(value_cache);
+  // this thread's unit of its KV head's rows: a cache row of block b, offset
+  // o is at (b * H_kv * B + o) * DV units from these (block ids and the
+  // block stride in units fit 32 bits: one 32 x 32 -> 64-bit product)
+  const uint4* kc_my = kc + head_off_v + my_unit;
+  const uint4* vc_my = vc + head_off_v + my_unit;
+  const uint32_t blk_units = static_cast<uint32_t>(blk_stride_v);
 
   // The step's cache writes, in the same launch: no workgroup reads a slot
   // written here.  Keys from the sequence's first new position p0 on come
   // from the step's key/value rows, the old slots of a copied tail block
-  // from its source block.  Each row stores the rows of its own tokens as
-  // its tiles load them (and, for KV head 0, their slots); the sequence's
+  // from its source block.  Each row stores the rows of its own tokens
+  // after its attention (and, for KV head 0, their slots); the sequence's
   // first row copies the old slots here.
   int p0 = INT_MAX, seq_q0 = 0, special = INT_MAX;
   int64_t cow = -1;
-  if (ap.qsl) {
+  // this thread's unit of new row p0 and of slot 0 of the copied tail
+  // block's source (strides below 2^31 units)
+  const uint4 *key_new = nullptr, *value_new = nullptr, *key_cow = nullptr, *value_cow = nullptr;
+  const uint32_t key_str = static_cast<uint32_t>(ap.key_stride_v);
+  const uint32_t value_str = static_cast<uint32_t>(ap.value_stride_v);
+  if (APPEND) {
     seq_q0 = ap.qsl[s];
     p0 = L - qlen - (q0 - seq_q0);
+    key_new = ap.key + seq_q0 * ap.key_stride_v + kvh * DV + my_unit;
+    value_new = ap.value + seq_q0 * ap.value_stride_v + kvh * DV + my_unit;
     cow = ap.cow_src ? ap.cow_src[s] : -1;
+    key_cow = kc_my + max(cow, int64_t{0}) * blk_stride_v;
+    value_cow = vc_my + max(cow, int64_t{0}) * blk_stride_v;
     special = cow >= 0 ? (p0 >> log2_block) << log2_block : p0;  // first key read elsewhere
     if (cow >= 0 && q0 == seq_q0) {
       const int jb = p0 >> log2_block;
@@ -178,178 +199,217 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     }
   }
 
-  for (int c0 = lo_min; c0 < L; c0 += kChunkTokens) {
-    const int c1 = min(c0 + kChunkTokens, L);
-    const int b0 = c0 >> log2_block;
-    const int nb = ((c1 - 1) >> log2_block) - b0 + 1;
-    for (int i = tid; i < nb; i += NT) sm_bt[i] = bt_row[b0 + i];
-    __syncthreads();
-    const int ntiles = (c1 - c0 + KT - 1) / KT;
-    // rows of tile t into registers; rows past the chunk repeat its last row,
-    // so tiles beyond the last are loaded too (unconditional loads keep the
-    // wait counts of the pipeline static) and hit that one row
-    // thread (my_keys, my_unit) moves keys 4 my_keys .. + 3, dims 8 my_unit
-    // .. + 7 of each tile
-    auto gload = [&](int t, uint4 (&pk)[PER], uint4 (&pv)[PER]) {
+  // keys [lo_min, L) in two ranges: the cache's rows of the tiles before
+  // the first key read elsewhere (all of them without the step's writes),
+  // then the rest, one copy of the loop per range (no branch on the range
+  // in the pipeline).  The ranges meet on a tile boundary of the single
+  // range: the same tiles, so the same arithmetic, as without the writes.
+  const int split =
+      APPEND ? lo_min + (max(min(special, L) - lo_min, 0) / KT) * KT : L;
+  auto range = [&](auto phase_tag, int r_begin, int r_end) {
+    constexpr bool phase = decltype(phase_tag)::value;
+    for (int c0 = r_begin; c0 < r_end; c0 += kChunkTokens) {
+      const int c1 = min(c0 + kChunkTokens, r_end);
+      const int b0 = c0 >> log2_block;
+      const int nb = ((c1 - 1) >> log2_block) - b0 + 1;
+      for (int i = tid; i < nb; i += NT) sm_bt[i] = bt_row[b0 + i];
+      __syncthreads();
+      const int ntiles = (c1 - c0 + KT - 1) / KT;
+      // rows of tile t into registers; rows past the chunk repeat its last row,
+      // so tiles beyond the last are loaded too (unconditional loads keep the
+      // wait counts of the pipeline static) and hit that one row
+      // thread (my_keys, my_unit) moves keys 4 my_keys .. + 3, dims 8 my_unit
+      // .. + 7 of each tile; the addresses first, then one load per key and
+      // cache (loads in branches would leave the pipeline's waits to the
+      // compiler's most cautious count)
+      auto gload = [&](int t, uint4 (&pk)[PER], uint4 (&pv)[PER]) {
+        const int t0 = c0 + t * KT + 4 * my_keys;  // this thread's first key of the tile
+        const uint4 *ks[PER], *vs[PER];
+        if constexpr (APPEND && phase) {
+          // cache rows (first tile only), the copied tail block's old
+          // slots, then the step's new rows: selects, no branches
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int tok = min(c0 + t * KT + 4 * my_keys + j, c1 - 1);
-        const uint4 *ks, *vs;
-        if (tok < special) {  // the sequence's other blocks read these rows too: cached loads
-          const int64_t idx = static_cast<int64_t>(sm_bt[(tok >> log2_block) - b0]) *
-                              blk_stride_v + head_off_v + (tok & (B - 1)) * DV;
-          ks = kc + idx;
-          vs = vc + idx;
-        } else if (tok >= p0) {  // a new row of the step
-          ks = ap.key + (seq_q0 + tok - p0) * ap.key_stride_v + kvh * DV;
-          vs = ap.value + (seq_q0 + tok - p0) * ap.value_stride_v + kvh * DV;
-        } else {  // an old slot of the copied tail block
-          const int64_t idx = cow * blk_stride_v + head_off_v + (tok & (B - 1)) * DV;
-          ks = kc + idx;
-          vs = vc + idx;
+          for (int j = 0; j < PER; ++j) {
+            const int tok = min(t0 + j, c1 - 1);
+            const uint64_t r = static_cast<uint32_t>(max(tok - p0, 0));
+            const uint32_t off = (tok & (B - 1)) * DV;
+            const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
+                                     sm_bt[(tok >> log2_block) - b0])) * blk_units;
+            const bool fresh = tok >= p0, copied = tok >= special;
+            const uint4 *kf = key_new + r * key_str, *vf = value_new + r * value_str;
+            const uint4 *kw = key_cow + off, *vw = value_cow + off;
+            const uint4 *kr = kc_my + row + off, *vr = vc_my + row + off;
+            ks[j] = __builtin_unpredictable(fresh) ? kf : __builtin_unpredictable(copied) ? kw : kr;
+            vs[j] = __builtin_unpredictable(fresh) ? vf : __builtin_unpredictable(copied) ? vw : vr;
+          }
+        } else if constexpr (BIG_B) {
+          // the four keys (or the chunk's last key they are clamped to) share
+          // one block: blocks hold a multiple of 4 keys and t0 is 4-aligned
+          const int tc = min(t0, c1 - 1);
+          const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
+                                   sm_bt[(tc >> log2_block) - b0])) * blk_units;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const uint32_t off = (min(t0 + j, c1 - 1) & (B - 1)) * DV;
+            ks[j] = kc_my + row + off;
+            vs[j] = vc_my + row + off;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const int tok = min(t0 + j, c1 - 1);
+            const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
+                                     sm_bt[(tok >> log2_block) - b0])) * blk_units;
+            const uint32_t off = (tok & (B - 1)) * DV;
+            ks[j] = kc_my + row + off;
+            vs[j] = vc_my + row + off;
+          }
         }
-        pk[j] = load_cached(ks + my_unit);
-        pv[j] = load_cached(vs + my_unit);
-      }
-    };
-    auto lstore = [&](int t, int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) sk[buf][(4 * my_keys + j) * ROW + my_unit] = pk[j];
-      if (ap.qsl) {  // this row's own tokens go to their cache slots
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-          const int tok = c0 + t * KT + 4 * my_keys + j;
-          if (tok >= L - qlen && tok < c1) {
-            const int64_t phys = sm_bt[(tok >> log2_block) - b0];
-            const int64_t dst = phys * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + my_unit;
-            ap.key_cache[dst] = pk[j];
-            ap.value_cache[dst] = pv[j];
-            if (ap.slot_mapping && kvh == 0 && my_unit == 0)
-              ap.slot_mapping[q0 + tok - (L - qlen)] = phys * B + (tok & (B - 1));
-          }
+          pk[j] = load_cached(ks[j]);
+          pv[j] = load_cached(vs[j]);
         }
-      }
-      // each dim's four keys as one 8-byte piece
-      uint2* vt = reinterpret_cast<uint2*>(sv[buf]);
+      };
+      auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = dword(pv[0], w), x1 = dword(pv[1], w);
-        const uint32_t x2 = dword(pv[2], w), x3 = dword(pv[3], w);
-        vt[v_store[2 * w]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u),
-                                        __builtin_amdgcn_perm(x3, x2, 0x05040100u));
-        vt[v_store[2 * w + 1]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u),
-                                            __builtin_amdgcn_perm(x3, x2, 0x07060302u));
-      }
-    };
-    // One tile in two halves: scores and softmax, then the value products.
-    // Between them the pipeline stores the next tile and issues the loads of
-    // a later one, so that their instructions interleave with the MFMAs.
-    // Tiles outside a wave's keys run too (their probabilities are 0).
-    constexpr int NS = KT / 16;
-    auto scores = [&](int t, int buf, uint4 (&phi)[NS / 2], uint4 (&plo)[NS / 2]) {
-      const int t0 = c0 + t * KT;
-      // scores of the whole tile first (independent MFMA chains): lane
-      // (col, grp) gets those of keys 16 st + 4 grp + j of its column
-      f32x4 sc[NS];
+        for (int j = 0; j < PER; ++j) sk[buf][(4 * my_keys + j) * ROW + my_unit] = pk[j];
+        // each dim's four keys as one 8-byte piece
+        uint2* vt = reinterpret_cast<uint2*>(sv[buf]);
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        sc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = dword(pv[0], w), x1 = dword(pv[1], w);
+          const uint32_t x2 = dword(pv[2], w), x3 = dword(pv[3], w);
+          vt[v_store[2 * w]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u),
+                                          __builtin_amdgcn_perm(x3, x2, 0x05040100u));
+          vt[v_store[2 * w + 1]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u),
+                                              __builtin_amdgcn_perm(x3, x2, 0x07060302u));
+        }
+      };
+      // One tile in two halves: scores and softmax, then the value products.
+      // Between them the pipeline stores the next tile and issues the loads of
+      // a later one, so that their instructions interleave with the MFMAs.
+      // Tiles outside a wave's keys run too (their probabilities are 0).
+      constexpr int NS = KT / 16;
+      auto scores = [&](int t, int buf, uint4 (&phi)[NS / 2]) {
+        const int t0 = c0 + t * KT;
+        // scores of the whole tile first (independent MFMA chains): lane
+        // (col, grp) gets those of keys 16 st + 4 grp + j of its column
+        f32x4 sc[NS];
 #pragma unroll
-        for (int k = 0; k < NK; ++k)
-          sc[st] = MM::k32(sk[buf][(st * 16 + col) * ROW + k * 4 + grp], qv[k], sc[st]);
-      }
-      // a tile inside every column's keys needs no mask (wave-uniform)
-      if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
+        for (int st = 0; st < NS; ++st) {
+          sc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k = 0; k < NK; ++k)
+            sc[st] = MM::k32(sk[buf][(st * 16 + col) * ROW + k * 4 + grp], qv[k], sc[st]);
+        }
+        // a tile inside every column's keys needs no mask (wave-uniform)
+        if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
+#pragma unroll
+          for (int st = 0; st < NS; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int tt = t0 + st * 16 + 4 * grp + j;
+              const bool vis = (tt < bound) & (tt >= lo) & (tt < c1);
+              sc[st][j] = vis ? sc[st][j] : -INFINITY;
+            }
+        }
+        float mt = -INFINITY;
 #pragma unroll
         for (int st = 0; st < NS; ++st)
+          mt = fmaxf(mt, fmaxf(fmaxf(sc[st][0], sc[st][1]), fmaxf(sc[st][2], sc[st][3])));
+        mt = column_max(mt) * scale_log2;
+        // The reference maximum moves only when the tile's maximum exceeds it
+        // by more than 2^8: probabilities stay below 256 and the
+        // accumulators are rescaled only on such rare jumps.
+        const float mref = mt > m + 8.0f ? mt : m;
+        const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
+        const float corr = __builtin_amdgcn_exp2f(m - ms);
+        if (__any(mref != m)) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tt = t0 + st * 16 + 4 * grp + j;
-            const bool vis = (tt < bound) & (tt >= lo) & (tt < c1);
-            sc[st][j] = vis ? sc[st][j] : -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-        mt = fmaxf(mt, fmaxf(fmaxf(sc[st][0], sc[st][1]), fmaxf(sc[st][2], sc[st][3])));
-      mt = column_max(mt) * scale_log2;
-      // The reference maximum moves only when the tile's maximum exceeds it
-      // by more than 2^8: probabilities stay below 256 and the
-      // accumulators are rescaled only on such rare jumps.
-      const float mref = mt > m + 8.0f ? mt : m;
-      const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
-      const float corr = __builtin_amdgcn_exp2f(m - ms);
-      float p[NS][4];
-      float tsum = 0.0f;
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[st][j] = __builtin_amdgcn_exp2f(fmaf(sc[st][j], scale_log2, -ms));
-          tsum += p[st][j];
+          for (int e = 0; e < NE; ++e) o[e] *= corr;
         }
-      lsum = lsum * corr + tsum;
-      if (__any(mref != m)) {
+        m = mref;
+        // Probabilities rounded once to the storage's 16-bit type, two per
+        // conversion, for the value products over pairs of sub-tiles (K = 32
+        // keys per MFMA), and summed as rounded: the output is then exactly a
+        // convex combination of the values with these weights, each within
+        // 2^-9 (bf16) or 2^-12 (fp16) of its own probability.
+        float tsum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) o[e] *= corr;
-      }
-      m = mref;
-      // probabilities in 16 bits for the value products over pairs of
-      // sub-tiles (K = 32 keys per MFMA).  bf16 keeps 8 significant bits, so
-      // its rounding remainder goes into a second product; fp16 rounding
-      // (11 bits) is already at the level of the output's own.
+        for (int sp = 0; sp < NS; sp += 2) {
+          uint32_t w[4];
 #pragma unroll
-      for (int sp = 0; sp < NS; sp += 2) {
-        uint32_t hi[8], rem[8];
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float back, unused;
-            hi[4 * h + j] = MM::round16(p[sp + h][j], back);
-            rem[4 * h + j] = kSplitP ? MM::round16(p[sp + h][j] - back, unused) : 0u;
-          }
-        phi[sp / 2] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                 hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-        plo[sp / 2] = make_uint4(rem[0] | (rem[1] << 16), rem[2] | (rem[3] << 16),
-                                 rem[4] | (rem[5] << 16), rem[6] | (rem[7] << 16));
-      }
-    };
-    auto values = [&](int buf, const uint4 (&phi)[NS / 2], const uint4 (&plo)[NS / 2]) {
-#pragma unroll
-      for (int sp = 0; sp < NS; sp += 2) {
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          // dim 16 e + col of the eight keys, in the order of phi
-          const uint4 a = sv[buf][value_slot(16 * e + col, 2 * sp + grp)];
-          o[e] = MM::k32(a, phi[sp / 2], o[e]);
-          if constexpr (kSplitP) o[e] = MM::k32(a, plo[sp / 2], o[e]);
+            for (int j = 0; j < 4; j += 2) {
+              w[2 * h + j / 2] =
+                  MM::pack2(__builtin_amdgcn_exp2f(fmaf(sc[sp + h][j], scale_log2, -ms)),
+                            __builtin_amdgcn_exp2f(fmaf(sc[sp + h][j + 1], scale_log2, -ms)));
+              tsum = MM::sum2(w[2 * h + j / 2], tsum);
+            }
+          phi[sp / 2] = make_uint4(w[0], w[1], w[2], w[3]);
         }
+        lsum = lsum * corr + tsum;
+      };
+      auto values = [&](int buf, const uint4 (&phi)[NS / 2]) {
+#pragma unroll
+        for (int sp = 0; sp < NS; sp += 2) {
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
+            // dim 16 e + col of the eight keys, in the order of phi
+            const uint4 a = sv[buf][value_slot(16 * e + col, 2 * sp + grp)];
+            o[e] = MM::k32(a, phi[sp / 2], o[e]);
+          }
+        }
+      };
+      // LDS holds tile t and t + 1 alternately; registers A and B carry the
+      // loads of the next two tiles, so two tiles' rows are in flight while
+      // one is computed
+      uint4 ak[PER], av[PER], bk[PER], bv[PER];
+      gload(0, ak, av);
+      lstore(0, ak, av);
+      gload(1, ak, av);
+      gload(2, bk, bv);
+      __syncthreads();
+      // (pairs of tiles with no exit between them: the waits for the loads
+      // in flight stay counted, not full drains)
+      uint4 phi[NS / 2];
+      int t = 0;
+      for (; t + 1 < ntiles; t += 2) {
+        scores(t, 0, phi);
+        lstore(1, ak, av);
+        gload(t + 3, ak, av);
+        values(0, phi);
+        __syncthreads();
+        scores(t + 1, 1, phi);
+        lstore(0, bk, bv);
+        gload(t + 4, bk, bv);
+        values(1, phi);
+        __syncthreads();
       }
-    };
-    // LDS holds tile t and t + 1 alternately; registers A and B carry the
-    // loads of the next two tiles, so two tiles' rows are in flight while
-    // one is computed
-    uint4 ak[PER], av[PER], bk[PER], bv[PER];
-    gload(0, ak, av);
-    lstore(0, 0, ak, av);
-    gload(1, ak, av);
-    gload(2, bk, bv);
-    __syncthreads();
-    uint4 phi[NS / 2], plo[NS / 2];
-    for (int t = 0; t < ntiles; t += 2) {
-      scores(t, 0, phi, plo);
-      lstore(t + 1, 1, ak, av);
-      gload(t + 3, ak, av);
-      values(0, phi, plo);
-      __syncthreads();
-      if (t + 1 >= ntiles) break;
-      scores(t + 1, 1, phi, plo);
-      lstore(t + 2, 0, bk, bv);
-      gload(t + 4, bk, bv);
-      values(1, phi, plo);
-      __syncthreads();
+      if (t < ntiles) {  // an odd last tile, in buffer 0
+        scores(t, 0, phi);
+        values(0, phi);
+      }
+    }
+  };
+  range(std::false_type{}, lo_min, split);
+  if constexpr (APPEND) range(std::true_type{}, split, L);
+
+  if (APPEND) {
+    // this row's own tokens to their slots (and, for KV head 0, the slots to
+    // the mapping), after the pipeline: its stores would hold up the waits
+    // for the loads in flight
+    for (int i = tid; i < qlen * DV; i += NT) {
+      const int tq = i / DV, u = i % DV;
+      const int tok = L - qlen + tq;
+      const int64_t phys = bt_row[tok >> log2_block];
+      const int64_t dst = phys * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + u;
+      ap.key_cache[dst] = ap.key[(q0 + tq) * ap.key_stride_v + kvh * DV + u];
+      ap.value_cache[dst] = ap.value[(q0 + tq) * ap.value_stride_v + kvh * DV + u];
+      if (ap.slot_mapping && kvh == 0 && u == 0)
+        ap.slot_mapping[q0 + tq] = phys * B + (tok & (B - 1));
     }
   }
 
@@ -385,16 +445,24 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_rows) * a.num_kv_heads));
   const float sl2 = a.scale * kLog2e;
-  if (a.dtype == PA_BF16)
-    hipLaunchKernelGGL(prefill_kernel<PA_BF16>, grid, dim3(kPrefillWaves * 64), 0, stream, a.out,
-                       a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
-                       a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,
-                       a.num_kv_heads, log2_block, log2_group, sl2, a.window, a.append);
-  else
-    hipLaunchKernelGGL(prefill_kernel<PA_F16>, grid, dim3(kPrefillWaves * 64), 0, stream, a.out,
-                       a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,
-                       a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,
-                       a.num_kv_heads, log2_block, log2_group, sl2, a.window, a.append);
+  const bool big = log2_block >= 2, append = a.append.qsl != nullptr;
+#define PA_PREFILL(DT, BIG, APP)                                                              \
+  hipLaunchKernelGGL((prefill_kernel<DT, BIG, APP>), grid, dim3(kPrefillWaves * 64), 0, stream, \
+                     a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,   \
+                     a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,   \
+                     a.num_kv_heads, log2_block, log2_group, sl2, a.window, a.append)
+#define PA_PREFILL_DT(DT)                            \
+  if (big && append) PA_PREFILL(DT, true, true);     \
+  else if (big) PA_PREFILL(DT, true, false);         \
+  else if (append) PA_PREFILL(DT, false, true);      \
+  else PA_PREFILL(DT, false, false)
+  if (a.dtype == PA_BF16) {
+    PA_PREFILL_DT(PA_BF16);
+  } else {
+    PA_PREFILL_DT(PA_F16);
+  }
+#undef PA_PREFILL_DT
+#undef PA_PREFILL
   return hipGetLastError();
 }
 

@@ -859,6 +859,8 @@ int32_t pa_prefill_step(void* out, const void* query, void* key_cache, void* val
       (value_stride * eb) % 16 != 0 || !aligned16(key) || !aligned16(value))
     return fail(PA_EINVAL, "pa_prefill_step: key/value rows must be 16-byte aligned with a "
                            "stride of at least num_kv_heads * head_size elements");
+  if (key_stride * eb / 16 > INT32_MAX || value_stride * eb / 16 > INT32_MAX)
+    return fail(PA_EINVAL, "pa_prefill_step: key/value row strides must stay below 2^35 bytes");
   a.append = pa::dev::AppendArgs{query_start_loc, cow_src, static_cast<const uint4*>(key),
                                  static_cast<const uint4*>(value), key_stride * eb / 16,
                                  value_stride * eb / 16, static_cast<uint4*>(key_cache),

@@ -287,6 +287,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 template <int DT>
@@ -308,6 +309,16 @@ struct Mma<PA_BF16> {
     back = static_cast<float>(h);
     return __builtin_bit_cast(uint16_t, h);
   }
+  // a and b rounded to nearest even, a in the low half (one conversion)
+  __device__ static uint32_t pack2(float a, float b) {
+    const float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf162_t));
+  }
+  // acc + the two 16-bit values of p, in fp32 (one dot product with (1, 1))
+  __device__ static float sum2(uint32_t p, float acc) {
+    const bf162_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, p), one, acc, false);
+  }
 };
 
 template <>
@@ -324,6 +335,14 @@ struct Mma<PA_F16> {
     const _Float16 h = static_cast<_Float16>(x);
     back = static_cast<float>(h);
     return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static uint32_t pack2(float a, float b) {
+    const float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
+  }
+  __device__ static float sum2(uint32_t p, float acc) {
+    const half2_t one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, p), one, acc, false);
   }
 };
 
