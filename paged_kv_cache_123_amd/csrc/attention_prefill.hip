@@ -4,24 +4,29 @@
 // step's tokens out by query_start_loc).  The result is that of
 // pa_paged_attention_multi; only the work layout differs.
 //
-// The host cuts each sequence's new tokens into query blocks of 64/G tokens
-// (pa_query_blocks): with G query heads per KV head, a block holds 64 query
+// The host cuts each sequence's new tokens into query blocks of 128/G tokens
+// (pa_query_blocks): with G query heads per KV head, a block holds 128 query
 // vectors (token, head).  One workgroup of four waves serves one (block, KV
-// head); wave w owns query vectors 16w .. 16w+15, the 16 columns of its
-// matrix-core tiles.  The workgroup walks the keys the block sees in tiles of
-// 64 tokens, double-buffered in LDS, with the loads of the next two tiles in
-// registers while one is computed, so each K/V row is read once per 64
-// query vectors.  Every wave sees every tile, keeps the online softmax of
-// its own columns and writes its outputs itself: no merge across waves.  K
-// rows sit in LDS as stored, padded to 17 16-byte units so that the 16 rows
-// one score MFMA reads fall into different banks; V is transposed into the
-// value MFMA's operand order (value_slot).
+// head); wave w owns query vectors 32w .. 32w+31, two groups of 16, the
+// columns of its matrix-core tiles.  The workgroup walks the keys the block
+// sees in tiles of 32 tokens, double-buffered in LDS, with the loads of the
+// next two tiles in registers while one is computed, so each K/V row is read
+// from memory once per 128 query vectors and from LDS once per 32.  Each
+// operand fragment a wave reads from LDS feeds the MFMAs of both of its
+// groups.  Every wave sees every tile, keeps the online softmax of its own
+// columns and writes its outputs itself: no merge across waves.
+//
+// K and V rows sit in LDS as stored, K rows padded to 17 16-byte units so
+// that the 16 rows one score MFMA reads fall into different banks, V rows to
+// 18 units so that the 8 rows of half a wave's transposing read do; the value
+// MFMA's operand (8 keys of one dim per lane) comes from the transposing LDS
+// read of 16-bit elements.
 //
 // With the step's cache writes in the same launch (pa_prefill_step), keys
 // from a sequence's first new position on are read from the step's key/value
 // rows and the old slots of a copied tail block from its source block, so no
 // workgroup reads a slot the launch writes; each row stores its own tokens'
-// rows as its tiles bring them through the registers.
+// rows after its attention.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -38,7 +43,8 @@ namespace {
 using namespace dev;
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillTile = 64;  // key tokens per LDS tile
+constexpr int kPrefillGroups = 2;  // 16-column query groups per wave
+constexpr int kPrefillTile = 32;   // key tokens per LDS tile
 
 // Maximum over the four lane groups of a column (lanes 16 and 32 apart):
 // each permlane swap trades rows of 16 lanes between its two results, so
@@ -52,18 +58,20 @@ __device__ __forceinline__ float column_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Transposed value tile: row d (one dim) holds the tile's 64 keys of that
-// dim, 128 bytes = 8 units of 16 bytes.  Unit k of a row holds the eight keys
-// one lane passes to a K = 32 value MFMA (keys 32 (k/4) + 4 (k%4) + 0..3 and
-// the same plus 16, the order of the probabilities of lane group k%4), and it
-// is stored at unit k ^ (d ^ d/8) % 8: the 16 dims one MFMA reads (16 e ..
-// 16 e + 15) fall into distinct units, and so, two by two, do the 16 dims of
-// one 8-byte store instruction.
-__device__ __forceinline__ int value_slot(int d, int k) {
-  return d * 8 + (k ^ ((d ^ (d >> 3)) & 7));
+typedef short lds_s4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) lds_s4_t* lds_s4_ptr;
+
+// Transposing LDS read of 16-bit elements: in each group of 16 lanes, lane
+// i gets element i % 4 of the 4-element pieces that lanes i / 4, i / 4 + 4,
+// i / 4 + 8 and i / 4 + 12 address.  With lane 4 r + c pointing at row r,
+// elements 4 c .. 4 c + 3 of a row-major tile, lane i receives the four rows'
+// element i: a column.
+__device__ __forceinline__ uint2 read_columns(const void* lds_addr) {
+  const lds_s4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_addr));
+  return __builtin_bit_cast(uint2, x);
 }
 
-// BIG_B: blocks of at least 4 tokens, so that the four keys a thread moves
+// BIG_B: blocks of at least 2 tokens, so that the two keys a thread moves
 // per tile share one block.  APPEND: the step's cache writes ride in the
 // launch (pa_prefill_step).
 template <int DT, bool BIG_B, bool APPEND>
@@ -76,20 +84,21 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     int32_t log2_group, float scale_log2, int32_t window, AppendArgs ap) {
   constexpr int NW = kPrefillWaves;
   constexpr int NT = NW * 64;
+  constexpr int QG = kPrefillGroups;
   constexpr int D = 128;
   constexpr int DV = D / 8;        // 16-byte units per token row
-  constexpr int NK = D / 32;       // score MFMAs per 16-token sub-tile
-  constexpr int NE = 8;            // value MFMA chunks
+  constexpr int NK = D / 32;       // score MFMAs per 16-token sub-tile and group
+  constexpr int NE = 8;            // value MFMA chunks (16 dims each)
   constexpr int KT = kPrefillTile;
-  constexpr int ROW = DV + 1;      // padded LDS row, in 16-byte units
-  constexpr int PER = 4;           // keys of each cache a thread moves per tile
-  static_assert(KT * DV == NT * PER && KT % 32 == 0, "tile shape");
+  constexpr int NS = KT / 16;      // score sub-tiles per tile
+  constexpr int KROW = DV + 1;     // padded LDS rows, in 16-byte units
+  constexpr int VROW = DV + 2;
+  constexpr int PER = 2;           // keys of each cache a thread moves per tile
+  static_assert(KT * DV == NT * PER && NS == 2, "tile shape");
   using MM = Mma<DT>;
 
-  __shared__ uint4 sk[2][KT * ROW];
-  // values transposed: 128 dims x 64 keys of 16 bits per buffer, keys in
-  // MFMA operand order and 16-byte units XOR-swizzled by the dim (value_slot)
-  __shared__ uint4 sv[2][D * KT / 8];
+  __shared__ uint4 sk[2][KT * KROW];
+  __shared__ uint4 sv[2][KT * VROW];
   __shared__ int32_t sm_bt[kChunkTokens];
 
   // without a list, the last row first: the rows of a sequence run together,
@@ -107,51 +116,67 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int gmask = (1 << log2_group) - 1;
-  const int v = wave * 16 + col;    // query vector of this lane's column
-  const int qi = v >> log2_group;   // its token within the block
-  const bool valid = qi < qlen;
-  const int h = (kvh << log2_group) + (v & gmask);
-  // keys this column sees: [lo, bound)
-  const int bound = valid ? L - qlen + qi + 1 : 0;
-  const int lo = !valid ? INT_MAX : window > 0 ? max(0, bound - window) : 0;
-  // the block's first visible key, rounded down to a multiple of 4 with
-  // blocks of 4 or more keys (the keys before it are masked and lie in its
-  // block): a thread's four keys of a tile then share one block
-  const int lo_first = window > 0 ? max(0, L - qlen + 1 - window) : 0;
-  const int lo_min = BIG_B ? lo_first & ~3 : lo_first;
-  // and the keys every column of this wave sees: [wlo_max, whi_min) (empty
-  // when a column has no query)
-  int whi_min = valid ? bound : 0, wlo_max = valid ? lo : INT_MAX;
+  // group g's column of this lane: query vector v[g], its token qi[g] within
+  // the block and its head hq[g]; the keys it sees: [lo[g], bound[g])
+  int qi[QG], hq[QG], bound[QG], lo[QG];
+  bool valid[QG];
+  // the keys every column of this wave sees, [wlo_max, whi_min) (empty when
+  // a column has no query), and those some column sees, [wlo_min, whi_max)
+  int whi_min = INT_MAX, wlo_max = 0, whi_max = 0, wlo_min = INT_MAX;
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const int v = wave * (16 * QG) + g * 16 + col;
+    qi[g] = v >> log2_group;
+    valid[g] = qi[g] < qlen;
+    hq[g] = (kvh << log2_group) + (v & gmask);
+    bound[g] = valid[g] ? L - qlen + qi[g] + 1 : 0;
+    lo[g] = !valid[g] ? INT_MAX : window > 0 ? max(0, bound[g] - window) : 0;
+    whi_min = min(whi_min, bound[g]);
+    wlo_max = max(wlo_max, valid[g] ? lo[g] : INT_MAX);
+    whi_max = max(whi_max, bound[g]);
+    wlo_min = min(wlo_min, lo[g]);
+  }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     whi_min = min(whi_min, __shfl_xor(whi_min, off));
     wlo_max = max(wlo_max, __shfl_xor(wlo_max, off));
+    whi_max = max(whi_max, __shfl_xor(whi_max, off));
+    wlo_min = min(wlo_min, __shfl_xor(wlo_min, off));
+  }
+  // the block's first visible key, rounded down to an even key with blocks
+  // of 2 or more keys (a key before it is masked and lies in its block): a
+  // thread's two keys of a tile then share one block
+  const int lo_first = window > 0 ? max(0, L - qlen + 1 - window) : 0;
+  const int lo_min = BIG_B ? lo_first & ~1 : lo_first;
+
+  uint4 qv[QG][NK];
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      qv[g][k] = make_uint4(0, 0, 0, 0);
+      if (valid[g])
+        qv[g][k] = *reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(query) +
+            (static_cast<int64_t>(q0 + qi[g]) * num_heads + hq[g]) * D + k * 32 + grp * 8);
+    }
+  f32x4 o[QG][NE];
+  float m[QG], lsum[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) o[g][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m[g] = -INFINITY;
+    lsum[g] = 0.0f;
   }
 
-  uint4 qv[NK];
-#pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    qv[k] = make_uint4(0, 0, 0, 0);
-    if (valid)
-      qv[k] = *reinterpret_cast<const uint4*>(
-          static_cast<const uint16_t*>(query) +
-          (static_cast<int64_t>(q0 + qi) * num_heads + h) * D + k * 32 + grp * 8);
-  }
-  f32x4 o[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) o[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, lsum = 0.0f;
-
-  // this thread's share of each tile's loads, and where its four keys of
-  // each of its eight dims go in the transposed value tile (8-byte units):
-  // keys 4 my_keys .. + 3 = 32 a + 16 b + 4 g + 0..3 sit in unit 4 a + g,
-  // half b
+  // this thread's share of each tile's loads: keys 2 my_keys, 2 my_keys + 1,
+  // dims 8 my_unit .. + 7
   const int my_unit = tid & 15, my_keys = tid >> 4;
-  int v_store[8];
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd)
-    v_store[dd] = 2 * value_slot(8 * my_unit + dd, 4 * (my_keys >> 3) + (my_keys & 3)) +
-                  ((my_keys >> 2) & 1);
+  // where this lane's transposing value reads start (bytes into a buffer):
+  // lane 4 a + c of lane group grp points at row 4 grp + a, dims 4 c .. + 3;
+  // chunk e adds 32 e bytes, the second half of the 32 keys 16 rows
+  const int v_read = (4 * grp + (col >> 2)) * VROW * 16 + 8 * (col & 3);
 
   const int B = 1 << log2_block;
   const int64_t blk_stride_v = static_cast<int64_t>(num_kv_heads) * B * DV;
@@ -215,15 +240,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       for (int i = tid; i < nb; i += NT) sm_bt[i] = bt_row[b0 + i];
       __syncthreads();
       const int ntiles = (c1 - c0 + KT - 1) / KT;
-      // rows of tile t into registers; rows past the chunk repeat its last row,
-      // so tiles beyond the last are loaded too (unconditional loads keep the
-      // wait counts of the pipeline static) and hit that one row
-      // thread (my_keys, my_unit) moves keys 4 my_keys .. + 3, dims 8 my_unit
-      // .. + 7 of each tile; the addresses first, then one load per key and
-      // cache (loads in branches would leave the pipeline's waits to the
-      // compiler's most cautious count)
+      // rows of tile t into registers; rows past the chunk repeat its last
+      // row, so tiles beyond the last are loaded too (unconditional loads
+      // keep the wait counts of the pipeline static) and hit that one row.
+      // The addresses first, then one load per key and cache (loads in
+      // branches would leave the pipeline's waits to the compiler's most
+      // cautious count).
       auto gload = [&](int t, uint4 (&pk)[PER], uint4 (&pv)[PER]) {
-        const int t0 = c0 + t * KT + 4 * my_keys;  // this thread's first key of the tile
+        const int t0 = c0 + t * KT + 2 * my_keys;  // this thread's first key of the tile
         const uint4 *ks[PER], *vs[PER];
         if constexpr (APPEND && phase) {
           // cache rows (first tile only), the copied tail block's old
@@ -231,20 +255,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 #pragma unroll
           for (int j = 0; j < PER; ++j) {
             const int tok = min(t0 + j, c1 - 1);
-            const uint64_t r = static_cast<uint32_t>(max(tok - p0, 0));
+            const uint64_t rr = static_cast<uint32_t>(max(tok - p0, 0));
             const uint32_t off = (tok & (B - 1)) * DV;
             const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
                                      sm_bt[(tok >> log2_block) - b0])) * blk_units;
             const bool fresh = tok >= p0, copied = tok >= special;
-            const uint4 *kf = key_new + r * key_str, *vf = value_new + r * value_str;
+            const uint4 *kf = key_new + rr * key_str, *vf = value_new + rr * value_str;
             const uint4 *kw = key_cow + off, *vw = value_cow + off;
             const uint4 *kr = kc_my + row + off, *vr = vc_my + row + off;
             ks[j] = __builtin_unpredictable(fresh) ? kf : __builtin_unpredictable(copied) ? kw : kr;
             vs[j] = __builtin_unpredictable(fresh) ? vf : __builtin_unpredictable(copied) ? vw : vr;
           }
         } else if constexpr (BIG_B) {
-          // the four keys (or the chunk's last key they are clamped to) share
-          // one block: blocks hold a multiple of 4 keys and t0 is 4-aligned
+          // the two keys (or the chunk's last key they are clamped to) share
+          // one block: blocks hold an even number of keys and t0 is even
           const int tc = min(t0, c1 - 1);
           const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
                                    sm_bt[(tc >> log2_block) - b0])) * blk_units;
@@ -273,122 +297,125 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       };
       auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) sk[buf][(4 * my_keys + j) * ROW + my_unit] = pk[j];
-        // each dim's four keys as one 8-byte piece
-        uint2* vt = reinterpret_cast<uint2*>(sv[buf]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x0 = dword(pv[0], w), x1 = dword(pv[1], w);
-          const uint32_t x2 = dword(pv[2], w), x3 = dword(pv[3], w);
-          vt[v_store[2 * w]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u),
-                                          __builtin_amdgcn_perm(x3, x2, 0x05040100u));
-          vt[v_store[2 * w + 1]] = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u),
-                                              __builtin_amdgcn_perm(x3, x2, 0x07060302u));
+        for (int j = 0; j < PER; ++j) {
+          sk[buf][(2 * my_keys + j) * KROW + my_unit] = pk[j];
+          sv[buf][(2 * my_keys + j) * VROW + my_unit] = pv[j];
         }
       };
-      // One tile in two halves: scores and softmax, then the value products.
-      // Between them the pipeline stores the next tile and issues the loads of
-      // a later one, so that their instructions interleave with the MFMAs.
-      // Tiles outside a wave's keys run too (their probabilities are 0).
-      constexpr int NS = KT / 16;
-      auto scores = [&](int t, int buf, uint4 (&phi)[NS / 2]) {
+      // whether any column of this wave sees a key of the tile (uniform):
+      // a tile no column sees leaves every column's softmax as it is
+      auto seen = [&](int t) {
         const int t0 = c0 + t * KT;
-        // scores of the whole tile first (independent MFMA chains): lane
-        // (col, grp) gets those of keys 16 st + 4 grp + j of its column
-        f32x4 sc[NS];
+        return t0 < whi_max && t0 + KT > wlo_min;
+      };
+      // One tile in two halves: scores and softmax, then the value products.
+      // Between them the pipeline stores the next tile and issues the loads
+      // of a later one, so that their instructions interleave with the MFMAs.
+      auto scores = [&](int t, int buf, uint4 (&phi)[QG]) {
+        const int t0 = c0 + t * KT;
+        // lane (col, grp) gets the scores of keys 16 st + 4 grp + j of its
+        // column in each group; one K fragment feeds both groups
+        f32x4 sc[QG][NS];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          sc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int g = 0; g < QG; ++g)
 #pragma unroll
-          for (int k = 0; k < NK; ++k)
-            sc[st] = MM::k32(sk[buf][(st * 16 + col) * ROW + k * 4 + grp], qv[k], sc[st]);
-        }
+          for (int st = 0; st < NS; ++st) sc[g][st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int k = 0; k < NK; ++k) {
+            const uint4 a = sk[buf][(st * 16 + col) * KROW + k * 4 + grp];
+#pragma unroll
+            for (int g = 0; g < QG; ++g) sc[g][st] = MM::k32(a, qv[g][k], sc[g][st]);
+          }
         // a tile inside every column's keys needs no mask (wave-uniform)
         if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
 #pragma unroll
-          for (int st = 0; st < NS; ++st)
+          for (int g = 0; g < QG; ++g)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int tt = t0 + st * 16 + 4 * grp + j;
-              const bool vis = (tt < bound) & (tt >= lo) & (tt < c1);
-              sc[st][j] = vis ? sc[st][j] : -INFINITY;
-            }
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int tt = t0 + st * 16 + 4 * grp + j;
+                const bool vis = (tt < bound[g]) & (tt >= lo[g]) & (tt < c1);
+                sc[g][st][j] = vis ? sc[g][st][j] : -INFINITY;
+              }
         }
-        float mt = -INFINITY;
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
-          mt = fmaxf(mt, fmaxf(fmaxf(sc[st][0], sc[st][1]), fmaxf(sc[st][2], sc[st][3])));
-        mt = column_max(mt) * scale_log2;
-        // The reference maximum moves only when the tile's maximum exceeds it
-        // by more than 2^8: probabilities stay below 256 and the
-        // accumulators are rescaled only on such rare jumps.
-        const float mref = mt > m + 8.0f ? mt : m;
-        const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
-        const float corr = __builtin_amdgcn_exp2f(m - ms);
-        if (__any(mref != m)) {
+        for (int g = 0; g < QG; ++g) {
+          float mt = fmaxf(fmaxf(fmaxf(sc[g][0][0], sc[g][0][1]), fmaxf(sc[g][0][2], sc[g][0][3])),
+                           fmaxf(fmaxf(sc[g][1][0], sc[g][1][1]), fmaxf(sc[g][1][2], sc[g][1][3])));
+          mt = column_max(mt) * scale_log2;
+          // The reference maximum moves only when the tile's maximum
+          // exceeds it by more than 2^8: probabilities stay below 256 and
+          // the accumulators are rescaled only on such rare jumps.
+          const float mref = mt > m[g] + 8.0f ? mt : m[g];
+          const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
+          const float corr = __builtin_amdgcn_exp2f(m[g] - ms);
+          if (__any(mref != m[g])) {
 #pragma unroll
-          for (int e = 0; e < NE; ++e) o[e] *= corr;
-        }
-        m = mref;
-        // Probabilities rounded once to the storage's 16-bit type, two per
-        // conversion, for the value products over pairs of sub-tiles (K = 32
-        // keys per MFMA), and summed as rounded: the output is then exactly a
-        // convex combination of the values with these weights, each within
-        // 2^-9 (bf16) or 2^-12 (fp16) of its own probability.
-        float tsum = 0.0f;
-#pragma unroll
-        for (int sp = 0; sp < NS; sp += 2) {
+            for (int e = 0; e < NE; ++e) o[g][e] *= corr;
+          }
+          m[g] = mref;
+          // Probabilities rounded once to the storage's 16-bit type, two
+          // per conversion, for the value products (K = 32 keys per MFMA),
+          // and summed as rounded: the output is then exactly a convex
+          // combination of the values with these weights, each within
+          // 2^-9 (bf16) or 2^-12 (fp16) of its own probability.
+          float tsum = 0.0f;
           uint32_t w[4];
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+          for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int j = 0; j < 4; j += 2) {
-              w[2 * h + j / 2] =
-                  MM::pack2(__builtin_amdgcn_exp2f(fmaf(sc[sp + h][j], scale_log2, -ms)),
-                            __builtin_amdgcn_exp2f(fmaf(sc[sp + h][j + 1], scale_log2, -ms)));
-              tsum = MM::sum2(w[2 * h + j / 2], tsum);
+              w[2 * hh + j / 2] =
+                  MM::pack2(__builtin_amdgcn_exp2f(fmaf(sc[g][hh][j], scale_log2, -ms)),
+                            __builtin_amdgcn_exp2f(fmaf(sc[g][hh][j + 1], scale_log2, -ms)));
+              tsum = MM::sum2(w[2 * hh + j / 2], tsum);
             }
-          phi[sp / 2] = make_uint4(w[0], w[1], w[2], w[3]);
+          phi[g] = make_uint4(w[0], w[1], w[2], w[3]);
+          lsum[g] = lsum[g] * corr + tsum;
         }
-        lsum = lsum * corr + tsum;
       };
-      auto values = [&](int buf, const uint4 (&phi)[NS / 2]) {
+      auto values = [&](int buf, const uint4 (&phi)[QG]) {
+        const char* vb = reinterpret_cast<const char*>(sv[buf]) + v_read;
 #pragma unroll
-        for (int sp = 0; sp < NS; sp += 2) {
+        for (int e = 0; e < NE; ++e) {
+          // dim 16 e + col of keys 4 grp + 0..3 and 16 + 4 grp + 0..3: the
+          // order of the probabilities in phi
+          const uint2 x0 = read_columns(vb + 32 * e);
+          const uint2 x1 = read_columns(vb + 32 * e + 16 * VROW * 16);
+          const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            // dim 16 e + col of the eight keys, in the order of phi
-            const uint4 a = sv[buf][value_slot(16 * e + col, 2 * sp + grp)];
-            o[e] = MM::k32(a, phi[sp / 2], o[e]);
-          }
+          for (int g = 0; g < QG; ++g) o[g][e] = MM::k32(a, phi[g], o[g][e]);
         }
       };
       // LDS holds tile t and t + 1 alternately; registers A and B carry the
       // loads of the next two tiles, so two tiles' rows are in flight while
-      // one is computed
+      // one is computed (pairs of tiles with no exit between them: the
+      // waits for the loads in flight stay counted, not full drains)
       uint4 ak[PER], av[PER], bk[PER], bv[PER];
       gload(0, ak, av);
       lstore(0, ak, av);
       gload(1, ak, av);
       gload(2, bk, bv);
       __syncthreads();
-      // (pairs of tiles with no exit between them: the waits for the loads
-      // in flight stay counted, not full drains)
-      uint4 phi[NS / 2];
+      uint4 phi[QG];
       int t = 0;
       for (; t + 1 < ntiles; t += 2) {
-        scores(t, 0, phi);
+        const bool s0 = seen(t), s1 = seen(t + 1);
+        if (s0) scores(t, 0, phi);
         lstore(1, ak, av);
         gload(t + 3, ak, av);
-        values(0, phi);
+        if (s0) values(0, phi);
         __syncthreads();
-        scores(t + 1, 1, phi);
+        if (s1) scores(t + 1, 1, phi);
         lstore(0, bk, bv);
         gload(t + 4, bk, bv);
-        values(1, phi);
+        if (s1) values(1, phi);
         __syncthreads();
       }
-      if (t < ntiles) {  // an odd last tile, in buffer 0
+      if (t < ntiles && seen(t)) {  // an odd last tile, in buffer 0
         scores(t, 0, phi);
         values(0, phi);
       }
@@ -413,30 +440,29 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     }
   }
 
-  // per-column sum over the four lane groups (disjoint key slots)
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (!valid) return;
-  // lane (col, grp) holds dims 16 e + 4 grp + j of its column: four
-  // contiguous dims per e, stored as one 8-byte piece
-  uint16_t* dst = static_cast<uint16_t*>(out) +
-                  (static_cast<int64_t>(q0 + qi) * num_heads + h) * D + 4 * grp;
-  const float inv = 1.0f / lsum;
 #pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    uint32_t w[4];
+  for (int g = 0; g < QG; ++g) {
+    // per-column sum over the four lane groups (disjoint key slots)
+    float l = lsum[g];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!valid[g]) continue;
+    // lane (col, grp) holds dims 16 e + 4 grp + j of its column: four
+    // contiguous dims per e, stored as one 8-byte piece
+    uint16_t* dst = static_cast<uint16_t*>(out) +
+                    (static_cast<int64_t>(q0 + qi[g]) * num_heads + hq[g]) * D + 4 * grp;
+    const float inv = 1.0f / l;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float back;
-      w[j] = MM::round16(o[e][j] * inv, back);
-    }
-    *reinterpret_cast<uint2*>(dst + 16 * e) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+    for (int e = 0; e < NE; ++e)
+      *reinterpret_cast<uint2*>(dst + 16 * e) =
+          make_uint2(MM::pack2(o[g][e][0] * inv, o[g][e][1] * inv),
+                     MM::pack2(o[g][e][2] * inv, o[g][e][3] * inv));
   }
 }
 
 }  // namespace
 
-int prefill_block_tokens(int group) { return kPrefillWaves * 16 / group; }
+int prefill_block_tokens(int group) { return kPrefillWaves * kPrefillGroups * 16 / group; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   int log2_block = 0;
@@ -445,7 +471,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_rows) * a.num_kv_heads));
   const float sl2 = a.scale * kLog2e;
-  const bool big = log2_block >= 2, append = a.append.qsl != nullptr;
+  const bool big = log2_block >= 1, append = a.append.qsl != nullptr;
 #define PA_PREFILL(DT, BIG, APP)                                                              \
   hipLaunchKernelGGL((prefill_kernel<DT, BIG, APP>), grid, dim3(kPrefillWaves * 64), 0, stream, \
                      a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,   \

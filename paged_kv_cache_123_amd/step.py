@@ -82,7 +82,7 @@ class DecodeStep:
     sequence's new tokens) instead of one query per sequence; a sequence with
     more new tokens than one workgroup holds as query vectors (a prefill
     chunk) is attended as several query blocks (pa_query_blocks): with 16-bit
-    storage, head_size 128 and no partitions the blocks hold 64 query vectors
+    storage, head_size 128 and no partitions the blocks hold 128 query vectors
     and run on the prefill kernel (pa_paged_attention_prefill, or
     pa_prefill_step with the cache writes in the same launch) unless
     ``prefill_kernel`` is False; otherwise on the decode kernels after the

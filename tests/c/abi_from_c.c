@@ -56,8 +56,9 @@ int main(void) {
   const int32_t qsl[3] = {0, 70, 80};
   int32_t tokens = 0, rseq[8], rlen[8], rqsl[9];
   int64_t rows = 0;
-  CHECK(pa_prefill_block_tokens(32, 8, &tokens) == PA_OK && tokens == 16);
-  CHECK(pa_query_blocks(qlens, qsl, 2, tokens, rseq, rlen, rqsl, 8, &rows) == PA_OK && rows == 6);
+  CHECK(pa_prefill_block_tokens(32, 8, &tokens) == PA_OK && tokens == 32);
+  /* (blocks of 16 tokens here) */
+  CHECK(pa_query_blocks(qlens, qsl, 2, 16, rseq, rlen, rqsl, 8, &rows) == PA_OK && rows == 6);
   CHECK(rlen[0] == 46 && rlen[4] == 100 && rseq[4] == 0 && rseq[5] == 1 && rlen[5] == 30);
   CHECK(rqsl[4] == 64 && rqsl[5] == 70 && rqsl[6] == 80);
   printf("abi_from_c ok %s\n", pa_version());

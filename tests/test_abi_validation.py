@@ -199,7 +199,7 @@ def test_set_decode_kernel_rejects_unknown_modes():
     assert L.pa_set_decode_kernel(prev) == 0
 
 
-@pytest.mark.parametrize("H,Hkv,tokens", [(32, 32, 64), (4, 2, 32), (64, 16, 16), (64, 8, 8)])
+@pytest.mark.parametrize("H,Hkv,tokens", [(32, 32, 128), (4, 2, 64), (64, 16, 32), (64, 8, 16)])
 def test_prefill_block_tokens(H, Hkv, tokens):
     from paged_kv_cache_123_amd import ops
     assert ops.prefill_block_tokens(H, Hkv) == tokens

@@ -28,8 +28,8 @@ def draw_case(seed: int) -> dict:
     c["window"] = 0 if rng.random() < 0.6 else int(rng.integers(1, 700))
     n = int(rng.integers(2, 6))
     c["lens"] = [int(x) for x in rng.integers(20, 2300, size=n)]
-    # chunks longer than one prefill block (64 / G tokens) in most sequences
-    c["new"] = [min(L, int(x)) for L, x in zip(c["lens"], rng.integers(1, 201, size=n))]
+    # chunks longer than one prefill block (128 / G tokens) in most sequences
+    c["new"] = [min(L, int(x)) for L, x in zip(c["lens"], rng.integers(1, 401, size=n))]
     return c
 
 
