@@ -9,9 +9,10 @@
 // vectors (token, head).  One workgroup of four waves serves one (block, KV
 // head); wave w owns query vectors 32w .. 32w+31, two groups of 16, the
 // columns of its matrix-core tiles.  The workgroup walks the keys the block
-// sees in tiles of 32 tokens, double-buffered in LDS, with the loads of the
-// next two tiles in registers while one is computed, so each K/V row is read
-// from memory once per 128 query vectors and from LDS once per 32.  Each
+// sees in tiles of 64 tokens, double-buffered in LDS, with the loads of the
+// next two tiles in registers while one is computed (one with the step's
+// writes), so each K/V row is read from memory once per 128 query vectors
+// and from LDS once per 32.  Each
 // operand fragment a wave reads from LDS feeds the MFMAs of both of its
 // groups.  Every wave sees every tile, keeps the online softmax of its own
 // columns and writes its outputs itself: no merge across waves.
@@ -44,7 +45,7 @@ using namespace dev;
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillGroups = 2;  // 16-column query groups per wave
-constexpr int kPrefillTile = 32;   // key tokens per LDS tile
+constexpr int kPrefillTile = 64;   // key tokens per LDS tile
 
 // Maximum over the four lane groups of a column (lanes 16 and 32 apart):
 // each permlane swap trades rows of 16 lanes between its two results, so
@@ -71,7 +72,7 @@ __device__ __forceinline__ uint2 read_columns(const void* lds_addr) {
   return __builtin_bit_cast(uint2, x);
 }
 
-// BIG_B: blocks of at least 2 tokens, so that the two keys a thread moves
+// BIG_B: blocks of at least 4 tokens, so that the four keys a thread moves
 // per tile share one block.  APPEND: the step's cache writes ride in the
 // launch (pa_prefill_step).
 template <int DT, bool BIG_B, bool APPEND>
@@ -93,8 +94,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   constexpr int NS = KT / 16;      // score sub-tiles per tile
   constexpr int KROW = DV + 1;     // padded LDS rows, in 16-byte units
   constexpr int VROW = DV + 2;
-  constexpr int PER = 2;           // keys of each cache a thread moves per tile
-  static_assert(KT * DV == NT * PER && NS == 2, "tile shape");
+  constexpr int PER = KT * DV / NT;  // keys of each cache a thread moves per tile
+  constexpr int NP = NS / 2;       // value MFMAs (K = 32 keys) per tile and dim chunk
+  static_assert(KT * DV == NT * PER && NS % 2 == 0, "tile shape");
   using MM = Mma<DT>;
 
   __shared__ uint4 sk[2][KT * KROW];
@@ -143,11 +145,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     whi_max = max(whi_max, __shfl_xor(whi_max, off));
     wlo_min = min(wlo_min, __shfl_xor(wlo_min, off));
   }
-  // the block's first visible key, rounded down to an even key with blocks
-  // of 2 or more keys (a key before it is masked and lies in its block): a
-  // thread's two keys of a tile then share one block
+  // the block's first visible key, rounded down to a multiple of 4 with
+  // blocks of 4 or more keys (a key before it is masked and lies in its
+  // block): a thread's four keys of a tile then share one block
   const int lo_first = window > 0 ? max(0, L - qlen + 1 - window) : 0;
-  const int lo_min = BIG_B ? lo_first & ~1 : lo_first;
+  const int lo_min = BIG_B ? lo_first & ~(PER - 1) : lo_first;
 
   uint4 qv[QG][NK];
 #pragma unroll
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       // branches would leave the pipeline's waits to the compiler's most
       // cautious count).
       auto gload = [&](int t, uint4 (&pk)[PER], uint4 (&pv)[PER]) {
-        const int t0 = c0 + t * KT + 2 * my_keys;  // this thread's first key of the tile
+        const int t0 = c0 + t * KT + PER * my_keys;  // this thread's first key of the tile
         const uint4 *ks[PER], *vs[PER];
         if constexpr (APPEND && phase) {
           // cache rows (first tile only), the copied tail block's old
@@ -267,8 +269,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             vs[j] = __builtin_unpredictable(fresh) ? vf : __builtin_unpredictable(copied) ? vw : vr;
           }
         } else if constexpr (BIG_B) {
-          // the two keys (or the chunk's last key they are clamped to) share
-          // one block: blocks hold an even number of keys and t0 is even
+          // the four keys (or the chunk's last key they are clamped to) share
+          // one block: blocks hold a multiple of 4 keys and t0 is a multiple
+          // of 4
           const int tc = min(t0, c1 - 1);
           const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
                                    sm_bt[(tc >> log2_block) - b0])) * blk_units;
@@ -298,8 +301,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-          sk[buf][(2 * my_keys + j) * KROW + my_unit] = pk[j];
-          sv[buf][(2 * my_keys + j) * VROW + my_unit] = pv[j];
+          sk[buf][(PER * my_keys + j) * KROW + my_unit] = pk[j];
+          sv[buf][(PER * my_keys + j) * VROW + my_unit] = pv[j];
         }
       };
       // whether any column of this wave sees a key of the tile (uniform):
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       // One tile in two halves: scores and softmax, then the value products.
       // Between them the pipeline stores the next tile and issues the loads
       // of a later one, so that their instructions interleave with the MFMAs.
-      auto scores = [&](int t, int buf, uint4 (&phi)[QG]) {
+      auto scores = [&](int t, int buf, uint4 (&phi)[QG][NP]) {
         const int t0 = c0 + t * KT;
         // lane (col, grp) gets the scores of keys 16 st + 4 grp + j of its
         // column in each group; one K fragment feeds both groups
@@ -343,8 +346,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         }
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
-          float mt = fmaxf(fmaxf(fmaxf(sc[g][0][0], sc[g][0][1]), fmaxf(sc[g][0][2], sc[g][0][3])),
-                           fmaxf(fmaxf(sc[g][1][0], sc[g][1][1]), fmaxf(sc[g][1][2], sc[g][1][3])));
+          float mt = -INFINITY;
+#pragma unroll
+          for (int st = 0; st < NS; ++st)
+            mt = fmaxf(mt, fmaxf(fmaxf(sc[g][st][0], sc[g][st][1]), fmaxf(sc[g][st][2], sc[g][st][3])));
           mt = column_max(mt) * scale_log2;
           // The reference maximum moves only when the tile's maximum
           // exceeds it by more than 2^8: probabilities stay below 256 and
@@ -363,55 +368,67 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
           // combination of the values with these weights, each within
           // 2^-9 (bf16) or 2^-12 (fp16) of its own probability.
           float tsum = 0.0f;
-          uint32_t w[4];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
+          for (int sp = 0; sp < NP; ++sp) {
+            uint32_t w[4];
 #pragma unroll
-            for (int j = 0; j < 4; j += 2) {
-              w[2 * hh + j / 2] =
-                  MM::pack2(__builtin_amdgcn_exp2f(fmaf(sc[g][hh][j], scale_log2, -ms)),
-                            __builtin_amdgcn_exp2f(fmaf(sc[g][hh][j + 1], scale_log2, -ms)));
-              tsum = MM::sum2(w[2 * hh + j / 2], tsum);
-            }
-          phi[g] = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int j = 0; j < 4; j += 2) {
+                w[2 * hh + j / 2] = MM::pack2(
+                    __builtin_amdgcn_exp2f(fmaf(sc[g][2 * sp + hh][j], scale_log2, -ms)),
+                    __builtin_amdgcn_exp2f(fmaf(sc[g][2 * sp + hh][j + 1], scale_log2, -ms)));
+                tsum = MM::sum2(w[2 * hh + j / 2], tsum);
+              }
+            phi[g][sp] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
           lsum[g] = lsum[g] * corr + tsum;
         }
       };
-      auto values = [&](int buf, const uint4 (&phi)[QG]) {
+      auto values = [&](int buf, const uint4 (&phi)[QG][NP]) {
         const char* vb = reinterpret_cast<const char*>(sv[buf]) + v_read;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          // dim 16 e + col of keys 4 grp + 0..3 and 16 + 4 grp + 0..3: the
-          // order of the probabilities in phi
-          const uint2 x0 = read_columns(vb + 32 * e);
-          const uint2 x1 = read_columns(vb + 32 * e + 16 * VROW * 16);
-          const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        for (int sp = 0; sp < NP; ++sp)
 #pragma unroll
-          for (int g = 0; g < QG; ++g) o[g][e] = MM::k32(a, phi[g], o[g][e]);
-        }
+          for (int e = 0; e < NE; ++e) {
+            // dim 16 e + col of keys 32 sp + 4 grp + 0..3 and the same + 16:
+            // the order of the probabilities in phi
+            const uint2 x0 = read_columns(vb + 32 * e + 32 * sp * VROW * 16);
+            const uint2 x1 = read_columns(vb + 32 * e + (32 * sp + 16) * VROW * 16);
+            const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
+#pragma unroll
+            for (int g = 0; g < QG; ++g) o[g][e] = MM::k32(a, phi[g][sp], o[g][e]);
+          }
       };
       // LDS holds tile t and t + 1 alternately; registers A and B carry the
       // loads of the next two tiles, so two tiles' rows are in flight while
       // one is computed (pairs of tiles with no exit between them: the
-      // waits for the loads in flight stay counted, not full drains)
-      uint4 ak[PER], av[PER], bk[PER], bv[PER];
+      // waits for the loads in flight stay counted, not full drains).  With
+      // the step's writes (more registers live) one tile is in flight, in A.
+      constexpr bool two = !APPEND;
+      uint4 ak[PER], av[PER], bk[two ? PER : 1], bv[two ? PER : 1];
       gload(0, ak, av);
       lstore(0, ak, av);
       gload(1, ak, av);
-      gload(2, bk, bv);
+      if constexpr (two) gload(2, bk, bv);
       __syncthreads();
-      uint4 phi[QG];
+      uint4 phi[QG][NP];
       int t = 0;
       for (; t + 1 < ntiles; t += 2) {
         const bool s0 = seen(t), s1 = seen(t + 1);
         if (s0) scores(t, 0, phi);
         lstore(1, ak, av);
-        gload(t + 3, ak, av);
+        gload(t + (two ? 3 : 2), ak, av);
         if (s0) values(0, phi);
         __syncthreads();
         if (s1) scores(t + 1, 1, phi);
-        lstore(0, bk, bv);
-        gload(t + 4, bk, bv);
+        if constexpr (two) {
+          lstore(0, bk, bv);
+          gload(t + 4, bk, bv);
+        } else {
+          lstore(0, ak, av);
+          gload(t + 3, ak, av);
+        }
         if (s1) values(1, phi);
         __syncthreads();
       }
@@ -471,7 +488,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_rows) * a.num_kv_heads));
   const float sl2 = a.scale * kLog2e;
-  const bool big = log2_block >= 1, append = a.append.qsl != nullptr;
+  // (keys a thread moves per tile: tile x 16 units / threads)
+  const bool big = (1 << log2_block) >= kPrefillTile * 16 / (kPrefillWaves * 64);
+  const bool append = a.append.qsl != nullptr;
 #define PA_PREFILL(DT, BIG, APP)                                                              \
   hipLaunchKernelGGL((prefill_kernel<DT, BIG, APP>), grid, dim3(kPrefillWaves * 64), 0, stream, \
                      a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,   \
