@@ -750,7 +750,7 @@ def measure(args, w, cascade_arg=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": pmc_traffic(w.name, attn_bytes),
+            "traffic": pmc_traffic(w.name + ("_unfused" if args.unfused else ""), attn_bytes),
             "algorithmic_bytes_per_launch": attn_bytes,
             "algorithmic_flops_per_launch": flops,
         },
