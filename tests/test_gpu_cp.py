@@ -141,6 +141,70 @@ def test_cp_rank_without_tokens():
         assert torch.all(st.l == 0) and torch.all(st.m == -float("inf"))
 
 
+def test_cp_decode_step_full_size_every_sequence():
+    """The 8-rank long-context batch at full size: every one of the 32
+    sequences on two heads, each rank's partials and the merged output
+    against the oracle, and the bytes of those heads' slices of every block
+    of every sequence in each rank's cache (the rank's scatter included)."""
+    _require_gpu()
+    from oracle.attention import paged_attention_partials
+    from test_gpu_parity import _two_heads
+    w = W.long_context_cp8_bf16()
+    world = w.extra["cp_world"]
+    print(f"[cp] {w.name} full size, every sequence, NB={w.num_blocks} per rank", flush=True)
+    vals = W.make_cp_values(w, DEV)
+    steps = _steps(w, vals)
+    ora = OracleStep(w)
+    H = w.num_heads
+    G = w.num_heads // w.num_kv_heads
+    assert G == 1  # heads map one to one onto the copied KV heads
+    q = to_host(vals["query"])
+    nk, nv = to_host(vals["new_key"]), to_host(vals["new_value"])
+    seqs = []
+    for s in range(w.num_seqs):
+        live = np.flatnonzero(ora.tables[s] >= 0)
+        seqs.append((live, ora.tables[s][live].astype(np.int64), _two_heads(s, H)))
+    parts = {s: [] for s in range(w.num_seqs)}
+    for r, st in enumerate(steps):
+        pre = []
+        for live, blocks, heads in seqs:
+            idx = torch.from_numpy(blocks).to(DEV)
+            hs = torch.tensor(heads, device=DEV)
+            pre.append((to_host(vals["key_caches"][r].index_select(0, idx).index_select(1, hs)),
+                        to_host(vals["value_caches"][r].index_select(0, idx).index_select(1, hs))))
+        st.run(merge=False)
+        torch.cuda.synchronize()
+        slots = ora.cp_slot_mapping(r)
+        assert to_host(st.slot_mapping).tolist() == slots
+        lens = ora.cp_local_lens(r)
+        for s, ((live, blocks, heads), (kc, vc)) in enumerate(zip(seqs, pre)):
+            if slots[s] >= 0:  # this rank holds the new token's position
+                blk, off = divmod(slots[s], w.block_size)
+                j = int(np.flatnonzero(blocks == blk)[0])
+                kc[j, :, off, :] = nk[s][heads]
+                vc[j, :, off, :] = nv[s][heads]
+            idx = torch.from_numpy(blocks).to(DEV)
+            hs = torch.tensor(heads, device=DEV)
+            assert np.array_equal(
+                to_host(st.key_cache.index_select(0, idx).index_select(1, hs)), kc)
+            assert np.array_equal(
+                to_host(st.value_cache.index_select(0, idx).index_select(1, hs)), vc)
+            table = np.full((1, ora.tables.shape[1]), -1, dtype=np.int64)
+            table[0, live] = np.arange(live.size)
+            want = paged_attention_partials(np.ascontiguousarray(q[s:s + 1][:, heads]), kc, vc,
+                                            table, lens[s:s + 1], w.scale, w.dtype)
+            hh = torch.tensor(heads, device=DEV)
+            got = (st.m[s:s + 1].index_select(1, hh), st.l[s:s + 1].index_select(1, hh),
+                   st.o[s:s + 1].index_select(1, hh))
+            check_partials(got, want, w.dtype, f"rank {r} seq {s}")
+            parts[s].append(want)
+    out = to_host(steps[0].merge())
+    torch.cuda.synchronize()
+    for s, (live, blocks, heads) in enumerate(seqs):
+        want = ora.cp_merge(*(np.stack([p[i] for p in parts[s]]) for i in range(3)))
+        check_attention(out[s:s + 1][:, heads], want, w.dtype, f"cp8 merged seq {s}")
+
+
 def test_cp_decode_step_full_size_sampled():
     """32 x 32768 tokens over 8 ranks (4096 per rank, B=64, partitions of
     512): every rank's decode step at full size, the oracle on two sampled

@@ -271,6 +271,66 @@ def test_long_context_full_size_sampled(decode_kernel):
     assert np.isfinite(decode(got, w.dtype)).all()
 
 
+def _two_heads(s: int, H: int):
+    """Two distinct query heads of sequence s, spread over the heads."""
+    a, b = s % H, (7 * s + 13) % H
+    return [a, b] if a != b else [a, (a + 1) % H]
+
+
+def test_long_context_full_size_every_sequence():
+    """32 x 32768 tokens, B=64, partitions of 512, at full size: every one of
+    the 32 sequences on two heads each against the oracle, and the bytes of
+    those heads' slices of every block of every sequence (the step's scatter
+    included) on the device."""
+    _require_gpu()
+    from oracle.attention import paged_attention
+    w = W.long_context_bf16()
+    print(f"[parity] {w.name} full size, every sequence, NB={w.num_blocks}", flush=True)
+    vals = W.make_values(w, DEV)
+    ora = OracleStep(w)
+    H, B = w.num_heads, w.block_size
+    G = w.num_heads // w.num_kv_heads
+    pre = []
+    for s in range(w.num_seqs):
+        n = int(-(-int(ora.context_lens[s]) // B))
+        blocks = ora.tables[s][:n].astype(np.int64)
+        assert (blocks >= 0).all()
+        kv_heads = sorted({h // G for h in _two_heads(s, H)})
+        idx = torch.from_numpy(blocks).to(DEV)
+        hs = torch.tensor(kv_heads, device=DEV)
+        pre.append((blocks, kv_heads,
+                    to_host(vals["key_cache"].index_select(0, idx).index_select(1, hs)),
+                    to_host(vals["value_cache"].index_select(0, idx).index_select(1, hs))))
+    host_q = to_host(vals["query"])
+    new_k, new_v = to_host(vals["new_key"]), to_host(vals["new_value"])
+    step = _step(w, vals)
+    assert np.array_equal(step.tables_host.astype(np.int64), ora.tables)
+    out = step.run()
+    torch.cuda.synchronize()
+    slots = ora.slot_mapping()
+    assert to_host(step.slot_mapping).tolist() == slots
+    got_all = to_host(out)
+    for s, (blocks, kv_heads, kc, vc) in enumerate(pre):
+        blk, off = divmod(slots[s], B)  # one new token per sequence, row s
+        j = int(np.flatnonzero(blocks == blk)[0])
+        kc[j, :, off, :] = new_k[s][kv_heads]
+        vc[j, :, off, :] = new_v[s][kv_heads]
+        idx = torch.from_numpy(blocks).to(DEV)
+        hs = torch.tensor(kv_heads, device=DEV)
+        assert np.array_equal(to_host(step.key_cache.index_select(0, idx).index_select(1, hs)), kc)
+        assert np.array_equal(to_host(step.value_cache.index_select(0, idx).index_select(1, hs)),
+                              vc)
+        heads = _two_heads(s, H)
+        # the sequence alone, its table remapped onto the copied blocks and
+        # each head onto its copied KV head (one query head per KV head here)
+        assert G == 1
+        order = [kv_heads.index(h) for h in heads]
+        q = np.ascontiguousarray(host_q[s:s + 1][:, heads])
+        want = paged_attention(q, kc[:, order], vc[:, order], np.arange(len(blocks))[None, :],
+                               ora.context_lens[s:s + 1], w.scale, w.dtype)
+        check_attention(got_all[s][heads][None], want, w.dtype, f"long_context seq {s}")
+
+
 # ---- edge cases: ragged tails, block sizes, head sizes, groups, dtypes ------
 
 EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 100, 257]

@@ -136,6 +136,61 @@ def test_window_full_size_sampled(decode_kernel):
     check_attention(got[sel], want[sel], w.dtype, "windowed sampled")
 
 
+def test_window_full_size_every_sequence():
+    """The Mistral-style batch at full size: every one of the 64 sequences on
+    two query heads against the oracle (each head alone, on the slice of its
+    KV head of the blocks its table still holds), and those slices' bytes on
+    the device, the step's scatter included."""
+    _require_gpu()
+    from oracle.attention import paged_attention
+    from test_gpu_parity import _two_heads
+    w = W.mistral7b_swa_bf16()
+    print(f"[window] {w.name} full size, every sequence, NB={w.num_blocks}", flush=True)
+    vals = W.make_values(w, DEV)
+    ora = OracleStep(w)
+    H, B = w.num_heads, w.block_size
+    G = w.num_heads // w.num_kv_heads
+    W_ = w.extra["sliding_window"]
+    pre = []
+    for s in range(w.num_seqs):
+        row = ora.tables[s]
+        live = np.flatnonzero(row >= 0)
+        blocks = row[live].astype(np.int64)
+        kv_heads = sorted({h // G for h in _two_heads(s, H)})
+        idx = torch.from_numpy(blocks).to(DEV)
+        hs = torch.tensor(kv_heads, device=DEV)
+        pre.append((live, blocks, kv_heads,
+                    to_host(vals["key_cache"].index_select(0, idx).index_select(1, hs)),
+                    to_host(vals["value_cache"].index_select(0, idx).index_select(1, hs))))
+    host_q = to_host(vals["query"])
+    new_k, new_v = to_host(vals["new_key"]), to_host(vals["new_value"])
+    step = _step(w, vals)
+    assert np.array_equal(step.tables_host.astype(np.int64), ora.tables)
+    out = step.run(fused=True)
+    torch.cuda.synchronize()
+    slots = ora.slot_mapping()
+    assert to_host(step.slot_mapping).tolist() == slots
+    got_all = to_host(out)
+    for s, (live, blocks, kv_heads, kc, vc) in enumerate(pre):
+        blk, off = divmod(slots[s], B)  # one new token per sequence, row s
+        j = int(np.flatnonzero(blocks == blk)[0])
+        kc[j, :, off, :] = new_k[s][kv_heads]
+        vc[j, :, off, :] = new_v[s][kv_heads]
+        idx = torch.from_numpy(blocks).to(DEV)
+        hs = torch.tensor(kv_heads, device=DEV)
+        assert np.array_equal(to_host(step.key_cache.index_select(0, idx).index_select(1, hs)), kc)
+        assert np.array_equal(to_host(step.value_cache.index_select(0, idx).index_select(1, hs)),
+                              vc)
+        # the sequence's table onto the copied blocks (released entries stay -1)
+        table = np.full((1, ora.tables.shape[1]), -1, dtype=np.int64)
+        table[0, live] = np.arange(live.size)
+        for h in _two_heads(s, H):
+            g = kv_heads.index(h // G)
+            want = paged_attention(host_q[s:s + 1, h:h + 1], kc[:, g:g + 1], vc[:, g:g + 1], table,
+                                   ora.context_lens[s:s + 1], w.scale, w.dtype, window=W_)
+            check_attention(got_all[s:s + 1, h:h + 1], want, w.dtype, f"window seq {s} head {h}")
+
+
 # ---- kernel blocks smaller than the allocator's blocks -----------------------
 
 KB_CASES = [
