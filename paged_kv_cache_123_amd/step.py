@@ -296,8 +296,14 @@ class DecodeStep:
     def fused(self):
         """The whole step as one launch (pa_decode_step, or pa_prefill_step for
         query blocks on the prefill kernel).  The arguments are
-        checked and marshalled on the first call; later calls launch them on
-        the current stream."""
+        checked and marshalled on the first call (or by prepare_fused); later
+        calls launch them on the current stream."""
+        self.prepare_fused()
+        ops.launch_prepared(self._fused_call)
+
+    def prepare_fused(self):
+        """The one-launch step's checks and argument marshalling, without a
+        launch (host only; done once)."""
         if not self.fused_ok:
             raise ValueError("a copy-on-write of a block of several kernel blocks, or query "
                              "blocks on the decode kernels (they read each other's new rows "
@@ -324,7 +330,6 @@ class DecodeStep:
                     self.plan, self.query_start_loc, self.new_key, self.new_value,
                     self.cow_src, self.slot_mapping, self.workspace, self.shared_blocks,
                     self.max_query_len, self.sliding_window)
-        ops.launch_prepared(self._fused_call)
 
     def run(self, fused: bool = False):
         """The whole step; returns ``out`` [num_seqs, num_heads, head_size].
