@@ -10,12 +10,12 @@
 // head); wave w owns query vectors 32w .. 32w+31, two groups of 16, the
 // columns of its matrix-core tiles.  The workgroup walks the keys the block
 // sees in tiles of 64 tokens, double-buffered in LDS, with the loads of the
-// next two tiles in registers while one is computed (one with the step's
-// writes), so each K/V row is read from memory once per 128 query vectors
-// and from LDS once per 32.  Each
-// operand fragment a wave reads from LDS feeds the MFMAs of both of its
-// groups.  Every wave sees every tile, keeps the online softmax of its own
-// columns and writes its outputs itself: no merge across waves.
+// next tile in registers while one is computed, so each K/V row is read from
+// memory once per 128 query vectors and from LDS once per 32.  Each operand
+// fragment a wave reads from LDS feeds the MFMAs of both of its groups, and
+// the fragments of the next MFMAs are read while the current ones run.
+// Every wave sees every tile, keeps the online softmax of its own columns and
+// writes its outputs itself: no merge across waves.
 //
 // K and V rows sit in LDS as stored, K rows padded to 17 16-byte units so
 // that the 16 rows one score MFMA reads fall into different banks, V rows to
@@ -269,17 +269,21 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             vs[j] = __builtin_unpredictable(fresh) ? vf : __builtin_unpredictable(copied) ? vw : vr;
           }
         } else if constexpr (BIG_B) {
-          // the four keys (or the chunk's last key they are clamped to) share
-          // one block: blocks hold a multiple of 4 keys and t0 is a multiple
-          // of 4
-          const int tc = min(t0, c1 - 1);
+          // the four keys share one block: blocks hold a multiple of 4 keys
+          // and t0 is a multiple of 4.  Past the chunk's end the K rows are
+          // the block's next slots (scores of keys past the end are masked)
+          // and the V rows repeat the chunk's last key (a slot past the
+          // sequence may hold anything, and its probability 0 must not meet
+          // a NaN); a thread whose keys all lie past the end moves the
+          // chunk's last four
+          const int tc = min(t0, (c1 - 1) & ~(PER - 1));
           const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
                                    sm_bt[(tc >> log2_block) - b0])) * blk_units;
+          const uint4* kb = kc_my + row + (tc & (B - 1)) * DV;
 #pragma unroll
           for (int j = 0; j < PER; ++j) {
-            const uint32_t off = (min(t0 + j, c1 - 1) & (B - 1)) * DV;
-            ks[j] = kc_my + row + off;
-            vs[j] = vc_my + row + off;
+            ks[j] = kb + j * DV;
+            vs[j] = vc_my + row + (min(tc + j, c1 - 1) & (B - 1)) * DV;
           }
         } else {
 #pragma unroll
@@ -323,26 +327,54 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         for (int g = 0; g < QG; ++g)
 #pragma unroll
           for (int st = 0; st < NS; ++st) sc[g][st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // the K fragments of sub-tile st + 1 are read while the MFMAs of
+        // sub-tile st run (the scheduler barrier keeps the reads ahead)
+        uint4 ka[2][NK];
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
+        for (int k = 0; k < NK; ++k) ka[0][k] = sk[buf][col * KROW + k * 4 + grp];
+        // a wave issuing MFMAs wins the issue arbitration over one doing its
+        // softmax on the same SIMD, so that the two overlap
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int k = 0; k < NK; ++k) {
-            const uint4 a = sk[buf][(st * 16 + col) * KROW + k * 4 + grp];
+        for (int st = 0; st < NS; ++st) {
+          if (st + 1 < NS) {
 #pragma unroll
-            for (int g = 0; g < QG; ++g) sc[g][st] = MM::k32(a, qv[g][k], sc[g][st]);
+            for (int k = 0; k < NK; ++k)
+              ka[(st + 1) & 1][k] = sk[buf][((st + 1) * 16 + col) * KROW + k * 4 + grp];
           }
-        // a tile inside every column's keys needs no mask (wave-uniform)
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int k = 0; k < NK; ++k)
+#pragma unroll
+            for (int g = 0; g < QG; ++g) sc[g][st] = MM::k32(ka[st & 1][k], qv[g][k], sc[g][st]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // a tile inside every column's keys needs no mask (wave-uniform);
+        // otherwise key st * 16 + j past this lane's first (t0 + 4 grp) is
+        // visible below hi and, with a window, from lw on (a column without
+        // a query has hi <= 0 and lw beyond every key)
         if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
+          const int rel = t0 + 4 * grp;
 #pragma unroll
-          for (int g = 0; g < QG; ++g)
+          for (int g = 0; g < QG; ++g) {
+            const int hi = min(bound[g], c1) - rel;
+            const int lw = lo[g] - rel;
+            if (window > 0) {
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
+              for (int st = 0; st < NS; ++st)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int tt = t0 + st * 16 + 4 * grp + j;
-                const bool vis = (tt < bound[g]) & (tt >= lo[g]) & (tt < c1);
-                sc[g][st][j] = vis ? sc[g][st][j] : -INFINITY;
-              }
+                for (int j = 0; j < 4; ++j) {
+                  const bool vis = (st * 16 + j < hi) & (st * 16 + j >= lw);
+                  sc[g][st][j] = vis ? sc[g][st][j] : -INFINITY;
+                }
+            } else {
+#pragma unroll
+              for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  sc[g][st][j] = st * 16 + j < hi ? sc[g][st][j] : -INFINITY;
+            }
+          }
         }
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
@@ -387,30 +419,39 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       };
       auto values = [&](int buf, const uint4 (&phi)[QG][NP]) {
         const char* vb = reinterpret_cast<const char*>(sv[buf]) + v_read;
+        // dim 16 e + col of keys 32 sp + 4 grp + 0..3 and the same + 16 (the
+        // order of the probabilities in phi), read VD steps ahead of the
+        // MFMAs that take them
+        constexpr int VD = 3;
+        constexpr int NV = NP * NE;
+        uint4 va[VD + 1];
+        auto vread = [&](int i) {
+          const int sp = i / NE, e = i % NE;
+          const uint2 x0 = read_columns(vb + 32 * e + 32 * sp * VROW * 16);
+          const uint2 x1 = read_columns(vb + 32 * e + (32 * sp + 16) * VROW * 16);
+          return make_uint4(x0.x, x0.y, x1.x, x1.y);
+        };
 #pragma unroll
-        for (int sp = 0; sp < NP; ++sp)
+        for (int i = 0; i < VD; ++i) va[i] = vread(i);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            // dim 16 e + col of keys 32 sp + 4 grp + 0..3 and the same + 16:
-            // the order of the probabilities in phi
-            const uint2 x0 = read_columns(vb + 32 * e + 32 * sp * VROW * 16);
-            const uint2 x1 = read_columns(vb + 32 * e + (32 * sp + 16) * VROW * 16);
-            const uint4 a = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        for (int i = 0; i < NV; ++i) {
+          if (i + VD < NV) va[(i + VD) % (VD + 1)] = vread(i + VD);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int g = 0; g < QG; ++g) o[g][e] = MM::k32(a, phi[g][sp], o[g][e]);
-          }
+          for (int g = 0; g < QG; ++g)
+            o[g][i % NE] = MM::k32(va[i % (VD + 1)], phi[g][i / NE], o[g][i % NE]);
+        }
+        __builtin_amdgcn_s_setprio(0);
       };
-      // LDS holds tile t and t + 1 alternately; registers A and B carry the
-      // loads of the next two tiles, so two tiles' rows are in flight while
-      // one is computed (pairs of tiles with no exit between them: the
-      // waits for the loads in flight stay counted, not full drains).  With
-      // the step's writes (more registers live) one tile is in flight, in A.
-      constexpr bool two = !APPEND;
-      uint4 ak[PER], av[PER], bk[two ? PER : 1], bv[two ? PER : 1];
+      // LDS holds tile t and t + 1 alternately; registers carry the loads
+      // of the tile after, so one tile's rows are in flight while one is
+      // computed (pairs of tiles with no exit between them: the waits for
+      // the loads in flight stay counted, not full drains)
+      uint4 ak[PER], av[PER];
       gload(0, ak, av);
       lstore(0, ak, av);
       gload(1, ak, av);
-      if constexpr (two) gload(2, bk, bv);
       __syncthreads();
       uint4 phi[QG][NP];
       int t = 0;
@@ -418,17 +459,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         const bool s0 = seen(t), s1 = seen(t + 1);
         if (s0) scores(t, 0, phi);
         lstore(1, ak, av);
-        gload(t + (two ? 3 : 2), ak, av);
+        gload(t + 2, ak, av);
         if (s0) values(0, phi);
         __syncthreads();
         if (s1) scores(t + 1, 1, phi);
-        if constexpr (two) {
-          lstore(0, bk, bv);
-          gload(t + 4, bk, bv);
-        } else {
-          lstore(0, ak, av);
-          gload(t + 3, ak, av);
-        }
+        lstore(0, ak, av);
+        gload(t + 3, ak, av);
         if (s1) values(1, phi);
         __syncthreads();
       }
