@@ -363,8 +363,11 @@ int32_t pa_decode_plan_window(const int32_t* context_lens, const int32_t* query_
  * reads the prefix once and then each member's own tokens, and every
  * sequence outside a chunk has the item (s, 0).  Output `plan` (host int32,
  * capacity entries), plan_len entries in all:
- *   [2 * num_items]  items, largest first as in pa_decode_plan (by the
- *                    tokens they read)
+ *   [2 * num_items]  items, largest first: with partitions as in
+ *                    pa_decode_plan (by the tokens they read, in buckets of
+ *                    256); single pass by the tokens they read counted in
+ *                    16-token tiles per piece (no buckets), ties in batch
+ *                    order of their first sequence
  *   [1]              number of chunks C
  *   [C + 1]          offsets of the chunks' member lists
  *   [offsets[C]]     members (batch rows)

@@ -19,6 +19,7 @@
 
 namespace {
 constexpr int32_t kGranule = 256;
+constexpr int32_t kTileTokens = 16;  // keys per tile of the cascade kernel
 }
 
 extern "C" int32_t pa_decode_plan_window(const int32_t* context_lens,
@@ -171,8 +172,8 @@ struct PlanItem {
 // section: C, the C + 1 member offsets, optionally the C prefix lengths, the
 // members.
 int32_t write_plan(const char* who, std::vector<PlanItem>& v, const CascadeGroups& g,
-                   bool with_prefix, int32_t* plan, int64_t capacity, int64_t* num_items,
-                   int64_t* plan_len, int32_t* max_members) {
+                   bool with_prefix, int32_t granule, int32_t* plan, int64_t capacity,
+                   int64_t* num_items, int64_t* plan_len, int32_t* max_members) {
   const int32_t num_chunks = static_cast<int32_t>(g.prefix.size());
   int32_t widest = 0;
   for (int32_t c = 0; c < num_chunks; ++c) widest = std::max(widest, g.off[c + 1] - g.off[c]);
@@ -183,9 +184,9 @@ int32_t write_plan(const char* who, std::vector<PlanItem>& v, const CascadeGroup
   if (!plan) return PA_OK;  // size query
   if (capacity < *plan_len)
     return pa::fail(PA_EINVAL, (std::string(who) + ": capacity smaller than the plan").c_str());
-  std::stable_sort(v.begin(), v.end(), [](const PlanItem& a, const PlanItem& b) {
-    const int32_t ba = (a.tokens + kGranule - 1) / kGranule;
-    const int32_t bb = (b.tokens + kGranule - 1) / kGranule;
+  std::stable_sort(v.begin(), v.end(), [granule](const PlanItem& a, const PlanItem& b) {
+    const int32_t ba = (a.tokens + granule - 1) / granule;
+    const int32_t bb = (b.tokens + granule - 1) / granule;
     return ba != bb ? ba > bb : a.key < b.key;
   });
   int64_t w = 0;
@@ -253,10 +254,13 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
   const int32_t num_chunks = static_cast<int32_t>(g.prefix.size());
   for (int32_t c = 0; c < num_chunks; ++c) {
     if (single) {  // the prefix once, then each member's own tokens
+      // (counted in the kernel's 16-token tiles: a member's last tile costs
+      // a whole one)
       const int32_t prefix = g.prefix[c];
-      int64_t tokens = prefix;
+      int64_t tokens = (prefix + kTileTokens - 1) / kTileTokens * kTileTokens;
       for (int32_t k = g.off[c]; k < g.off[c + 1]; ++k)
-        tokens += context_lens[g.members[k]] - prefix;
+        tokens += (context_lens[g.members[k]] - prefix + kTileTokens - 1) / kTileTokens *
+                  kTileTokens;
       v.push_back({static_cast<int32_t>(std::min<int64_t>(tokens, INT32_MAX)),
                    g.members[g.off[c]], -1 - c, prefix});
       continue;
@@ -279,7 +283,10 @@ extern "C" int32_t pa_decode_plan_cascade(const int32_t* context_lens,
     for (int32_t p = own_from[s]; static_cast<int64_t>(p) * partition_size < L; ++p)
       v.push_back({std::min((p + 1) * partition_size, L) - p * partition_size, s, s, p});
   }
-  return write_plan(who, v, g, false, plan, capacity, num_items, plan_len, max_members);
+  // single pass: one round of workgroups, whose end is that of the longest
+  // items, so those go first, ordered exactly (in the kernel's tiles)
+  return write_plan(who, v, g, false, single ? kTileTokens : kGranule, plan, capacity, num_items,
+                    plan_len, max_members);
 }
 
 // Chunk size of a step's cascade plan: a single-pass plan runs one
@@ -354,7 +361,7 @@ extern "C" int32_t pa_decode_plan_cascade_chunked(
     for (int32_t p = 0; static_cast<int64_t>(p) * chunk_tokens < L; ++p)
       v.push_back({std::min((p + 1) * chunk_tokens, L) - p * chunk_tokens, s, s, p});
   }
-  return write_plan(who, v, g, true, plan, capacity, num_items, plan_len, max_members);
+  return write_plan(who, v, g, true, kGranule, plan, capacity, num_items, plan_len, max_members);
 }
 
 // Query blocks: sequence s's n_s new tokens (rows [qsl[s], qsl[s+1]) of the
