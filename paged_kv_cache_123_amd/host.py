@@ -50,11 +50,14 @@ class Pool:
                                    None if order is None else _p32(order),
                                    ctypes.byref(handle)))
         self._h = handle
+        # kept here: at interpreter exit the module's globals may already be
+        # gone when the last pools are collected
+        self._destroy = lib().pa_pool_destroy
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib().pa_pool_destroy(h)
+            self._destroy(h)
             self._h = None
 
     def add_seq(self, seq: int) -> None:

@@ -221,3 +221,22 @@ def test_map_to_kernel_blocks_matches_oracle():
         map_to_kernel_blocks([2 ** 30], 4)  # kernel ids past int32
     with pytest.raises(PagedKVError):
         map_to_kernel_blocks([1], 0)
+
+
+def test_pool_destroyed_after_its_modules_are_torn_down():
+    """A pool collected at interpreter exit, after the loader module's
+    globals have been cleared, still releases its handle without an error
+    (simulated in a child process by clearing those globals first)."""
+    import os
+    import subprocess
+    import sys
+    repo = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import paged_kv_cache_123_amd._lib as L\n"
+            "import paged_kv_cache_123_amd.host as H\n"
+            "p = H.Pool(8, 4)\np.add_seq(0)\np.append(0, 5)\n"
+            "for name in ('_LIB', 'os', 'LIB_PATH'):\n    setattr(L, name, None)\n"
+            "H.lib = None\n"
+            "p.__del__()\nassert p._h is None\nprint('released')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=repo, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0 and "released" in r.stdout, r.stderr
