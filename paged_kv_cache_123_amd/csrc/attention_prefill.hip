@@ -17,11 +17,12 @@
 // Every wave sees every tile, keeps the online softmax of its own columns and
 // writes its outputs itself: no merge across waves.
 //
-// K and V rows sit in LDS as stored, K rows padded to 17 16-byte units so
-// that the 16 rows one score MFMA reads fall into different banks, V rows to
-// 18 units so that the 8 rows of half a wave's transposing read do; the value
-// MFMA's operand (8 keys of one dim per lane) comes from the transposing LDS
-// read of 16-bit elements.
+// K and V rows sit in LDS as stored, padded to 18 16-byte units: the 16-byte
+// K fragments a wave reads for a score MFMA (16 rows, 4 units) and the
+// transposing V reads (8 rows of half a wave) then fall into distinct banks,
+// and a read moves 1 KB in 4 cycles (at 17 units the K reads took 8); the
+// value MFMA's operand (8 keys of one dim per lane) comes from the
+// transposing LDS read of 16-bit elements.
 //
 // With the step's cache writes in the same launch (pa_prefill_step), keys
 // from a sequence's first new position on are read from the step's key/value
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   constexpr int NE = 8;            // value MFMA chunks (16 dims each)
   constexpr int KT = kPrefillTile;
   constexpr int NS = KT / 16;      // score sub-tiles per tile
-  constexpr int KROW = DV + 1;     // padded LDS rows, in 16-byte units
+  constexpr int KROW = DV + 2;     // padded LDS rows, in 16-byte units
   constexpr int VROW = DV + 2;
   constexpr int PER = KT * DV / NT;  // keys of each cache a thread moves per tile
   constexpr int NP = NS / 2;       // value MFMAs (K = 32 keys) per tile and dim chunk
