@@ -236,6 +236,45 @@ def read_reference(nbytes: int = 2 << 30, reps: int = 10):
     return out
 
 
+def cascade_timeline(step, fused: bool) -> dict:
+    """One more step of a cascade plan with the kernel's per-workgroup
+    timeline: when the workgroups start, how long each spends before its
+    first tiles are described (set-up) and streaming them, and when they end,
+    in microseconds from the first start; stream times by the wave slot the
+    workgroup's first wave took on its SIMD (0: the first workgroup placed on
+    it) and by XCD."""
+    import torch
+
+    from paged_kv_cache_123_amd import ops
+    ops.timeline_reset()
+    if fused:
+        step.fused()
+    else:
+        step.attention()
+    torch.cuda.synchronize()
+    rec = ops.timeline_read().astype(np.int64)
+    if len(rec) == 0:
+        return {"workgroups": 0, "note": "no cascade launch in this step"}
+    us = 0.01  # 100 MHz counter ticks
+    t0 = rec[:, 0].min()
+    start, setup = (rec[:, 0] - t0) * us, (rec[:, 1] - rec[:, 0]) * us
+    stream, end = (rec[:, 2] - rec[:, 1]) * us, (rec[:, 2] - t0) * us
+    hw = rec[:, 3] & 0xFFFFFFFF
+    slot, xcc = hw & 0xF, (rec[:, 3] >> 32) & 0xF
+
+    def dist(x):
+        return {q: round(float(np.percentile(x, p)), 2)
+                for q, p in (("min", 0), ("p10", 10), ("median", 50), ("p90", 90), ("max", 100))}
+    return {
+        "workgroups": int(len(rec)), "start_us": dist(start), "setup_us": dist(setup),
+        "stream_us": dist(stream), "end_us": dist(end),
+        "stream_us_by_wave_slot": {int(k): round(float(stream[slot == k].mean()), 2)
+                                   for k in np.unique(slot)},
+        "stream_us_by_xcd": {int(k): round(float(stream[xcc == k].mean()), 2)
+                             for k in np.unique(xcc)},
+    }
+
+
 def calibrate_counters() -> dict:
     """Kernels of known byte count for scaling FETCH_SIZE / WRITE_SIZE: the read
     probe over 1 GiB (reads only) and copy_blocks of 2048 blocks of 128 KiB in
@@ -866,6 +905,10 @@ def main():
     ap.add_argument("--no-read-reference", action="store_true")
     ap.add_argument("--calibrate-counters", action="store_true",
                     help="only run kernels of known byte count (for rocprofv3 --pmc scaling)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="after the timing, one more step with the cascade kernel's "
+                         "per-workgroup timeline (needs a library built with PA_TIMELINE=1, "
+                         "named by PAGEDKV_LIBRARY)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-KV path here runs on a single GPU "
@@ -909,6 +952,8 @@ def main():
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": res["dtype"], "data": "synthetic"}
     result.update({k: v for k, v in res.items() if k not in result and k != "unit"})
+    if args.timeline:
+        result["timeline"] = cascade_timeline(step, not args.unfused and step.fused_ok)
     if any(op[0] == "request" for op in w.prefill):
         result["host_prefix_cache"] = time_prefix_cache(w)
     if step.num_tokens > w.num_seqs or len(step.cow_pairs_host):

@@ -971,6 +971,27 @@ int32_t pa_merge_attention_partials(void* out, const float* max_logits, const fl
 int32_t pa_probe_read_blocks(const void* buffer, const int32_t* block_order, int64_t num_blocks,
                              void* sink, int32_t grid, int32_t non_temporal, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Diagnostic (not part of the decode path): a per-workgroup timeline of the
+ * single-pass cascade kernel, recorded only by a library built with
+ * PA_TIMELINE=1 (python -m paged_kv_cache_123_amd.build -D PA_TIMELINE=1
+ * --out PATH); the default build returns PA_EINVAL from both calls.
+ * Workgroup i < 8192 of the last cascade launch writes record i: four
+ * uint64 words, the GPU real-time counter (100 MHz, one clock for every CU)
+ * at its entry, when its first round of tiles has been described, and at
+ * its exit, then (XCC id << 32) | HW_ID register (CU, SIMD and wave slot of
+ * its first wave).  Concurrent cascade launches overwrite each other's
+ * records.
+ *   pa_timeline_reset: clears the records (asynchronous on stream).
+ *   pa_timeline_read: copies min(capacity, 8192) records to host memory
+ *     (records: host uint64 [4 * capacity]; synchronous) and sets
+ *     *num_records to the number of leading records written since the reset.
+ * Errors: PA_EINVAL for a default build, null pointers or capacity < 1;
+ * PA_ELAUNCH when the clear or the copy fails.
+ * ---------------------------------------------------------------------- */
+int32_t pa_timeline_reset(void* stream);
+int32_t pa_timeline_read(uint64_t* records, int64_t capacity, int64_t* num_records);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,8 @@ SIGNATURES = {
                                                  _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                                  _i64, _vp, _vp, _sz, _i32, _vp]),
     "pa_probe_read_blocks": (_i32, [_vp, _vp, _i64, _vp, _i32, _i32, _vp]),
+    "pa_timeline_reset": (_i32, [_vp]),
+    "pa_timeline_read": (_i32, [_vp, _i64, _pi64]),
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32,
                               _i32, _f32, _i32, _i32, _vp, _i64, _vp, _vp, _sz, _vp, _vp, _vp,
                               _i64, _i64, _vp, _vp, _i32, _i32, _vp]),

@@ -35,12 +35,27 @@
 #include "decode_common.h"
 #include "launch.h"
 #include "pagedkv.h"
+#include "status.h"
 
 #ifndef PA_MFMA_OCCUPANCY
 #define PA_MFMA_OCCUPANCY
 #endif
 
+// Per-workgroup timeline of the single-pass cascade kernel, compiled in only
+// with PA_TIMELINE=1 (a diagnostic build): workgroup i < kTimelineMax
+// records the real-time counter (100 MHz) at entry, when its first round of
+// tiles is described, and at exit, and the hardware ids of the CU it ran on.
+#ifndef PA_TIMELINE
+#define PA_TIMELINE 0
+#endif
+
 namespace pa {
+
+constexpr int64_t kTimelineMax = 8192;
+#if PA_TIMELINE
+__device__ uint64_t g_timeline[kTimelineMax * 4];
+#endif
+
 namespace {
 
 using namespace dev;
@@ -340,6 +355,10 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
   constexpr int U = 4;
   static_assert(NQ >= 1 && NQ <= 16, "query vectors must fit the 16 MFMA columns");
 
+#if PA_TIMELINE
+  const uint64_t tl_entry = __builtin_amdgcn_s_memrealtime();
+  uint64_t tl_ready = 0;
+#endif
   const int2 it = items[blockIdx.x / num_kv_heads];
   const int kvh = static_cast<int>(blockIdx.x % num_kv_heads);
   __shared__ int32_t sm_mem[kMaxMembers];  // members (batch rows)
@@ -589,6 +608,9 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
       for (int j = 0; j < 4; ++j) vis[j] = live & (d.y + grp + 4 * j < d.z);
       mfma_tile_update<DT>(kr, vr, qv, vis, scale_log2, m, lsum, o);
     };
+#if PA_TIMELINE
+    if (tl_ready == 0) tl_ready = __builtin_amdgcn_s_memrealtime();
+#endif
     // this wave's tiles of the round through a ring of kCascadePrefetch + 1 slots
     constexpr int NBUF = kCascadePrefetch + 1;
     int first, my;
@@ -688,6 +710,19 @@ __global__ __launch_bounds__(NW * 64) PA_MFMA_OCCUPANCY void cascade_decode_kern
       }
     }
   }
+#if PA_TIMELINE
+  __syncthreads();
+  if (threadIdx.x == 0 && blockIdx.x < kTimelineMax) {
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    uint64_t* rec = g_timeline + 4 * static_cast<int64_t>(blockIdx.x);
+    rec[0] = tl_entry;
+    rec[1] = tl_ready;
+    rec[2] = __builtin_amdgcn_s_memrealtime();
+    rec[3] = (static_cast<uint64_t>(xcc) << 32) | hw;
+  }
+#endif
 }
 
 template <int DT, int NQ>
@@ -741,3 +776,34 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace pa
+
+extern "C" int32_t pa_timeline_reset(void* stream) {
+#if PA_TIMELINE
+  void* dev = nullptr;
+  if (hipGetSymbolAddress(&dev, HIP_SYMBOL(pa::g_timeline)) != hipSuccess ||
+      hipMemsetAsync(dev, 0, sizeof(uint64_t) * 4 * pa::kTimelineMax,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return pa::fail(PA_ELAUNCH, "pa_timeline_reset: could not clear the records");
+  return PA_OK;
+#else
+  (void)stream;
+  return pa::fail(PA_EINVAL, "pa_timeline_reset: library built without PA_TIMELINE");
+#endif
+}
+
+extern "C" int32_t pa_timeline_read(uint64_t* records, int64_t capacity, int64_t* num_records) {
+  if (!records || !num_records || capacity < 1)
+    return pa::fail(PA_EINVAL, "pa_timeline_read: bad argument");
+#if PA_TIMELINE
+  const int64_t n = capacity < pa::kTimelineMax ? capacity : pa::kTimelineMax;
+  if (hipMemcpyFromSymbol(records, HIP_SYMBOL(pa::g_timeline), sizeof(uint64_t) * 4 * n, 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return pa::fail(PA_ELAUNCH, "pa_timeline_read: copy failed");
+  int64_t k = 0;
+  while (k < n && records[4 * k] != 0) ++k;
+  *num_records = k;
+  return PA_OK;
+#else
+  return pa::fail(PA_EINVAL, "pa_timeline_read: library built without PA_TIMELINE");
+#endif
+}

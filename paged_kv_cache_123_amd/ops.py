@@ -539,6 +539,21 @@ def probe_read_blocks(buffer: torch.Tensor, block_order: torch.Tensor, sink: tor
                                      int(non_temporal), _stream()))
 
 
+def timeline_reset() -> None:
+    """Diagnostic: clear the cascade kernel's per-workgroup timeline (a
+    library built with PA_TIMELINE=1 only; raises otherwise)."""
+    check(lib().pa_timeline_reset(_stream()))
+
+
+def timeline_read(capacity: int = 8192) -> np.ndarray:
+    """Diagnostic: the timeline records of the last cascade launch, uint64
+    [n, 4] (entry, tiles described, exit: 100 MHz counter; hardware ids)."""
+    rec = np.zeros((capacity, 4), dtype=np.uint64)
+    n = ctypes.c_int64(0)
+    check(lib().pa_timeline_read(rec.ctypes.data, capacity, ctypes.byref(n)))
+    return rec[:n.value].copy()
+
+
 def decode_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                 value_cache: torch.Tensor, block_tables: torch.Tensor,
                 context_lens: torch.Tensor, scale: float, max_context_len: int,

@@ -212,3 +212,17 @@ def test_prefill_block_tokens_rejects_bad_heads(H, Hkv):
     t = ctypes.c_int32(0)
     assert lib().pa_prefill_block_tokens(H, Hkv, ctypes.byref(t)) == PA_EINVAL
     assert lib().pa_last_error().decode().startswith("pa_prefill_block_tokens")
+
+
+def test_timeline_calls_refuse_in_the_default_build():
+    """The per-workgroup timeline is recorded only by a PA_TIMELINE build;
+    the default library says so instead of returning stale records."""
+    import ctypes
+    from paged_kv_cache_123_amd._lib import PA_EINVAL, lib
+    L = lib()
+    buf = (ctypes.c_uint64 * 8)()
+    n = ctypes.c_int64(-1)
+    assert L.pa_timeline_read(ctypes.cast(buf, ctypes.c_void_p), 2, ctypes.byref(n)) == PA_EINVAL
+    assert b"PA_TIMELINE" in L.pa_last_error()
+    assert L.pa_timeline_reset(None) == PA_EINVAL
+    assert L.pa_timeline_read(None, 2, ctypes.byref(n)) == PA_EINVAL
