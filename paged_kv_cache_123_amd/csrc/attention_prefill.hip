@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   constexpr int VROW = DV + 2;
   constexpr int PER = KT * DV / NT;  // keys of each cache a thread moves per tile
   constexpr int NP = NS / 2;       // value MFMAs (K = 32 keys) per tile and dim chunk
-  static_assert(KT * DV == NT * PER && NS % 2 == 0, "tile shape");
+  static_assert(KT * DV == NT * PER && NS % 2 == 0 && NT % DV == 0, "tile shape");
   using MM = Mma<DT>;
 
   __shared__ uint4 sk[2][KT * KROW];
@@ -479,18 +479,51 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   if constexpr (APPEND) range(std::true_type{}, split, L);
 
   if (APPEND) {
-    // this row's own tokens to their slots (and, for KV head 0, the slots to
-    // the mapping), after the pipeline: its stores would hold up the waits
-    // for the loads in flight
-    for (int i = tid; i < qlen * DV; i += NT) {
-      const int tq = i / DV, u = i % DV;
-      const int tok = L - qlen + tq;
-      const int64_t phys = bt_row[tok >> log2_block];
-      const int64_t dst = phys * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + u;
-      ap.key_cache[dst] = ap.key[(q0 + tq) * ap.key_stride_v + kvh * DV + u];
-      ap.value_cache[dst] = ap.value[(q0 + tq) * ap.value_stride_v + kvh * DV + u];
-      if (ap.slot_mapping && kvh == 0 && u == 0)
-        ap.slot_mapping[q0 + tq] = phys * B + (tok & (B - 1));
+    // this row's own tokens to their slots (and, for KV head 0, their slots
+    // to the mapping), after the pipeline: its stores would hold up the
+    // waits for the loads in flight.  A full row (as many units as a full
+    // query block of one head) loads its table entries, then all its K
+    // units, then all its V units before it stores them: one round trip to
+    // memory per cache.  Shorter rows (a sequence's last, or several heads
+    // per block) take one unit per thread at a time.
+    constexpr int EPI = kPrefillWaves * kPrefillGroups * 16 * DV / NT;
+    if (qlen * DV == EPI * NT) {
+      int64_t dst[EPI];
+#pragma unroll
+      for (int e = 0; e < EPI; ++e)
+        dst[e] = bt_row[(L - qlen + (tid + e * NT) / DV) >> log2_block];
+#pragma unroll
+      for (int e = 0; e < EPI; ++e) {
+        const int tq = (tid + e * NT) / DV, u = tid % DV;  // NT is a multiple of DV
+        const int tok = L - qlen + tq;
+        if (ap.slot_mapping && kvh == 0 && u == 0)
+          ap.slot_mapping[q0 + tq] = dst[e] * B + (tok & (B - 1));
+        dst[e] = dst[e] * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + u;
+      }
+      auto move = [&](const uint4* rows, int64_t stride, uint4* cache) {
+        const uint4* src[EPI];
+#pragma unroll
+        for (int e = 0; e < EPI; ++e)
+          src[e] = rows + (q0 + (tid + e * NT) / DV) * stride + kvh * DV + tid % DV;
+        uint4 r[EPI];
+#pragma unroll
+        for (int e = 0; e < EPI; ++e) r[e] = load_cached(src[e]);
+#pragma unroll
+        for (int e = 0; e < EPI; ++e) cache[dst[e]] = r[e];
+      };
+      move(ap.key, ap.key_stride_v, ap.key_cache);
+      move(ap.value, ap.value_stride_v, ap.value_cache);
+    } else {
+      for (int i = tid; i < qlen * DV; i += NT) {
+        const int tq = i / DV, u = i % DV;
+        const int tok = L - qlen + tq;
+        const int64_t phys = bt_row[tok >> log2_block];
+        const int64_t dst = phys * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + u;
+        ap.key_cache[dst] = ap.key[(q0 + tq) * ap.key_stride_v + kvh * DV + u];
+        ap.value_cache[dst] = ap.value[(q0 + tq) * ap.value_stride_v + kvh * DV + u];
+        if (ap.slot_mapping && kvh == 0 && u == 0)
+          ap.slot_mapping[q0 + tq] = phys * B + (tok & (B - 1));
+      }
     }
   }
 
