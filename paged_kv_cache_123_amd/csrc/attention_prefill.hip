@@ -163,15 +163,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             static_cast<const uint16_t*>(query) +
             (static_cast<int64_t>(q0 + qi[g]) * num_heads + hq[g]) * D + k * 32 + grp * 8);
     }
+  // per column: the reference maximum as subtracted (ms: 0 before the
+  // column's first visible key) and the raw score above which a lane asks
+  // to move it (thr: -inf before the first visible key)
   f32x4 o[QG][NE];
-  float m[QG], lsum[QG];
+  float ms[QG], thr[QG], lsum[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) o[g][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    m[g] = -INFINITY;
+    ms[g] = 0.0f;
+    thr[g] = -INFINITY;
     lsum[g] = 0.0f;
   }
+  const float inv_scale_log2 = 1.0f / scale_log2;
 
   // this thread's share of each tile's loads: keys 2 my_keys, 2 my_keys + 1,
   // dims 8 my_unit .. + 7
@@ -280,11 +285,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
           const int tc = min(t0, (c1 - 1) & ~(PER - 1));
           const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(
                                    sm_bt[(tc >> log2_block) - b0])) * blk_units;
-          const uint4* kb = kc_my + row + (tc & (B - 1)) * DV;
+          const uint32_t slot = (tc & (B - 1)) * DV;
+          const uint4* kb = kc_my + row + slot;
+          const uint4* vb = vc_my + row + slot;
+          // the chunk's last key is at most PER - 1 keys past tc, in its block
+          const uint32_t last = static_cast<uint32_t>(c1 - 1 - tc);
 #pragma unroll
           for (int j = 0; j < PER; ++j) {
             ks[j] = kb + j * DV;
-            vs[j] = vc_my + row + (min(tc + j, c1 - 1) & (B - 1)) * DV;
+            vs[j] = vb + min(static_cast<uint32_t>(j), last) * DV;
           }
         } else {
 #pragma unroll
@@ -377,24 +386,42 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             }
           }
         }
+        // The reference maximum of a column moves only when the tile's
+        // maximum exceeds it by more than 2^8 (probabilities stay below 256
+        // and the accumulators are rescaled only on such rare jumps).  Each
+        // lane first compares its own raw scores with its column's
+        // threshold; only when some lane of the wave asks does the wave
+        // reduce the maxima across lanes and move the references.
+        float lmax[QG];
+        bool jump = false;
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
-          float mt = -INFINITY;
+          lmax[g] = -INFINITY;
 #pragma unroll
           for (int st = 0; st < NS; ++st)
-            mt = fmaxf(mt, fmaxf(fmaxf(sc[g][st][0], sc[g][st][1]), fmaxf(sc[g][st][2], sc[g][st][3])));
-          mt = column_max(mt) * scale_log2;
-          // The reference maximum moves only when the tile's maximum
-          // exceeds it by more than 2^8: probabilities stay below 256 and
-          // the accumulators are rescaled only on such rare jumps.
-          const float mref = mt > m[g] + 8.0f ? mt : m[g];
-          const float ms = mref == -INFINITY ? 0.0f : mref;  // no visible key yet
-          const float corr = __builtin_amdgcn_exp2f(m[g] - ms);
-          if (__any(mref != m[g])) {
+            lmax[g] = fmaxf(lmax[g], fmaxf(fmaxf(sc[g][st][0], sc[g][st][1]),
+                                           fmaxf(sc[g][st][2], sc[g][st][3])));
+          jump |= lmax[g] > thr[g];
+        }
+        if (__any(jump)) {
 #pragma unroll
-            for (int e = 0; e < NE; ++e) o[g][e] *= corr;
+          for (int g = 0; g < QG; ++g) {
+            const float mt = column_max(lmax[g]) * scale_log2;
+            const float mold = thr[g] == -INFINITY ? -INFINITY : ms[g];
+            const float mref = mt > mold + 8.0f ? mt : mold;
+            const float mnew = mref == -INFINITY ? 0.0f : mref;
+            const float corr = __builtin_amdgcn_exp2f(mold - mnew);
+            if (__any(mref != mold)) {
+#pragma unroll
+              for (int e = 0; e < NE; ++e) o[g][e] *= corr;
+            }
+            lsum[g] *= corr;
+            ms[g] = mnew;
+            thr[g] = mref == -INFINITY ? -INFINITY : (mref + 8.0f) * inv_scale_log2;
           }
-          m[g] = mref;
+        }
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
           // Probabilities rounded once to the storage's 16-bit type, two
           // per conversion, for the value products (K = 32 keys per MFMA),
           // and summed as rounded: the output is then exactly a convex
@@ -409,13 +436,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
 #pragma unroll
               for (int j = 0; j < 4; j += 2) {
                 w[2 * hh + j / 2] = MM::pack2(
-                    __builtin_amdgcn_exp2f(fmaf(sc[g][2 * sp + hh][j], scale_log2, -ms)),
-                    __builtin_amdgcn_exp2f(fmaf(sc[g][2 * sp + hh][j + 1], scale_log2, -ms)));
+                    __builtin_amdgcn_exp2f(fmaf(sc[g][2 * sp + hh][j], scale_log2, -ms[g])),
+                    __builtin_amdgcn_exp2f(fmaf(sc[g][2 * sp + hh][j + 1], scale_log2, -ms[g])));
                 tsum = MM::sum2(w[2 * hh + j / 2], tsum);
               }
             phi[g][sp] = make_uint4(w[0], w[1], w[2], w[3]);
           }
-          lsum[g] = lsum[g] * corr + tsum;
+          lsum[g] += tsum;
         }
       };
       auto values = [&](int buf, const uint4 (&phi)[QG][NP]) {
