@@ -163,20 +163,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             static_cast<const uint16_t*>(query) +
             (static_cast<int64_t>(q0 + qi[g]) * num_heads + hq[g]) * D + k * 32 + grp * 8);
     }
-  // per column: the reference maximum as subtracted (ms: 0 before the
-  // column's first visible key) and the raw score above which a lane asks
-  // to move it (thr: -inf before the first visible key)
+  // per column: the reference maximum m (-inf before the column's first
+  // visible key) and the value subtracted, ms (m, or 0 while m is -inf);
+  // all_set: every column of the wave has a reference (wave-uniform)
   f32x4 o[QG][NE];
-  float ms[QG], thr[QG], lsum[QG];
+  float m[QG], ms[QG], lsum[QG];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) o[g][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m[g] = -INFINITY;
     ms[g] = 0.0f;
-    thr[g] = -INFINITY;
     lsum[g] = 0.0f;
   }
-  const float inv_scale_log2 = 1.0f / scale_log2;
+  bool all_set = false;
 
   // this thread's share of each tile's loads: keys 2 my_keys, 2 my_keys + 1,
   // dims 8 my_unit .. + 7
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
         // otherwise key st * 16 + j past this lane's first (t0 + 4 grp) is
         // visible below hi and, with a window, from lw on (a column without
         // a query has hi <= 0 and lw beyond every key)
-        if (!(t0 >= wlo_max && t0 + KT <= min(whi_min, c1))) {
+        const bool masked = !(t0 >= wlo_max && t0 + KT <= min(whi_min, c1));
+        if (masked) {
           const int rel = t0 + 4 * grp;
 #pragma unroll
           for (int g = 0; g < QG; ++g) {
@@ -386,47 +387,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
             }
           }
         }
-        // The reference maximum of a column moves only when the tile's
-        // maximum exceeds it by more than 2^8 (probabilities stay below 256
-        // and the accumulators are rescaled only on such rare jumps).  Each
-        // lane first compares its own raw scores with its column's
-        // threshold; only when some lane of the wave asks does the wave
-        // reduce the maxima across lanes and move the references.
-        float lmax[QG];
-        bool jump = false;
-#pragma unroll
-        for (int g = 0; g < QG; ++g) {
-          lmax[g] = -INFINITY;
-#pragma unroll
-          for (int st = 0; st < NS; ++st)
-            lmax[g] = fmaxf(lmax[g], fmaxf(fmaxf(sc[g][st][0], sc[g][st][1]),
-                                           fmaxf(sc[g][st][2], sc[g][st][3])));
-          jump |= lmax[g] > thr[g];
-        }
-        if (__any(jump)) {
-#pragma unroll
-          for (int g = 0; g < QG; ++g) {
-            const float mt = column_max(lmax[g]) * scale_log2;
-            const float mold = thr[g] == -INFINITY ? -INFINITY : ms[g];
-            const float mref = mt > mold + 8.0f ? mt : mold;
-            const float mnew = mref == -INFINITY ? 0.0f : mref;
-            const float corr = __builtin_amdgcn_exp2f(mold - mnew);
-            if (__any(mref != mold)) {
-#pragma unroll
-              for (int e = 0; e < NE; ++e) o[g][e] *= corr;
-            }
-            lsum[g] *= corr;
-            ms[g] = mnew;
-            thr[g] = mref == -INFINITY ? -INFINITY : (mref + 8.0f) * inv_scale_log2;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < QG; ++g) {
-          // Probabilities rounded once to the storage's 16-bit type, two
-          // per conversion, for the value products (K = 32 keys per MFMA),
-          // and summed as rounded: the output is then exactly a convex
-          // combination of the values with these weights, each within
-          // 2^-9 (bf16) or 2^-12 (fp16) of its own probability.
+        // Probabilities rounded once to the storage's 16-bit type, two per
+        // conversion, for the value products (K = 32 keys per MFMA), and
+        // summed as rounded: the output is then exactly a convex combination
+        // of the values with these weights, each within 2^-9 (bf16) or
+        // 2^-12 (fp16) of its own probability.
+        auto probs = [&](int g) {
           float tsum = 0.0f;
 #pragma unroll
           for (int sp = 0; sp < NP; ++sp) {
@@ -442,8 +408,55 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
               }
             phi[g][sp] = make_uint4(w[0], w[1], w[2], w[3]);
           }
-          lsum[g] += tsum;
+          return tsum;
+        };
+        // The reference maximum of a column moves only when the tile's
+        // maximum exceeds it by more than 2^8: probabilities stay below 256
+        // and the accumulators are rescaled only on such rare jumps.  Once
+        // every column of the wave that has a query has a reference, a tile
+        // first takes its probabilities against the current references: a
+        // lane's sum of at most 256 bounds each of its terms, and only when
+        // some lane's sum exceeds that does the wave reduce the maxima
+        // across lanes, move the references and take the probabilities
+        // again.  Until then every tile reduces the maxima first.
+        float tsum[QG];
+        bool full = !all_set;
+        if (!full) {
+          bool over = false;
+#pragma unroll
+          for (int g = 0; g < QG; ++g) {
+            tsum[g] = probs(g);
+            over |= tsum[g] > 256.0f;
+          }
+          full = __any(over);
         }
+        if (full) {
+          bool set = true;
+#pragma unroll
+          for (int g = 0; g < QG; ++g) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+              mt = fmaxf(mt, fmaxf(fmaxf(sc[g][st][0], sc[g][st][1]),
+                                   fmaxf(sc[g][st][2], sc[g][st][3])));
+            mt = column_max(mt) * scale_log2;
+            const float mref = mt > m[g] + 8.0f ? mt : m[g];
+            const float mnew = mref == -INFINITY ? 0.0f : mref;
+            const float corr = __builtin_amdgcn_exp2f(m[g] - mnew);
+            if (__any(mref != m[g])) {
+#pragma unroll
+              for (int e = 0; e < NE; ++e) o[g][e] *= corr;
+            }
+            lsum[g] *= corr;
+            m[g] = mref;
+            ms[g] = mnew;
+            set &= (mref != -INFINITY) | !valid[g];
+            tsum[g] = probs(g);
+          }
+          all_set = __all(set);
+        }
+#pragma unroll
+        for (int g = 0; g < QG; ++g) lsum[g] += tsum[g];
       };
       auto values = [&](int buf, const uint4 (&phi)[QG][NP]) {
         const char* vb = reinterpret_cast<const char*>(sv[buf]) + v_read;
