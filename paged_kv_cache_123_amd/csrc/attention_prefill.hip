@@ -202,9 +202,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   // The step's cache writes, in the same launch: no workgroup reads a slot
   // written here.  Keys from the sequence's first new position p0 on come
   // from the step's key/value rows, the old slots of a copied tail block
-  // from its source block.  Each row stores the rows of its own tokens
-  // after its attention (and, for KV head 0, their slots); the sequence's
-  // first row copies the old slots here.
+  // from its source block.  Each row stores the rows of its own tokens to
+  // their slots as its tile loop loads them (and, for KV head 0, the slots
+  // to the mapping at its end); the sequence's first row copies the old
+  // slots here.
   int p0 = INT_MAX, seq_q0 = 0, special = INT_MAX;
   int64_t cow = -1;
   // this thread's unit of new row p0 and of slot 0 of the copied tail
@@ -312,11 +313,28 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
           pv[j] = load_cached(vs[j]);
         }
       };
-      auto lstore = [&](int buf, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
+      auto lstore = [&](int buf, int t, const uint4 (&pk)[PER], const uint4 (&pv)[PER]) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
           sk[buf][(PER * my_keys + j) * KROW + my_unit] = pk[j];
           sv[buf][(PER * my_keys + j) * VROW + my_unit] = pv[j];
+        }
+        if constexpr (APPEND && phase) {
+          // the row's own tokens, as loaded from the step's rows, to their
+          // cache slots (the stores precede the next tile's loads, so the
+          // waits for those stay counted)
+          const int t0 = c0 + t * KT + PER * my_keys;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const int tok = t0 + j;
+            if (tok >= L - qlen && tok < c1) {
+              const int64_t slot =
+                  static_cast<int64_t>(sm_bt[(tok >> log2_block) - b0]) * blk_stride_v +
+                  head_off_v + (tok & (B - 1)) * DV + my_unit;
+              ap.key_cache[slot] = pk[j];
+              ap.value_cache[slot] = pv[j];
+            }
+          }
         }
       };
       // whether any column of this wave sees a key of the tile (uniform):
@@ -491,7 +509,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       // the loads in flight stay counted, not full drains)
       uint4 ak[PER], av[PER];
       gload(0, ak, av);
-      lstore(0, ak, av);
+      lstore(0, 0, ak, av);
       gload(1, ak, av);
       __syncthreads();
       uint4 phi[QG][NP];
@@ -499,12 +517,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       for (; t + 1 < ntiles; t += 2) {
         const bool s0 = seen(t), s1 = seen(t + 1);
         if (s0) scores(t, 0, phi);
-        lstore(1, ak, av);
+        lstore(1, t + 1, ak, av);
         gload(t + 2, ak, av);
         if (s0) values(0, phi);
         __syncthreads();
         if (s1) scores(t + 1, 1, phi);
-        lstore(0, ak, av);
+        lstore(0, t + 2, ak, av);
         gload(t + 3, ak, av);
         if (s1) values(1, phi);
         __syncthreads();
@@ -518,52 +536,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   range(std::false_type{}, lo_min, split);
   if constexpr (APPEND) range(std::true_type{}, split, L);
 
-  if (APPEND) {
-    // this row's own tokens to their slots (and, for KV head 0, their slots
-    // to the mapping), after the pipeline: its stores would hold up the
-    // waits for the loads in flight.  A full row (as many units as a full
-    // query block of one head) loads its table entries, then all its K
-    // units, then all its V units before it stores them: one round trip to
-    // memory per cache.  Shorter rows (a sequence's last, or several heads
-    // per block) take one unit per thread at a time.
-    constexpr int EPI = kPrefillWaves * kPrefillGroups * 16 * DV / NT;
-    if (qlen * DV == EPI * NT) {
-      int64_t dst[EPI];
-#pragma unroll
-      for (int e = 0; e < EPI; ++e)
-        dst[e] = bt_row[(L - qlen + (tid + e * NT) / DV) >> log2_block];
-#pragma unroll
-      for (int e = 0; e < EPI; ++e) {
-        const int tq = (tid + e * NT) / DV, u = tid % DV;  // NT is a multiple of DV
-        const int tok = L - qlen + tq;
-        if (ap.slot_mapping && kvh == 0 && u == 0)
-          ap.slot_mapping[q0 + tq] = dst[e] * B + (tok & (B - 1));
-        dst[e] = dst[e] * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + u;
-      }
-      auto move = [&](const uint4* rows, int64_t stride, uint4* cache) {
-        const uint4* src[EPI];
-#pragma unroll
-        for (int e = 0; e < EPI; ++e)
-          src[e] = rows + (q0 + (tid + e * NT) / DV) * stride + kvh * DV + tid % DV;
-        uint4 r[EPI];
-#pragma unroll
-        for (int e = 0; e < EPI; ++e) r[e] = load_cached(src[e]);
-#pragma unroll
-        for (int e = 0; e < EPI; ++e) cache[dst[e]] = r[e];
-      };
-      move(ap.key, ap.key_stride_v, ap.key_cache);
-      move(ap.value, ap.value_stride_v, ap.value_cache);
-    } else {
-      for (int i = tid; i < qlen * DV; i += NT) {
-        const int tq = i / DV, u = i % DV;
-        const int tok = L - qlen + tq;
-        const int64_t phys = bt_row[tok >> log2_block];
-        const int64_t dst = phys * blk_stride_v + head_off_v + (tok & (B - 1)) * DV + u;
-        ap.key_cache[dst] = ap.key[(q0 + tq) * ap.key_stride_v + kvh * DV + u];
-        ap.value_cache[dst] = ap.value[(q0 + tq) * ap.value_stride_v + kvh * DV + u];
-        if (ap.slot_mapping && kvh == 0 && u == 0)
-          ap.slot_mapping[q0 + tq] = phys * B + (tok & (B - 1));
-      }
+  if (APPEND && ap.slot_mapping && kvh == 0) {
+    // the slots of this row's tokens to the mapping
+    for (int i = tid; i < qlen; i += NT) {
+      const int tok = L - qlen + i;
+      ap.slot_mapping[q0 + i] = static_cast<int64_t>(bt_row[tok >> log2_block]) * B + (tok & (B - 1));
     }
   }
 
