@@ -587,6 +587,28 @@ int32_t pa_query_block_hints(const int32_t* row_seq, const int32_t* row_lens, in
                              const int32_t* seq_shared_blocks, int32_t num_seqs,
                              int32_t block_size, int32_t* row_shared_out);
 
+/* pa_prefill_plan (host): the launch order of pa_paged_attention_prefill and
+ * pa_prefill_step over query-block rows, as their work_items list.  A row's
+ * size is the number of keys it reads (its length, or with a sliding window
+ * W the positions from its first query's window on); the rows of a sequence
+ * go together, sequences by their largest row, largest first (ties by
+ * sequence index), and within a sequence largest row first.  The rows of a
+ * sequence read the same K/V rows, so launched together they find them in
+ * the caches, and large pieces of work first leave small ones to fill the
+ * end of the launch.  Each workgroup computes one (row, KV head) whatever
+ * the order: results do not depend on it.
+ *   row_seq, row_lens   host int32 [num_rows], as pa_query_blocks wrote them
+ *   row_qlens           host int32 [num_rows]: new tokens of each row
+ *                       (row_qsl[r + 1] - row_qsl[r]), or NULL = 1
+ *   sliding_window      as for pa_paged_attention_prefill (0 = none)
+ *   items               host int32 [num_rows][2] (output): (row, 0) pairs
+ * PA_EINVAL for null arrays, num_rows < 1, sliding_window < 0, a negative
+ * sequence index or length, or a row whose new tokens are outside
+ * [0, length]. */
+int32_t pa_prefill_plan(const int32_t* row_seq, const int32_t* row_lens,
+                        const int32_t* row_qlens, int32_t num_rows, int32_t sliding_window,
+                        int32_t* items);
+
 /* ------------------------------------------------------------------------
  * Prefill attention over query blocks on the matrix cores (16-bit storage,
  * head_size 128, single pass): the result of pa_paged_attention_multi for

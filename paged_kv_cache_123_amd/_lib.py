@@ -81,6 +81,7 @@ SIGNATURES = {
                                                   _vp, _i64, _i32, _vp, _sz, _vp]),
     "pa_query_blocks": (_i32, [_pi32, _pi32, _i32, _i32, _pi32, _pi32, _pi32, _i64, _pi64]),
     "pa_query_block_hints": (_i32, [_pi32, _pi32, _i32, _pi32, _i32, _i32, _pi32]),
+    "pa_prefill_plan": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _pi32]),
     "pa_prefill_block_tokens": (_i32, [_i32, _i32, _pi32]),
     "pa_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,

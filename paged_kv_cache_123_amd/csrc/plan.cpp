@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -427,6 +428,44 @@ extern "C" int32_t pa_query_block_hints(const int32_t* row_seq, const int32_t* r
                             ? static_cast<int32_t>((static_cast<int64_t>(row_lens[r]) +
                                                     block_size - 1) / block_size)
                             : (seq_shared_blocks ? seq_shared_blocks[s] : 0);
+  }
+  return PA_OK;
+}
+
+// Launch order of the prefill kernel's rows: sequences by their largest
+// row (keys read), largest first, a sequence's rows together, largest first.
+extern "C" int32_t pa_prefill_plan(const int32_t* row_seq, const int32_t* row_lens,
+                                   const int32_t* row_qlens, int32_t num_rows,
+                                   int32_t sliding_window, int32_t* items) {
+  if (!row_seq || !row_lens || !items || num_rows < 1 || sliding_window < 0)
+    return pa::fail(PA_EINVAL, "pa_prefill_plan: bad argument");
+  std::vector<int64_t> size(num_rows);
+  std::map<int32_t, int64_t> seq_size;
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const int64_t L = row_lens[r];
+    const int64_t n = row_qlens ? row_qlens[r] : 1;
+    if (row_seq[r] < 0 || L < 0 || n < 0 || n > L)
+      return pa::fail(PA_EINVAL, "pa_prefill_plan: row sequence, length or tokens out of range");
+    const int64_t lo = sliding_window > 0 ? std::max<int64_t>(0, L - n + 1 - sliding_window) : 0;
+    size[r] = L - lo;
+    int64_t& m = seq_size[row_seq[r]];
+    m = std::max(m, size[r]);
+  }
+  std::vector<int64_t> seq_key(num_rows);
+  std::vector<int32_t> order(num_rows);
+  for (int32_t r = 0; r < num_rows; ++r) {
+    seq_key[r] = seq_size[row_seq[r]];
+    order[r] = r;
+  }
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    if (seq_key[a] != seq_key[b]) return seq_key[a] > seq_key[b];
+    if (row_seq[a] != row_seq[b]) return row_seq[a] < row_seq[b];
+    if (size[a] != size[b]) return size[a] > size[b];
+    return a < b;
+  });
+  for (int32_t i = 0; i < num_rows; ++i) {
+    items[2 * i] = order[i];
+    items[2 * i + 1] = 0;
   }
   return PA_OK;
 }

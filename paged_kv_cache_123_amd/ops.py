@@ -422,6 +422,26 @@ def query_block_hints(row_seq, row_lens, seq_shared_blocks, block_size: int) -> 
     return out
 
 
+def prefill_plan(row_seq, row_lens, row_qlens=None, sliding_window: int = 0) -> np.ndarray:
+    """Launch order of the prefill kernel's rows (pa_prefill_plan): host
+    int32 [num_rows, 2] of (row, 0), for work_items."""
+    rs = np.ascontiguousarray(np.asarray(row_seq, dtype=np.int32))
+    rl = np.ascontiguousarray(np.asarray(row_lens, dtype=np.int32))
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    qp = None
+    if row_qlens is not None:
+        rq = np.ascontiguousarray(np.asarray(row_qlens, dtype=np.int32))
+        if rq.size != rs.size:
+            raise ValueError("row_qlens must have one entry per row")
+        qp = rq.ctypes.data_as(p32)
+    if rl.size != rs.size:
+        raise ValueError("row_lens must have one entry per row")
+    out = np.empty((rs.size, 2), dtype=np.int32)
+    check(lib().pa_prefill_plan(rs.ctypes.data_as(p32), rl.ctypes.data_as(p32), qp, rs.size,
+                                sliding_window, out.ctypes.data_as(p32)))
+    return out
+
+
 def prefill_block_tokens(num_heads: int, num_kv_heads: int) -> int:
     """New tokens per query block of the prefill kernel (pa_prefill_block_tokens)."""
     t = ctypes.c_int32(0)

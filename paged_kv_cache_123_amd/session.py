@@ -185,12 +185,13 @@ class PagedKVCache:
         if matrix and not self.partition_size:
             row_seq, row_lens, row_qsl = ops.query_blocks(
                 lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
+            items = ops.prefill_plan(row_seq, row_lens, np.diff(row_qsl), self.sliding_window)
             ops.prefill_step(out, query, self.key_cache, self.value_cache, tab,
                              torch.from_numpy(row_seq).to(dev), torch.from_numpy(row_lens).to(dev),
                              torch.from_numpy(row_qsl).to(dev), scale, max_len,
                              torch.from_numpy(qsl_host).to(dev), key, value,
-                             torch.from_numpy(cow_src).to(dev), None, None,
-                             self.sliding_window)
+                             torch.from_numpy(cow_src).to(dev), None,
+                             torch.from_numpy(items).to(dev), self.sliding_window)
             return out
         if len(cow_pairs):
             ops.copy_blocks(self.key_cache, self.value_cache, torch.from_numpy(cow_pairs).to(dev))

@@ -233,6 +233,11 @@ class DecodeStep:
                 self.attn_max_query_len = int(np.diff(row_qsl).max())
                 self.attn_shared = torch.from_numpy(row_shared).to(dev)
                 self.row_seq = torch.from_numpy(row_seq).to(dev)
+                if self.prefill_rows:
+                    # launch order: a sequence's rows together, the largest
+                    # sequences first
+                    self.prefill_items = torch.from_numpy(ops.prefill_plan(
+                        row_seq, row_lens, np.diff(row_qsl), self.sliding_window)).to(dev)
         self.plan = torch.from_numpy(self.plan_host).to(dev)
         self._fused_call = None  # the one-launch step's marshalled arguments
         self.workspace = None
@@ -268,7 +273,7 @@ class DecodeStep:
             ops.paged_attention_prefill(self.out, self.query, self.key_cache, self.value_cache,
                                         self.block_tables, self.row_seq, self.attn_lens,
                                         self.attn_qsl, self.scale, self.max_context_len,
-                                        None, self.sliding_window)
+                                        self.prefill_items, self.sliding_window)
         elif self.all_queries:
             ops.paged_attention_multi(self.out, self.query, self.key_cache, self.value_cache,
                                       self.attn_tables, self.attn_lens, self.attn_qsl,
@@ -314,7 +319,7 @@ class DecodeStep:
                     self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
                     self.row_seq, self.attn_lens, self.attn_qsl, self.scale,
                     self.max_context_len, self.query_start_loc, self.new_key, self.new_value,
-                    self.cow_src, self.slot_mapping, None, self.sliding_window)
+                    self.cow_src, self.slot_mapping, self.prefill_items, self.sliding_window)
             elif self.cascade:
                 self._fused_call = ops.prepare_decode_step_cascade(
                     self.out, self.query, self.key_cache, self.value_cache, self.block_tables,

@@ -375,3 +375,51 @@ def test_query_blocks_reject_bad_arguments():
         ops.query_blocks([5], [0, 0], 4)  # no new token
     with pytest.raises(PagedKVError):
         ops.query_blocks([5], [0, 3], 0)
+
+
+# ---- prefill launch order ---------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("window", [0, 300])
+def test_prefill_plan_groups_sequences_largest_first(seed, window):
+    """Every row once as (row, 0); a sequence's rows contiguous; sequences by
+    their largest row (keys read) non-increasing, ties by sequence index;
+    rows of a sequence by size non-increasing."""
+    from paged_kv_cache_123_amd import ops
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 12))
+    new = rng.integers(1, 600, size=S)
+    lens = new + rng.integers(0, 2000, size=S)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl, int(rng.choice([16, 64, 128])))
+    qlen = np.diff(row_qsl)
+    items = ops.prefill_plan(row_seq, row_lens, qlen, window)
+    assert items.shape == (len(row_seq), 2) and (items[:, 1] == 0).all()
+    rows = items[:, 0].tolist()
+    assert sorted(rows) == list(range(len(row_seq)))
+
+    def size(r):  # keys row r reads, written out from the window rule
+        L, n = int(row_lens[r]), int(qlen[r])
+        return L - (max(0, L - n + 1 - window) if window else 0)
+
+    seqs = [int(row_seq[r]) for r in rows]
+    firsts = [s for i, s in enumerate(seqs) if i == 0 or seqs[i - 1] != s]
+    assert len(firsts) == len(set(seqs)), "a sequence's rows are split"
+    top = {s: max(size(r) for r in range(len(row_seq)) if row_seq[r] == s) for s in firsts}
+    keys = [(-top[s], s) for s in firsts]
+    assert keys == sorted(keys)
+    for s in firsts:
+        sizes = [size(r) for r in rows if row_seq[r] == s]
+        assert sizes == sorted(sizes, reverse=True)
+
+
+def test_prefill_plan_rejects_bad_arguments():
+    from paged_kv_cache_123_amd import PagedKVError, ops
+    with pytest.raises(PagedKVError):
+        ops.prefill_plan([0], [5], [6])      # more new tokens than the length
+    with pytest.raises(PagedKVError):
+        ops.prefill_plan([-1], [5], [1])     # negative sequence
+    with pytest.raises(PagedKVError):
+        ops.prefill_plan([0], [5], [1], -1)  # negative window
+    with pytest.raises(ValueError):
+        ops.prefill_plan([0, 0], [5], [1, 1])
