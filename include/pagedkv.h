@@ -616,7 +616,7 @@ int32_t pa_prefill_plan(const int32_t* row_seq, const int32_t* row_lens,
  * into LDS for all query vectors of a block instead of once per 16 of them.
  *
  * pa_prefill_block_tokens (host): *tokens receives the max_block to give
- * pa_query_blocks, 64 / (num_heads / num_kv_heads) new tokens per block.
+ * pa_query_blocks, 128 / (num_heads / num_kv_heads) new tokens per block.
  * PA_EINVAL for a null tokens or a head ratio other than 1, 2, 4 or 8.
  *
  * pa_paged_attention_prefill: one workgroup per (row, KV head).
