@@ -40,6 +40,9 @@ CASES = [
     # a window whose start falls inside a table chunk; whole prompts as one chunk
     ("bf16", 128, 16, 4, [5000, 700], [300, 700], 0, 2500),
     ("f16", 128, 32, 2, [640, 64], [640, 64], 0, 0),
+    # more new tokens than one table chunk: a row's own tokens straddle the
+    # second chunk's start in the one-launch step's range of new rows
+    ("bf16", 128, 16, 1, [2600, 300], [2500, 300], 0, 0),
 ]
 
 
