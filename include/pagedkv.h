@@ -629,9 +629,10 @@ int32_t pa_prefill_plan(const int32_t* row_seq, const int32_t* row_lens,
  *                       pa_prefill_block_tokens of them (tokens past that
  *                       leave their outputs undefined)
  *   work_items          device int32 [num_rows][2], may be NULL: launch order,
- *                       (row, 0) for every row once, e.g. pa_decode_plan_window
- *                       over row_lens (largest first); NULL = the last row
- *                       first, so that a sequence's rows run together
+ *                       (row, 0) for every row once, e.g. pa_prefill_plan
+ *                       (a sequence's rows together, the largest sequences
+ *                       first); NULL = the last row first, so that a
+ *                       sequence's rows run together
  *   max_context_len     host bound on row_lens, checked against bt_stride
  *   sliding_window      as for pa_paged_attention_multi
  * Every key a row sees, its own new tokens included, must already be in the
