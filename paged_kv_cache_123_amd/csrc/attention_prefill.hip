@@ -28,7 +28,7 @@
 // from a sequence's first new position on are read from the step's key/value
 // rows and the old slots of a copied tail block from its source block, so no
 // workgroup reads a slot the launch writes; each row stores its own tokens'
-// rows after its attention.
+// rows to their slots as its tile loop loads them.
 #include <hip/hip_runtime.h>
 
 #include <climits>
