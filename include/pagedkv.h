@@ -609,6 +609,25 @@ int32_t pa_prefill_plan(const int32_t* row_seq, const int32_t* row_lens,
                         const int32_t* row_qlens, int32_t num_rows, int32_t sliding_window,
                         int32_t* items);
 
+/* pa_prefill_plan_split (host): the work list of pa_paged_attention_prefill_split,
+ * (row, p) pairs: for each row the partitions of partition_size keys from
+ * the one holding its first visible key (0, or with a sliding window W the
+ * start of its first query's window) to the one holding its last key
+ * (ceil(row_lens[r] / partition_size) - 1).  The rows of a sequence go
+ * together, sequences by their largest row (keys read), largest first, and
+ * within a sequence by partition, then by row size.
+ *   row_seq, row_lens, row_qlens, sliding_window   as for pa_prefill_plan
+ *   items        host int32 [capacity][2] (output), or NULL to count only
+ *   num_items    host (output): the number of items
+ * PA_EINVAL for null row arrays or num_items, num_rows < 1,
+ * sliding_window < 0, partition_size < 1, a negative sequence index, a
+ * length below 1, new tokens outside [0, length], or a capacity below the
+ * count. */
+int32_t pa_prefill_plan_split(const int32_t* row_seq, const int32_t* row_lens,
+                              const int32_t* row_qlens, int32_t num_rows, int32_t sliding_window,
+                              int32_t partition_size, int32_t* items, int64_t capacity,
+                              int64_t* num_items);
+
 /* ------------------------------------------------------------------------
  * Prefill attention over query blocks on the matrix cores (16-bit storage,
  * head_size 128, single pass): the result of pa_paged_attention_multi for
@@ -652,6 +671,41 @@ int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key
                                    int32_t max_context_len, float scale, int32_t dtype,
                                    const int32_t* work_items, int32_t sliding_window,
                                    void* stream);
+
+/* pa_paged_attention_prefill_split: pa_paged_attention_prefill with the keys
+ * of each row cut into partitions of partition_size, for batches with too
+ * few (row, KV head) workgroups to fill the GPU (a long context under few
+ * rows).  One workgroup per (work item, KV head) attends partition p of row
+ * r and writes each of the row's query vectors' partial (m, l, o) to the
+ * split workspace, as pa_paged_attention_decode_split's partition kernel
+ * does; a merge launch then combines the partitions of each new token (those
+ * below the row's length, from the token's window on) into out: the split-K
+ * partition/merge described above (not in the pages), with the prefill
+ * kernel's tiles.
+ *   work_items      device int32 [num_work_items][2]: (row, p) pairs, every
+ *                   partition of every row that holds a key one of its
+ *                   tokens sees (pa_prefill_plan_split lists exactly those);
+ *                   a missing item leaves the outputs that need it undefined,
+ *                   a p at or past ceil(max_context_len / partition_size)
+ *                   writes nothing
+ *   partition_size  a multiple of 16 and of block_size, at most 4096
+ *   workspace       device, 256-byte aligned, at least pa_split_workspace_bytes(
+ *                   num_tokens, num_heads, head_size, max_context_len,
+ *                   partition_size) bytes (num_tokens = row_qsl[num_rows]:
+ *                   one workspace row per new token)
+ * The other arguments and the requirements on the caches are those of
+ * pa_paged_attention_prefill; the step's cache writes go first (there is no
+ * one-launch form with partitions).  Errors: as pa_paged_attention_prefill,
+ * plus PA_EINVAL for a null or empty work list, a bad partition_size,
+ * num_tokens outside [1, 2^31), or a missing, small or misaligned workspace. */
+int32_t pa_paged_attention_prefill_split(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* row_seq,
+    const int32_t* row_lens, const int32_t* row_qsl, int32_t num_rows, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t max_context_len,
+    float scale, int32_t dtype, const int32_t* work_items, int64_t num_work_items,
+    int32_t partition_size, int32_t sliding_window, void* workspace, size_t workspace_bytes,
+    int64_t num_tokens, void* stream);
 
 /* ------------------------------------------------------------------------
  * pa_prefill_step: pa_paged_attention_prefill with the step's cache writes

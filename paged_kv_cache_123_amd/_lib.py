@@ -82,10 +82,15 @@ SIGNATURES = {
     "pa_query_blocks": (_i32, [_pi32, _pi32, _i32, _i32, _pi32, _pi32, _pi32, _i64, _pi64]),
     "pa_query_block_hints": (_i32, [_pi32, _pi32, _i32, _pi32, _i32, _i32, _pi32]),
     "pa_prefill_plan": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _pi32]),
+    "pa_prefill_plan_split": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _i32, _pi32, _i64,
+                                     _pi64]),
     "pa_prefill_block_tokens": (_i32, [_i32, _i32, _pi32]),
     "pa_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,
                                           _vp]),
+    "pa_paged_attention_prefill_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                                _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                                _vp, _i64, _i32, _i32, _vp, _sz, _i64, _vp]),
     "pa_prefill_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32,
                                _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _vp, _vp, _i64,
                                _i64, _vp, _vp, _vp]),

@@ -395,10 +395,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeDst dst, PartView src,
   const int L = context_lens ? context_lens[s] : 0;
   const int np = context_lens ? min((L + partition_size - 1) / partition_size, num_parts)
                               : num_parts;
-  // one output row per new token of the sequence (one row when q_start is null)
+  // one output row per new token of the sequence (one row when q_start is
+  // null); workgroup y of the launch takes tokens y, y + gridDim.y, ...
   const int qlen = q_start ? q_start[s + 1] - q_start[s] : 1;
   const int64_t qrow0 = q_start ? q_start[s] : s;
-  for (int qi = 0; qi < qlen; ++qi) {
+  for (int qi = static_cast<int>(blockIdx.y); qi < qlen; qi += static_cast<int>(gridDim.y)) {
     const int64_t row = (qrow0 + qi) * num_heads + h;
     // with a sliding window, partitions before this row's window hold nothing
     const int p0 = window > 0 ? max(0, L - qlen + qi + 1 - window) / partition_size : 0;
@@ -520,24 +521,28 @@ template <int DT, int D>
 hipError_t launch_merge_t(const MergeDst& dst, const PartView& src, const int32_t* context_lens,
                           int32_t num_rows, int32_t num_heads, int32_t partition_size,
                           int32_t num_parts, const int32_t* q_start, int32_t window,
-                          hipStream_t stream) {
+                          int32_t token_split, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>((num_heads + 3) / 4) * num_rows;
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
-                     stream, dst, src, context_lens, num_heads, partition_size, num_parts, q_start,
-                     window);
+  hipLaunchKernelGGL((merge_kernel<DT, D>),
+                     dim3(static_cast<uint32_t>(grid), static_cast<uint32_t>(token_split)),
+                     dim3(256), 0, stream, dst, src, context_lens, num_heads, partition_size,
+                     num_parts, q_start, window);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(int32_t dtype, int32_t head_size, const MergeDst& dst,
                         const PartView& src, const int32_t* context_lens, int32_t num_rows,
                         int32_t num_heads, int32_t partition_size, int32_t num_parts,
-                        const int32_t* q_start, int32_t window, hipStream_t stream) {
+                        const int32_t* q_start, int32_t window, hipStream_t stream,
+                        int32_t token_split = 1) {
   const bool d64 = head_size == 64;
-#define PA_MERGE(DT)                                                                        \
-  return d64 ? launch_merge_t<DT, 64>(dst, src, context_lens, num_rows, num_heads,          \
-                                      partition_size, num_parts, q_start, window, stream)   \
-             : launch_merge_t<DT, 128>(dst, src, context_lens, num_rows, num_heads,         \
-                                       partition_size, num_parts, q_start, window, stream)
+#define PA_MERGE(DT)                                                                     \
+  return d64 ? launch_merge_t<DT, 64>(dst, src, context_lens, num_rows, num_heads,       \
+                                      partition_size, num_parts, q_start, window,        \
+                                      token_split, stream)                               \
+             : launch_merge_t<DT, 128>(dst, src, context_lens, num_rows, num_heads,      \
+                                       partition_size, num_parts, q_start, window,       \
+                                       token_split, stream)
   switch (dtype) {
     case PA_F32: PA_MERGE(PA_F32);
     case PA_F16: PA_MERGE(PA_F16);
@@ -604,7 +609,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t stream) {
   return launch_merge(a.dtype, a.head_size, MergeDst{a.out, nullptr, nullptr, nullptr},
                       split_parts(a), a.context_lens, a.num_seqs, a.num_heads, a.partition_size,
-                      a.num_partitions, a.q_start, a.window, stream);
+                      a.num_partitions, a.q_start, a.window, stream, a.merge_token_split);
 }
 
 hipError_t launch_split_reduce_partials(const DecodeArgs& a, float* m, float* l, float* o,

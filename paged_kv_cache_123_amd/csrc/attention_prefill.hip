@@ -75,15 +75,21 @@ __device__ __forceinline__ uint2 read_columns(const void* lds_addr) {
 
 // BIG_B: blocks of at least 4 tokens, so that the four keys a thread moves
 // per tile share one block.  APPEND: the step's cache writes ride in the
-// launch (pa_prefill_step).
-template <int DT, bool BIG_B, bool APPEND>
+// launch (pa_prefill_step).  SPLIT: the workgroup of item (row, p) attends
+// the keys of partition p, [p P, (p + 1) P), and writes each query vector's
+// partial (m, l, o) to the split workspace for the merge kernel
+// (pa_paged_attention_prefill_split; not with APPEND).
+template <int DT, bool BIG_B, bool APPEND, bool SPLIT>
 __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query, const void* key_cache,
     const void* value_cache, const int32_t* __restrict__ block_tables, int64_t bt_stride,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_lens,
     const int32_t* __restrict__ row_qsl, const int32_t* __restrict__ work_items,
     int32_t num_rows, int32_t num_heads, int32_t num_kv_heads, int32_t log2_block,
-    int32_t log2_group, float scale_log2, int32_t window, AppendArgs ap) {
+    int32_t log2_group, float scale_log2, int32_t window, AppendArgs ap,
+    int32_t partition_size, int32_t num_partitions, float* __restrict__ ws_max,
+    float* __restrict__ ws_sum, float* __restrict__ ws_out) {
+  static_assert(!(APPEND && SPLIT), "the step's writes go with single-pass launches");
   constexpr int NW = kPrefillWaves;
   constexpr int NT = NW * 64;
   constexpr int QG = kPrefillGroups;
@@ -108,6 +114,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
   // its longest first
   const int item = static_cast<int>(blockIdx.x / num_kv_heads);
   const int r = work_items ? work_items[2 * item] : num_rows - 1 - item;
+  const int part = SPLIT ? work_items[2 * item + 1] : 0;
+  if (SPLIT && (part < 0 || part >= num_partitions)) return;  // outside the workspace
   const int kvh = static_cast<int>(blockIdx.x % num_kv_heads);
   const int s = row_seq[r];
   const int L = row_lens[r];
@@ -533,8 +541,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
       }
     }
   };
-  range(std::false_type{}, lo_min, split);
-  if constexpr (APPEND) range(std::true_type{}, split, L);
+  if constexpr (SPLIT) {
+    // the partition's keys (a multiple of 16 from its start, so a thread's
+    // four keys still share one block)
+    range(std::false_type{}, max(lo_min, part * partition_size),
+          min(L, (part + 1) * partition_size));
+  } else {
+    range(std::false_type{}, lo_min, split);
+    if constexpr (APPEND) range(std::true_type{}, split, L);
+  }
 
   if (APPEND && ap.slot_mapping && kvh == 0) {
     // the slots of this row's tokens to the mapping
@@ -551,6 +566,23 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (!valid[g]) continue;
+    if constexpr (SPLIT) {
+      // the partial of the column's vector: its reference (natural-log
+      // units), its sum and its normalised output, or (-inf, 0, 0) when
+      // the partition holds no key it sees; lane (col, grp) holds dims
+      // 16 e + 4 grp + j
+      const int64_t slot =
+          (static_cast<int64_t>(q0 + qi[g]) * num_heads + hq[g]) * num_partitions + part;
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float* dsto = ws_out + slot * D + 4 * grp;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) *reinterpret_cast<f32x4*>(dsto + 16 * e) = o[g][e] * inv;
+      if (grp == 0) {
+        ws_max[slot] = l > 0.0f ? ms[g] * kLn2 : -INFINITY;
+        ws_sum[slot] = l;
+      }
+      continue;
+    }
     // lane (col, grp) holds dims 16 e + 4 grp + j of its column: four
     // contiguous dims per e, stored as one 8-byte piece
     uint16_t* dst = static_cast<uint16_t*>(out) +
@@ -573,21 +605,27 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   while ((1 << log2_block) < a.block_size) ++log2_block;
   int log2_group = 0;
   while ((1 << log2_group) < a.num_heads / a.num_kv_heads) ++log2_group;
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_rows) * a.num_kv_heads));
+  const bool split = a.partition_size > 0;
+  const dim3 grid(static_cast<uint32_t>((split ? a.num_items : static_cast<int64_t>(a.num_rows)) *
+                                        a.num_kv_heads));
   const float sl2 = a.scale * kLog2e;
   // (keys a thread moves per tile: tile x 16 units / threads)
   const bool big = (1 << log2_block) >= kPrefillTile * 16 / (kPrefillWaves * 64);
   const bool append = a.append.qsl != nullptr;
-#define PA_PREFILL(DT, BIG, APP)                                                              \
-  hipLaunchKernelGGL((prefill_kernel<DT, BIG, APP>), grid, dim3(kPrefillWaves * 64), 0, stream, \
-                     a.out, a.query, a.key_cache, a.value_cache, a.block_tables, a.bt_stride,   \
-                     a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows, a.num_heads,   \
-                     a.num_kv_heads, log2_block, log2_group, sl2, a.window, a.append)
-#define PA_PREFILL_DT(DT)                            \
-  if (big && append) PA_PREFILL(DT, true, true);     \
-  else if (big) PA_PREFILL(DT, true, false);         \
-  else if (append) PA_PREFILL(DT, false, true);      \
-  else PA_PREFILL(DT, false, false)
+#define PA_PREFILL(DT, BIG, APP, SPL)                                                          \
+  hipLaunchKernelGGL((prefill_kernel<DT, BIG, APP, SPL>), grid, dim3(kPrefillWaves * 64), 0,    \
+                     stream, a.out, a.query, a.key_cache, a.value_cache, a.block_tables,        \
+                     a.bt_stride, a.row_seq, a.row_lens, a.row_qsl, a.work_items, a.num_rows,   \
+                     a.num_heads, a.num_kv_heads, log2_block, log2_group, sl2, a.window,        \
+                     a.append, a.partition_size, a.num_partitions, a.ws_max, a.ws_sum, a.ws_out)
+#define PA_PREFILL_DT(DT)                                  \
+  if (split && big) PA_PREFILL(DT, true, false, true);     \
+  else if (split) PA_PREFILL(DT, false, false, true);      \
+  else if (big && append) PA_PREFILL(DT, true, true, false); \
+  else if (big) PA_PREFILL(DT, true, false, false);        \
+  else if (append) PA_PREFILL(DT, false, true, false);     \
+  else PA_PREFILL(DT, false, false, false)
+  if (split && append) return hipErrorInvalidValue;
   if (a.dtype == PA_BF16) {
     PA_PREFILL_DT(PA_BF16);
   } else {

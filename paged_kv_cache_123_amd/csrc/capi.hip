@@ -2,6 +2,7 @@
 // validation, then the launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -834,6 +835,58 @@ int32_t pa_paged_attention_prefill(void* out, const void* query, const void* key
   const int32_t st = check_prefill(who, a, bt_stride, head_size, max_context_len);
   if (st != PA_OK) return st;
   return launched(pa::launch_prefill(a, static_cast<hipStream_t>(stream)), who);
+}
+
+int32_t pa_paged_attention_prefill_split(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int64_t bt_stride, const int32_t* row_seq,
+    const int32_t* row_lens, const int32_t* row_qsl, int32_t num_rows, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t max_context_len,
+    float scale, int32_t dtype, const int32_t* work_items, int64_t num_work_items,
+    int32_t partition_size, int32_t sliding_window, void* workspace, size_t workspace_bytes,
+    int64_t num_tokens, void* stream) {
+  const char* who = "pa_paged_attention_prefill_split";
+  pa::PrefillArgs a{out, query, key_cache, value_cache, block_tables, bt_stride, row_seq,
+                    row_lens, row_qsl, work_items, num_rows, num_heads, num_kv_heads,
+                    block_size, scale, dtype, sliding_window};
+  int32_t st = check_prefill(who, a, bt_stride, head_size, max_context_len);
+  if (st != PA_OK) return st;
+  if (!work_items || num_work_items < 1 ||
+      num_work_items > static_cast<int64_t>(0x7fffffff) / num_kv_heads)
+    return fail(PA_EINVAL, "pa_paged_attention_prefill_split: bad work list");
+  if (partition_size < 16 || partition_size > 4096 || partition_size % 16 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PA_EINVAL, "pa_paged_attention_prefill_split: bad partition_size");
+  if (num_tokens < 1 || num_tokens > 0x7fffffff)
+    return fail(PA_EINVAL, "pa_paged_attention_prefill_split: num_tokens out of range");
+  const size_t need = pa_split_workspace_bytes(static_cast<int32_t>(num_tokens), num_heads,
+                                               head_size, max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_EINVAL,
+                "pa_paged_attention_prefill_split: workspace missing, too small or misaligned");
+  const SplitLayout w =
+      split_layout(num_tokens, num_heads, head_size, max_context_len, partition_size);
+  // the merge: one output row per new token of each query-block row, over the
+  // partitions below the row's length (from the row's window on)
+  pa::DecodeArgs d{out, query, key_cache, value_cache, block_tables, bt_stride, row_lens,
+                   num_rows, num_heads, num_kv_heads, head_size, block_size, 0, 1, scale, dtype,
+                   nullptr, nullptr, nullptr, nullptr, 0};
+  d.q_start = row_qsl;
+  d.window = sliding_window;
+  // a row holds up to 128 / G tokens: up to 32 merge workgroups per (row,
+  // four heads), each taking every 32nd token
+  d.merge_token_split = std::min(32, pa::prefill_block_tokens(num_heads / num_kv_heads));
+  set_split(d, workspace, w, partition_size);
+  a.partition_size = partition_size;
+  a.num_partitions = w.np;
+  a.num_items = num_work_items;
+  a.ws_max = d.ws_max;
+  a.ws_sum = d.ws_sum;
+  a.ws_out = d.ws_out;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launched(pa::launch_prefill(a, s), "pa_paged_attention_prefill_split (partitions)");
+  if (st != PA_OK) return st;
+  return launched(pa::launch_split_reduce(d, s), "pa_paged_attention_prefill_split (merge)");
 }
 
 int32_t pa_prefill_step(void* out, const void* query, void* key_cache, void* value_cache,

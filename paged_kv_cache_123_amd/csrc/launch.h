@@ -60,6 +60,8 @@ struct DecodeArgs {
   int32_t max_group = 0;      // members of the widest group item (cascade plan), 0 for none
   bool cascade_chunked = false;  // a chunked cascade plan on the single-pass kernel,
                                  // writing partials of partition_size-token slots
+  int32_t merge_token_split = 1;  // workgroups per (row, head group) of the merge, each
+                                  // merging every merge_token_split-th new token
 };
 
 // Query vectors one workgroup serves: (new tokens per sequence) x (query heads
@@ -104,6 +106,13 @@ struct PrefillArgs {
   int32_t dtype;
   int32_t window;
   dev::AppendArgs append{};  // the step's cache writes (append.qsl == nullptr: none)
+  // split launches (partition_size > 0): work_items holds num_items (row, p)
+  // pairs and the partials go to the split workspace's three sections
+  int32_t partition_size = 0, num_partitions = 0;
+  int64_t num_items = 0;
+  float* ws_max = nullptr;
+  float* ws_sum = nullptr;
+  float* ws_out = nullptr;
 };
 int prefill_block_tokens(int group);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -470,6 +470,57 @@ extern "C" int32_t pa_prefill_plan(const int32_t* row_seq, const int32_t* row_le
   return PA_OK;
 }
 
+// Split launch order of the prefill kernel: per row, the partitions from the
+// one holding its first visible key to the one holding its last; sequences
+// by their largest row, largest first, and within a sequence by partition,
+// then by row size, so that the items reading one partition's rows run
+// together.
+extern "C" int32_t pa_prefill_plan_split(const int32_t* row_seq, const int32_t* row_lens,
+                                         const int32_t* row_qlens, int32_t num_rows,
+                                         int32_t sliding_window, int32_t partition_size,
+                                         int32_t* items, int64_t capacity, int64_t* num_items) {
+  if (!row_seq || !row_lens || !num_items || num_rows < 1 || sliding_window < 0 ||
+      partition_size < 1)
+    return pa::fail(PA_EINVAL, "pa_prefill_plan_split: bad argument");
+  struct Item {
+    int32_t row, part;
+  };
+  std::vector<Item> all;
+  std::vector<int64_t> size(num_rows);
+  std::map<int32_t, int64_t> seq_size;
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const int64_t L = row_lens[r];
+    const int64_t n = row_qlens ? row_qlens[r] : 1;
+    if (row_seq[r] < 0 || L < 1 || n < 0 || n > L)
+      return pa::fail(PA_EINVAL,
+                      "pa_prefill_plan_split: row sequence, length or tokens out of range");
+    const int64_t lo = sliding_window > 0 ? std::max<int64_t>(0, L - n + 1 - sliding_window) : 0;
+    size[r] = L - lo;
+    int64_t& m = seq_size[row_seq[r]];
+    m = std::max(m, size[r]);
+    const int64_t p_end = (L + partition_size - 1) / partition_size;
+    for (int64_t p = lo / partition_size; p < p_end; ++p)
+      all.push_back({r, static_cast<int32_t>(p)});
+  }
+  *num_items = static_cast<int64_t>(all.size());
+  if (!items) return PA_OK;
+  if (capacity < *num_items)
+    return pa::fail(PA_EINVAL, "pa_prefill_plan_split: capacity below the item count");
+  std::sort(all.begin(), all.end(), [&](const Item& a, const Item& b) {
+    const int64_t sa = seq_size[row_seq[a.row]], sb = seq_size[row_seq[b.row]];
+    if (sa != sb) return sa > sb;
+    if (row_seq[a.row] != row_seq[b.row]) return row_seq[a.row] < row_seq[b.row];
+    if (a.part != b.part) return a.part < b.part;
+    if (size[a.row] != size[b.row]) return size[a.row] > size[b.row];
+    return a.row < b.row;
+  });
+  for (size_t i = 0; i < all.size(); ++i) {
+    items[2 * i] = all[i].row;
+    items[2 * i + 1] = all[i].part;
+  }
+  return PA_OK;
+}
+
 // Members whose decode queries fill the matrix cores' 16 columns of a group
 // item: 16 / (num_heads / num_kv_heads), at most 8; 0 where the group items'
 // kernels do not exist (fp32 storage, head_size other than 128).

@@ -442,6 +442,25 @@ def prefill_plan(row_seq, row_lens, row_qlens=None, sliding_window: int = 0) -> 
     return out
 
 
+def prefill_plan_split(row_seq, row_lens, row_qlens, sliding_window: int,
+                       partition_size: int) -> np.ndarray:
+    """Work list of the split prefill kernel (pa_prefill_plan_split): host
+    int32 [num_items, 2] of (row, partition)."""
+    rs = np.ascontiguousarray(np.asarray(row_seq, dtype=np.int32))
+    rl = np.ascontiguousarray(np.asarray(row_lens, dtype=np.int32))
+    rq = np.ascontiguousarray(np.asarray(row_qlens, dtype=np.int32))
+    if rl.size != rs.size or rq.size != rs.size:
+        raise ValueError("row_lens and row_qlens must have one entry per row")
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    n = ctypes.c_int64(0)
+    args = (rs.ctypes.data_as(p32), rl.ctypes.data_as(p32), rq.ctypes.data_as(p32), rs.size,
+            sliding_window, partition_size)
+    check(lib().pa_prefill_plan_split(*args, None, 0, ctypes.byref(n)))
+    out = np.empty((max(n.value, 1), 2), dtype=np.int32)
+    check(lib().pa_prefill_plan_split(*args, out.ctypes.data_as(p32), n.value, ctypes.byref(n)))
+    return out[:n.value]
+
+
 def prefill_block_tokens(num_heads: int, num_kv_heads: int) -> int:
     """New tokens per query block of the prefill kernel (pa_prefill_block_tokens)."""
     t = ctypes.c_int32(0)
@@ -785,6 +804,43 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: t
         block_tables.data_ptr(), block_tables.stride(0), row_seq.data_ptr(), row_lens.data_ptr(),
         row_qsl.data_ptr(), R, query.shape[1], hkv, D, B, max_context_len, scale,
         _dtype(key_cache), items or None, sliding_window, _stream()))
+
+
+def paged_attention_prefill_split(out: torch.Tensor, query: torch.Tensor,
+                                  key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, row_seq: torch.Tensor,
+                                  row_lens: torch.Tensor, row_qsl: torch.Tensor, scale: float,
+                                  max_context_len: int, work_items: torch.Tensor,
+                                  partition_size: int, workspace: torch.Tensor,
+                                  sliding_window: int = 0) -> None:
+    """pa_paged_attention_prefill_split: the prefill kernel over (row,
+    partition) work items (prefill_plan_split) and the merge; workspace from
+    alloc_split_workspace(num_tokens, ...)."""
+    _dev(out, query, key_cache, value_cache, block_tables, row_seq, row_lens, row_qsl,
+         work_items, workspace)
+    nb, hkv, B, D = _cache_shape(key_cache, value_cache)
+    if query.dim() != 3 or query.shape[2] != D or out.shape != query.shape:
+        raise ValueError("query/out must be [num_tokens, num_heads, head_size]")
+    if query.dtype != key_cache.dtype or out.dtype != key_cache.dtype:
+        raise TypeError("query/out must have the cache dtype")
+    for n, t in (("query", query), ("out", out), ("block_tables", block_tables),
+                 ("row_seq", row_seq), ("row_lens", row_lens), ("row_qsl", row_qsl),
+                 ("work_items", work_items), ("workspace", workspace)):
+        _contig(n, t)
+    R = row_seq.numel()
+    for n, t, size in (("row_seq", row_seq, R), ("row_lens", row_lens, R),
+                       ("row_qsl", row_qsl, R + 1)):
+        if t.dtype != torch.int32 or t.numel() != size:
+            raise ValueError(f"{n} must be int32 with {size} entries")
+    if work_items.dtype != torch.int32 or work_items.dim() != 2 or work_items.shape[1] != 2:
+        raise ValueError("work_items must be int32 [num_items, 2]")
+    check(lib().pa_paged_attention_prefill_split(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.stride(0), row_seq.data_ptr(), row_lens.data_ptr(),
+        row_qsl.data_ptr(), R, query.shape[1], hkv, D, B, max_context_len, scale,
+        _dtype(key_cache), work_items.data_ptr(), work_items.shape[0], partition_size,
+        sliding_window, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        query.shape[0], _stream()))
 
 
 def prepare_prefill_step(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

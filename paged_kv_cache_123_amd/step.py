@@ -211,13 +211,15 @@ class DecodeStep:
                 raise ValueError("one new token's query heads exceed a workgroup's query vectors")
             if self.max_query_len > block:
                 self.query_blocks = True
-                # single pass on the matrix cores: the prefill kernel's larger
-                # blocks, each K/V tile staged once in LDS for the whole block;
-                # it reads the step's new rows from their inputs, so the step
-                # can run as one launch.  On the decode kernels, blocks of one
-                # sequence read each other's new rows from the cache.
-                self.prefill_rows = prefill_kernel and matrix and not self.partition_size
-                self.fused_ok = self.fused_ok and self.prefill_rows
+                # on the matrix cores: the prefill kernel's larger blocks, each
+                # K/V tile staged once in LDS for the whole block; in a single
+                # pass it reads the step's new rows from their inputs, so the
+                # step can run as one launch (with partitions: the cache
+                # writes first, then the split kernel and its merge).  On the
+                # decode kernels, blocks of one sequence read each other's new
+                # rows from the cache.
+                self.prefill_rows = prefill_kernel and matrix
+                self.fused_ok = self.fused_ok and self.prefill_rows and not self.partition_size
                 if self.prefill_rows:
                     block = ops.prefill_block_tokens(H, values["key_cache"].shape[1])
                 row_seq, row_lens, row_qsl = ops.query_blocks(lens, self.query_start_loc_host,
@@ -233,7 +235,12 @@ class DecodeStep:
                 self.attn_max_query_len = int(np.diff(row_qsl).max())
                 self.attn_shared = torch.from_numpy(row_shared).to(dev)
                 self.row_seq = torch.from_numpy(row_seq).to(dev)
-                if self.prefill_rows:
+                if self.prefill_rows and self.partition_size:
+                    # (row, partition) items, a sequence's together
+                    self.prefill_items = torch.from_numpy(ops.prefill_plan_split(
+                        row_seq, row_lens, np.diff(row_qsl), self.sliding_window,
+                        self.partition_size)).to(dev)
+                elif self.prefill_rows:
                     # launch order: a sequence's rows together, the largest
                     # sequences first
                     self.prefill_items = torch.from_numpy(ops.prefill_plan(
@@ -269,6 +276,13 @@ class DecodeStep:
                                         self.partition_size or self.cascade_chunk, self.plan,
                                         self.num_items, self.max_group, self.workspace,
                                         chunked=bool(self.cascade_chunk))
+        elif self.prefill_rows and self.partition_size:
+            ops.paged_attention_prefill_split(self.out, self.query, self.key_cache,
+                                              self.value_cache, self.block_tables, self.row_seq,
+                                              self.attn_lens, self.attn_qsl, self.scale,
+                                              self.max_context_len, self.prefill_items,
+                                              self.partition_size, self.workspace,
+                                              self.sliding_window)
         elif self.prefill_rows:
             ops.paged_attention_prefill(self.out, self.query, self.key_cache, self.value_cache,
                                         self.block_tables, self.row_seq, self.attn_lens,
@@ -310,9 +324,10 @@ class DecodeStep:
         """The one-launch step's checks and argument marshalling, without a
         launch (host only; done once)."""
         if not self.fused_ok:
-            raise ValueError("a copy-on-write of a block of several kernel blocks, or query "
+            raise ValueError("a copy-on-write of a block of several kernel blocks, query "
                              "blocks on the decode kernels (they read each other's new rows "
-                             "from the cache), need the separate calls: run the step unfused")
+                             "from the cache) or split query blocks need the separate calls: "
+                             "run the step unfused")
         if self._fused_call is None:
             if self.prefill_rows:
                 self._fused_call = ops.prepare_prefill_step(

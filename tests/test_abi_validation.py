@@ -32,6 +32,11 @@ def _prefill(**kw):
             a["scale"], a["dtype"], a["items"], a["window"], None]
 
 
+def _prefill_split(items=P, n_items=5, part=32, window=0, ws=P, ws_bytes=1 << 30, tokens=40,
+                   **kw):
+    return _prefill(**kw)[:-3] + [items, n_items, part, window, ws, ws_bytes, tokens, None]
+
+
 CASES = [
     # (entry point, arguments, expected text in pa_last_error)
     ("pa_paged_attention_decode", _decode(S=0) + [None], "sizes must be >= 1"),
@@ -173,6 +178,19 @@ CASES = [
      "needs 16-bit storage and head_size 128"),
     ("pa_prefill_step", _prefill(window=-1)[:-1] + [P, P, P, 256, 256, None, None, None],
      "sliding_window < 0"),
+    ("pa_paged_attention_prefill_split", _prefill_split(window=-1), "sliding_window < 0"),
+    ("pa_paged_attention_prefill_split", _prefill_split(dtype=F32),
+     "needs 16-bit storage and head_size 128"),
+    ("pa_paged_attention_prefill_split", _prefill_split(items=None), "bad work list"),
+    ("pa_paged_attention_prefill_split", _prefill_split(n_items=0), "bad work list"),
+    ("pa_paged_attention_prefill_split", _prefill_split(part=24), "bad partition_size"),
+    ("pa_paged_attention_prefill_split", _prefill_split(part=8, B=8, bt_stride=16),
+     "bad partition_size"),
+    ("pa_paged_attention_prefill_split", _prefill_split(part=4112), "bad partition_size"),
+    ("pa_paged_attention_prefill_split", _prefill_split(tokens=0), "num_tokens out of range"),
+    ("pa_paged_attention_prefill_split", _prefill_split(ws=None), "workspace missing"),
+    ("pa_paged_attention_prefill_split", _prefill_split(ws_bytes=64), "too small"),
+    ("pa_paged_attention_prefill_split", _prefill_split(ws=P + 4), "misaligned"),
     ("pa_validate_tables", [None, 8, P, 2, 16, 100, 0, P, None], "NULL pointer"),
     ("pa_validate_tables", [P, 8, P, 0, 16, 100, 0, P, None], "bad sizes"),
     ("pa_validate_tables", [P, 8, P, 2, 16, 100, -1, P, None], "bad sizes"),

@@ -43,6 +43,11 @@ CASES = [
     # more new tokens than one table chunk: a row's own tokens straddle the
     # second chunk's start in the one-launch step's range of new rows
     ("bf16", 128, 16, 1, [2600, 300], [2500, 300], 0, 0),
+    # long contexts under few rows, in partitions (the split prefill kernel
+    # and its merge), with and without a window
+    ("bf16", 128, 16, 1, [6000], [600], 1024, 0),
+    ("f16", 128, 16, 8, [5000, 900], [400, 900], 512, 1500),
+    ("bf16", 128, 32, 2, [3100, 2300], [200, 130], 2048, 0),
 ]
 
 
@@ -56,8 +61,8 @@ def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window,
     _require_gpu()
     from paged_kv_cache_123_amd.step import DecodeStep
     matrix = dtype != "f32" and D == 128
-    if prefill_kernel and (decode_kernel == "valu" or not matrix or part):
-        pytest.skip("the prefill kernel runs 16-bit, head_size 128, single pass; once")
+    if prefill_kernel and (decode_kernel == "valu" or not matrix):
+        pytest.skip("the prefill kernel runs 16-bit, head_size 128; once")
     print(f"[prefill] {dtype} D={D} B={B} G={G} new={new} P={part} W={window} "
           f"kernel={'prefill' if prefill_kernel else decode_kernel}", flush=True)
     w = W.custom_multi("prefill", 31, lens, new, dtype=dtype, H=2 * G, Hkv=2, D=D, B=B,
@@ -68,10 +73,12 @@ def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window,
                       part, all_queries=True, sliding_window=window,
                       prefill_kernel=prefill_kernel)
     assert step.query_blocks, "the chunks should need several query blocks"
-    assert step.prefill_rows == (prefill_kernel and matrix and not part)
-    if not step.prefill_rows:
+    assert step.prefill_rows == (prefill_kernel and matrix)
+    assert step.fused_ok == (step.prefill_rows and not part)
+    if not step.fused_ok:
         with pytest.raises(ValueError):
-            step.fused()  # blocks of one sequence read each other's new rows from the cache
+            step.fused()  # the decode kernels read each other's new rows from the cache;
+            # the split prefill kernel has no one-launch form
     out = step.run().clone()
     torch.cuda.synchronize()
     ora = OracleStep(w)
@@ -82,7 +89,7 @@ def test_prefill_chunks_as_query_blocks(dtype, D, B, G, lens, new, part, window,
         assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
     want = ora.attention_multi(host["query"], kc, vc)
     check_attention(to_host(out), want, w.dtype, f"prefill {dtype} G={G} P={part} W={window}")
-    if step.prefill_rows:
+    if step.fused_ok:
         # the one-launch step (pa_prefill_step) on a fresh copy of the caches
         # before the step: the same caches, slots and output, bit for bit
         vals2 = W.make_values(w, DEV)

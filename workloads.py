@@ -316,6 +316,29 @@ def qwen72b_prefill512_bf16(num_seqs=16, chunk=512):
     return w
 
 
+def llama7b_longprefill_fp16(prefix=32256, chunk=512, partition_size=4096):
+    """One sequence of the Llama-7B layer with a long cached prefix taking a
+    512-token prefill chunk: four query blocks x 32 KV heads give only 128
+    workgroups in one pass, so the keys are cut into partitions (the split
+    prefill kernel and its merge)."""
+    w = custom_multi("llama7b_longprefill_fp16", 10, [prefix + chunk], [chunk], dtype="f16",
+                     H=32, Hkv=32, D=128, B=16, partition_size=partition_size)
+    w.notes = (f"1 sequence, cached prefix {prefix} + a {chunk}-token prefill chunk (every new "
+               f"token a query, causal); 32x128 MHA fp16, B=16, partitions of {partition_size}")
+    return w
+
+
+def qwen72b_longprefill_bf16(prefix=32256, chunk=512, partition_size=4096):
+    """The long-prefix prefill chunk on the Qwen2.5-72B-style GQA layer (64
+    query / 8 KV heads, bf16): 32 query blocks x 8 KV heads, 256 workgroups in
+    one pass (one per CU), partitions by default."""
+    w = custom_multi("qwen72b_longprefill_bf16", 11, [prefix + chunk], [chunk], dtype="bf16",
+                     H=64, Hkv=8, D=128, B=16, sigma=0.5, partition_size=partition_size)
+    w.notes = (f"1 sequence, cached prefix {prefix} + a {chunk}-token prefill chunk; GQA 64q/8kv "
+               f"x 128 bf16, B=16, partitions of {partition_size}")
+    return w
+
+
 def qwen72b_gqa_spec2_bf16(num_seqs=256, drafts=2):
     """The GQA batch verifying 2 speculative tokens per sequence (2 x 8 query
     vectors per KV head fill the 16 matrix-core columns)."""
@@ -452,6 +475,8 @@ CONFIGS = {
     "llama7b_spec4_fp16": llama7b_spec4_fp16,
     "llama7b_prefill512_fp16": llama7b_prefill512_fp16,
     "qwen72b_prefill512_bf16": qwen72b_prefill512_bf16,
+    "llama7b_longprefill_fp16": llama7b_longprefill_fp16,
+    "qwen72b_longprefill_bf16": qwen72b_longprefill_bf16,
     "qwen72b_gqa_spec2_bf16": qwen72b_gqa_spec2_bf16,
     "long_context_cp8_bf16": long_context_cp8_bf16,
     "qwen72b_gqa_tp8_bf16": qwen72b_gqa_tp8_bf16,
