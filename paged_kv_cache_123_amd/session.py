@@ -174,7 +174,9 @@ class PagedKVCache:
         """A step whose sequences bring more new tokens than a workgroup holds,
         attended over query blocks (pa_query_blocks): on the prefill kernel
         with the cache writes in the same launch (pa_prefill_step), else the
-        cache writes (copy-on-write, slot mapping, scatter) first."""
+        cache writes (copy-on-write, slot mapping, scatter) first, then the
+        split prefill kernel (partitions, on the matrix cores) or the decode
+        kernels."""
         dev = self.device
         T = len(positions)
         tab = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
@@ -200,6 +202,21 @@ class PagedKVCache:
                                  torch.from_numpy(positions).to(dev), tab, self.block_size, slots,
                                  T)
         ops.reshape_and_cache(key, value, self.key_cache, self.value_cache, slots)
+        if matrix:
+            # partitions on the matrix cores: the split prefill kernel and its merge
+            row_seq, row_lens, row_qsl = ops.query_blocks(
+                lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
+            items = ops.prefill_plan_split(row_seq, row_lens, np.diff(row_qsl),
+                                           self.sliding_window, self.partition_size)
+            workspace = ops.alloc_split_workspace(T, H, self.head_size, max_len,
+                                                  self.partition_size, dev)
+            ops.paged_attention_prefill_split(
+                out, query, self.key_cache, self.value_cache, tab,
+                torch.from_numpy(row_seq).to(dev), torch.from_numpy(row_lens).to(dev),
+                torch.from_numpy(row_qsl).to(dev), scale, max_len,
+                torch.from_numpy(items).to(dev), self.partition_size, workspace,
+                self.sliding_window)
+            return out
         block = (16 if matrix else 8) // (H // self.num_kv_heads)
         row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl_host, block)
         # a sequence cut into several rows has all of its blocks read by each

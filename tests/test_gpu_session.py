@@ -114,7 +114,7 @@ def test_many_steps_against_the_oracle(dtype, B, G, window, part, cascade):
 
 @pytest.mark.parametrize("dtype,B,G,window,part", [
     ("f16", 16, 1, 0, 0), ("bf16", 16, 4, 0, 0), ("bf16", 8, 2, 40, 0), ("f32", 8, 2, 0, 0),
-    ("f16", 16, 2, 0, 32),
+    ("f16", 16, 2, 0, 32), ("bf16", 16, 4, 40, 64),
 ])
 def test_every_new_token_a_query_over_many_steps(dtype, B, G, window, part):
     """Prompts and prefill chunks with every new token a query (query blocks,
