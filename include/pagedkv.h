@@ -628,6 +628,17 @@ int32_t pa_prefill_plan_split(const int32_t* row_seq, const int32_t* row_lens,
                               int32_t partition_size, int32_t* items, int64_t capacity,
                               int64_t* num_items);
 
+/* pa_prefill_auto_partition (host): the partition size a caller without one
+ * should give the split prefill, or 0 for one pass.  4096 when the rows
+ * would give fewer (row, KV head) workgroups than two per CU of an MI355X
+ * (512) and the longest row holds at least 8192 keys (and 4096 is a
+ * multiple of block_size), else 0.  (One sequence of 32k keys taking a
+ * 512-token chunk: 128 workgroups on a 32-KV-head layer; its split launch is
+ * 2.3x faster than the one pass.)  PA_EINVAL for a null output,
+ * num_rows, num_kv_heads or block_size below 1, or a negative length. */
+int32_t pa_prefill_auto_partition(int32_t num_rows, int32_t num_kv_heads, int32_t max_row_len,
+                                  int32_t block_size, int32_t* partition_size);
+
 /* ------------------------------------------------------------------------
  * Prefill attention over query blocks on the matrix cores (16-bit storage,
  * head_size 128, single pass): the result of pa_paged_attention_multi for

@@ -84,6 +84,7 @@ SIGNATURES = {
     "pa_prefill_plan": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _pi32]),
     "pa_prefill_plan_split": (_i32, [_pi32, _pi32, _pi32, _i32, _i32, _i32, _pi32, _i64,
                                      _pi64]),
+    "pa_prefill_auto_partition": (_i32, [_i32, _i32, _i32, _i32, _pi32]),
     "pa_prefill_block_tokens": (_i32, [_i32, _i32, _pi32]),
     "pa_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,

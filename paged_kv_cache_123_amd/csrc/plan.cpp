@@ -521,6 +521,22 @@ extern "C" int32_t pa_prefill_plan_split(const int32_t* row_seq, const int32_t* 
   return PA_OK;
 }
 
+// Partitions for the split prefill when one pass leaves the GPU mostly idle:
+// fewer (row, KV head) workgroups than two per CU of an MI355X (256 CUs) and
+// a row of at least 8192 keys; 0 otherwise.
+extern "C" int32_t pa_prefill_auto_partition(int32_t num_rows, int32_t num_kv_heads,
+                                             int32_t max_row_len, int32_t block_size,
+                                             int32_t* partition_size) {
+  if (!partition_size || num_rows < 1 || num_kv_heads < 1 || max_row_len < 0 || block_size < 1)
+    return pa::fail(PA_EINVAL, "pa_prefill_auto_partition: bad argument");
+  constexpr int64_t kSlots = 2 * 256;
+  constexpr int32_t kPartition = 4096;
+  const bool few = static_cast<int64_t>(num_rows) * num_kv_heads < kSlots;
+  *partition_size =
+      few && max_row_len >= 2 * kPartition && kPartition % block_size == 0 ? kPartition : 0;
+  return PA_OK;
+}
+
 // Members whose decode queries fill the matrix cores' 16 columns of a group
 // item: 16 / (num_heads / num_kv_heads), at most 8; 0 where the group items'
 // kernels do not exist (fp32 storage, head_size other than 128).

@@ -461,6 +461,16 @@ def prefill_plan_split(row_seq, row_lens, row_qlens, sliding_window: int,
     return out[:n.value]
 
 
+def prefill_auto_partition(num_rows: int, num_kv_heads: int, max_row_len: int,
+                           block_size: int) -> int:
+    """Partition size for the split prefill when one pass would leave the GPU
+    mostly idle, else 0 (pa_prefill_auto_partition)."""
+    p = ctypes.c_int32(0)
+    check(lib().pa_prefill_auto_partition(num_rows, num_kv_heads, max_row_len, block_size,
+                                          ctypes.byref(p)))
+    return p.value
+
+
 def prefill_block_tokens(num_heads: int, num_kv_heads: int) -> int:
     """New tokens per query block of the prefill kernel (pa_prefill_block_tokens)."""
     t = ctypes.c_int32(0)

@@ -184,9 +184,17 @@ class PagedKVCache:
         out = torch.empty_like(query)
         H = query.shape[1]
         max_len = int(lens.max())
-        if matrix and not self.partition_size:
+        part = self.partition_size
+        if matrix and not part:
             row_seq, row_lens, row_qsl = ops.query_blocks(
                 lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
+            # a long context under few rows goes to the split kernel by itself
+            keys = int(row_lens.max())
+            if self.sliding_window:
+                keys = min(keys, self.sliding_window + int(np.diff(row_qsl).max()))
+            part = ops.prefill_auto_partition(len(row_seq), self.num_kv_heads, keys,
+                                              self.block_size)
+        if matrix and not part:
             items = ops.prefill_plan(row_seq, row_lens, np.diff(row_qsl), self.sliding_window)
             ops.prefill_step(out, query, self.key_cache, self.value_cache, tab,
                              torch.from_numpy(row_seq).to(dev), torch.from_numpy(row_lens).to(dev),
@@ -207,15 +215,13 @@ class PagedKVCache:
             row_seq, row_lens, row_qsl = ops.query_blocks(
                 lens, qsl_host, ops.prefill_block_tokens(H, self.num_kv_heads))
             items = ops.prefill_plan_split(row_seq, row_lens, np.diff(row_qsl),
-                                           self.sliding_window, self.partition_size)
-            workspace = ops.alloc_split_workspace(T, H, self.head_size, max_len,
-                                                  self.partition_size, dev)
+                                           self.sliding_window, part)
+            workspace = ops.alloc_split_workspace(T, H, self.head_size, max_len, part, dev)
             ops.paged_attention_prefill_split(
                 out, query, self.key_cache, self.value_cache, tab,
                 torch.from_numpy(row_seq).to(dev), torch.from_numpy(row_lens).to(dev),
                 torch.from_numpy(row_qsl).to(dev), scale, max_len,
-                torch.from_numpy(items).to(dev), self.partition_size, workspace,
-                self.sliding_window)
+                torch.from_numpy(items).to(dev), part, workspace, self.sliding_window)
             return out
         block = (16 if matrix else 8) // (H // self.num_kv_heads)
         row_seq, row_lens, row_qsl = ops.query_blocks(lens, qsl_host, block)

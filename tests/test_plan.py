@@ -471,3 +471,16 @@ def test_prefill_plan_split_rejects_bad_arguments():
         ops.prefill_plan_split([0], [5], [1], 0, 0)     # no partition size
     with pytest.raises(PagedKVError):
         ops.prefill_plan_split([0], [5], [1], -1, 64)   # negative window
+
+
+def test_prefill_auto_partition_rule():
+    """4096 when the rows give fewer than 512 (row, KV head) workgroups and the
+    longest row holds at least 8192 keys; 0 otherwise."""
+    from paged_kv_cache_123_amd import PagedKVError, ops
+    assert ops.prefill_auto_partition(4, 32, 32768, 16) == 4096
+    assert ops.prefill_auto_partition(15, 32, 8192, 16) == 4096
+    assert ops.prefill_auto_partition(16, 32, 8192, 16) == 0     # 512 workgroups
+    assert ops.prefill_auto_partition(4, 32, 8191, 16) == 0      # too short
+    assert ops.prefill_auto_partition(4, 32, 32768, 48) == 0     # 4096 not a multiple of B
+    with pytest.raises(PagedKVError):
+        ops.prefill_auto_partition(0, 32, 100, 16)
